@@ -1,0 +1,12 @@
+"""CPU oracle of the W4A8 MoE routed-expert layer (test infrastructure only).
+
+Imported by the tests, the smoke check and the benchmark's CPU-baseline leg;
+never by the product path.
+"""
+from .w4a8_oracle import *  # noqa: F401,F403
+from .w4a8_oracle import (E4M3_VALUES, FP8_MAX, GROUP, SHRINK_RATIOS,  # noqa: F401
+                          bf16_bits_to_f32, dequant_weights, e4m3_decode, e4m3_encode,
+                          f32_to_bf16_bits, fp8_block_quant_dequant, grouped_gemm,
+                          grouped_gemm_exact_groups, int4_pack, int4_unpack, moe_layer,
+                          permute, quant_act, quant_rows, quantize_int4_g128, relative_l2,
+                          route, swiglu, swiglu_f32, unpermute)
