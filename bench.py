@@ -1,0 +1,192 @@
+#!/usr/bin/env python3
+"""Benchmark of the W4A8 MoE routed-expert layer on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 1]
+
+A step is one pass of the whole layer (quant_act, route, permute, gate/up
+grouped GEMM, SwiGLU, down grouped GEMM, combine) over one batch of
+synthetic tokens, inputs already resident in HBM.  The default workload is
+decode at 128 tokens (H=6144, I=2048, 256 experts, top-8), the shape the
+headline metric is quoted on; --config 3 runs the 8K-token prefill.
+
+Prints ONE JSON line: layer tokens/s, the roofline of the dominant kernel
+(the gate/up grouped GEMM, timed with events on its own stream), and the CPU
+oracle timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE layer tokens/s + % HBM peak (decode T=128) and % FP8 MFMA peak (prefill T=8192)"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+FP8_PEAK_TFLOPS = 5000.0       # MI355X dense FP8 MFMA, published (no sparsity)
+
+
+def kernel_sources_hash() -> str:
+    """Hash of the grouped-GEMM sources: counter files taken on other code are ignored."""
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "quantized_grouped_gemm_token_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        if name.startswith("gemm_") or name in ("common.hpp",):
+            with open(os.path.join(csrc, name), "rb") as f:
+                h.update(name.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(path: str, kernel_hash: str):
+    """HBM bytes per launch from a committed rocprofv3 counter summary, if it
+    was taken on the current kernel sources."""
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        d = json.load(f)
+    if d.get("kernel_sources_hash") != kernel_hash:
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(wl, n_tokens: int) -> dict:
+    """The oracle layer on the first n_tokens tokens (single thread)."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_limits
+        limit = threadpool_limits(limits=1)
+    except Exception:   # pragma: no cover - threadpoolctl is installed in this image
+        limit = None
+    sel = np.arange(n_tokens)
+    t0 = time.perf_counter()
+    res = oracle.moe_layer(wl.x_bf16[sel], wl.logits[sel], wl.w13, wl.s13, wl.w2, wl.s2, k=wl.shape.k)
+    dt = time.perf_counter() - t0
+    if limit is not None:
+        limit.restore_original_limits()
+    touched = int((np.diff(res["offsets"]) > 0).sum())
+    return {"value": n_tokens / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"oracle layer (numpy, fp64 sums, 1 thread) on {n_tokens} of the {wl.shape.T} tokens of "
+                      f"'{wl.shape.name}', touching {touched} experts; {dt:.1f} s wall"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=1, help="workload index: 1 decode T=128 (default), "
+                                                          "2 decode T=256, 3 prefill T=8192, 4 skewed T=16384")
+    ap.add_argument("--cpu-tokens", type=int, default=16, help="tokens in the CPU oracle sample (0: skip)")
+    ap.add_argument("--quiet", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
+              "(the layer holds all experts on one device and has no multi-GPU path)", file=sys.stderr)
+        return 2
+
+    import torch
+
+    from quantized_grouped_gemm_token_amd import ops, workloads
+    from quantized_grouped_gemm_token_amd.layer import W4A8MoE
+
+    log = (lambda *a: None) if args.quiet else (lambda *a: print("[bench]", *a, file=sys.stderr, flush=True))
+    if not ops.w4a8_moe_device_supported():
+        print("bench.py: cuda:0 is not a gfx950: " + ops.last_error(), file=sys.stderr)
+        return 1
+    dev = "cuda:0"
+    t0 = time.time()
+    wl = workloads.make_config(args.config)
+    sh = wl.shape
+    log(f"generated {sh.name} in {time.time() - t0:.1f} s")
+    to = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)  # noqa: E731
+    moe = W4A8MoE(to(wl.w13), to(wl.s13), to(wl.w2), to(wl.s2), k=sh.k)
+    x = torch.from_numpy(wl.x_bf16.view(np.int16)).to(dev).view(torch.bfloat16)
+    logits = to(wl.logits)
+    y = torch.empty((sh.T, sh.H), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    for _ in range(args.warmup):
+        moe(x, logits, y)
+    torch.cuda.synchronize()
+    log(f"warmup {args.warmup} done")
+
+    steps = W4A8MoE.STEPS
+    evs = [{s: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for s in steps}
+           for _ in range(args.steps)]
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for i in range(args.steps):
+        moe(x, logits, y, events=evs[i])
+    stop.record(stream)
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(stop)
+    ms_step = total_ms / args.steps
+    per_step = {s: float(np.mean([e[s][0].elapsed_time(e[s][1]) for e in evs])) for s in steps}
+    log("per step ms: " + ", ".join(f"{k}={v:.4f}" for k, v in per_step.items()))
+
+    # algorithmic work of the routed experts actually touched
+    offsets = moe.buffers(sh.T)["offsets"].cpu().numpy()
+    counts = np.diff(offsets)
+    touched = int((counts > 0).sum())
+    R = sh.T * sh.k
+    w13_bytes = 2 * sh.I * sh.H // 2 + 2 * sh.I * (sh.H // 128) * 4
+    w2_bytes = sh.H * sh.I // 2 + sh.H * (sh.I // 128) * 4
+    gate_up_bytes = touched * w13_bytes + sh.T * sh.H + sh.T * 4 + R * 4 + (sh.E + 1) * 4 + R * 2 * sh.I * 4
+    gate_up_flops = 2.0 * R * 2 * sh.I * sh.H
+    down_flops = 2.0 * R * sh.H * sh.I
+    t_gu = per_step["gemm_gate_up"] * 1e-3
+    t_dn = per_step["gemm_down"] * 1e-3
+    decode = args.config in (0, 1, 2)
+    khash = kernel_sources_hash()
+    kernel = "gg_stream" if decode else "gg_tiled"
+    traffic = load_traffic(os.path.join(ROOT, "profiles", f"{kernel}_config{args.config}_pmc.json"), khash)
+    if decode:
+        achieved = gate_up_bytes / t_gu / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic}
+    else:
+        achieved = gate_up_flops / t_gu / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / FP8_PEAK_TFLOPS, 4), "traffic": traffic}
+    roof["kernel"] = f"{kernel} (gate/up grouped GEMM)"
+    roof["algorithmic_bytes"] = int(gate_up_bytes)
+    roof["algorithmic_flops"] = gate_up_flops
+    roof["avg_launch_ms"] = round(per_step["gemm_gate_up"], 5)
+
+    both_weight_bytes = touched * (w13_bytes + w2_bytes)
+    gemms = {"weight_GBps": round(both_weight_bytes / (t_gu + t_dn) / 1e9, 1),
+             "tflops": round((gate_up_flops + down_flops) / (t_gu + t_dn) / 1e12, 2),
+             "hbm_frac_weights": round(both_weight_bytes / (t_gu + t_dn) / 1e9 / HBM_PEAK_GBS, 4),
+             "mfma_frac": round((gate_up_flops + down_flops) / (t_gu + t_dn) / 1e12 / FP8_PEAK_TFLOPS, 4),
+             "touched_experts": touched, "max_rows_per_expert": int(counts.max()),
+             "empty_experts": int((counts == 0).sum())}
+
+    cpu = None
+    if args.cpu_tokens > 0:
+        log(f"CPU oracle on {args.cpu_tokens} tokens ...")
+        cpu = cpu_baseline(wl, min(args.cpu_tokens, sh.T))
+
+    line = {
+        "metric": METRIC, "value": round(sh.T / (ms_step * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "fp8e4m3 x int4 (fp32 accumulate)",
+        "data": "synthetic (seeded; uniform INT4 words, lognormal scales, N(0,1) bf16 activations)",
+        "config": {"workload": sh.name, "tokens": sh.T, "hidden": sh.H, "intermediate": sh.I, "experts": sh.E,
+                   "top_k": sh.k, "group": 128},
+        "roofline": roof, "cpu_baseline": cpu, "gemms": gemms,
+        "step_ms": {k: round(v, 5) for k, v in per_step.items()},
+        "device": torch.cuda.get_device_name(0), "kernel_sources_hash": khash,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,187 @@
+/*
+ * w4a8_moe.h -- C ABI of the W4A8 mixture-of-experts routed-expert layer
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * The layer, as the "GLM-5.3-W4A8" model card (gpustack) describes its
+ * format in section 量化方式 (quantization method) and in its intro:
+ *   - routed-expert weights are symmetric INT4, one scale per group of 128
+ *     along the contraction axis K, stored compressed-tensors
+ *     "pack-quantized": uint4b8 nibbles (u = q + 8), eight per int32 word;
+ *   - activations are quantized to FP8 per token, dynamically, at run time;
+ *   - the grouped GEMM turns the INT4 weights into FP8 inside the kernel and
+ *     never dequantizes them to BF16.
+ * Each expert has three projections (gate, up, down: "从 755GB 到 395GB",
+ * Bitdeer AI blog, section 难点在于显存限制).  The layer's seven steps are the
+ * six calls below, chained in this order:
+ *   quant_act -> route -> permute -> grouped_gemm (gate/up) -> swiglu ->
+ *   grouped_gemm (down) -> unpermute.
+ *
+ * Conventions shared by every call
+ *   - Array pointers are DEVICE pointers; arrays are row-major, contiguous
+ *     unless a leading dimension is given.  "u8 E4M3" arrays hold OCP
+ *     E4M3FN codes (bias 7, max 448, no infinities).
+ *   - Packed weights: int32 [E][N][K/8]; the nibble for k sits at bits
+ *     4*(k mod 8) of word k/8 and holds q + 8 (q in -8..7).
+ *     Group scales: fp32 [E][N][K/128].
+ *   - The caller owns every buffer, including workspaces.  The library does
+ *     not allocate, free, or keep any pointer after a call returns.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Every call
+ *     only enqueues work on it and never synchronizes; ragged sizes (expert
+ *     row offsets) stay on the device, so a chained layer is capturable.
+ *   - Return value: W4A8_OK (0) or a w4a8_status code.  All argument checks
+ *     run on the host before anything is launched: an error means nothing
+ *     was enqueued.  w4a8_moe_last_error() gives the calling thread's last
+ *     error detail.  Sizes of zero tokens/rows are valid no-ops.
+ *   - Data preconditions that are NOT checked (undefined if violated):
+ *     expert ids in [0, E); offsets monotone with offsets[E] == M_total;
+ *     gather rows in range; no NaN/Inf in activations, logits or scales.
+ *   - Every result is deterministic: the same inputs give bit-identical
+ *     outputs from run to run.
+ */
+#ifndef W4A8_MOE_H
+#define W4A8_MOE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum w4a8_status {
+  W4A8_OK = 0,
+  W4A8_ERR_NULL = 1,      /* a required pointer is NULL                        */
+  W4A8_ERR_SHAPE = 2,     /* a size breaks the shape rules of the call         */
+  W4A8_ERR_ALIGN = 3,     /* a pointer or leading dimension is misaligned      */
+  W4A8_ERR_DEVICE = 4,    /* no HIP device, or the current device is not gfx950 */
+  W4A8_ERR_HIP = 5,       /* a HIP runtime call or a kernel launch failed      */
+  W4A8_ERR_WORKSPACE = 6  /* the workspace is smaller than required            */
+} w4a8_status;
+
+/* y_dtype values of w4a8_moe_unpermute */
+#define W4A8_Y_F32 0
+#define W4A8_Y_BF16 1
+
+/* algo values of w4a8_moe_grouped_gemm_algo */
+#define W4A8_GG_AUTO 0     /* choose from M_total / E                             */
+#define W4A8_GG_STREAM 1   /* weight-streaming kernel for few rows per expert     */
+#define W4A8_GG_TILED 2    /* LDS-tiled persistent kernel for many rows per expert */
+
+/*
+ * Step 1 -- per-token dynamic FP8 quantization of the activations.
+ * ("GLM-5.3-W4A8" card, section 量化方式 and the comparison table of section
+ * 与其他 4-bit 版本的差异: FP8, per token, dynamic.)
+ *   For each token t: amax = max_k |x[t,k]|, sx[t] = fl32(amax / 448)
+ *   (1.0 if the row is all zero), qx[t,k] = E4M3(fl32(x[t,k] / sx[t])),
+ *   rounded to nearest, ties to even, saturating at +-448, sign kept on 0.
+ *   x_bf16 : bf16 bit patterns [T][ld_x] (first H columns used); 16-byte
+ *            aligned, ld_x % 8 == 0, ld_x >= H.
+ *   qx     : u8 E4M3 [T][H], 8-byte aligned.     sx : fp32 [T].
+ *   Rules  : T >= 0, H > 0, H % 128 == 0.
+ */
+int w4a8_moe_quant_act(const uint16_t* x_bf16, int64_t T, int64_t H, int64_t ld_x,
+                       uint8_t* qx, float* sx, void* stream);
+
+/*
+ * Step 2 -- top-k softmax routing of each token to the routed experts.
+ * (256 routed experts per MoE layer: "从 755GB 到 395GB", section
+ * 我们量化了什么; the router itself stays BF16 per the "GLM-5.3-W4A8" card,
+ * section 量化方式, so its logits are an input here.)
+ *   ids[t, 0..k-1] = the k largest logits[t, :] in descending order, equal
+ *   logits ordered by the lower expert index; p = softmax(logits[t, :]);
+ *   w[t, j] = p[ids_j] / sum_j' p[ids_j'] if renormalize, else p[ids_j].
+ *   logits : fp32 [T][E].   ids : int32 [T][k].   w : fp32 [T][k].
+ *   Rules  : T >= 0, 1 <= k <= E <= 1024, T * k < 2^31.
+ */
+int w4a8_moe_route(const float* logits, int64_t T, int32_t E, int32_t k, int32_t renormalize,
+                   int32_t* ids, float* w, void* stream);
+
+/* Bytes of device workspace w4a8_moe_permute needs (>= 0), or -1 on bad sizes. */
+int64_t w4a8_moe_permute_workspace_bytes(int64_t T, int32_t k, int32_t E);
+
+/*
+ * Step 3 -- group the T*k routed rows by expert (a stable counting sort).
+ * (The expert-parallel dispatch of the pages' engines, "GLM-5.3-W4A8" card,
+ * sections 性能 and 部署, done here inside one GPU.)
+ *   f = t*k + j indexes ids.  counts[e] = #{f : ids[f] == e};
+ *   offsets = exclusive prefix sum of counts (E + 1 entries, offsets[E] = T*k);
+ *   rows of expert e are offsets[e] .. offsets[e+1]-1, ordered by f;
+ *   row_token[p] = token of routed row p;  inv_pos[f] = row of index f.
+ *   ids : int32 [T*k].  offsets : int32 [E+1].  row_token, inv_pos : int32 [T*k].
+ *   workspace : device memory of w4a8_moe_permute_workspace_bytes(T, k, E)
+ *   bytes, 4-byte aligned (contents need no initialisation).
+ *   Rules : T >= 0, 1 <= k <= E <= 1024, T * k < 2^31.  T == 0 still writes
+ *   offsets (all zero).
+ */
+int w4a8_moe_permute(const int32_t* ids, int64_t T, int32_t k, int32_t E,
+                     int32_t* offsets, int32_t* row_token, int32_t* inv_pos,
+                     void* workspace, int64_t workspace_bytes, void* stream);
+
+/*
+ * Steps 4 and 6 -- grouped W4A8 GEMM over the experts' row ranges.
+ * ("GLM-5.3-W4A8" card, section 量化方式: INT4 weights become FP8 inside
+ * the kernel, FP8 matrix multiply, no BF16 dequantization.)
+ *   For expert e and each row p in [offsets[e], offsets[e+1]), with
+ *   r = a_rows ? a_rows[p] : p:
+ *     out[p, n] = a_scale[r] * sum_g w_scale[e, n, g] *
+ *                 sum_{k in group g} E4M3(a[r, k]) * q[e, n, k]
+ *   a        : u8 E4M3 [*][K], 16-byte aligned (source rows; gathered by
+ *              a_rows when it is not NULL).   a_scale : fp32 [*].
+ *   a_rows   : int32 [M_total] or NULL.
+ *   offsets  : int32 [E+1] on the device, offsets[E] == M_total.
+ *   w_packed : int32 [E][N][K/8], 16-byte aligned.   w_scale : fp32 [E][N][K/128].
+ *   out      : fp32 [M_total][N], 16-byte aligned.
+ *   Rules    : M_total >= 0, 1 <= E <= 1024, N > 0, N % 64 == 0, K > 0,
+ *              K % 128 == 0.
+ *   Accumulation is fp32 per 128-wide group, then the group scale is
+ *   applied in fp32; the result matches the exact sum to ~1e-6 relative.
+ */
+int w4a8_moe_grouped_gemm(const uint8_t* a, const float* a_scale, const int32_t* a_rows,
+                          int64_t M_total, const int32_t* offsets, int32_t E,
+                          const int32_t* w_packed, const float* w_scale,
+                          int64_t N, int64_t K, float* out, void* stream);
+
+/* As w4a8_moe_grouped_gemm, with the kernel chosen by `algo` (W4A8_GG_*).
+ * Every algo computes the same result; the choice only affects speed. */
+int w4a8_moe_grouped_gemm_algo(const uint8_t* a, const float* a_scale, const int32_t* a_rows,
+                               int64_t M_total, const int32_t* offsets, int32_t E,
+                               const int32_t* w_packed, const float* w_scale,
+                               int64_t N, int64_t K, float* out, int32_t algo, void* stream);
+
+/*
+ * Step 5 -- SwiGLU of the gate/up output and per-row FP8 re-quantization.
+ * (Three projections per expert: Bitdeer AI blog, section 难点在于显存限制;
+ * per-token FP8 activations: "GLM-5.3-W4A8" card, section 量化方式.)
+ *   gate = h[p, 0:I], up = h[p, I:2I]; act = silu(gate) * up in fp32,
+ *   silu(z) = z / (1 + exp(-z)); then the step-1 rule per routed row:
+ *   sa[p] = fl32(amax / 448), qa[p, i] = E4M3(fl32(act / sa[p])).
+ *   h : fp32 [M][2I], 16-byte aligned.  qa : u8 E4M3 [M][I], 4-byte aligned.
+ *   sa : fp32 [M].   Rules : M >= 0, I > 0, I % 128 == 0.
+ */
+int w4a8_moe_swiglu(const float* h, int64_t M, int64_t I, uint8_t* qa, float* sa, void* stream);
+
+/*
+ * Step 7 -- routing-weighted combine of the k expert outputs of each token.
+ *   y[t, :] = sum_{j = 0..k-1} w[t, j] * o[inv_pos[t*k + j], :]  (fp32, j ascending)
+ *   o : fp32 [T*k][H], 16-byte aligned.  inv_pos : int32 [T*k].  w : fp32 [T][k].
+ *   y : [T][H], fp32 (y_dtype W4A8_Y_F32, 16-byte aligned) or bf16 bit
+ *       patterns rounded to nearest even (W4A8_Y_BF16, 8-byte aligned).
+ *   Rules : T >= 0, k >= 1, H > 0, H % 128 == 0, T * k < 2^31.
+ */
+int w4a8_moe_unpermute(const float* o, const int32_t* inv_pos, const float* w,
+                       int64_t T, int32_t k, int64_t H, void* y, int32_t y_dtype, void* stream);
+
+/* Static name of a status code ("W4A8_OK", ...). */
+const char* w4a8_moe_status_string(int status);
+
+/* Detail of the calling thread's last error ("" if none).  Valid until the
+ * thread's next call into the library. */
+const char* w4a8_moe_last_error(void);
+
+/* 1 if the current HIP device is a gfx950, 0 otherwise (including no device). */
+int w4a8_moe_device_supported(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* W4A8_MOE_H */

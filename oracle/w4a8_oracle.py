@@ -44,6 +44,8 @@ end of each step, which is where the GPU path also materialises a result.
 """
 from __future__ import annotations
 
+import sys
+
 import numpy as np
 
 FP8_MAX = 448.0          # largest finite E4M3FN magnitude
@@ -138,19 +140,29 @@ def int4_pack(q) -> np.ndarray:
 
 
 def int4_unpack(words) -> np.ndarray:
-    """Inverse of int4_pack: int32 words [..., K/8] -> int8 q [..., K]."""
-    w = np.asarray(words, dtype=np.int32).view(np.uint32).astype(np.uint64)
-    shifts = (4 * np.arange(NIBBLES_PER_WORD, dtype=np.uint64))
-    u = (w[..., None] >> shifts) & np.uint64(0xF)
-    q = u.astype(np.int16) - UINT4B8_BIAS
-    return q.reshape(*w.shape[:-1], w.shape[-1] * NIBBLES_PER_WORD).astype(np.int8)
+    """Inverse of int4_pack: int32 words [..., K/8] -> int8 q [..., K].
+
+    Read byte by byte: byte j of word c (little-endian) holds k = 8c + 2j in
+    its low nibble and k = 8c + 2j + 1 in its high nibble.
+    """
+    if sys.byteorder != "little":
+        raise RuntimeError("the oracle reads packed words as little-endian bytes")
+    w = np.ascontiguousarray(np.asarray(words, dtype=np.int32))
+    b = w.view(np.uint8).reshape(*w.shape[:-1], w.shape[-1] * 4)
+    q = np.empty((*w.shape[:-1], w.shape[-1] * NIBBLES_PER_WORD), dtype=np.int8)
+    q[..., 0::2] = b & 0xF
+    q[..., 1::2] = b >> 4
+    q -= UINT4B8_BIAS
+    return q
 
 
 def dequant_weights(words, scales) -> np.ndarray:
     """fp64 weights q[n, k] * s[n, k // 128] of one expert (exact in fp64)."""
-    q = int4_unpack(words).astype(np.float64)
-    s = np.asarray(scales, dtype=np.float32).astype(np.float64)
-    return q * np.repeat(s, GROUP, axis=-1)
+    q = int4_unpack(words)
+    K = q.shape[-1]
+    W = q.astype(np.float64).reshape(*q.shape[:-1], K // GROUP, GROUP)
+    W *= np.asarray(scales, dtype=np.float32).astype(np.float64)[..., None]
+    return W.reshape(*q.shape[:-1], K)
 
 
 # --------------------------------------------------------------------------

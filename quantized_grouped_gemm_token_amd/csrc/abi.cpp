@@ -1,0 +1,216 @@
+// C ABI of the W4A8 MoE layer: host-side argument checks, then kernel
+// launches on the caller's stream.  Every check runs before anything is
+// enqueued, so an error status means no work was launched.
+#include "w4a8_moe.h"
+
+#include <atomic>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "kernels.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int status, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return status;
+}
+
+int ok() {
+  g_last_error.clear();
+  return W4A8_OK;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_device_ok[kMaxDevices];   // 0 unknown, 1 gfx950, 2 other
+
+// 1 if the current device is a gfx950; fills the error detail otherwise.
+int check_device() {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(W4A8_ERR_DEVICE, "no usable HIP device (%s)", hipGetErrorString(e));
+  }
+  if (dev >= 0 && dev < kMaxDevices) {
+    const int c = g_device_ok[dev].load(std::memory_order_relaxed);
+    if (c == 1) return W4A8_OK;
+  }
+  hipDeviceProp_t prop;
+  e = hipGetDeviceProperties(&prop, dev);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(W4A8_ERR_DEVICE, "hipGetDeviceProperties(%d) failed (%s)", dev, hipGetErrorString(e));
+  }
+  const bool good = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+  if (dev >= 0 && dev < kMaxDevices) g_device_ok[dev].store(good ? 1 : 2, std::memory_order_relaxed);
+  if (!good)
+    return fail(W4A8_ERR_DEVICE, "device %d is %s; this library runs on gfx950 (MI355X) only", dev,
+                prop.gcnArchName);
+  return W4A8_OK;
+}
+
+int launched(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(W4A8_ERR_HIP, "%s: launch failed (%s)", what, hipGetErrorString(e));
+  return ok();
+}
+
+hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+constexpr int64_t kMaxRows = (int64_t)1 << 31;   // row indices are int32
+
+}  // namespace
+
+extern "C" {
+
+const char* w4a8_moe_status_string(int status) {
+  switch (status) {
+    case W4A8_OK: return "W4A8_OK";
+    case W4A8_ERR_NULL: return "W4A8_ERR_NULL";
+    case W4A8_ERR_SHAPE: return "W4A8_ERR_SHAPE";
+    case W4A8_ERR_ALIGN: return "W4A8_ERR_ALIGN";
+    case W4A8_ERR_DEVICE: return "W4A8_ERR_DEVICE";
+    case W4A8_ERR_HIP: return "W4A8_ERR_HIP";
+    case W4A8_ERR_WORKSPACE: return "W4A8_ERR_WORKSPACE";
+    default: return "W4A8_ERR_UNKNOWN";
+  }
+}
+
+const char* w4a8_moe_last_error(void) { return g_last_error.c_str(); }
+
+int w4a8_moe_device_supported(void) { return check_device() == W4A8_OK ? 1 : 0; }
+
+int w4a8_moe_quant_act(const uint16_t* x_bf16, int64_t T, int64_t H, int64_t ld_x, uint8_t* qx, float* sx,
+                       void* stream) {
+  if (T < 0 || T >= kMaxRows) return fail(W4A8_ERR_SHAPE, "quant_act: T=%lld out of range", (long long)T);
+  if (H <= 0 || H % 128) return fail(W4A8_ERR_SHAPE, "quant_act: H=%lld must be a positive multiple of 128",
+                                     (long long)H);
+  if (ld_x < H || ld_x % 8)
+    return fail(W4A8_ERR_SHAPE, "quant_act: ld_x=%lld must be >= H and a multiple of 8", (long long)ld_x);
+  if (T == 0) return ok();
+  if (!x_bf16 || !qx || !sx) return fail(W4A8_ERR_NULL, "quant_act: null pointer");
+  if (!aligned(x_bf16, 16) || !aligned(qx, 8) || !aligned(sx, 4))
+    return fail(W4A8_ERR_ALIGN, "quant_act: x must be 16-byte, qx 8-byte, sx 4-byte aligned");
+  if (int st = check_device()) return st;
+  (void)hipGetLastError();
+  return launched(w4a8::launch_quant_act(x_bf16, T, H, ld_x, qx, sx, as_stream(stream)), "quant_act");
+}
+
+int w4a8_moe_route(const float* logits, int64_t T, int32_t E, int32_t k, int32_t renormalize, int32_t* ids,
+                   float* w, void* stream) {
+  if (T < 0) return fail(W4A8_ERR_SHAPE, "route: T=%lld < 0", (long long)T);
+  if (E < 1 || E > 1024 || k < 1 || k > E)
+    return fail(W4A8_ERR_SHAPE, "route: need 1 <= k <= E <= 1024 (k=%d, E=%d)", k, E);
+  if (T * (int64_t)k >= kMaxRows) return fail(W4A8_ERR_SHAPE, "route: T*k must be < 2^31");
+  if (T == 0) return ok();
+  if (!logits || !ids || !w) return fail(W4A8_ERR_NULL, "route: null pointer");
+  if (!aligned(logits, 4) || !aligned(ids, 4) || !aligned(w, 4))
+    return fail(W4A8_ERR_ALIGN, "route: arrays must be 4-byte aligned");
+  if (int st = check_device()) return st;
+  (void)hipGetLastError();
+  return launched(w4a8::launch_route(logits, T, E, k, renormalize ? 1 : 0, ids, w, as_stream(stream)), "route");
+}
+
+int64_t w4a8_moe_permute_workspace_bytes(int64_t T, int32_t k, int32_t E) {
+  if (T < 0 || E < 1 || E > 1024 || k < 1 || k > E || T * (int64_t)k >= kMaxRows) return -1;
+  return w4a8::permute_workspace_bytes(T * (int64_t)k, E);
+}
+
+int w4a8_moe_permute(const int32_t* ids, int64_t T, int32_t k, int32_t E, int32_t* offsets, int32_t* row_token,
+                     int32_t* inv_pos, void* workspace, int64_t workspace_bytes, void* stream) {
+  if (T < 0) return fail(W4A8_ERR_SHAPE, "permute: T=%lld < 0", (long long)T);
+  if (E < 1 || E > 1024 || k < 1 || k > E)
+    return fail(W4A8_ERR_SHAPE, "permute: need 1 <= k <= E <= 1024 (k=%d, E=%d)", k, E);
+  if (T * (int64_t)k >= kMaxRows) return fail(W4A8_ERR_SHAPE, "permute: T*k must be < 2^31");
+  if (!offsets || !workspace) return fail(W4A8_ERR_NULL, "permute: null offsets or workspace");
+  if (T > 0 && (!ids || !row_token || !inv_pos)) return fail(W4A8_ERR_NULL, "permute: null pointer");
+  const int64_t need = w4a8::permute_workspace_bytes(T * (int64_t)k, E);
+  if (workspace_bytes < need)
+    return fail(W4A8_ERR_WORKSPACE, "permute: workspace of %lld bytes, need %lld", (long long)workspace_bytes,
+                (long long)need);
+  if (!aligned(ids, 4) || !aligned(offsets, 4) || !aligned(row_token, 4) || !aligned(inv_pos, 4) ||
+      !aligned(workspace, 4))
+    return fail(W4A8_ERR_ALIGN, "permute: arrays must be 4-byte aligned");
+  if (int st = check_device()) return st;
+  (void)hipGetLastError();
+  return launched(w4a8::launch_permute(ids, T * (int64_t)k, k, E, offsets, row_token, inv_pos,
+                                       static_cast<int32_t*>(workspace), as_stream(stream)),
+                  "permute");
+}
+
+int w4a8_moe_grouped_gemm_algo(const uint8_t* a, const float* a_scale, const int32_t* a_rows, int64_t M_total,
+                               const int32_t* offsets, int32_t E, const int32_t* w_packed, const float* w_scale,
+                               int64_t N, int64_t K, float* out, int32_t algo, void* stream) {
+  if (M_total < 0 || M_total >= kMaxRows)
+    return fail(W4A8_ERR_SHAPE, "grouped_gemm: M_total=%lld out of range", (long long)M_total);
+  if (E < 1 || E > 1024) return fail(W4A8_ERR_SHAPE, "grouped_gemm: E=%d must be in [1, 1024]", E);
+  if (N <= 0 || N % 64) return fail(W4A8_ERR_SHAPE, "grouped_gemm: N=%lld must be a positive multiple of 64",
+                                    (long long)N);
+  if (K <= 0 || K % 128) return fail(W4A8_ERR_SHAPE, "grouped_gemm: K=%lld must be a positive multiple of 128",
+                                     (long long)K);
+  if (algo < W4A8_GG_AUTO || algo > W4A8_GG_TILED)
+    return fail(W4A8_ERR_SHAPE, "grouped_gemm: unknown algo %d", algo);
+  if (M_total == 0) return ok();
+  if (!a || !a_scale || !offsets || !w_packed || !w_scale || !out)
+    return fail(W4A8_ERR_NULL, "grouped_gemm: null pointer");
+  if (!aligned(a, 16) || !aligned(w_packed, 16) || !aligned(out, 16) || !aligned(a_scale, 4) ||
+      !aligned(w_scale, 4) || !aligned(offsets, 4) || !aligned(a_rows, 4))
+    return fail(W4A8_ERR_ALIGN, "grouped_gemm: a, w_packed and out must be 16-byte aligned, the rest 4-byte");
+  if (int st = check_device()) return st;
+  const w4a8::GemmArgs g{a, a_scale, a_rows, M_total, offsets, E, w_packed, w_scale, N, K, out};
+  if (algo == W4A8_GG_AUTO) algo = (M_total <= 32 * (int64_t)E) ? W4A8_GG_STREAM : W4A8_GG_TILED;
+  (void)hipGetLastError();
+  if (algo == W4A8_GG_STREAM) return launched(w4a8::launch_gg_stream(g, as_stream(stream)), "grouped_gemm");
+  return launched(w4a8::launch_gg_tiled(g, as_stream(stream)), "grouped_gemm");
+}
+
+int w4a8_moe_grouped_gemm(const uint8_t* a, const float* a_scale, const int32_t* a_rows, int64_t M_total,
+                          const int32_t* offsets, int32_t E, const int32_t* w_packed, const float* w_scale,
+                          int64_t N, int64_t K, float* out, void* stream) {
+  return w4a8_moe_grouped_gemm_algo(a, a_scale, a_rows, M_total, offsets, E, w_packed, w_scale, N, K, out,
+                                    W4A8_GG_AUTO, stream);
+}
+
+int w4a8_moe_swiglu(const float* h, int64_t M, int64_t I, uint8_t* qa, float* sa, void* stream) {
+  if (M < 0 || M >= kMaxRows) return fail(W4A8_ERR_SHAPE, "swiglu: M=%lld out of range", (long long)M);
+  if (I <= 0 || I % 128) return fail(W4A8_ERR_SHAPE, "swiglu: I=%lld must be a positive multiple of 128",
+                                     (long long)I);
+  if (M == 0) return ok();
+  if (!h || !qa || !sa) return fail(W4A8_ERR_NULL, "swiglu: null pointer");
+  if (!aligned(h, 16) || !aligned(qa, 4) || !aligned(sa, 4))
+    return fail(W4A8_ERR_ALIGN, "swiglu: h must be 16-byte, qa and sa 4-byte aligned");
+  if (int st = check_device()) return st;
+  (void)hipGetLastError();
+  return launched(w4a8::launch_swiglu(h, M, I, qa, sa, as_stream(stream)), "swiglu");
+}
+
+int w4a8_moe_unpermute(const float* o, const int32_t* inv_pos, const float* w, int64_t T, int32_t k, int64_t H,
+                       void* y, int32_t y_dtype, void* stream) {
+  if (T < 0 || T >= kMaxRows) return fail(W4A8_ERR_SHAPE, "unpermute: T=%lld out of range", (long long)T);
+  if (k < 1 || T * (int64_t)k >= kMaxRows) return fail(W4A8_ERR_SHAPE, "unpermute: bad k=%d", k);
+  if (H <= 0 || H % 128) return fail(W4A8_ERR_SHAPE, "unpermute: H=%lld must be a positive multiple of 128",
+                                     (long long)H);
+  if (y_dtype != W4A8_Y_F32 && y_dtype != W4A8_Y_BF16)
+    return fail(W4A8_ERR_SHAPE, "unpermute: y_dtype=%d must be W4A8_Y_F32 or W4A8_Y_BF16", y_dtype);
+  if (T == 0) return ok();
+  if (!o || !inv_pos || !w || !y) return fail(W4A8_ERR_NULL, "unpermute: null pointer");
+  if (!aligned(o, 16) || !aligned(inv_pos, 4) || !aligned(w, 4) || !aligned(y, y_dtype == W4A8_Y_F32 ? 16 : 8))
+    return fail(W4A8_ERR_ALIGN, "unpermute: o and f32 y must be 16-byte, bf16 y 8-byte aligned");
+  if (int st = check_device()) return st;
+  (void)hipGetLastError();
+  return launched(w4a8::launch_unpermute(o, inv_pos, w, T, k, H, y, y_dtype == W4A8_Y_BF16, as_stream(stream)),
+                  "unpermute");
+}
+
+}  // extern "C"

@@ -1,0 +1,62 @@
+// Pieces shared by the grouped W4A8 GEMM kernels.
+//
+// The GEMM never dequantizes the INT4 weights to BF16 ("GLM-5.3-W4A8" card,
+// section 量化方式: the INT4 weights become FP8 inside the kernel and feed the
+// FP8 matrix cores).  On gfx950 that FP8 conversion is free:
+//
+//   * a stored nibble u = q + 8 (0..15), zero-extended to a byte and read as
+//     E4M3, is exactly u * 2^-9: E4M3 spaces its subnormals and its first
+//     normal binade evenly by 2^-9, so the bytes 0x00..0x0F are linear;
+//   * so  sum_k a_k q_k = 2^9 * sum_k a_k (u_k 2^-9)  -  8 * sum_k a_k.
+//     The second term is one more MFMA of the same A tile against a constant
+//     B of -2^-6 (E4M3 0x88), used as the accumulator input C of the real
+//     MFMA:  D = A x U(2^-9) + A x (-2^-6)  = 2^-9 * A x Q   (every product
+//     is exact, the sums are fp32);
+//   * then acc += s[n, g] * D per 128-wide group (one fp32 FMA per output per
+//     group), and the 2^9 goes into the epilogue with the token scale.
+//
+// The only work per weight is splitting the nibbles of a word into bytes
+// (two ANDs, a shift and two byte permutes per 8 weights).
+#pragma once
+
+#include "common.hpp"
+
+namespace w4a8 {
+
+typedef int v8i __attribute__((ext_vector_type(8)));     // 32 E4M3 bytes
+typedef float v4f __attribute__((ext_vector_type(4)));   // 16x16 fp32 tile, 4 per lane
+
+constexpr int kBiasWord = (int)0x88888888u;                // four E4M3 -2^-6
+constexpr float kUnitScale = 512.0f;                        // 2^9
+
+// v_mfma_f32_16x16x128_f8f6f4 with both operands E4M3 and no block scaling.
+// Lane l supplies A row (l % 16) and B column (l % 16), K elements
+// 32 * (l / 16) .. +32 of the 128 (the same K map for both operands);
+// D lane l holds column l % 16, rows 4 * (l / 16) .. +3.
+__device__ __forceinline__ v4f mfma16x16x128(v8i a, v8i b, v4f c) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
+// 32 packed nibbles (K order: word c holds k = 8c .. 8c+7, nibble j at bits
+// 4j) -> 32 bytes u_k in K order, each read by the MFMA as u_k * 2^-9.
+__device__ __forceinline__ v8i nibbles_to_fp8(i32x4 w) {
+  const uint32_t ws[4] = {(uint32_t)w[0], (uint32_t)w[1], (uint32_t)w[2], (uint32_t)w[3]};
+  v8i r;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const uint32_t lo = ws[c] & 0x0f0f0f0fu;           // u0 u2 u4 u6
+    const uint32_t hi = (ws[c] >> 4) & 0x0f0f0f0fu;    // u1 u3 u5 u7
+    r[2 * c] = (int)__builtin_amdgcn_perm(hi, lo, 0x05010400u);       // u0 u1 u2 u3
+    r[2 * c + 1] = (int)__builtin_amdgcn_perm(hi, lo, 0x07030602u);   // u4 u5 u6 u7
+  }
+  return r;
+}
+
+__device__ __forceinline__ v8i bias_operand() {
+  v8i b;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) b[i] = kBiasWord;
+  return b;
+}
+
+}  // namespace w4a8

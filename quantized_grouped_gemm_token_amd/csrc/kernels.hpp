@@ -1,0 +1,37 @@
+// Internal launchers of the W4A8 MoE kernels (called by the C ABI after it
+// has validated every argument on the host).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace w4a8 {
+
+struct GemmArgs {
+  const uint8_t* a;
+  const float* a_scale;
+  const int32_t* a_rows;
+  int64_t M_total;
+  const int32_t* offsets;
+  int E;
+  const int32_t* w_packed;
+  const float* w_scale;
+  int64_t N;
+  int64_t K;
+  float* out;
+};
+
+hipError_t launch_quant_act(const uint16_t* x, int64_t T, int64_t H, int64_t ld, uint8_t* q, float* s,
+                            hipStream_t stream);
+hipError_t launch_route(const float* logits, int64_t T, int E, int k, int renormalize, int32_t* ids, float* w,
+                        hipStream_t stream);
+int64_t permute_workspace_bytes(int64_t R, int E);
+hipError_t launch_permute(const int32_t* ids, int64_t R, int k, int E, int32_t* offsets, int32_t* row_token,
+                          int32_t* inv_pos, int32_t* counts, hipStream_t stream);
+hipError_t launch_gg_stream(const GemmArgs& g, hipStream_t stream);
+hipError_t launch_gg_tiled(const GemmArgs& g, hipStream_t stream);
+hipError_t launch_swiglu(const float* h, int64_t M, int64_t I, uint8_t* q, float* s, hipStream_t stream);
+hipError_t launch_unpermute(const float* o, const int32_t* inv_pos, const float* w, int64_t T, int k, int64_t H,
+                            void* y, int bf16_out, hipStream_t stream);
+
+}  // namespace w4a8

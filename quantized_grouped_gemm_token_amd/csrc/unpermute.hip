@@ -1,0 +1,51 @@
+// Layer step 7: routing-weighted combine of each token's k expert outputs.
+//
+// y[t, :] = sum_j w[t, j] * o[inv_pos[t*k + j], :], fp32, j ascending (a
+// fixed order, so the result is deterministic).  A routed index that was
+// not routed (inv_pos < 0) contributes nothing.
+//
+// Grid: (T tokens, H / 1024 column chunks); each thread owns 4 columns.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace w4a8 {
+
+template <bool BF16_OUT>
+__global__ __launch_bounds__(256) void unpermute_kernel(const float* __restrict__ o,
+                                                        const int32_t* __restrict__ inv_pos,
+                                                        const float* __restrict__ w, int k, int64_t H,
+                                                        void* __restrict__ y) {
+  const int64_t t = blockIdx.x;
+  const int64_t col = ((int64_t)blockIdx.y * 256 + threadIdx.x) * 4;
+  if (col >= H) return;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int j = 0; j < k; ++j) {
+    const int p = inv_pos[t * k + j];
+    if (p < 0) continue;
+    const float wj = w[t * k + j];
+    const f32x4 v = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(o + (int64_t)p * H + col));
+    acc.x = fmaf(wj, v[0], acc.x);
+    acc.y = fmaf(wj, v[1], acc.y);
+    acc.z = fmaf(wj, v[2], acc.z);
+    acc.w = fmaf(wj, v[3], acc.w);
+  }
+  if (BF16_OUT) {
+    const uint32_t lo = f32_to_bf16(acc.x) | (f32_to_bf16(acc.y) << 16);
+    const uint32_t hi = f32_to_bf16(acc.z) | (f32_to_bf16(acc.w) << 16);
+    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(y) + t * H + col) = make_uint2(lo, hi);
+  } else {
+    *reinterpret_cast<float4*>(static_cast<float*>(y) + t * H + col) = acc;
+  }
+}
+
+hipError_t launch_unpermute(const float* o, const int32_t* inv_pos, const float* w, int64_t T, int k, int64_t H,
+                            void* y, int bf16_out, hipStream_t stream) {
+  const dim3 grid((unsigned)T, (unsigned)((H + 1023) / 1024));
+  if (bf16_out)
+    hipLaunchKernelGGL(unpermute_kernel<true>, grid, dim3(256), 0, stream, o, inv_pos, w, k, H, y);
+  else
+    hipLaunchKernelGGL(unpermute_kernel<false>, grid, dim3(256), 0, stream, o, inv_pos, w, k, H, y);
+  return hipGetLastError();
+}
+
+}  // namespace w4a8

@@ -1,0 +1,81 @@
+"""The W4A8 MoE routed-expert layer: the seven library steps chained on one stream.
+
+    quant_act -> route -> permute -> grouped_gemm(W13) -> swiglu ->
+    grouped_gemm(W2) -> unpermute
+
+Expert weights stay resident on the GPU in the packed format (int32
+[E][N][K/8] words of uint4b8 nibbles and fp32 [E][N][K/128] group scales).
+Intermediate buffers are allocated once per token count and reused, so a
+forward pass enqueues kernels only: no allocation, no host synchronisation.
+"""
+from __future__ import annotations
+
+import torch
+
+from . import ops
+
+
+class W4A8MoE:
+    def __init__(self, w13: torch.Tensor, s13: torch.Tensor, w2: torch.Tensor, s2: torch.Tensor, k: int,
+                 renormalize: bool = True):
+        E, N13, KW13 = w13.shape
+        E2, H, KW2 = w2.shape
+        if E2 != E or N13 % 2 or KW13 * 8 != H or KW2 * 8 * 2 != N13:
+            raise ValueError("w13 must be [E, 2I, H/8] and w2 [E, H, I/8]")
+        self.w13, self.s13, self.w2, self.s2 = w13, s13, w2, s2
+        self.E, self.H, self.I, self.k = E, H, N13 // 2, k
+        self.renormalize = renormalize
+        self._bufs: dict[int, dict] = {}
+
+    def buffers(self, T: int) -> dict:
+        """Intermediate buffers for T tokens (allocated on first use)."""
+        if T not in self._bufs:
+            dev = self.w13.device
+            R = T * self.k
+            nbytes = ops.w4a8_moe_permute_workspace_bytes(T, self.k, self.E)
+            e = lambda shape, dt: torch.empty(shape, dtype=dt, device=dev)  # noqa: E731
+            self._bufs[T] = dict(
+                qx=e((T, self.H), torch.uint8), sx=e((T,), torch.float32),
+                ids=e((T, self.k), torch.int32), w=e((T, self.k), torch.float32),
+                offsets=e((self.E + 1,), torch.int32), row_token=e((R,), torch.int32),
+                inv_pos=e((R,), torch.int32), workspace=e((max(nbytes, 4),), torch.uint8),
+                h=e((R, 2 * self.I), torch.float32), qa=e((R, self.I), torch.uint8), sa=e((R,), torch.float32),
+                o=e((R, self.H), torch.float32),
+            )
+        return self._bufs[T]
+
+    STEPS = ("quant_act", "route", "permute", "gemm_gate_up", "swiglu", "gemm_down", "unpermute")
+
+    def forward(self, x: torch.Tensor, logits: torch.Tensor, y: torch.Tensor | None = None,
+                y_dtype: torch.dtype = torch.float32, algo: int = ops.W4A8_GG_AUTO,
+                events: dict | None = None) -> torch.Tensor:
+        """x bf16 [T, H], router logits fp32 [T, E] -> y [T, H].
+
+        events, if given, maps step names (STEPS) to (start, end) CUDA events
+        that are recorded on the current stream around each step.
+        """
+        T = x.shape[0]
+        b = self.buffers(T)
+        R = T * self.k
+
+        def step(name, fn, *args):
+            ev = events.get(name) if events else None
+            if ev:
+                ev[0].record()
+            r = fn(*args)
+            if ev:
+                ev[1].record()
+            return r
+
+        step("quant_act", ops.w4a8_moe_quant_act, x, b["qx"], b["sx"])
+        step("route", ops.w4a8_moe_route, logits, self.k, self.renormalize, b["ids"], b["w"])
+        step("permute", ops.w4a8_moe_permute, b["ids"], self.E, b["offsets"], b["row_token"], b["inv_pos"],
+             b["workspace"])
+        step("gemm_gate_up", ops.w4a8_moe_grouped_gemm, b["qx"], b["sx"], b["row_token"], b["offsets"], self.w13,
+             self.s13, R, b["h"], algo)
+        step("swiglu", ops.w4a8_moe_swiglu, b["h"], b["qa"], b["sa"])
+        step("gemm_down", ops.w4a8_moe_grouped_gemm, b["qa"], b["sa"], None, b["offsets"], self.w2, self.s2, R,
+             b["o"], algo)
+        return step("unpermute", ops.w4a8_moe_unpermute, b["o"], b["inv_pos"], b["w"], y, y_dtype)
+
+    __call__ = forward

@@ -1,0 +1,243 @@
+"""Python binding of the W4A8 MoE C ABI (include/w4a8_moe.h).
+
+Argument marshalling only: each function checks dtypes, devices, shapes and
+contiguity of torch tensors, allocates outputs the caller did not pass, and
+calls the library function of the same name on torch's current stream.
+Every step of the layer runs in the library's HIP kernels.  The library must
+have been built (``quantized_grouped_gemm_token_amd.build``); without it
+every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libw4a8moe.so")
+
+W4A8_Y_F32 = 0
+W4A8_Y_BF16 = 1
+W4A8_GG_AUTO = 0
+W4A8_GG_STREAM = 1
+W4A8_GG_TILED = 2
+
+_lib = None
+
+_c_p = ctypes.c_void_p
+_i64 = ctypes.c_int64
+_i32 = ctypes.c_int32
+
+_SIGNATURES = {
+    "w4a8_moe_quant_act": (ctypes.c_int, [_c_p, _i64, _i64, _i64, _c_p, _c_p, _c_p]),
+    "w4a8_moe_route": (ctypes.c_int, [_c_p, _i64, _i32, _i32, _i32, _c_p, _c_p, _c_p]),
+    "w4a8_moe_permute_workspace_bytes": (ctypes.c_int64, [_i64, _i32, _i32]),
+    "w4a8_moe_permute": (ctypes.c_int, [_c_p, _i64, _i32, _i32, _c_p, _c_p, _c_p, _c_p, _i64, _c_p]),
+    "w4a8_moe_grouped_gemm": (ctypes.c_int, [_c_p, _c_p, _c_p, _i64, _c_p, _i32, _c_p, _c_p, _i64, _i64, _c_p,
+                                             _c_p]),
+    "w4a8_moe_grouped_gemm_algo": (ctypes.c_int, [_c_p, _c_p, _c_p, _i64, _c_p, _i32, _c_p, _c_p, _i64, _i64,
+                                                  _c_p, _i32, _c_p]),
+    "w4a8_moe_swiglu": (ctypes.c_int, [_c_p, _i64, _i64, _c_p, _c_p, _c_p]),
+    "w4a8_moe_unpermute": (ctypes.c_int, [_c_p, _c_p, _c_p, _i64, _i32, _i64, _c_p, _i32, _c_p]),
+    "w4a8_moe_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "w4a8_moe_last_error": (ctypes.c_char_p, []),
+    "w4a8_moe_device_supported": (ctypes.c_int, []),
+}
+
+
+class W4A8Error(RuntimeError):
+    """A nonzero status from the library."""
+
+    def __init__(self, func: str, status: int, detail: str):
+        super().__init__(f"{func}: {detail} [{status_string(status)}]")
+        self.status = status
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m quantized_grouped_gemm_token_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGNATURES.items():
+            f = getattr(L, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = L
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().w4a8_moe_status_string(status).decode()
+
+
+def last_error() -> str:
+    return lib().w4a8_moe_last_error().decode()
+
+
+def _check(func: str, status: int) -> None:
+    if status != 0:
+        raise W4A8Error(func, status, last_error())
+
+
+def w4a8_moe_device_supported() -> bool:
+    return bool(lib().w4a8_moe_device_supported())
+
+
+# ---------------------------------------------------------------- helpers
+def _p(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(dev: torch.device):
+    return torch.cuda.current_stream(dev).cuda_stream
+
+
+def _need(t: torch.Tensor, name: str, dtype, ndim: int, dev: torch.device | None = None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got shape {tuple(t.shape)}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if dev is not None and t.device != dev:
+        raise ValueError(f"{name} is on {t.device}, expected {dev}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+# ------------------------------------------------------------------ calls
+def w4a8_moe_quant_act(x: torch.Tensor, qx: torch.Tensor | None = None, sx: torch.Tensor | None = None):
+    """bf16 [T, H] -> (E4M3 codes uint8 [T, H], per-token scales fp32 [T])."""
+    _need(x, "x", torch.bfloat16, 2)
+    T, H = x.shape
+    dev = x.device
+    qx = torch.empty((T, H), dtype=torch.uint8, device=dev) if qx is None else qx
+    sx = torch.empty((T,), dtype=torch.float32, device=dev) if sx is None else sx
+    _need(qx, "qx", torch.uint8, 2, dev)
+    _need(sx, "sx", torch.float32, 1, dev)
+    if tuple(qx.shape) != (T, H) or tuple(sx.shape) != (T,):
+        raise ValueError("qx / sx shapes do not match x")
+    _check("w4a8_moe_quant_act", lib().w4a8_moe_quant_act(_p(x), T, H, H, _p(qx), _p(sx), _stream(dev)))
+    return qx, sx
+
+
+def w4a8_moe_route(logits: torch.Tensor, k: int, renormalize: bool = True,
+                   ids: torch.Tensor | None = None, w: torch.Tensor | None = None):
+    """fp32 logits [T, E] -> (expert ids int32 [T, k], weights fp32 [T, k])."""
+    _need(logits, "logits", torch.float32, 2)
+    T, E = logits.shape
+    dev = logits.device
+    ids = torch.empty((T, k), dtype=torch.int32, device=dev) if ids is None else ids
+    w = torch.empty((T, k), dtype=torch.float32, device=dev) if w is None else w
+    _need(ids, "ids", torch.int32, 2, dev)
+    _need(w, "w", torch.float32, 2, dev)
+    if tuple(ids.shape) != (T, k) or tuple(w.shape) != (T, k):
+        raise ValueError("ids / w must be [T, k]")
+    _check("w4a8_moe_route", lib().w4a8_moe_route(_p(logits), T, E, k, int(bool(renormalize)), _p(ids), _p(w),
+                                                  _stream(dev)))
+    return ids, w
+
+
+def w4a8_moe_permute_workspace_bytes(T: int, k: int, E: int) -> int:
+    n = lib().w4a8_moe_permute_workspace_bytes(T, k, E)
+    if n < 0:
+        raise ValueError(f"bad sizes T={T} k={k} E={E}")
+    return n
+
+
+def w4a8_moe_permute(ids: torch.Tensor, E: int, offsets=None, row_token=None, inv_pos=None, workspace=None):
+    """ids int32 [T, k] -> (offsets int32 [E+1], row_token int32 [T*k], inv_pos int32 [T*k])."""
+    _need(ids, "ids", torch.int32, 2)
+    T, k = ids.shape
+    dev = ids.device
+    R = T * k
+    offsets = torch.empty((E + 1,), dtype=torch.int32, device=dev) if offsets is None else offsets
+    row_token = torch.empty((R,), dtype=torch.int32, device=dev) if row_token is None else row_token
+    inv_pos = torch.empty((R,), dtype=torch.int32, device=dev) if inv_pos is None else inv_pos
+    nbytes = w4a8_moe_permute_workspace_bytes(T, k, E)
+    if workspace is None:
+        workspace = torch.empty((max(nbytes, 4),), dtype=torch.uint8, device=dev)
+    _need(offsets, "offsets", torch.int32, 1, dev)
+    _need(row_token, "row_token", torch.int32, 1, dev)
+    _need(inv_pos, "inv_pos", torch.int32, 1, dev)
+    _need(workspace, "workspace", torch.uint8, 1, dev)
+    if offsets.numel() != E + 1 or row_token.numel() != R or inv_pos.numel() != R:
+        raise ValueError("offsets must be [E+1], row_token / inv_pos [T*k]")
+    _check("w4a8_moe_permute", lib().w4a8_moe_permute(_p(ids), T, k, E, _p(offsets), _p(row_token), _p(inv_pos),
+                                                      _p(workspace), workspace.numel(), _stream(dev)))
+    return offsets, row_token, inv_pos
+
+
+def w4a8_moe_grouped_gemm(a: torch.Tensor, a_scale: torch.Tensor, a_rows: torch.Tensor | None,
+                          offsets: torch.Tensor, w_packed: torch.Tensor, w_scale: torch.Tensor, M_total: int,
+                          out: torch.Tensor | None = None, algo: int = W4A8_GG_AUTO):
+    """Grouped W4A8 GEMM -> out fp32 [M_total, N] (rows of expert e: offsets[e]..offsets[e+1])."""
+    _need(a, "a", torch.uint8, 2)
+    dev = a.device
+    _need(a_scale, "a_scale", torch.float32, 1, dev)
+    if a_rows is not None:
+        _need(a_rows, "a_rows", torch.int32, 1, dev)
+        if a_rows.numel() < M_total:
+            raise ValueError("a_rows must hold M_total entries")
+    _need(offsets, "offsets", torch.int32, 1, dev)
+    _need(w_packed, "w_packed", torch.int32, 3, dev)
+    _need(w_scale, "w_scale", torch.float32, 3, dev)
+    E, N, KW = w_packed.shape
+    K = a.shape[1]
+    if KW * 8 != K or tuple(w_scale.shape) != (E, N, K // 128) or offsets.numel() != E + 1:
+        raise ValueError("w_packed [E,N,K/8], w_scale [E,N,K/128] and offsets [E+1] must match a [*,K]")
+    if a_scale.numel() != a.shape[0]:
+        raise ValueError("a_scale must have one entry per row of a")
+    out = torch.empty((M_total, N), dtype=torch.float32, device=dev) if out is None else out
+    _need(out, "out", torch.float32, 2, dev)
+    if tuple(out.shape) != (M_total, N):
+        raise ValueError("out must be [M_total, N]")
+    _check("w4a8_moe_grouped_gemm",
+           lib().w4a8_moe_grouped_gemm_algo(_p(a), _p(a_scale), _p(a_rows), M_total, _p(offsets), E,
+                                            _p(w_packed), _p(w_scale), N, K, _p(out), algo, _stream(dev)))
+    return out
+
+
+def w4a8_moe_swiglu(h: torch.Tensor, qa: torch.Tensor | None = None, sa: torch.Tensor | None = None):
+    """fp32 [M, 2I] -> (E4M3 codes uint8 [M, I], per-row scales fp32 [M])."""
+    _need(h, "h", torch.float32, 2)
+    M, I2 = h.shape
+    I = I2 // 2
+    dev = h.device
+    qa = torch.empty((M, I), dtype=torch.uint8, device=dev) if qa is None else qa
+    sa = torch.empty((M,), dtype=torch.float32, device=dev) if sa is None else sa
+    _need(qa, "qa", torch.uint8, 2, dev)
+    _need(sa, "sa", torch.float32, 1, dev)
+    if I2 % 2 or tuple(qa.shape) != (M, I) or tuple(sa.shape) != (M,):
+        raise ValueError("h must be [M, 2I], qa [M, I], sa [M]")
+    _check("w4a8_moe_swiglu", lib().w4a8_moe_swiglu(_p(h), M, I, _p(qa), _p(sa), _stream(dev)))
+    return qa, sa
+
+
+def w4a8_moe_unpermute(o: torch.Tensor, inv_pos: torch.Tensor, w: torch.Tensor,
+                       y: torch.Tensor | None = None, y_dtype: torch.dtype = torch.float32):
+    """o fp32 [T*k, H], inv_pos int32 [T*k], w fp32 [T, k] -> y [T, H] (fp32 or bf16)."""
+    _need(o, "o", torch.float32, 2)
+    dev = o.device
+    _need(inv_pos, "inv_pos", torch.int32, 1, dev)
+    _need(w, "w", torch.float32, 2, dev)
+    T, k = w.shape
+    H = o.shape[1]
+    if inv_pos.numel() != T * k or o.shape[0] < T * k:
+        raise ValueError("inv_pos must be [T*k] and o at least [T*k, H]")
+    if y is None:
+        y = torch.empty((T, H), dtype=y_dtype, device=dev)
+    if y.dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("y must be float32 or bfloat16")
+    _need(y, "y", y.dtype, 2, dev)
+    if tuple(y.shape) != (T, H):
+        raise ValueError("y must be [T, H]")
+    code = W4A8_Y_F32 if y.dtype == torch.float32 else W4A8_Y_BF16
+    _check("w4a8_moe_unpermute", lib().w4a8_moe_unpermute(_p(o), _p(inv_pos), _p(w), T, k, H, _p(y), code,
+                                                          _stream(dev)))
+    return y

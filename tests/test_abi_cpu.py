@@ -1,0 +1,158 @@
+"""The C ABI library without a GPU: it loads, exports every declared symbol,
+and rejects bad arguments on the host before touching a device.
+
+Pointers passed here are never dereferenced: every call either fails a host
+check or (on a machine without a gfx950) the device check.  The calls that
+would pass every check are made only when no supported device is present.
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+import torch
+
+from quantized_grouped_gemm_token_amd import ops
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "w4a8_moe.h")
+
+OK, ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_DEVICE, ERR_HIP, ERR_WORKSPACE = range(7)
+P = 0x10000          # a fake, 64 KiB-aligned address (never dereferenced)
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"\b(w4a8_moe_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    return ops.lib()
+
+
+@pytest.fixture(scope="module")
+def no_device(L):
+    return L.w4a8_moe_device_supported() == 0
+
+
+def test_exports_every_declared_symbol(L):
+    syms = declared_symbols()
+    assert len(syms) >= 10
+    for s in syms:
+        assert hasattr(L, s), s
+    out = subprocess.run(["nm", "-D", "--defined-only", ops.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\bT (w4a8_moe_\w+)", out))
+    assert set(syms) <= exported
+
+
+def test_status_strings(L):
+    names = [ops.status_string(i) for i in range(7)]
+    assert names == ["W4A8_OK", "W4A8_ERR_NULL", "W4A8_ERR_SHAPE", "W4A8_ERR_ALIGN", "W4A8_ERR_DEVICE",
+                     "W4A8_ERR_HIP", "W4A8_ERR_WORKSPACE"]
+    assert ops.status_string(99) == "W4A8_ERR_UNKNOWN"
+
+
+def test_quant_act_checks(L):
+    f = L.w4a8_moe_quant_act
+    assert f(P, 4, 100, 100, P, P, None) == ERR_SHAPE            # H % 128
+    assert f(P, 4, 256, 200, P, P, None) == ERR_SHAPE            # ld < H
+    assert f(P, 4, 256, 260, P, P, None) == ERR_SHAPE            # ld % 8
+    assert f(P, -1, 256, 256, P, P, None) == ERR_SHAPE
+    assert f(None, 4, 256, 256, P, P, None) == ERR_NULL
+    assert f(P + 8, 4, 256, 256, P, P, None) == ERR_ALIGN        # x not 16-byte aligned
+    assert f(P, 4, 256, 256, P + 4, P, None) == ERR_ALIGN        # qx not 8-byte aligned
+    assert f(None, 0, 256, 256, None, None, None) == OK          # T = 0 is a no-op
+
+
+def test_route_checks(L):
+    f = L.w4a8_moe_route
+    assert f(P, 4, 8, 9, 1, P, P, None) == ERR_SHAPE             # k > E
+    assert f(P, 4, 2048, 8, 1, P, P, None) == ERR_SHAPE          # E > 1024
+    assert f(P, 4, 8, 0, 1, P, P, None) == ERR_SHAPE
+    assert f(P, 4, 8, 2, 1, None, P, None) == ERR_NULL
+    assert f(P + 2, 4, 8, 2, 1, P, P, None) == ERR_ALIGN
+    assert f(None, 0, 8, 2, 1, None, None, None) == OK
+
+
+def test_permute_checks(L):
+    ws = L.w4a8_moe_permute_workspace_bytes
+    assert ws(128, 8, 256) == 256 * 4
+    assert ws(16384, 8, 256) == 128 * 256 * 4
+    assert ws(0, 8, 256) == 256 * 4
+    assert ws(4, 9, 8) == -1
+    f = L.w4a8_moe_permute
+    need = ws(128, 8, 256)
+    assert f(P, 128, 8, 256, P, P, P, P, need - 4, None) == ERR_WORKSPACE
+    assert f(P, 128, 8, 256, None, P, P, P, need, None) == ERR_NULL
+    assert f(P, 128, 8, 256, P, P, P, None, need, None) == ERR_NULL
+    assert f(P, 128, 9, 8, P, P, P, P, need, None) == ERR_SHAPE
+    assert f(P, 128, 8, 256, P + 1, P, P, P, need, None) == ERR_ALIGN
+
+
+def test_grouped_gemm_checks(L):
+    f = L.w4a8_moe_grouped_gemm
+    good = dict(a=P, sa=P, rows=None, M=64, off=P, E=8, w=P, ws=P, N=256, K=256, out=P)
+
+    def call(**kw):
+        d = dict(good, **kw)
+        return f(d["a"], d["sa"], d["rows"], d["M"], d["off"], d["E"], d["w"], d["ws"], d["N"], d["K"], d["out"],
+                 None)
+    assert call(N=96) == ERR_SHAPE                # N % 64
+    assert call(K=192) == ERR_SHAPE               # K % 128
+    assert call(E=0) == ERR_SHAPE
+    assert call(E=2000) == ERR_SHAPE
+    assert call(M=-1) == ERR_SHAPE
+    assert call(w=None) == ERR_NULL
+    assert call(off=None) == ERR_NULL
+    assert call(a=P + 8) == ERR_ALIGN
+    assert call(w=P + 4) == ERR_ALIGN
+    assert call(out=P + 4) == ERR_ALIGN
+    assert call(M=0, a=None, w=None) == OK        # no rows: no-op
+    g = L.w4a8_moe_grouped_gemm_algo
+    assert g(P, P, None, 64, P, 8, P, P, 256, 256, P, 7, None) == ERR_SHAPE   # unknown algo
+
+
+def test_swiglu_unpermute_checks(L):
+    assert L.w4a8_moe_swiglu(P, 4, 100, P, P, None) == ERR_SHAPE
+    assert L.w4a8_moe_swiglu(P + 4, 4, 128, P, P, None) == ERR_ALIGN
+    assert L.w4a8_moe_swiglu(None, 4, 128, P, P, None) == ERR_NULL
+    assert L.w4a8_moe_swiglu(None, 0, 128, None, None, None) == OK
+    u = L.w4a8_moe_unpermute
+    assert u(P, P, P, 4, 2, 100, P, 0, None) == ERR_SHAPE
+    assert u(P, P, P, 4, 2, 256, P, 5, None) == ERR_SHAPE        # bad y dtype
+    assert u(P, P, P, 4, 0, 256, P, 0, None) == ERR_SHAPE
+    assert u(P, P, P, 4, 2, 256, P + 8, 0, None) == ERR_ALIGN    # f32 y needs 16 bytes
+    assert u(P, P, None, 4, 2, 256, P, 0, None) == ERR_NULL
+    assert u(None, None, None, 0, 2, 256, None, 0, None) == OK
+
+
+def test_valid_calls_report_missing_device(L, no_device):
+    if not no_device:
+        pytest.skip("a supported GPU is present; these fake pointers must not reach it")
+    assert L.w4a8_moe_quant_act(P, 4, 256, 256, P, P, None) == ERR_DEVICE
+    assert "gfx950" in ops.last_error() or "device" in ops.last_error()
+    assert L.w4a8_moe_route(P, 4, 8, 2, 1, P, P, None) == ERR_DEVICE
+    assert L.w4a8_moe_permute(P, 4, 2, 8, P, P, P, P, 4096, None) == ERR_DEVICE
+    assert L.w4a8_moe_grouped_gemm(P, P, None, 8, P, 8, P, P, 256, 256, P, None) == ERR_DEVICE
+    assert L.w4a8_moe_swiglu(P, 4, 128, P, P, None) == ERR_DEVICE
+    assert L.w4a8_moe_unpermute(P, P, P, 4, 2, 256, P, 0, None) == ERR_DEVICE
+    assert L.w4a8_moe_device_supported() == 0
+
+
+def test_last_error_is_per_call(L):
+    assert L.w4a8_moe_swiglu(P, 4, 100, P, P, None) == ERR_SHAPE
+    assert "I=100" in ops.last_error()
+    assert L.w4a8_moe_swiglu(None, 0, 128, None, None, None) == OK
+    assert ops.last_error() == ""
+
+
+def test_binding_rejects_host_tensors():
+    x = torch.zeros((4, 256), dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        ops.w4a8_moe_quant_act(x)
+    with pytest.raises(TypeError):
+        ops.w4a8_moe_quant_act(torch.zeros((4, 256), dtype=torch.float32))
+    with pytest.raises(ValueError):
+        ops.w4a8_moe_route(torch.zeros((4, 8), dtype=torch.float32), 2)
