@@ -84,6 +84,9 @@ def main() -> int:
                                                           "2 decode T=256, 3 prefill T=8192, 4 skewed T=16384")
     ap.add_argument("--cpu-tokens", type=int, default=16, help="tokens in the CPU oracle sample (0: skip)")
     ap.add_argument("--quiet", action="store_true")
+    ap.add_argument("--copy-bytes", type=int, default=0,
+                    help="instead of the layer, run a plain device copy of this many bytes (5 times): the "
+                         "reference for scaling HBM byte counters")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
@@ -96,6 +99,21 @@ def main() -> int:
     from quantized_grouped_gemm_token_amd.layer import W4A8MoE
 
     log = (lambda *a: None) if args.quiet else (lambda *a: print("[bench]", *a, file=sys.stderr, flush=True))
+    if args.copy_bytes:
+        n = args.copy_bytes // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        ev0.record()
+        for _ in range(5):
+            dst.copy_(src)
+        ev1.record()
+        torch.cuda.synchronize()
+        ms = ev0.elapsed_time(ev1) / 5
+        print(json.dumps({"copy_bytes_each_way": n * 4, "ms_per_copy": round(ms, 5),
+                          "GBps_read_plus_write": round(2 * n * 4 / ms / 1e6, 1)}), flush=True)
+        return 0
     if not ops.w4a8_moe_device_supported():
         print("bench.py: cuda:0 is not a gfx950: " + ops.last_error(), file=sys.stderr)
         return 1

@@ -1,147 +1,257 @@
 // Grouped W4A8 GEMM, weight-streaming form: for few rows per expert (decode).
 //
 // With a handful of tokens per expert the GEMM is bound by reading the INT4
-// weights from HBM once.  Each wave owns NSUB x 16 weight rows (output
-// columns) of one expert and streams them along K with 16-byte loads: lane l
-// reads the 16 bytes (32 nibbles) of column l % 16 for the K quarter l / 16
-// of each 128-wide group, which is exactly its B operand of the
-// 16x16x128 FP8 MFMA -- no LDS, no shuffles.  The expert's rows (A, FP8
-// codes, gathered through a_rows) come from L2 in 16-row tiles.
+// weights from HBM once, so the kernel is built around the load pattern HBM
+// serves best: every weight load instruction of a wave reads 8 weight rows x
+// 128 contiguous bytes (8 lanes per row, 16 bytes each).  A wave owns NS
+// subtiles of 16 weight rows (output columns) of one expert and walks K two
+// 128-wide groups at a time (128 packed bytes per row = 2 groups):
 //
-// Grid: (ceil(N / (64 * NSUB)), E); 256 threads = 4 waves side by side in N.
-// An expert with no rows returns at once; one with more than 16 * MSUB rows
-// loops over M blocks, re-streaming its weights (the tiled kernel is the one
-// for many rows per expert).
+//   load A: rows 0..7 of the subtile  -- lanes col < 8 take group g quarter kq,
+//                                        lanes col >= 8 take group g+1 quarter kq
+//   load B: rows 8..15                -- col >= 8 take group g, col < 8 group g+1
+//
+// (lane = col + 16 * kq).  The MFMA B operand of group g is A on the lanes
+// col < 8 and B on the others (one select per word); that of group g+1 is
+// the other half of each, rotated by 8 lanes inside each 16-lane row (one
+// DPP move per word).
+//
+// The 4 waves of a workgroup share the expert's activation rows (FP8 codes,
+// up to 16 rows per M block, gathered through a_rows): they are staged in
+// LDS once per chunk of CH group pairs, directly in MFMA operand order, double
+// buffered, with one barrier per chunk.  Group scales are read as 16-byte
+// vectors (4 groups) when the group count allows.
+//
+// Grid: (ceil(N / (64 NS)), E); 256 threads = 4 waves side by side in N.  An
+// expert with no rows returns at once; one with more than 16 rows loops over
+// M blocks, re-streaming its weights (the tiled kernel is the one for many
+// rows per expert).
 #include "gemm_common.hpp"
 #include "kernels.hpp"
 
 namespace w4a8 {
 
-template <int NSUB, int MSUB, int U>
-struct StreamStage {
-  i32x4 wb[U][NSUB];
-  float sc[U][NSUB];
-  v8i av[U][MSUB];
+constexpr int kStreamThreads = 256;
+
+// v_mov_b32 with DPP row_ror:8 -- lane i of each 16-lane row takes lane i^8
+__device__ __forceinline__ int row_ror8(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, 0x128, 0xf, 0xf, false);
+}
+
+// LDS image of the activation tile of one chunk: for each group h of the
+// chunk and MFMA lane L, the 32 bytes lane L feeds to the MFMA (row L % 16,
+// K quarter L / 16 of group h).
+template <int CH>
+struct StreamSmem {
+  uint8_t a[2][2 * CH][64][32];
 };
 
-template <int NSUB, int MSUB, int U>
-__device__ __forceinline__ void stream_load(StreamStage<NSUB, MSUB, U>& st, const int32_t* const (&wrow)[NSUB],
-                                            const float* const (&srow)[NSUB],
-                                            const uint8_t* const (&arow)[MSUB], int g0) {
+// Chunk of activations -> registers: thread t loads rows t / 16 (16 B chunks
+// t % 16, +16, +32, ... of the chunk's 256*CH bytes per row).
+template <int CH>
+struct AChunk {
+  static constexpr int kPerThread = (16 * 256 * CH) / (16 * kStreamThreads);   // 16-byte pieces per thread
+  i32x4 v[kPerThread];
+};
+
+template <int CH>
+__device__ __forceinline__ void a_chunk_load(AChunk<CH>& r, const uint8_t* arow_t, int g0, int ngroups) {
+  const int c0 = threadIdx.x & 15;
 #pragma unroll
-  for (int u = 0; u < U; ++u) {
-    const int g = g0 + u;
-#pragma unroll
-    for (int s = 0; s < NSUB; ++s) {
-      st.wb[u][s] = __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(wrow[s] + g * 16));
-      st.sc[u][s] = srow[s][g];
-    }
-#pragma unroll
-    for (int t = 0; t < MSUB; ++t) st.av[u][t] = *reinterpret_cast<const v8i*>(arow[t] + g * kGroup);
+  for (int i = 0; i < AChunk<CH>::kPerThread; ++i) {
+    const int c = c0 + 16 * i;               // 16-byte piece of the chunk's row bytes
+    if (c * 16 < ngroups * kGroup) r.v[i] = *reinterpret_cast<const i32x4*>(arow_t + g0 * kGroup + c * 16);
   }
 }
 
-template <int NSUB, int MSUB, int U>
-__device__ __forceinline__ void stream_compute(const StreamStage<NSUB, MSUB, U>& st, v4f (&acc)[MSUB][NSUB]) {
+template <int CH>
+__device__ __forceinline__ void a_chunk_store(const AChunk<CH>& r, StreamSmem<CH>& sm, int buf, int ngroups) {
+  const int row = threadIdx.x >> 4, c0 = threadIdx.x & 15;
+#pragma unroll
+  for (int i = 0; i < AChunk<CH>::kPerThread; ++i) {
+    const int c = c0 + 16 * i;
+    const int k = c * 16;                    // byte within the chunk's row
+    if (k < ngroups * kGroup) {
+      const int h = k >> 7, kk = k & 127;    // group within the chunk, K within the group
+      *reinterpret_cast<i32x4*>(&sm.a[buf][h][row + 16 * (kk >> 5)][kk & 31]) = r.v[i];
+    }
+  }
+}
+
+template <int NS>
+struct WPair {
+  i32x4 wa[NS], wb[NS];
+};
+
+template <int NS>
+__device__ __forceinline__ void w_pair_load(WPair<NS>& w, const uint8_t* const (&pa)[NS],
+                                            const uint8_t* const (&pb)[NS], int g) {
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    w.wa[s] = __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(pa[s] + g * 64));
+    w.wb[s] = __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(pb[s] + g * 64));
+  }
+}
+
+// one group pair: B operands from the two wide loads, A operands from LDS
+template <int NS>
+__device__ __forceinline__ void pair_compute(const WPair<NS>& w, const float (&s0)[NS], const float (&s1)[NS],
+                                             const uint8_t* a0, const uint8_t* a1, bool lo,
+                                             v4f (&acc)[NS]) {
+  const v8i av0 = *reinterpret_cast<const v8i*>(a0);
+  const v8i av1 = *reinterpret_cast<const v8i*>(a1);
   const v8i kb = bias_operand();
   const v4f zero = {0.f, 0.f, 0.f, 0.f};
+  const v4f c0 = mfma16x16x128(av0, kb, zero);
+  const v4f c1 = mfma16x16x128(av1, kb, zero);
 #pragma unroll
-  for (int u = 0; u < U; ++u) {
-    v4f bias[MSUB];
+  for (int s = 0; s < NS; ++s) {
+    i32x4 t0, t1;
 #pragma unroll
-    for (int t = 0; t < MSUB; ++t) bias[t] = mfma16x16x128(st.av[u][t], kb, zero);
-#pragma unroll
-    for (int s = 0; s < NSUB; ++s) {
-      const v8i b = nibbles_to_fp8(st.wb[u][s]);
-#pragma unroll
-      for (int t = 0; t < MSUB; ++t) {
-        const v4f d = mfma16x16x128(st.av[u][t], b, bias[t]);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) acc[t][s][r] = fmaf(st.sc[u][s], d[r], acc[t][s][r]);
-      }
+    for (int q = 0; q < 4; ++q) {
+      t0[q] = lo ? w.wa[s][q] : w.wb[s][q];
+      t1[q] = row_ror8(lo ? w.wb[s][q] : w.wa[s][q]);
     }
+    const v4f d0 = mfma16x16x128(av0, nibbles_to_fp8(t0), c0);
+    const v4f d1 = mfma16x16x128(av1, nibbles_to_fp8(t1), c1);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) acc[s][r] = fmaf(s1[s], d1[r], fmaf(s0[s], d0[r], acc[s][r]));
   }
 }
 
-template <int NSUB, int MSUB, int U>
-__global__ __launch_bounds__(256) void gg_stream_kernel(const uint8_t* __restrict__ a,
-                                                        const float* __restrict__ a_scale,
-                                                        const int32_t* __restrict__ a_rows,
-                                                        const int32_t* __restrict__ offsets,
-                                                        const int32_t* __restrict__ w_packed,
-                                                        const float* __restrict__ w_scale, int64_t N, int64_t K,
-                                                        float* __restrict__ out) {
+template <int NS, int CH>
+__global__ __launch_bounds__(kStreamThreads) void gg_stream_kernel(const uint8_t* __restrict__ a,
+                                                                   const float* __restrict__ a_scale,
+                                                                   const int32_t* __restrict__ a_rows,
+                                                                   const int32_t* __restrict__ offsets,
+                                                                   const int32_t* __restrict__ w_packed,
+                                                                   const float* __restrict__ w_scale, int64_t N,
+                                                                   int64_t K, float* __restrict__ out) {
+  __shared__ StreamSmem<CH> sm;
   const int e = blockIdx.y;
   const int r0 = offsets[e], r1 = offsets[e + 1];
   if (r1 <= r0) return;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int col = lane & 15, kq = lane >> 4;
-  const int64_t n_base = ((int64_t)blockIdx.x * 4 + wave) * (16 * NSUB);
-  if (n_base >= N) return;
+  const bool lo = col < 8;
+  const int64_t n0 = ((int64_t)blockIdx.x * 4 + wave) * (16 * NS);
+  const bool active = n0 < N;                // waves past N only help stage activations
   const int G = (int)(K >> 7);
-  const int64_t kw = K >> 3;   // int32 words per weight row
+  const int64_t row_bytes = K >> 1;
+  const bool vec_scales = (G & 3) == 0 && (reinterpret_cast<uintptr_t>(w_scale) & 15) == 0;
 
-  const int32_t* wrow[NSUB];
-  const float* srow[NSUB];
+  const uint8_t* pa[NS];
+  const uint8_t* pb[NS];
+  const float* srow[NS];
 #pragma unroll
-  for (int s = 0; s < NSUB; ++s) {
-    const int64_t n = n_base + s * 16 + col;
-    wrow[s] = w_packed + ((int64_t)e * N + n) * kw + kq * 4;
-    srow[s] = w_scale + ((int64_t)e * N + n) * G;
+  for (int s = 0; s < NS; ++s) {
+    const int64_t nb = active ? n0 + 16 * s : 0;
+    const uint8_t* wbase = reinterpret_cast<const uint8_t*>(w_packed) + ((int64_t)e * N + nb) * row_bytes;
+    pa[s] = wbase + (int64_t)(col & 7) * row_bytes + (lo ? 0 : 64) + kq * 16;
+    pb[s] = wbase + (int64_t)(8 + (col & 7)) * row_bytes + (lo ? 64 : 0) + kq * 16;
+    srow[s] = w_scale + ((int64_t)e * N + nb + col) * G;
   }
 
-  for (int m0 = r0; m0 < r1; m0 += 16 * MSUB) {
-    const uint8_t* arow[MSUB];
+  for (int m0 = r0; m0 < r1; m0 += 16) {
+    // activation row staged by this thread (rows past the end repeat the last one; never stored)
+    const int p_t = min(m0 + (int)(threadIdx.x >> 4), r1 - 1);
+    const uint8_t* arow_t = a + (int64_t)(a_rows ? a_rows[p_t] : p_t) * K;
+    v4f acc[NS];
 #pragma unroll
-    for (int t = 0; t < MSUB; ++t) {
-      const int p = min(m0 + t * 16 + col, r1 - 1);   // rows past the end repeat the last one (not stored)
-      const int64_t src = a_rows ? a_rows[p] : p;
-      arow[t] = a + src * K + kq * 32;
-    }
-    v4f acc[MSUB][NSUB];
-#pragma unroll
-    for (int t = 0; t < MSUB; ++t)
-#pragma unroll
-      for (int s = 0; s < NSUB; ++s) acc[t][s] = v4f{0.f, 0.f, 0.f, 0.f};
+    for (int s = 0; s < NS; ++s) acc[s] = v4f{0.f, 0.f, 0.f, 0.f};
 
-    int g0 = 0;
-    for (; g0 + U <= G; g0 += U) {
-      StreamStage<NSUB, MSUB, U> st;
-      stream_load(st, wrow, srow, arow, g0);
-      stream_compute(st, acc);
+    const int nchunks = (G + 2 * CH - 1) / (2 * CH);
+    {
+      AChunk<CH> ar;
+      a_chunk_load(ar, arow_t, 0, min(G, 2 * CH));
+      a_chunk_store(ar, sm, 0, min(G, 2 * CH));
     }
-    for (; g0 < G; ++g0) {
-      StreamStage<NSUB, MSUB, 1> st;
-      stream_load(st, wrow, srow, arow, g0);
-      stream_compute(st, acc);
+    __syncthreads();
+    for (int ci = 0; ci < nchunks; ++ci) {
+      const int g0 = ci * 2 * CH;
+      const int ng = min(2 * CH, G - g0);    // groups in this chunk
+      const int buf = ci & 1;
+      AChunk<CH> next;
+      const bool has_next = ci + 1 < nchunks;
+      const int ng_next = has_next ? min(2 * CH, G - g0 - 2 * CH) : 0;
+      if (has_next) a_chunk_load(next, arow_t, g0 + 2 * CH, ng_next);
+      if (active) {
+        // scales of this chunk's groups for each subtile
+        float sc[NS][2 * CH];
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+          if (vec_scales && ng == 2 * CH) {
+#pragma unroll
+            for (int v = 0; v < (2 * CH) / 4; ++v) {
+              const f32x4 q4 = *reinterpret_cast<const f32x4*>(srow[s] + g0 + 4 * v);
+              sc[s][4 * v] = q4[0]; sc[s][4 * v + 1] = q4[1]; sc[s][4 * v + 2] = q4[2]; sc[s][4 * v + 3] = q4[3];
+            }
+          } else {
+#pragma unroll
+            for (int h = 0; h < 2 * CH; ++h) sc[s][h] = h < ng ? srow[s][g0 + h] : 0.f;
+          }
+        }
+        const int npairs = ng >> 1;
+#pragma unroll
+        for (int u = 0; u < CH; u += 2) {
+          if (u < npairs) {
+            WPair<NS> w0, w1;
+            w_pair_load(w0, pa, pb, g0 + 2 * u);
+            const bool two = u + 1 < npairs;
+            if (two) w_pair_load(w1, pa, pb, g0 + 2 * u + 2);
+            float s0[NS], s1[NS];
+#pragma unroll
+            for (int s = 0; s < NS; ++s) { s0[s] = sc[s][2 * u]; s1[s] = sc[s][2 * u + 1]; }
+            pair_compute(w0, s0, s1, &sm.a[buf][2 * u][lane][0], &sm.a[buf][2 * u + 1][lane][0], lo, acc);
+            if (two) {
+#pragma unroll
+              for (int s = 0; s < NS; ++s) { s0[s] = sc[s][2 * u + 2]; s1[s] = sc[s][2 * u + 3]; }
+              pair_compute(w1, s0, s1, &sm.a[buf][2 * u + 2][lane][0], &sm.a[buf][2 * u + 3][lane][0], lo, acc);
+            }
+          }
+        }
+        if (ng & 1) {   // a last single group: each lane reads its own column's quarter
+          const int h = ng - 1;
+          const v8i av = *reinterpret_cast<const v8i*>(&sm.a[buf][h][lane][0]);
+          const v4f c = mfma16x16x128(av, bias_operand(), v4f{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+          for (int s = 0; s < NS; ++s) {
+            const uint8_t* pself = pa[s] - (lo ? 0 : 64) + (int64_t)(col - (col & 7)) * row_bytes;
+            const i32x4 wq = __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(pself + (g0 + h) * 64));
+            const v4f d = mfma16x16x128(av, nibbles_to_fp8(wq), c);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc[s][r] = fmaf(sc[s][h], d[r], acc[s][r]);
+          }
+        }
+      }
+      if (has_next) a_chunk_store(next, sm, buf ^ 1, ng_next);
+      __syncthreads();
     }
 
-#pragma unroll
-    for (int t = 0; t < MSUB; ++t) {
+    if (active) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int p = m0 + t * 16 + kq * 4 + r;
+        const int p = m0 + kq * 4 + r;
         if (p < r1) {
           const int64_t src = a_rows ? a_rows[p] : p;
           const float rs = a_scale[src] * kUnitScale;
 #pragma unroll
-          for (int s = 0; s < NSUB; ++s) out[(int64_t)p * N + n_base + s * 16 + col] = acc[t][s][r] * rs;
+          for (int s = 0; s < NS; ++s) out[(int64_t)p * N + n0 + 16 * s + col] = acc[s][r] * rs;
         }
       }
     }
   }
 }
 
+template <int NS, int CH>
+static void launch_variant(const GemmArgs& g, hipStream_t stream) {
+  const dim3 grid((unsigned)((g.N + 64 * NS - 1) / (64 * NS)), (unsigned)g.E);
+  hipLaunchKernelGGL((gg_stream_kernel<NS, CH>), grid, dim3(kStreamThreads), 0, stream, g.a, g.a_scale, g.a_rows,
+                     g.offsets, g.w_packed, g.w_scale, g.N, g.K, g.out);
+}
+
 hipError_t launch_gg_stream(const GemmArgs& g, hipStream_t stream) {
-  constexpr int NSUB = 2, U = 4;
-  const dim3 block(256);
-  const dim3 grid((unsigned)((g.N + 64 * NSUB - 1) / (64 * NSUB)), (unsigned)g.E);
-  if (g.M_total <= 4 * g.E)
-    hipLaunchKernelGGL((gg_stream_kernel<NSUB, 1, U>), grid, block, 0, stream, g.a, g.a_scale, g.a_rows,
-                       g.offsets, g.w_packed, g.w_scale, g.N, g.K, g.out);
-  else
-    hipLaunchKernelGGL((gg_stream_kernel<NSUB, 4, U>), grid, block, 0, stream, g.a, g.a_scale, g.a_rows,
-                       g.offsets, g.w_packed, g.w_scale, g.N, g.K, g.out);
+  launch_variant<4, 4>(g, stream);
   return hipGetLastError();
 }
 
