@@ -7,7 +7,9 @@ linked into one shared library next to this file.  Flags:
   * -O3, C++17, position independent;
   * packed fp32 instructions disabled (-packed-fp32-ops) for every kernel;
   * fp32 division and square root correctly rounded (the FP8 codes are
-    bit-exact only with IEEE division).
+    bit-exact only with IEEE division);
+  * MFMA results kept in VGPRs (the GEMMs scale every MFMA result on the
+    VALU right away, which cannot read accumulation registers).
 """
 from __future__ import annotations
 
@@ -38,6 +40,7 @@ COMMON = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-fhip-fp32-correctly-rounded-divide-sqrt",
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wall", "-Wno-unused-command-line-argument",
     f"-I{INCLUDE}", f"-I{CSRC}",
 ]

@@ -34,9 +34,7 @@ namespace w4a8 {
 constexpr int kStreamThreads = 256;
 
 // v_mov_b32 with DPP row_ror:8 -- lane i of each 16-lane row takes lane i^8
-__device__ __forceinline__ int row_ror8(int v) {
-  return __builtin_amdgcn_update_dpp(0, v, 0x128, 0xf, 0xf, false);
-}
+__device__ __forceinline__ int row_ror8(int v) { return __builtin_amdgcn_mov_dpp(v, 0x128, 0xf, 0xf, true); }
 
 // LDS image of the activation tile of one chunk: for each group h of the
 // chunk and MFMA lane L, the 32 bytes lane L feeds to the MFMA (row L % 16,
@@ -131,7 +129,8 @@ __global__ __launch_bounds__(kStreamThreads) void gg_stream_kernel(const uint8_t
   const int e = blockIdx.y;
   const int r0 = offsets[e], r1 = offsets[e + 1];
   if (r1 <= r0) return;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
   const int col = lane & 15, kq = lane >> 4;
   const bool lo = col < 8;
   const int64_t n0 = ((int64_t)blockIdx.x * 4 + wave) * (16 * NS);
