@@ -44,15 +44,27 @@ def kernel_sources_hash() -> str:
 
 
 def load_traffic(path: str, kernel_hash: str):
-    """HBM bytes per launch from a committed rocprofv3 counter summary, if it
-    was taken on the current kernel sources."""
+    """HBM bytes per launch from a committed rocprofv3 counter summary (text,
+    one "key: value" per line), if it was taken on the current kernel sources."""
     if not os.path.exists(path):
         return None
+    fields = {}
     with open(path) as f:
-        d = json.load(f)
-    if d.get("kernel_sources_hash") != kernel_hash:
+        for line in f:
+            key, sep, val = line.partition(":")
+            if sep and not line.startswith(("#", " ", "|", "`")):
+                fields[key.strip()] = val.strip()
+    if fields.get("kernel_sources_hash") != kernel_hash:
         return None
-    return d.get("hbm_bytes_per_launch")
+    try:
+        return int(float(fields["hbm_bytes_per_launch"]))
+    except (KeyError, ValueError):
+        return None
+
+
+def workload_tag(shape) -> str:
+    """File-name tag of a workload, e.g. decode_T128."""
+    return shape.name.split()[0] + f"_T{shape.T}"
 
 
 def cpu_baseline(wl, n_tokens: int) -> dict:
@@ -164,7 +176,7 @@ def main() -> int:
     decode = args.config in (0, 1, 2)
     khash = kernel_sources_hash()
     kernel = "gg_stream" if decode else "gg_tiled"
-    traffic = load_traffic(os.path.join(ROOT, "profiles", f"{kernel}_config{args.config}_pmc.json"), khash)
+    traffic = load_traffic(os.path.join(ROOT, "profiles", f"{kernel}_{workload_tag(sh)}_pmc.txt"), khash)
     if decode:
         achieved = gate_up_bytes / t_gu / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
