@@ -25,6 +25,7 @@ namespace w4a8 {
 
 typedef int v8i __attribute__((ext_vector_type(8)));     // 32 E4M3 bytes
 typedef float v4f __attribute__((ext_vector_type(4)));   // 16x16 fp32 tile, 4 per lane
+typedef float v16f __attribute__((ext_vector_type(16))); // 32x32 fp32 tile, 16 per lane
 
 constexpr int kBiasWord = (int)0x88888888u;                // four E4M3 -2^-6
 constexpr float kUnitScale = 512.0f;                        // 2^9
@@ -35,6 +36,14 @@ constexpr float kUnitScale = 512.0f;                        // 2^9
 // D lane l holds column l % 16, rows 4 * (l / 16) .. +3.
 __device__ __forceinline__ v4f mfma16x16x128(v8i a, v8i b, v4f c) {
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
+// v_mfma_f32_32x32x64_f8f6f4 with both operands E4M3 and no block scaling.
+// Lane l supplies A row (l % 32) and B column (l % 32), K elements
+// 32 * (l / 32) .. +32 of the 64; D element v of lane l is row
+// 8 * (v / 4) + 4 * (l / 32) + v % 4, column l % 32.
+__device__ __forceinline__ v16f mfma32x32x64(v8i a, v8i b, v16f c) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
 }
 
 // 32 packed nibbles (K order: word c holds k = 8c .. 8c+7, nibble j at bits

@@ -1,69 +1,71 @@
 // Grouped W4A8 GEMM, tiled form: for many rows per expert (prefill).
 //
-// A persistent kernel (one 256-thread workgroup per CU) walks the ragged
-// list of tiles of all experts.  A tile is up to 128 rows of one expert (an
-// "M block") by 256 output columns; wave w owns columns 64w..64w+63 for all
-// of the tile's rows (8 row subtiles x 4 column subtiles of 16x16 MFMA
-// outputs, 128 fp32 accumulators per lane).  Because every wave covers every
-// row, a short last M block costs only its own 16-row subtiles.
+// A persistent kernel (one 1024-thread workgroup per CU, four waves per
+// SIMD) walks the ragged list of tiles of all experts.  A tile is up to 256
+// rows of one expert by 256 output columns.  Wave w = 8 rg + cg owns the 32
+// columns 32 cg .. 32 cg + 31 and the 32-row blocks rg, rg + 2, rg + 4, rg + 6
+// (interleaved, so that a short tile still splits its rows over both row
+// groups).  Its outputs are four 32x32 MFMA tiles, 64 fp32 accumulators per
+// lane.  Four waves per SIMD are what lets the matrix core run while other
+// waves do the per-group scale FMAs and the nibble unpacking.
 //
-// K is walked one 128-wide group at a time through a 4-stage LDS ring filled
-// by direct global-to-LDS loads (no registers), issued 3 groups ahead:
-//   * the activation rows (FP8 codes, gathered through a_rows) in MFMA
-//     operand order -- 16 KB per group;
-//   * each wave's own packed INT4 weights of the group (lane col + 16 kq
-//     takes quarter kq of weight row col: exactly its MFMA B operand);
-//   * each wave's 64 group scales.
-// Each wave turns its weights into MFMA B operands in registers (nibbles read
-// as E4M3 bytes u * 2^-9, see gemm_common.hpp), and the +8 offset of the
-// uint4b8 nibbles is removed with the per-row group sums of the activations,
-// computed once per workgroup by one extra MFMA per row subtile, one group
-// ahead, and shared through LDS.  Each group's partial product is scaled into
-// the fp32 accumulators with the weights' group scale.  One barrier per
-// group.
+// K is walked one 128-wide group at a time through a 3-slot LDS ring filled
+// by direct global-to-LDS loads, two groups ahead.  Per group a slot holds
+//   * the 256 activation rows (FP8 codes, gathered through a_rows): 128 bytes
+//     per row, loaded as 8 rows x 128 contiguous bytes per instruction; the
+//     16-byte chunks of a row are XOR-swizzled so that the MFMA operand reads
+//     are free of LDS bank conflicts;
+//   * the 256 weight columns: 64 packed bytes each (16 columns x 64 bytes per
+//     instruction), swizzled the same way.
+// The group scales of 4 groups are loaded at once (16 bytes per column).
 //
-// Tile order: each XCD runs windows of consecutive tiles of an expert at the
-// same time (see the tile loop), so a weight tile and an activation block are
-// fetched from HBM about once and served to the other tiles of the window by
-// that XCD's L2.
+// The +8 offset of the uint4b8 nibbles is removed with the per-row sums of
+// the activation codes of each group (see gemm_common.hpp): wave w loads
+// exactly the 16 activation rows whose sums it computes, with one 16x16x128
+// MFMA against the constant -2^-6, so the sums of group g + 1 are ready as
+// soon as the wave's own loads have landed and are published by the one
+// barrier per group.
+//
+// Tile order: each XCD runs windows of consecutive tiles (an expert's tiles
+// are numbered N block by N block, M blocks adjacent) at the same time, so a
+// weight tile and an activation block are fetched from HBM about once and
+// served to the other tiles of the window by that XCD's L2.
 #include "gemm_common.hpp"
 #include "kernels.hpp"
 
 namespace w4a8 {
 
-constexpr int kTileM = 128;           // rows per tile (M block)
-constexpr int kTileN = 256;           // columns per tile (4 waves x 64)
-constexpr int kTiledThreads = 256;
+constexpr int kTM = 256;              // rows per tile
+constexpr int kTN = 256;              // columns per tile
 constexpr int kMaxExperts = 1024;
 constexpr int kXcds = 8;              // accelerator complex dies of an MI355X (round-robin dispatch)
+#ifndef GG_TILED_WAVES
+#define GG_TILED_WAVES 8                // waves per workgroup
+#define GG_TILED_NJ 2                   // 32-column blocks per wave
+#endif
 
-constexpr int kStages = 4;            // LDS ring depth (groups)
-
-// One ring slot: everything one 128-wide K group of a tile needs.  The slots
-// are separate LDS variables, addressed with compile-time slot numbers, so
-// that the compiler can tell the slot being read from the slots still being
-// filled and does not wait for every load in flight before each LDS read.
+// One ring slot: the activation rows and the weight columns of one group.
+//   a: row r, 16-byte chunk c (K bytes 16c..16c+15 of the group) at r*128 + 16*(c ^ ((r >> 1) & 7))
+//   w: column n, chunk c (packed bytes 16c..16c+15) at n*64 + 16*(c ^ ((n >> 2) & 3))
+// The three slots are separate LDS variables addressed with compile-time
+// slot numbers, so that the compiler can tell the slot being read from the
+// slots still being filled.
 struct __attribute__((aligned(16))) RingSlot {
-  // activations in MFMA operand order: lane L's 32 bytes are split in two
-  // 16-byte planes so that every LDS read is 64 lanes x 16 consecutive bytes
-  // (conflict free) and every direct load fills one plane
-  uint8_t a[8][2][64][16];   // [row subtile][half][MFMA lane][16 B]
-  uint8_t w[4][4][64][16];   // [wave][column subtile][lane][16 B] packed INT4
-  float sc[4][64];           // [wave][column] group scales
+  uint8_t a[kTM * kGroup];
+  uint8_t w[kTN * kGroup / 2];
 };
 
 template <int S>
-__device__ __forceinline__ RingSlot& slot(RingSlot& r0, RingSlot& r1, RingSlot& r2, RingSlot& r3) {
+__device__ __forceinline__ RingSlot& slot(RingSlot& r0, RingSlot& r1, RingSlot& r2) {
   if constexpr (S == 0) return r0;
   else if constexpr (S == 1) return r1;
-  else if constexpr (S == 2) return r2;
-  else return r3;
+  else return r2;
 }
 
-// Workgroup barrier that leaves direct-to-LDS loads in flight: __syncthreads'
-// release fence would wait for all of them.  The caller waits for what the
-// other waves need (its LDS writes and the loads that must have landed); the
-// empty asm statements keep the compiler from moving memory accesses across.
+// Workgroup barrier that leaves direct-to-LDS loads in flight (__syncthreads'
+// release fence would wait for all of them).  The caller waits for what the
+// other waves need; the empty asm statements keep the compiler from moving
+// memory accesses across.
 __device__ __forceinline__ void barrier_loads_in_flight() {
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_barrier();
@@ -82,40 +84,69 @@ __device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t r, uint32_t voff, ui
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 4, voff, soff, 0, 0);
 }
 
-__device__ __forceinline__ int tiles_of(int rows, int nb) { return ((rows + kTileM - 1) / kTileM) * nb; }
-
 template <typename T>
 __device__ __forceinline__ T lds_load(const void* p) {
   return *reinterpret_cast<const T*>(__builtin_assume_aligned(p, 16));
 }
 
-__global__ __launch_bounds__(kTiledThreads, 1) void gg_tiled_kernel(const uint8_t* __restrict__ a,
-                                                                   const float* __restrict__ a_scale,
-                                                                   const int32_t* __restrict__ a_rows,
-                                                                   const int32_t* __restrict__ offsets, int E,
-                                                                   const int32_t* __restrict__ w_packed,
-                                                                   const float* __restrict__ w_scale, int64_t N,
-                                                                   int64_t K, float* __restrict__ out) {
-  __shared__ RingSlot ring0, ring1, ring2, ring3;
-  __shared__ __attribute__((aligned(16))) float bias_sm[kStages][kTileM];   // -2^-6 * group code sums per row
-  __shared__ int tile_start[kMaxExperts + 1];                              // first tile index of each expert
+// One fp32 LDS read the compiler's wait analysis does not see: the scale
+// quads are filled by direct loads into a buffer whose half being read the
+// compiler cannot tell from the half being filled.  The read waits for
+// itself.
+__device__ __forceinline__ float lds_read_f32_self_waiting(const float* p) {
+  float v;
+  const uint32_t addr = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) float*)p;
+  asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(addr) : "memory");
+  return v;
+}
+
+__device__ __forceinline__ int tiles_of(int rows, int nb) { return ((rows + kTM - 1) / kTM) * nb; }
+
+// kWaves waves per workgroup; each wave owns kNJ blocks of 32 columns.
+template <int kWaves, int kNJ>
+__global__ __launch_bounds__(kWaves * kWave, 1) void gg_tiled_kernel(const uint8_t* __restrict__ a,
+                                                              const float* __restrict__ a_scale,
+                                                              const int32_t* __restrict__ a_rows,
+                                                              const int32_t* __restrict__ offsets, int E,
+                                                              const int32_t* __restrict__ w_packed,
+                                                              const float* __restrict__ w_scale, int64_t N,
+                                                              int64_t K, float* __restrict__ out) {
+  __shared__ RingSlot ring0, ring1, ring2;
+  __shared__ __attribute__((aligned(16))) float scq[2][4 * kTN];   // scale quads: [quad parity][column * 4 + g % 4]
+                                                                    // (or [g % 4][column] when loaded per group)
+  __shared__ __attribute__((aligned(16))) float bias_sm[2][kTM];   // -2^-6 * group code sums: [group parity][row]
+  __shared__ __attribute__((aligned(16))) float ascale_sm[kTM];    // token scales of the tile's rows
+  __shared__ int tile_start[kMaxExperts + 1];                      // first tile index of each expert
+  __shared__ int wsum[kWaves];
+  constexpr int kThreads = kWaves * kWave;
+  constexpr int kColGroups = kTN / (32 * kNJ);         // waves side by side in N
+  constexpr int kRowGroups = kWaves / kColGroups;      // waves side by side in M
+  constexpr int kBlocks = (kTM / 32) / kRowGroups;     // 32-row blocks per wave
+  constexpr int kARows = kTM / kWaves;                 // activation rows each wave loads (and sums)
+  constexpr int kWCols = kTN / kWaves;                 // weight columns each wave loads
+  constexpr int kStageLoads = kARows / 8 + kWCols / 16;
+  static_assert(kColGroups * kRowGroups == kWaves && kBlocks * kRowGroups * 32 == kTM, "wave grid");
+  static_assert(kARows % 16 == 0 && kWCols % 16 == 0, "load roles");
+
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: keeps wave-indexed values scalar
-  const int col = lane & 15, kq = lane >> 4;
-  const int NB = (int)((N + kTileN - 1) / kTileN);
+  const int i32 = lane & 31, kh = lane >> 5;                   // 32x32 MFMA lane roles
+  const int rg = wave / kColGroups, cg = wave % kColGroups;    // row group, column group
+  const int NB = (int)((N + kTN - 1) / kTN);
   const int G = (int)(K >> 7);
   const uint32_t row_bytes = (uint32_t)(K >> 1);
+  // scale quads as 16-byte loads need 4 | G and a 16-byte aligned scale array
+  const bool vec_scales = (G & 3) == 0 && (reinterpret_cast<uintptr_t>(w_scale) & 15) == 0;
 
   // ---- tile numbering: exclusive prefix of per-expert tile counts (wave-level scans)
   {
-    __shared__ int wsum[4];
-    constexpr int kPer = kMaxExperts / kTiledThreads;   // experts per thread
+    constexpr int kPer = kMaxExperts / kThreads;   // experts per thread
     int cnt[kPer];
     int local = 0;
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
-      const int e = tid * kPer + i;
-      cnt[i] = e < E ? tiles_of(offsets[e + 1] - offsets[e], NB) : 0;
+      const int ex = tid * kPer + i;
+      cnt[i] = ex < E ? tiles_of(offsets[ex + 1] - offsets[ex], NB) : 0;
       local += cnt[i];
     }
     int incl = local;
@@ -124,29 +155,41 @@ __global__ __launch_bounds__(kTiledThreads, 1) void gg_tiled_kernel(const uint8_
       const int o = __shfl_up(incl, off, kWave);
       if (lane >= off) incl += o;
     }
-    if (lane == 63) wsum[wave] = incl;
+    if (lane == kWave - 1) wsum[wave] = incl;
     __syncthreads();
-    int base = 0;
-    for (int w = 0; w < wave; ++w) base += wsum[w];
-    int run = base + incl - local;
+    int run = 0;
+    for (int w = 0; w < wave; ++w) run += wsum[w];
+    run += incl - local;
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
-      const int e = tid * kPer + i;
-      if (e < E) tile_start[e] = run;
+      const int ex = tid * kPer + i;
+      if (ex < E) tile_start[ex] = run;
       run += cnt[i];
     }
-    if (tid == kTiledThreads - 1) tile_start[E] = run;   // the grand total
+    if (tid == kThreads - 1) tile_start[E] = run;   // the grand total
     __syncthreads();
   }
   const int total = tile_start[E];
 
+  // lane-constant parts of the swizzled LDS addresses
+  const int fa = (i32 >> 1) & 7;                  // activation swizzle of rows 32b + i32
+  const int fw = (i32 >> 2) & 3;                  // weight swizzle of columns 32cg + i32
+  const uint32_t a_rd0 = (uint32_t)i32 * kGroup + 16u * (uint32_t)((2 * kh) ^ fa);       // half 0, K bytes 32kh..+15
+  const uint32_t a_rd1 = (uint32_t)i32 * kGroup + 16u * (uint32_t)((2 * kh + 1) ^ fa);   // half 0, +16..+31
+  const uint32_t a_rd2 = (uint32_t)i32 * kGroup + 16u * (uint32_t)((4 + 2 * kh) ^ fa);   // half 1
+  const uint32_t a_rd3 = (uint32_t)i32 * kGroup + 16u * (uint32_t)((5 + 2 * kh) ^ fa);
+  const uint32_t w_rd0 = (uint32_t)(32 * kNJ * cg + i32) * 64u + 16u * (uint32_t)(kh ^ fw);         // half 0
+  const uint32_t w_rd1 = (uint32_t)(32 * kNJ * cg + i32) * 64u + 16u * (uint32_t)((2 + kh) ^ fw);   // half 1
+  // the row-sum MFMAs of this wave's rows (16x16x128 layout: row lane % 16, K bytes 32 (lane / 16) ..)
+  const int bl = lane & 15, bq = lane >> 4;
+  const int fb = (bl >> 1) & 7;
+  const uint32_t b_rd0 = (uint32_t)(kARows * wave + bl) * kGroup + 16u * (uint32_t)((2 * bq) ^ fb);
+  const uint32_t b_rd1 = (uint32_t)(kARows * wave + bl) * kGroup + 16u * (uint32_t)((2 * bq + 1) ^ fb);
+
   // Tile t runs on the XCD and in the round that keep data sharing local:
   // workgroups are dispatched round-robin over the XCDs, so workgroup w sits
   // on XCD w % X.  Each round hands the X XCDs consecutive windows of grid/X
-  // tiles; tiles are numbered expert by expert, N block by N block, with the
-  // M blocks of one N block adjacent, so a window (the tiles one XCD runs at
-  // the same time) shares its weight tiles and activation blocks in that
-  // XCD's L2.
+  // tiles.
   const int grid = gridDim.x;
   const bool xcd_windows = (grid % kXcds) == 0;
   const int window = grid / kXcds;
@@ -160,154 +203,188 @@ __global__ __launch_bounds__(kTiledThreads, 1) void gg_tiled_kernel(const uint8_
     }
     const int e = lo_e;
     const int r_e = offsets[e], rows_e = offsets[e + 1] - r_e;
-    const int mbs = (rows_e + kTileM - 1) / kTileM;
+    const int mbs = (rows_e + kTM - 1) / kTM;
     const int local = t - tile_start[e];
     const int mb = local % mbs;
     const int nb = local / mbs;
-    const int r0 = r_e + mb * kTileM;
-    const int mlen = min(kTileM, rows_e - mb * kTileM);
-    const int nsub = (mlen + 15) >> 4;
-    const int n0 = nb * kTileN + wave * 64;
-    const bool active = n0 < N;
+    const int r0 = r_e + mb * kTM;
+    const int mlen = min(kTM, rows_e - mb * kTM);
+    const int n0 = nb * kTN;
+    const bool active = n0 + 32 * kNJ * cg < N;   // N % 64 == 0: a wave's column group is wholly in or out
 
-    // activation bytes this lane stages: row subtiles 2*wave, 2*wave+1, row lane % 16,
-    // quarter lane / 16 of each group
+    // ---- direct-load roles of this lane
+    // activations: rows kARows wave + 8 q + lane / 8, chunk position lane % 8
     const __amdgpu_buffer_rsrc_t ra = buffer_rsrc(a, 0xffffffffu);
-    uint32_t aoff[2];
+    uint32_t aoff[kARows / 8];
 #pragma unroll
-    for (int i2 = 0; i2 < 2; ++i2) {
-      const int rl = min(16 * (2 * wave + i2) + col, mlen - 1);
-      const int p = r0 + rl;
-      aoff[i2] = (uint32_t)(a_rows ? a_rows[p] : p) * (uint32_t)K + (uint32_t)(kq * 32);
+    for (int q = 0; q < kARows / 8; ++q) {
+      const int r = kARows * wave + 8 * q + (lane >> 3);
+      const int p = r0 + min(r, mlen - 1);
+      const int c = (lane & 7) ^ ((r >> 1) & 7);
+      aoff[q] = (uint32_t)(a_rows ? a_rows[p] : p) * (uint32_t)K + 16u * (uint32_t)c;
     }
-    // weights of this wave: expert e, columns n0 + 16j + col, quarter kq of each group
+    // weights: columns kWCols wave + 16 q + lane / 4 of the tile, chunk position lane % 4
     const __amdgpu_buffer_rsrc_t rw =
         buffer_rsrc(reinterpret_cast<const uint8_t*>(w_packed) + (int64_t)e * N * row_bytes, (uint32_t)N * row_bytes);
+    uint32_t woff[kWCols / 16];
+#pragma unroll
+    for (int q = 0; q < kWCols / 16; ++q) {
+      const int n = kWCols * wave + 16 * q + (lane >> 2);
+      const int c = (lane & 3) ^ ((n >> 2) & 3);
+      woff[q] = (uint32_t)min(n0 + n, (int)N - 1) * row_bytes + 16u * (uint32_t)c;
+    }
+    // scales (waves 0..3): column 64 wave + lane of the tile
     const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(w_scale + (int64_t)e * N * G, (uint32_t)(N * G * 4));
-    const int nw = active ? n0 : 0;   // a wave past the last column block loads (and ignores) block 0
-    const uint32_t woff = (uint32_t)(nw + col) * row_bytes + kq * 16;
-    const uint32_t soff = (uint32_t)(nw + lane) * (uint32_t)G * 4u;   // this lane's column for the scales
+    const uint32_t soff = (uint32_t)min(n0 + 64 * (wave & 3) + lane, (int)N - 1) * (uint32_t)G * 4u;
+    const bool scale_loader = wave < 4;
 
-    // Stage group g into slot S: 4 activation loads, 4 weight loads and 1 scale
-    // load per wave (a wave past the last column block loads column block 0,
-    // so that every wave has the same 9 loads in flight).
+    // loads of group g into slot S (and, on every fourth group, the scale quad of groups g .. g+3)
     auto stage = [&](auto S_, int g) {
-      RingSlot& sl = slot<decltype(S_)::value>(ring0, ring1, ring2, ring3);
+      RingSlot& sl = slot<decltype(S_)::value>(ring0, ring1, ring2);
 #pragma unroll
-      for (int i2 = 0; i2 < 2; ++i2)
+      for (int q = 0; q < kARows / 8; ++q)
+        dma16(ra, aoff[q], (uint32_t)g * kGroup, &sl.a[(kARows * wave + 8 * q) * kGroup]);
 #pragma unroll
-        for (int half = 0; half < 2; ++half)
-          dma16(ra, aoff[i2], (uint32_t)(g * kGroup + half * 16), &sl.a[2 * wave + i2][half][0][0]);
+      for (int q = 0; q < kWCols / 16; ++q) dma16(rw, woff[q], (uint32_t)g * 64u, &sl.w[(kWCols * wave + 16 * q) * 64]);
+      if (scale_loader && (g & 3) == 0) {
+        float* dst = &scq[(g >> 2) & 1][0];
+        if (vec_scales) {
+          dma16(rs, soff, (uint32_t)g * 4u, dst + 256 * wave);
+        } else {
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        dma16(rw, woff, (uint32_t)(16 * j) * row_bytes + (uint32_t)(g * 64), &sl.w[wave][j][0][0]);
-      dma4(rs, soff, (uint32_t)g * 4u, &sl.sc[wave][0]);
-    };
-    // group sums of this wave's two row subtiles for the group in slot S -> bias_sm[S]
-    auto row_sums = [&](auto S_) {
-      constexpr int S = decltype(S_)::value;
-      RingSlot& sl = slot<S>(ring0, ring1, ring2, ring3);
-      const v8i kb = bias_operand();
-#pragma unroll
-      for (int i2 = 0; i2 < 2; ++i2) {
-        const int i = 2 * wave + i2;
-        if (i < nsub) {
-          const uint8_t* ap = &sl.a[i][0][lane][0];
-          const i32x4 x0 = lds_load<i32x4>(ap);
-          const i32x4 x1 = lds_load<i32x4>(ap + 1024);
-          const v8i av = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
-          const v4f c = mfma16x16x128(av, kb, v4f{0.f, 0.f, 0.f, 0.f});
-          if (col == 0) *reinterpret_cast<v4f*>(&bias_sm[S][16 * i + 4 * kq]) = c;
+          for (int j = 0; j < 4; ++j) dma4(rs, soff, (uint32_t)(g + j) * 4u, dst + kTN * j + 64 * wave);
         }
       }
     };
-
-    v4f acc[8][4];
+    // loads that stage(g) issues on this wave
+    auto stage_loads = [&](int g) {
+      return kStageLoads + ((scale_loader && (g & 3) == 0) ? (vec_scales ? 1 : 4) : 0);
+    };
+    // -2^-6 * (sum of the activation codes) of this wave's rows for the group in slot S
+    auto row_sums = [&](auto S_, int g) {
+      const RingSlot& sl = slot<decltype(S_)::value>(ring0, ring1, ring2);
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+      for (int q = 0; q < kARows / 16; ++q) {
+        const i32x4 x0 = lds_load<i32x4>(&sl.a[b_rd0 + q * 16 * kGroup]);
+        const i32x4 x1 = lds_load<i32x4>(&sl.a[b_rd1 + q * 16 * kGroup]);
+        const v8i av = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+        const v4f c = mfma16x16x128(av, bias_operand(), v4f{0.f, 0.f, 0.f, 0.f});
+        if (bl == 0) *reinterpret_cast<v4f*>(&bias_sm[g & 1][kARows * wave + 16 * q + 4 * bq]) = c;
+      }
+    };
 
-    // one K group in slot S: prefetch group g+3, share the row sums of group
-    // g+1, multiply group g, then wait until group g+2 has landed
+    v16f acc[kBlocks][kNJ];
+#pragma unroll
+    for (int i = 0; i < kBlocks; ++i)
+#pragma unroll
+      for (int j = 0; j < kNJ; ++j)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+
+    // one K group in slot S: prefetch group g+2, multiply group g, then wait
+    // for this wave's loads of group g+1, publish its row sums, and barrier
     auto step = [&](auto S_, int g) {
       constexpr int S = decltype(S_)::value;
       if (g >= G) return;
-      if (g + 3 < G) stage(std::integral_constant<int, (S + 3) % kStages>{}, g + 3);
-      if (g + 1 < G) row_sums(std::integral_constant<int, (S + 1) % kStages>{});
+      const bool more = g + 2 < G;
+      if (more) stage(std::integral_constant<int, (S + 2) % 3>{}, g + 2);
       if (active) {
-        RingSlot& sl = slot<S>(ring0, ring1, ring2, ring3);
-        const uint8_t* abase = &sl.a[0][0][lane][0];               // + i*2K + half*1K
-        const uint8_t* wbase = &sl.w[wave][0][lane][0];             // + j*1K
-        const float* bbase = &bias_sm[S][4 * kq];                   // + 16i
-        v8i b[4];
-        float s4[4];
+        const RingSlot& sl = slot<S>(ring0, ring1, ring2);
+        v8i b0[kNJ], b1[kNJ];
+        float s[kNJ];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          b[j] = nibbles_to_fp8(lds_load<i32x4>(wbase + j * 1024));
-          s4[j] = sl.sc[wave][16 * j + col];
+        for (int j = 0; j < kNJ; ++j) {
+          b0[j] = nibbles_to_fp8(lds_load<i32x4>(&sl.w[w_rd0 + j * 32 * 64]));
+          b1[j] = nibbles_to_fp8(lds_load<i32x4>(&sl.w[w_rd1 + j * 32 * 64]));
+          const int col = 32 * (kNJ * cg + j) + i32;
+          s[j] = lds_read_f32_self_waiting(
+              &scq[(g >> 2) & 1][vec_scales ? col * 4 + (g & 3) : (g & 3) * kTN + col]);
         }
+        const float* bb = &bias_sm[g & 1][4 * kh];
 #pragma unroll
-        for (int ii = 0; ii < 4; ++ii) {
-          if (2 * ii < nsub) {
+        for (int i = 0; i < kBlocks; ++i) {
+          const int blk = rg + kRowGroups * i;
+          if (32 * blk < mlen) {
+            const uint8_t* ab = &sl.a[blk * 32 * kGroup];
+            const i32x4 x0 = lds_load<i32x4>(ab + a_rd0);
+            const i32x4 x1 = lds_load<i32x4>(ab + a_rd1);
+            const i32x4 x2 = lds_load<i32x4>(ab + a_rd2);
+            const i32x4 x3 = lds_load<i32x4>(ab + a_rd3);
+            const v8i a0 = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+            const v8i a1 = {x2[0], x2[1], x2[2], x2[3], x3[0], x3[1], x3[2], x3[3]};
+            v16f cb;
 #pragma unroll
-            for (int i = 2 * ii; i < 2 * ii + 2; ++i) {
-              const i32x4 x0 = lds_load<i32x4>(abase + i * 2048);
-              const i32x4 x1 = lds_load<i32x4>(abase + i * 2048 + 1024);
-              const v8i av = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
-              const v4f cb = lds_load<v4f>(bbase + 16 * i);
+            for (int q = 0; q < 4; ++q) {
+              const v4f t4 = lds_load<v4f>(bb + 32 * blk + 8 * q);
 #pragma unroll
-              for (int j = 0; j < 4; ++j) {
-                const v4f d = mfma16x16x128(av, b[j], cb);
+              for (int r = 0; r < 4; ++r) cb[4 * q + r] = t4[r];
+            }
 #pragma unroll
-                for (int r = 0; r < 4; ++r) acc[i][j][r] = fmaf(s4[j], d[r], acc[i][j][r]);
-              }
+            for (int j = 0; j < kNJ; ++j) {
+              v16f c = mfma32x32x64(a0, b0[j], cb);
+              c = mfma32x32x64(a1, b1[j], c);
+#pragma unroll
+              for (int v = 0; v < 16; ++v) acc[i][j][v] = fmaf(s[j], c[v], acc[i][j][v]);
             }
           }
         }
       }
-      // this wave's LDS writes done and group g+2 landed (only the 9 loads of
-      // group g+3 may stay in flight), then the other waves' parts
-      if (g + 3 < G) __builtin_amdgcn_s_waitcnt(0x0079);   // vmcnt(9) lgkmcnt(0)
-      else __builtin_amdgcn_s_waitcnt(0);
+      // this wave's loads of group g+1 landed (only those of group g+2 may stay in flight)
+      if (more) {
+        const int n = stage_loads(g + 2);
+        if (n == kStageLoads) __builtin_amdgcn_s_waitcnt(0x0F70 | kStageLoads);
+        else if (n == kStageLoads + 1) __builtin_amdgcn_s_waitcnt(0x0F70 | (kStageLoads + 1));
+        else __builtin_amdgcn_s_waitcnt(0x0F70 | (kStageLoads + 4));
+      } else {
+        __builtin_amdgcn_s_waitcnt(0x0F70);                    // vmcnt(0)
+      }
+      if (g + 1 < G) row_sums(std::integral_constant<int, (S + 1) % 3>{}, g + 1);
+      __builtin_amdgcn_s_waitcnt(0xC07F);                      // lgkmcnt(0): LDS writes done
       barrier_loads_in_flight();
     };
 
-    // prologue: groups 0..2 in flight, group 0 landed and its row sums shared
+    // prologue: groups 0 and 1 in flight, this wave's rows of group 0 landed, their sums published
     stage(std::integral_constant<int, 0>{}, 0);
-    if (G > 1) stage(std::integral_constant<int, 1>{}, 1);
-    if (G > 2) stage(std::integral_constant<int, 2>{}, 2);
-    __builtin_amdgcn_s_waitcnt(0);
+    if (G > 1) {
+      stage(std::integral_constant<int, 1>{}, 1);
+      __builtin_amdgcn_s_waitcnt(0x0F70 | kStageLoads);       // stage(1) has no scale quad
+    } else {
+      __builtin_amdgcn_s_waitcnt(0x0F70);
+    }
+    row_sums(std::integral_constant<int, 0>{}, 0);
+    __builtin_amdgcn_s_waitcnt(0xC07F);
     barrier_loads_in_flight();
-    row_sums(std::integral_constant<int, 0>{});
-    __builtin_amdgcn_s_waitcnt(0);
-    barrier_loads_in_flight();
+    // the token scales of the tile's rows (read in the epilogue; every wave is past the previous epilogue)
+    if (scale_loader) {
+      const int r = 64 * wave + lane;
+      const int p = r0 + min(r, mlen - 1);
+      dma4(buffer_rsrc(a_scale, 0xffffffffu), (uint32_t)(a_rows ? a_rows[p] : p) * 4u, 0, &ascale_sm[64 * wave]);
+    }
 
-    for (int g = 0; g < G; g += kStages) {
+    for (int g = 0; g < G; g += 3) {
       step(std::integral_constant<int, 0>{}, g);
       step(std::integral_constant<int, 1>{}, g + 1);
       step(std::integral_constant<int, 2>{}, g + 2);
-      step(std::integral_constant<int, 3>{}, g + 3);
     }
 
     if (active) {
-      // the lane's first output row; opaque to the optimizer so that the 32
-      // row indices below are formed here rather than kept live in registers
-      // through the whole kernel
-      int row4 = 4 * kq;
-      asm volatile("" : "+v"(row4));
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        if (i < nsub) {
+      for (int i = 0; i < kBlocks; ++i) {
+        const int blk = rg + kRowGroups * i;
+        if (32 * blk < mlen) {
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int rl = 16 * i + row4 + r;
-            if (rl < mlen) {
-              const int p = r0 + rl;
-              const float rs = a_scale[a_rows ? a_rows[p] : p] * kUnitScale;
+          for (int q = 0; q < 4; ++q) {
+            const int rt = 32 * blk + 8 * q + 4 * kh;
+            const v4f sc4 = lds_load<v4f>(&ascale_sm[rt]);
 #pragma unroll
-              for (int j = 0; j < 4; ++j)
-                __builtin_nontemporal_store(acc[i][j][r] * rs, out + (int64_t)p * N + n0 + 16 * j + col);
+            for (int r = 0; r < 4; ++r) {
+              if (rt + r < mlen) {
+                const int64_t p = r0 + rt + r;
+#pragma unroll
+                for (int j = 0; j < kNJ; ++j)
+                  __builtin_nontemporal_store(acc[i][j][4 * q + r] * (sc4[r] * kUnitScale),
+                                              out + p * N + n0 + 32 * (kNJ * cg + j) + i32);
+              }
             }
           }
         }
@@ -334,7 +411,8 @@ hipError_t launch_gg_tiled(const GemmArgs& g, hipStream_t stream) {
   constexpr int64_t k4G = (int64_t)1 << 32;
   if (g.M_total * g.K >= k4G || g.N * (g.K / 2) >= k4G || g.N * (g.K / 128) * 4 >= k4G)
     return launch_gg_stream(g, stream);
-  hipLaunchKernelGGL(gg_tiled_kernel, dim3(cu_count()), dim3(kTiledThreads), 0, stream, g.a, g.a_scale,
+  constexpr int kW = GG_TILED_WAVES, kJ = GG_TILED_NJ;
+  hipLaunchKernelGGL((gg_tiled_kernel<kW, kJ>), dim3(cu_count()), dim3(kW * kWave), 0, stream, g.a, g.a_scale,
                      g.a_rows, g.offsets, g.E, g.w_packed, g.w_scale, g.N, g.K, g.out);
   return hipGetLastError();
 }
