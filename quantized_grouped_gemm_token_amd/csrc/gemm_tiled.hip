@@ -1,13 +1,13 @@
 // Grouped W4A8 GEMM, tiled form: for many rows per expert (prefill).
 //
-// A persistent kernel (one 1024-thread workgroup per CU, four waves per
-// SIMD) walks the ragged list of tiles of all experts.  A tile is up to 256
-// rows of one expert by 256 output columns.  Wave w = 8 rg + cg owns the 32
-// columns 32 cg .. 32 cg + 31 and the 32-row blocks rg, rg + 2, rg + 4, rg + 6
+// A persistent kernel (one workgroup of kWaves waves per CU) walks the ragged
+// list of tiles of all experts.  A tile is up to 256 rows of one expert by
+// 256 output columns.  With 8 waves (two per SIMD, so that the matrix core
+// runs while the other wave does the per-group scale FMAs and the nibble
+// unpacking), wave w = 4 rg + cg owns the 64 columns 64 cg .. 64 cg + 63 and
+// the 32-row blocks rg, rg + 2, rg + 4, rg + 6
 // (interleaved, so that a short tile still splits its rows over both row
-// groups).  Its outputs are four 32x32 MFMA tiles, 64 fp32 accumulators per
-// lane.  Four waves per SIMD are what lets the matrix core run while other
-// waves do the per-group scale FMAs and the nibble unpacking.
+// groups).
 //
 // K is walked one 128-wide group at a time through a 3-slot LDS ring filled
 // by direct global-to-LDS loads, two groups ahead.  Per group a slot holds
@@ -20,11 +20,11 @@
 // The group scales of 4 groups are loaded at once (16 bytes per column).
 //
 // The +8 offset of the uint4b8 nibbles is removed with the per-row sums of
-// the activation codes of each group (see gemm_common.hpp): wave w loads
-// exactly the 16 activation rows whose sums it computes, with one 16x16x128
-// MFMA against the constant -2^-6, so the sums of group g + 1 are ready as
-// soon as the wave's own loads have landed and are published by the one
-// barrier per group.
+// the activation codes of each group (see gemm_common.hpp): each wave loads
+// exactly the activation rows whose sums it computes, with 16x16x128 MFMAs
+// against the constant -2^-6, so the sums of group g + 1 are computed in the
+// middle of group g's products, as soon as the wave's own loads of g + 1 have
+// landed, and are published by the one barrier per group.
 //
 // Tile order: each XCD runs windows of consecutive tiles (an expert's tiles
 // are numbered N block by N block, M blocks adjacent) at the same time, so a
@@ -43,6 +43,7 @@ constexpr int kXcds = 8;              // accelerator complex dies of an MI355X (
 #define GG_TILED_WAVES 8                // waves per workgroup
 #define GG_TILED_NJ 2                   // 32-column blocks per wave
 #endif
+
 
 // One ring slot: the activation rows and the weight columns of one group.
 //   a: row r, 16-byte chunk c (K bytes 16c..16c+15 of the group) at r*128 + 16*(c ^ ((r >> 1) & 7))
@@ -89,17 +90,6 @@ __device__ __forceinline__ T lds_load(const void* p) {
   return *reinterpret_cast<const T*>(__builtin_assume_aligned(p, 16));
 }
 
-// One fp32 LDS read the compiler's wait analysis does not see: the scale
-// quads are filled by direct loads into a buffer whose half being read the
-// compiler cannot tell from the half being filled.  The read waits for
-// itself.
-__device__ __forceinline__ float lds_read_f32_self_waiting(const float* p) {
-  float v;
-  const uint32_t addr = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) float*)p;
-  asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(addr) : "memory");
-  return v;
-}
-
 __device__ __forceinline__ int tiles_of(int rows, int nb) { return ((rows + kTM - 1) / kTM) * nb; }
 
 // kWaves waves per workgroup; each wave owns kNJ blocks of 32 columns.
@@ -124,7 +114,6 @@ __global__ __launch_bounds__(kWaves * kWave, 1) void gg_tiled_kernel(const uint8
   constexpr int kBlocks = (kTM / 32) / kRowGroups;     // 32-row blocks per wave
   constexpr int kARows = kTM / kWaves;                 // activation rows each wave loads (and sums)
   constexpr int kWCols = kTN / kWaves;                 // weight columns each wave loads
-  constexpr int kStageLoads = kARows / 8 + kWCols / 16;
   static_assert(kColGroups * kRowGroups == kWaves && kBlocks * kRowGroups * 32 == kTM, "wave grid");
   static_assert(kARows % 16 == 0 && kWCols % 16 == 0, "load roles");
 
@@ -238,14 +227,10 @@ __global__ __launch_bounds__(kWaves * kWave, 1) void gg_tiled_kernel(const uint8
     const uint32_t soff = (uint32_t)min(n0 + 64 * (wave & 3) + lane, (int)N - 1) * (uint32_t)G * 4u;
     const bool scale_loader = wave < 4;
 
-    // loads of group g into slot S (and, on every fourth group, the scale quad of groups g .. g+3)
+    // loads of group g into slot S (and, on every fourth group, first the scale quad of groups g .. g+3:
+    // issued first, a wait for it leaves the group's other loads in flight)
     auto stage = [&](auto S_, int g) {
       RingSlot& sl = slot<decltype(S_)::value>(ring0, ring1, ring2);
-#pragma unroll
-      for (int q = 0; q < kARows / 8; ++q)
-        dma16(ra, aoff[q], (uint32_t)g * kGroup, &sl.a[(kARows * wave + 8 * q) * kGroup]);
-#pragma unroll
-      for (int q = 0; q < kWCols / 16; ++q) dma16(rw, woff[q], (uint32_t)g * 64u, &sl.w[(kWCols * wave + 16 * q) * 64]);
       if (scale_loader && (g & 3) == 0) {
         float* dst = &scq[(g >> 2) & 1][0];
         if (vec_scales) {
@@ -255,10 +240,23 @@ __global__ __launch_bounds__(kWaves * kWave, 1) void gg_tiled_kernel(const uint8
           for (int j = 0; j < 4; ++j) dma4(rs, soff, (uint32_t)(g + j) * 4u, dst + kTN * j + 64 * wave);
         }
       }
+#pragma unroll
+      for (int q = 0; q < kARows / 8; ++q)
+        dma16(ra, aoff[q], (uint32_t)g * kGroup, &sl.a[(kARows * wave + 8 * q) * kGroup]);
+#pragma unroll
+      for (int q = 0; q < kWCols / 16; ++q) dma16(rw, woff[q], (uint32_t)g * 64u, &sl.w[(kWCols * wave + 16 * q) * 64]);
     };
     // loads that stage(g) issues on this wave
     auto stage_loads = [&](int g) {
-      return kStageLoads + ((scale_loader && (g & 3) == 0) ? (vec_scales ? 1 : 4) : 0);
+      return kARows / 8 + kWCols / 16 + ((scale_loader && (g & 3) == 0) ? (vec_scales ? 1 : 4) : 0);
+    };
+    // wait until at most n of this wave's loads are in flight (n is one of the stage_loads values)
+    auto wait_loads = [&](int n) {
+      constexpr int base = kARows / 8 + kWCols / 16;
+      static_assert(base + 4 <= 15, "vmcnt field");
+      if (n == base) __builtin_amdgcn_s_waitcnt(0x0F70 | base);
+      else if (n == base + 1) __builtin_amdgcn_s_waitcnt(0x0F70 | (base + 1));
+      else __builtin_amdgcn_s_waitcnt(0x0F70 | (base + 4));
     };
     // -2^-6 * (sum of the activation codes) of this wave's rows for the group in slot S
     auto row_sums = [&](auto S_, int g) {
@@ -281,73 +279,80 @@ __global__ __launch_bounds__(kWaves * kWave, 1) void gg_tiled_kernel(const uint8
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
-    // one K group in slot S: prefetch group g+2, multiply group g, then wait
-    // for this wave's loads of group g+1, publish its row sums, and barrier
+    // One K group in slot S: prefetch group g+2; multiply group g; in the
+    // middle, once this wave's loads of group g+1 have landed, publish that
+    // group's row sums; then one barrier.
     auto step = [&](auto S_, int g) {
       constexpr int S = decltype(S_)::value;
       if (g >= G) return;
       const bool more = g + 2 < G;
+      // scales of group g (read before this step's loads are issued: the only
+      // direct load into scq that can be in flight is the next quad's, issued
+      // first in its group, so waiting for it keeps that group's loads going)
+      float s[kNJ];
+#pragma unroll
+      for (int j = 0; j < kNJ; ++j) {
+        const int col = 32 * (kNJ * cg + j) + i32;
+        s[j] = scq[(g >> 2) & 1][vec_scales ? col * 4 + (g & 3) : (g & 3) * kTN + col];
+      }
       if (more) stage(std::integral_constant<int, (S + 2) % 3>{}, g + 2);
+      const RingSlot& sl = slot<S>(ring0, ring1, ring2);
+      v8i b0[kNJ], b1[kNJ];
       if (active) {
-        const RingSlot& sl = slot<S>(ring0, ring1, ring2);
-        v8i b0[kNJ], b1[kNJ];
-        float s[kNJ];
 #pragma unroll
         for (int j = 0; j < kNJ; ++j) {
           b0[j] = nibbles_to_fp8(lds_load<i32x4>(&sl.w[w_rd0 + j * 32 * 64]));
           b1[j] = nibbles_to_fp8(lds_load<i32x4>(&sl.w[w_rd1 + j * 32 * 64]));
-          const int col = 32 * (kNJ * cg + j) + i32;
-          s[j] = lds_read_f32_self_waiting(
-              &scq[(g >> 2) & 1][vec_scales ? col * 4 + (g & 3) : (g & 3) * kTN + col]);
         }
-        const float* bb = &bias_sm[g & 1][4 * kh];
+      }
+      const float* bb = &bias_sm[g & 1][4 * kh];
+      auto block = [&](int i) {
+        const int blk = rg + kRowGroups * i;
+        if (active && 32 * blk < mlen) {
+          const uint8_t* ab = &sl.a[blk * 32 * kGroup];
+          const i32x4 x0 = lds_load<i32x4>(ab + a_rd0);
+          const i32x4 x1 = lds_load<i32x4>(ab + a_rd1);
+          const i32x4 x2 = lds_load<i32x4>(ab + a_rd2);
+          const i32x4 x3 = lds_load<i32x4>(ab + a_rd3);
+          const v8i a0 = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+          const v8i a1 = {x2[0], x2[1], x2[2], x2[3], x3[0], x3[1], x3[2], x3[3]};
 #pragma unroll
-        for (int i = 0; i < kBlocks; ++i) {
-          const int blk = rg + kRowGroups * i;
-          if (32 * blk < mlen) {
-            const uint8_t* ab = &sl.a[blk * 32 * kGroup];
-            const i32x4 x0 = lds_load<i32x4>(ab + a_rd0);
-            const i32x4 x1 = lds_load<i32x4>(ab + a_rd1);
-            const i32x4 x2 = lds_load<i32x4>(ab + a_rd2);
-            const i32x4 x3 = lds_load<i32x4>(ab + a_rd3);
-            const v8i a0 = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
-            const v8i a1 = {x2[0], x2[1], x2[2], x2[3], x3[0], x3[1], x3[2], x3[3]};
-            v16f cb;
+          for (int j = 0; j < kNJ; ++j) {
+            v16f c;   // the row sums enter as the accumulator input (read per column block: no copies)
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
               const v4f t4 = lds_load<v4f>(bb + 32 * blk + 8 * q);
 #pragma unroll
-              for (int r = 0; r < 4; ++r) cb[4 * q + r] = t4[r];
+              for (int r = 0; r < 4; ++r) c[4 * q + r] = t4[r];
             }
+            c = mfma32x32x64(a0, b0[j], c);
+            c = mfma32x32x64(a1, b1[j], c);
 #pragma unroll
-            for (int j = 0; j < kNJ; ++j) {
-              v16f c = mfma32x32x64(a0, b0[j], cb);
-              c = mfma32x32x64(a1, b1[j], c);
-#pragma unroll
-              for (int v = 0; v < 16; ++v) acc[i][j][v] = fmaf(s[j], c[v], acc[i][j][v]);
-            }
+            for (int v = 0; v < 16; ++v) acc[i][j][v] = fmaf(s[j], c[v], acc[i][j][v]);
           }
         }
-      }
+      };
+#pragma unroll
+      for (int i = 0; i < kBlocks / 2; ++i) block(i);
       // this wave's loads of group g+1 landed (only those of group g+2 may stay in flight)
       if (more) {
-        const int n = stage_loads(g + 2);
-        if (n == kStageLoads) __builtin_amdgcn_s_waitcnt(0x0F70 | kStageLoads);
-        else if (n == kStageLoads + 1) __builtin_amdgcn_s_waitcnt(0x0F70 | (kStageLoads + 1));
-        else __builtin_amdgcn_s_waitcnt(0x0F70 | (kStageLoads + 4));
+        wait_loads(stage_loads(g + 2));
       } else {
         __builtin_amdgcn_s_waitcnt(0x0F70);                    // vmcnt(0)
       }
       if (g + 1 < G) row_sums(std::integral_constant<int, (S + 1) % 3>{}, g + 1);
+#pragma unroll
+      for (int i = kBlocks / 2; i < kBlocks; ++i) block(i);
       __builtin_amdgcn_s_waitcnt(0xC07F);                      // lgkmcnt(0): LDS writes done
       barrier_loads_in_flight();
     };
 
     // prologue: groups 0 and 1 in flight, this wave's rows of group 0 landed, their sums published
+    // (and the scale quad of groups 0..3, read after the barrier)
     stage(std::integral_constant<int, 0>{}, 0);
     if (G > 1) {
       stage(std::integral_constant<int, 1>{}, 1);
-      __builtin_amdgcn_s_waitcnt(0x0F70 | kStageLoads);       // stage(1) has no scale quad
+      wait_loads(stage_loads(1));
     } else {
       __builtin_amdgcn_s_waitcnt(0x0F70);
     }
