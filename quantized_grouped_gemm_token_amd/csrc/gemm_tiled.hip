@@ -332,15 +332,16 @@ __global__ __launch_bounds__(kWaves * kWave, 1) void gg_tiled_kernel(const uint8
           }
         }
       };
+      // this wave's loads of group g+1 landed (only those of group g+2 may stay in
+      // flight); then the row sums of group g+1
+      auto mid = [&]() {
+        if (more) wait_loads(stage_loads(g + 2));
+        else __builtin_amdgcn_s_waitcnt(0x0F70);              // vmcnt(0)
+        if (g + 1 < G) row_sums(std::integral_constant<int, (S + 1) % 3>{}, g + 1);
+      };
 #pragma unroll
       for (int i = 0; i < kBlocks / 2; ++i) block(i);
-      // this wave's loads of group g+1 landed (only those of group g+2 may stay in flight)
-      if (more) {
-        wait_loads(stage_loads(g + 2));
-      } else {
-        __builtin_amdgcn_s_waitcnt(0x0F70);                    // vmcnt(0)
-      }
-      if (g + 1 < G) row_sums(std::integral_constant<int, (S + 1) % 3>{}, g + 1);
+      mid();
 #pragma unroll
       for (int i = kBlocks / 2; i < kBlocks; ++i) block(i);
       __builtin_amdgcn_s_waitcnt(0xC07F);                      // lgkmcnt(0): LDS writes done
