@@ -87,6 +87,62 @@ def cpu_baseline(wl, n_tokens: int) -> dict:
                       f"'{wl.shape.name}', touching {touched} experts; {dt:.1f} s wall"}
 
 
+def bench_wquant(args, log) -> int:
+    """The weight quantizer on the gate/up weights of 16 experts (fp32 [16, 4096, 6144])."""
+    import torch
+
+    from quantized_grouped_gemm_token_amd import ops
+
+    E, N, K = 16, 4096, 6144
+    gen = torch.Generator(device="cuda:0").manual_seed(1234)
+    w = torch.randn((E, N, K), generator=gen, device="cuda:0", dtype=torch.float32) * 0.02
+    packed = torch.empty((E, N, K // 8), dtype=torch.int32, device="cuda:0")
+    scales = torch.empty((E, N, K // 128), dtype=torch.float32, device="cuda:0")
+    for _ in range(max(args.warmup, 1)):
+        ops.w4a8_moe_quantize_weights(w, True, packed, scales)
+    stream = torch.cuda.current_stream()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        ops.w4a8_moe_quantize_weights(w, True, packed, scales)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / args.steps
+    in_bytes = w.numel() * 4
+    moved = in_bytes + packed.numel() * 4 + scales.numel() * 4
+    log(f"quantize {E}x{N}x{K}: {ms:.3f} ms")
+    cpu = None
+    if args.cpu_tokens > 0:
+        import oracle
+        try:
+            from threadpoolctl import threadpool_limits
+            limit = threadpool_limits(limits=1)
+        except Exception:   # pragma: no cover
+            limit = None
+        rows = 256
+        sample = w[0, :rows].cpu().numpy()
+        t0 = time.perf_counter()
+        oracle.quantize_int4_g128(sample)
+        dt = time.perf_counter() - t0
+        if limit is not None:
+            limit.restore_original_limits()
+        cpu = {"value": round(rows * K * 4 / dt / 1e9, 4), "unit": "GB/s of fp32 weights", "cores": 1,
+               "kind": "oracle", "sample": f"oracle quantizer on {rows} rows x {K} of the same weights; "
+                                           f"{dt:.1f} s wall"}
+    line = {"metric": "INT4 g128 weight quantizer (11-ratio MSE clip) GB/s of fp32 weights", "value":
+            round(in_bytes / ms / 1e6, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+            "dtype": "f32 in, int4 + f32 scales out (fp64 decisions)", "data": "synthetic (seeded N(0, 0.02))",
+            "config": {"workload": f"gate/up weights of {E} experts [{E}, {N}, {K}]"},
+            "roofline": {"bound": "alu", "achieved": round(moved / ms / 1e6, 1), "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": round(moved / ms / 1e6 / HBM_PEAK_GBS, 4), "traffic": None,
+                         "note": "fraction of HBM peak; the kernel spends its time on the fp64 decisions"},
+            "cpu_baseline": cpu}
+    print(json.dumps(line), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -96,6 +152,8 @@ def main() -> int:
                                                           "2 decode T=256, 3 prefill T=8192, 4 skewed T=16384")
     ap.add_argument("--cpu-tokens", type=int, default=16, help="tokens in the CPU oracle sample (0: skip)")
     ap.add_argument("--quiet", action="store_true")
+    ap.add_argument("--op", choices=("layer", "wquant"), default="layer",
+                    help="layer: the MoE layer (default); wquant: the offline INT4 weight quantizer")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="instead of the layer, run a plain device copy of this many bytes (5 times): the "
                          "reference for scaling HBM byte counters")
@@ -129,6 +187,8 @@ def main() -> int:
     if not ops.w4a8_moe_device_supported():
         print("bench.py: cuda:0 is not a gfx950: " + ops.last_error(), file=sys.stderr)
         return 1
+    if args.op == "wquant":
+        return bench_wquant(args, log)
     dev = "cuda:0"
     t0 = time.time()
     wl = workloads.make_config(args.config)

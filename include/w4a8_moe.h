@@ -172,6 +172,26 @@ int w4a8_moe_swiglu(const float* h, int64_t M, int64_t I, uint8_t* qa, float* sa
 int w4a8_moe_unpermute(const float* o, const int32_t* inv_pos, const float* w,
                        int64_t T, int32_t k, int64_t H, void* y, int32_t y_dtype, void* stream);
 
+/*
+ * Offline step before the layer -- quantize expert weights to the layer's
+ * INT4 format.  ("GLM-5.3-W4A8" card, section 量化方式: float32 weights,
+ * symmetric INT4 with group size 128 along K, each group's scale chosen by the
+ * smallest squared error over 11 shrink ratios 1.00, 0.97, ..., 0.70, packed
+ * as compressed-tensors uint4b8 in int32.)
+ *   For every row n and group g of 128 weights:
+ *     amax = max |w| over the group (1 if it is all zero);
+ *     s_r = fl32(r * amax / 7);  q_r = clamp(round-half-even(w / s_r), -8, 7)
+ *     (the exact quotient rounded);  with mse_clip the group keeps the r of
+ *     smallest sum (w - q_r s_r)^2 (fp64 sums; the larger r on ties), without
+ *     it r = 1 (plain round-to-nearest).
+ *   w        : fp32 [rows][K] (rows = experts x output channels), 8-byte aligned.
+ *   w_packed : int32 [rows][K/8]: nibble k at bits 4 (k mod 8) of word k/8, holding q + 8.
+ *   w_scale  : fp32 [rows][K/128].
+ *   Rules    : rows >= 0, K > 0, K % 128 == 0.  Inputs must be finite.
+ */
+int w4a8_moe_quantize_weights(const float* w, int64_t rows, int64_t K, int32_t mse_clip,
+                              int32_t* w_packed, float* w_scale, void* stream);
+
 /* Static name of a status code ("W4A8_OK", ...). */
 const char* w4a8_moe_status_string(int status);
 

@@ -195,6 +195,22 @@ int w4a8_moe_swiglu(const float* h, int64_t M, int64_t I, uint8_t* qa, float* sa
   return launched(w4a8::launch_swiglu(h, M, I, qa, sa, as_stream(stream)), "swiglu");
 }
 
+int w4a8_moe_quantize_weights(const float* w, int64_t rows, int64_t K, int32_t mse_clip, int32_t* w_packed,
+                              float* w_scale, void* stream) {
+  if (rows < 0 || rows >= kMaxRows) return fail(W4A8_ERR_SHAPE, "quantize_weights: rows=%lld out of range",
+                                                (long long)rows);
+  if (K <= 0 || K % 128) return fail(W4A8_ERR_SHAPE, "quantize_weights: K=%lld must be a positive multiple of 128",
+                                     (long long)K);
+  if (rows == 0) return ok();
+  if (!w || !w_packed || !w_scale) return fail(W4A8_ERR_NULL, "quantize_weights: null pointer");
+  if (!aligned(w, 8) || !aligned(w_packed, 4) || !aligned(w_scale, 4))
+    return fail(W4A8_ERR_ALIGN, "quantize_weights: w must be 8-byte aligned, w_packed and w_scale 4-byte");
+  if (int st = check_device()) return st;
+  (void)hipGetLastError();
+  return launched(w4a8::launch_wquant(w, rows, K, mse_clip ? 1 : 0, w_packed, w_scale, as_stream(stream)),
+                  "quantize_weights");
+}
+
 int w4a8_moe_unpermute(const float* o, const int32_t* inv_pos, const float* w, int64_t T, int32_t k, int64_t H,
                        void* y, int32_t y_dtype, void* stream) {
   if (T < 0 || T >= kMaxRows) return fail(W4A8_ERR_SHAPE, "unpermute: T=%lld out of range", (long long)T);

@@ -31,6 +31,8 @@ hipError_t launch_permute(const int32_t* ids, int64_t R, int k, int E, int32_t* 
 hipError_t launch_gg_stream(const GemmArgs& g, hipStream_t stream);
 hipError_t launch_gg_tiled(const GemmArgs& g, hipStream_t stream);
 hipError_t launch_swiglu(const float* h, int64_t M, int64_t I, uint8_t* q, float* s, hipStream_t stream);
+hipError_t launch_wquant(const float* w, int64_t rows, int64_t K, int mse_clip, int32_t* packed, float* scales,
+                         hipStream_t stream);
 hipError_t launch_unpermute(const float* o, const int32_t* inv_pos, const float* w, int64_t T, int k, int64_t H,
                             void* y, int bf16_out, hipStream_t stream);
 

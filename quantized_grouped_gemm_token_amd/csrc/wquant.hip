@@ -1,0 +1,93 @@
+// Weight quantizer: the offline step that produces the layer's expert weights.
+//
+// "GLM-5.3-W4A8" card, section 量化方式: after the FP8 blocks are dequantized
+// to float32, every routed-expert weight is quantized to symmetric INT4 with
+// group size 128 along K; each group's scale is the one, among 11 shrink
+// ratios from 1.00 down to 0.70, whose reconstruction has the smallest squared
+// error; the result is packed as uint4b8 nibbles (q + 8) in int32 words.
+//
+// Per group:  amax = max |w| (1 if the group is all zero);
+//             s_r  = fl32(r * amax / 7) for r = 1.00, 0.97, ..., 0.70;
+//             q_r  = clamp(round-half-even(w / s_r), -8, 7);
+//             keep the r with the smallest sum (w - q_r s_r)^2, the larger r on ties.
+// The quotient is rounded as the exact value would be, and the squared
+// errors are summed in fp64, so the choice does not depend on fp32 rounding.
+//
+// One wave per group: lane l holds weights 2l and 2l+1 (one 8-byte load), and
+// writes byte l of the group's 64 packed bytes (low nibble k = 2l, high nibble
+// k = 2l + 1), which is exactly the int32 word layout (nibble k at bits
+// 4 (k mod 8) of word k / 8, little-endian).
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace w4a8 {
+
+constexpr int kShrinkCount = 11;
+__constant__ double kShrink[kShrinkCount] = {1.00, 0.97, 0.94, 0.91, 0.88, 0.85, 0.82, 0.79, 0.76, 0.73, 0.70};
+
+// round(w / s) to the nearest integer, ties to even, as the exact quotient
+// rounds.  The fp32 quotient is within one of that integer; w - (q +- 1/2) s
+// is exact in fp64 whenever it is near zero (q +- 1/2 has 5 significant bits
+// and s 24, so the product is exact, and w is then within a factor of two of
+// it), so its sign decides the neighbouring integer exactly.
+__device__ __forceinline__ float rne_quotient(float w, float s) {
+  float q = rintf(w / s);
+  const double wd = w, sd = s;
+  const double above = wd - ((double)q + 0.5) * sd;   // > 0: the quotient exceeds q + 1/2
+  if (above > 0.0 || (above == 0.0 && (((int)q) & 1))) return q + 1.0f;
+  const double below = wd - ((double)q - 0.5) * sd;   // < 0: the quotient is under q - 1/2
+  if (below < 0.0 || (below == 0.0 && (((int)q) & 1))) return q - 1.0f;
+  return q;
+}
+
+__device__ __forceinline__ double wave_sum_f64(double v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, kWave);
+  return v;
+}
+
+__global__ __launch_bounds__(256) void wquant_kernel(const float* __restrict__ w, int64_t groups, int G,
+                                                     int mse_clip, uint8_t* __restrict__ packed,
+                                                     float* __restrict__ scales) {
+  const int lane = threadIdx.x & 63;
+  const int64_t waves = (int64_t)gridDim.x * (blockDim.x >> 6);
+  for (int64_t gi = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6); gi < groups; gi += waves) {
+    // group gi = (row gi / G, group gi % G): its 128 weights are contiguous
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
+    const f32x2 v = __builtin_nontemporal_load(reinterpret_cast<const f32x2*>(w + gi * kGroup) + lane);
+    float amax = wave_max(fmaxf(fabsf(v.x), fabsf(v.y)));
+    if (amax == 0.0f) amax = 1.0f;
+    double best_err = 0.0;
+    float best_s = 0.0f;
+    const int nr = mse_clip ? kShrinkCount : 1;
+    for (int i = 0; i < nr; ++i) {
+      const float s = (float)(kShrink[i] * (double)amax / 7.0);
+      const float q0 = fminf(fmaxf(rne_quotient(v.x, s), -8.0f), 7.0f);
+      const float q1 = fminf(fmaxf(rne_quotient(v.y, s), -8.0f), 7.0f);
+      const double e0 = (double)v.x - (double)q0 * (double)s;
+      const double e1 = (double)v.y - (double)q1 * (double)s;
+      const double err = wave_sum_f64(e0 * e0 + e1 * e1);
+      if (i == 0 || err < best_err) {   // wave-uniform: every lane holds the same sum
+        best_err = err;
+        best_s = s;
+      }
+    }
+    const int u0 = (int)fminf(fmaxf(rne_quotient(v.x, best_s), -8.0f), 7.0f) + 8;
+    const int u1 = (int)fminf(fmaxf(rne_quotient(v.y, best_s), -8.0f), 7.0f) + 8;
+    packed[gi * (kGroup / 2) + lane] = (uint8_t)(u0 | (u1 << 4));
+    if (lane == 0) scales[gi] = best_s;
+  }
+}
+
+hipError_t launch_wquant(const float* w, int64_t rows, int64_t K, int mse_clip, int32_t* packed, float* scales,
+                         hipStream_t stream) {
+  const int G = (int)(K / kGroup);
+  const int64_t groups = rows * G;
+  if (groups == 0) return hipSuccess;
+  const int64_t blocks = std::min<int64_t>((groups + 3) / 4, 65536);
+  hipLaunchKernelGGL(wquant_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, w, groups, G, mse_clip,
+                     reinterpret_cast<uint8_t*>(packed), scales);
+  return hipGetLastError();
+}
+
+}  // namespace w4a8

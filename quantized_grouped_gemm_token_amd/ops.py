@@ -39,6 +39,7 @@ _SIGNATURES = {
                                                   _c_p, _i32, _c_p]),
     "w4a8_moe_swiglu": (ctypes.c_int, [_c_p, _i64, _i64, _c_p, _c_p, _c_p]),
     "w4a8_moe_unpermute": (ctypes.c_int, [_c_p, _c_p, _c_p, _i64, _i32, _i64, _c_p, _i32, _c_p]),
+    "w4a8_moe_quantize_weights": (ctypes.c_int, [_c_p, _i64, _i64, _i32, _c_p, _c_p, _c_p]),
     "w4a8_moe_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "w4a8_moe_last_error": (ctypes.c_char_p, []),
     "w4a8_moe_device_supported": (ctypes.c_int, []),
@@ -241,3 +242,31 @@ def w4a8_moe_unpermute(o: torch.Tensor, inv_pos: torch.Tensor, w: torch.Tensor,
     _check("w4a8_moe_unpermute", lib().w4a8_moe_unpermute(_p(o), _p(inv_pos), _p(w), T, k, H, _p(y), code,
                                                           _stream(dev)))
     return y
+
+
+def w4a8_moe_quantize_weights(w: torch.Tensor, mse_clip: bool = True, w_packed: torch.Tensor | None = None,
+                              w_scale: torch.Tensor | None = None):
+    """fp32 [..., K] -> (packed int32 [..., K/8], group scales fp32 [..., K/128]).
+
+    Every leading dimension is flattened into rows (experts x output channels)."""
+    if not isinstance(w, torch.Tensor) or w.dim() < 1:
+        raise TypeError("w must be a torch.Tensor with a K dimension")
+    _need(w, "w", torch.float32, w.dim())
+    K = w.shape[-1]
+    lead = tuple(w.shape[:-1])
+    rows = 1
+    for d in lead:
+        rows *= int(d)
+    dev = w.device
+    if K % 128:
+        raise ValueError("K must be a multiple of 128")
+    w_packed = torch.empty(lead + (K // 8,), dtype=torch.int32, device=dev) if w_packed is None else w_packed
+    w_scale = torch.empty(lead + (K // 128,), dtype=torch.float32, device=dev) if w_scale is None else w_scale
+    _need(w_packed, "w_packed", torch.int32, len(lead) + 1, dev)
+    _need(w_scale, "w_scale", torch.float32, len(lead) + 1, dev)
+    if tuple(w_packed.shape) != lead + (K // 8,) or tuple(w_scale.shape) != lead + (K // 128,):
+        raise ValueError("w_packed must be [..., K/8] and w_scale [..., K/128]")
+    _check("w4a8_moe_quantize_weights",
+           lib().w4a8_moe_quantize_weights(_p(w), rows, K, 1 if mse_clip else 0, _p(w_packed), _p(w_scale),
+                                           _stream(dev)))
+    return w_packed, w_scale

@@ -128,6 +128,16 @@ def test_swiglu_unpermute_checks(L):
     assert u(None, None, None, 0, 2, 256, None, 0, None) == OK
 
 
+def test_quantize_weights_checks(L):
+    q = L.w4a8_moe_quantize_weights
+    assert q(P, 4, 100, 1, P, P, None) == ERR_SHAPE             # K % 128
+    assert q(P, -1, 128, 1, P, P, None) == ERR_SHAPE
+    assert q(None, 4, 128, 1, P, P, None) == ERR_NULL
+    assert q(P + 4, 4, 128, 1, P, P, None) == ERR_ALIGN         # w not 8-byte aligned
+    assert q(P, 4, 128, 1, P + 2, P, None) == ERR_ALIGN
+    assert q(None, 0, 128, 1, None, None, None) == OK
+
+
 def test_valid_calls_report_missing_device(L, no_device):
     if not no_device:
         pytest.skip("a supported GPU is present; these fake pointers must not reach it")
@@ -138,6 +148,7 @@ def test_valid_calls_report_missing_device(L, no_device):
     assert L.w4a8_moe_grouped_gemm(P, P, None, 8, P, 8, P, P, 256, 256, P, None) == ERR_DEVICE
     assert L.w4a8_moe_swiglu(P, 4, 128, P, P, None) == ERR_DEVICE
     assert L.w4a8_moe_unpermute(P, P, P, 4, 2, 256, P, 0, None) == ERR_DEVICE
+    assert L.w4a8_moe_quantize_weights(P, 4, 256, 1, P, P, None) == ERR_DEVICE
     assert L.w4a8_moe_device_supported() == 0
 
 
