@@ -250,7 +250,7 @@ static void launch_variant(const GemmArgs& g, hipStream_t stream) {
 }
 
 hipError_t launch_gg_stream(const GemmArgs& g, hipStream_t stream) {
-  launch_variant<4, 4>(g, stream);
+  launch_variant<2, 4>(g, stream);
   return hipGetLastError();
 }
 
