@@ -10,3 +10,5 @@ from .w4a8_oracle import (E4M3_VALUES, FP8_MAX, GROUP, SHRINK_RATIOS,  # noqa: F
                           grouped_gemm_exact_groups, int4_pack, int4_unpack, moe_layer,
                           permute, quant_act, quant_rows, quantize_int4_g128, relative_l2,
                           route, swiglu, swiglu_f32, unpermute)
+from .channel_int8_oracle import (grouped_gemm_i8, moe_layer_i8, quant_act_i8,  # noqa: F401
+                                  quant_rows_i8, quantize_int4_channel, swiglu_i8)
