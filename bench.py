@@ -67,7 +67,7 @@ def workload_tag(shape) -> str:
     return shape.name.split()[0] + f"_T{shape.T}"
 
 
-def cpu_baseline(wl, n_tokens: int) -> dict:
+def cpu_baseline(wl, n_tokens: int, channel: bool = False) -> dict:
     """The oracle layer on the first n_tokens tokens (single thread)."""
     import oracle
     try:
@@ -77,7 +77,12 @@ def cpu_baseline(wl, n_tokens: int) -> dict:
         limit = None
     sel = np.arange(n_tokens)
     t0 = time.perf_counter()
-    res = oracle.moe_layer(wl.x_bf16[sel], wl.logits[sel], wl.w13, wl.s13, wl.w2, wl.s2, k=wl.shape.k)
+    if channel:
+        from quantized_grouped_gemm_token_amd import workloads
+        s13c, s2c = workloads.channel_scales(wl)
+        res = oracle.moe_layer_i8(wl.x_bf16[sel], wl.logits[sel], wl.w13, s13c, wl.w2, s2c, k=wl.shape.k)
+    else:
+        res = oracle.moe_layer(wl.x_bf16[sel], wl.logits[sel], wl.w13, wl.s13, wl.w2, wl.s2, k=wl.shape.k)
     dt = time.perf_counter() - t0
     if limit is not None:
         limit.restore_original_limits()
@@ -152,6 +157,8 @@ def main() -> int:
                                                           "2 decode T=256, 3 prefill T=8192, 4 skewed T=16384")
     ap.add_argument("--cpu-tokens", type=int, default=16, help="tokens in the CPU oracle sample (0: skip)")
     ap.add_argument("--quiet", action="store_true")
+    ap.add_argument("--scheme", choices=("g128", "channel"), default="g128",
+                    help="g128: INT4 group-128 x FP8 per token (default); channel: per-channel INT4 x INT8 per token")
     ap.add_argument("--op", choices=("layer", "wquant"), default="layer",
                     help="layer: the MoE layer (default); wquant: the offline INT4 weight quantizer")
     ap.add_argument("--copy-bytes", type=int, default=0,
@@ -166,7 +173,7 @@ def main() -> int:
     import torch
 
     from quantized_grouped_gemm_token_amd import ops, workloads
-    from quantized_grouped_gemm_token_amd.layer import W4A8MoE
+    from quantized_grouped_gemm_token_amd.layer import W4A8MoE, W4A8MoEChannel
 
     log = (lambda *a: None) if args.quiet else (lambda *a: print("[bench]", *a, file=sys.stderr, flush=True))
     if args.copy_bytes:
@@ -195,7 +202,12 @@ def main() -> int:
     sh = wl.shape
     log(f"generated {sh.name} in {time.time() - t0:.1f} s")
     to = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)  # noqa: E731
-    moe = W4A8MoE(to(wl.w13), to(wl.s13), to(wl.w2), to(wl.s2), k=sh.k)
+    channel = args.scheme == "channel"
+    if channel:
+        s13c, s2c = workloads.channel_scales(wl)
+        moe = W4A8MoEChannel(to(wl.w13), to(s13c), to(wl.w2), to(s2c), k=sh.k)
+    else:
+        moe = W4A8MoE(to(wl.w13), to(wl.s13), to(wl.w2), to(wl.s2), k=sh.k)
     x = torch.from_numpy(wl.x_bf16.view(np.int16)).to(dev).view(torch.bfloat16)
     logits = to(wl.logits)
     y = torch.empty((sh.T, sh.H), dtype=torch.float32, device=dev)
@@ -226,9 +238,10 @@ def main() -> int:
     counts = np.diff(offsets)
     touched = int((counts > 0).sum())
     R = sh.T * sh.k
-    w13_bytes = 2 * sh.I * sh.H // 2 + 2 * sh.I * (sh.H // 128) * 4
-    w2_bytes = sh.H * sh.I // 2 + sh.H * (sh.I // 128) * 4
-    gate_up_bytes = touched * w13_bytes + sh.T * sh.H + sh.T * 4 + R * 4 + (sh.E + 1) * 4 + R * 2 * sh.I * 4
+    w13_bytes = 2 * sh.I * sh.H // 2 + 2 * sh.I * (1 if channel else sh.H // 128) * 4
+    w2_bytes = sh.H * sh.I // 2 + sh.H * (1 if channel else sh.I // 128) * 4
+    gate_up_bytes = (touched * w13_bytes + sh.T * sh.H + sh.T * 4 * (2 if channel else 1) + R * 4 + (sh.E + 1) * 4
+                     + R * 2 * sh.I * 4)
     gate_up_flops = 2.0 * R * 2 * sh.I * sh.H
     down_flops = 2.0 * R * sh.H * sh.I
     t_gu = per_step["gemm_gate_up"] * 1e-3
@@ -236,15 +249,17 @@ def main() -> int:
     decode = args.config in (0, 1, 2)
     khash = kernel_sources_hash()
     kernel = "gg_stream" if decode else "gg_tiled"
-    traffic = load_traffic(os.path.join(ROOT, "profiles", f"{kernel}_{workload_tag(sh)}_pmc.txt"), khash)
+    tag = workload_tag(sh) + ("_channel" if channel else "")
+    traffic = load_traffic(os.path.join(ROOT, "profiles", f"{kernel}_{tag}_pmc.txt"), khash)
     if decode:
         achieved = gate_up_bytes / t_gu / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic}
     else:
         achieved = gate_up_flops / t_gu / 1e12
-        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(achieved / FP8_PEAK_TFLOPS, 4), "traffic": traffic}
+        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": FP8_PEAK_TFLOPS,
+                "unit": "TOP/s" if channel else "TFLOP/s", "frac": round(achieved / FP8_PEAK_TFLOPS, 4),
+                "traffic": traffic}
     roof["kernel"] = f"{kernel} (gate/up grouped GEMM)"
     roof["algorithmic_bytes"] = int(gate_up_bytes)
     roof["algorithmic_flops"] = gate_up_flops
@@ -261,15 +276,16 @@ def main() -> int:
     cpu = None
     if args.cpu_tokens > 0:
         log(f"CPU oracle on {args.cpu_tokens} tokens ...")
-        cpu = cpu_baseline(wl, min(args.cpu_tokens, sh.T))
+        cpu = cpu_baseline(wl, min(args.cpu_tokens, sh.T), channel)
 
     line = {
         "metric": METRIC, "value": round(sh.T / (ms_step * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 5), "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "fp8e4m3 x int4 (fp32 accumulate)",
+        "scaling": "weak", "vs_baseline": None,
+        "dtype": "int8 x int4 (int32 accumulate)" if channel else "fp8e4m3 x int4 (fp32 accumulate)",
         "data": "synthetic (seeded; uniform INT4 words, lognormal scales, N(0,1) bf16 activations)",
         "config": {"workload": sh.name, "tokens": sh.T, "hidden": sh.H, "intermediate": sh.I, "experts": sh.E,
-                   "top_k": sh.k, "group": 128},
+                   "top_k": sh.k, "scheme": "per-channel int4 x per-token int8" if channel else "int4 g128 x fp8"},
         "roofline": roof, "cpu_baseline": cpu, "gemms": gemms,
         "step_ms": {k: round(v, 5) for k, v in per_step.items()},
         "device": torch.cuda.get_device_name(0), "kernel_sources_hash": khash,

@@ -192,6 +192,64 @@ int w4a8_moe_unpermute(const float* o, const int32_t* inv_pos, const float* w,
 int w4a8_moe_quantize_weights(const float* w, int64_t rows, int64_t K, int32_t mse_clip,
                               int32_t* w_packed, float* w_scale, void* stream);
 
+/*
+ * ---- The per-channel INT4 x per-token INT8 variant ---------------------
+ * ("GLM-5.3-Channel-INT4-w4a8" card, section 1: routed experts INT4 W4A8
+ * with weights quantized RTN, static, per channel; activations INT8,
+ * dynamic, per token.)  Routing, permutation and the combine are shared with
+ * the group-128 FP8 form above; these calls replace steps 1, 4, 5 and 6.
+ */
+
+/*
+ * Step 1, INT8 -- per-token quantization of bf16 activations.
+ *   scale sx[t] = fl32(amax / 127) (1.0 for an all-zero row);
+ *   qx[t, k] = clamp(round-half-even(fl32(x[t, k] / sx[t])), -127, 127);
+ *   rowsum[t] = sum_k qx[t, k] (the INT8 GEMM uses it to undo the +8
+ *   offset of the stored weight nibbles).
+ *   x : bf16 [T][ld_x] (H used), 16-byte aligned.  qx : int8 [T][H], 8-byte
+ *   aligned.  sx : fp32 [T].  rowsum : int32 [T].
+ *   Rules : T >= 0, H > 0, H % 128 == 0, ld_x >= H, ld_x % 8 == 0.
+ */
+int w4a8_moe_quant_act_i8(const uint16_t* x_bf16, int64_t T, int64_t H, int64_t ld_x,
+                          int8_t* qx, float* sx, int32_t* rowsum, void* stream);
+
+/*
+ * Steps 4 and 6, INT8 -- grouped GEMM with per-channel INT4 weights.
+ *   For expert e and each row p in [offsets[e], offsets[e+1]), with
+ *   r = a_rows ? a_rows[p] : p:
+ *     out[p, n] = a_scale[r] * w_scale[e, n] * sum_k a[r, k] * q[e, n, k]
+ *   computed as (sum_k a u - 8 rowsum[r]) with u = q + 8, exact in int32
+ *   (K <= 2^20), then the two scales in fp32.
+ *   a : int8 [*][K], 16-byte aligned.  a_scale : fp32 [*].  a_rowsum : int32 [*].
+ *   a_rows, offsets : as in w4a8_moe_grouped_gemm.
+ *   w_packed : int32 [E][N][K/8] uint4b8, 16-byte aligned.  w_scale : fp32 [E][N].
+ *   out : fp32 [M_total][N], 16-byte aligned.  algo : W4A8_GG_*.
+ *   Rules : as in w4a8_moe_grouped_gemm, and K <= 2^20.
+ */
+int w4a8_moe_grouped_gemm_i8(const int8_t* a, const float* a_scale, const int32_t* a_rowsum,
+                             const int32_t* a_rows, int64_t M_total, const int32_t* offsets, int32_t E,
+                             const int32_t* w_packed, const float* w_scale, int64_t N, int64_t K,
+                             float* out, int32_t algo, void* stream);
+
+/*
+ * Step 5, INT8 -- SwiGLU of the gate/up output, then the step-1 INT8 rule
+ * per routed row (with row sums).
+ *   h : fp32 [M][2I], 16-byte aligned.  qa : int8 [M][I], 4-byte aligned.
+ *   sa : fp32 [M].  rowsum : int32 [M].  Rules : M >= 0, I > 0, I % 128 == 0.
+ */
+int w4a8_moe_swiglu_i8(const float* h, int64_t M, int64_t I, int8_t* qa, float* sa, int32_t* rowsum,
+                       void* stream);
+
+/*
+ * Offline, INT8 variant -- per-channel RTN INT4 weights.
+ *   s[n] = fl32(amax_n / 7) (1/7 for an all-zero row);
+ *   q = clamp(round-half-even(w / s[n]), -8, 7) (the exact quotient rounded).
+ *   w : fp32 [rows][K], 8-byte aligned.  w_packed : int32 [rows][K/8] uint4b8.
+ *   w_scale : fp32 [rows].  Rules : rows >= 0, K > 0, K % 128 == 0.
+ */
+int w4a8_moe_quantize_weights_channel(const float* w, int64_t rows, int64_t K, int32_t* w_packed,
+                                      float* w_scale, void* stream);
+
 /* Static name of a status code ("W4A8_OK", ...). */
 const char* w4a8_moe_status_string(int status);
 

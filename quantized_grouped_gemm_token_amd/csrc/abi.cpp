@@ -168,7 +168,7 @@ int w4a8_moe_grouped_gemm_algo(const uint8_t* a, const float* a_scale, const int
       !aligned(w_scale, 4) || !aligned(offsets, 4) || !aligned(a_rows, 4))
     return fail(W4A8_ERR_ALIGN, "grouped_gemm: a, w_packed and out must be 16-byte aligned, the rest 4-byte");
   if (int st = check_device()) return st;
-  const w4a8::GemmArgs g{a, a_scale, a_rows, M_total, offsets, E, w_packed, w_scale, N, K, out};
+  const w4a8::GemmArgs g{a, a_scale, nullptr, a_rows, M_total, offsets, E, w_packed, w_scale, N, K, out};
   if (algo == W4A8_GG_AUTO) algo = (M_total <= 32 * (int64_t)E) ? W4A8_GG_STREAM : W4A8_GG_TILED;
   (void)hipGetLastError();
   if (algo == W4A8_GG_STREAM) return launched(w4a8::launch_gg_stream(g, as_stream(stream)), "grouped_gemm");
@@ -209,6 +209,82 @@ int w4a8_moe_quantize_weights(const float* w, int64_t rows, int64_t K, int32_t m
   (void)hipGetLastError();
   return launched(w4a8::launch_wquant(w, rows, K, mse_clip ? 1 : 0, w_packed, w_scale, as_stream(stream)),
                   "quantize_weights");
+}
+
+int w4a8_moe_quant_act_i8(const uint16_t* x_bf16, int64_t T, int64_t H, int64_t ld_x, int8_t* qx, float* sx,
+                          int32_t* rowsum, void* stream) {
+  if (T < 0 || T >= kMaxRows) return fail(W4A8_ERR_SHAPE, "quant_act_i8: T=%lld out of range", (long long)T);
+  if (H <= 0 || H % 128) return fail(W4A8_ERR_SHAPE, "quant_act_i8: H=%lld must be a positive multiple of 128",
+                                     (long long)H);
+  if (ld_x < H || ld_x % 8) return fail(W4A8_ERR_SHAPE, "quant_act_i8: ld_x=%lld must be >= H and a multiple of 8",
+                                        (long long)ld_x);
+  if (T == 0) return ok();
+  if (!x_bf16 || !qx || !sx || !rowsum) return fail(W4A8_ERR_NULL, "quant_act_i8: null pointer");
+  if (!aligned(x_bf16, 16) || !aligned(qx, 8) || !aligned(sx, 4) || !aligned(rowsum, 4))
+    return fail(W4A8_ERR_ALIGN, "quant_act_i8: x must be 16-byte aligned, qx 8-byte, sx and rowsum 4-byte");
+  if (int st = check_device()) return st;
+  (void)hipGetLastError();
+  return launched(w4a8::launch_quant_act_i8(x_bf16, T, H, ld_x, qx, sx, rowsum, as_stream(stream)),
+                  "quant_act_i8");
+}
+
+int w4a8_moe_swiglu_i8(const float* h, int64_t M, int64_t I, int8_t* qa, float* sa, int32_t* rowsum,
+                       void* stream) {
+  if (M < 0 || M >= kMaxRows) return fail(W4A8_ERR_SHAPE, "swiglu_i8: M=%lld out of range", (long long)M);
+  if (I <= 0 || I % 128) return fail(W4A8_ERR_SHAPE, "swiglu_i8: I=%lld must be a positive multiple of 128",
+                                     (long long)I);
+  if (M == 0) return ok();
+  if (!h || !qa || !sa || !rowsum) return fail(W4A8_ERR_NULL, "swiglu_i8: null pointer");
+  if (!aligned(h, 16) || !aligned(qa, 4) || !aligned(sa, 4) || !aligned(rowsum, 4))
+    return fail(W4A8_ERR_ALIGN, "swiglu_i8: h must be 16-byte aligned, qa, sa and rowsum 4-byte");
+  if (int st = check_device()) return st;
+  (void)hipGetLastError();
+  return launched(w4a8::launch_swiglu_i8(h, M, I, qa, sa, rowsum, as_stream(stream)), "swiglu_i8");
+}
+
+int w4a8_moe_grouped_gemm_i8(const int8_t* a, const float* a_scale, const int32_t* a_rowsum, const int32_t* a_rows,
+                             int64_t M_total, const int32_t* offsets, int32_t E, const int32_t* w_packed,
+                             const float* w_scale, int64_t N, int64_t K, float* out, int32_t algo, void* stream) {
+  if (M_total < 0 || M_total >= kMaxRows)
+    return fail(W4A8_ERR_SHAPE, "grouped_gemm_i8: M_total=%lld out of range", (long long)M_total);
+  if (E < 1 || E > 1024) return fail(W4A8_ERR_SHAPE, "grouped_gemm_i8: E=%d must be in [1, 1024]", E);
+  if (N <= 0 || N % 64) return fail(W4A8_ERR_SHAPE, "grouped_gemm_i8: N=%lld must be a positive multiple of 64",
+                                    (long long)N);
+  if (K <= 0 || K % 128) return fail(W4A8_ERR_SHAPE, "grouped_gemm_i8: K=%lld must be a positive multiple of 128",
+                                     (long long)K);
+  if (K > (int64_t)1 << 20) return fail(W4A8_ERR_SHAPE, "grouped_gemm_i8: K=%lld would overflow the int32 sums",
+                                        (long long)K);
+  if (algo < W4A8_GG_AUTO || algo > W4A8_GG_TILED)
+    return fail(W4A8_ERR_SHAPE, "grouped_gemm_i8: unknown algo %d", algo);
+  if (M_total == 0) return ok();
+  if (!a || !a_scale || !a_rowsum || !offsets || !w_packed || !w_scale || !out)
+    return fail(W4A8_ERR_NULL, "grouped_gemm_i8: null pointer");
+  if (!aligned(a, 16) || !aligned(w_packed, 16) || !aligned(out, 16) || !aligned(a_scale, 4) ||
+      !aligned(a_rowsum, 4) || !aligned(w_scale, 4) || !aligned(offsets, 4) || !aligned(a_rows, 4))
+    return fail(W4A8_ERR_ALIGN, "grouped_gemm_i8: a, w_packed and out must be 16-byte aligned, the rest 4-byte");
+  if (int st = check_device()) return st;
+  const w4a8::GemmArgs g{reinterpret_cast<const uint8_t*>(a), a_scale, a_rowsum, a_rows, M_total, offsets, E,
+                         w_packed, w_scale, N, K, out};
+  if (algo == W4A8_GG_AUTO) algo = (M_total <= 32 * (int64_t)E) ? W4A8_GG_STREAM : W4A8_GG_TILED;
+  (void)hipGetLastError();
+  if (algo == W4A8_GG_STREAM) return launched(w4a8::launch_gg_stream(g, as_stream(stream)), "grouped_gemm_i8");
+  return launched(w4a8::launch_gg_tiled(g, as_stream(stream)), "grouped_gemm_i8");
+}
+
+int w4a8_moe_quantize_weights_channel(const float* w, int64_t rows, int64_t K, int32_t* w_packed, float* w_scale,
+                                      void* stream) {
+  if (rows < 0 || rows >= kMaxRows)
+    return fail(W4A8_ERR_SHAPE, "quantize_weights_channel: rows=%lld out of range", (long long)rows);
+  if (K <= 0 || K % 128)
+    return fail(W4A8_ERR_SHAPE, "quantize_weights_channel: K=%lld must be a positive multiple of 128", (long long)K);
+  if (rows == 0) return ok();
+  if (!w || !w_packed || !w_scale) return fail(W4A8_ERR_NULL, "quantize_weights_channel: null pointer");
+  if (!aligned(w, 8) || !aligned(w_packed, 4) || !aligned(w_scale, 4))
+    return fail(W4A8_ERR_ALIGN, "quantize_weights_channel: w must be 8-byte aligned, w_packed and w_scale 4-byte");
+  if (int st = check_device()) return st;
+  (void)hipGetLastError();
+  return launched(w4a8::launch_wquant_channel(w, rows, K, w_packed, w_scale, as_stream(stream)),
+                  "quantize_weights_channel");
 }
 
 int w4a8_moe_unpermute(const float* o, const int32_t* inv_pos, const float* w, int64_t T, int32_t k, int64_t H,

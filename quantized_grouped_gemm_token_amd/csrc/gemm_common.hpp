@@ -38,6 +38,22 @@ __device__ __forceinline__ v4f mfma16x16x128(v8i a, v8i b, v4f c) {
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
 }
 
+// INT8 matrix-core products for the per-channel variant (int32 accumulation).
+// 16x16x64: lane l supplies A row (l % 16) and B column (l % 16), K elements
+// 16 * (l / 16) .. +16 of the 64; D as in the 16x16 FP8 form.
+// 32x32x32: lane l supplies A row (l % 32) and B column (l % 32), K elements
+// 16 * (l / 32) .. +16 of the 32; D as in the 32x32 FP8 form.
+// A 32-byte FP8 operand of a lane becomes two INT8 operands (its 16-byte
+// halves, with the same split on both sides), so the kernels keep their FP8
+// data layout: the two products cover the same K elements between them.
+typedef int v16i __attribute__((ext_vector_type(16)));
+__device__ __forceinline__ i32x4 mfma_i8_16x16x64(i32x4 a, i32x4 b, i32x4 c) {
+  return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ v16i mfma_i8_32x32x32(i32x4 a, i32x4 b, v16i c) {
+  return __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, c, 0, 0, 0);
+}
+
 // v_mfma_f32_32x32x64_f8f6f4 with both operands E4M3 and no block scaling.
 // Lane l supplies A row (l % 32) and B column (l % 32), K elements
 // 32 * (l / 32) .. +32 of the 64; D element v of lane l is row

@@ -29,6 +29,8 @@
 #include "gemm_common.hpp"
 #include "kernels.hpp"
 
+#include <type_traits>
+
 namespace w4a8 {
 
 constexpr int kStreamThreads = 256;
@@ -117,9 +119,36 @@ __device__ __forceinline__ void pair_compute(const WPair<NS>& w, const float (&s
   }
 }
 
-template <int NS, int CH>
+// the per-channel INT8 form of one group pair: int32 products, no scales
+// (the nibbles u = q + 8 are the INT8 B operand; the offset is removed with
+// the activation row sums in the epilogue)
+template <int NS>
+__device__ __forceinline__ void pair_compute_i8(const WPair<NS>& w, const uint8_t* a0, const uint8_t* a1, bool lo,
+                                                i32x4 (&acc)[NS]) {
+  const v8i av0 = *reinterpret_cast<const v8i*>(a0);
+  const v8i av1 = *reinterpret_cast<const v8i*>(a1);
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    i32x4 t0, t1;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      t0[q] = lo ? w.wa[s][q] : w.wb[s][q];
+      t1[q] = row_ror8(lo ? w.wb[s][q] : w.wa[s][q]);
+    }
+    const v8i b0 = nibbles_to_fp8(t0), b1 = nibbles_to_fp8(t1);
+    acc[s] = mfma_i8_16x16x64(av0.lo, b0.lo, acc[s]);
+    acc[s] = mfma_i8_16x16x64(av0.hi, b0.hi, acc[s]);
+    acc[s] = mfma_i8_16x16x64(av1.lo, b1.lo, acc[s]);
+    acc[s] = mfma_i8_16x16x64(av1.hi, b1.hi, acc[s]);
+  }
+}
+
+// kInt8: the per-channel variant (INT8 activations with row sums a_rowsum,
+// one scale per weight row in w_scale [E][N]); otherwise the group-128 FP8 form.
+template <int NS, int CH, bool kInt8>
 __global__ __launch_bounds__(kStreamThreads) void gg_stream_kernel(const uint8_t* __restrict__ a,
                                                                    const float* __restrict__ a_scale,
+                                                                   const int32_t* __restrict__ a_rowsum,
                                                                    const int32_t* __restrict__ a_rows,
                                                                    const int32_t* __restrict__ offsets,
                                                                    const int32_t* __restrict__ w_packed,
@@ -155,9 +184,10 @@ __global__ __launch_bounds__(kStreamThreads) void gg_stream_kernel(const uint8_t
     // activation row staged by this thread (rows past the end repeat the last one; never stored)
     const int p_t = min(m0 + (int)(threadIdx.x >> 4), r1 - 1);
     const uint8_t* arow_t = a + (int64_t)(a_rows ? a_rows[p_t] : p_t) * K;
-    v4f acc[NS];
+    using Acc = std::conditional_t<kInt8, i32x4, v4f>;
+    Acc acc[NS];
 #pragma unroll
-    for (int s = 0; s < NS; ++s) acc[s] = v4f{0.f, 0.f, 0.f, 0.f};
+    for (int s = 0; s < NS; ++s) acc[s] = Acc{0, 0, 0, 0};
 
     const int nchunks = (G + 2 * CH - 1) / (2 * CH);
     {
@@ -174,7 +204,35 @@ __global__ __launch_bounds__(kStreamThreads) void gg_stream_kernel(const uint8_t
       const bool has_next = ci + 1 < nchunks;
       const int ng_next = has_next ? min(2 * CH, G - g0 - 2 * CH) : 0;
       if (has_next) a_chunk_load(next, arow_t, g0 + 2 * CH, ng_next);
-      if (active) {
+      if constexpr (kInt8) {
+        if (active) {
+          const int npairs = ng >> 1;
+#pragma unroll
+          for (int u = 0; u < CH; u += 2) {
+            if (u < npairs) {
+              WPair<NS> w0, w1;
+              w_pair_load(w0, pa, pb, g0 + 2 * u);
+              const bool two = u + 1 < npairs;
+              if (two) w_pair_load(w1, pa, pb, g0 + 2 * u + 2);
+              pair_compute_i8(w0, &sm.a[buf][2 * u][lane][0], &sm.a[buf][2 * u + 1][lane][0], lo, acc);
+              if (two)
+                pair_compute_i8(w1, &sm.a[buf][2 * u + 2][lane][0], &sm.a[buf][2 * u + 3][lane][0], lo, acc);
+            }
+          }
+          if (ng & 1) {   // a last single group: each lane reads its own column's quarter
+            const int h = ng - 1;
+            const v8i av = *reinterpret_cast<const v8i*>(&sm.a[buf][h][lane][0]);
+#pragma unroll
+            for (int s = 0; s < NS; ++s) {
+              const uint8_t* pself = pa[s] - (lo ? 0 : 64) + (int64_t)(col - (col & 7)) * row_bytes;
+              const i32x4 wq = __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(pself + (g0 + h) * 64));
+              const v8i b = nibbles_to_fp8(wq);
+              acc[s] = mfma_i8_16x16x64(av.lo, b.lo, acc[s]);
+              acc[s] = mfma_i8_16x16x64(av.hi, b.hi, acc[s]);
+            }
+          }
+        }
+      } else if (active) {
         // scales of this chunk's groups for each subtile
         float sc[NS][2 * CH];
 #pragma unroll
@@ -228,29 +286,49 @@ __global__ __launch_bounds__(kStreamThreads) void gg_stream_kernel(const uint8_t
     }
 
     if (active) {
+      if constexpr (kInt8) {
+        // out = a_scale * w_scale * (sum a u - 8 sum a): the integer part is exact
+        float ws[NS];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int p = m0 + kq * 4 + r;
-        if (p < r1) {
-          const int64_t src = a_rows ? a_rows[p] : p;
-          const float rs = a_scale[src] * kUnitScale;
+        for (int s = 0; s < NS; ++s) ws[s] = w_scale[(int64_t)e * N + n0 + 16 * s + col];
 #pragma unroll
-          for (int s = 0; s < NS; ++s) out[(int64_t)p * N + n0 + 16 * s + col] = acc[s][r] * rs;
+        for (int r = 0; r < 4; ++r) {
+          const int p = m0 + kq * 4 + r;
+          if (p < r1) {
+            const int64_t src = a_rows ? a_rows[p] : p;
+            const int off = 8 * a_rowsum[src];
+            const float as = a_scale[src];
+#pragma unroll
+            for (int s = 0; s < NS; ++s)
+              out[(int64_t)p * N + n0 + 16 * s + col] = (float)(acc[s][r] - off) * as * ws[s];
+          }
+        }
+      } else {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int p = m0 + kq * 4 + r;
+          if (p < r1) {
+            const int64_t src = a_rows ? a_rows[p] : p;
+            const float rs = a_scale[src] * kUnitScale;
+#pragma unroll
+            for (int s = 0; s < NS; ++s) out[(int64_t)p * N + n0 + 16 * s + col] = acc[s][r] * rs;
+          }
         }
       }
     }
   }
 }
 
-template <int NS, int CH>
+template <int NS, int CH, bool kInt8 = false>
 static void launch_variant(const GemmArgs& g, hipStream_t stream) {
   const dim3 grid((unsigned)((g.N + 64 * NS - 1) / (64 * NS)), (unsigned)g.E);
-  hipLaunchKernelGGL((gg_stream_kernel<NS, CH>), grid, dim3(kStreamThreads), 0, stream, g.a, g.a_scale, g.a_rows,
-                     g.offsets, g.w_packed, g.w_scale, g.N, g.K, g.out);
+  hipLaunchKernelGGL((gg_stream_kernel<NS, CH, kInt8>), grid, dim3(kStreamThreads), 0, stream, g.a, g.a_scale,
+                     g.a_rowsum, g.a_rows, g.offsets, g.w_packed, g.w_scale, g.N, g.K, g.out);
 }
 
 hipError_t launch_gg_stream(const GemmArgs& g, hipStream_t stream) {
-  launch_variant<2, 4>(g, stream);
+  if (g.a_rowsum) launch_variant<2, 4, true>(g, stream);
+  else launch_variant<2, 4>(g, stream);
   return hipGetLastError();
 }
 

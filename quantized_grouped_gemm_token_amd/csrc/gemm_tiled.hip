@@ -33,6 +33,8 @@
 #include "gemm_common.hpp"
 #include "kernels.hpp"
 
+#include <type_traits>
+
 namespace w4a8 {
 
 constexpr int kTM = 256;              // rows per tile
@@ -93,9 +95,14 @@ __device__ __forceinline__ T lds_load(const void* p) {
 __device__ __forceinline__ int tiles_of(int rows, int nb) { return ((rows + kTM - 1) / kTM) * nb; }
 
 // kWaves waves per workgroup; each wave owns kNJ blocks of 32 columns.
-template <int kWaves, int kNJ>
+// kInt8: the per-channel variant (INT8 activations with row code sums
+// a_rowsum, one scale per weight row in w_scale [E][N]): int32 products
+// accumulated by the matrix core over all of K, no group scales, no row-sum
+// MFMAs; otherwise the group-128 FP8 form.
+template <int kWaves, int kNJ, bool kInt8>
 __global__ __launch_bounds__(kWaves * kWave, 1) void gg_tiled_kernel(const uint8_t* __restrict__ a,
                                                               const float* __restrict__ a_scale,
+                                                              const int32_t* __restrict__ a_rowsum,
                                                               const int32_t* __restrict__ a_rows,
                                                               const int32_t* __restrict__ offsets, int E,
                                                               const int32_t* __restrict__ w_packed,
@@ -126,6 +133,7 @@ __global__ __launch_bounds__(kWaves * kWave, 1) void gg_tiled_kernel(const uint8
   const uint32_t row_bytes = (uint32_t)(K >> 1);
   // scale quads as 16-byte loads need 4 | G and a 16-byte aligned scale array
   const bool vec_scales = (G & 3) == 0 && (reinterpret_cast<uintptr_t>(w_scale) & 15) == 0;
+  int* rowsum_sm = reinterpret_cast<int*>(&bias_sm[0][0]);   // the INT8 form has no group sums: row code sums
 
   // ---- tile numbering: exclusive prefix of per-expert tile counts (wave-level scans)
   {
@@ -225,7 +233,7 @@ __global__ __launch_bounds__(kWaves * kWave, 1) void gg_tiled_kernel(const uint8
     // scales (waves 0..3): column 64 wave + lane of the tile
     const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(w_scale + (int64_t)e * N * G, (uint32_t)(N * G * 4));
     const uint32_t soff = (uint32_t)min(n0 + 64 * (wave & 3) + lane, (int)N - 1) * (uint32_t)G * 4u;
-    const bool scale_loader = wave < 4;
+    const bool scale_loader = !kInt8 && wave < 4;   // the group-scale quads (FP8 form)
 
     // loads of group g into slot S (and, on every fourth group, first the scale quad of groups g .. g+3:
     // issued first, a wait for it leaves the group's other loads in flight)
@@ -271,13 +279,14 @@ __global__ __launch_bounds__(kWaves * kWave, 1) void gg_tiled_kernel(const uint8
       }
     };
 
-    v16f acc[kBlocks][kNJ];
+    using Acc = std::conditional_t<kInt8, v16i, v16f>;
+    Acc acc[kBlocks][kNJ];
 #pragma unroll
     for (int i = 0; i < kBlocks; ++i)
 #pragma unroll
       for (int j = 0; j < kNJ; ++j)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+        for (int v = 0; v < 16; ++v) acc[i][j][v] = 0;
 
     // One K group in slot S: prefetch group g+2; multiply group g; in the
     // middle, once this wave's loads of group g+1 have landed, publish that
@@ -290,10 +299,12 @@ __global__ __launch_bounds__(kWaves * kWave, 1) void gg_tiled_kernel(const uint8
       // direct load into scq that can be in flight is the next quad's, issued
       // first in its group, so waiting for it keeps that group's loads going)
       float s[kNJ];
+      if constexpr (!kInt8) {
 #pragma unroll
-      for (int j = 0; j < kNJ; ++j) {
-        const int col = 32 * (kNJ * cg + j) + i32;
-        s[j] = scq[(g >> 2) & 1][vec_scales ? col * 4 + (g & 3) : (g & 3) * kTN + col];
+        for (int j = 0; j < kNJ; ++j) {
+          const int col = 32 * (kNJ * cg + j) + i32;
+          s[j] = scq[(g >> 2) & 1][vec_scales ? col * 4 + (g & 3) : (g & 3) * kTN + col];
+        }
       }
       if (more) stage(std::integral_constant<int, (S + 2) % 3>{}, g + 2);
       const RingSlot& sl = slot<S>(ring0, ring1, ring2);
@@ -316,6 +327,16 @@ __global__ __launch_bounds__(kWaves * kWave, 1) void gg_tiled_kernel(const uint8
           const i32x4 x3 = lds_load<i32x4>(ab + a_rd3);
           const v8i a0 = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
           const v8i a1 = {x2[0], x2[1], x2[2], x2[3], x3[0], x3[1], x3[2], x3[3]};
+          if constexpr (kInt8) {
+#pragma unroll
+            for (int j = 0; j < kNJ; ++j) {
+              acc[i][j] = mfma_i8_32x32x32(a0.lo, b0[j].lo, acc[i][j]);
+              acc[i][j] = mfma_i8_32x32x32(a0.hi, b0[j].hi, acc[i][j]);
+              acc[i][j] = mfma_i8_32x32x32(a1.lo, b1[j].lo, acc[i][j]);
+              acc[i][j] = mfma_i8_32x32x32(a1.hi, b1[j].hi, acc[i][j]);
+            }
+            return;
+          }
 #pragma unroll
           for (int j = 0; j < kNJ; ++j) {
             v16f c;   // the row sums enter as the accumulator input (read per column block: no copies)
@@ -328,7 +349,9 @@ __global__ __launch_bounds__(kWaves * kWave, 1) void gg_tiled_kernel(const uint8
             c = mfma32x32x64(a0, b0[j], c);
             c = mfma32x32x64(a1, b1[j], c);
 #pragma unroll
-            for (int v = 0; v < 16; ++v) acc[i][j][v] = fmaf(s[j], c[v], acc[i][j][v]);
+            for (int v = 0; v < 16; ++v) {
+              if constexpr (!kInt8) acc[i][j][v] = fmaf(s[j], c[v], acc[i][j][v]);
+            }
           }
         }
       };
@@ -337,7 +360,7 @@ __global__ __launch_bounds__(kWaves * kWave, 1) void gg_tiled_kernel(const uint8
       auto mid = [&]() {
         if (more) wait_loads(stage_loads(g + 2));
         else __builtin_amdgcn_s_waitcnt(0x0F70);              // vmcnt(0)
-        if (g + 1 < G) row_sums(std::integral_constant<int, (S + 1) % 3>{}, g + 1);
+        if (!kInt8 && g + 1 < G) row_sums(std::integral_constant<int, (S + 1) % 3>{}, g + 1);
       };
 #pragma unroll
       for (int i = 0; i < kBlocks / 2; ++i) block(i);
@@ -357,14 +380,17 @@ __global__ __launch_bounds__(kWaves * kWave, 1) void gg_tiled_kernel(const uint8
     } else {
       __builtin_amdgcn_s_waitcnt(0x0F70);
     }
-    row_sums(std::integral_constant<int, 0>{}, 0);
+    if (!kInt8) row_sums(std::integral_constant<int, 0>{}, 0);
     __builtin_amdgcn_s_waitcnt(0xC07F);
     barrier_loads_in_flight();
-    // the token scales of the tile's rows (read in the epilogue; every wave is past the previous epilogue)
-    if (scale_loader) {
+    // the token scales (and in the INT8 form the row code sums) of the tile's
+    // rows, read in the epilogue; every wave is past the previous epilogue
+    if (wave < 4) {
       const int r = 64 * wave + lane;
       const int p = r0 + min(r, mlen - 1);
-      dma4(buffer_rsrc(a_scale, 0xffffffffu), (uint32_t)(a_rows ? a_rows[p] : p) * 4u, 0, &ascale_sm[64 * wave]);
+      const uint32_t src = (uint32_t)(a_rows ? a_rows[p] : p) * 4u;
+      dma4(buffer_rsrc(a_scale, 0xffffffffu), src, 0, &ascale_sm[64 * wave]);
+      if constexpr (kInt8) dma4(buffer_rsrc(a_rowsum, 0xffffffffu), src, 0, &rowsum_sm[64 * wave]);
     }
 
     for (int g = 0; g < G; g += 3) {
@@ -382,14 +408,24 @@ __global__ __launch_bounds__(kWaves * kWave, 1) void gg_tiled_kernel(const uint8
           for (int q = 0; q < 4; ++q) {
             const int rt = 32 * blk + 8 * q + 4 * kh;
             const v4f sc4 = lds_load<v4f>(&ascale_sm[rt]);
+            i32x4 rs4 = {0, 0, 0, 0};
+            float ws[kNJ];
+            if constexpr (kInt8) {
+              rs4 = lds_load<i32x4>(&rowsum_sm[rt]);
+#pragma unroll
+              for (int j = 0; j < kNJ; ++j) ws[j] = w_scale[(int64_t)e * N + n0 + 32 * (kNJ * cg + j) + i32];
+            }
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
               if (rt + r < mlen) {
                 const int64_t p = r0 + rt + r;
 #pragma unroll
-                for (int j = 0; j < kNJ; ++j)
-                  __builtin_nontemporal_store(acc[i][j][4 * q + r] * (sc4[r] * kUnitScale),
-                                              out + p * N + n0 + 32 * (kNJ * cg + j) + i32);
+                for (int j = 0; j < kNJ; ++j) {
+                  float v;
+                  if constexpr (kInt8) v = (float)(acc[i][j][4 * q + r] - 8 * rs4[r]) * sc4[r] * ws[j];
+                  else v = acc[i][j][4 * q + r] * (sc4[r] * kUnitScale);
+                  __builtin_nontemporal_store(v, out + p * N + n0 + 32 * (kNJ * cg + j) + i32);
+                }
               }
             }
           }
@@ -415,11 +451,15 @@ static int cu_count() {
 hipError_t launch_gg_tiled(const GemmArgs& g, hipStream_t stream) {
   // the tiled kernel addresses its operands with 32-bit byte offsets
   constexpr int64_t k4G = (int64_t)1 << 32;
-  if (g.M_total * g.K >= k4G || g.N * (g.K / 2) >= k4G || g.N * (g.K / 128) * 4 >= k4G)
+  if (g.M_total * g.K >= k4G || g.M_total * 4 >= k4G || g.N * (g.K / 2) >= k4G || g.N * (g.K / 128) * 4 >= k4G)
     return launch_gg_stream(g, stream);
   constexpr int kW = GG_TILED_WAVES, kJ = GG_TILED_NJ;
-  hipLaunchKernelGGL((gg_tiled_kernel<kW, kJ>), dim3(cu_count()), dim3(kW * kWave), 0, stream, g.a, g.a_scale,
-                     g.a_rows, g.offsets, g.E, g.w_packed, g.w_scale, g.N, g.K, g.out);
+  if (g.a_rowsum)
+    hipLaunchKernelGGL((gg_tiled_kernel<kW, kJ, true>), dim3(cu_count()), dim3(kW * kWave), 0, stream, g.a,
+                       g.a_scale, g.a_rowsum, g.a_rows, g.offsets, g.E, g.w_packed, g.w_scale, g.N, g.K, g.out);
+  else
+    hipLaunchKernelGGL((gg_tiled_kernel<kW, kJ, false>), dim3(cu_count()), dim3(kW * kWave), 0, stream, g.a,
+                       g.a_scale, nullptr, g.a_rows, g.offsets, g.E, g.w_packed, g.w_scale, g.N, g.K, g.out);
   return hipGetLastError();
 }
 

@@ -7,9 +7,13 @@
 
 namespace w4a8 {
 
+// One grouped GEMM.  a_rowsum == nullptr: the group-128 FP8 form (w_scale
+// [E][N][K/128]); otherwise the per-channel INT8 form (INT8 activations with
+// their row code sums, w_scale [E][N]).
 struct GemmArgs {
   const uint8_t* a;
   const float* a_scale;
+  const int32_t* a_rowsum;
   const int32_t* a_rows;
   int64_t M_total;
   const int32_t* offsets;
@@ -31,6 +35,12 @@ hipError_t launch_permute(const int32_t* ids, int64_t R, int k, int E, int32_t* 
 hipError_t launch_gg_stream(const GemmArgs& g, hipStream_t stream);
 hipError_t launch_gg_tiled(const GemmArgs& g, hipStream_t stream);
 hipError_t launch_swiglu(const float* h, int64_t M, int64_t I, uint8_t* q, float* s, hipStream_t stream);
+hipError_t launch_quant_act_i8(const uint16_t* x, int64_t T, int64_t H, int64_t ld, int8_t* q, float* s,
+                               int32_t* rowsum, hipStream_t stream);
+hipError_t launch_swiglu_i8(const float* h, int64_t M, int64_t I, int8_t* q, float* s, int32_t* rowsum,
+                            hipStream_t stream);
+hipError_t launch_wquant_channel(const float* w, int64_t rows, int64_t K, int32_t* packed, float* scales,
+                                 hipStream_t stream);
 hipError_t launch_wquant(const float* w, int64_t rows, int64_t K, int mse_clip, int32_t* packed, float* scales,
                          hipStream_t stream);
 hipError_t launch_unpermute(const float* o, const int32_t* inv_pos, const float* w, int64_t T, int k, int64_t H,

@@ -79,6 +79,49 @@ __global__ __launch_bounds__(256) void wquant_kernel(const float* __restrict__ w
   }
 }
 
+// Per-channel RTN ("GLM-5.3-Channel-INT4-w4a8" card, section 1: RTN, static,
+// per channel): one scale per weight row, s = fl32(amax / 7) (1/7 for an
+// all-zero row), q = clamp(round-half-even(w / s), -8, 7) from the exact
+// quotient.  One 256-thread block per row: the row's amax, then its codes.
+__global__ __launch_bounds__(256) void wquant_channel_kernel(const float* __restrict__ w, int64_t rows,
+                                                             int64_t K, uint8_t* __restrict__ packed,
+                                                             float* __restrict__ scales) {
+  __shared__ float part[4];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  for (int64_t row = blockIdx.x; row < rows; row += gridDim.x) {
+    const f32x2* wr = reinterpret_cast<const f32x2*>(w + row * K);
+    float amax = 0.0f;
+    for (int64_t c = threadIdx.x; c < K / 2; c += 256) {
+      const f32x2 v = wr[c];
+      amax = fmaxf(amax, fmaxf(fabsf(v.x), fabsf(v.y)));
+    }
+    amax = wave_max(amax);
+    if (lane == 0) part[wave] = amax;
+    __syncthreads();
+    amax = fmaxf(fmaxf(part[0], part[1]), fmaxf(part[2], part[3]));
+    if (amax == 0.0f) amax = 1.0f;
+    const float s = (float)((double)amax / 7.0);
+    for (int64_t c = threadIdx.x; c < K / 2; c += 256) {
+      const f32x2 v = wr[c];
+      const int u0 = (int)fminf(fmaxf(rne_quotient(v.x, s), -8.0f), 7.0f) + 8;
+      const int u1 = (int)fminf(fmaxf(rne_quotient(v.y, s), -8.0f), 7.0f) + 8;
+      packed[row * (K / 2) + c] = (uint8_t)(u0 | (u1 << 4));
+    }
+    if (threadIdx.x == 0) scales[row] = s;
+    __syncthreads();   // part[] is reused by the next row
+  }
+}
+
+hipError_t launch_wquant_channel(const float* w, int64_t rows, int64_t K, int32_t* packed, float* scales,
+                                 hipStream_t stream) {
+  if (rows == 0) return hipSuccess;
+  const int64_t blocks = std::min<int64_t>(rows, 65536);
+  hipLaunchKernelGGL(wquant_channel_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, w, rows, K,
+                     reinterpret_cast<uint8_t*>(packed), scales);
+  return hipGetLastError();
+}
+
 hipError_t launch_wquant(const float* w, int64_t rows, int64_t K, int mse_clip, int32_t* packed, float* scales,
                          hipStream_t stream) {
   const int G = (int)(K / kGroup);

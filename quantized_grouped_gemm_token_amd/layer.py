@@ -5,6 +5,8 @@
 
 Expert weights stay resident on the GPU in the packed format (int32
 [E][N][K/8] words of uint4b8 nibbles and fp32 [E][N][K/128] group scales).
+W4A8MoEChannel is the per-channel INT4 x per-token INT8 variant: fp32 [E][N]
+scales, INT8 activations.
 Intermediate buffers are allocated once per token count and reused, so a
 forward pass enqueues kernels only: no allocation, no host synchronisation.
 """
@@ -76,6 +78,52 @@ class W4A8MoE:
         step("swiglu", ops.w4a8_moe_swiglu, b["h"], b["qa"], b["sa"])
         step("gemm_down", ops.w4a8_moe_grouped_gemm, b["qa"], b["sa"], None, b["offsets"], self.w2, self.s2, R,
              b["o"], algo)
+        return step("unpermute", ops.w4a8_moe_unpermute, b["o"], b["inv_pos"], b["w"], y, y_dtype)
+
+    __call__ = forward
+
+
+class W4A8MoEChannel(W4A8MoE):
+    """The per-channel INT4 x per-token INT8 variant: s13 [E, 2I] and s2 [E, H]
+    are per-channel scales; steps 1, 4, 5 and 6 use the INT8 calls."""
+
+    def buffers(self, T: int) -> dict:
+        if T not in self._bufs:
+            b = dict(super().buffers(T))
+            dev = self.w13.device
+            R = T * self.k
+            b["qx"] = torch.empty((T, self.H), dtype=torch.int8, device=dev)
+            b["rx"] = torch.empty((T,), dtype=torch.int32, device=dev)
+            b["qa"] = torch.empty((R, self.I), dtype=torch.int8, device=dev)
+            b["ra"] = torch.empty((R,), dtype=torch.int32, device=dev)
+            self._bufs[T] = b
+        return self._bufs[T]
+
+    def forward(self, x: torch.Tensor, logits: torch.Tensor, y: torch.Tensor | None = None,
+                y_dtype: torch.dtype = torch.float32, algo: int = ops.W4A8_GG_AUTO,
+                events: dict | None = None) -> torch.Tensor:
+        T = x.shape[0]
+        b = self.buffers(T)
+        R = T * self.k
+
+        def step(name, fn, *args):
+            ev = events.get(name) if events else None
+            if ev:
+                ev[0].record()
+            r = fn(*args)
+            if ev:
+                ev[1].record()
+            return r
+
+        step("quant_act", ops.w4a8_moe_quant_act_i8, x, b["qx"], b["sx"], b["rx"])
+        step("route", ops.w4a8_moe_route, logits, self.k, self.renormalize, b["ids"], b["w"])
+        step("permute", ops.w4a8_moe_permute, b["ids"], self.E, b["offsets"], b["row_token"], b["inv_pos"],
+             b["workspace"])
+        step("gemm_gate_up", ops.w4a8_moe_grouped_gemm_i8, b["qx"], b["sx"], b["rx"], b["row_token"], b["offsets"],
+             self.w13, self.s13, b["h"], R, algo)
+        step("swiglu", ops.w4a8_moe_swiglu_i8, b["h"], b["qa"], b["sa"], b["ra"])
+        step("gemm_down", ops.w4a8_moe_grouped_gemm_i8, b["qa"], b["sa"], b["ra"], None, b["offsets"], self.w2,
+             self.s2, b["o"], R, algo)
         return step("unpermute", ops.w4a8_moe_unpermute, b["o"], b["inv_pos"], b["w"], y, y_dtype)
 
     __call__ = forward

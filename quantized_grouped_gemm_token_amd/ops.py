@@ -40,6 +40,11 @@ _SIGNATURES = {
     "w4a8_moe_swiglu": (ctypes.c_int, [_c_p, _i64, _i64, _c_p, _c_p, _c_p]),
     "w4a8_moe_unpermute": (ctypes.c_int, [_c_p, _c_p, _c_p, _i64, _i32, _i64, _c_p, _i32, _c_p]),
     "w4a8_moe_quantize_weights": (ctypes.c_int, [_c_p, _i64, _i64, _i32, _c_p, _c_p, _c_p]),
+    "w4a8_moe_quant_act_i8": (ctypes.c_int, [_c_p, _i64, _i64, _i64, _c_p, _c_p, _c_p, _c_p]),
+    "w4a8_moe_grouped_gemm_i8": (ctypes.c_int, [_c_p, _c_p, _c_p, _c_p, _i64, _c_p, _i32, _c_p, _c_p, _i64, _i64,
+                                                _c_p, _i32, _c_p]),
+    "w4a8_moe_swiglu_i8": (ctypes.c_int, [_c_p, _i64, _i64, _c_p, _c_p, _c_p, _c_p]),
+    "w4a8_moe_quantize_weights_channel": (ctypes.c_int, [_c_p, _i64, _i64, _c_p, _c_p, _c_p]),
     "w4a8_moe_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "w4a8_moe_last_error": (ctypes.c_char_p, []),
     "w4a8_moe_device_supported": (ctypes.c_int, []),
@@ -269,4 +274,96 @@ def w4a8_moe_quantize_weights(w: torch.Tensor, mse_clip: bool = True, w_packed: 
     _check("w4a8_moe_quantize_weights",
            lib().w4a8_moe_quantize_weights(_p(w), rows, K, 1 if mse_clip else 0, _p(w_packed), _p(w_scale),
                                            _stream(dev)))
+    return w_packed, w_scale
+
+
+# ---- the per-channel INT4 x per-token INT8 variant ------------------------
+def w4a8_moe_quant_act_i8(x: torch.Tensor, qx=None, sx=None, rowsum=None):
+    """bf16 [T, H] -> (int8 codes [T, H], scales fp32 [T], code row sums int32 [T])."""
+    _need(x, "x", torch.bfloat16, 2)
+    T, H = x.shape
+    dev = x.device
+    qx = torch.empty((T, H), dtype=torch.int8, device=dev) if qx is None else qx
+    sx = torch.empty((T,), dtype=torch.float32, device=dev) if sx is None else sx
+    rowsum = torch.empty((T,), dtype=torch.int32, device=dev) if rowsum is None else rowsum
+    _need(qx, "qx", torch.int8, 2, dev)
+    _need(sx, "sx", torch.float32, 1, dev)
+    _need(rowsum, "rowsum", torch.int32, 1, dev)
+    if tuple(qx.shape) != (T, H) or tuple(sx.shape) != (T,) or tuple(rowsum.shape) != (T,):
+        raise ValueError("qx must be [T, H], sx and rowsum [T]")
+    _check("w4a8_moe_quant_act_i8", lib().w4a8_moe_quant_act_i8(_p(x), T, H, x.stride(0), _p(qx), _p(sx),
+                                                                _p(rowsum), _stream(dev)))
+    return qx, sx, rowsum
+
+
+def w4a8_moe_grouped_gemm_i8(a: torch.Tensor, a_scale: torch.Tensor, a_rowsum: torch.Tensor,
+                             a_rows: torch.Tensor | None, offsets: torch.Tensor, w_packed: torch.Tensor,
+                             w_scale: torch.Tensor, out: torch.Tensor | None = None, M_total: int | None = None,
+                             algo: int = W4A8_GG_AUTO):
+    """int8 [*, K] activations x per-channel INT4 experts [E, N, K/8] (scales [E, N]) -> fp32 [M_total, N]."""
+    _need(a, "a", torch.int8, 2)
+    dev = a.device
+    _need(a_scale, "a_scale", torch.float32, 1, dev)
+    _need(a_rowsum, "a_rowsum", torch.int32, 1, dev)
+    _need(offsets, "offsets", torch.int32, 1, dev)
+    _need(w_packed, "w_packed", torch.int32, 3, dev)
+    _need(w_scale, "w_scale", torch.float32, 2, dev)
+    E, N, K8 = w_packed.shape
+    K = K8 * 8
+    if a.shape[1] != K or tuple(w_scale.shape) != (E, N) or offsets.numel() != E + 1:
+        raise ValueError("a must be [*, K], w_scale [E, N], offsets [E+1]")
+    if a_rows is not None:
+        _need(a_rows, "a_rows", torch.int32, 1, dev)
+        M = a_rows.numel() if M_total is None else M_total
+    else:
+        M = a.shape[0] if M_total is None else M_total
+    out = torch.empty((M, N), dtype=torch.float32, device=dev) if out is None else out
+    _need(out, "out", torch.float32, 2, dev)
+    if out.shape[0] < M or out.shape[1] != N:
+        raise ValueError("out must be at least [M_total, N]")
+    _check("w4a8_moe_grouped_gemm_i8",
+           lib().w4a8_moe_grouped_gemm_i8(_p(a), _p(a_scale), _p(a_rowsum), _p(a_rows), M, _p(offsets), E,
+                                          _p(w_packed), _p(w_scale), N, K, _p(out), algo, _stream(dev)))
+    return out
+
+
+def w4a8_moe_swiglu_i8(h: torch.Tensor, qa=None, sa=None, rowsum=None):
+    """fp32 [M, 2I] -> (int8 codes [M, I], scales fp32 [M], code row sums int32 [M])."""
+    _need(h, "h", torch.float32, 2)
+    M, I2 = h.shape
+    I = I2 // 2
+    dev = h.device
+    qa = torch.empty((M, I), dtype=torch.int8, device=dev) if qa is None else qa
+    sa = torch.empty((M,), dtype=torch.float32, device=dev) if sa is None else sa
+    rowsum = torch.empty((M,), dtype=torch.int32, device=dev) if rowsum is None else rowsum
+    _need(qa, "qa", torch.int8, 2, dev)
+    _need(sa, "sa", torch.float32, 1, dev)
+    _need(rowsum, "rowsum", torch.int32, 1, dev)
+    if I2 % 2 or tuple(qa.shape) != (M, I) or tuple(sa.shape) != (M,) or tuple(rowsum.shape) != (M,):
+        raise ValueError("h must be [M, 2I], qa [M, I], sa and rowsum [M]")
+    _check("w4a8_moe_swiglu_i8", lib().w4a8_moe_swiglu_i8(_p(h), M, I, _p(qa), _p(sa), _p(rowsum), _stream(dev)))
+    return qa, sa, rowsum
+
+
+def w4a8_moe_quantize_weights_channel(w: torch.Tensor, w_packed=None, w_scale=None):
+    """fp32 [..., K] -> (packed int32 [..., K/8], per-row scales fp32 [...])."""
+    if not isinstance(w, torch.Tensor) or w.dim() < 1:
+        raise TypeError("w must be a torch.Tensor with a K dimension")
+    _need(w, "w", torch.float32, w.dim())
+    K = w.shape[-1]
+    lead = tuple(w.shape[:-1])
+    rows = 1
+    for d in lead:
+        rows *= int(d)
+    dev = w.device
+    if K % 128:
+        raise ValueError("K must be a multiple of 128")
+    w_packed = torch.empty(lead + (K // 8,), dtype=torch.int32, device=dev) if w_packed is None else w_packed
+    w_scale = torch.empty(lead, dtype=torch.float32, device=dev) if w_scale is None else w_scale
+    _need(w_packed, "w_packed", torch.int32, len(lead) + 1, dev)
+    _need(w_scale, "w_scale", torch.float32, len(lead), dev)
+    if tuple(w_packed.shape) != lead + (K // 8,) or tuple(w_scale.shape) != lead:
+        raise ValueError("w_packed must be [..., K/8] and w_scale [...]")
+    _check("w4a8_moe_quantize_weights_channel",
+           lib().w4a8_moe_quantize_weights_channel(_p(w), rows, K, _p(w_packed), _p(w_scale), _stream(dev)))
     return w_packed, w_scale

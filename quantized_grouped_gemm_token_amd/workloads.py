@@ -19,7 +19,10 @@ intermediate size 2048 implied by the card's section 局限性 (TP8 slices of
   Zipf(1.1) law over a seeded ranking of the experts.
 
 Streams: numpy PCG64 seeded by SeedSequence(1000 + index), spawned in the
-fixed order W13, S13, W2, S2, x, outlier channels, logits, expert ranking.
+fixed order W13, S13, W2, S2, x, outlier channels, logits, expert ranking;
+a ninth child draws the per-channel scales of the per-channel INT4 x INT8
+variant (lognormal(-4, 0.5), fp32 [E, 2I] and [E, H]), which reuses the
+same packed words.
 """
 from __future__ import annotations
 
@@ -121,3 +124,12 @@ def make_config(index: int, with_weights: bool = True) -> Workload:
 def make_custom(T: int, H: int, I: int, E: int, k: int, seed: int, **kw) -> Workload:
     """A workload of any shape (tests: ragged tails, edge cases)."""
     return make_workload(Shape(f"custom T={T} H={H} I={I} E={E} top-{k}", T, H, I, E, k, **kw), seed)
+
+
+def channel_scales(wl: Workload) -> tuple[np.ndarray, np.ndarray]:
+    """Per-channel weight scales of the per-channel variant: fp32 [E, 2I] and [E, H]."""
+    sh = wl.shape
+    g = np.random.Generator(np.random.PCG64(np.random.SeedSequence(wl.seed).spawn(9)[8]))
+    s13 = g.lognormal(mean=-4.0, sigma=0.5, size=(sh.E, 2 * sh.I)).astype(np.float32)
+    s2 = g.lognormal(mean=-4.0, sigma=0.5, size=(sh.E, sh.H)).astype(np.float32)
+    return s13, s2
