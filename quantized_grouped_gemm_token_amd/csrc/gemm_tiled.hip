@@ -1,13 +1,11 @@
 // Grouped W4A8 GEMM, tiled form: for many rows per expert (prefill).
 //
-// A persistent kernel (one workgroup of kWaves waves per CU) walks the ragged
+// A persistent kernel (one workgroup of 8 waves per CU) walks the ragged
 // list of tiles of all experts.  A tile is up to 256 rows of one expert by
-// 256 output columns.  With 8 waves (two per SIMD, so that the matrix core
-// runs while the other wave does the per-group scale FMAs and the nibble
-// unpacking), wave w = 4 rg + cg owns the 64 columns 64 cg .. 64 cg + 63 and
-// the 32-row blocks rg, rg + 2, rg + 4, rg + 6
+// 256 output columns.  Wave w = 4 rg + cg owns the 64 columns 64 cg .. +63
+// (four 16-column B blocks) and the 16-row A blocks rg, rg + 2, .., rg + 14
 // (interleaved, so that a short tile still splits its rows over both row
-// groups).
+// groups): 8 x 4 products of 16x16x128 per K group, one MFMA each.
 //
 // K is walked one 128-wide group at a time through a 3-slot LDS ring filled
 // by direct global-to-LDS loads, two groups ahead.  Per group a slot holds
@@ -19,12 +17,19 @@
 //     instruction), swizzled the same way.
 // The group scales of 4 groups are loaded at once (16 bytes per column).
 //
+// Within a group the products are software-pipelined over the A blocks:
+// while the matrix core runs the four MFMAs of block i, the VALU applies the
+// group scale to block i - 1 (acc += s * D, one FMA per output), and the LDS
+// reads of block i + 1 are in flight.  Two waves share a SIMD, so one wave's
+// nibble unpacking also overlaps the other's products.
+//
 // The +8 offset of the uint4b8 nibbles is removed with the per-row sums of
 // the activation codes of each group (see gemm_common.hpp): each wave loads
 // exactly the activation rows whose sums it computes, with 16x16x128 MFMAs
 // against the constant -2^-6, so the sums of group g + 1 are computed in the
 // middle of group g's products, as soon as the wave's own loads of g + 1 have
-// landed, and are published by the one barrier per group.
+// landed, and are published by the one barrier per group.  They enter each
+// product as its accumulator input.
 //
 // Tile order: each XCD runs windows of consecutive tiles (an expert's tiles
 // are numbered N block by N block, M blocks adjacent) at the same time, so a
@@ -41,11 +46,15 @@ constexpr int kTM = 256;              // rows per tile
 constexpr int kTN = 256;              // columns per tile
 constexpr int kMaxExperts = 1024;
 constexpr int kXcds = 8;              // accelerator complex dies of an MI355X (round-robin dispatch)
-#ifndef GG_TILED_WAVES
-#define GG_TILED_WAVES 8                // waves per workgroup
-#define GG_TILED_NJ 2                   // 32-column blocks per wave
-#endif
-
+constexpr int kWaves = 8;             // waves per workgroup: 2 row groups x 4 column groups
+constexpr int kThreads = kWaves * kWave;
+constexpr int kColGroups = 4;
+constexpr int kRowGroups = kWaves / kColGroups;
+constexpr int kABlocks = kTM / 16 / kRowGroups;   // 16-row A blocks per wave
+constexpr int kBBlocks = kTN / 16 / kColGroups;   // 16-column B blocks per wave
+constexpr int kARows = kTM / kWaves;              // activation rows each wave loads (and sums)
+constexpr int kWCols = kTN / kWaves;              // weight columns each wave loads
+static_assert(kARows % 16 == 0 && kWCols % 16 == 0, "load roles");
 
 // One ring slot: the activation rows and the weight columns of one group.
 //   a: row r, 16-byte chunk c (K bytes 16c..16c+15 of the group) at r*128 + 16*(c ^ ((r >> 1) & 7))
@@ -94,20 +103,19 @@ __device__ __forceinline__ T lds_load(const void* p) {
 
 __device__ __forceinline__ int tiles_of(int rows, int nb) { return ((rows + kTM - 1) / kTM) * nb; }
 
-// kWaves waves per workgroup; each wave owns kNJ blocks of 32 columns.
 // kInt8: the per-channel variant (INT8 activations with row code sums
 // a_rowsum, one scale per weight row in w_scale [E][N]): int32 products
 // accumulated by the matrix core over all of K, no group scales, no row-sum
 // MFMAs; otherwise the group-128 FP8 form.
-template <int kWaves, int kNJ, bool kInt8>
-__global__ __launch_bounds__(kWaves * kWave, 1) void gg_tiled_kernel(const uint8_t* __restrict__ a,
-                                                              const float* __restrict__ a_scale,
-                                                              const int32_t* __restrict__ a_rowsum,
-                                                              const int32_t* __restrict__ a_rows,
-                                                              const int32_t* __restrict__ offsets, int E,
-                                                              const int32_t* __restrict__ w_packed,
-                                                              const float* __restrict__ w_scale, int64_t N,
-                                                              int64_t K, float* __restrict__ out) {
+template <bool kInt8>
+__global__ __launch_bounds__(kThreads, 1) void gg_tiled_kernel(const uint8_t* __restrict__ a,
+                                                               const float* __restrict__ a_scale,
+                                                               const int32_t* __restrict__ a_rowsum,
+                                                               const int32_t* __restrict__ a_rows,
+                                                               const int32_t* __restrict__ offsets, int E,
+                                                               const int32_t* __restrict__ w_packed,
+                                                               const float* __restrict__ w_scale, int64_t N,
+                                                               int64_t K, float* __restrict__ out) {
   __shared__ RingSlot ring0, ring1, ring2;
   __shared__ __attribute__((aligned(16))) float scq[2][4 * kTN];   // scale quads: [quad parity][column * 4 + g % 4]
                                                                     // (or [g % 4][column] when loaded per group)
@@ -115,18 +123,10 @@ __global__ __launch_bounds__(kWaves * kWave, 1) void gg_tiled_kernel(const uint8
   __shared__ __attribute__((aligned(16))) float ascale_sm[kTM];    // token scales of the tile's rows
   __shared__ int tile_start[kMaxExperts + 1];                      // first tile index of each expert
   __shared__ int wsum[kWaves];
-  constexpr int kThreads = kWaves * kWave;
-  constexpr int kColGroups = kTN / (32 * kNJ);         // waves side by side in N
-  constexpr int kRowGroups = kWaves / kColGroups;      // waves side by side in M
-  constexpr int kBlocks = (kTM / 32) / kRowGroups;     // 32-row blocks per wave
-  constexpr int kARows = kTM / kWaves;                 // activation rows each wave loads (and sums)
-  constexpr int kWCols = kTN / kWaves;                 // weight columns each wave loads
-  static_assert(kColGroups * kRowGroups == kWaves && kBlocks * kRowGroups * 32 == kTM, "wave grid");
-  static_assert(kARows % 16 == 0 && kWCols % 16 == 0, "load roles");
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: keeps wave-indexed values scalar
-  const int i32 = lane & 31, kh = lane >> 5;                   // 32x32 MFMA lane roles
+  const int lr = lane & 15, lq = lane >> 4;                    // 16x16x128 lane roles: row/column, K quarter
   const int rg = wave / kColGroups, cg = wave % kColGroups;    // row group, column group
   const int NB = (int)((N + kTN - 1) / kTN);
   const int G = (int)(K >> 7);
@@ -168,20 +168,14 @@ __global__ __launch_bounds__(kWaves * kWave, 1) void gg_tiled_kernel(const uint8
   }
   const int total = tile_start[E];
 
-  // lane-constant parts of the swizzled LDS addresses
-  const int fa = (i32 >> 1) & 7;                  // activation swizzle of rows 32b + i32
-  const int fw = (i32 >> 2) & 3;                  // weight swizzle of columns 32cg + i32
-  const uint32_t a_rd0 = (uint32_t)i32 * kGroup + 16u * (uint32_t)((2 * kh) ^ fa);       // half 0, K bytes 32kh..+15
-  const uint32_t a_rd1 = (uint32_t)i32 * kGroup + 16u * (uint32_t)((2 * kh + 1) ^ fa);   // half 0, +16..+31
-  const uint32_t a_rd2 = (uint32_t)i32 * kGroup + 16u * (uint32_t)((4 + 2 * kh) ^ fa);   // half 1
-  const uint32_t a_rd3 = (uint32_t)i32 * kGroup + 16u * (uint32_t)((5 + 2 * kh) ^ fa);
-  const uint32_t w_rd0 = (uint32_t)(32 * kNJ * cg + i32) * 64u + 16u * (uint32_t)(kh ^ fw);         // half 0
-  const uint32_t w_rd1 = (uint32_t)(32 * kNJ * cg + i32) * 64u + 16u * (uint32_t)((2 + kh) ^ fw);   // half 1
-  // the row-sum MFMAs of this wave's rows (16x16x128 layout: row lane % 16, K bytes 32 (lane / 16) ..)
-  const int bl = lane & 15, bq = lane >> 4;
-  const int fb = (bl >> 1) & 7;
-  const uint32_t b_rd0 = (uint32_t)(kARows * wave + bl) * kGroup + 16u * (uint32_t)((2 * bq) ^ fb);
-  const uint32_t b_rd1 = (uint32_t)(kARows * wave + bl) * kGroup + 16u * (uint32_t)((2 * bq + 1) ^ fb);
+  // lane-constant parts of the swizzled LDS addresses (the row or column
+  // bases of the blocks are multiples of 16, so the swizzle depends on lr only)
+  const int fa = (lr >> 1) & 7;                   // activation swizzle of row 16 b + lr
+  const uint32_t a_rd0 = (uint32_t)lr * kGroup + 16u * (uint32_t)((2 * lq) ^ fa);       // K bytes 32 lq .. +15
+  const uint32_t a_rd1 = (uint32_t)lr * kGroup + 16u * (uint32_t)((2 * lq + 1) ^ fa);   // K bytes 32 lq + 16 .. +31
+  const uint32_t w_rd = (uint32_t)(64 * cg + lr) * 64u + 16u * (uint32_t)(lq ^ ((lr >> 2) & 3));   // B block 0
+  // this wave's own activation rows, for the row-sum MFMAs
+  const uint32_t b_base = (uint32_t)(kARows * wave) * kGroup;   // wave-uniform
 
   // Tile t runs on the XCD and in the round that keep data sharing local:
   // workgroups are dispatched round-robin over the XCDs, so workgroup w sits
@@ -198,7 +192,7 @@ __global__ __launch_bounds__(kWaves * kWave, 1) void gg_tiled_kernel(const uint8
       const int mid = (lo_e + hi_e) >> 1;
       if (tile_start[mid] <= t) lo_e = mid; else hi_e = mid;
     }
-    const int e = lo_e;
+    const int e = __builtin_amdgcn_readfirstlane(lo_e);
     const int r_e = offsets[e], rows_e = offsets[e + 1] - r_e;
     const int mbs = (rows_e + kTM - 1) / kTM;
     const int local = t - tile_start[e];
@@ -207,7 +201,10 @@ __global__ __launch_bounds__(kWaves * kWave, 1) void gg_tiled_kernel(const uint8
     const int r0 = r_e + mb * kTM;
     const int mlen = min(kTM, rows_e - mb * kTM);
     const int n0 = nb * kTN;
-    const bool active = n0 + 32 * kNJ * cg < N;   // N % 64 == 0: a wave's column group is wholly in or out
+    // A blocks of this wave holding rows of the tile: blocks rg + 2 i < ceil(mlen / 16)
+    // (N % 64 == 0: a wave's column group is wholly in or out)
+    const int nact =
+        __builtin_amdgcn_readfirstlane(n0 + 64 * cg < N ? min(kABlocks, (((mlen + 15) >> 4) - rg + 1) >> 1) : 0);
 
     // ---- direct-load roles of this lane
     // activations: rows kARows wave + 8 q + lane / 8, chunk position lane % 8
@@ -223,13 +220,12 @@ __global__ __launch_bounds__(kWaves * kWave, 1) void gg_tiled_kernel(const uint8
     // weights: columns kWCols wave + 16 q + lane / 4 of the tile, chunk position lane % 4
     const __amdgpu_buffer_rsrc_t rw =
         buffer_rsrc(reinterpret_cast<const uint8_t*>(w_packed) + (int64_t)e * N * row_bytes, (uint32_t)N * row_bytes);
-    uint32_t woff[kWCols / 16];
-#pragma unroll
-    for (int q = 0; q < kWCols / 16; ++q) {
-      const int n = kWCols * wave + 16 * q + (lane >> 2);
-      const int c = (lane & 3) ^ ((n >> 2) & 3);
-      woff[q] = (uint32_t)min(n0 + n, (int)N - 1) * row_bytes + 16u * (uint32_t)c;
-    }
+    // (columns n and n + 16 q have the same swizzle, so one lane offset serves
+    // every q.  N % 64 == 0, so a wave's 32 columns are either all below N or
+    // all past it, where the lane offset itself is out of the buffer's range
+    // and the loads return zeros)
+    const uint32_t woff = (uint32_t)(n0 + kWCols * wave + (lane >> 2)) * row_bytes +
+                          16u * (uint32_t)((lane & 3) ^ ((lane >> 4) & 3));
     // scales (waves 0..3): column 64 wave + lane of the tile
     const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(w_scale + (int64_t)e * N * G, (uint32_t)(N * G * 4));
     const uint32_t soff = (uint32_t)min(n0 + 64 * (wave & 3) + lane, (int)N - 1) * (uint32_t)G * 4u;
@@ -252,7 +248,8 @@ __global__ __launch_bounds__(kWaves * kWave, 1) void gg_tiled_kernel(const uint8
       for (int q = 0; q < kARows / 8; ++q)
         dma16(ra, aoff[q], (uint32_t)g * kGroup, &sl.a[(kARows * wave + 8 * q) * kGroup]);
 #pragma unroll
-      for (int q = 0; q < kWCols / 16; ++q) dma16(rw, woff[q], (uint32_t)g * 64u, &sl.w[(kWCols * wave + 16 * q) * 64]);
+      for (int q = 0; q < kWCols / 16; ++q)
+        dma16(rw, woff, (uint32_t)g * 64u + (uint32_t)(16 * q) * row_bytes, &sl.w[(kWCols * wave + 16 * q) * 64]);
     };
     // loads that stage(g) issues on this wave
     auto stage_loads = [&](int g) {
@@ -271,167 +268,191 @@ __global__ __launch_bounds__(kWaves * kWave, 1) void gg_tiled_kernel(const uint8
       const RingSlot& sl = slot<decltype(S_)::value>(ring0, ring1, ring2);
 #pragma unroll
       for (int q = 0; q < kARows / 16; ++q) {
-        const i32x4 x0 = lds_load<i32x4>(&sl.a[b_rd0 + q * 16 * kGroup]);
-        const i32x4 x1 = lds_load<i32x4>(&sl.a[b_rd1 + q * 16 * kGroup]);
+        const i32x4 x0 = lds_load<i32x4>(&sl.a[b_base + a_rd0 + q * 16 * kGroup]);
+        const i32x4 x1 = lds_load<i32x4>(&sl.a[b_base + a_rd1 + q * 16 * kGroup]);
         const v8i av = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
         const v4f c = mfma16x16x128(av, bias_operand(), v4f{0.f, 0.f, 0.f, 0.f});
-        if (bl == 0) *reinterpret_cast<v4f*>(&bias_sm[g & 1][kARows * wave + 16 * q + 4 * bq]) = c;
+        if (lr == 0) *reinterpret_cast<v4f*>(&bias_sm[g & 1][kARows * wave + 16 * q + 4 * lq]) = c;
       }
     };
 
-    using Acc = std::conditional_t<kInt8, v16i, v16f>;
-    Acc acc[kBlocks][kNJ];
-#pragma unroll
-    for (int i = 0; i < kBlocks; ++i)
-#pragma unroll
-      for (int j = 0; j < kNJ; ++j)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) acc[i][j][v] = 0;
+    // The rest of the tile (K loop and epilogue) is compiled for kNB = 0, 1, 2,
+    // 4 and 8 A blocks per wave, without branches between the blocks; a wave
+    // with nact blocks holding rows runs the smallest kNB >= nact (the blocks
+    // past nact multiply clamped rows, which the epilogue drops).
+    auto run_tile = [=](auto NB_) mutable {
+      constexpr int kNB = decltype(NB_)::value;
+      using Acc = std::conditional_t<kInt8, i32x4, v4f>;
+      Acc acc[kNB > 0 ? kNB : 1][kBBlocks];
+  #pragma unroll
+      for (int i = 0; i < (kNB > 0 ? kNB : 1); ++i)
+  #pragma unroll
+        for (int j = 0; j < kBBlocks; ++j)
+  #pragma unroll
+          for (int v = 0; v < 4; ++v) acc[i][j][v] = 0;
 
-    // One K group in slot S: prefetch group g+2; multiply group g; in the
-    // middle, once this wave's loads of group g+1 have landed, publish that
-    // group's row sums; then one barrier.
-    auto step = [&](auto S_, int g) {
-      constexpr int S = decltype(S_)::value;
-      if (g >= G) return;
-      const bool more = g + 2 < G;
-      // scales of group g (read before this step's loads are issued: the only
-      // direct load into scq that can be in flight is the next quad's, issued
-      // first in its group, so waiting for it keeps that group's loads going)
-      float s[kNJ];
-      if constexpr (!kInt8) {
-#pragma unroll
-        for (int j = 0; j < kNJ; ++j) {
-          const int col = 32 * (kNJ * cg + j) + i32;
-          s[j] = scq[(g >> 2) & 1][vec_scales ? col * 4 + (g & 3) : (g & 3) * kTN + col];
-        }
-      }
-      if (more) stage(std::integral_constant<int, (S + 2) % 3>{}, g + 2);
-      const RingSlot& sl = slot<S>(ring0, ring1, ring2);
-      v8i b0[kNJ], b1[kNJ];
-      if (active) {
-#pragma unroll
-        for (int j = 0; j < kNJ; ++j) {
-          b0[j] = nibbles_to_fp8(lds_load<i32x4>(&sl.w[w_rd0 + j * 32 * 64]));
-          b1[j] = nibbles_to_fp8(lds_load<i32x4>(&sl.w[w_rd1 + j * 32 * 64]));
-        }
-      }
-      const float* bb = &bias_sm[g & 1][4 * kh];
-      auto block = [&](int i) {
-        const int blk = rg + kRowGroups * i;
-        if (active && 32 * blk < mlen) {
-          const uint8_t* ab = &sl.a[blk * 32 * kGroup];
-          const i32x4 x0 = lds_load<i32x4>(ab + a_rd0);
-          const i32x4 x1 = lds_load<i32x4>(ab + a_rd1);
-          const i32x4 x2 = lds_load<i32x4>(ab + a_rd2);
-          const i32x4 x3 = lds_load<i32x4>(ab + a_rd3);
-          const v8i a0 = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
-          const v8i a1 = {x2[0], x2[1], x2[2], x2[3], x3[0], x3[1], x3[2], x3[3]};
-          if constexpr (kInt8) {
-#pragma unroll
-            for (int j = 0; j < kNJ; ++j) {
-              acc[i][j] = mfma_i8_32x32x32(a0.lo, b0[j].lo, acc[i][j]);
-              acc[i][j] = mfma_i8_32x32x32(a0.hi, b0[j].hi, acc[i][j]);
-              acc[i][j] = mfma_i8_32x32x32(a1.lo, b1[j].lo, acc[i][j]);
-              acc[i][j] = mfma_i8_32x32x32(a1.hi, b1[j].hi, acc[i][j]);
-            }
-            return;
-          }
-#pragma unroll
-          for (int j = 0; j < kNJ; ++j) {
-            v16f c;   // the row sums enter as the accumulator input (read per column block: no copies)
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              const v4f t4 = lds_load<v4f>(bb + 32 * blk + 8 * q);
-#pragma unroll
-              for (int r = 0; r < 4; ++r) c[4 * q + r] = t4[r];
-            }
-            c = mfma32x32x64(a0, b0[j], c);
-            c = mfma32x32x64(a1, b1[j], c);
-#pragma unroll
-            for (int v = 0; v < 16; ++v) {
-              if constexpr (!kInt8) acc[i][j][v] = fmaf(s[j], c[v], acc[i][j][v]);
-            }
+      // One K group in slot S: prefetch group g+2; multiply group g; in the
+      // middle, once this wave's loads of group g+1 have landed, publish that
+      // group's row sums; then one barrier.
+      auto step = [&](auto S_, int g) {
+        constexpr int S = decltype(S_)::value;
+        if (g >= G) return;
+        const bool more = g + 2 < G;
+        // scales of group g (read before this step's loads are issued: the only
+        // direct load into scq that can be in flight is the next quad's, issued
+        // first in its group, so waiting for it keeps that group's loads going)
+        float s[kBBlocks];
+        if constexpr (!kInt8) {
+  #pragma unroll
+          for (int j = 0; j < kBBlocks; ++j) {
+            const int col = 64 * cg + 16 * j + lr;
+            s[j] = scq[(g >> 2) & 1][vec_scales ? col * 4 + (g & 3) : (g & 3) * kTN + col];
           }
         }
-      };
-      // this wave's loads of group g+1 landed (only those of group g+2 may stay in
-      // flight); then the row sums of group g+1
-      auto mid = [&]() {
-        if (more) wait_loads(stage_loads(g + 2));
-        else __builtin_amdgcn_s_waitcnt(0x0F70);              // vmcnt(0)
-        if (!kInt8 && g + 1 < G) row_sums(std::integral_constant<int, (S + 1) % 3>{}, g + 1);
-      };
+        if (more) stage(std::integral_constant<int, (S + 2) % 3>{}, g + 2);
+        const RingSlot& sl = slot<S>(ring0, ring1, ring2);
+        // this wave's loads of group g+1 landed (only those of group g+2 may stay
+        // in flight); then the row sums of group g+1
+        auto mid = [&]() {
+          if (more) wait_loads(stage_loads(g + 2));
+          else __builtin_amdgcn_s_waitcnt(0x0F70);              // vmcnt(0)
+          if (!kInt8 && g + 1 < G) row_sums(std::integral_constant<int, (S + 1) % 3>{}, g + 1);
+        };
+        // the products of this group: kNB A blocks x kBBlocks B blocks
+        auto compute = [&]() {
+          v8i b[kBBlocks];
 #pragma unroll
-      for (int i = 0; i < kBlocks / 2; ++i) block(i);
-      mid();
+          for (int j = 0; j < kBBlocks; ++j) b[j] = nibbles_to_fp8(lds_load<i32x4>(&sl.w[w_rd + j * 16 * 64]));
+          const float* bsum = &bias_sm[g & 1][16 * rg + 4 * lq];
+          // operands of A block i (row block rg + 2 i): two 16-byte halves of the lane's 32 K bytes
+          auto load_a = [&](int i) {
+            const uint8_t* ab = &sl.a[(16 * (rg + 2 * i)) * kGroup];
+            const i32x4 x0 = lds_load<i32x4>(ab + a_rd0);
+            const i32x4 x1 = lds_load<i32x4>(ab + a_rd1);
+            return v8i{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+          };
+          v8i av[2];
+          v4f bias[2];
+          v4f c[kBBlocks];   // products of the block in flight; each is scaled into acc just before it is reused
+          av[0] = load_a(0);
+          if constexpr (!kInt8) bias[0] = lds_load<v4f>(bsum);
+          auto scale_into = [&](auto I_, int j) {   // acc[i] += s * D for B block j
+            constexpr int i = decltype(I_)::value;
 #pragma unroll
-      for (int i = kBlocks / 2; i < kBlocks; ++i) block(i);
-      __builtin_amdgcn_s_waitcnt(0xC07F);                      // lgkmcnt(0): LDS writes done
+            for (int v = 0; v < 4; ++v) acc[i][j][v] = fmaf(s[j], c[j][v], acc[i][j][v]);
+            asm volatile("" : "+v"(acc[i][j]));   // the FMAs stay here: sunk later they would hold c live
+          };
+          // region i: the products of A block i, each right after the group
+          // scale of block i - 1 has been applied to the same B block (the
+          // matrix core runs block i while the VALU scales block i - 1); the LDS
+          // reads of block i + 1 are issued first
+          auto region = [&](auto I_) {
+            constexpr int i = decltype(I_)::value;
+            if constexpr (i < kNB) {
+              if constexpr (i + 1 < kNB) {
+                av[(i + 1) & 1] = load_a(i + 1);
+                if constexpr (!kInt8) bias[(i + 1) & 1] = lds_load<v4f>(bsum + 32 * (i + 1));
+              }
+#pragma unroll
+              for (int j = 0; j < kBBlocks; ++j) {
+                if constexpr (kInt8) {
+                  const v8i x = av[i & 1];
+                  const i32x4 a_lo = {x[0], x[1], x[2], x[3]}, a_hi = {x[4], x[5], x[6], x[7]};
+                  const i32x4 b_lo = {b[j][0], b[j][1], b[j][2], b[j][3]}, b_hi = {b[j][4], b[j][5], b[j][6], b[j][7]};
+                  acc[i][j] = mfma_i8_16x16x64(a_lo, b_lo, acc[i][j]);
+                  acc[i][j] = mfma_i8_16x16x64(a_hi, b_hi, acc[i][j]);
+                } else {
+                  if constexpr (i >= 1) scale_into(std::integral_constant<int, i - 1>{}, j);
+                  c[j] = mfma16x16x128(av[i & 1], b[j], bias[i & 1]);
+                }
+              }
+            } else if constexpr (!kInt8 && i == kNB && i >= 1) {
+#pragma unroll
+              for (int j = 0; j < kBBlocks; ++j) scale_into(std::integral_constant<int, i - 1>{}, j);
+            }
+            __builtin_amdgcn_sched_barrier(0);   // regions stay in order: no hoisting of later reads
+            if constexpr (i == (kNB - 1) / 2) mid();   // the middle of the group's products
+          };
+          region(std::integral_constant<int, 0>{});
+          region(std::integral_constant<int, 1>{});
+          region(std::integral_constant<int, 2>{});
+          region(std::integral_constant<int, 3>{});
+          region(std::integral_constant<int, 4>{});
+          region(std::integral_constant<int, 5>{});
+          region(std::integral_constant<int, 6>{});
+          region(std::integral_constant<int, 7>{});
+          region(std::integral_constant<int, 8>{});
+        };
+        if constexpr (kNB > 0) compute();
+        else mid();
+        __builtin_amdgcn_s_waitcnt(0xC07F);                      // lgkmcnt(0): LDS writes done
+        barrier_loads_in_flight();
+      };
+
+      // prologue: groups 0 and 1 in flight, this wave's rows of group 0 landed, their sums published
+      // (and the scale quad of groups 0..3, read after the barrier)
+      stage(std::integral_constant<int, 0>{}, 0);
+      if (G > 1) {
+        stage(std::integral_constant<int, 1>{}, 1);
+        wait_loads(stage_loads(1));
+      } else {
+        __builtin_amdgcn_s_waitcnt(0x0F70);
+      }
+      if (!kInt8) row_sums(std::integral_constant<int, 0>{}, 0);
+      __builtin_amdgcn_s_waitcnt(0xC07F);
       barrier_loads_in_flight();
-    };
+      // the token scales (and in the INT8 form the row code sums) of the tile's
+      // rows, read in the epilogue; every wave is past the previous epilogue
+      if (wave < 4) {
+        const int r = 64 * wave + lane;
+        const int p = r0 + min(r, mlen - 1);
+        const uint32_t src = (uint32_t)(a_rows ? a_rows[p] : p) * 4u;
+        dma4(buffer_rsrc(a_scale, 0xffffffffu), src, 0, &ascale_sm[64 * wave]);
+        if constexpr (kInt8) dma4(buffer_rsrc(a_rowsum, 0xffffffffu), src, 0, &rowsum_sm[64 * wave]);
+      }
 
-    // prologue: groups 0 and 1 in flight, this wave's rows of group 0 landed, their sums published
-    // (and the scale quad of groups 0..3, read after the barrier)
-    stage(std::integral_constant<int, 0>{}, 0);
-    if (G > 1) {
-      stage(std::integral_constant<int, 1>{}, 1);
-      wait_loads(stage_loads(1));
-    } else {
-      __builtin_amdgcn_s_waitcnt(0x0F70);
-    }
-    if (!kInt8) row_sums(std::integral_constant<int, 0>{}, 0);
-    __builtin_amdgcn_s_waitcnt(0xC07F);
-    barrier_loads_in_flight();
-    // the token scales (and in the INT8 form the row code sums) of the tile's
-    // rows, read in the epilogue; every wave is past the previous epilogue
-    if (wave < 4) {
-      const int r = 64 * wave + lane;
-      const int p = r0 + min(r, mlen - 1);
-      const uint32_t src = (uint32_t)(a_rows ? a_rows[p] : p) * 4u;
-      dma4(buffer_rsrc(a_scale, 0xffffffffu), src, 0, &ascale_sm[64 * wave]);
-      if constexpr (kInt8) dma4(buffer_rsrc(a_rowsum, 0xffffffffu), src, 0, &rowsum_sm[64 * wave]);
-    }
+      for (int g = 0; g < G; g += 3) {
+        step(std::integral_constant<int, 0>{}, g);
+        step(std::integral_constant<int, 1>{}, g + 1);
+        step(std::integral_constant<int, 2>{}, g + 2);
+      }
 
-    for (int g = 0; g < G; g += 3) {
-      step(std::integral_constant<int, 0>{}, g);
-      step(std::integral_constant<int, 1>{}, g + 1);
-      step(std::integral_constant<int, 2>{}, g + 2);
-    }
-
-    if (active) {
-#pragma unroll
-      for (int i = 0; i < kBlocks; ++i) {
-        const int blk = rg + kRowGroups * i;
-        if (32 * blk < mlen) {
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const int rt = 32 * blk + 8 * q + 4 * kh;
+      // ---- epilogue: D lane holds column lr of its B block, rows 4 lq .. +3 of its A block
+      if (kNB > 0) {
+        float ws[kBBlocks];
+        if constexpr (kInt8) {
+  #pragma unroll
+          for (int j = 0; j < kBBlocks; ++j) ws[j] = w_scale[(int64_t)e * N + n0 + 64 * cg + 16 * j + lr];
+        }
+  #pragma unroll
+        for (int i = 0; i < kABlocks; ++i) {
+          if (i < kNB && 16 * (rg + 2 * i) < mlen) {
+            const int rt = 16 * (rg + 2 * i) + 4 * lq;
             const v4f sc4 = lds_load<v4f>(&ascale_sm[rt]);
             i32x4 rs4 = {0, 0, 0, 0};
-            float ws[kNJ];
-            if constexpr (kInt8) {
-              rs4 = lds_load<i32x4>(&rowsum_sm[rt]);
-#pragma unroll
-              for (int j = 0; j < kNJ; ++j) ws[j] = w_scale[(int64_t)e * N + n0 + 32 * (kNJ * cg + j) + i32];
-            }
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              if (rt + r < mlen) {
-                const int64_t p = r0 + rt + r;
-#pragma unroll
-                for (int j = 0; j < kNJ; ++j) {
-                  float v;
-                  if constexpr (kInt8) v = (float)(acc[i][j][4 * q + r] - 8 * rs4[r]) * sc4[r] * ws[j];
-                  else v = acc[i][j][4 * q + r] * (sc4[r] * kUnitScale);
-                  __builtin_nontemporal_store(v, out + p * N + n0 + 32 * (kNJ * cg + j) + i32);
+            if constexpr (kInt8) rs4 = lds_load<i32x4>(&rowsum_sm[rt]);
+  #pragma unroll
+            for (int v = 0; v < 4; ++v) {
+              if (rt + v < mlen) {
+                float* orow = out + (int64_t)(r0 + rt + v) * N + n0 + 64 * cg + lr;
+  #pragma unroll
+                for (int j = 0; j < kBBlocks; ++j) {
+                  float y;
+                  if constexpr (kInt8) y = (float)(acc[i][j][v] - 8 * rs4[v]) * sc4[v] * ws[j];
+                  else y = acc[i][j][v] * (sc4[v] * kUnitScale);
+                  __builtin_nontemporal_store(y, orow + 16 * j);
                 }
               }
             }
           }
         }
       }
-    }
+    };
+    if (nact > 4) run_tile(std::integral_constant<int, 8>{});
+    else if (nact > 2) run_tile(std::integral_constant<int, 4>{});
+    else if (nact == 2) run_tile(std::integral_constant<int, 2>{});
+    else if (nact == 1) run_tile(std::integral_constant<int, 1>{});
+    else run_tile(std::integral_constant<int, 0>{});
   }
 }
 
@@ -453,13 +474,12 @@ hipError_t launch_gg_tiled(const GemmArgs& g, hipStream_t stream) {
   constexpr int64_t k4G = (int64_t)1 << 32;
   if (g.M_total * g.K >= k4G || g.M_total * 4 >= k4G || g.N * (g.K / 2) >= k4G || g.N * (g.K / 128) * 4 >= k4G)
     return launch_gg_stream(g, stream);
-  constexpr int kW = GG_TILED_WAVES, kJ = GG_TILED_NJ;
   if (g.a_rowsum)
-    hipLaunchKernelGGL((gg_tiled_kernel<kW, kJ, true>), dim3(cu_count()), dim3(kW * kWave), 0, stream, g.a,
-                       g.a_scale, g.a_rowsum, g.a_rows, g.offsets, g.E, g.w_packed, g.w_scale, g.N, g.K, g.out);
+    hipLaunchKernelGGL((gg_tiled_kernel<true>), dim3(cu_count()), dim3(kThreads), 0, stream, g.a, g.a_scale,
+                       g.a_rowsum, g.a_rows, g.offsets, g.E, g.w_packed, g.w_scale, g.N, g.K, g.out);
   else
-    hipLaunchKernelGGL((gg_tiled_kernel<kW, kJ, false>), dim3(cu_count()), dim3(kW * kWave), 0, stream, g.a,
-                       g.a_scale, nullptr, g.a_rows, g.offsets, g.E, g.w_packed, g.w_scale, g.N, g.K, g.out);
+    hipLaunchKernelGGL((gg_tiled_kernel<false>), dim3(cu_count()), dim3(kThreads), 0, stream, g.a, g.a_scale,
+                       nullptr, g.a_rows, g.offsets, g.E, g.w_packed, g.w_scale, g.N, g.K, g.out);
   return hipGetLastError();
 }
 

@@ -128,6 +128,7 @@ def _gemm_problem(rng, E, N, K, counts, src_rows=None):
     (5, 192, 128, [0, 0, 0, 5, 0], True),
     (2, 64, 1024, [300, 33], True),
     (8, 512, 640, [16, 16, 16, 16, 0, 15, 17, 1], False),
+    (3, 320, 256, [200, 241, 0], True),            # partial tiles of 7/8 row blocks; N not a multiple of 256
 ])
 def test_grouped_gemm(E, N, K, counts, gather, algo, rng):
     w, s, offsets, a, sa, rows = _gemm_problem(rng, E, N, K, counts, src_rows=40 if gather else None)
