@@ -1,27 +1,32 @@
 // Grouped W4A8 GEMM, tiled form: for many rows per expert (prefill).
 //
 // A persistent kernel (one workgroup of 8 waves per CU) walks the ragged
-// list of tiles of all experts.  A tile is up to 256 rows of one expert by
-// 256 output columns.  Wave w = 4 rg + cg owns the 64 columns 64 cg .. +63
-// (four 16-column B blocks) and the 16-row A blocks rg, rg + 2, .., rg + 14
-// (interleaved, so that a short tile still splits its rows over both row
-// groups): 8 x 4 products of 16x16x128 per K group, one MFMA each.
+// list of tiles of all experts.  An expert's rows are cut into square tiles
+// of up to 256 rows x 256 output columns, except a remainder of at most 128
+// rows, which gets wide tiles of 128 rows x 512 columns instead: half as many
+// tiles for the same weight bytes, so a short remainder costs about half as
+// much as it would in square tiles.
+//   square: wave w = 4 rg + cg owns the columns 64 cg .. +63 and the 16-row
+//           A blocks rg, rg + 2, .., rg + 14 (interleaved, so that a short
+//           tile still splits its rows over both row groups);
+//   wide:   wave w owns the columns 64 w .. +63 and the A blocks 0 .. 7.
+// Either way a wave computes up to 8 A blocks x 4 B blocks of 16x16x128
+// products per K group, one MFMA each.
 //
-// K is walked one 128-wide group at a time through a 3-slot LDS ring filled
-// by direct global-to-LDS loads, two groups ahead.  Per group a slot holds
-//   * the 256 activation rows (FP8 codes, gathered through a_rows): 128 bytes
-//     per row, loaded as 8 rows x 128 contiguous bytes per instruction; the
-//     16-byte chunks of a row are XOR-swizzled so that the MFMA operand reads
-//     are free of LDS bank conflicts;
-//   * the 256 weight columns: 64 packed bytes each (16 columns x 64 bytes per
-//     instruction), swizzled the same way.
-// The group scales of 4 groups are loaded at once (16 bytes per column).
+// K is walked one 128-wide group at a time through a 3-slot LDS ring (48 KB
+// per slot) filled by direct global-to-LDS loads, two groups ahead.  Per group
+// a slot holds the activation rows (FP8 codes, gathered through a_rows: 128
+// bytes per row, 8 rows per load instruction) and then the weight columns (64
+// packed bytes each, 16 columns per instruction).  The 16-byte chunks of a row
+// or column are XOR-swizzled so that the MFMA operand reads are free of LDS
+// bank conflicts.  The group scales of the tile's columns have a 3-slot ring
+// of their own (one 4-byte load per column and group).
 //
 // Within a group the products are software-pipelined over the A blocks:
-// while the matrix core runs the four MFMAs of block i, the VALU applies the
-// group scale to block i - 1 (acc += s * D, one FMA per output), and the LDS
-// reads of block i + 1 are in flight.  Two waves share a SIMD, so one wave's
-// nibble unpacking also overlaps the other's products.
+// the MFMAs of block i are issued between the group-scale FMAs of block i - 1
+// (acc += s * D, one FMA per output), and the LDS reads of block i + 1 are in
+// flight meanwhile.  The tile body is compiled for 0, 1, 2, 4 and 8 blocks per
+// wave, so that the hot loop has no per-block branches.
 //
 // The +8 offset of the uint4b8 nibbles is removed with the per-row sums of
 // the activation codes of each group (see gemm_common.hpp): each wave loads
@@ -31,10 +36,12 @@
 // landed, and are published by the one barrier per group.  They enter each
 // product as its accumulator input.
 //
-// Tile order: each XCD runs windows of consecutive tiles (an expert's tiles
-// are numbered N block by N block, M blocks adjacent) at the same time, so a
-// weight tile and an activation block are fetched from HBM about once and
-// served to the other tiles of the window by that XCD's L2.
+// Tile order: an expert's tiles are numbered by pairs of 256-column blocks:
+// the square tiles of both blocks (M blocks adjacent), then the wide tile
+// that covers the same 512 columns.  Each XCD runs windows of consecutive
+// tiles at the same time, so a weight tile and an activation block are
+// fetched from HBM about once and served to the other tiles of the window by
+// that XCD's L2.
 #include "gemm_common.hpp"
 #include "kernels.hpp"
 
@@ -42,33 +49,32 @@
 
 namespace w4a8 {
 
-constexpr int kTM = 256;              // rows per tile
-constexpr int kTN = 256;              // columns per tile
+constexpr int kTM = 256;              // rows of a square tile
+constexpr int kTN = 256;              // columns of a square tile
+constexpr int kWideRows = 128;        // rows of a wide tile (the most a remainder has)
+constexpr int kWideCols = 512;        // columns of a wide tile
 constexpr int kMaxExperts = 1024;
 constexpr int kXcds = 8;              // accelerator complex dies of an MI355X (round-robin dispatch)
-constexpr int kWaves = 8;             // waves per workgroup: 2 row groups x 4 column groups
+constexpr int kWaves = 8;             // waves per workgroup
 constexpr int kThreads = kWaves * kWave;
-constexpr int kColGroups = 4;
-constexpr int kRowGroups = kWaves / kColGroups;
-constexpr int kABlocks = kTM / 16 / kRowGroups;   // 16-row A blocks per wave
-constexpr int kBBlocks = kTN / 16 / kColGroups;   // 16-column B blocks per wave
-constexpr int kARows = kTM / kWaves;              // activation rows each wave loads (and sums)
-constexpr int kWCols = kTN / kWaves;              // weight columns each wave loads
-static_assert(kARows % 16 == 0 && kWCols % 16 == 0, "load roles");
+constexpr int kABlocks = 8;           // 16-row A blocks per wave (at most)
+constexpr int kBBlocks = 4;           // 16-column B blocks per wave
+constexpr int kSlotBytes = kTM * kGroup + kTN * kGroup / 2;   // 48 KB: either tile shape's group
+static_assert(kSlotBytes == kWideRows * kGroup + kWideCols * kGroup / 2, "slot sizes");
 
-// One ring slot: the activation rows and the weight columns of one group.
+// One ring slot: the activation rows of one group, then its weight columns.
 //   a: row r, 16-byte chunk c (K bytes 16c..16c+15 of the group) at r*128 + 16*(c ^ ((r >> 1) & 7))
-//   w: column n, chunk c (packed bytes 16c..16c+15) at n*64 + 16*(c ^ ((n >> 2) & 3))
+//   w: column n, chunk c (packed bytes 16c..16c+15) at W + n*64 + 16*(c ^ ((n >> 2) & 3)),
+//      W = 256 * 128 (square tile) or 128 * 128 (wide tile)
 // The three slots are separate LDS variables addressed with compile-time
 // slot numbers, so that the compiler can tell the slot being read from the
 // slots still being filled.
 struct __attribute__((aligned(16))) RingSlot {
-  uint8_t a[kTM * kGroup];
-  uint8_t w[kTN * kGroup / 2];
+  uint8_t b[kSlotBytes];
 };
 
-template <int S>
-__device__ __forceinline__ RingSlot& slot(RingSlot& r0, RingSlot& r1, RingSlot& r2) {
+template <int S, typename T>
+__device__ __forceinline__ T& slot(T& r0, T& r1, T& r2) {
   if constexpr (S == 0) return r0;
   else if constexpr (S == 1) return r1;
   else return r2;
@@ -101,7 +107,14 @@ __device__ __forceinline__ T lds_load(const void* p) {
   return *reinterpret_cast<const T*>(__builtin_assume_aligned(p, 16));
 }
 
-__device__ __forceinline__ int tiles_of(int rows, int nb) { return ((rows + kTM - 1) / kTM) * nb; }
+// tiles of an expert with `rows` rows: square tiles per 256-column block (the
+// full 256-row blocks, and a remainder above 128 rows), plus one wide tile per
+// 512 columns for a remainder of 1..128 rows
+__device__ __forceinline__ int square_mblocks(int rows) { return rows / kTM + (rows % kTM > kWideRows ? 1 : 0); }
+__device__ __forceinline__ int has_wide(int rows) { return (rows % kTM != 0 && rows % kTM <= kWideRows) ? 1 : 0; }
+__device__ __forceinline__ int tiles_of(int rows, int nb, int nw) {
+  return square_mblocks(rows) * nb + has_wide(rows) * nw;
+}
 
 // kInt8: the per-channel variant (INT8 activations with row code sums
 // a_rowsum, one scale per weight row in w_scale [E][N]): int32 products
@@ -117,8 +130,7 @@ __global__ __launch_bounds__(kThreads, 1) void gg_tiled_kernel(const uint8_t* __
                                                                const float* __restrict__ w_scale, int64_t N,
                                                                int64_t K, float* __restrict__ out) {
   __shared__ RingSlot ring0, ring1, ring2;
-  __shared__ __attribute__((aligned(16))) float scq[2][4 * kTN];   // scale quads: [quad parity][column * 4 + g % 4]
-                                                                    // (or [g % 4][column] when loaded per group)
+  __shared__ __attribute__((aligned(16))) float sc0[kWideCols], sc1[kWideCols], sc2[kWideCols];   // group scales
   __shared__ __attribute__((aligned(16))) float bias_sm[2][kTM];   // -2^-6 * group code sums: [group parity][row]
   __shared__ __attribute__((aligned(16))) float ascale_sm[kTM];    // token scales of the tile's rows
   __shared__ int tile_start[kMaxExperts + 1];                      // first tile index of each expert
@@ -127,12 +139,10 @@ __global__ __launch_bounds__(kThreads, 1) void gg_tiled_kernel(const uint8_t* __
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: keeps wave-indexed values scalar
   const int lr = lane & 15, lq = lane >> 4;                    // 16x16x128 lane roles: row/column, K quarter
-  const int rg = wave / kColGroups, cg = wave % kColGroups;    // row group, column group
-  const int NB = (int)((N + kTN - 1) / kTN);
+  const int NB = (int)((N + kTN - 1) / kTN);                   // 256-column blocks
+  const int NW = (NB + 1) / 2;                                 // 512-column blocks
   const int G = (int)(K >> 7);
   const uint32_t row_bytes = (uint32_t)(K >> 1);
-  // scale quads as 16-byte loads need 4 | G and a 16-byte aligned scale array
-  const bool vec_scales = (G & 3) == 0 && (reinterpret_cast<uintptr_t>(w_scale) & 15) == 0;
   int* rowsum_sm = reinterpret_cast<int*>(&bias_sm[0][0]);   // the INT8 form has no group sums: row code sums
 
   // ---- tile numbering: exclusive prefix of per-expert tile counts (wave-level scans)
@@ -143,7 +153,7 @@ __global__ __launch_bounds__(kThreads, 1) void gg_tiled_kernel(const uint8_t* __
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
       const int ex = tid * kPer + i;
-      cnt[i] = ex < E ? tiles_of(offsets[ex + 1] - offsets[ex], NB) : 0;
+      cnt[i] = ex < E ? tiles_of(offsets[ex + 1] - offsets[ex], NB, NW) : 0;
       local += cnt[i];
     }
     int incl = local;
@@ -173,9 +183,7 @@ __global__ __launch_bounds__(kThreads, 1) void gg_tiled_kernel(const uint8_t* __
   const int fa = (lr >> 1) & 7;                   // activation swizzle of row 16 b + lr
   const uint32_t a_rd0 = (uint32_t)lr * kGroup + 16u * (uint32_t)((2 * lq) ^ fa);       // K bytes 32 lq .. +15
   const uint32_t a_rd1 = (uint32_t)lr * kGroup + 16u * (uint32_t)((2 * lq + 1) ^ fa);   // K bytes 32 lq + 16 .. +31
-  const uint32_t w_rd = (uint32_t)(64 * cg + lr) * 64u + 16u * (uint32_t)(lq ^ ((lr >> 2) & 3));   // B block 0
-  // this wave's own activation rows, for the row-sum MFMAs
-  const uint32_t b_base = (uint32_t)(kARows * wave) * kGroup;   // wave-uniform
+  const uint32_t w_rd_lane = (uint32_t)lr * 64u + 16u * (uint32_t)(lq ^ ((lr >> 2) & 3));
 
   // Tile t runs on the XCD and in the round that keep data sharing local:
   // workgroups are dispatched round-robin over the XCDs, so workgroup w sits
@@ -186,7 +194,7 @@ __global__ __launch_bounds__(kThreads, 1) void gg_tiled_kernel(const uint8_t* __
   const int window = grid / kXcds;
   const int my_slot = xcd_windows ? (int)(blockIdx.x % kXcds) * window + (int)(blockIdx.x / kXcds) : (int)blockIdx.x;
   for (int t = my_slot; t < total; t += grid) {
-    // ---- which expert, M block and N block
+    // ---- which expert, and which tile of it
     int lo_e = 0, hi_e = E;                    // tile_start[lo_e] <= t < tile_start[hi_e]
     while (hi_e - lo_e > 1) {
       const int mid = (lo_e + hi_e) >> 1;
@@ -194,102 +202,112 @@ __global__ __launch_bounds__(kThreads, 1) void gg_tiled_kernel(const uint8_t* __
     }
     const int e = __builtin_amdgcn_readfirstlane(lo_e);
     const int r_e = offsets[e], rows_e = offsets[e + 1] - r_e;
-    const int mbs = (rows_e + kTM - 1) / kTM;
+    const int msq = square_mblocks(rows_e), wide = has_wide(rows_e);
     const int local = t - tile_start[e];
-    const int mb = local % mbs;
-    const int nb = local / mbs;
-    const int r0 = r_e + mb * kTM;
-    const int mlen = min(kTM, rows_e - mb * kTM);
-    const int n0 = nb * kTN;
-    // A blocks of this wave holding rows of the tile: blocks rg + 2 i < ceil(mlen / 16)
-    // (N % 64 == 0: a wave's column group is wholly in or out)
-    const int nact =
-        __builtin_amdgcn_readfirstlane(n0 + 64 * cg < N ? min(kABlocks, (((mlen + 15) >> 4) - rg + 1) >> 1) : 0);
-
-    // ---- direct-load roles of this lane
-    // activations: rows kARows wave + 8 q + lane / 8, chunk position lane % 8
-    const __amdgpu_buffer_rsrc_t ra = buffer_rsrc(a, 0xffffffffu);
-    uint32_t aoff[kARows / 8];
-#pragma unroll
-    for (int q = 0; q < kARows / 8; ++q) {
-      const int r = kARows * wave + 8 * q + (lane >> 3);
-      const int p = r0 + min(r, mlen - 1);
-      const int c = (lane & 7) ^ ((r >> 1) & 7);
-      aoff[q] = (uint32_t)(a_rows ? a_rows[p] : p) * (uint32_t)K + 16u * (uint32_t)c;
+    const int per_pair = 2 * msq + wide;       // tiles of one pair of 256-column blocks
+    const int pair = local / per_pair, rp = local - pair * per_pair;
+    bool is_wide;
+    int r0, mlen, n0;
+    if (rp < msq || (2 * pair + 1 < NB && rp < 2 * msq)) {
+      const int nb = rp < msq ? 2 * pair : 2 * pair + 1;
+      const int mb = rp < msq ? rp : rp - msq;
+      is_wide = false;
+      r0 = r_e + mb * kTM;
+      mlen = min(kTM, rows_e - mb * kTM);
+      n0 = nb * kTN;
+    } else {
+      is_wide = true;
+      r0 = r_e + (rows_e / kTM) * kTM;
+      mlen = rows_e % kTM;
+      n0 = pair * kWideCols;
     }
-    // weights: columns kWCols wave + 16 q + lane / 4 of the tile, chunk position lane % 4
-    const __amdgpu_buffer_rsrc_t rw =
-        buffer_rsrc(reinterpret_cast<const uint8_t*>(w_packed) + (int64_t)e * N * row_bytes, (uint32_t)N * row_bytes);
-    // (columns n and n + 16 q have the same swizzle, so one lane offset serves
-    // every q.  N % 64 == 0, so a wave's 32 columns are either all below N or
-    // all past it, where the lane offset itself is out of the buffer's range
-    // and the loads return zeros)
-    const uint32_t woff = (uint32_t)(n0 + kWCols * wave + (lane >> 2)) * row_bytes +
-                          16u * (uint32_t)((lane & 3) ^ ((lane >> 4) & 3));
-    // scales (waves 0..3): column 64 wave + lane of the tile
-    const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(w_scale + (int64_t)e * N * G, (uint32_t)(N * G * 4));
-    const uint32_t soff = (uint32_t)min(n0 + 64 * (wave & 3) + lane, (int)N - 1) * (uint32_t)G * 4u;
-    const bool scale_loader = !kInt8 && wave < 4;   // the group-scale quads (FP8 form)
 
-    // loads of group g into slot S (and, on every fourth group, first the scale quad of groups g .. g+3:
-    // issued first, a wait for it leaves the group's other loads in flight)
-    auto stage = [&](auto S_, int g) {
-      RingSlot& sl = slot<decltype(S_)::value>(ring0, ring1, ring2);
-      if (scale_loader && (g & 3) == 0) {
-        float* dst = &scq[(g >> 2) & 1][0];
-        if (vec_scales) {
-          dma16(rs, soff, (uint32_t)g * 4u, dst + 256 * wave);
-        } else {
-#pragma unroll
-          for (int j = 0; j < 4; ++j) dma4(rs, soff, (uint32_t)(g + j) * 4u, dst + kTN * j + 64 * wave);
-        }
-      }
-#pragma unroll
-      for (int q = 0; q < kARows / 8; ++q)
-        dma16(ra, aoff[q], (uint32_t)g * kGroup, &sl.a[(kARows * wave + 8 * q) * kGroup]);
-#pragma unroll
-      for (int q = 0; q < kWCols / 16; ++q)
-        dma16(rw, woff, (uint32_t)g * 64u + (uint32_t)(16 * q) * row_bytes, &sl.w[(kWCols * wave + 16 * q) * 64]);
-    };
-    // loads that stage(g) issues on this wave
-    auto stage_loads = [&](int g) {
-      return kARows / 8 + kWCols / 16 + ((scale_loader && (g & 3) == 0) ? (vec_scales ? 1 : 4) : 0);
-    };
-    // wait until at most n of this wave's loads are in flight (n is one of the stage_loads values)
-    auto wait_loads = [&](int n) {
-      constexpr int base = kARows / 8 + kWCols / 16;
-      static_assert(base + 4 <= 15, "vmcnt field");
-      if (n == base) __builtin_amdgcn_s_waitcnt(0x0F70 | base);
-      else if (n == base + 1) __builtin_amdgcn_s_waitcnt(0x0F70 | (base + 1));
-      else __builtin_amdgcn_s_waitcnt(0x0F70 | (base + 4));
-    };
-    // -2^-6 * (sum of the activation codes) of this wave's rows for the group in slot S
-    auto row_sums = [&](auto S_, int g) {
-      const RingSlot& sl = slot<decltype(S_)::value>(ring0, ring1, ring2);
-#pragma unroll
-      for (int q = 0; q < kARows / 16; ++q) {
-        const i32x4 x0 = lds_load<i32x4>(&sl.a[b_base + a_rd0 + q * 16 * kGroup]);
-        const i32x4 x1 = lds_load<i32x4>(&sl.a[b_base + a_rd1 + q * 16 * kGroup]);
-        const v8i av = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
-        const v4f c = mfma16x16x128(av, bias_operand(), v4f{0.f, 0.f, 0.f, 0.f});
-        if (lr == 0) *reinterpret_cast<v4f*>(&bias_sm[g & 1][kARows * wave + 16 * q + 4 * lq]) = c;
-      }
-    };
-
-    // The rest of the tile (K loop and epilogue) is compiled for kNB = 0, 1, 2,
-    // 4 and 8 A blocks per wave, without branches between the blocks; a wave
-    // with nact blocks holding rows runs the smallest kNB >= nact (the blocks
-    // past nact multiply clamped rows, which the epilogue drops).
-    auto run_tile = [=](auto NB_) mutable {
+    // The rest of the tile (K loop and epilogue) is compiled per tile shape
+    // and per number kNB of A blocks of the wave (0, 1, 2, 4 or 8), without
+    // branches between the blocks; a wave with nact blocks holding rows runs
+    // the smallest kNB >= nact (the blocks past nact multiply clamped rows,
+    // which the epilogue drops).
+    auto run_tile = [=](auto W_, auto NB_) mutable {
+      constexpr bool kWide = decltype(W_)::value;
       constexpr int kNB = decltype(NB_)::value;
+      constexpr int kRows = kWide ? kWideRows : kTM;       // rows of the tile
+      constexpr int kCols = kWide ? kWideCols : kTN;       // columns of the tile
+      constexpr int kARows = kRows / kWaves;               // activation rows each wave loads (and sums)
+      constexpr int kWCols = kCols / kWaves;               // weight columns each wave loads
+      constexpr int kALoads = kARows / 8, kWLoads = kWCols / 16;
+      constexpr uint32_t kWBase = kRows * kGroup;          // weight columns' offset in a slot
+      constexpr int kBlockStride = kWide ? 16 : 32;        // rows between a wave's A blocks
+      const int rg = kWide ? 0 : wave >> 2;                // row group (its first A block)
+      const int cg = kWide ? wave : wave & 3;              // column group (64 columns)
+      // this wave's group scales: columns 64 wave + lane (FP8 form; square tiles: waves 0..3)
+      const bool scale_loader = !kInt8 && (kWide || wave < 4);
+
+      // ---- direct-load roles of this lane
+      // activations: rows kARows wave + 8 q + lane / 8, chunk position lane % 8
+      const __amdgpu_buffer_rsrc_t ra = buffer_rsrc(a, 0xffffffffu);
+      uint32_t aoff[kALoads];
+#pragma unroll
+      for (int q = 0; q < kALoads; ++q) {
+        const int r = kARows * wave + 8 * q + (lane >> 3);
+        const int p = r0 + min(r, mlen - 1);
+        const int c = (lane & 7) ^ ((r >> 1) & 7);
+        aoff[q] = (uint32_t)(a_rows ? a_rows[p] : p) * (uint32_t)K + 16u * (uint32_t)c;
+      }
+      // weights: columns kWCols wave + 16 q + lane / 4 of the tile, chunk position lane % 4.
+      // Columns n and n + 16 q have the same swizzle, so one lane offset serves
+      // every q.  N % 64 == 0, so a wave's columns are either all below N or all
+      // past it, where the lane offset itself is out of the buffer's range and
+      // the loads return zeros.
+      const __amdgpu_buffer_rsrc_t rw =
+          buffer_rsrc(reinterpret_cast<const uint8_t*>(w_packed) + (int64_t)e * N * row_bytes, (uint32_t)N * row_bytes);
+      const uint32_t woff = (uint32_t)(n0 + kWCols * wave + (lane >> 2)) * row_bytes +
+                            16u * (uint32_t)((lane & 3) ^ ((lane >> 4) & 3));
+      const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(w_scale + (int64_t)e * N * G, (uint32_t)(N * G * 4));
+      const uint32_t soff = (uint32_t)min(n0 + 64 * wave + lane, (int)N - 1) * (uint32_t)G * 4u;
+
+      // loads of group g into slot S: the group scales, the activation rows, the weight columns
+      auto stage = [&](auto S_, int g) {
+        constexpr int S = decltype(S_)::value;
+        RingSlot& sl = slot<S>(ring0, ring1, ring2);
+        if (scale_loader) dma4(rs, soff, (uint32_t)g * 4u, &slot<S>(sc0, sc1, sc2)[64 * wave]);
+#pragma unroll
+        for (int q = 0; q < kALoads; ++q)
+          dma16(ra, aoff[q], (uint32_t)g * kGroup, &sl.b[(kARows * wave + 8 * q) * kGroup]);
+#pragma unroll
+        for (int q = 0; q < kWLoads; ++q)
+          dma16(rw, woff, (uint32_t)g * 64u + (uint32_t)(16 * q) * row_bytes,
+                &sl.b[kWBase + (kWCols * wave + 16 * q) * 64]);
+      };
+      // wait until only the loads of the group issued last are in flight
+      auto wait_last_stage = [&]() {
+        constexpr int kBase = kALoads + kWLoads;
+        static_assert(kBase + 1 <= 15, "vmcnt field");
+        if (scale_loader) __builtin_amdgcn_s_waitcnt(0x0F70 | (kBase + 1));
+        else __builtin_amdgcn_s_waitcnt(0x0F70 | kBase);
+      };
+      // -2^-6 * (sum of the activation codes) of this wave's rows for the group in slot S
+      auto row_sums = [&](auto S_, int g) {
+        const RingSlot& sl = slot<decltype(S_)::value>(ring0, ring1, ring2);
+#pragma unroll
+        for (int q = 0; q < kARows / 16; ++q) {
+          const i32x4 x0 = lds_load<i32x4>(&sl.b[(kARows * wave + 16 * q) * kGroup + a_rd0]);
+          const i32x4 x1 = lds_load<i32x4>(&sl.b[(kARows * wave + 16 * q) * kGroup + a_rd1]);
+          const v8i av = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+          const v4f c = mfma16x16x128(av, bias_operand(), v4f{0.f, 0.f, 0.f, 0.f});
+          if (lr == 0) *reinterpret_cast<v4f*>(&bias_sm[g & 1][kARows * wave + 16 * q + 4 * lq]) = c;
+        }
+      };
+
       using Acc = std::conditional_t<kInt8, i32x4, v4f>;
       Acc acc[kNB > 0 ? kNB : 1][kBBlocks];
-  #pragma unroll
+#pragma unroll
       for (int i = 0; i < (kNB > 0 ? kNB : 1); ++i)
-  #pragma unroll
+#pragma unroll
         for (int j = 0; j < kBBlocks; ++j)
-  #pragma unroll
+#pragma unroll
           for (int v = 0; v < 4; ++v) acc[i][j][v] = 0;
+      const uint32_t a_blk0 = (uint32_t)(16 * rg) * kGroup;             // first A block of the wave
+      const uint32_t w_rd = kWBase + (uint32_t)(64 * cg) * 64u + w_rd_lane;
 
       // One K group in slot S: prefetch group g+2; multiply group g; in the
       // middle, once this wave's loads of group g+1 have landed, publish that
@@ -298,23 +316,18 @@ __global__ __launch_bounds__(kThreads, 1) void gg_tiled_kernel(const uint8_t* __
         constexpr int S = decltype(S_)::value;
         if (g >= G) return;
         const bool more = g + 2 < G;
-        // scales of group g (read before this step's loads are issued: the only
-        // direct load into scq that can be in flight is the next quad's, issued
-        // first in its group, so waiting for it keeps that group's loads going)
+        // scales of group g
         float s[kBBlocks];
         if constexpr (!kInt8) {
-  #pragma unroll
-          for (int j = 0; j < kBBlocks; ++j) {
-            const int col = 64 * cg + 16 * j + lr;
-            s[j] = scq[(g >> 2) & 1][vec_scales ? col * 4 + (g & 3) : (g & 3) * kTN + col];
-          }
+#pragma unroll
+          for (int j = 0; j < kBBlocks; ++j) s[j] = slot<S>(sc0, sc1, sc2)[64 * cg + 16 * j + lr];
         }
         if (more) stage(std::integral_constant<int, (S + 2) % 3>{}, g + 2);
         const RingSlot& sl = slot<S>(ring0, ring1, ring2);
         // this wave's loads of group g+1 landed (only those of group g+2 may stay
         // in flight); then the row sums of group g+1
         auto mid = [&]() {
-          if (more) wait_loads(stage_loads(g + 2));
+          if (more) wait_last_stage();
           else __builtin_amdgcn_s_waitcnt(0x0F70);              // vmcnt(0)
           if (!kInt8 && g + 1 < G) row_sums(std::integral_constant<int, (S + 1) % 3>{}, g + 1);
         };
@@ -322,11 +335,11 @@ __global__ __launch_bounds__(kThreads, 1) void gg_tiled_kernel(const uint8_t* __
         auto compute = [&]() {
           v8i b[kBBlocks];
 #pragma unroll
-          for (int j = 0; j < kBBlocks; ++j) b[j] = nibbles_to_fp8(lds_load<i32x4>(&sl.w[w_rd + j * 16 * 64]));
+          for (int j = 0; j < kBBlocks; ++j) b[j] = nibbles_to_fp8(lds_load<i32x4>(&sl.b[w_rd + j * 16 * 64]));
           const float* bsum = &bias_sm[g & 1][16 * rg + 4 * lq];
-          // operands of A block i (row block rg + 2 i): two 16-byte halves of the lane's 32 K bytes
+          // operands of A block i: two 16-byte halves of the lane's 32 K bytes
           auto load_a = [&](int i) {
-            const uint8_t* ab = &sl.a[(16 * (rg + 2 * i)) * kGroup];
+            const uint8_t* ab = &sl.b[a_blk0 + (uint32_t)(kBlockStride * i) * kGroup];
             const i32x4 x0 = lds_load<i32x4>(ab + a_rd0);
             const i32x4 x1 = lds_load<i32x4>(ab + a_rd1);
             return v8i{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
@@ -351,7 +364,7 @@ __global__ __launch_bounds__(kThreads, 1) void gg_tiled_kernel(const uint8_t* __
             if constexpr (i < kNB) {
               if constexpr (i + 1 < kNB) {
                 av[(i + 1) & 1] = load_a(i + 1);
-                if constexpr (!kInt8) bias[(i + 1) & 1] = lds_load<v4f>(bsum + 32 * (i + 1));
+                if constexpr (!kInt8) bias[(i + 1) & 1] = lds_load<v4f>(bsum + kBlockStride * (i + 1));
               }
 #pragma unroll
               for (int j = 0; j < kBBlocks; ++j) {
@@ -390,11 +403,10 @@ __global__ __launch_bounds__(kThreads, 1) void gg_tiled_kernel(const uint8_t* __
       };
 
       // prologue: groups 0 and 1 in flight, this wave's rows of group 0 landed, their sums published
-      // (and the scale quad of groups 0..3, read after the barrier)
       stage(std::integral_constant<int, 0>{}, 0);
       if (G > 1) {
         stage(std::integral_constant<int, 1>{}, 1);
-        wait_loads(stage_loads(1));
+        wait_last_stage();
       } else {
         __builtin_amdgcn_s_waitcnt(0x0F70);
       }
@@ -403,7 +415,7 @@ __global__ __launch_bounds__(kThreads, 1) void gg_tiled_kernel(const uint8_t* __
       barrier_loads_in_flight();
       // the token scales (and in the INT8 form the row code sums) of the tile's
       // rows, read in the epilogue; every wave is past the previous epilogue
-      if (wave < 4) {
+      if (wave < kRows / 64) {
         const int r = 64 * wave + lane;
         const int p = r0 + min(r, mlen - 1);
         const uint32_t src = (uint32_t)(a_rows ? a_rows[p] : p) * 4u;
@@ -418,24 +430,24 @@ __global__ __launch_bounds__(kThreads, 1) void gg_tiled_kernel(const uint8_t* __
       }
 
       // ---- epilogue: D lane holds column lr of its B block, rows 4 lq .. +3 of its A block
-      if (kNB > 0) {
+      if constexpr (kNB > 0) {
         float ws[kBBlocks];
         if constexpr (kInt8) {
-  #pragma unroll
+#pragma unroll
           for (int j = 0; j < kBBlocks; ++j) ws[j] = w_scale[(int64_t)e * N + n0 + 64 * cg + 16 * j + lr];
         }
-  #pragma unroll
-        for (int i = 0; i < kABlocks; ++i) {
-          if (i < kNB && 16 * (rg + 2 * i) < mlen) {
-            const int rt = 16 * (rg + 2 * i) + 4 * lq;
+#pragma unroll
+        for (int i = 0; i < kNB; ++i) {
+          if (16 * rg + kBlockStride * i < mlen) {
+            const int rt = 16 * rg + kBlockStride * i + 4 * lq;
             const v4f sc4 = lds_load<v4f>(&ascale_sm[rt]);
             i32x4 rs4 = {0, 0, 0, 0};
             if constexpr (kInt8) rs4 = lds_load<i32x4>(&rowsum_sm[rt]);
-  #pragma unroll
+#pragma unroll
             for (int v = 0; v < 4; ++v) {
               if (rt + v < mlen) {
                 float* orow = out + (int64_t)(r0 + rt + v) * N + n0 + 64 * cg + lr;
-  #pragma unroll
+#pragma unroll
                 for (int j = 0; j < kBBlocks; ++j) {
                   float y;
                   if constexpr (kInt8) y = (float)(acc[i][j][v] - 8 * rs4[v]) * sc4[v] * ws[j];
@@ -448,11 +460,26 @@ __global__ __launch_bounds__(kThreads, 1) void gg_tiled_kernel(const uint8_t* __
         }
       }
     };
-    if (nact > 4) run_tile(std::integral_constant<int, 8>{});
-    else if (nact > 2) run_tile(std::integral_constant<int, 4>{});
-    else if (nact == 2) run_tile(std::integral_constant<int, 2>{});
-    else if (nact == 1) run_tile(std::integral_constant<int, 1>{});
-    else run_tile(std::integral_constant<int, 0>{});
+    // A blocks of this wave holding rows: wide tiles ceil(mlen / 16) (every
+    // wave), square tiles those of rg + 2 i < ceil(mlen / 16); none if the
+    // wave's 64 columns are past N (N % 64 == 0: a column group is wholly in
+    // or out).  A square tile has more than 128 rows, so each of its waves
+    // with columns has 4 to 8 blocks.
+    const int mb16 = (mlen + 15) >> 4;
+    if (is_wide) {
+      const int nact = __builtin_amdgcn_readfirstlane(n0 + 64 * wave < N ? min(kABlocks, mb16) : 0);
+      if (nact > 4) run_tile(std::true_type{}, std::integral_constant<int, 8>{});
+      else if (nact > 2) run_tile(std::true_type{}, std::integral_constant<int, 4>{});
+      else if (nact == 2) run_tile(std::true_type{}, std::integral_constant<int, 2>{});
+      else if (nact == 1) run_tile(std::true_type{}, std::integral_constant<int, 1>{});
+      else run_tile(std::true_type{}, std::integral_constant<int, 0>{});
+    } else {
+      const int rg = wave >> 2, cg = wave & 3;
+      const int nact = __builtin_amdgcn_readfirstlane(n0 + 64 * cg < N ? min(kABlocks, (mb16 - rg + 1) >> 1) : 0);
+      if (nact > 4) run_tile(std::false_type{}, std::integral_constant<int, 8>{});
+      else if (nact > 0) run_tile(std::false_type{}, std::integral_constant<int, 4>{});
+      else run_tile(std::false_type{}, std::integral_constant<int, 0>{});
+    }
   }
 }
 
