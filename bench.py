@@ -32,14 +32,16 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 FP8_PEAK_TFLOPS = 5000.0       # MI355X dense FP8 MFMA, published (no sparsity)
 
 
-def kernel_sources_hash() -> str:
-    """Hash of the grouped-GEMM sources: counter files taken on other code are ignored."""
+KERNEL_SOURCES = {"gg_stream": "gemm_stream.hip", "gg_tiled": "gemm_tiled.hip"}
+
+
+def kernel_sources_hash(kernel: str) -> str:
+    """Hash of one grouped-GEMM kernel's sources: counter files taken on other code are ignored."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "quantized_grouped_gemm_token_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
-        if name.startswith("gemm_") or name in ("common.hpp",):
-            with open(os.path.join(csrc, name), "rb") as f:
-                h.update(name.encode() + f.read())
+    for name in ("common.hpp", "gemm_common.hpp", KERNEL_SOURCES[kernel]):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + f.read())
     return h.hexdigest()[:16]
 
 
@@ -247,8 +249,8 @@ def main() -> int:
     t_gu = per_step["gemm_gate_up"] * 1e-3
     t_dn = per_step["gemm_down"] * 1e-3
     decode = args.config in (0, 1, 2)
-    khash = kernel_sources_hash()
     kernel = "gg_stream" if decode else "gg_tiled"
+    khash = kernel_sources_hash(kernel)
     tag = workload_tag(sh) + ("_channel" if channel else "")
     traffic = load_traffic(os.path.join(ROOT, "profiles", f"{kernel}_{tag}_pmc.txt"), khash)
     if decode:
