@@ -250,6 +250,63 @@ int w4a8_moe_swiglu_i8(const float* h, int64_t M, int64_t I, int8_t* qa, float* 
 int w4a8_moe_quantize_weights_channel(const float* w, int64_t rows, int64_t K, int32_t* w_packed,
                                       float* w_scale, void* stream);
 
+/*
+ * ---- Fused epilogues ------------------------------------------------------
+ * Steps 4 and 5 of the layer split differently: the gate/up GEMM applies
+ * SwiGLU in its epilogue and writes act = silu(gate) * up instead of the
+ * [M][2I] gate/up output, plus partial row maxima of |act|; the requant call
+ * then turns act into the step-5 codes.  The results are those of step 4
+ * followed by step 5 (the same fp32 values, the same scale and code rule)
+ * with half the intermediate bytes.  (The SwiGLU after the gate/up
+ * projection and the per-token re-quantization: "GLM-5.3-W4A8" card,
+ * sections 量化方式 and 与其他 4-bit 版本的差异.)
+ */
+
+/*
+ * Steps 4 + 5a, group-128 FP8 form.
+ *   For expert e and row p in [offsets[e], offsets[e+1]) (r = a_rows ? a_rows[p] : p):
+ *     gate[n] = h[p, n], up[n] = h[p, I + n] of w4a8_moe_grouped_gemm with N = 2I;
+ *     act[p, n] = silu(gate[n]) * up[n], silu(z) = z / (1 + e^-z), fp32 (hardware
+ *     exponential and reciprocal: within a few ulp of the exact value);
+ *     act_pmax[p, s], s < I/64: maxima of |act[p, :]| over parts of the row, whose
+ *     maximum is max_n |act[p, n]| (every entry is written; no zeroing needed).
+ *   a, a_scale, a_rows, offsets, algo : as in w4a8_moe_grouped_gemm.
+ *   w13 : int32 [E][2I][K/8] uint4b8 (gate rows 0..I-1, up rows I..2I-1), 16-byte aligned.
+ *   s13 : fp32 [E][2I][K/128].
+ *   act : fp32 [M_total][I], 16-byte aligned.  act_pmax : fp32 [M_total][I/64], 4-byte aligned.
+ *   Rules : I > 0, I % 128 == 0, K % 128 == 0, 1 <= E <= 1024; otherwise as in w4a8_moe_grouped_gemm.
+ */
+int w4a8_moe_grouped_gemm_swiglu(const uint8_t* a, const float* a_scale, const int32_t* a_rows, int64_t M_total,
+                                 const int32_t* offsets, int32_t E, const int32_t* w13, const float* s13, int64_t I,
+                                 int64_t K, float* act, float* act_pmax, int32_t algo, void* stream);
+
+/*
+ * Steps 4 + 5a, per-channel INT8 form: as w4a8_moe_grouped_gemm_swiglu with
+ * the products of w4a8_moe_grouped_gemm_i8 (a : int8 codes with row sums
+ * a_rowsum; s13 : fp32 [E][2I]; K <= 2^20).
+ */
+int w4a8_moe_grouped_gemm_swiglu_i8(const int8_t* a, const float* a_scale, const int32_t* a_rowsum,
+                                    const int32_t* a_rows, int64_t M_total, const int32_t* offsets, int32_t E,
+                                    const int32_t* w13, const float* s13, int64_t I, int64_t K, float* act,
+                                    float* act_pmax, int32_t algo, void* stream);
+
+/*
+ * Step 5b, FP8 -- the step-1 rule per row, from the row maxima of the fused GEMM:
+ *   m = max_s act_pmax[p, s]; sa[p] = fl32(m / 448) (1.0 if 0); qa[p, n] = E4M3(fl32(act[p, n] / sa[p])).
+ *   act : fp32 [M][I], 16-byte aligned.  act_pmax : fp32 [M][I/64] (partial maxima of |act|).
+ *   qa : u8 [M][I], 4-byte aligned.  sa : fp32 [M].  Rules : M >= 0, I > 0, I % 128 == 0.
+ */
+int w4a8_moe_requant(const float* act, const float* act_pmax, int64_t M, int64_t I, uint8_t* qa, float* sa,
+                     void* stream);
+
+/*
+ * Step 5b, INT8: sa[p] = fl32(m / 127) (1.0 if 0);
+ *   qa[p, n] = clamp(round-half-even(fl32(act[p, n] / sa[p])), -127, 127); rowsum[p] = sum_n qa[p, n].
+ *   qa : int8 [M][I], 4-byte aligned.  rowsum : int32 [M].  Otherwise as w4a8_moe_requant.
+ */
+int w4a8_moe_requant_i8(const float* act, const float* act_pmax, int64_t M, int64_t I, int8_t* qa, float* sa,
+                        int32_t* rowsum, void* stream);
+
 /* Static name of a status code ("W4A8_OK", ...). */
 const char* w4a8_moe_status_string(int status);
 

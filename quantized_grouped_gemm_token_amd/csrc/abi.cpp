@@ -287,6 +287,93 @@ int w4a8_moe_quantize_weights_channel(const float* w, int64_t rows, int64_t K, i
                   "quantize_weights_channel");
 }
 
+// the shape, pointer and alignment rules shared by the two fused gate/up GEMMs
+static int check_gemm_swiglu(const char* name, const void* a, const float* a_scale, const int32_t* a_rows,
+                             int64_t M_total, const int32_t* offsets, int32_t E, const int32_t* w13, const float* s13,
+                             int64_t I, int64_t K, const float* act, const float* act_pmax, int32_t algo) {
+  if (M_total < 0 || M_total >= kMaxRows)
+    return fail(W4A8_ERR_SHAPE, "%s: M_total=%lld out of range", name, (long long)M_total);
+  if (E < 1 || E > 1024) return fail(W4A8_ERR_SHAPE, "%s: E=%d must be in [1, 1024]", name, E);
+  if (I <= 0 || I % 128) return fail(W4A8_ERR_SHAPE, "%s: I=%lld must be a positive multiple of 128", name,
+                                     (long long)I);
+  if (K <= 0 || K % 128) return fail(W4A8_ERR_SHAPE, "%s: K=%lld must be a positive multiple of 128", name,
+                                     (long long)K);
+  if (algo < W4A8_GG_AUTO || algo > W4A8_GG_TILED) return fail(W4A8_ERR_SHAPE, "%s: unknown algo %d", name, algo);
+  if (M_total == 0) return W4A8_OK;
+  if (!a || !a_scale || !offsets || !w13 || !s13 || !act || !act_pmax) return fail(W4A8_ERR_NULL, "%s: null pointer", name);
+  if (!aligned(a, 16) || !aligned(w13, 16) || !aligned(act, 16) || !aligned(a_scale, 4) || !aligned(s13, 4) ||
+      !aligned(offsets, 4) || !aligned(a_rows, 4) || !aligned(act_pmax, 4))
+    return fail(W4A8_ERR_ALIGN, "%s: a, w13 and act must be 16-byte aligned, the rest 4-byte", name);
+  return W4A8_OK;
+}
+
+int w4a8_moe_grouped_gemm_swiglu(const uint8_t* a, const float* a_scale, const int32_t* a_rows, int64_t M_total,
+                                 const int32_t* offsets, int32_t E, const int32_t* w13, const float* s13, int64_t I,
+                                 int64_t K, float* act, float* act_pmax, int32_t algo, void* stream) {
+  if (int st = check_gemm_swiglu("grouped_gemm_swiglu", a, a_scale, a_rows, M_total, offsets, E, w13, s13, I, K, act,
+                                 act_pmax, algo))
+    return st;
+  if (M_total == 0) return ok();
+  if (int st = check_device()) return st;
+  w4a8::GemmArgs g{a, a_scale, nullptr, a_rows, M_total, offsets, E, w13, s13, 2 * I, K, act};
+  g.pmax = act_pmax;
+  if (algo == W4A8_GG_AUTO) algo = (M_total <= 32 * (int64_t)E) ? W4A8_GG_STREAM : W4A8_GG_TILED;
+  (void)hipGetLastError();
+  if (algo == W4A8_GG_STREAM) return launched(w4a8::launch_gg_stream(g, as_stream(stream)), "grouped_gemm_swiglu");
+  return launched(w4a8::launch_gg_tiled(g, as_stream(stream)), "grouped_gemm_swiglu");
+}
+
+int w4a8_moe_grouped_gemm_swiglu_i8(const int8_t* a, const float* a_scale, const int32_t* a_rowsum,
+                                    const int32_t* a_rows, int64_t M_total, const int32_t* offsets, int32_t E,
+                                    const int32_t* w13, const float* s13, int64_t I, int64_t K, float* act,
+                                    float* act_pmax, int32_t algo, void* stream) {
+  if (int st = check_gemm_swiglu("grouped_gemm_swiglu_i8", a, a_scale, a_rows, M_total, offsets, E, w13, s13, I, K,
+                                 act, act_pmax, algo))
+    return st;
+  if (K > (int64_t)1 << 20)
+    return fail(W4A8_ERR_SHAPE, "grouped_gemm_swiglu_i8: K=%lld would overflow the int32 sums", (long long)K);
+  if (M_total == 0) return ok();
+  if (!a_rowsum) return fail(W4A8_ERR_NULL, "grouped_gemm_swiglu_i8: null pointer");
+  if (!aligned(a_rowsum, 4)) return fail(W4A8_ERR_ALIGN, "grouped_gemm_swiglu_i8: a_rowsum must be 4-byte aligned");
+  if (int st = check_device()) return st;
+  w4a8::GemmArgs g{reinterpret_cast<const uint8_t*>(a), a_scale, a_rowsum, a_rows, M_total, offsets, E, w13, s13,
+                   2 * I, K, act};
+  g.pmax = act_pmax;
+  if (algo == W4A8_GG_AUTO) algo = (M_total <= 32 * (int64_t)E) ? W4A8_GG_STREAM : W4A8_GG_TILED;
+  (void)hipGetLastError();
+  if (algo == W4A8_GG_STREAM)
+    return launched(w4a8::launch_gg_stream(g, as_stream(stream)), "grouped_gemm_swiglu_i8");
+  return launched(w4a8::launch_gg_tiled(g, as_stream(stream)), "grouped_gemm_swiglu_i8");
+}
+
+int w4a8_moe_requant(const float* act, const float* act_pmax, int64_t M, int64_t I, uint8_t* qa, float* sa,
+                     void* stream) {
+  if (M < 0 || M >= kMaxRows) return fail(W4A8_ERR_SHAPE, "requant: M=%lld out of range", (long long)M);
+  if (I <= 0 || I % 128) return fail(W4A8_ERR_SHAPE, "requant: I=%lld must be a positive multiple of 128",
+                                     (long long)I);
+  if (M == 0) return ok();
+  if (!act || !act_pmax || !qa || !sa) return fail(W4A8_ERR_NULL, "requant: null pointer");
+  if (!aligned(act, 16) || !aligned(act_pmax, 4) || !aligned(qa, 4) || !aligned(sa, 4))
+    return fail(W4A8_ERR_ALIGN, "requant: act must be 16-byte aligned, act_pmax, qa and sa 4-byte");
+  if (int st = check_device()) return st;
+  (void)hipGetLastError();
+  return launched(w4a8::launch_requant(act, act_pmax, M, I, qa, sa, as_stream(stream)), "requant");
+}
+
+int w4a8_moe_requant_i8(const float* act, const float* act_pmax, int64_t M, int64_t I, int8_t* qa, float* sa,
+                        int32_t* rowsum, void* stream) {
+  if (M < 0 || M >= kMaxRows) return fail(W4A8_ERR_SHAPE, "requant_i8: M=%lld out of range", (long long)M);
+  if (I <= 0 || I % 128) return fail(W4A8_ERR_SHAPE, "requant_i8: I=%lld must be a positive multiple of 128",
+                                     (long long)I);
+  if (M == 0) return ok();
+  if (!act || !act_pmax || !qa || !sa || !rowsum) return fail(W4A8_ERR_NULL, "requant_i8: null pointer");
+  if (!aligned(act, 16) || !aligned(act_pmax, 4) || !aligned(qa, 4) || !aligned(sa, 4) || !aligned(rowsum, 4))
+    return fail(W4A8_ERR_ALIGN, "requant_i8: act must be 16-byte aligned, act_pmax, qa, sa and rowsum 4-byte");
+  if (int st = check_device()) return st;
+  (void)hipGetLastError();
+  return launched(w4a8::launch_requant_i8(act, act_pmax, M, I, qa, sa, rowsum, as_stream(stream)), "requant_i8");
+}
+
 int w4a8_moe_unpermute(const float* o, const int32_t* inv_pos, const float* w, int64_t T, int32_t k, int64_t H,
                        void* y, int32_t y_dtype, void* stream) {
   if (T < 0 || T >= kMaxRows) return fail(W4A8_ERR_SHAPE, "unpermute: T=%lld out of range", (long long)T);

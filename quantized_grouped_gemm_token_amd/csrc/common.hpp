@@ -59,6 +59,26 @@ __device__ __forceinline__ int wave_sum_int(int v) {
   return v;
 }
 
+// SwiGLU of one gate/up pair in fp32: silu(g) * u, silu(g) = g / (1 + e^-g)
+// (no clamp), with the hardware exponential and reciprocal (each within 1
+// ulp; the result within a few ulp of the exact value, far below the FP8 or
+// INT8 step that follows).  The SwiGLU kernel and the fused gate/up
+// epilogues both use this one expression, so they produce the same bits.
+__device__ __forceinline__ float silu_mul(float g, float u) {
+  return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;
+}
+
+// Max of v over each row of 16 lanes (one MFMA D column group), left in
+// every lane of the row: DPP row rotations by 8, 4, 2 and 1 (register
+// moves, no LDS round trip).
+__device__ __forceinline__ float max16(float v) {
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x128, 0xf, 0xf, true)));   // row_ror:8
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x124, 0xf, 0xf, true)));   // row_ror:4
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x122, 0xf, 0xf, true)));   // row_ror:2
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x121, 0xf, 0xf, true)));   // row_ror:1
+  return v;
+}
+
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 

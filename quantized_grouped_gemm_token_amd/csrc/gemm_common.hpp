@@ -77,6 +77,14 @@ __device__ __forceinline__ v8i nibbles_to_fp8(i32x4 w) {
   return r;
 }
 
+// Fused SwiGLU: the gate/up GEMM reads its weight rows interleaved by 16, so
+// that two neighbouring 16-column blocks of a tile hold the gate and the up
+// rows of the same 16 output columns.  Tile column v reads weight row
+//   gate_up_row(v) = (v / 16 odd ? half : 0) + 16 (v / 32) + v % 16,
+// half = I (gate rows 0..I-1, up rows I..2I-1), and feeds output column
+// 16 (v / 32) + v % 16 of act = silu(gate) * up.
+__device__ __forceinline__ int gate_up_row(int v, int half) { return ((v >> 4) & 1) * half + 16 * (v >> 5) + (v & 15); }
+
 __device__ __forceinline__ v8i bias_operand() {
   v8i b;
 #pragma unroll

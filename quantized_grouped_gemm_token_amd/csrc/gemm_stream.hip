@@ -44,6 +44,7 @@ __device__ __forceinline__ int row_ror8(int v) { return __builtin_amdgcn_mov_dpp
 template <int CH>
 struct StreamSmem {
   uint8_t a[2][2 * CH][64][32];
+  float rmax[4][16];                 // fused form: row max |act| of each wave's 16 output columns
 };
 
 // Chunk of activations -> registers: thread t loads rows t / 16 (16 B chunks
@@ -145,7 +146,11 @@ __device__ __forceinline__ void pair_compute_i8(const WPair<NS>& w, const uint8_
 
 // kInt8: the per-channel variant (INT8 activations with row sums a_rowsum,
 // one scale per weight row in w_scale [E][N]); otherwise the group-128 FP8 form.
-template <int NS, int CH, bool kInt8>
+// kSwiglu: the fused gate/up form: a wave's two subtiles are the gate and the
+// up rows of the same 16 output columns (gate_up_row), and the epilogue
+// writes act = silu(gate) * up [M][N/2] and the workgroup's max |act| of each
+// row (its 64 output columns) to pmax[p][blockIdx.x].
+template <int NS, int CH, bool kInt8, bool kSwiglu>
 __global__ __launch_bounds__(kStreamThreads) void gg_stream_kernel(const uint8_t* __restrict__ a,
                                                                    const float* __restrict__ a_scale,
                                                                    const int32_t* __restrict__ a_rowsum,
@@ -153,7 +158,9 @@ __global__ __launch_bounds__(kStreamThreads) void gg_stream_kernel(const uint8_t
                                                                    const int32_t* __restrict__ offsets,
                                                                    const int32_t* __restrict__ w_packed,
                                                                    const float* __restrict__ w_scale, int64_t N,
-                                                                   int64_t K, float* __restrict__ out) {
+                                                                   int64_t K, float* __restrict__ out,
+                                                                   float* __restrict__ pmax) {
+  static_assert(!kSwiglu || NS == 2, "fused SwiGLU pairs the two subtiles of a wave");
   __shared__ StreamSmem<CH> sm;
   const int e = blockIdx.y;
   const int r0 = offsets[e], r1 = offsets[e + 1];
@@ -173,7 +180,7 @@ __global__ __launch_bounds__(kStreamThreads) void gg_stream_kernel(const uint8_t
   const float* srow[NS];
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
-    const int64_t nb = active ? n0 + 16 * s : 0;
+    const int64_t nb = active ? (kSwiglu ? (int64_t)gate_up_row((int)(n0 + 16 * s), (int)(N / 2)) : n0 + 16 * s) : 0;
     const uint8_t* wbase = reinterpret_cast<const uint8_t*>(w_packed) + ((int64_t)e * N + nb) * row_bytes;
     pa[s] = wbase + (int64_t)(col & 7) * row_bytes + (lo ? 0 : 64) + kq * 16;
     pb[s] = wbase + (int64_t)(8 + (col & 7)) * row_bytes + (lo ? 64 : 0) + kq * 16;
@@ -290,11 +297,24 @@ __global__ __launch_bounds__(kStreamThreads) void gg_stream_kernel(const uint8_t
         // out = a_scale * w_scale * (sum a u - 8 sum a): the integer part is exact
         float ws[NS];
 #pragma unroll
-        for (int s = 0; s < NS; ++s) ws[s] = w_scale[(int64_t)e * N + n0 + 16 * s + col];
+        for (int s = 0; s < NS; ++s) {
+          const int v = (int)(n0 + 16 * s) + col;
+          ws[s] = w_scale[(int64_t)e * N + (kSwiglu ? gate_up_row(v, (int)(N / 2)) : v)];
+        }
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int p = m0 + kq * 4 + r;
-          if (p < r1) {
+          if constexpr (kSwiglu) {
+            // gate and up of output column n0 / 2 + col (rows past r1 compute on a repeated row, unstored)
+            const int pc = min(p, r1 - 1);
+            const int64_t src = a_rows ? a_rows[pc] : pc;
+            const int off = 8 * a_rowsum[src];
+            const float as = a_scale[src];
+            const float y = silu_mul((float)(acc[0][r] - off) * as * ws[0], (float)(acc[1][r] - off) * as * ws[1]);
+            const float m = max16(p < r1 ? fabsf(y) : 0.0f);
+            if (p < r1) out[(int64_t)p * (N / 2) + n0 / 2 + col] = y;
+            if (col == 0) sm.rmax[wave][kq * 4 + r] = m;
+          } else if (p < r1) {
             const int64_t src = a_rows ? a_rows[p] : p;
             const int off = 8 * a_rowsum[src];
             const float as = a_scale[src];
@@ -307,7 +327,15 @@ __global__ __launch_bounds__(kStreamThreads) void gg_stream_kernel(const uint8_t
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int p = m0 + kq * 4 + r;
-          if (p < r1) {
+          if constexpr (kSwiglu) {
+            const int pc = min(p, r1 - 1);
+            const int64_t src = a_rows ? a_rows[pc] : pc;
+            const float rs = a_scale[src] * kUnitScale;
+            const float y = silu_mul(acc[0][r] * rs, acc[1][r] * rs);
+            const float m = max16(p < r1 ? fabsf(y) : 0.0f);
+            if (p < r1) out[(int64_t)p * (N / 2) + n0 / 2 + col] = y;
+            if (col == 0) sm.rmax[wave][kq * 4 + r] = m;
+          } else if (p < r1) {
             const int64_t src = a_rows ? a_rows[p] : p;
             const float rs = a_scale[src] * kUnitScale;
 #pragma unroll
@@ -316,19 +344,34 @@ __global__ __launch_bounds__(kStreamThreads) void gg_stream_kernel(const uint8_t
         }
       }
     }
+    if constexpr (kSwiglu) {
+      // the workgroup's row maxima over its 4 waves (a wave past N counts 0)
+      if (!active && lane < 16) sm.rmax[wave][lane] = 0.0f;
+      __syncthreads();
+      if (threadIdx.x < 16 && m0 + (int)threadIdx.x < r1) {
+        const float m = fmaxf(fmaxf(sm.rmax[0][threadIdx.x], sm.rmax[1][threadIdx.x]),
+                              fmaxf(sm.rmax[2][threadIdx.x], sm.rmax[3][threadIdx.x]));
+        pmax[(int64_t)(m0 + threadIdx.x) * gridDim.x + blockIdx.x] = m;
+      }
+    }
   }
 }
 
-template <int NS, int CH, bool kInt8 = false>
+template <int NS, int CH, bool kInt8, bool kSwiglu>
 static void launch_variant(const GemmArgs& g, hipStream_t stream) {
   const dim3 grid((unsigned)((g.N + 64 * NS - 1) / (64 * NS)), (unsigned)g.E);
-  hipLaunchKernelGGL((gg_stream_kernel<NS, CH, kInt8>), grid, dim3(kStreamThreads), 0, stream, g.a, g.a_scale,
-                     g.a_rowsum, g.a_rows, g.offsets, g.w_packed, g.w_scale, g.N, g.K, g.out);
+  hipLaunchKernelGGL((gg_stream_kernel<NS, CH, kInt8, kSwiglu>), grid, dim3(kStreamThreads), 0, stream, g.a,
+                     g.a_scale, g.a_rowsum, g.a_rows, g.offsets, g.w_packed, g.w_scale, g.N, g.K, g.out, g.pmax);
 }
 
 hipError_t launch_gg_stream(const GemmArgs& g, hipStream_t stream) {
-  if (g.a_rowsum) launch_variant<2, 4, true>(g, stream);
-  else launch_variant<2, 4>(g, stream);
+  if (g.pmax) {
+    if (g.a_rowsum) launch_variant<2, 4, true, true>(g, stream);
+    else launch_variant<2, 4, false, true>(g, stream);
+  } else {
+    if (g.a_rowsum) launch_variant<2, 4, true, false>(g, stream);
+    else launch_variant<2, 4, false, false>(g, stream);
+  }
   return hipGetLastError();
 }
 

@@ -120,7 +120,12 @@ __device__ __forceinline__ int tiles_of(int rows, int nb, int nw) {
 // a_rowsum, one scale per weight row in w_scale [E][N]): int32 products
 // accumulated by the matrix core over all of K, no group scales, no row-sum
 // MFMAs; otherwise the group-128 FP8 form.
-template <bool kInt8>
+// kSwiglu: the fused gate/up form: tile column v multiplies weight row
+// gate_up_row(v), so a wave's B blocks 2 jp and 2 jp + 1 are the gate and the
+// up rows of the same 16 output columns; the epilogue writes
+// act = silu(gate) * up [M][N/2] and the tile's max |act| of each row to
+// pmax[p][s] for the slots s of 64 output columns the tile covers.
+template <bool kInt8, bool kSwiglu>
 __global__ __launch_bounds__(kThreads, 1) void gg_tiled_kernel(const uint8_t* __restrict__ a,
                                                                const float* __restrict__ a_scale,
                                                                const int32_t* __restrict__ a_rowsum,
@@ -128,13 +133,15 @@ __global__ __launch_bounds__(kThreads, 1) void gg_tiled_kernel(const uint8_t* __
                                                                const int32_t* __restrict__ offsets, int E,
                                                                const int32_t* __restrict__ w_packed,
                                                                const float* __restrict__ w_scale, int64_t N,
-                                                               int64_t K, float* __restrict__ out) {
+                                                               int64_t K, float* __restrict__ out,
+                                                               float* __restrict__ pmax) {
   __shared__ RingSlot ring0, ring1, ring2;
   __shared__ __attribute__((aligned(16))) float sc0[kWideCols], sc1[kWideCols], sc2[kWideCols];   // group scales
   __shared__ __attribute__((aligned(16))) float bias_sm[2][kTM];   // -2^-6 * group code sums: [group parity][row]
   __shared__ __attribute__((aligned(16))) float ascale_sm[kTM];    // token scales of the tile's rows
   __shared__ int tile_start[kMaxExperts + 1];                      // first tile index of each expert
   __shared__ int wsum[kWaves];
+  __shared__ unsigned int rmax_sm[2][kTM];                         // fused form: row max |act| of the tile, by tile parity
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: keeps wave-indexed values scalar
@@ -143,6 +150,7 @@ __global__ __launch_bounds__(kThreads, 1) void gg_tiled_kernel(const uint8_t* __
   const int NW = (NB + 1) / 2;                                 // 512-column blocks
   const int G = (int)(K >> 7);
   const uint32_t row_bytes = (uint32_t)(K >> 1);
+  const int half = (int)(N >> 1);                              // output columns of the fused form
   int* rowsum_sm = reinterpret_cast<int*>(&bias_sm[0][0]);   // the INT8 form has no group sums: row code sums
 
   // ---- tile numbering: exclusive prefix of per-expert tile counts (wave-level scans)
@@ -193,7 +201,8 @@ __global__ __launch_bounds__(kThreads, 1) void gg_tiled_kernel(const uint8_t* __
   const bool xcd_windows = (grid % kXcds) == 0;
   const int window = grid / kXcds;
   const int my_slot = xcd_windows ? (int)(blockIdx.x % kXcds) * window + (int)(blockIdx.x / kXcds) : (int)blockIdx.x;
-  for (int t = my_slot; t < total; t += grid) {
+  int tpar = 0;                                                    // parity of this workgroup's tile count
+  for (int t = my_slot; t < total; t += grid, tpar ^= 1) {
     // ---- which expert, and which tile of it
     int lo_e = 0, hi_e = E;                    // tile_start[lo_e] <= t < tile_start[hi_e]
     while (hi_e - lo_e > 1) {
@@ -260,10 +269,14 @@ __global__ __launch_bounds__(kThreads, 1) void gg_tiled_kernel(const uint8_t* __
       // the loads return zeros.
       const __amdgpu_buffer_rsrc_t rw =
           buffer_rsrc(reinterpret_cast<const uint8_t*>(w_packed) + (int64_t)e * N * row_bytes, (uint32_t)N * row_bytes);
-      const uint32_t woff = (uint32_t)(n0 + kWCols * wave + (lane >> 2)) * row_bytes +
+      // (fused form: the 16 columns of load q are weight rows gate_up_row(vb + 16 q) .. +15; their base
+      // goes into the scalar offset, and a wave past N reads rows from 0, unused)
+      const int vb = n0 + kWCols * wave < N ? n0 + kWCols * wave : 0;
+      const uint32_t woff = (kSwiglu ? 0u : (uint32_t)vb * row_bytes) + (uint32_t)(lane >> 2) * row_bytes +
                             16u * (uint32_t)((lane & 3) ^ ((lane >> 4) & 3));
       const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(w_scale + (int64_t)e * N * G, (uint32_t)(N * G * 4));
-      const uint32_t soff = (uint32_t)min(n0 + 64 * wave + lane, (int)N - 1) * (uint32_t)G * 4u;
+      const int scol = min(n0 + 64 * wave + lane, (int)N - 1);
+      const uint32_t soff = (uint32_t)(kSwiglu ? gate_up_row(scol, half) : scol) * (uint32_t)G * 4u;
 
       // loads of group g into slot S: the group scales, the activation rows, the weight columns
       auto stage = [&](auto S_, int g) {
@@ -275,7 +288,8 @@ __global__ __launch_bounds__(kThreads, 1) void gg_tiled_kernel(const uint8_t* __
           dma16(ra, aoff[q], (uint32_t)g * kGroup, &sl.b[(kARows * wave + 8 * q) * kGroup]);
 #pragma unroll
         for (int q = 0; q < kWLoads; ++q)
-          dma16(rw, woff, (uint32_t)g * 64u + (uint32_t)(16 * q) * row_bytes,
+          dma16(rw, woff,
+                (uint32_t)g * 64u + (uint32_t)(kSwiglu ? gate_up_row(vb + 16 * q, half) : 16 * q) * row_bytes,
                 &sl.b[kWBase + (kWCols * wave + 16 * q) * 64]);
       };
       // wait until only the loads of the group issued last are in flight
@@ -411,6 +425,9 @@ __global__ __launch_bounds__(kThreads, 1) void gg_tiled_kernel(const uint8_t* __
         __builtin_amdgcn_s_waitcnt(0x0F70);
       }
       if (!kInt8) row_sums(std::integral_constant<int, 0>{}, 0);
+      // the fused form's row maxima of this tile start at 0 (the previous use of this
+      // parity's array, two tiles back, ended before the last tile's first barrier)
+      if (kSwiglu && tid < kTM) rmax_sm[tpar][tid] = 0u;
       __builtin_amdgcn_s_waitcnt(0xC07F);
       barrier_loads_in_flight();
       // the token scales (and in the INT8 form the row code sums) of the tile's
@@ -431,10 +448,17 @@ __global__ __launch_bounds__(kThreads, 1) void gg_tiled_kernel(const uint8_t* __
 
       // ---- epilogue: D lane holds column lr of its B block, rows 4 lq .. +3 of its A block
       if constexpr (kNB > 0) {
+        // lane roles taken afresh: addresses built from them are not hoisted out of the tile
+        // loop, where they would live (and spill) across every K loop
+        int lr = lane & 15, lq = lane >> 4;
+        asm volatile("" : "+v"(lr), "+v"(lq));
         float ws[kBBlocks];
         if constexpr (kInt8) {
 #pragma unroll
-          for (int j = 0; j < kBBlocks; ++j) ws[j] = w_scale[(int64_t)e * N + n0 + 64 * cg + 16 * j + lr];
+          for (int j = 0; j < kBBlocks; ++j) {
+            const int v = n0 + 64 * cg + 16 * j + lr;
+            ws[j] = w_scale[(int64_t)e * N + (kSwiglu ? gate_up_row(v, half) : v)];
+          }
         }
 #pragma unroll
         for (int i = 0; i < kNB; ++i) {
@@ -443,20 +467,46 @@ __global__ __launch_bounds__(kThreads, 1) void gg_tiled_kernel(const uint8_t* __
             const v4f sc4 = lds_load<v4f>(&ascale_sm[rt]);
             i32x4 rs4 = {0, 0, 0, 0};
             if constexpr (kInt8) rs4 = lds_load<i32x4>(&rowsum_sm[rt]);
+            // the GEMM output of B block j and row v (the value the unfused form stores)
+            auto h = [&](int j, int v) {
+              if constexpr (kInt8) return (float)(acc[i][j][v] - 8 * rs4[v]) * sc4[v] * ws[j];
+              else return acc[i][j][v] * (sc4[v] * kUnitScale);
+            };
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
-              if (rt + v < mlen) {
+              if constexpr (kSwiglu) {
+                const bool ok = rt + v < mlen;
+                float* orow = out + (int64_t)(r0 + rt + v) * half + (n0 + 64 * cg) / 2 + lr;
+                float m = 0.0f;
+#pragma unroll
+                for (int jp = 0; jp < kBBlocks / 2; ++jp) {
+                  const float y = silu_mul(h(2 * jp, v), h(2 * jp + 1, v));
+                  if (ok) __builtin_nontemporal_store(y, orow + 16 * jp);
+                  m = fmaxf(m, fabsf(y));
+                }
+                m = max16(ok ? m : 0.0f);
+                if (ok && lr == 0) atomicMax(&rmax_sm[tpar][rt + v], __float_as_uint(m));
+              } else if (rt + v < mlen) {
                 float* orow = out + (int64_t)(r0 + rt + v) * N + n0 + 64 * cg + lr;
 #pragma unroll
-                for (int j = 0; j < kBBlocks; ++j) {
-                  float y;
-                  if constexpr (kInt8) y = (float)(acc[i][j][v] - 8 * rs4[v]) * sc4[v] * ws[j];
-                  else y = acc[i][j][v] * (sc4[v] * kUnitScale);
-                  __builtin_nontemporal_store(y, orow + 16 * j);
-                }
+                for (int j = 0; j < kBBlocks; ++j) __builtin_nontemporal_store(h(j, v), orow + 16 * j);
               }
             }
           }
+          __builtin_amdgcn_sched_barrier(0);   // one block at a time: its outputs' temporaries stay few
+        }
+      }
+      if constexpr (kSwiglu) {
+        // the tile's row maxima (reduced in LDS over the waves' column groups), stored once per
+        // 64-column slot of the tile (plain stores: no atomics, no zeroing of the output)
+        __builtin_amdgcn_s_waitcnt(0xC07F);
+        barrier_loads_in_flight();
+        if (tid < kRows && tid < mlen) {
+          const int slots = (int)(N >> 7), s0 = n0 >> 7;
+          const float m = __uint_as_float(rmax_sm[tpar][tid]);
+#pragma unroll
+          for (int q = 0; q < kCols / 128; ++q)
+            if (s0 + q < slots) pmax[(int64_t)(r0 + tid) * slots + s0 + q] = m;
         }
       }
     };
@@ -501,12 +551,17 @@ hipError_t launch_gg_tiled(const GemmArgs& g, hipStream_t stream) {
   constexpr int64_t k4G = (int64_t)1 << 32;
   if (g.M_total * g.K >= k4G || g.M_total * 4 >= k4G || g.N * (g.K / 2) >= k4G || g.N * (g.K / 128) * 4 >= k4G)
     return launch_gg_stream(g, stream);
-  if (g.a_rowsum)
-    hipLaunchKernelGGL((gg_tiled_kernel<true>), dim3(cu_count()), dim3(kThreads), 0, stream, g.a, g.a_scale,
-                       g.a_rowsum, g.a_rows, g.offsets, g.E, g.w_packed, g.w_scale, g.N, g.K, g.out);
-  else
-    hipLaunchKernelGGL((gg_tiled_kernel<false>), dim3(cu_count()), dim3(kThreads), 0, stream, g.a, g.a_scale,
-                       nullptr, g.a_rows, g.offsets, g.E, g.w_packed, g.w_scale, g.N, g.K, g.out);
+  auto go = [&](auto kernel) {
+    hipLaunchKernelGGL(kernel, dim3(cu_count()), dim3(kThreads), 0, stream, g.a, g.a_scale, g.a_rowsum, g.a_rows,
+                       g.offsets, g.E, g.w_packed, g.w_scale, g.N, g.K, g.out, g.pmax);
+  };
+  if (g.pmax) {
+    if (g.a_rowsum) go(gg_tiled_kernel<true, true>);
+    else go(gg_tiled_kernel<false, true>);
+  } else {
+    if (g.a_rowsum) go(gg_tiled_kernel<true, false>);
+    else go(gg_tiled_kernel<false, false>);
+  }
   return hipGetLastError();
 }
 

@@ -23,6 +23,11 @@ struct GemmArgs {
   int64_t N;
   int64_t K;
   float* out;
+  // fused SwiGLU (gate/up GEMM only): when set, out is act [M_total][N/2] =
+  // silu(gate) * up, gate and up being the weight rows n and N/2 + n, and
+  // pmax [M_total][N/128] gets row maxima of |act| (each entry over some of
+  // the row's columns; their max is the row's)
+  float* pmax = nullptr;
 };
 
 hipError_t launch_quant_act(const uint16_t* x, int64_t T, int64_t H, int64_t ld, uint8_t* q, float* s,
@@ -43,6 +48,10 @@ hipError_t launch_wquant_channel(const float* w, int64_t rows, int64_t K, int32_
                                  hipStream_t stream);
 hipError_t launch_wquant(const float* w, int64_t rows, int64_t K, int mse_clip, int32_t* packed, float* scales,
                          hipStream_t stream);
+hipError_t launch_requant(const float* act, const float* pmax, int64_t M, int64_t I, uint8_t* q, float* s,
+                          hipStream_t stream);
+hipError_t launch_requant_i8(const float* act, const float* pmax, int64_t M, int64_t I, int8_t* q, float* s,
+                             int32_t* rowsum, hipStream_t stream);
 hipError_t launch_unpermute(const float* o, const int32_t* inv_pos, const float* w, int64_t T, int k, int64_t H,
                             void* y, int bf16_out, hipStream_t stream);
 

@@ -79,7 +79,6 @@ __global__ __launch_bounds__(256) void quant_act_kernel(const uint16_t* __restri
 }
 
 // ---- step 5: silu(gate) * up, then the row quantizer -------------------
-__device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f + expf(-g)) * u; }
 
 template <bool kInt8>
 __global__ __launch_bounds__(256) void swiglu_quant_kernel(const float* __restrict__ h, int64_t M, int64_t I,
@@ -115,6 +114,57 @@ __global__ __launch_bounds__(256) void swiglu_quant_kernel(const float* __restri
     s[row] = scale;
     if constexpr (kInt8) rowsum[row] = sum;
   }
+}
+
+// ---- step 5 after a fused gate/up epilogue -------------------------------
+// The fused gate/up GEMM already wrote act = silu(gate) * up (fp32 [M][I])
+// and partial row maxima of |act| (pmax [M][I/64]); this is the second half
+// of the SwiGLU kernel above: the same scale and codes, from the same values.
+template <bool kInt8>
+__global__ __launch_bounds__(256) void requant_kernel(const float* __restrict__ act, const float* __restrict__ pmax,
+                                                      int64_t M, int64_t I, uint8_t* __restrict__ q,
+                                                      float* __restrict__ s, int32_t* __restrict__ rowsum) {
+  using C = RowCodec<kInt8>;
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= M) return;
+  const int64_t slots = I >> 6;
+  float m = 0.0f;
+  for (int64_t c = lane; c < slots; c += kWave) m = fmaxf(m, pmax[row * slots + c]);
+  m = wave_max(m);
+  const f32x4* ar = reinterpret_cast<const f32x4*>(act + row * I);
+  const float scale = m > 0.0f ? m / C::kMax : 1.0f;
+  uint32_t* qr = reinterpret_cast<uint32_t*>(q + row * I);
+  int sum = 0;
+  for (int64_t c = lane; c < (I >> 2); c += kWave) {
+    const f32x4 v = __builtin_nontemporal_load(ar + c);
+    const uint32_t c0 = C::code(v[0] / scale, sum);
+    const uint32_t c1 = C::code(v[1] / scale, sum);
+    const uint32_t c2 = C::code(v[2] / scale, sum);
+    const uint32_t c3 = C::code(v[3] / scale, sum);
+    qr[c] = c0 | (c1 << 8) | (c2 << 16) | (c3 << 24);
+  }
+  if constexpr (kInt8) sum = wave_sum_int(sum);
+  if (lane == 0) {
+    s[row] = scale;
+    if constexpr (kInt8) rowsum[row] = sum;
+  }
+}
+
+hipError_t launch_requant(const float* act, const float* pmax, int64_t M, int64_t I, uint8_t* q, float* s,
+                          hipStream_t stream) {
+  const int64_t blocks = (M + 3) / 4;
+  hipLaunchKernelGGL(requant_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, stream, act, pmax, M, I, q, s,
+                     nullptr);
+  return hipGetLastError();
+}
+
+hipError_t launch_requant_i8(const float* act, const float* pmax, int64_t M, int64_t I, int8_t* q, float* s,
+                             int32_t* rowsum, hipStream_t stream) {
+  const int64_t blocks = (M + 3) / 4;
+  hipLaunchKernelGGL(requant_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, stream, act, pmax, M, I,
+                     reinterpret_cast<uint8_t*>(q), s, rowsum);
+  return hipGetLastError();
 }
 
 hipError_t launch_quant_act(const uint16_t* x, int64_t T, int64_t H, int64_t ld, uint8_t* q, float* s,

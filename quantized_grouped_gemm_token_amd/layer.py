@@ -3,6 +3,11 @@
     quant_act -> route -> permute -> grouped_gemm(W13) -> swiglu ->
     grouped_gemm(W2) -> unpermute
 
+With fused=True (the default) steps 4 and 5 run as grouped_gemm_swiglu (the
+gate/up GEMM with SwiGLU in its epilogue, writing act = silu(gate) * up and
+partial row maxima of |act|) and requant (the codes of act): the same results with half
+the intermediate bytes.
+
 Expert weights stay resident on the GPU in the packed format (int32
 [E][N][K/8] words of uint4b8 nibbles and fp32 [E][N][K/128] group scales).
 W4A8MoEChannel is the per-channel INT4 x per-token INT8 variant: fp32 [E][N]
@@ -19,7 +24,7 @@ from . import ops
 
 class W4A8MoE:
     def __init__(self, w13: torch.Tensor, s13: torch.Tensor, w2: torch.Tensor, s2: torch.Tensor, k: int,
-                 renormalize: bool = True):
+                 renormalize: bool = True, fused: bool = True):
         E, N13, KW13 = w13.shape
         E2, H, KW2 = w2.shape
         if E2 != E or N13 % 2 or KW13 * 8 != H or KW2 * 8 * 2 != N13:
@@ -27,6 +32,7 @@ class W4A8MoE:
         self.w13, self.s13, self.w2, self.s2 = w13, s13, w2, s2
         self.E, self.H, self.I, self.k = E, H, N13 // 2, k
         self.renormalize = renormalize
+        self.fused = fused
         self._bufs: dict[int, dict] = {}
 
     def buffers(self, T: int) -> dict:
@@ -41,9 +47,12 @@ class W4A8MoE:
                 ids=e((T, self.k), torch.int32), w=e((T, self.k), torch.float32),
                 offsets=e((self.E + 1,), torch.int32), row_token=e((R,), torch.int32),
                 inv_pos=e((R,), torch.int32), workspace=e((max(nbytes, 4),), torch.uint8),
-                h=e((R, 2 * self.I), torch.float32), qa=e((R, self.I), torch.uint8), sa=e((R,), torch.float32),
-                o=e((R, self.H), torch.float32),
+                qa=e((R, self.I), torch.uint8), sa=e((R,), torch.float32), o=e((R, self.H), torch.float32),
             )
+            if self.fused:
+                self._bufs[T].update(act=e((R, self.I), torch.float32), pmax=e((R, self.I // 64), torch.float32))
+            else:
+                self._bufs[T].update(h=e((R, 2 * self.I), torch.float32))
         return self._bufs[T]
 
     STEPS = ("quant_act", "route", "permute", "gemm_gate_up", "swiglu", "gemm_down", "unpermute")
@@ -73,9 +82,14 @@ class W4A8MoE:
         step("route", ops.w4a8_moe_route, logits, self.k, self.renormalize, b["ids"], b["w"])
         step("permute", ops.w4a8_moe_permute, b["ids"], self.E, b["offsets"], b["row_token"], b["inv_pos"],
              b["workspace"])
-        step("gemm_gate_up", ops.w4a8_moe_grouped_gemm, b["qx"], b["sx"], b["row_token"], b["offsets"], self.w13,
-             self.s13, R, b["h"], algo)
-        step("swiglu", ops.w4a8_moe_swiglu, b["h"], b["qa"], b["sa"])
+        if self.fused:
+            step("gemm_gate_up", ops.w4a8_moe_grouped_gemm_swiglu, b["qx"], b["sx"], b["row_token"], b["offsets"],
+                 self.w13, self.s13, R, b["act"], b["pmax"], algo)
+            step("swiglu", ops.w4a8_moe_requant, b["act"], b["pmax"], b["qa"], b["sa"])
+        else:
+            step("gemm_gate_up", ops.w4a8_moe_grouped_gemm, b["qx"], b["sx"], b["row_token"], b["offsets"],
+                 self.w13, self.s13, R, b["h"], algo)
+            step("swiglu", ops.w4a8_moe_swiglu, b["h"], b["qa"], b["sa"])
         step("gemm_down", ops.w4a8_moe_grouped_gemm, b["qa"], b["sa"], None, b["offsets"], self.w2, self.s2, R,
              b["o"], algo)
         return step("unpermute", ops.w4a8_moe_unpermute, b["o"], b["inv_pos"], b["w"], y, y_dtype)
@@ -119,9 +133,14 @@ class W4A8MoEChannel(W4A8MoE):
         step("route", ops.w4a8_moe_route, logits, self.k, self.renormalize, b["ids"], b["w"])
         step("permute", ops.w4a8_moe_permute, b["ids"], self.E, b["offsets"], b["row_token"], b["inv_pos"],
              b["workspace"])
-        step("gemm_gate_up", ops.w4a8_moe_grouped_gemm_i8, b["qx"], b["sx"], b["rx"], b["row_token"], b["offsets"],
-             self.w13, self.s13, b["h"], R, algo)
-        step("swiglu", ops.w4a8_moe_swiglu_i8, b["h"], b["qa"], b["sa"], b["ra"])
+        if self.fused:
+            step("gemm_gate_up", ops.w4a8_moe_grouped_gemm_swiglu_i8, b["qx"], b["sx"], b["rx"], b["row_token"],
+                 b["offsets"], self.w13, self.s13, R, b["act"], b["pmax"], algo)
+            step("swiglu", ops.w4a8_moe_requant_i8, b["act"], b["pmax"], b["qa"], b["sa"], b["ra"])
+        else:
+            step("gemm_gate_up", ops.w4a8_moe_grouped_gemm_i8, b["qx"], b["sx"], b["rx"], b["row_token"],
+                 b["offsets"], self.w13, self.s13, b["h"], R, algo)
+            step("swiglu", ops.w4a8_moe_swiglu_i8, b["h"], b["qa"], b["sa"], b["ra"])
         step("gemm_down", ops.w4a8_moe_grouped_gemm_i8, b["qa"], b["sa"], b["ra"], None, b["offsets"], self.w2,
              self.s2, b["o"], R, algo)
         return step("unpermute", ops.w4a8_moe_unpermute, b["o"], b["inv_pos"], b["w"], y, y_dtype)

@@ -45,6 +45,12 @@ _SIGNATURES = {
                                                 _c_p, _i32, _c_p]),
     "w4a8_moe_swiglu_i8": (ctypes.c_int, [_c_p, _i64, _i64, _c_p, _c_p, _c_p, _c_p]),
     "w4a8_moe_quantize_weights_channel": (ctypes.c_int, [_c_p, _i64, _i64, _c_p, _c_p, _c_p]),
+    "w4a8_moe_grouped_gemm_swiglu": (ctypes.c_int, [_c_p, _c_p, _c_p, _i64, _c_p, _i32, _c_p, _c_p, _i64, _i64,
+                                                    _c_p, _c_p, _i32, _c_p]),
+    "w4a8_moe_grouped_gemm_swiglu_i8": (ctypes.c_int, [_c_p, _c_p, _c_p, _c_p, _i64, _c_p, _i32, _c_p, _c_p, _i64,
+                                                       _i64, _c_p, _c_p, _i32, _c_p]),
+    "w4a8_moe_requant": (ctypes.c_int, [_c_p, _c_p, _i64, _i64, _c_p, _c_p, _c_p]),
+    "w4a8_moe_requant_i8": (ctypes.c_int, [_c_p, _c_p, _i64, _i64, _c_p, _c_p, _c_p, _c_p]),
     "w4a8_moe_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "w4a8_moe_last_error": (ctypes.c_char_p, []),
     "w4a8_moe_device_supported": (ctypes.c_int, []),
@@ -367,3 +373,112 @@ def w4a8_moe_quantize_weights_channel(w: torch.Tensor, w_packed=None, w_scale=No
     _check("w4a8_moe_quantize_weights_channel",
            lib().w4a8_moe_quantize_weights_channel(_p(w), rows, K, _p(w_packed), _p(w_scale), _stream(dev)))
     return w_packed, w_scale
+
+
+# ------------------------------------------------------------------ fused epilogues
+def _act_out(M: int, I: int, dev, act, act_pmax):
+    act = torch.empty((M, I), dtype=torch.float32, device=dev) if act is None else act
+    act_pmax = torch.empty((M, I // 64), dtype=torch.float32, device=dev) if act_pmax is None else act_pmax
+    _need(act, "act", torch.float32, 2, dev)
+    _need(act_pmax, "act_pmax", torch.float32, 2, dev)
+    if act.shape[0] < M or act.shape[1] != I or act_pmax.shape[0] < M or act_pmax.shape[1] != I // 64:
+        raise ValueError("act must be at least [M_total, I] and act_pmax [M_total, I/64]")
+    return act, act_pmax
+
+
+def w4a8_moe_grouped_gemm_swiglu(a: torch.Tensor, a_scale: torch.Tensor, a_rows: torch.Tensor | None,
+                                 offsets: torch.Tensor, w13: torch.Tensor, s13: torch.Tensor, M_total: int,
+                                 act: torch.Tensor | None = None, act_pmax: torch.Tensor | None = None,
+                                 algo: int = W4A8_GG_AUTO):
+    """Gate/up GEMM with SwiGLU in its epilogue -> (act fp32 [M_total, I], partial row maxima of |act| [M_total, I/64])."""
+    _need(a, "a", torch.uint8, 2)
+    dev = a.device
+    _need(a_scale, "a_scale", torch.float32, 1, dev)
+    if a_rows is not None:
+        _need(a_rows, "a_rows", torch.int32, 1, dev)
+        if a_rows.numel() < M_total:
+            raise ValueError("a_rows must hold M_total entries")
+    _need(offsets, "offsets", torch.int32, 1, dev)
+    _need(w13, "w13", torch.int32, 3, dev)
+    _need(s13, "s13", torch.float32, 3, dev)
+    E, N2, KW = w13.shape
+    K = a.shape[1]
+    if N2 % 2 or KW * 8 != K or tuple(s13.shape) != (E, N2, K // 128) or offsets.numel() != E + 1:
+        raise ValueError("w13 [E,2I,K/8], s13 [E,2I,K/128] and offsets [E+1] must match a [*,K]")
+    if a_scale.numel() != a.shape[0]:
+        raise ValueError("a_scale must have one entry per row of a")
+    I = N2 // 2
+    act, act_pmax = _act_out(M_total, I, dev, act, act_pmax)
+    _check("w4a8_moe_grouped_gemm_swiglu",
+           lib().w4a8_moe_grouped_gemm_swiglu(_p(a), _p(a_scale), _p(a_rows), M_total, _p(offsets), E, _p(w13),
+                                              _p(s13), I, K, _p(act), _p(act_pmax), algo, _stream(dev)))
+    return act, act_pmax
+
+
+def w4a8_moe_grouped_gemm_swiglu_i8(a: torch.Tensor, a_scale: torch.Tensor, a_rowsum: torch.Tensor,
+                                    a_rows: torch.Tensor | None, offsets: torch.Tensor, w13: torch.Tensor,
+                                    s13: torch.Tensor, M_total: int, act: torch.Tensor | None = None,
+                                    act_pmax: torch.Tensor | None = None, algo: int = W4A8_GG_AUTO):
+    """INT8 form of w4a8_moe_grouped_gemm_swiglu (per-channel scales s13 [E, 2I])."""
+    _need(a, "a", torch.int8, 2)
+    dev = a.device
+    _need(a_scale, "a_scale", torch.float32, 1, dev)
+    _need(a_rowsum, "a_rowsum", torch.int32, 1, dev)
+    if a_rows is not None:
+        _need(a_rows, "a_rows", torch.int32, 1, dev)
+        if a_rows.numel() < M_total:
+            raise ValueError("a_rows must hold M_total entries")
+    _need(offsets, "offsets", torch.int32, 1, dev)
+    _need(w13, "w13", torch.int32, 3, dev)
+    _need(s13, "s13", torch.float32, 2, dev)
+    E, N2, KW = w13.shape
+    K = a.shape[1]
+    if N2 % 2 or KW * 8 != K or tuple(s13.shape) != (E, N2) or offsets.numel() != E + 1:
+        raise ValueError("w13 [E,2I,K/8], s13 [E,2I] and offsets [E+1] must match a [*,K]")
+    I = N2 // 2
+    act, act_pmax = _act_out(M_total, I, dev, act, act_pmax)
+    _check("w4a8_moe_grouped_gemm_swiglu_i8",
+           lib().w4a8_moe_grouped_gemm_swiglu_i8(_p(a), _p(a_scale), _p(a_rowsum), _p(a_rows), M_total,
+                                                 _p(offsets), E, _p(w13), _p(s13), I, K, _p(act), _p(act_pmax),
+                                                 algo, _stream(dev)))
+    return act, act_pmax
+
+
+def w4a8_moe_requant(act: torch.Tensor, act_pmax: torch.Tensor, qa=None, sa=None, M: int | None = None):
+    """act fp32 [M, I] with its partial row maxima [M, I/64] -> (E4M3 codes uint8 [M, I], scales fp32 [M])."""
+    _need(act, "act", torch.float32, 2)
+    dev = act.device
+    _need(act_pmax, "act_pmax", torch.float32, 2, dev)
+    M = act.shape[0] if M is None else M
+    I = act.shape[1]
+    qa = torch.empty((M, I), dtype=torch.uint8, device=dev) if qa is None else qa
+    sa = torch.empty((M,), dtype=torch.float32, device=dev) if sa is None else sa
+    _need(qa, "qa", torch.uint8, 2, dev)
+    _need(sa, "sa", torch.float32, 1, dev)
+    if act.shape[0] < M or act_pmax.shape[0] < M or act_pmax.shape[1] != I // 64 or qa.shape[0] < M \
+            or qa.shape[1] != I or sa.numel() < M:
+        raise ValueError("act, act_pmax, qa and sa must hold M rows of I")
+    _check("w4a8_moe_requant", lib().w4a8_moe_requant(_p(act), _p(act_pmax), M, I, _p(qa), _p(sa), _stream(dev)))
+    return qa, sa
+
+
+def w4a8_moe_requant_i8(act: torch.Tensor, act_pmax: torch.Tensor, qa=None, sa=None, rowsum=None,
+                        M: int | None = None):
+    """act fp32 [M, I] with its partial row maxima [M, I/64] -> (int8 codes, scales fp32 [M], code row sums [M])."""
+    _need(act, "act", torch.float32, 2)
+    dev = act.device
+    _need(act_pmax, "act_pmax", torch.float32, 2, dev)
+    M = act.shape[0] if M is None else M
+    I = act.shape[1]
+    qa = torch.empty((M, I), dtype=torch.int8, device=dev) if qa is None else qa
+    sa = torch.empty((M,), dtype=torch.float32, device=dev) if sa is None else sa
+    rowsum = torch.empty((M,), dtype=torch.int32, device=dev) if rowsum is None else rowsum
+    _need(qa, "qa", torch.int8, 2, dev)
+    _need(sa, "sa", torch.float32, 1, dev)
+    _need(rowsum, "rowsum", torch.int32, 1, dev)
+    if act.shape[0] < M or act_pmax.shape[0] < M or act_pmax.shape[1] != I // 64 or qa.shape[0] < M \
+            or qa.shape[1] != I or sa.numel() < M or rowsum.numel() < M:
+        raise ValueError("act, act_pmax, qa, sa and rowsum must hold M rows of I")
+    _check("w4a8_moe_requant_i8", lib().w4a8_moe_requant_i8(_p(act), _p(act_pmax), M, I, _p(qa), _p(sa),
+                                                            _p(rowsum), _stream(dev)))
+    return qa, sa, rowsum

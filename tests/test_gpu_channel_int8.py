@@ -92,6 +92,43 @@ def test_grouped_gemm_i8(E, N, K, counts, gather, algo, rng):
     assert rel.max(initial=0.0) <= 1e-6, rel.max()
 
 
+# ------------------------------------------------------- steps 4 + 5, fused
+@pytest.mark.parametrize("algo", ALGOS)
+@pytest.mark.parametrize("E,I,K,counts,gather", [
+    (4, 128, 128, [3, 0, 17, 1], True),
+    (3, 384, 384, [40, 1, 300], True),               # N = 768: a wide tile half past N
+    (2, 256, 2048, [257, 31], False),
+])
+def test_grouped_gemm_swiglu_i8(E, I, K, counts, gather, algo, rng):
+    codes, scale, rowsum, rows, offsets, words, ws = _problem(rng, E, 2 * I, K, counts, gather)
+    R = int(offsets[-1])
+    want = oracle.swiglu_f32(oracle.grouped_gemm_i8(codes, scale, rows, offsets, words, ws))
+    say(f"grouped_gemm_swiglu_i8 E={E} I={I} K={K} counts={counts} algo={algo}")
+    act, pmax = ops.w4a8_moe_grouped_gemm_swiglu_i8(
+        to_dev(codes), to_dev(scale), to_dev(rowsum), to_dev(rows) if rows is not None else None, to_dev(offsets),
+        to_dev(words), to_dev(ws), R, algo=algo)
+    act, pmax = host(act), host(pmax)
+    # the GEMM values differ from the oracle's by the rounding of the scale product only
+    assert_float_parity(act, want, "grouped_gemm_swiglu_i8", fro_tight=1e-5)
+    assert pmax.shape == (R, I // 64)
+    assert np.array_equal(pmax.max(axis=1), np.abs(act).max(axis=1))
+    assert np.all(pmax <= np.abs(act).max(axis=1, keepdims=True))
+
+
+@pytest.mark.parametrize("M,I", [(1, 128), (300, 2048)])
+def test_requant_i8(M, I, rng):
+    act = (rng.standard_normal((M, I)) * 3.0).astype(np.float32)
+    if M > 2:
+        act[1] = 0.0
+    pmax = np.abs(act).reshape(M, I // 64, 64).max(axis=2).astype(np.float32)
+    say(f"requant_i8 M={M} I={I}")
+    q, sq, rs = ops.w4a8_moe_requant_i8(to_dev(act), to_dev(pmax))
+    q_ref, s_ref, r_ref = oracle.quant_rows_i8(act)
+    assert np.array_equal(host(sq).view(np.uint32), s_ref.view(np.uint32))
+    assert np.array_equal(host(q), q_ref)
+    assert np.array_equal(host(rs), r_ref)
+
+
 # ------------------------------------------------------------------ step 5
 @pytest.mark.parametrize("M,I", [(5, 128), (300, 2048)])
 def test_swiglu_i8(M, I, rng):
@@ -126,14 +163,15 @@ def test_quantize_weights_channel(N, K, rng):
 
 
 # ------------------------------------------------------------------ the layer
+@pytest.mark.parametrize("fused", [True, False])
 @pytest.mark.parametrize("cfg", [0, "mid"])
 @pytest.mark.parametrize("algo", ALGOS)
-def test_layer_channel_int8(cfg, algo):
+def test_layer_channel_int8(cfg, algo, fused):
     wl = workloads.make_config(0) if cfg == 0 else workloads.make_custom(64, 1024, 256, 16, 4, seed=77)
     sh = wl.shape
     s13, s2 = workloads.channel_scales(wl)
-    say(f"layer_i8 {sh.name} algo={algo}")
-    moe = W4A8MoEChannel(to_dev(wl.w13), to_dev(s13), to_dev(wl.w2), to_dev(s2), k=sh.k)
+    say(f"layer_i8 {sh.name} algo={algo} fused={fused}")
+    moe = W4A8MoEChannel(to_dev(wl.w13), to_dev(s13), to_dev(wl.w2), to_dev(s2), k=sh.k, fused=fused)
     y = host(moe(bf16_to_dev(wl.x_bf16), to_dev(wl.logits), algo=algo))
     ref = oracle.moe_layer_i8(wl.x_bf16, wl.logits, wl.w13, s13, wl.w2, s2, k=sh.k)
     assert_float_parity(y, ref["y"], f"layer_i8 {sh.name}")

@@ -123,11 +123,23 @@ def test_sampled_rows_per_call(index):
     qx, sx = oracle.quant_act(wl.x_bf16[tokens])
     # gate/up GEMM: GPU rows P of the full run vs the oracle on those rows
     h = oracle.grouped_gemm(qx, sx, None, sub_off, wl.w13, wl.s13)
-    assert_float_parity(got["h"][P], h, f"config {index} gate/up", fro_tight=GEMM_FRO_TIGHT)
+    a32 = oracle.swiglu_f32(h)
+    # the layer runs the gate/up GEMM with SwiGLU fused into its epilogue
+    assert_float_parity(got["act"][P], a32, f"config {index} gate/up + SwiGLU", fro_tight=GEMM_FRO_TIGHT)
+    assert np.array_equal(got["pmax"][P].max(axis=1), np.abs(got["act"][P]).max(axis=1))
+    qa, sa = oracle.quant_rows(a32)
+    # the fused path's requant on the oracle's activations: bit-exact
+    pm = np.abs(a32).reshape(a32.shape[0], -1, 64).max(axis=2).astype(np.float32)
+    rq, rs = ops.w4a8_moe_requant(to_dev(a32), to_dev(pm))
+    assert np.array_equal(host(rq), qa) and np.array_equal(host(rs).view(np.uint32), sa.view(np.uint32))
+    # the unfused gate/up GEMM on the sampled rows, both kernels
+    for algo in (ops.W4A8_GG_STREAM, ops.W4A8_GG_TILED):
+        say(f"config {index}: gate/up GEMM on {P.size} rows algo={algo}")
+        gh = ops.w4a8_moe_grouped_gemm(to_dev(qx), to_dev(sx), None, to_dev(sub_off), moe.w13, moe.s13, P.size,
+                                       algo=algo)
+        assert_float_parity(host(gh), h, f"config {index} gate/up algo={algo}", fro_tight=GEMM_FRO_TIGHT)
     # SwiGLU on the oracle's h
     say(f"config {index}: swiglu on {P.size} oracle rows")
-    a32 = oracle.swiglu_f32(h)
-    qa, sa = oracle.quant_rows(a32)
     gq, gs = ops.w4a8_moe_swiglu(to_dev(h))
     gq, gs = host(gq), host(gs)
     assert np.all(np.abs(gs.astype(np.float64) - sa) <= 1e-6 * sa)

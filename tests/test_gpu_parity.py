@@ -157,6 +157,63 @@ def test_grouped_gemm_exact_integers(algo, rng):
     assert np.array_equal(host(out), want)
 
 
+# ------------------------------------------------------- steps 4 + 5, fused
+def _pmax_of(act):
+    """Partial row maxima of |act|, one per 64 columns (what the fused GEMM may write)."""
+    M, I = act.shape
+    return np.abs(act).reshape(M, I // 64, 64).max(axis=2).astype(np.float32)
+
+
+def _check_pmax(pmax, act):
+    # every entry is the max over some of the row's columns; their max is the row's
+    M, I = act.shape
+    assert pmax.shape == (M, I // 64)
+    row = np.abs(act).max(axis=1)
+    assert np.array_equal(pmax.max(axis=1), row)
+    assert np.all(pmax <= row[:, None])
+
+@pytest.mark.parametrize("algo", ALGOS)
+@pytest.mark.parametrize("E,I,K,counts,gather", [
+    (4, 128, 256, [3, 0, 17, 1], True),
+    (3, 256, 384, [70, 1, 129], False),
+    (2, 384, 1024, [300, 33], True),                  # N = 768: a wide tile half past N
+    (3, 128, 640, [200, 241, 0], True),
+])
+def test_grouped_gemm_swiglu(E, I, K, counts, gather, algo, rng):
+    w, s, offsets, a, sa, rows = _gemm_problem(rng, E, 2 * I, K, counts, src_rows=40 if gather else None)
+    h = oracle.grouped_gemm(a, sa, rows, offsets, w, s)
+    want = oracle.swiglu_f32(h)
+    M = int(offsets[-1])
+    say(f"grouped_gemm_swiglu E={E} I={I} K={K} counts={counts} gather={gather} algo={algo}")
+    act, pmax = ops.w4a8_moe_grouped_gemm_swiglu(to_dev(a), to_dev(sa), None if rows is None else to_dev(rows),
+                                                 to_dev(offsets), to_dev(w), to_dev(s), M, algo=algo)
+    act, pmax = host(act), host(pmax)
+    assert_float_parity(act, want, "grouped_gemm_swiglu", fro_tight=GEMM_FRO_TIGHT)
+    _check_pmax(pmax, act)
+    # the codes of the fused path against the unfused one on the same inputs
+    out = ops.w4a8_moe_grouped_gemm(to_dev(a), to_dev(sa), None if rows is None else to_dev(rows), to_dev(offsets),
+                                    to_dev(w), to_dev(s), M, algo=algo)
+    q_ref, s_ref = ops.w4a8_moe_swiglu(out)
+    q, sq = ops.w4a8_moe_requant(to_dev(act), to_dev(pmax))
+    q, sq, q_ref, s_ref = host(q), host(sq), host(q_ref), host(s_ref)
+    assert np.allclose(sq, s_ref, rtol=1e-5, atol=0)
+    diff = q != q_ref
+    assert np.all(near_midpoint(want, s_ref, rel=1e-4)[diff]), f"{int(diff.sum())} codes differ off a midpoint"
+
+
+@pytest.mark.parametrize("M,I", [(1, 128), (37, 256), (500, 2048)])
+def test_requant(M, I, rng):
+    act = (rng.standard_normal((M, I)) * np.exp2(rng.integers(-6, 6, size=(M, 1)))).astype(np.float32)
+    if M > 2:
+        act[1] = 0.0                                   # zero row: scale 1, codes 0
+    pmax = _pmax_of(act)
+    say(f"requant M={M} I={I}")
+    q, sq = ops.w4a8_moe_requant(to_dev(act), to_dev(pmax))
+    q_ref, s_ref = oracle.quant_rows(act)
+    assert np.array_equal(host(sq).view(np.uint32), s_ref.view(np.uint32))
+    assert np.array_equal(host(q), q_ref)
+
+
 # ------------------------------------------------------------------ step 5
 @pytest.mark.parametrize("M,I", [(1, 128), (37, 256), (500, 2048)])
 def test_swiglu(M, I, rng):
@@ -194,12 +251,12 @@ def test_unpermute(T, k, H, dt, rng):
 
 
 # -------------------------------------------------------------- whole layer
-def _layer_vs_oracle(wl, algo=ops.W4A8_GG_AUTO, y_dtype=torch.float32):
+def _layer_vs_oracle(wl, algo=ops.W4A8_GG_AUTO, y_dtype=torch.float32, fused=True):
     sh = wl.shape
     maxrel_bar = edge_shape_maxrel(sh.H) if sh.name.startswith("custom") else 1e-2
     res = oracle.moe_layer(wl.x_bf16, wl.logits, wl.w13, wl.s13, wl.w2, wl.s2, k=sh.k)
-    say(f"layer {sh.name} algo={algo}")
-    moe = W4A8MoE(to_dev(wl.w13), to_dev(wl.s13), to_dev(wl.w2), to_dev(wl.s2), k=sh.k)
+    say(f"layer {sh.name} algo={algo} fused={fused}")
+    moe = W4A8MoE(to_dev(wl.w13), to_dev(wl.s13), to_dev(wl.w2), to_dev(wl.s2), k=sh.k, fused=fused)
     y = moe(bf16_to_dev(wl.x_bf16), to_dev(wl.logits), algo=algo, y_dtype=y_dtype)
     b = moe.buffers(sh.T)
     assert np.array_equal(host(b["qx"]), res["qx"])
@@ -208,7 +265,12 @@ def _layer_vs_oracle(wl, algo=ops.W4A8_GG_AUTO, y_dtype=torch.float32):
     assert np.all(np.abs(host(b["w"]).astype(np.float64) - res["w"]) <= 1e-6 * np.abs(res["w"]))
     for name in ("offsets", "row_token", "inv_pos"):
         assert np.array_equal(host(b[name]), res[name]), name
-    assert_float_parity(host(b["h"]), res["h"], "gate/up", fro_tight=GEMM_FRO_TIGHT)
+    if fused:
+        act = host(b["act"])
+        assert_float_parity(act, res["a_f32"], "gate/up + SwiGLU", fro_tight=GEMM_FRO_TIGHT)
+        assert np.array_equal(host(b["pmax"]).max(axis=1), np.abs(act).max(axis=1)), "row maxima of act"
+    else:
+        assert_float_parity(host(b["h"]), res["h"], "gate/up", fro_tight=GEMM_FRO_TIGHT)
     yy = host(y)
     if y_dtype == torch.bfloat16:
         yy = oracle.bf16_bits_to_f32(yy)
@@ -224,6 +286,11 @@ def _layer_vs_oracle(wl, algo=ops.W4A8_GG_AUTO, y_dtype=torch.float32):
     r = assert_float_parity(yy, y_ref, "layer output", maxrel=maxrel_bar)
     say(f"layer output vs oracle: fro {fro_own:.2e}; {flips} midpoint code choices; vs matching reference {r}")
     return moe, y, r
+
+
+@pytest.mark.parametrize("algo", ALGOS)
+def test_layer_unfused(algo):
+    _layer_vs_oracle(workloads.make_custom(37, 384, 256, 5, 3, seed=21), algo=algo, fused=False)
 
 
 @pytest.mark.parametrize("algo", ALGOS)
