@@ -248,8 +248,11 @@ def main() -> int:
     R = sh.T * sh.k
     w13_bytes = 2 * sh.I * sh.H // 2 + 2 * sh.I * (1 if channel else sh.H // 128) * 4
     w2_bytes = sh.H * sh.I // 2 + sh.H * (1 if channel else sh.I // 128) * 4
+    # the layer's gate/up GEMM has SwiGLU fused into its epilogue: it writes act [R][I] and
+    # the partial row maxima [R][I/64] (fp32) instead of the [R][2I] gate/up output
+    out_bytes = R * sh.I * 4 + R * (sh.I // 64) * 4 if moe.fused else R * 2 * sh.I * 4
     gate_up_bytes = (touched * w13_bytes + sh.T * sh.H + sh.T * 4 * (2 if channel else 1) + R * 4 + (sh.E + 1) * 4
-                     + R * 2 * sh.I * 4)
+                     + out_bytes)
     gate_up_flops = 2.0 * R * 2 * sh.I * sh.H
     down_flops = 2.0 * R * sh.H * sh.I
     t_gu = per_step["gemm_gate_up"] * 1e-3
