@@ -73,7 +73,7 @@ def workload_tag(shape) -> str:
     return shape.name.split()[0] + f"_T{shape.T}"
 
 
-def cpu_baseline(wl, n_tokens: int, channel: bool = False) -> dict:
+def cpu_baseline(wl, n_tokens: int, scheme: str = "g128") -> dict:
     """The oracle layer on the first n_tokens tokens (single thread)."""
     import oracle
     try:
@@ -83,10 +83,14 @@ def cpu_baseline(wl, n_tokens: int, channel: bool = False) -> dict:
         limit = None
     sel = np.arange(n_tokens)
     t0 = time.perf_counter()
-    if channel:
+    if scheme == "channel":
         from quantized_grouped_gemm_token_amd import workloads
         s13c, s2c = workloads.channel_scales(wl)
         res = oracle.moe_layer_i8(wl.x_bf16[sel], wl.logits[sel], wl.w13, s13c, wl.w2, s2c, k=wl.shape.k)
+    elif scheme == "mxfp4":
+        from quantized_grouped_gemm_token_amd import workloads
+        w13m, s13m, w2m, s2m = workloads.mxfp4_weights(wl)
+        res = oracle.moe_layer_mxfp4(wl.x_bf16[sel], wl.logits[sel], w13m, s13m, w2m, s2m, k=wl.shape.k)
     else:
         res = oracle.moe_layer(wl.x_bf16[sel], wl.logits[sel], wl.w13, wl.s13, wl.w2, wl.s2, k=wl.shape.k)
     dt = time.perf_counter() - t0
@@ -165,8 +169,9 @@ def main() -> int:
                                                           "2 decode T=256, 3 prefill T=8192, 4 skewed T=16384")
     ap.add_argument("--cpu-tokens", type=int, default=16, help="tokens in the CPU oracle sample (0: skip)")
     ap.add_argument("--quiet", action="store_true")
-    ap.add_argument("--scheme", choices=("g128", "channel"), default="g128",
-                    help="g128: INT4 group-128 x FP8 per token (default); channel: per-channel INT4 x INT8 per token")
+    ap.add_argument("--scheme", choices=("g128", "channel", "mxfp4"), default="g128",
+                    help="g128: INT4 group-128 x FP8 per token (default); channel: per-channel INT4 x INT8 per "
+                         "token; mxfp4: MXFP4 group-32 x FP8 per token")
     ap.add_argument("--op", choices=("layer", "wquant"), default="layer",
                     help="layer: the MoE layer (default); wquant: the offline INT4 weight quantizer")
     ap.add_argument("--copy-bytes", type=int, default=0,
@@ -181,7 +186,7 @@ def main() -> int:
     import torch
 
     from quantized_grouped_gemm_token_amd import ops, workloads
-    from quantized_grouped_gemm_token_amd.layer import W4A8MoE, W4A8MoEChannel
+    from quantized_grouped_gemm_token_amd.layer import W4A8MoE, W4A8MoEChannel, W4A8MoEMxfp4
 
     log = (lambda *a: None) if args.quiet else (lambda *a: print("[bench]", *a, file=sys.stderr, flush=True))
     if args.copy_bytes:
@@ -211,9 +216,13 @@ def main() -> int:
     log(f"generated {sh.name} in {time.time() - t0:.1f} s")
     to = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)  # noqa: E731
     channel = args.scheme == "channel"
+    mxfp4 = args.scheme == "mxfp4"
     if channel:
         s13c, s2c = workloads.channel_scales(wl)
         moe = W4A8MoEChannel(to(wl.w13), to(s13c), to(wl.w2), to(s2c), k=sh.k)
+    elif mxfp4:
+        w13m, s13m, w2m, s2m = workloads.mxfp4_weights(wl)
+        moe = W4A8MoEMxfp4(to(w13m), to(s13m), to(w2m), to(s2m), k=sh.k)
     else:
         moe = W4A8MoE(to(wl.w13), to(wl.s13), to(wl.w2), to(wl.s2), k=sh.k)
     x = torch.from_numpy(wl.x_bf16.view(np.int16)).to(dev).view(torch.bfloat16)
@@ -246,8 +255,11 @@ def main() -> int:
     counts = np.diff(offsets)
     touched = int((counts > 0).sum())
     R = sh.T * sh.k
-    w13_bytes = 2 * sh.I * sh.H // 2 + 2 * sh.I * (1 if channel else sh.H // 128) * 4
-    w2_bytes = sh.H * sh.I // 2 + sh.H * (1 if channel else sh.I // 128) * 4
+    # packed 4-bit weights plus scales: fp32 per row (channel), fp32 per 128 (g128), one E8M0 byte per 32 (mxfp4)
+    def scale_bytes(n_rows, k):
+        return n_rows * (4 if channel else (k // 32 if mxfp4 else k // 128 * 4))
+    w13_bytes = 2 * sh.I * sh.H // 2 + scale_bytes(2 * sh.I, sh.H)
+    w2_bytes = sh.H * sh.I // 2 + scale_bytes(sh.H, sh.I)
     # the layer's gate/up GEMM has SwiGLU fused into its epilogue: it writes act [R][I] and
     # the partial row maxima [R][I/64] (fp32) instead of the [R][2I] gate/up output
     out_bytes = R * sh.I * 4 + R * (sh.I // 64) * 4 if moe.fused else R * 2 * sh.I * 4
@@ -260,7 +272,7 @@ def main() -> int:
     decode = args.config in (0, 1, 2)
     kernel = "gg_stream" if decode else "gg_tiled"
     khash = kernel_sources_hash(kernel)
-    tag = workload_tag(sh) + ("_channel" if channel else "")
+    tag = workload_tag(sh) + ("" if args.scheme == "g128" else "_" + args.scheme)
     traffic = load_traffic(os.path.join(ROOT, "profiles", f"{kernel}_{tag}_pmc.txt"), khash)
     if decode:
         achieved = gate_up_bytes / t_gu / 1e9
@@ -287,16 +299,18 @@ def main() -> int:
     cpu = None
     if args.cpu_tokens > 0:
         log(f"CPU oracle on {args.cpu_tokens} tokens ...")
-        cpu = cpu_baseline(wl, min(args.cpu_tokens, sh.T), channel)
+        cpu = cpu_baseline(wl, min(args.cpu_tokens, sh.T), args.scheme)
 
     line = {
         "metric": METRIC, "value": round(sh.T / (ms_step * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 5), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None,
-        "dtype": "int8 x int4 (int32 accumulate)" if channel else "fp8e4m3 x int4 (fp32 accumulate)",
-        "data": "synthetic (seeded; uniform INT4 words, lognormal scales, N(0,1) bf16 activations)",
+        "dtype": {"channel": "int8 x int4 (int32 accumulate)", "mxfp4": "fp8e4m3 x mxfp4 e2m1 (fp32 accumulate)",
+                  "g128": "fp8e4m3 x int4 (fp32 accumulate)"}[args.scheme],
+        "data": "synthetic (seeded; uniform 4-bit codes, lognormal scales, N(0,1) bf16 activations)",
         "config": {"workload": sh.name, "tokens": sh.T, "hidden": sh.H, "intermediate": sh.I, "experts": sh.E,
-                   "top_k": sh.k, "scheme": "per-channel int4 x per-token int8" if channel else "int4 g128 x fp8"},
+                   "top_k": sh.k, "scheme": {"channel": "per-channel int4 x per-token int8",
+                                             "mxfp4": "mxfp4 g32 x fp8", "g128": "int4 g128 x fp8"}[args.scheme]},
         "roofline": roof, "cpu_baseline": cpu, "gemms": gemms,
         "step_ms": {k: round(v, 5) for k, v in per_step.items()},
         "device": torch.cuda.get_device_name(0), "kernel_sources_hash": khash,

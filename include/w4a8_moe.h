@@ -307,6 +307,55 @@ int w4a8_moe_requant(const float* act, const float* act_pmax, int64_t M, int64_t
 int w4a8_moe_requant_i8(const float* act, const float* act_pmax, int64_t M, int64_t I, int8_t* qa, float* sa,
                         int32_t* rowsum, void* stream);
 
+/*
+ * ---- MXFP4 group-32 weights ----------------------------------------------
+ * The 4-bit alternative the "GLM-5.3-W4A8" card compares INT4 group 128
+ * against (section 量化方式: MXFP4 with groups of 32, and the note that
+ * Hopper has no FP4 matrix cores).  gfx950 multiplies FP4 by FP8 in its
+ * matrix cores, so the same per-token FP8 activations (steps 1 and 5) meet
+ * MXFP4 weights; routing, permutation, requant and combine are unchanged.
+ * The format is the Open Compute Project microscaling one: E2M1 elements
+ * (magnitudes 0, .5, 1, 1.5, 2, 3, 4, 6; bit 3 the sign) sharing one E8M0
+ * scale (byte b = 2^(b - 127)) per 32 consecutive weights along K.
+ *   Weights : u8 [E][N][K/2], element k of a row in the low nibble of byte
+ *             k/2 when k is even, the high nibble when odd.
+ *   Scales  : u8 [E][N][K/32], the E8M0 byte of elements 32j .. 32j+31.
+ */
+
+/*
+ * Offline weight quantizer, MXFP4.  Per block of 32 (rows x K fp32, row-major):
+ *   amax = max |w| (1 if the block is all zero); X = floor(log2 amax) - 2,
+ *   clamped to [-127, 127]; w_scale byte = X + 127;
+ *   code = E2M1 of w * 2^-X: the nearest magnitude, ties to the code with
+ *   mantissa bit 0, saturating at 6, with the sign bit of w.
+ *   w : fp32 [rows][K], 16-byte aligned.  w_packed : u8 [rows][K/2], 2-byte aligned.
+ *   w_scale : u8 [rows][K/32].  Rules : rows >= 0, K > 0, K % 32 == 0.
+ */
+int w4a8_moe_quantize_weights_mxfp4(const float* w, int64_t rows, int64_t K, uint8_t* w_packed, uint8_t* w_scale,
+                                    void* stream);
+
+/*
+ * Step 4, MXFP4 weights:
+ *   out[p, n] = a_scale[r] * sum_k E4M3(a[r, k]) * E2M1(w[e, n, k]) * 2^(w_scale[e, n, k/32] - 127)
+ *   (r = a_rows ? a_rows[p] : p; exact products, fp32 sums).
+ *   a, a_scale, a_rows, offsets, out, algo : as in w4a8_moe_grouped_gemm_algo.
+ *   w_packed : u8 [E][N][K/2], 16-byte aligned.  w_scale : u8 [E][N][K/32], 4-byte aligned.
+ *   Rules : N % 64 == 0, K % 128 == 0, 1 <= E <= 1024; errors as in w4a8_moe_grouped_gemm_algo.
+ */
+int w4a8_moe_grouped_gemm_mxfp4(const uint8_t* a, const float* a_scale, const int32_t* a_rows, int64_t M_total,
+                                const int32_t* offsets, int32_t E, const uint8_t* w_packed, const uint8_t* w_scale,
+                                int64_t N, int64_t K, float* out, int32_t algo, void* stream);
+
+/*
+ * Steps 4 + 5a, MXFP4 weights: as w4a8_moe_grouped_gemm_swiglu with the
+ * products of w4a8_moe_grouped_gemm_mxfp4 (w13 : u8 [E][2I][K/2], 16-byte
+ * aligned; s13 : u8 [E][2I][K/32], 4-byte aligned).  Follow with w4a8_moe_requant.
+ */
+int w4a8_moe_grouped_gemm_swiglu_mxfp4(const uint8_t* a, const float* a_scale, const int32_t* a_rows,
+                                       int64_t M_total, const int32_t* offsets, int32_t E, const uint8_t* w13,
+                                       const uint8_t* s13, int64_t I, int64_t K, float* act, float* act_pmax,
+                                       int32_t algo, void* stream);
+
 /* Static name of a status code ("W4A8_OK", ...). */
 const char* w4a8_moe_status_string(int status);
 

@@ -289,7 +289,7 @@ int w4a8_moe_quantize_weights_channel(const float* w, int64_t rows, int64_t K, i
 
 // the shape, pointer and alignment rules shared by the two fused gate/up GEMMs
 static int check_gemm_swiglu(const char* name, const void* a, const float* a_scale, const int32_t* a_rows,
-                             int64_t M_total, const int32_t* offsets, int32_t E, const int32_t* w13, const float* s13,
+                             int64_t M_total, const int32_t* offsets, int32_t E, const void* w13, const void* s13,
                              int64_t I, int64_t K, const float* act, const float* act_pmax, int32_t algo) {
   if (M_total < 0 || M_total >= kMaxRows)
     return fail(W4A8_ERR_SHAPE, "%s: M_total=%lld out of range", name, (long long)M_total);
@@ -372,6 +372,72 @@ int w4a8_moe_requant_i8(const float* act, const float* act_pmax, int64_t M, int6
   if (int st = check_device()) return st;
   (void)hipGetLastError();
   return launched(w4a8::launch_requant_i8(act, act_pmax, M, I, qa, sa, rowsum, as_stream(stream)), "requant_i8");
+}
+
+int w4a8_moe_quantize_weights_mxfp4(const float* w, int64_t rows, int64_t K, uint8_t* w_packed, uint8_t* w_scale,
+                                    void* stream) {
+  if (rows < 0 || rows >= kMaxRows)
+    return fail(W4A8_ERR_SHAPE, "quantize_weights_mxfp4: rows=%lld out of range", (long long)rows);
+  if (K <= 0 || K % 32 || K >= kMaxRows)
+    return fail(W4A8_ERR_SHAPE, "quantize_weights_mxfp4: K=%lld must be a positive multiple of 32 below 2^31",
+                (long long)K);
+  if (rows == 0) return ok();
+  if (!w || !w_packed || !w_scale) return fail(W4A8_ERR_NULL, "quantize_weights_mxfp4: null pointer");
+  if (!aligned(w, 16) || !aligned(w_packed, 2))
+    return fail(W4A8_ERR_ALIGN, "quantize_weights_mxfp4: w must be 16-byte aligned, w_packed 2-byte");
+  if (int st = check_device()) return st;
+  (void)hipGetLastError();
+  return launched(w4a8::launch_wquant_mxfp4(w, rows, K, w_packed, w_scale, as_stream(stream)),
+                  "quantize_weights_mxfp4");
+}
+
+// the kernel for an MXFP4 GEMM (plain or fused), once every argument is checked
+static int run_gemm_mx(w4a8::GemmArgs g, int32_t algo, const char* name, void* stream) {
+  g.mx = true;
+  if (algo == W4A8_GG_AUTO) algo = (g.M_total <= 32 * (int64_t)g.E) ? W4A8_GG_STREAM : W4A8_GG_TILED;
+  (void)hipGetLastError();
+  if (algo == W4A8_GG_STREAM) return launched(w4a8::launch_gg_stream(g, as_stream(stream)), name);
+  return launched(w4a8::launch_gg_tiled(g, as_stream(stream)), name);
+}
+
+int w4a8_moe_grouped_gemm_mxfp4(const uint8_t* a, const float* a_scale, const int32_t* a_rows, int64_t M_total,
+                                const int32_t* offsets, int32_t E, const uint8_t* w_packed, const uint8_t* w_scale,
+                                int64_t N, int64_t K, float* out, int32_t algo, void* stream) {
+  if (M_total < 0 || M_total >= kMaxRows)
+    return fail(W4A8_ERR_SHAPE, "grouped_gemm_mxfp4: M_total=%lld out of range", (long long)M_total);
+  if (E < 1 || E > 1024) return fail(W4A8_ERR_SHAPE, "grouped_gemm_mxfp4: E=%d must be in [1, 1024]", E);
+  if (N <= 0 || N % 64)
+    return fail(W4A8_ERR_SHAPE, "grouped_gemm_mxfp4: N=%lld must be a positive multiple of 64", (long long)N);
+  if (K <= 0 || K % 128)
+    return fail(W4A8_ERR_SHAPE, "grouped_gemm_mxfp4: K=%lld must be a positive multiple of 128", (long long)K);
+  if (algo < W4A8_GG_AUTO || algo > W4A8_GG_TILED)
+    return fail(W4A8_ERR_SHAPE, "grouped_gemm_mxfp4: unknown algo %d", algo);
+  if (M_total == 0) return ok();
+  if (!a || !a_scale || !offsets || !w_packed || !w_scale || !out)
+    return fail(W4A8_ERR_NULL, "grouped_gemm_mxfp4: null pointer");
+  if (!aligned(a, 16) || !aligned(w_packed, 16) || !aligned(out, 16) || !aligned(a_scale, 4) ||
+      !aligned(w_scale, 4) || !aligned(offsets, 4) || !aligned(a_rows, 4))
+    return fail(W4A8_ERR_ALIGN, "grouped_gemm_mxfp4: a, w_packed and out must be 16-byte aligned, the rest 4-byte");
+  if (int st = check_device()) return st;
+  const w4a8::GemmArgs g{a, a_scale, nullptr, a_rows, M_total, offsets, E,
+                         reinterpret_cast<const int32_t*>(w_packed), reinterpret_cast<const float*>(w_scale), N, K,
+                         out};
+  return run_gemm_mx(g, algo, "grouped_gemm_mxfp4", stream);
+}
+
+int w4a8_moe_grouped_gemm_swiglu_mxfp4(const uint8_t* a, const float* a_scale, const int32_t* a_rows,
+                                       int64_t M_total, const int32_t* offsets, int32_t E, const uint8_t* w13,
+                                       const uint8_t* s13, int64_t I, int64_t K, float* act, float* act_pmax,
+                                       int32_t algo, void* stream) {
+  if (int st = check_gemm_swiglu("grouped_gemm_swiglu_mxfp4", a, a_scale, a_rows, M_total, offsets, E, w13, s13, I,
+                                 K, act, act_pmax, algo))
+    return st;
+  if (M_total == 0) return ok();
+  if (int st = check_device()) return st;
+  w4a8::GemmArgs g{a, a_scale, nullptr, a_rows, M_total, offsets, E, reinterpret_cast<const int32_t*>(w13),
+                   reinterpret_cast<const float*>(s13), 2 * I, K, act};
+  g.pmax = act_pmax;
+  return run_gemm_mx(g, algo, "grouped_gemm_swiglu_mxfp4", stream);
 }
 
 int w4a8_moe_unpermute(const float* o, const int32_t* inv_pos, const float* w, int64_t T, int32_t k, int64_t H,

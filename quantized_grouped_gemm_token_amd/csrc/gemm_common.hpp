@@ -38,6 +38,29 @@ __device__ __forceinline__ v4f mfma16x16x128(v8i a, v8i b, v4f c) {
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
 }
 
+// v_mfma_scale_f32_16x16x128_f8f6f4 with A E4M3 (unit block scales) and B
+// MXFP4: E2M1 codes with E8M0 block scales applied by the matrix core.
+// With an FP4 B the matrix core reads the K elements of the two operands in
+// different orders:
+//   B: lane l supplies column l % 16, K elements 32 (l / 16) .. +32 as 16
+//      packed bytes (element k in the low nibble of byte k/2 when k is even)
+//      in the first four dwords of the operand; byte 0 of its scale operand
+//      is the E8M0 scale of exactly those 32 elements (one MX block);
+//   A: lane l supplies row l % 16, K bytes 16 (l / 16) .. +16 in its first
+//      four dwords and K bytes 64 + 16 (l / 16) .. +16 in the last four.
+// D as in the FP8 form.  The products are exact; D = C + sum in fp32.
+__device__ __forceinline__ v4f mfma_mx(v8i a, i32x4 b, v4f c, int scale_b) {
+  const v8i bb = {b[0], b[1], b[2], b[3], 0, 0, 0, 0};
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, bb, c, 0, 4, 0, 0x7F7F7F7F, 0, scale_b);
+}
+
+// The three weight forms of the grouped GEMM kernels.
+enum WeightForm : int {
+  kFormG128 = 0,      // INT4 group 128 (uint4b8 in int32 words) x FP8 activations, fp32 group scales
+  kFormChannel = 1,   // INT4 per channel x INT8 activations, int32 accumulation
+  kFormMx = 2,        // MXFP4 group 32 x FP8 activations, E8M0 block scales in the matrix core
+};
+
 // INT8 matrix-core products for the per-channel variant (int32 accumulation).
 // 16x16x64: lane l supplies A row (l % 16) and B column (l % 16), K elements
 // 16 * (l / 16) .. +16 of the 64; D as in the 16x16 FP8 form.

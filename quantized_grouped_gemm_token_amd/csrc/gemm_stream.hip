@@ -22,6 +22,14 @@
 // buffered, with one barrier per chunk.  Group scales are read as 16-byte
 // vectors (4 groups) when the group count allows.
 //
+// MXFP4 weights (group 32) have the same 64 packed bytes per row and group,
+// so the same loads and selects give each lane the 16 bytes of its K quarter,
+// which are the B operand as they are; the group's word of E8M0 block scales
+// is read where the fp32 group scale is, and the lane passes its quarter's
+// byte to the matrix core, which applies it: the products accumulate straight
+// into acc.  The activations are staged in the K order the FP4 form of the
+// instruction reads (16-byte chunks q and q + 4 for lane group q).
+//
 // Grid: (ceil(N / (64 NS)), E); 256 threads = 4 waves side by side in N.  An
 // expert with no rows returns at once; one with more than 16 rows loops over
 // M blocks, re-streaming its weights (the tiled kernel is the one for many
@@ -40,7 +48,8 @@ __device__ __forceinline__ int row_ror8(int v) { return __builtin_amdgcn_mov_dpp
 
 // LDS image of the activation tile of one chunk: for each group h of the
 // chunk and MFMA lane L, the 32 bytes lane L feeds to the MFMA (row L % 16,
-// K quarter L / 16 of group h).
+// K bytes 32 (L / 16) .. +31 of group h; MX form: K bytes 16 (L / 16) .. +15
+// and 64 + 16 (L / 16) .. +15).
 template <int CH>
 struct StreamSmem {
   uint8_t a[2][2 * CH][64][32];
@@ -65,7 +74,7 @@ __device__ __forceinline__ void a_chunk_load(AChunk<CH>& r, const uint8_t* arow_
   }
 }
 
-template <int CH>
+template <int CH, bool kMx>
 __device__ __forceinline__ void a_chunk_store(const AChunk<CH>& r, StreamSmem<CH>& sm, int buf, int ngroups) {
   const int row = threadIdx.x >> 4, c0 = threadIdx.x & 15;
 #pragma unroll
@@ -74,7 +83,8 @@ __device__ __forceinline__ void a_chunk_store(const AChunk<CH>& r, StreamSmem<CH
     const int k = c * 16;                    // byte within the chunk's row
     if (k < ngroups * kGroup) {
       const int h = k >> 7, kk = k & 127;    // group within the chunk, K within the group
-      *reinterpret_cast<i32x4*>(&sm.a[buf][h][row + 16 * (kk >> 5)][kk & 31]) = r.v[i];
+      const int q = kMx ? (kk >> 4) & 3 : kk >> 5, o = kMx ? (kk >> 6) * 16 : kk & 31;   // lane group, byte in it
+      *reinterpret_cast<i32x4*>(&sm.a[buf][h][row + 16 * q][o]) = r.v[i];
     }
   }
 }
@@ -120,6 +130,26 @@ __device__ __forceinline__ void pair_compute(const WPair<NS>& w, const float (&s
   }
 }
 
+// the MXFP4 form of one group pair: sb0 / sb1 hold the lane's E8M0 scale
+// bytes (byte 0) of groups g and g + 1
+template <int NS>
+__device__ __forceinline__ void pair_compute_mx(const WPair<NS>& w, const int (&sb0)[NS], const int (&sb1)[NS],
+                                                const uint8_t* a0, const uint8_t* a1, bool lo, v4f (&acc)[NS]) {
+  const v8i av0 = *reinterpret_cast<const v8i*>(a0);
+  const v8i av1 = *reinterpret_cast<const v8i*>(a1);
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    i32x4 t0, t1;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      t0[q] = lo ? w.wa[s][q] : w.wb[s][q];
+      t1[q] = row_ror8(lo ? w.wb[s][q] : w.wa[s][q]);
+    }
+    acc[s] = mfma_mx(av0, t0, acc[s], sb0[s]);
+    acc[s] = mfma_mx(av1, t1, acc[s], sb1[s]);
+  }
+}
+
 // the per-channel INT8 form of one group pair: int32 products, no scales
 // (the nibbles u = q + 8 are the INT8 B operand; the offset is removed with
 // the activation row sums in the epilogue)
@@ -144,13 +174,14 @@ __device__ __forceinline__ void pair_compute_i8(const WPair<NS>& w, const uint8_
   }
 }
 
-// kInt8: the per-channel variant (INT8 activations with row sums a_rowsum,
-// one scale per weight row in w_scale [E][N]); otherwise the group-128 FP8 form.
+// kForm: kFormChannel, the per-channel variant (INT8 activations with row sums
+// a_rowsum, one scale per weight row in w_scale [E][N]); kFormG128, the
+// group-128 FP8 form; kFormMx, MXFP4 weights (w_scale holds the E8M0 bytes).
 // kSwiglu: the fused gate/up form: a wave's two subtiles are the gate and the
 // up rows of the same 16 output columns (gate_up_row), and the epilogue
 // writes act = silu(gate) * up [M][N/2] and the workgroup's max |act| of each
 // row (its 64 output columns) to pmax[p][blockIdx.x].
-template <int NS, int CH, bool kInt8, bool kSwiglu>
+template <int NS, int CH, int kForm, bool kSwiglu>
 __global__ __launch_bounds__(kStreamThreads) void gg_stream_kernel(const uint8_t* __restrict__ a,
                                                                    const float* __restrict__ a_scale,
                                                                    const int32_t* __restrict__ a_rowsum,
@@ -161,6 +192,8 @@ __global__ __launch_bounds__(kStreamThreads) void gg_stream_kernel(const uint8_t
                                                                    int64_t K, float* __restrict__ out,
                                                                    float* __restrict__ pmax) {
   static_assert(!kSwiglu || NS == 2, "fused SwiGLU pairs the two subtiles of a wave");
+  constexpr bool kInt8 = kForm == kFormChannel;
+  constexpr bool kMx = kForm == kFormMx;
   __shared__ StreamSmem<CH> sm;
   const int e = blockIdx.y;
   const int r0 = offsets[e], r1 = offsets[e + 1];
@@ -200,7 +233,7 @@ __global__ __launch_bounds__(kStreamThreads) void gg_stream_kernel(const uint8_t
     {
       AChunk<CH> ar;
       a_chunk_load(ar, arow_t, 0, min(G, 2 * CH));
-      a_chunk_store(ar, sm, 0, min(G, 2 * CH));
+      a_chunk_store<CH, kMx>(ar, sm, 0, min(G, 2 * CH));
     }
     __syncthreads();
     for (int ci = 0; ci < nchunks; ++ci) {
@@ -240,19 +273,26 @@ __global__ __launch_bounds__(kStreamThreads) void gg_stream_kernel(const uint8_t
           }
         }
       } else if (active) {
-        // scales of this chunk's groups for each subtile
-        float sc[NS][2 * CH];
+        // scales of this chunk's groups for each subtile, as bits: fp32 group
+        // scales, or (MX) words of E8M0 bytes, shifted so that byte 0 is the
+        // lane's K quarter
+        uint32_t sc[NS][2 * CH];
 #pragma unroll
         for (int s = 0; s < NS; ++s) {
+          const uint32_t* srw = reinterpret_cast<const uint32_t*>(srow[s]);
           if (vec_scales && ng == 2 * CH) {
 #pragma unroll
             for (int v = 0; v < (2 * CH) / 4; ++v) {
-              const f32x4 q4 = *reinterpret_cast<const f32x4*>(srow[s] + g0 + 4 * v);
+              const u32x4 q4 = *reinterpret_cast<const u32x4*>(srw + g0 + 4 * v);
               sc[s][4 * v] = q4[0]; sc[s][4 * v + 1] = q4[1]; sc[s][4 * v + 2] = q4[2]; sc[s][4 * v + 3] = q4[3];
             }
           } else {
 #pragma unroll
-            for (int h = 0; h < 2 * CH; ++h) sc[s][h] = h < ng ? srow[s][g0 + h] : 0.f;
+            for (int h = 0; h < 2 * CH; ++h) sc[s][h] = h < ng ? srw[g0 + h] : 0u;
+          }
+          if constexpr (kMx) {
+#pragma unroll
+            for (int h = 0; h < 2 * CH; ++h) sc[s][h] >>= 8 * kq;
           }
         }
         const int npairs = ng >> 1;
@@ -263,32 +303,55 @@ __global__ __launch_bounds__(kStreamThreads) void gg_stream_kernel(const uint8_t
             w_pair_load(w0, pa, pb, g0 + 2 * u);
             const bool two = u + 1 < npairs;
             if (two) w_pair_load(w1, pa, pb, g0 + 2 * u + 2);
-            float s0[NS], s1[NS];
+            if constexpr (kMx) {
+              int s0[NS], s1[NS];
 #pragma unroll
-            for (int s = 0; s < NS; ++s) { s0[s] = sc[s][2 * u]; s1[s] = sc[s][2 * u + 1]; }
-            pair_compute(w0, s0, s1, &sm.a[buf][2 * u][lane][0], &sm.a[buf][2 * u + 1][lane][0], lo, acc);
-            if (two) {
+              for (int s = 0; s < NS; ++s) { s0[s] = (int)sc[s][2 * u]; s1[s] = (int)sc[s][2 * u + 1]; }
+              pair_compute_mx(w0, s0, s1, &sm.a[buf][2 * u][lane][0], &sm.a[buf][2 * u + 1][lane][0], lo, acc);
+              if (two) {
 #pragma unroll
-              for (int s = 0; s < NS; ++s) { s0[s] = sc[s][2 * u + 2]; s1[s] = sc[s][2 * u + 3]; }
-              pair_compute(w1, s0, s1, &sm.a[buf][2 * u + 2][lane][0], &sm.a[buf][2 * u + 3][lane][0], lo, acc);
+                for (int s = 0; s < NS; ++s) { s0[s] = (int)sc[s][2 * u + 2]; s1[s] = (int)sc[s][2 * u + 3]; }
+                pair_compute_mx(w1, s0, s1, &sm.a[buf][2 * u + 2][lane][0], &sm.a[buf][2 * u + 3][lane][0], lo,
+                                acc);
+              }
+            } else {
+              float s0[NS], s1[NS];
+#pragma unroll
+              for (int s = 0; s < NS; ++s) {
+                s0[s] = __uint_as_float(sc[s][2 * u]);
+                s1[s] = __uint_as_float(sc[s][2 * u + 1]);
+              }
+              pair_compute(w0, s0, s1, &sm.a[buf][2 * u][lane][0], &sm.a[buf][2 * u + 1][lane][0], lo, acc);
+              if (two) {
+#pragma unroll
+                for (int s = 0; s < NS; ++s) {
+                  s0[s] = __uint_as_float(sc[s][2 * u + 2]);
+                  s1[s] = __uint_as_float(sc[s][2 * u + 3]);
+                }
+                pair_compute(w1, s0, s1, &sm.a[buf][2 * u + 2][lane][0], &sm.a[buf][2 * u + 3][lane][0], lo, acc);
+              }
             }
           }
         }
         if (ng & 1) {   // a last single group: each lane reads its own column's quarter
           const int h = ng - 1;
           const v8i av = *reinterpret_cast<const v8i*>(&sm.a[buf][h][lane][0]);
-          const v4f c = mfma16x16x128(av, bias_operand(), v4f{0.f, 0.f, 0.f, 0.f});
+          const v4f c = kMx ? v4f{0.f, 0.f, 0.f, 0.f} : mfma16x16x128(av, bias_operand(), v4f{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
           for (int s = 0; s < NS; ++s) {
             const uint8_t* pself = pa[s] - (lo ? 0 : 64) + (int64_t)(col - (col & 7)) * row_bytes;
             const i32x4 wq = __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(pself + (g0 + h) * 64));
-            const v4f d = mfma16x16x128(av, nibbles_to_fp8(wq), c);
+            if constexpr (kMx) {
+              acc[s] = mfma_mx(av, wq, acc[s], (int)sc[s][h]);
+            } else {
+              const v4f d = mfma16x16x128(av, nibbles_to_fp8(wq), c);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) acc[s][r] = fmaf(sc[s][h], d[r], acc[s][r]);
+              for (int r = 0; r < 4; ++r) acc[s][r] = fmaf(__uint_as_float(sc[s][h]), d[r], acc[s][r]);
+            }
           }
         }
       }
-      if (has_next) a_chunk_store(next, sm, buf ^ 1, ng_next);
+      if (has_next) a_chunk_store<CH, kMx>(next, sm, buf ^ 1, ng_next);
       __syncthreads();
     }
 
@@ -330,14 +393,14 @@ __global__ __launch_bounds__(kStreamThreads) void gg_stream_kernel(const uint8_t
           if constexpr (kSwiglu) {
             const int pc = min(p, r1 - 1);
             const int64_t src = a_rows ? a_rows[pc] : pc;
-            const float rs = a_scale[src] * kUnitScale;
+            const float rs = a_scale[src] * (kMx ? 1.0f : kUnitScale);
             const float y = silu_mul(acc[0][r] * rs, acc[1][r] * rs);
             const float m = max16(p < r1 ? fabsf(y) : 0.0f);
             if (p < r1) out[(int64_t)p * (N / 2) + n0 / 2 + col] = y;
             if (col == 0) sm.rmax[wave][kq * 4 + r] = m;
           } else if (p < r1) {
             const int64_t src = a_rows ? a_rows[p] : p;
-            const float rs = a_scale[src] * kUnitScale;
+            const float rs = a_scale[src] * (kMx ? 1.0f : kUnitScale);
 #pragma unroll
             for (int s = 0; s < NS; ++s) out[(int64_t)p * N + n0 + 16 * s + col] = acc[s][r] * rs;
           }
@@ -357,20 +420,22 @@ __global__ __launch_bounds__(kStreamThreads) void gg_stream_kernel(const uint8_t
   }
 }
 
-template <int NS, int CH, bool kInt8, bool kSwiglu>
+template <int NS, int CH, int kForm, bool kSwiglu>
 static void launch_variant(const GemmArgs& g, hipStream_t stream) {
   const dim3 grid((unsigned)((g.N + 64 * NS - 1) / (64 * NS)), (unsigned)g.E);
-  hipLaunchKernelGGL((gg_stream_kernel<NS, CH, kInt8, kSwiglu>), grid, dim3(kStreamThreads), 0, stream, g.a,
+  hipLaunchKernelGGL((gg_stream_kernel<NS, CH, kForm, kSwiglu>), grid, dim3(kStreamThreads), 0, stream, g.a,
                      g.a_scale, g.a_rowsum, g.a_rows, g.offsets, g.w_packed, g.w_scale, g.N, g.K, g.out, g.pmax);
 }
 
 hipError_t launch_gg_stream(const GemmArgs& g, hipStream_t stream) {
   if (g.pmax) {
-    if (g.a_rowsum) launch_variant<2, 4, true, true>(g, stream);
-    else launch_variant<2, 4, false, true>(g, stream);
+    if (g.a_rowsum) launch_variant<2, 4, kFormChannel, true>(g, stream);
+    else if (g.mx) launch_variant<2, 4, kFormMx, true>(g, stream);
+    else launch_variant<2, 4, kFormG128, true>(g, stream);
   } else {
-    if (g.a_rowsum) launch_variant<2, 4, true, false>(g, stream);
-    else launch_variant<2, 4, false, false>(g, stream);
+    if (g.a_rowsum) launch_variant<2, 4, kFormChannel, false>(g, stream);
+    else if (g.mx) launch_variant<2, 4, kFormMx, false>(g, stream);
+    else launch_variant<2, 4, kFormG128, false>(g, stream);
   }
   return hipGetLastError();
 }

@@ -36,6 +36,15 @@
 // landed, and are published by the one barrier per group.  They enter each
 // product as its accumulator input.
 //
+// MXFP4 weights (group 32) use the same ring and the same loads: 64 packed
+// bytes per column and group, and one 4-byte word of E8M0 scales per column
+// and group (the four 32-element blocks of the group) in place of the fp32
+// group scale.  The matrix core applies the block scales itself, so the
+// group's products accumulate straight into acc (no scale FMAs, no row sums:
+// E2M1 is signed), the weight bytes are the B operand as they are, and the A
+// operand is read as the 16-byte chunks q and q + 4 that the FP4 form of the
+// instruction pairs with B's K quarter q.
+//
 // Tile order: an expert's tiles are numbered by pairs of 256-column blocks:
 // the square tiles of both blocks (M blocks adjacent), then the wide tile
 // that covers the same 512 columns.  Each XCD runs windows of consecutive
@@ -116,16 +125,17 @@ __device__ __forceinline__ int tiles_of(int rows, int nb, int nw) {
   return square_mblocks(rows) * nb + has_wide(rows) * nw;
 }
 
-// kInt8: the per-channel variant (INT8 activations with row code sums
-// a_rowsum, one scale per weight row in w_scale [E][N]): int32 products
-// accumulated by the matrix core over all of K, no group scales, no row-sum
-// MFMAs; otherwise the group-128 FP8 form.
+// kForm: kFormG128, the group-128 FP8 form; kFormChannel, the per-channel
+// variant (INT8 activations with row code sums a_rowsum, one scale per weight
+// row in w_scale [E][N]): int32 products accumulated by the matrix core over
+// all of K, no group scales, no row-sum MFMAs; kFormMx, MXFP4 weights (w_scale
+// holds the E8M0 bytes).
 // kSwiglu: the fused gate/up form: tile column v multiplies weight row
 // gate_up_row(v), so a wave's B blocks 2 jp and 2 jp + 1 are the gate and the
 // up rows of the same 16 output columns; the epilogue writes
 // act = silu(gate) * up [M][N/2] and the tile's max |act| of each row to
 // pmax[p][s] for the slots s of 64 output columns the tile covers.
-template <bool kInt8, bool kSwiglu>
+template <int kForm, bool kSwiglu>
 __global__ __launch_bounds__(kThreads, 1) void gg_tiled_kernel(const uint8_t* __restrict__ a,
                                                                const float* __restrict__ a_scale,
                                                                const int32_t* __restrict__ a_rowsum,
@@ -135,8 +145,10 @@ __global__ __launch_bounds__(kThreads, 1) void gg_tiled_kernel(const uint8_t* __
                                                                const float* __restrict__ w_scale, int64_t N,
                                                                int64_t K, float* __restrict__ out,
                                                                float* __restrict__ pmax) {
+  constexpr bool kInt8 = kForm == kFormChannel;
+  constexpr bool kMx = kForm == kFormMx;
   __shared__ RingSlot ring0, ring1, ring2;
-  __shared__ __attribute__((aligned(16))) float sc0[kWideCols], sc1[kWideCols], sc2[kWideCols];   // group scales
+  __shared__ __attribute__((aligned(16))) float sc0[kWideCols], sc1[kWideCols], sc2[kWideCols];   // group scales (MX: E8M0 words)
   __shared__ __attribute__((aligned(16))) float bias_sm[2][kTM];   // -2^-6 * group code sums: [group parity][row]
   __shared__ __attribute__((aligned(16))) float ascale_sm[kTM];    // token scales of the tile's rows
   __shared__ int tile_start[kMaxExperts + 1];                      // first tile index of each expert
@@ -187,10 +199,13 @@ __global__ __launch_bounds__(kThreads, 1) void gg_tiled_kernel(const uint8_t* __
   const int total = tile_start[E];
 
   // lane-constant parts of the swizzled LDS addresses (the row or column
-  // bases of the blocks are multiples of 16, so the swizzle depends on lr only)
+  // bases of the blocks are multiples of 16, so the swizzle depends on lr only);
+  // the A operand's two 16-byte chunks: 2 lq and 2 lq + 1 (K bytes 32 lq .. +31),
+  // in the MX form lq and lq + 4
   const int fa = (lr >> 1) & 7;                   // activation swizzle of row 16 b + lr
-  const uint32_t a_rd0 = (uint32_t)lr * kGroup + 16u * (uint32_t)((2 * lq) ^ fa);       // K bytes 32 lq .. +15
-  const uint32_t a_rd1 = (uint32_t)lr * kGroup + 16u * (uint32_t)((2 * lq + 1) ^ fa);   // K bytes 32 lq + 16 .. +31
+  const int ca0 = kMx ? lq : 2 * lq, ca1 = kMx ? lq + 4 : 2 * lq + 1;
+  const uint32_t a_rd0 = (uint32_t)lr * kGroup + 16u * (uint32_t)(ca0 ^ fa);
+  const uint32_t a_rd1 = (uint32_t)lr * kGroup + 16u * (uint32_t)(ca1 ^ fa);
   const uint32_t w_rd_lane = (uint32_t)lr * 64u + 16u * (uint32_t)(lq ^ ((lr >> 2) & 3));
 
   // Tile t runs on the XCD and in the round that keep data sharing local:
@@ -330,9 +345,14 @@ __global__ __launch_bounds__(kThreads, 1) void gg_tiled_kernel(const uint8_t* __
         constexpr int S = decltype(S_)::value;
         if (g >= G) return;
         const bool more = g + 2 < G;
-        // scales of group g
+        // scales of group g (MX: the E8M0 byte of the lane's K quarter, in byte 0)
         float s[kBBlocks];
-        if constexpr (!kInt8) {
+        int sb[kBBlocks];
+        if constexpr (kMx) {
+#pragma unroll
+          for (int j = 0; j < kBBlocks; ++j)
+            sb[j] = (int)(__float_as_uint(slot<S>(sc0, sc1, sc2)[64 * cg + 16 * j + lr]) >> (8 * lq));
+        } else if constexpr (!kInt8) {
 #pragma unroll
           for (int j = 0; j < kBBlocks; ++j) s[j] = slot<S>(sc0, sc1, sc2)[64 * cg + 16 * j + lr];
         }
@@ -343,13 +363,17 @@ __global__ __launch_bounds__(kThreads, 1) void gg_tiled_kernel(const uint8_t* __
         auto mid = [&]() {
           if (more) wait_last_stage();
           else __builtin_amdgcn_s_waitcnt(0x0F70);              // vmcnt(0)
-          if (!kInt8 && g + 1 < G) row_sums(std::integral_constant<int, (S + 1) % 3>{}, g + 1);
+          if (!kInt8 && !kMx && g + 1 < G) row_sums(std::integral_constant<int, (S + 1) % 3>{}, g + 1);
         };
         // the products of this group: kNB A blocks x kBBlocks B blocks
         auto compute = [&]() {
           v8i b[kBBlocks];
+          i32x4 bx[kBBlocks];   // MX: the packed bytes are the operand
 #pragma unroll
-          for (int j = 0; j < kBBlocks; ++j) b[j] = nibbles_to_fp8(lds_load<i32x4>(&sl.b[w_rd + j * 16 * 64]));
+          for (int j = 0; j < kBBlocks; ++j) {
+            if constexpr (kMx) bx[j] = lds_load<i32x4>(&sl.b[w_rd + j * 16 * 64]);
+            else b[j] = nibbles_to_fp8(lds_load<i32x4>(&sl.b[w_rd + j * 16 * 64]));
+          }
           const float* bsum = &bias_sm[g & 1][16 * rg + 4 * lq];
           // operands of A block i: two 16-byte halves of the lane's 32 K bytes
           auto load_a = [&](int i) {
@@ -362,7 +386,7 @@ __global__ __launch_bounds__(kThreads, 1) void gg_tiled_kernel(const uint8_t* __
           v4f bias[2];
           v4f c[kBBlocks];   // products of the block in flight; each is scaled into acc just before it is reused
           av[0] = load_a(0);
-          if constexpr (!kInt8) bias[0] = lds_load<v4f>(bsum);
+          if constexpr (!kInt8 && !kMx) bias[0] = lds_load<v4f>(bsum);
           auto scale_into = [&](auto I_, int j) {   // acc[i] += s * D for B block j
             constexpr int i = decltype(I_)::value;
 #pragma unroll
@@ -378,11 +402,13 @@ __global__ __launch_bounds__(kThreads, 1) void gg_tiled_kernel(const uint8_t* __
             if constexpr (i < kNB) {
               if constexpr (i + 1 < kNB) {
                 av[(i + 1) & 1] = load_a(i + 1);
-                if constexpr (!kInt8) bias[(i + 1) & 1] = lds_load<v4f>(bsum + kBlockStride * (i + 1));
+                if constexpr (!kInt8 && !kMx) bias[(i + 1) & 1] = lds_load<v4f>(bsum + kBlockStride * (i + 1));
               }
 #pragma unroll
               for (int j = 0; j < kBBlocks; ++j) {
-                if constexpr (kInt8) {
+                if constexpr (kMx) {
+                  acc[i][j] = mfma_mx(av[i & 1], bx[j], acc[i][j], sb[j]);
+                } else if constexpr (kInt8) {
                   const v8i x = av[i & 1];
                   const i32x4 a_lo = {x[0], x[1], x[2], x[3]}, a_hi = {x[4], x[5], x[6], x[7]};
                   const i32x4 b_lo = {b[j][0], b[j][1], b[j][2], b[j][3]}, b_hi = {b[j][4], b[j][5], b[j][6], b[j][7]};
@@ -393,7 +419,7 @@ __global__ __launch_bounds__(kThreads, 1) void gg_tiled_kernel(const uint8_t* __
                   c[j] = mfma16x16x128(av[i & 1], b[j], bias[i & 1]);
                 }
               }
-            } else if constexpr (!kInt8 && i == kNB && i >= 1) {
+            } else if constexpr (!kInt8 && !kMx && i == kNB && i >= 1) {
 #pragma unroll
               for (int j = 0; j < kBBlocks; ++j) scale_into(std::integral_constant<int, i - 1>{}, j);
             }
@@ -424,7 +450,7 @@ __global__ __launch_bounds__(kThreads, 1) void gg_tiled_kernel(const uint8_t* __
       } else {
         __builtin_amdgcn_s_waitcnt(0x0F70);
       }
-      if (!kInt8) row_sums(std::integral_constant<int, 0>{}, 0);
+      if (!kInt8 && !kMx) row_sums(std::integral_constant<int, 0>{}, 0);
       // the fused form's row maxima of this tile start at 0 (the previous use of this
       // parity's array, two tiles back, ended before the last tile's first barrier)
       if (kSwiglu && tid < kTM) rmax_sm[tpar][tid] = 0u;
@@ -470,6 +496,7 @@ __global__ __launch_bounds__(kThreads, 1) void gg_tiled_kernel(const uint8_t* __
             // the GEMM output of B block j and row v (the value the unfused form stores)
             auto h = [&](int j, int v) {
               if constexpr (kInt8) return (float)(acc[i][j][v] - 8 * rs4[v]) * sc4[v] * ws[j];
+              else if constexpr (kMx) return acc[i][j][v] * sc4[v];
               else return acc[i][j][v] * (sc4[v] * kUnitScale);
             };
 #pragma unroll
@@ -556,11 +583,13 @@ hipError_t launch_gg_tiled(const GemmArgs& g, hipStream_t stream) {
                        g.offsets, g.E, g.w_packed, g.w_scale, g.N, g.K, g.out, g.pmax);
   };
   if (g.pmax) {
-    if (g.a_rowsum) go(gg_tiled_kernel<true, true>);
-    else go(gg_tiled_kernel<false, true>);
+    if (g.a_rowsum) go(gg_tiled_kernel<kFormChannel, true>);
+    else if (g.mx) go(gg_tiled_kernel<kFormMx, true>);
+    else go(gg_tiled_kernel<kFormG128, true>);
   } else {
-    if (g.a_rowsum) go(gg_tiled_kernel<true, false>);
-    else go(gg_tiled_kernel<false, false>);
+    if (g.a_rowsum) go(gg_tiled_kernel<kFormChannel, false>);
+    else if (g.mx) go(gg_tiled_kernel<kFormMx, false>);
+    else go(gg_tiled_kernel<kFormG128, false>);
   }
   return hipGetLastError();
 }

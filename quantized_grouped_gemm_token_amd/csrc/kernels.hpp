@@ -8,8 +8,8 @@
 namespace w4a8 {
 
 // One grouped GEMM.  a_rowsum == nullptr: the group-128 FP8 form (w_scale
-// [E][N][K/128]); otherwise the per-channel INT8 form (INT8 activations with
-// their row code sums, w_scale [E][N]).
+// [E][N][K/128]), or with mx set the MXFP4 form; otherwise the per-channel
+// INT8 form (INT8 activations with their row code sums, w_scale [E][N]).
 struct GemmArgs {
   const uint8_t* a;
   const float* a_scale;
@@ -28,6 +28,10 @@ struct GemmArgs {
   // pmax [M_total][N/128] gets row maxima of |act| (each entry over some of
   // the row's columns; their max is the row's)
   float* pmax = nullptr;
+  // MXFP4 weights: w_packed holds E2M1 codes [E][N][K/2] (element k in the low
+  // nibble of byte k/2 when k is even) and w_scale the E8M0 block scales
+  // [E][N][K/32] as bytes, read one 4-byte word per 128-wide K group
+  bool mx = false;
 };
 
 hipError_t launch_quant_act(const uint16_t* x, int64_t T, int64_t H, int64_t ld, uint8_t* q, float* s,
@@ -48,6 +52,8 @@ hipError_t launch_wquant_channel(const float* w, int64_t rows, int64_t K, int32_
                                  hipStream_t stream);
 hipError_t launch_wquant(const float* w, int64_t rows, int64_t K, int mse_clip, int32_t* packed, float* scales,
                          hipStream_t stream);
+hipError_t launch_wquant_mxfp4(const float* w, int64_t rows, int64_t K, uint8_t* packed, uint8_t* scales,
+                               hipStream_t stream);
 hipError_t launch_requant(const float* act, const float* pmax, int64_t M, int64_t I, uint8_t* q, float* s,
                           hipStream_t stream);
 hipError_t launch_requant_i8(const float* act, const float* pmax, int64_t M, int64_t I, int8_t* q, float* s,

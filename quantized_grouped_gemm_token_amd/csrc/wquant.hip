@@ -113,6 +113,59 @@ __global__ __launch_bounds__(256) void wquant_channel_kernel(const float* __rest
   }
 }
 
+// MXFP4 (Open Compute Project microscaling format), the 4-bit alternative the
+// "GLM-5.3-W4A8" card compares against in section 量化方式 (groups of 32):
+// E2M1 elements with one E8M0 scale per 32 consecutive weights along K.
+// Per block:  amax = max |w| (1 if the block is all zero);
+//             X = floor(log2 amax) - 2 (2 = the exponent of E2M1's top
+//             binade), clamped to [-127, 127]; scale byte X + 127;
+//             code = E2M1 of w * 2^-X: nearest of 0, .5, 1, 1.5, 2, 3, 4, 6,
+//             ties to the code with mantissa bit 0, saturating at 6, with the
+//             sign bit of w (so -0 and tiny negatives keep it).
+// w * 2^-X is exact (a power-of-two scaling; a result too small to stay
+// normal lies far below the first rounding threshold, 0.25).
+// Eight lanes per block: each holds 4 consecutive weights (one 16-byte load)
+// and writes their 2 packed bytes (element k in the low nibble of byte k / 2
+// when k is even); the block's max comes from DPP moves inside the 8 lanes.
+__device__ __forceinline__ uint32_t e2m1_code(float w, float x) {
+  const float a = fabsf(x);
+  const uint32_t c = (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) + (uint32_t)(a > 1.25f) +
+                     (uint32_t)(a >= 1.75f) + (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) + (uint32_t)(a > 5.0f);
+  return c | ((__float_as_uint(w) >> 28) & 8u);
+}
+
+__global__ __launch_bounds__(256) void wquant_mxfp4_kernel(const float* __restrict__ w, int64_t pieces,
+                                                           uint16_t* __restrict__ packed,
+                                                           uint8_t* __restrict__ scales) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;   // a multiple of 8: a block's lanes move together
+  for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < pieces; t += stride) {
+    const f32x4 v = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(w) + t);
+    float m = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
+    m = fmaxf(m, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(m), 0xB1, 0xf, 0xf, true)));    // quad [1,0,3,2]
+    m = fmaxf(m, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(m), 0x4E, 0xf, 0xf, true)));    // quad [2,3,0,1]
+    m = fmaxf(m, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(m), 0x141, 0xf, 0xf, true)));   // half-row mirror
+    if (m == 0.0f) m = 1.0f;
+    int e;
+    (void)frexpf(m, &e);                                    // m = f 2^e, f in [0.5, 1): floor(log2 m) = e - 1
+    const int X = min(max(e - 3, -127), 127);
+    uint32_t c[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) c[i] = e2m1_code(v[i], ldexpf(v[i], -X));
+    packed[t] = (uint16_t)(c[0] | (c[1] << 4) | (c[2] << 8) | (c[3] << 12));
+    if ((t & 7) == 0) scales[t >> 3] = (uint8_t)(X + 127);
+  }
+}
+
+hipError_t launch_wquant_mxfp4(const float* w, int64_t rows, int64_t K, uint8_t* packed, uint8_t* scales,
+                               hipStream_t stream) {
+  const int64_t pieces = rows * K / 4;
+  if (pieces == 0) return hipSuccess;
+  const int64_t blocks = std::min<int64_t>((pieces + 255) / 256, 8192);
+  hipLaunchKernelGGL(wquant_mxfp4_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, w, pieces,
+                     reinterpret_cast<uint16_t*>(packed), scales);
+  return hipGetLastError();
+}
+
 hipError_t launch_wquant_channel(const float* w, int64_t rows, int64_t K, int32_t* packed, float* scales,
                                  hipStream_t stream) {
   if (rows == 0) return hipSuccess;

@@ -11,7 +11,9 @@ the intermediate bytes.
 Expert weights stay resident on the GPU in the packed format (int32
 [E][N][K/8] words of uint4b8 nibbles and fp32 [E][N][K/128] group scales).
 W4A8MoEChannel is the per-channel INT4 x per-token INT8 variant: fp32 [E][N]
-scales, INT8 activations.
+scales, INT8 activations.  W4A8MoEMxfp4 holds MXFP4 group-32 experts (E2M1
+codes uint8 [E][N][K/2], E8M0 scales uint8 [E][N][K/32]) and uses the same
+FP8 activations.
 Intermediate buffers are allocated once per token count and reused, so a
 forward pass enqueues kernels only: no allocation, no host synchronisation.
 """
@@ -23,12 +25,17 @@ from . import ops
 
 
 class W4A8MoE:
+    K_PER_ITEM = 8                                        # K elements per item of a weight row (int32 words)
+    GEMM = staticmethod(ops.w4a8_moe_grouped_gemm)
+    GEMM_SWIGLU = staticmethod(ops.w4a8_moe_grouped_gemm_swiglu)
+
     def __init__(self, w13: torch.Tensor, s13: torch.Tensor, w2: torch.Tensor, s2: torch.Tensor, k: int,
                  renormalize: bool = True, fused: bool = True):
         E, N13, KW13 = w13.shape
         E2, H, KW2 = w2.shape
-        if E2 != E or N13 % 2 or KW13 * 8 != H or KW2 * 8 * 2 != N13:
-            raise ValueError("w13 must be [E, 2I, H/8] and w2 [E, H, I/8]")
+        c = self.K_PER_ITEM
+        if E2 != E or N13 % 2 or KW13 * c != H or KW2 * c * 2 != N13:
+            raise ValueError(f"w13 must be [E, 2I, H/{c}] and w2 [E, H, I/{c}]")
         self.w13, self.s13, self.w2, self.s2 = w13, s13, w2, s2
         self.E, self.H, self.I, self.k = E, H, N13 // 2, k
         self.renormalize = renormalize
@@ -83,15 +90,14 @@ class W4A8MoE:
         step("permute", ops.w4a8_moe_permute, b["ids"], self.E, b["offsets"], b["row_token"], b["inv_pos"],
              b["workspace"])
         if self.fused:
-            step("gemm_gate_up", ops.w4a8_moe_grouped_gemm_swiglu, b["qx"], b["sx"], b["row_token"], b["offsets"],
+            step("gemm_gate_up", self.GEMM_SWIGLU, b["qx"], b["sx"], b["row_token"], b["offsets"],
                  self.w13, self.s13, R, b["act"], b["pmax"], algo)
             step("swiglu", ops.w4a8_moe_requant, b["act"], b["pmax"], b["qa"], b["sa"])
         else:
-            step("gemm_gate_up", ops.w4a8_moe_grouped_gemm, b["qx"], b["sx"], b["row_token"], b["offsets"],
+            step("gemm_gate_up", self.GEMM, b["qx"], b["sx"], b["row_token"], b["offsets"],
                  self.w13, self.s13, R, b["h"], algo)
             step("swiglu", ops.w4a8_moe_swiglu, b["h"], b["qa"], b["sa"])
-        step("gemm_down", ops.w4a8_moe_grouped_gemm, b["qa"], b["sa"], None, b["offsets"], self.w2, self.s2, R,
-             b["o"], algo)
+        step("gemm_down", self.GEMM, b["qa"], b["sa"], None, b["offsets"], self.w2, self.s2, R, b["o"], algo)
         return step("unpermute", ops.w4a8_moe_unpermute, b["o"], b["inv_pos"], b["w"], y, y_dtype)
 
     __call__ = forward
@@ -146,3 +152,12 @@ class W4A8MoEChannel(W4A8MoE):
         return step("unpermute", ops.w4a8_moe_unpermute, b["o"], b["inv_pos"], b["w"], y, y_dtype)
 
     __call__ = forward
+
+
+class W4A8MoEMxfp4(W4A8MoE):
+    """MXFP4 group-32 experts (w13 uint8 [E, 2I, H/2], s13 uint8 [E, 2I, H/32],
+    w2 uint8 [E, H, I/2], s2 uint8 [E, H, I/32]) with the FP8 activations of
+    the group-128 form: only the two GEMMs differ."""
+    K_PER_ITEM = 2                                        # two E2M1 codes per byte
+    GEMM = staticmethod(ops.w4a8_moe_grouped_gemm_mxfp4)
+    GEMM_SWIGLU = staticmethod(ops.w4a8_moe_grouped_gemm_swiglu_mxfp4)

@@ -51,6 +51,11 @@ _SIGNATURES = {
                                                        _i64, _c_p, _c_p, _i32, _c_p]),
     "w4a8_moe_requant": (ctypes.c_int, [_c_p, _c_p, _i64, _i64, _c_p, _c_p, _c_p]),
     "w4a8_moe_requant_i8": (ctypes.c_int, [_c_p, _c_p, _i64, _i64, _c_p, _c_p, _c_p, _c_p]),
+    "w4a8_moe_quantize_weights_mxfp4": (ctypes.c_int, [_c_p, _i64, _i64, _c_p, _c_p, _c_p]),
+    "w4a8_moe_grouped_gemm_mxfp4": (ctypes.c_int, [_c_p, _c_p, _c_p, _i64, _c_p, _i32, _c_p, _c_p, _i64, _i64,
+                                                   _c_p, _i32, _c_p]),
+    "w4a8_moe_grouped_gemm_swiglu_mxfp4": (ctypes.c_int, [_c_p, _c_p, _c_p, _i64, _c_p, _i32, _c_p, _c_p, _i64,
+                                                          _i64, _c_p, _c_p, _i32, _c_p]),
     "w4a8_moe_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "w4a8_moe_last_error": (ctypes.c_char_p, []),
     "w4a8_moe_device_supported": (ctypes.c_int, []),
@@ -482,3 +487,83 @@ def w4a8_moe_requant_i8(act: torch.Tensor, act_pmax: torch.Tensor, qa=None, sa=N
     _check("w4a8_moe_requant_i8", lib().w4a8_moe_requant_i8(_p(act), _p(act_pmax), M, I, _p(qa), _p(sa),
                                                             _p(rowsum), _stream(dev)))
     return qa, sa, rowsum
+
+
+# ---- MXFP4 group-32 weights x per-token FP8 activations ---------------------
+def w4a8_moe_quantize_weights_mxfp4(w: torch.Tensor, w_packed=None, w_scale=None):
+    """fp32 [..., K] -> (E2M1 codes uint8 [..., K/2], E8M0 block scales uint8 [..., K/32]).
+
+    Every leading dimension is flattened into rows (experts x output channels)."""
+    if not isinstance(w, torch.Tensor) or w.dim() < 1:
+        raise TypeError("w must be a torch.Tensor with a K dimension")
+    _need(w, "w", torch.float32, w.dim())
+    K = w.shape[-1]
+    lead = tuple(w.shape[:-1])
+    rows = 1
+    for d in lead:
+        rows *= int(d)
+    dev = w.device
+    if K % 32:
+        raise ValueError("K must be a multiple of 32")
+    w_packed = torch.empty(lead + (K // 2,), dtype=torch.uint8, device=dev) if w_packed is None else w_packed
+    w_scale = torch.empty(lead + (K // 32,), dtype=torch.uint8, device=dev) if w_scale is None else w_scale
+    _need(w_packed, "w_packed", torch.uint8, len(lead) + 1, dev)
+    _need(w_scale, "w_scale", torch.uint8, len(lead) + 1, dev)
+    if tuple(w_packed.shape) != lead + (K // 2,) or tuple(w_scale.shape) != lead + (K // 32,):
+        raise ValueError("w_packed must be [..., K/2] and w_scale [..., K/32]")
+    _check("w4a8_moe_quantize_weights_mxfp4",
+           lib().w4a8_moe_quantize_weights_mxfp4(_p(w), rows, K, _p(w_packed), _p(w_scale), _stream(dev)))
+    return w_packed, w_scale
+
+
+def _check_mx_weights(a, a_scale, a_rows, offsets, w, s, M_total, names):
+    _need(a, "a", torch.uint8, 2)
+    dev = a.device
+    _need(a_scale, "a_scale", torch.float32, 1, dev)
+    if a_rows is not None:
+        _need(a_rows, "a_rows", torch.int32, 1, dev)
+        if a_rows.numel() < M_total:
+            raise ValueError("a_rows must hold M_total entries")
+    _need(offsets, "offsets", torch.int32, 1, dev)
+    _need(w, names[0], torch.uint8, 3, dev)
+    _need(s, names[1], torch.uint8, 3, dev)
+    E, N, KB = w.shape
+    K = a.shape[1]
+    if KB * 2 != K or tuple(s.shape) != (E, N, K // 32) or offsets.numel() != E + 1:
+        raise ValueError(f"{names[0]} [E,N,K/2], {names[1]} [E,N,K/32] and offsets [E+1] must match a [*,K]")
+    if a_scale.numel() != a.shape[0]:
+        raise ValueError("a_scale must have one entry per row of a")
+    return dev, E, N, K
+
+
+def w4a8_moe_grouped_gemm_mxfp4(a: torch.Tensor, a_scale: torch.Tensor, a_rows: torch.Tensor | None,
+                                offsets: torch.Tensor, w_packed: torch.Tensor, w_scale: torch.Tensor, M_total: int,
+                                out: torch.Tensor | None = None, algo: int = W4A8_GG_AUTO):
+    """Grouped FP8 x MXFP4 GEMM -> out fp32 [M_total, N] (rows of expert e: offsets[e]..offsets[e+1])."""
+    dev, E, N, K = _check_mx_weights(a, a_scale, a_rows, offsets, w_packed, w_scale, M_total,
+                                     ("w_packed", "w_scale"))
+    out = torch.empty((M_total, N), dtype=torch.float32, device=dev) if out is None else out
+    _need(out, "out", torch.float32, 2, dev)
+    if tuple(out.shape) != (M_total, N):
+        raise ValueError("out must be [M_total, N]")
+    _check("w4a8_moe_grouped_gemm_mxfp4",
+           lib().w4a8_moe_grouped_gemm_mxfp4(_p(a), _p(a_scale), _p(a_rows), M_total, _p(offsets), E,
+                                             _p(w_packed), _p(w_scale), N, K, _p(out), algo, _stream(dev)))
+    return out
+
+
+def w4a8_moe_grouped_gemm_swiglu_mxfp4(a: torch.Tensor, a_scale: torch.Tensor, a_rows: torch.Tensor | None,
+                                       offsets: torch.Tensor, w13: torch.Tensor, s13: torch.Tensor, M_total: int,
+                                       act: torch.Tensor | None = None, act_pmax: torch.Tensor | None = None,
+                                       algo: int = W4A8_GG_AUTO):
+    """MXFP4 gate/up GEMM with SwiGLU in its epilogue -> (act fp32 [M_total, I], partial row maxima [M_total, I/64])."""
+    dev, E, N2, K = _check_mx_weights(a, a_scale, a_rows, offsets, w13, s13, M_total, ("w13", "s13"))
+    if N2 % 2:
+        raise ValueError("w13 must have 2I rows")
+    I = N2 // 2
+    act, act_pmax = _act_out(M_total, I, dev, act, act_pmax)
+    _check("w4a8_moe_grouped_gemm_swiglu_mxfp4",
+           lib().w4a8_moe_grouped_gemm_swiglu_mxfp4(_p(a), _p(a_scale), _p(a_rows), M_total, _p(offsets), E,
+                                                    _p(w13), _p(s13), I, K, _p(act), _p(act_pmax), algo,
+                                                    _stream(dev)))
+    return act, act_pmax

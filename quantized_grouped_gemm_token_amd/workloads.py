@@ -22,7 +22,10 @@ Streams: numpy PCG64 seeded by SeedSequence(1000 + index), spawned in the
 fixed order W13, S13, W2, S2, x, outlier channels, logits, expert ranking;
 a ninth child draws the per-channel scales of the per-channel INT4 x INT8
 variant (lognormal(-4, 0.5), fp32 [E, 2I] and [E, H]), which reuses the
-same packed words.
+same packed words; a tenth draws the MXFP4 experts: uniform random bytes
+(every E2M1 code equally likely, as the INT4 nibbles are) and E8M0 scale bytes
+127 + rint(log2 s), s ~ lognormal(-4, 0.5) (the group-128 scale law, rounded
+to a power of two).
 """
 from __future__ import annotations
 
@@ -133,3 +136,19 @@ def channel_scales(wl: Workload) -> tuple[np.ndarray, np.ndarray]:
     s13 = g.lognormal(mean=-4.0, sigma=0.5, size=(sh.E, 2 * sh.I)).astype(np.float32)
     s2 = g.lognormal(mean=-4.0, sigma=0.5, size=(sh.E, sh.H)).astype(np.float32)
     return s13, s2
+
+
+def mxfp4_weights(wl: Workload) -> tuple[np.ndarray, np.ndarray, np.ndarray, np.ndarray]:
+    """MXFP4 experts of the workload's shape: w13 uint8 [E, 2I, H/2], s13 uint8 [E, 2I, H/32],
+    w2 uint8 [E, H, I/2], s2 uint8 [E, H, I/32]."""
+    sh = wl.shape
+    g = np.random.Generator(np.random.PCG64(np.random.SeedSequence(wl.seed).spawn(10)[9]))
+
+    def scales(shape):
+        return (127 + np.rint(np.log2(g.lognormal(mean=-4.0, sigma=0.5, size=shape)))).astype(np.uint8)
+
+    w13 = g.integers(0, 256, size=(sh.E, 2 * sh.I, sh.H // 2), dtype=np.uint8)
+    s13 = scales((sh.E, 2 * sh.I, sh.H // 32))
+    w2 = g.integers(0, 256, size=(sh.E, sh.H, sh.I // 2), dtype=np.uint8)
+    s2 = scales((sh.E, sh.H, sh.I // 32))
+    return w13, s13, w2, s2
