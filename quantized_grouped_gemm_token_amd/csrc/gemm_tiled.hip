@@ -103,12 +103,24 @@ __device__ __forceinline__ void barrier_loads_in_flight() {
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
-// direct loads into LDS: lane l's bytes (at rsrc + voff + soff) go to lds + size * l
+// LDS byte address of a pointer into a __shared__ variable
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+// Direct loads into LDS: lane l's bytes (at rsrc + voff + soff) go to lds + size * l
+// (M0 holds the wave's LDS base).  They are issued from inline assembly, which the
+// compiler does not see as writing LDS: given the builtin, its wait insertion cannot
+// always tell the ring slot being filled from the one being read, and adds a full
+// vmcnt(0) before the group's LDS reads, which drains the prefetch.  The kernel orders
+// these loads itself: its own vmcnt waits, then the barrier, before any wave reads
+// the slot.  They write no register, so nothing the compiler allocates is in flight.
 __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, void* lds) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, voff, soff, 0, 0);
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+               :: "s"(lds_addr(lds)), "v"(voff), "s"(r), "s"(soff) : "memory", "m0");
 }
 __device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, void* lds) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 4, voff, soff, 0, 0);
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, %3 offen lds"
+               :: "s"(lds_addr(lds)), "v"(voff), "s"(r), "s"(soff) : "memory", "m0");
 }
 
 template <typename T>
@@ -442,6 +454,14 @@ __global__ __launch_bounds__(kThreads, 1) void gg_tiled_kernel(const uint8_t* __
         barrier_loads_in_flight();
       };
 
+      // byte offsets of the token scales (and row code sums) of the tile's rows, read
+      // here: a wait for them after the stages below would wait for those as well
+      uint32_t asrc = 0;
+      if (wave < kRows / 64) {
+        const int p = r0 + min(64 * wave + lane, mlen - 1);
+        asrc = (uint32_t)(a_rows ? a_rows[p] : p) * 4u;
+      }
+      asm volatile("" :: "v"(asrc));
       // prologue: groups 0 and 1 in flight, this wave's rows of group 0 landed, their sums published
       stage(std::integral_constant<int, 0>{}, 0);
       if (G > 1) {
@@ -457,13 +477,11 @@ __global__ __launch_bounds__(kThreads, 1) void gg_tiled_kernel(const uint8_t* __
       __builtin_amdgcn_s_waitcnt(0xC07F);
       barrier_loads_in_flight();
       // the token scales (and in the INT8 form the row code sums) of the tile's
-      // rows, read in the epilogue; every wave is past the previous epilogue
+      // rows, read in the epilogue (every wave is past the previous epilogue); the
+      // K loop's last step waits for every load, so they have landed by then
       if (wave < kRows / 64) {
-        const int r = 64 * wave + lane;
-        const int p = r0 + min(r, mlen - 1);
-        const uint32_t src = (uint32_t)(a_rows ? a_rows[p] : p) * 4u;
-        dma4(buffer_rsrc(a_scale, 0xffffffffu), src, 0, &ascale_sm[64 * wave]);
-        if constexpr (kInt8) dma4(buffer_rsrc(a_rowsum, 0xffffffffu), src, 0, &rowsum_sm[64 * wave]);
+        dma4(buffer_rsrc(a_scale, 0xffffffffu), asrc, 0, &ascale_sm[64 * wave]);
+        if constexpr (kInt8) dma4(buffer_rsrc(a_rowsum, 0xffffffffu), asrc, 0, &rowsum_sm[64 * wave]);
       }
 
       for (int g = 0; g < G; g += 3) {
