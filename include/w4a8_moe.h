@@ -317,9 +317,16 @@ int w4a8_moe_requant_i8(const float* act, const float* act_pmax, int64_t M, int6
  * The format is the Open Compute Project microscaling one: E2M1 elements
  * (magnitudes 0, .5, 1, 1.5, 2, 3, 4, 6; bit 3 the sign) sharing one E8M0
  * scale (byte b = 2^(b - 127)) per 32 consecutive weights along K.
+ * Row-major storage (what the quantizer writes):
  *   Weights : u8 [E][N][K/2], element k of a row in the low nibble of byte
  *             k/2 when k is even, the high nibble when odd.
  *   Scales  : u8 [E][N][K/32], the E8M0 byte of elements 32j .. 32j+31.
+ * GEMM storage (what w4a8_moe_prepack_mxfp4 writes and the GEMMs read), the
+ * same bytes permuted, G = K/128:
+ *   Weights : u8 [E][N/16][G][16][64]: the 64 bytes of row n and K group g
+ *             (row-major bytes 64g .. 64g+63) at ((e (N/16) + n/16) G + g) 1024 + 64 (n % 16).
+ *   Scales  : u8 [E][G][N][4]: the 4 bytes of row n and group g (row-major
+ *             bytes 4g .. 4g+3) at ((e G + g) N + n) 4.
  */
 
 /*
@@ -335,11 +342,23 @@ int w4a8_moe_quantize_weights_mxfp4(const float* w, int64_t rows, int64_t K, uin
                                     void* stream);
 
 /*
+ * Offline layout step, MXFP4: row-major weights and scales -> GEMM storage
+ * (a permutation of bytes; see above).  Reads w_packed u8 [E][N][K/2] and
+ * w_scale u8 [E][N][K/32]; writes w_blk u8 [E][N/16][K/128][16][64] and
+ * s_blk u8 [E][K/128][N][4] (no overlap with the inputs).
+ *   Rules : 0 <= E <= 1024, N % 16 == 0, K % 128 == 0; weights 16-byte
+ *   aligned, scales 4-byte aligned.
+ */
+int w4a8_moe_prepack_mxfp4(const uint8_t* w_packed, const uint8_t* w_scale, int32_t E, int64_t N, int64_t K,
+                           uint8_t* w_blk, uint8_t* s_blk, void* stream);
+
+/*
  * Step 4, MXFP4 weights:
  *   out[p, n] = a_scale[r] * sum_k E4M3(a[r, k]) * E2M1(w[e, n, k]) * 2^(w_scale[e, n, k/32] - 127)
  *   (r = a_rows ? a_rows[p] : p; exact products, fp32 sums).
  *   a, a_scale, a_rows, offsets, out, algo : as in w4a8_moe_grouped_gemm_algo.
- *   w_packed : u8 [E][N][K/2], 16-byte aligned.  w_scale : u8 [E][N][K/32], 4-byte aligned.
+ *   w_packed : GEMM storage u8 [E][N/16][K/128][16][64], 16-byte aligned.
+ *   w_scale : GEMM storage u8 [E][K/128][N][4], 4-byte aligned.
  *   Rules : N % 64 == 0, K % 128 == 0, 1 <= E <= 1024; errors as in w4a8_moe_grouped_gemm_algo.
  */
 int w4a8_moe_grouped_gemm_mxfp4(const uint8_t* a, const float* a_scale, const int32_t* a_rows, int64_t M_total,
@@ -348,8 +367,9 @@ int w4a8_moe_grouped_gemm_mxfp4(const uint8_t* a, const float* a_scale, const in
 
 /*
  * Steps 4 + 5a, MXFP4 weights: as w4a8_moe_grouped_gemm_swiglu with the
- * products of w4a8_moe_grouped_gemm_mxfp4 (w13 : u8 [E][2I][K/2], 16-byte
- * aligned; s13 : u8 [E][2I][K/32], 4-byte aligned).  Follow with w4a8_moe_requant.
+ * products of w4a8_moe_grouped_gemm_mxfp4 (w13 : GEMM storage of the [E][2I]
+ * rows, 16-byte aligned; s13 : GEMM storage of their scales, 4-byte aligned).
+ * Follow with w4a8_moe_requant.
  */
 int w4a8_moe_grouped_gemm_swiglu_mxfp4(const uint8_t* a, const float* a_scale, const int32_t* a_rows,
                                        int64_t M_total, const int32_t* offsets, int32_t E, const uint8_t* w13,

@@ -22,11 +22,12 @@
 // buffered, with one barrier per chunk.  Group scales are read as 16-byte
 // vectors (4 groups) when the group count allows.
 //
-// MXFP4 weights (group 32) have the same 64 packed bytes per row and group,
-// so the same loads and selects give each lane the 16 bytes of its K quarter,
-// which are the B operand as they are; the group's word of E8M0 block scales
-// is read where the fp32 group scale is, and the lane passes its quarter's
-// byte to the matrix core, which applies it: the products accumulate straight
+// MXFP4 weights (group 32) come in the GEMM layout, where the 64 packed bytes
+// of one group of 16 rows are one contiguous 1 KB piece: one 16-byte load per
+// lane and group reads a whole piece, and gives each lane the bytes of its row
+// and K quarter, which are the B operand as they are.  The group's word of E8M0
+// block scales (scales are group-major) is shifted so that the lane's quarter
+// is byte 0, and the matrix core applies it: the products accumulate straight
 // into acc.  The activations are staged in the K order the FP4 form of the
 // instruction reads (16-byte chunks q and q + 4 for lane group q).
 //
@@ -130,23 +131,28 @@ __device__ __forceinline__ void pair_compute(const WPair<NS>& w, const float (&s
   }
 }
 
+// MXFP4: the B operands of groups g and g + 1 (one 16-byte load each from the
+// subtile's 1 KB pieces, at the lane's row and quarter)
+template <int NS>
+__device__ __forceinline__ void w_pair_load_mx(WPair<NS>& w, const uint8_t* const (&pw)[NS], int g) {
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    w.wa[s] = __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(pw[s] + g * 1024));
+    w.wb[s] = __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(pw[s] + (g + 1) * 1024));
+  }
+}
+
 // the MXFP4 form of one group pair: sb0 / sb1 hold the lane's E8M0 scale
 // bytes (byte 0) of groups g and g + 1
 template <int NS>
 __device__ __forceinline__ void pair_compute_mx(const WPair<NS>& w, const int (&sb0)[NS], const int (&sb1)[NS],
-                                                const uint8_t* a0, const uint8_t* a1, bool lo, v4f (&acc)[NS]) {
+                                                const uint8_t* a0, const uint8_t* a1, v4f (&acc)[NS]) {
   const v8i av0 = *reinterpret_cast<const v8i*>(a0);
   const v8i av1 = *reinterpret_cast<const v8i*>(a1);
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
-    i32x4 t0, t1;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      t0[q] = lo ? w.wa[s][q] : w.wb[s][q];
-      t1[q] = row_ror8(lo ? w.wb[s][q] : w.wa[s][q]);
-    }
-    acc[s] = mfma_mx(av0, t0, acc[s], sb0[s]);
-    acc[s] = mfma_mx(av1, t1, acc[s], sb1[s]);
+    acc[s] = mfma_mx(av0, w.wa[s], acc[s], sb0[s]);
+    acc[s] = mfma_mx(av1, w.wb[s], acc[s], sb1[s]);
   }
 }
 
@@ -215,9 +221,16 @@ __global__ __launch_bounds__(kStreamThreads) void gg_stream_kernel(const uint8_t
   for (int s = 0; s < NS; ++s) {
     const int64_t nb = active ? (kSwiglu ? (int64_t)gate_up_row((int)(n0 + 16 * s), (int)(N / 2)) : n0 + 16 * s) : 0;
     const uint8_t* wbase = reinterpret_cast<const uint8_t*>(w_packed) + ((int64_t)e * N + nb) * row_bytes;
-    pa[s] = wbase + (int64_t)(col & 7) * row_bytes + (lo ? 0 : 64) + kq * 16;
-    pb[s] = wbase + (int64_t)(8 + (col & 7)) * row_bytes + (lo ? 64 : 0) + kq * 16;
-    srow[s] = w_scale + ((int64_t)e * N + nb + col) * G;
+    if constexpr (kMx) {
+      // rows nb .. nb+15 are G pieces of 1 KB from wbase; scales [E][G][N] words
+      pa[s] = wbase + col * 64 + kq * 16;
+      pb[s] = pa[s];
+      srow[s] = w_scale + (int64_t)e * N * G + nb + col;
+    } else {
+      pa[s] = wbase + (int64_t)(col & 7) * row_bytes + (lo ? 0 : 64) + kq * 16;
+      pb[s] = wbase + (int64_t)(8 + (col & 7)) * row_bytes + (lo ? 64 : 0) + kq * 16;
+      srow[s] = w_scale + ((int64_t)e * N + nb + col) * G;
+    }
   }
 
   for (int m0 = r0; m0 < r1; m0 += 16) {
@@ -280,7 +293,10 @@ __global__ __launch_bounds__(kStreamThreads) void gg_stream_kernel(const uint8_t
 #pragma unroll
         for (int s = 0; s < NS; ++s) {
           const uint32_t* srw = reinterpret_cast<const uint32_t*>(srow[s]);
-          if (vec_scales && ng == 2 * CH) {
+          if constexpr (kMx) {
+#pragma unroll
+            for (int h = 0; h < 2 * CH; ++h) sc[s][h] = h < ng ? srw[(int64_t)(g0 + h) * N] : 0u;
+          } else if (vec_scales && ng == 2 * CH) {
 #pragma unroll
             for (int v = 0; v < (2 * CH) / 4; ++v) {
               const u32x4 q4 = *reinterpret_cast<const u32x4*>(srw + g0 + 4 * v);
@@ -300,19 +316,23 @@ __global__ __launch_bounds__(kStreamThreads) void gg_stream_kernel(const uint8_t
         for (int u = 0; u < CH; u += 2) {
           if (u < npairs) {
             WPair<NS> w0, w1;
-            w_pair_load(w0, pa, pb, g0 + 2 * u);
             const bool two = u + 1 < npairs;
-            if (two) w_pair_load(w1, pa, pb, g0 + 2 * u + 2);
+            if constexpr (kMx) {
+              w_pair_load_mx(w0, pa, g0 + 2 * u);
+              if (two) w_pair_load_mx(w1, pa, g0 + 2 * u + 2);
+            } else {
+              w_pair_load(w0, pa, pb, g0 + 2 * u);
+              if (two) w_pair_load(w1, pa, pb, g0 + 2 * u + 2);
+            }
             if constexpr (kMx) {
               int s0[NS], s1[NS];
 #pragma unroll
               for (int s = 0; s < NS; ++s) { s0[s] = (int)sc[s][2 * u]; s1[s] = (int)sc[s][2 * u + 1]; }
-              pair_compute_mx(w0, s0, s1, &sm.a[buf][2 * u][lane][0], &sm.a[buf][2 * u + 1][lane][0], lo, acc);
+              pair_compute_mx(w0, s0, s1, &sm.a[buf][2 * u][lane][0], &sm.a[buf][2 * u + 1][lane][0], acc);
               if (two) {
 #pragma unroll
                 for (int s = 0; s < NS; ++s) { s0[s] = (int)sc[s][2 * u + 2]; s1[s] = (int)sc[s][2 * u + 3]; }
-                pair_compute_mx(w1, s0, s1, &sm.a[buf][2 * u + 2][lane][0], &sm.a[buf][2 * u + 3][lane][0], lo,
-                                acc);
+                pair_compute_mx(w1, s0, s1, &sm.a[buf][2 * u + 2][lane][0], &sm.a[buf][2 * u + 3][lane][0], acc);
               }
             } else {
               float s0[NS], s1[NS];
@@ -339,11 +359,12 @@ __global__ __launch_bounds__(kStreamThreads) void gg_stream_kernel(const uint8_t
           const v4f c = kMx ? v4f{0.f, 0.f, 0.f, 0.f} : mfma16x16x128(av, bias_operand(), v4f{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
           for (int s = 0; s < NS; ++s) {
-            const uint8_t* pself = pa[s] - (lo ? 0 : 64) + (int64_t)(col - (col & 7)) * row_bytes;
-            const i32x4 wq = __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(pself + (g0 + h) * 64));
             if constexpr (kMx) {
+              const i32x4 wq = __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(pa[s] + (g0 + h) * 1024));
               acc[s] = mfma_mx(av, wq, acc[s], (int)sc[s][h]);
             } else {
+              const uint8_t* pself = pa[s] - (lo ? 0 : 64) + (int64_t)(col - (col & 7)) * row_bytes;
+              const i32x4 wq = __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(pself + (g0 + h) * 64));
               const v4f d = mfma16x16x128(av, nibbles_to_fp8(wq), c);
 #pragma unroll
               for (int r = 0; r < 4; ++r) acc[s][r] = fmaf(__uint_as_float(sc[s][h]), d[r], acc[s][r]);

@@ -36,10 +36,13 @@
 // landed, and are published by the one barrier per group.  They enter each
 // product as its accumulator input.
 //
-// MXFP4 weights (group 32) use the same ring and the same loads: 64 packed
-// bytes per column and group, and one 4-byte word of E8M0 scales per column
-// and group (the four 32-element blocks of the group) in place of the fp32
-// group scale.  The matrix core applies the block scales itself, so the
+// MXFP4 weights (group 32) use the same ring: 64 packed bytes per column and
+// group, and one 4-byte word of E8M0 scales per column and group (the four
+// 32-element blocks of the group) in place of the fp32 group scale.  They come
+// in the GEMM layout (16 columns x 128 K contiguous, scales group-major), so
+// each weight load reads one contiguous 1 KB piece and each scale load 256
+// contiguous bytes: whole cache lines, where the row-major layout reads half a
+// line per column and group and a scale word per line.  The matrix core applies the block scales itself, so the
 // group's products accumulate straight into acc (no scale FMAs, no row sums:
 // E2M1 is signed), the weight bytes are the B operand as they are, and the A
 // operand is read as the 16-byte chunks q and q + 4 that the FP4 form of the
@@ -298,26 +301,32 @@ __global__ __launch_bounds__(kThreads, 1) void gg_tiled_kernel(const uint8_t* __
           buffer_rsrc(reinterpret_cast<const uint8_t*>(w_packed) + (int64_t)e * N * row_bytes, (uint32_t)N * row_bytes);
       // (fused form: the 16 columns of load q are weight rows gate_up_row(vb + 16 q) .. +15; their base
       // goes into the scalar offset, and a wave past N reads rows from 0, unused)
+      // (MX: 16 columns x 128 K are one contiguous 1 KB piece, column n of it at 64 n)
       const int vb = n0 + kWCols * wave < N ? n0 + kWCols * wave : 0;
-      const uint32_t woff = (kSwiglu ? 0u : (uint32_t)vb * row_bytes) + (uint32_t)(lane >> 2) * row_bytes +
-                            16u * (uint32_t)((lane & 3) ^ ((lane >> 4) & 3));
+      const uint32_t wsw = 16u * (uint32_t)((lane & 3) ^ ((lane >> 4) & 3));
+      const uint32_t woff = kMx ? (uint32_t)(lane >> 2) * 64u + wsw
+                                : (kSwiglu ? 0u : (uint32_t)vb * row_bytes) + (uint32_t)(lane >> 2) * row_bytes + wsw;
       const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(w_scale + (int64_t)e * N * G, (uint32_t)(N * G * 4));
       const int scol = min(n0 + 64 * wave + lane, (int)N - 1);
-      const uint32_t soff = (uint32_t)(kSwiglu ? gate_up_row(scol, half) : scol) * (uint32_t)G * 4u;
+      // (MX: the scale words of group g of all columns are contiguous)
+      const uint32_t soff = (uint32_t)(kSwiglu ? gate_up_row(scol, half) : scol) * (kMx ? 4u : (uint32_t)G * 4u);
+      const uint32_t sstep = kMx ? (uint32_t)N * 4u : 4u;    // scale offset step per group
 
       // loads of group g into slot S: the group scales, the activation rows, the weight columns
       auto stage = [&](auto S_, int g) {
         constexpr int S = decltype(S_)::value;
         RingSlot& sl = slot<S>(ring0, ring1, ring2);
-        if (scale_loader) dma4(rs, soff, (uint32_t)g * 4u, &slot<S>(sc0, sc1, sc2)[64 * wave]);
+        if (scale_loader) dma4(rs, soff, (uint32_t)g * sstep, &slot<S>(sc0, sc1, sc2)[64 * wave]);
 #pragma unroll
         for (int q = 0; q < kALoads; ++q)
           dma16(ra, aoff[q], (uint32_t)g * kGroup, &sl.b[(kARows * wave + 8 * q) * kGroup]);
 #pragma unroll
-        for (int q = 0; q < kWLoads; ++q)
-          dma16(rw, woff,
-                (uint32_t)g * 64u + (uint32_t)(kSwiglu ? gate_up_row(vb + 16 * q, half) : 16 * q) * row_bytes,
-                &sl.b[kWBase + (kWCols * wave + 16 * q) * 64]);
+        for (int q = 0; q < kWLoads; ++q) {
+          const int v = kSwiglu ? gate_up_row(vb + 16 * q, half) : vb + 16 * q;   // first weight row of load q
+          const uint32_t so = kMx ? ((uint32_t)(v >> 4) * (uint32_t)G + (uint32_t)g) * 1024u
+                                  : (uint32_t)g * 64u + (uint32_t)(kSwiglu ? v : 16 * q) * row_bytes;
+          dma16(rw, woff, so, &sl.b[kWBase + (kWCols * wave + 16 * q) * 64]);
+        }
       };
       // wait until only the loads of the group issued last are in flight
       auto wait_last_stage = [&]() {

@@ -155,9 +155,15 @@ class W4A8MoEChannel(W4A8MoE):
 
 
 class W4A8MoEMxfp4(W4A8MoE):
-    """MXFP4 group-32 experts (w13 uint8 [E, 2I, H/2], s13 uint8 [E, 2I, H/32],
-    w2 uint8 [E, H, I/2], s2 uint8 [E, H, I/32]) with the FP8 activations of
-    the group-128 form: only the two GEMMs differ."""
+    """MXFP4 group-32 experts given row-major (w13 uint8 [E, 2I, H/2], s13 uint8
+    [E, 2I, H/32], w2 uint8 [E, H, I/2], s2 uint8 [E, H, I/32]) and kept in the
+    GEMM storage (prepack_mxfp4, once at construction), with the FP8
+    activations of the group-128 form: only the two GEMMs differ."""
     K_PER_ITEM = 2                                        # two E2M1 codes per byte
     GEMM = staticmethod(ops.w4a8_moe_grouped_gemm_mxfp4)
     GEMM_SWIGLU = staticmethod(ops.w4a8_moe_grouped_gemm_swiglu_mxfp4)
+
+    def __init__(self, w13, s13, w2, s2, k: int, renormalize: bool = True, fused: bool = True):
+        super().__init__(w13, s13, w2, s2, k, renormalize, fused)
+        self.w13, self.s13 = ops.w4a8_moe_prepack_mxfp4(w13, s13)
+        self.w2, self.s2 = ops.w4a8_moe_prepack_mxfp4(w2, s2)

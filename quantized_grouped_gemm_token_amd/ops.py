@@ -52,6 +52,7 @@ _SIGNATURES = {
     "w4a8_moe_requant": (ctypes.c_int, [_c_p, _c_p, _i64, _i64, _c_p, _c_p, _c_p]),
     "w4a8_moe_requant_i8": (ctypes.c_int, [_c_p, _c_p, _i64, _i64, _c_p, _c_p, _c_p, _c_p]),
     "w4a8_moe_quantize_weights_mxfp4": (ctypes.c_int, [_c_p, _i64, _i64, _c_p, _c_p, _c_p]),
+    "w4a8_moe_prepack_mxfp4": (ctypes.c_int, [_c_p, _c_p, _i32, _i64, _i64, _c_p, _c_p, _c_p]),
     "w4a8_moe_grouped_gemm_mxfp4": (ctypes.c_int, [_c_p, _c_p, _c_p, _i64, _c_p, _i32, _c_p, _c_p, _i64, _i64,
                                                    _c_p, _i32, _c_p]),
     "w4a8_moe_grouped_gemm_swiglu_mxfp4": (ctypes.c_int, [_c_p, _c_p, _c_p, _i64, _c_p, _i32, _c_p, _c_p, _i64,
@@ -516,7 +517,30 @@ def w4a8_moe_quantize_weights_mxfp4(w: torch.Tensor, w_packed=None, w_scale=None
     return w_packed, w_scale
 
 
+def w4a8_moe_prepack_mxfp4(w_packed: torch.Tensor, w_scale: torch.Tensor, w_blk=None, s_blk=None):
+    """Row-major MXFP4 (codes uint8 [E, N, K/2], scales uint8 [E, N, K/32]) -> the GEMM storage
+    (w_blk uint8 [E, N/16, K/128, 16, 64], s_blk uint8 [E, K/128, N, 4])."""
+    _need(w_packed, "w_packed", torch.uint8, 3)
+    dev = w_packed.device
+    _need(w_scale, "w_scale", torch.uint8, 3, dev)
+    E, N, KB = w_packed.shape
+    K = 2 * KB
+    if N % 16 or K % 128 or tuple(w_scale.shape) != (E, N, K // 32):
+        raise ValueError("w_packed must be [E, N, K/2] with N % 16 == 0 and K % 128 == 0, w_scale [E, N, K/32]")
+    G = K // 128
+    w_blk = torch.empty((E, N // 16, G, 16, 64), dtype=torch.uint8, device=dev) if w_blk is None else w_blk
+    s_blk = torch.empty((E, G, N, 4), dtype=torch.uint8, device=dev) if s_blk is None else s_blk
+    _need(w_blk, "w_blk", torch.uint8, 5, dev)
+    _need(s_blk, "s_blk", torch.uint8, 4, dev)
+    if tuple(w_blk.shape) != (E, N // 16, G, 16, 64) or tuple(s_blk.shape) != (E, G, N, 4):
+        raise ValueError("w_blk must be [E, N/16, K/128, 16, 64] and s_blk [E, K/128, N, 4]")
+    _check("w4a8_moe_prepack_mxfp4",
+           lib().w4a8_moe_prepack_mxfp4(_p(w_packed), _p(w_scale), E, N, K, _p(w_blk), _p(s_blk), _stream(dev)))
+    return w_blk, s_blk
+
+
 def _check_mx_weights(a, a_scale, a_rows, offsets, w, s, M_total, names):
+    """Checks of a GEMM on MXFP4 weights in the GEMM storage: w [E, N/16, K/128, 16, 64], s [E, K/128, N, 4]."""
     _need(a, "a", torch.uint8, 2)
     dev = a.device
     _need(a_scale, "a_scale", torch.float32, 1, dev)
@@ -525,12 +549,15 @@ def _check_mx_weights(a, a_scale, a_rows, offsets, w, s, M_total, names):
         if a_rows.numel() < M_total:
             raise ValueError("a_rows must hold M_total entries")
     _need(offsets, "offsets", torch.int32, 1, dev)
-    _need(w, names[0], torch.uint8, 3, dev)
-    _need(s, names[1], torch.uint8, 3, dev)
-    E, N, KB = w.shape
+    _need(w, names[0], torch.uint8, 5, dev)
+    _need(s, names[1], torch.uint8, 4, dev)
+    E, NB, G, sixteen, sixtyfour = w.shape
+    N = 16 * NB
     K = a.shape[1]
-    if KB * 2 != K or tuple(s.shape) != (E, N, K // 32) or offsets.numel() != E + 1:
-        raise ValueError(f"{names[0]} [E,N,K/2], {names[1]} [E,N,K/32] and offsets [E+1] must match a [*,K]")
+    if (sixteen, sixtyfour) != (16, 64) or G * 128 != K or tuple(s.shape) != (E, G, N, 4) or \
+            offsets.numel() != E + 1:
+        raise ValueError(f"{names[0]} [E,N/16,K/128,16,64], {names[1]} [E,K/128,N,4] and offsets [E+1] must match "
+                         "a [*,K] (prepack_mxfp4 writes this storage)")
     if a_scale.numel() != a.shape[0]:
         raise ValueError("a_scale must have one entry per row of a")
     return dev, E, N, K

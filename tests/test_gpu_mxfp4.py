@@ -52,7 +52,24 @@ def test_quantize_weights_mxfp4(N, K, rng):
     assert np.array_equal(host(packed), mx.fp4_pack(codes_ref))
 
 
+# ------------------------------------------------------------------ layout step
+@pytest.mark.parametrize("E,N,K", [(1, 16, 128), (3, 64, 384), (2, 4096, 6144)])
+def test_prepack_mxfp4(E, N, K, rng):
+    w = rng.integers(0, 256, size=(E, N, K // 2), dtype=np.uint8)
+    s = rng.integers(0, 256, size=(E, N, K // 32), dtype=np.uint8)
+    say(f"prepack_mxfp4 E={E} N={N} K={K}")
+    wb, sb = ops.w4a8_moe_prepack_mxfp4(to_dev(w), to_dev(s))
+    G = K // 128
+    # GEMM storage: [E][N/16][G][16][64] weight bytes, [E][G][N][4] scale bytes
+    assert np.array_equal(host(wb), w.reshape(E, N // 16, 16, G, 64).transpose(0, 1, 3, 2, 4))
+    assert np.array_equal(host(sb), s.reshape(E, N, G, 4).transpose(0, 2, 1, 3))
+
+
 # ------------------------------------------------------------------ steps 4 and 6
+def _prepacked(w, s):
+    return ops.w4a8_moe_prepack_mxfp4(to_dev(w), to_dev(s))
+
+
 def _problem(rng, E, N, K, counts, src_rows=None, scale_lo=118, scale_hi=136):
     w = rng.integers(0, 256, size=(E, N, K // 2), dtype=np.uint8)
     s = rng.integers(scale_lo, scale_hi, size=(E, N, K // 32)).astype(np.uint8)
@@ -67,8 +84,9 @@ def _problem(rng, E, N, K, counts, src_rows=None, scale_lo=118, scale_hi=136):
 
 def _gemm(w, s, offsets, a, sa, rows, algo):
     M = int(offsets[-1])
+    wb, sb = _prepacked(w, s)
     out = ops.w4a8_moe_grouped_gemm_mxfp4(to_dev(a), to_dev(sa), None if rows is None else to_dev(rows),
-                                          to_dev(offsets), to_dev(w), to_dev(s), M, algo=algo)
+                                          to_dev(offsets), wb, sb, M, algo=algo)
     return host(out)
 
 
@@ -120,8 +138,9 @@ def test_grouped_gemm_swiglu_mxfp4(E, I, K, counts, gather, algo, rng):
     M = int(offsets[-1])
     want = oracle.swiglu_f32(mx.grouped_gemm_mxfp4(a, sa, rows, offsets, w, s))
     say(f"grouped_gemm_swiglu_mxfp4 E={E} I={I} K={K} counts={counts} algo={algo}")
+    wb, sb = _prepacked(w, s)
     act, pmax = ops.w4a8_moe_grouped_gemm_swiglu_mxfp4(to_dev(a), to_dev(sa), None if rows is None else to_dev(rows),
-                                                       to_dev(offsets), to_dev(w), to_dev(s), M, algo=algo)
+                                                       to_dev(offsets), wb, sb, M, algo=algo)
     act, pmax = host(act), host(pmax)
     assert_float_parity(act, want, "grouped_gemm_swiglu_mxfp4", fro_tight=GEMM_FRO_TIGHT)
     row = np.abs(act).max(axis=1)
@@ -130,7 +149,7 @@ def test_grouped_gemm_swiglu_mxfp4(E, I, K, counts, gather, algo, rng):
     assert np.all(pmax <= row[:, None])
     # the fused path's codes against the unfused one's on the same inputs
     out = ops.w4a8_moe_grouped_gemm_mxfp4(to_dev(a), to_dev(sa), None if rows is None else to_dev(rows),
-                                          to_dev(offsets), to_dev(w), to_dev(s), M, algo=algo)
+                                          to_dev(offsets), wb, sb, M, algo=algo)
     q_ref, s_ref = ops.w4a8_moe_swiglu(out)
     q, sq = ops.w4a8_moe_requant(to_dev(act), to_dev(pmax))
     q, sq, q_ref, s_ref = host(q), host(sq), host(q_ref), host(s_ref)
