@@ -117,6 +117,35 @@ int w4a8_moe_permute(const int32_t* ids, int64_t T, int32_t k, int32_t E,
                      void* workspace, int64_t workspace_bytes, void* stream);
 
 /*
+ * ---- GEMM storage of the expert weights ------------------------------------
+ * The grouped GEMMs read the 4-bit weights in a permuted order, written once
+ * by a prepack call: the 64 packed bytes of one 128-wide K group of 16
+ * consecutive weight rows are one contiguous 1 KB piece, and the per-group
+ * scales are group-major.  (The INT4 form the pages store, int32 uint4b8
+ * words row by row, is the input of w4a8_moe_prepack_int4.)  G = K/128:
+ *   weights : int32 [E][N/16][G][16][16] (INT4) or u8 [E][N/16][G][16][64]
+ *             (MXFP4): row n, group g (row-major words 16g .. 16g+15, bytes
+ *             64g .. 64g+63) at byte ((e (N/16) + n/16) G + g) 1024 + 64 (n % 16);
+ *   scales  : fp32 [E][G][N] (INT4 group 128) or u8 [E][G][N][4] (MXFP4):
+ *             row n, group g at ((e G + g) N + n) 4.  Per-channel scales
+ *             ([E][N]) need no change.
+ * Reading whole 1 KB pieces and group-major scales, every weight and scale
+ * load fills whole cache lines.
+ */
+
+/*
+ * Offline layout step, INT4: row-major uint4b8 words w_packed int32 [E][N][K/8]
+ * (and, for the group-128 form, w_scale fp32 [E][N][K/128]) -> GEMM storage
+ * w_blk int32 [E][N/16][K/128][16][16] (and s_blk fp32 [E][K/128][N]).  A
+ * permutation of bytes.  Pass w_scale = s_blk = NULL for per-channel scales,
+ * which the GEMMs read as they are.
+ *   Rules : 0 <= E <= 1024, N % 16 == 0, K % 128 == 0; weights 16-byte
+ *   aligned, scales 4-byte aligned; no overlap of inputs and outputs.
+ */
+int w4a8_moe_prepack_int4(const int32_t* w_packed, const float* w_scale, int32_t E, int64_t N, int64_t K,
+                          int32_t* w_blk, float* s_blk, void* stream);
+
+/*
  * Steps 4 and 6 -- grouped W4A8 GEMM over the experts' row ranges.
  * ("GLM-5.3-W4A8" card, section 量化方式: INT4 weights become FP8 inside
  * the kernel, FP8 matrix multiply, no BF16 dequantization.)
@@ -128,7 +157,9 @@ int w4a8_moe_permute(const int32_t* ids, int64_t T, int32_t k, int32_t E,
  *              a_rows when it is not NULL).   a_scale : fp32 [*].
  *   a_rows   : int32 [M_total] or NULL.
  *   offsets  : int32 [E+1] on the device, offsets[E] == M_total.
- *   w_packed : int32 [E][N][K/8], 16-byte aligned.   w_scale : fp32 [E][N][K/128].
+ *   w_packed : GEMM storage int32 [E][N/16][K/128][16][16] of q + 8
+ *              (w4a8_moe_prepack_int4), 16-byte aligned.
+ *   w_scale  : GEMM storage fp32 [E][K/128][N].
  *   out      : fp32 [M_total][N], 16-byte aligned.
  *   Rules    : M_total >= 0, 1 <= E <= 1024, N > 0, N % 64 == 0, K > 0,
  *              K % 128 == 0.  Unchecked: with a_rows, a_rows[p] * K < 2^32.
@@ -222,7 +253,8 @@ int w4a8_moe_quant_act_i8(const uint16_t* x_bf16, int64_t T, int64_t H, int64_t 
  *   (K <= 2^20), then the two scales in fp32.
  *   a : int8 [*][K], 16-byte aligned.  a_scale : fp32 [*].  a_rowsum : int32 [*].
  *   a_rows, offsets : as in w4a8_moe_grouped_gemm.
- *   w_packed : int32 [E][N][K/8] uint4b8, 16-byte aligned.  w_scale : fp32 [E][N].
+ *   w_packed : GEMM storage int32 [E][N/16][K/128][16][16] uint4b8 (w4a8_moe_prepack_int4),
+ *              16-byte aligned.  w_scale : fp32 [E][N].
  *   out : fp32 [M_total][N], 16-byte aligned.  algo : W4A8_GG_*.
  *   Rules : as in w4a8_moe_grouped_gemm, and K <= 2^20.
  */
@@ -271,8 +303,9 @@ int w4a8_moe_quantize_weights_channel(const float* w, int64_t rows, int64_t K, i
  *     act_pmax[p, s], s < I/64: maxima of |act[p, :]| over parts of the row, whose
  *     maximum is max_n |act[p, n]| (every entry is written; no zeroing needed).
  *   a, a_scale, a_rows, offsets, algo : as in w4a8_moe_grouped_gemm.
- *   w13 : int32 [E][2I][K/8] uint4b8 (gate rows 0..I-1, up rows I..2I-1), 16-byte aligned.
- *   s13 : fp32 [E][2I][K/128].
+ *   w13 : GEMM storage of the int32 uint4b8 rows [E][2I] (gate rows 0..I-1, up rows
+ *         I..2I-1), 16-byte aligned.
+ *   s13 : GEMM storage fp32 [E][K/128][2I].
  *   act : fp32 [M_total][I], 16-byte aligned.  act_pmax : fp32 [M_total][I/64], 4-byte aligned.
  *   Rules : I > 0, I % 128 == 0, K % 128 == 0, 1 <= E <= 1024; otherwise as in w4a8_moe_grouped_gemm.
  */

@@ -404,8 +404,25 @@ int w4a8_moe_prepack_mxfp4(const uint8_t* w_packed, const uint8_t* w_scale, int3
     return fail(W4A8_ERR_ALIGN, "prepack_mxfp4: weights must be 16-byte aligned, scales 4-byte");
   if (int st = check_device()) return st;
   (void)hipGetLastError();
-  return launched(w4a8::launch_prepack_mxfp4(w_packed, w_scale, E, N, K, w_blk, s_blk, as_stream(stream)),
-                  "prepack_mxfp4");
+  return launched(w4a8::launch_prepack(w_packed, w_scale, E, N, K, w_blk, s_blk, as_stream(stream)), "prepack_mxfp4");
+}
+
+int w4a8_moe_prepack_int4(const int32_t* w_packed, const float* w_scale, int32_t E, int64_t N, int64_t K,
+                          int32_t* w_blk, float* s_blk, void* stream) {
+  if (E < 0 || E > 1024) return fail(W4A8_ERR_SHAPE, "prepack_int4: E=%d must be in [0, 1024]", E);
+  if (N <= 0 || N % 16 || N >= kMaxRows)
+    return fail(W4A8_ERR_SHAPE, "prepack_int4: N=%lld must be a positive multiple of 16", (long long)N);
+  if (K <= 0 || K % 128 || K >= kMaxRows)
+    return fail(W4A8_ERR_SHAPE, "prepack_int4: K=%lld must be a positive multiple of 128", (long long)K);
+  if (E == 0) return ok();
+  if (!w_packed || !w_blk) return fail(W4A8_ERR_NULL, "prepack_int4: null weight pointer");
+  if ((w_scale == nullptr) != (s_blk == nullptr))
+    return fail(W4A8_ERR_NULL, "prepack_int4: w_scale and s_blk must both be given or both be null");
+  if (!aligned(w_packed, 16) || !aligned(w_blk, 16) || !aligned(w_scale, 4) || !aligned(s_blk, 4))
+    return fail(W4A8_ERR_ALIGN, "prepack_int4: weights must be 16-byte aligned, scales 4-byte");
+  if (int st = check_device()) return st;
+  (void)hipGetLastError();
+  return launched(w4a8::launch_prepack(w_packed, w_scale, E, N, K, w_blk, s_blk, as_stream(stream)), "prepack_int4");
 }
 
 // the kernel for an MXFP4 GEMM (plain or fused), once every argument is checked

@@ -1,35 +1,27 @@
 // Grouped W4A8 GEMM, weight-streaming form: for few rows per expert (decode).
 //
-// With a handful of tokens per expert the GEMM is bound by reading the INT4
+// With a handful of tokens per expert the GEMM is bound by reading the 4-bit
 // weights from HBM once, so the kernel is built around the load pattern HBM
-// serves best: every weight load instruction of a wave reads 8 weight rows x
-// 128 contiguous bytes (8 lanes per row, 16 bytes each).  A wave owns NS
-// subtiles of 16 weight rows (output columns) of one expert and walks K two
-// 128-wide groups at a time (128 packed bytes per row = 2 groups):
-//
-//   load A: rows 0..7 of the subtile  -- lanes col < 8 take group g quarter kq,
-//                                        lanes col >= 8 take group g+1 quarter kq
-//   load B: rows 8..15                -- col >= 8 take group g, col < 8 group g+1
-//
-// (lane = col + 16 * kq).  The MFMA B operand of group g is A on the lanes
-// col < 8 and B on the others (one select per word); that of group g+1 is
-// the other half of each, rotated by 8 lanes inside each 16-lane row (one
-// DPP move per word).
+// serves best.  The weights come in the GEMM storage, where the 64 packed
+// bytes of one 128-wide K group of 16 rows are one contiguous 1 KB piece: one
+// 16-byte load per lane and group reads a whole piece (lane = col + 16 kq
+// takes row col, bytes 16 kq .. +15, i.e. K elements 32 kq .. +31), and that
+// is exactly the lane's MFMA B operand (INT4: after splitting the nibbles
+// into bytes; MXFP4: as it is).  A wave owns NS subtiles of 16 weight rows
+// (output columns) of one expert and walks K two groups at a time, so each
+// subtile streams 2 KB per step.
 //
 // The 4 waves of a workgroup share the expert's activation rows (FP8 codes,
 // up to 16 rows per M block, gathered through a_rows): they are staged in
 // LDS once per chunk of CH group pairs, directly in MFMA operand order, double
-// buffered, with one barrier per chunk.  Group scales are read as 16-byte
-// vectors (4 groups) when the group count allows.
+// buffered, with one barrier per chunk.  Per-group scales are group-major: a
+// lane reads the word of its row for each group.
 //
-// MXFP4 weights (group 32) come in the GEMM layout, where the 64 packed bytes
-// of one group of 16 rows are one contiguous 1 KB piece: one 16-byte load per
-// lane and group reads a whole piece, and gives each lane the bytes of its row
-// and K quarter, which are the B operand as they are.  The group's word of E8M0
-// block scales (scales are group-major) is shifted so that the lane's quarter
-// is byte 0, and the matrix core applies it: the products accumulate straight
-// into acc.  The activations are staged in the K order the FP4 form of the
-// instruction reads (16-byte chunks q and q + 4 for lane group q).
+// MXFP4 weights (group 32): the group's word of E8M0 block scales is shifted
+// so that the lane's quarter is byte 0, and the matrix core applies it: the
+// products accumulate straight into acc.  The activations are staged in the
+// K order the FP4 form of the instruction reads (16-byte chunks q and q + 4
+// for lane group q).
 //
 // Grid: (ceil(N / (64 NS)), E); 256 threads = 4 waves side by side in N.  An
 // expert with no rows returns at once; one with more than 16 rows loops over
@@ -43,9 +35,6 @@
 namespace w4a8 {
 
 constexpr int kStreamThreads = 256;
-
-// v_mov_b32 with DPP row_ror:8 -- lane i of each 16-lane row takes lane i^8
-__device__ __forceinline__ int row_ror8(int v) { return __builtin_amdgcn_mov_dpp(v, 0x128, 0xf, 0xf, true); }
 
 // LDS image of the activation tile of one chunk: for each group h of the
 // chunk and MFMA lane L, the 32 bytes lane L feeds to the MFMA (row L % 16,
@@ -90,26 +79,26 @@ __device__ __forceinline__ void a_chunk_store(const AChunk<CH>& r, StreamSmem<CH
   }
 }
 
+// the lane's 16 weight bytes of groups g and g + 1 for each subtile
 template <int NS>
 struct WPair {
   i32x4 wa[NS], wb[NS];
 };
 
 template <int NS>
-__device__ __forceinline__ void w_pair_load(WPair<NS>& w, const uint8_t* const (&pa)[NS],
-                                            const uint8_t* const (&pb)[NS], int g) {
+__device__ __forceinline__ void w_pair_load(WPair<NS>& w, const uint8_t* const (&pw)[NS], int g) {
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
-    w.wa[s] = __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(pa[s] + g * 64));
-    w.wb[s] = __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(pb[s] + g * 64));
+    w.wa[s] = __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(pw[s] + g * 1024));
+    w.wb[s] = __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(pw[s] + (g + 1) * 1024));
   }
 }
 
-// one group pair: B operands from the two wide loads, A operands from LDS
+// group-128 INT4 form of one group pair: A operands from LDS, the +8 offset
+// removed by the bias MFMAs (accumulator input), then acc += s * D per group
 template <int NS>
 __device__ __forceinline__ void pair_compute(const WPair<NS>& w, const float (&s0)[NS], const float (&s1)[NS],
-                                             const uint8_t* a0, const uint8_t* a1, bool lo,
-                                             v4f (&acc)[NS]) {
+                                             const uint8_t* a0, const uint8_t* a1, v4f (&acc)[NS]) {
   const v8i av0 = *reinterpret_cast<const v8i*>(a0);
   const v8i av1 = *reinterpret_cast<const v8i*>(a1);
   const v8i kb = bias_operand();
@@ -118,27 +107,10 @@ __device__ __forceinline__ void pair_compute(const WPair<NS>& w, const float (&s
   const v4f c1 = mfma16x16x128(av1, kb, zero);
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
-    i32x4 t0, t1;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      t0[q] = lo ? w.wa[s][q] : w.wb[s][q];
-      t1[q] = row_ror8(lo ? w.wb[s][q] : w.wa[s][q]);
-    }
-    const v4f d0 = mfma16x16x128(av0, nibbles_to_fp8(t0), c0);
-    const v4f d1 = mfma16x16x128(av1, nibbles_to_fp8(t1), c1);
+    const v4f d0 = mfma16x16x128(av0, nibbles_to_fp8(w.wa[s]), c0);
+    const v4f d1 = mfma16x16x128(av1, nibbles_to_fp8(w.wb[s]), c1);
 #pragma unroll
     for (int r = 0; r < 4; ++r) acc[s][r] = fmaf(s1[s], d1[r], fmaf(s0[s], d0[r], acc[s][r]));
-  }
-}
-
-// MXFP4: the B operands of groups g and g + 1 (one 16-byte load each from the
-// subtile's 1 KB pieces, at the lane's row and quarter)
-template <int NS>
-__device__ __forceinline__ void w_pair_load_mx(WPair<NS>& w, const uint8_t* const (&pw)[NS], int g) {
-#pragma unroll
-  for (int s = 0; s < NS; ++s) {
-    w.wa[s] = __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(pw[s] + g * 1024));
-    w.wb[s] = __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(pw[s] + (g + 1) * 1024));
   }
 }
 
@@ -160,19 +132,13 @@ __device__ __forceinline__ void pair_compute_mx(const WPair<NS>& w, const int (&
 // (the nibbles u = q + 8 are the INT8 B operand; the offset is removed with
 // the activation row sums in the epilogue)
 template <int NS>
-__device__ __forceinline__ void pair_compute_i8(const WPair<NS>& w, const uint8_t* a0, const uint8_t* a1, bool lo,
+__device__ __forceinline__ void pair_compute_i8(const WPair<NS>& w, const uint8_t* a0, const uint8_t* a1,
                                                 i32x4 (&acc)[NS]) {
   const v8i av0 = *reinterpret_cast<const v8i*>(a0);
   const v8i av1 = *reinterpret_cast<const v8i*>(a1);
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
-    i32x4 t0, t1;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      t0[q] = lo ? w.wa[s][q] : w.wb[s][q];
-      t1[q] = row_ror8(lo ? w.wb[s][q] : w.wa[s][q]);
-    }
-    const v8i b0 = nibbles_to_fp8(t0), b1 = nibbles_to_fp8(t1);
+    const v8i b0 = nibbles_to_fp8(w.wa[s]), b1 = nibbles_to_fp8(w.wb[s]);
     acc[s] = mfma_i8_16x16x64(av0.lo, b0.lo, acc[s]);
     acc[s] = mfma_i8_16x16x64(av0.hi, b0.hi, acc[s]);
     acc[s] = mfma_i8_16x16x64(av1.lo, b1.lo, acc[s]);
@@ -182,7 +148,8 @@ __device__ __forceinline__ void pair_compute_i8(const WPair<NS>& w, const uint8_
 
 // kForm: kFormChannel, the per-channel variant (INT8 activations with row sums
 // a_rowsum, one scale per weight row in w_scale [E][N]); kFormG128, the
-// group-128 FP8 form; kFormMx, MXFP4 weights (w_scale holds the E8M0 bytes).
+// group-128 FP8 form (w_scale [E][K/128][N]); kFormMx, MXFP4 weights (w_scale
+// holds the E8M0 words, [E][K/128][N]).
 // kSwiglu: the fused gate/up form: a wave's two subtiles are the gate and the
 // up rows of the same 16 output columns (gate_up_row), and the epilogue
 // writes act = silu(gate) * up [M][N/2] and the workgroup's max |act| of each
@@ -207,30 +174,20 @@ __global__ __launch_bounds__(kStreamThreads) void gg_stream_kernel(const uint8_t
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
   const int col = lane & 15, kq = lane >> 4;
-  const bool lo = col < 8;
   const int64_t n0 = ((int64_t)blockIdx.x * 4 + wave) * (16 * NS);
   const bool active = n0 < N;                // waves past N only help stage activations
   const int G = (int)(K >> 7);
   const int64_t row_bytes = K >> 1;
-  const bool vec_scales = (G & 3) == 0 && (reinterpret_cast<uintptr_t>(w_scale) & 15) == 0;
 
-  const uint8_t* pa[NS];
-  const uint8_t* pb[NS];
-  const float* srow[NS];
+  // subtile s: weight rows nb .. nb+15 are the G pieces of 1 KB from their block's base;
+  // the lane reads row col, bytes 16 kq .. +15 of each.  Group scales: word (g, nb + col).
+  const uint8_t* pw[NS];
+  const uint32_t* srow[NS];
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
     const int64_t nb = active ? (kSwiglu ? (int64_t)gate_up_row((int)(n0 + 16 * s), (int)(N / 2)) : n0 + 16 * s) : 0;
-    const uint8_t* wbase = reinterpret_cast<const uint8_t*>(w_packed) + ((int64_t)e * N + nb) * row_bytes;
-    if constexpr (kMx) {
-      // rows nb .. nb+15 are G pieces of 1 KB from wbase; scales [E][G][N] words
-      pa[s] = wbase + col * 64 + kq * 16;
-      pb[s] = pa[s];
-      srow[s] = w_scale + (int64_t)e * N * G + nb + col;
-    } else {
-      pa[s] = wbase + (int64_t)(col & 7) * row_bytes + (lo ? 0 : 64) + kq * 16;
-      pb[s] = wbase + (int64_t)(8 + (col & 7)) * row_bytes + (lo ? 64 : 0) + kq * 16;
-      srow[s] = w_scale + ((int64_t)e * N + nb + col) * G;
-    }
+    pw[s] = reinterpret_cast<const uint8_t*>(w_packed) + ((int64_t)e * N + nb) * row_bytes + col * 64 + kq * 16;
+    srow[s] = reinterpret_cast<const uint32_t*>(w_scale) + (int64_t)e * N * G + nb + col;
   }
 
   for (int m0 = r0; m0 < r1; m0 += 16) {
@@ -257,58 +214,17 @@ __global__ __launch_bounds__(kStreamThreads) void gg_stream_kernel(const uint8_t
       const bool has_next = ci + 1 < nchunks;
       const int ng_next = has_next ? min(2 * CH, G - g0 - 2 * CH) : 0;
       if (has_next) a_chunk_load(next, arow_t, g0 + 2 * CH, ng_next);
-      if constexpr (kInt8) {
-        if (active) {
-          const int npairs = ng >> 1;
-#pragma unroll
-          for (int u = 0; u < CH; u += 2) {
-            if (u < npairs) {
-              WPair<NS> w0, w1;
-              w_pair_load(w0, pa, pb, g0 + 2 * u);
-              const bool two = u + 1 < npairs;
-              if (two) w_pair_load(w1, pa, pb, g0 + 2 * u + 2);
-              pair_compute_i8(w0, &sm.a[buf][2 * u][lane][0], &sm.a[buf][2 * u + 1][lane][0], lo, acc);
-              if (two)
-                pair_compute_i8(w1, &sm.a[buf][2 * u + 2][lane][0], &sm.a[buf][2 * u + 3][lane][0], lo, acc);
-            }
-          }
-          if (ng & 1) {   // a last single group: each lane reads its own column's quarter
-            const int h = ng - 1;
-            const v8i av = *reinterpret_cast<const v8i*>(&sm.a[buf][h][lane][0]);
-#pragma unroll
-            for (int s = 0; s < NS; ++s) {
-              const uint8_t* pself = pa[s] - (lo ? 0 : 64) + (int64_t)(col - (col & 7)) * row_bytes;
-              const i32x4 wq = __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(pself + (g0 + h) * 64));
-              const v8i b = nibbles_to_fp8(wq);
-              acc[s] = mfma_i8_16x16x64(av.lo, b.lo, acc[s]);
-              acc[s] = mfma_i8_16x16x64(av.hi, b.hi, acc[s]);
-            }
-          }
-        }
-      } else if (active) {
-        // scales of this chunk's groups for each subtile, as bits: fp32 group
-        // scales, or (MX) words of E8M0 bytes, shifted so that byte 0 is the
-        // lane's K quarter
+      if (active) {
+        // group scales of this chunk (bits: fp32, or MX words shifted so that byte 0 is the lane's quarter)
         uint32_t sc[NS][2 * CH];
+        if constexpr (!kInt8) {
 #pragma unroll
-        for (int s = 0; s < NS; ++s) {
-          const uint32_t* srw = reinterpret_cast<const uint32_t*>(srow[s]);
-          if constexpr (kMx) {
+          for (int s = 0; s < NS; ++s) {
 #pragma unroll
-            for (int h = 0; h < 2 * CH; ++h) sc[s][h] = h < ng ? srw[(int64_t)(g0 + h) * N] : 0u;
-          } else if (vec_scales && ng == 2 * CH) {
-#pragma unroll
-            for (int v = 0; v < (2 * CH) / 4; ++v) {
-              const u32x4 q4 = *reinterpret_cast<const u32x4*>(srw + g0 + 4 * v);
-              sc[s][4 * v] = q4[0]; sc[s][4 * v + 1] = q4[1]; sc[s][4 * v + 2] = q4[2]; sc[s][4 * v + 3] = q4[3];
+            for (int h = 0; h < 2 * CH; ++h) {
+              sc[s][h] = h < ng ? srow[s][(int64_t)(g0 + h) * N] : 0u;
+              if constexpr (kMx) sc[s][h] >>= 8 * kq;
             }
-          } else {
-#pragma unroll
-            for (int h = 0; h < 2 * CH; ++h) sc[s][h] = h < ng ? srw[g0 + h] : 0u;
-          }
-          if constexpr (kMx) {
-#pragma unroll
-            for (int h = 0; h < 2 * CH; ++h) sc[s][h] >>= 8 * kq;
           }
         }
         const int npairs = ng >> 1;
@@ -317,22 +233,24 @@ __global__ __launch_bounds__(kStreamThreads) void gg_stream_kernel(const uint8_t
           if (u < npairs) {
             WPair<NS> w0, w1;
             const bool two = u + 1 < npairs;
-            if constexpr (kMx) {
-              w_pair_load_mx(w0, pa, g0 + 2 * u);
-              if (two) w_pair_load_mx(w1, pa, g0 + 2 * u + 2);
-            } else {
-              w_pair_load(w0, pa, pb, g0 + 2 * u);
-              if (two) w_pair_load(w1, pa, pb, g0 + 2 * u + 2);
-            }
-            if constexpr (kMx) {
+            w_pair_load(w0, pw, g0 + 2 * u);
+            if (two) w_pair_load(w1, pw, g0 + 2 * u + 2);
+            const uint8_t* a00 = &sm.a[buf][2 * u][lane][0];
+            const uint8_t* a01 = &sm.a[buf][2 * u + 1][lane][0];
+            const uint8_t* a10 = &sm.a[buf][2 * u + 2][lane][0];
+            const uint8_t* a11 = &sm.a[buf][2 * u + 3][lane][0];
+            if constexpr (kInt8) {
+              pair_compute_i8(w0, a00, a01, acc);
+              if (two) pair_compute_i8(w1, a10, a11, acc);
+            } else if constexpr (kMx) {
               int s0[NS], s1[NS];
 #pragma unroll
               for (int s = 0; s < NS; ++s) { s0[s] = (int)sc[s][2 * u]; s1[s] = (int)sc[s][2 * u + 1]; }
-              pair_compute_mx(w0, s0, s1, &sm.a[buf][2 * u][lane][0], &sm.a[buf][2 * u + 1][lane][0], acc);
+              pair_compute_mx(w0, s0, s1, a00, a01, acc);
               if (two) {
 #pragma unroll
                 for (int s = 0; s < NS; ++s) { s0[s] = (int)sc[s][2 * u + 2]; s1[s] = (int)sc[s][2 * u + 3]; }
-                pair_compute_mx(w1, s0, s1, &sm.a[buf][2 * u + 2][lane][0], &sm.a[buf][2 * u + 3][lane][0], acc);
+                pair_compute_mx(w1, s0, s1, a10, a11, acc);
               }
             } else {
               float s0[NS], s1[NS];
@@ -341,30 +259,33 @@ __global__ __launch_bounds__(kStreamThreads) void gg_stream_kernel(const uint8_t
                 s0[s] = __uint_as_float(sc[s][2 * u]);
                 s1[s] = __uint_as_float(sc[s][2 * u + 1]);
               }
-              pair_compute(w0, s0, s1, &sm.a[buf][2 * u][lane][0], &sm.a[buf][2 * u + 1][lane][0], lo, acc);
+              pair_compute(w0, s0, s1, a00, a01, acc);
               if (two) {
 #pragma unroll
                 for (int s = 0; s < NS; ++s) {
                   s0[s] = __uint_as_float(sc[s][2 * u + 2]);
                   s1[s] = __uint_as_float(sc[s][2 * u + 3]);
                 }
-                pair_compute(w1, s0, s1, &sm.a[buf][2 * u + 2][lane][0], &sm.a[buf][2 * u + 3][lane][0], lo, acc);
+                pair_compute(w1, s0, s1, a10, a11, acc);
               }
             }
           }
         }
-        if (ng & 1) {   // a last single group: each lane reads its own column's quarter
+        if (ng & 1) {   // a last single group
           const int h = ng - 1;
           const v8i av = *reinterpret_cast<const v8i*>(&sm.a[buf][h][lane][0]);
-          const v4f c = kMx ? v4f{0.f, 0.f, 0.f, 0.f} : mfma16x16x128(av, bias_operand(), v4f{0.f, 0.f, 0.f, 0.f});
+          const v4f c = (kInt8 || kMx) ? v4f{0.f, 0.f, 0.f, 0.f}
+                                       : mfma16x16x128(av, bias_operand(), v4f{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
           for (int s = 0; s < NS; ++s) {
-            if constexpr (kMx) {
-              const i32x4 wq = __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(pa[s] + (g0 + h) * 1024));
+            const i32x4 wq = __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(pw[s] + (g0 + h) * 1024));
+            if constexpr (kInt8) {
+              const v8i b = nibbles_to_fp8(wq);
+              acc[s] = mfma_i8_16x16x64(av.lo, b.lo, acc[s]);
+              acc[s] = mfma_i8_16x16x64(av.hi, b.hi, acc[s]);
+            } else if constexpr (kMx) {
               acc[s] = mfma_mx(av, wq, acc[s], (int)sc[s][h]);
             } else {
-              const uint8_t* pself = pa[s] - (lo ? 0 : 64) + (int64_t)(col - (col & 7)) * row_bytes;
-              const i32x4 wq = __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(pself + (g0 + h) * 64));
               const v4f d = mfma16x16x128(av, nibbles_to_fp8(wq), c);
 #pragma unroll
               for (int r = 0; r < 4; ++r) acc[s][r] = fmaf(__uint_as_float(sc[s][h]), d[r], acc[s][r]);

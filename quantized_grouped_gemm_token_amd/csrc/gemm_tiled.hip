@@ -36,13 +36,14 @@
 // landed, and are published by the one barrier per group.  They enter each
 // product as its accumulator input.
 //
+// The weights come in the GEMM storage (16 columns x 128 K contiguous, scales
+// group-major), so each weight load reads one contiguous 1 KB piece and each
+// scale load 256 contiguous bytes: whole cache lines, where a row-major layout
+// reads half a line per column and group and a line per scale word.
+//
 // MXFP4 weights (group 32) use the same ring: 64 packed bytes per column and
 // group, and one 4-byte word of E8M0 scales per column and group (the four
-// 32-element blocks of the group) in place of the fp32 group scale.  They come
-// in the GEMM layout (16 columns x 128 K contiguous, scales group-major), so
-// each weight load reads one contiguous 1 KB piece and each scale load 256
-// contiguous bytes: whole cache lines, where the row-major layout reads half a
-// line per column and group and a scale word per line.  The matrix core applies the block scales itself, so the
+// 32-element blocks of the group) in place of the fp32 group scale.  The matrix core applies the block scales itself, so the
 // group's products accumulate straight into acc (no scale FMAs, no row sums:
 // E2M1 is signed), the weight bytes are the B operand as they are, and the A
 // operand is read as the 16-byte chunks q and q + 4 that the FP4 form of the
@@ -74,7 +75,8 @@ constexpr int kBBlocks = 4;           // 16-column B blocks per wave
 constexpr int kSlotBytes = kTM * kGroup + kTN * kGroup / 2;   // 48 KB: either tile shape's group
 static_assert(kSlotBytes == kWideRows * kGroup + kWideCols * kGroup / 2, "slot sizes");
 
-// One ring slot: the activation rows of one group, then its weight columns.
+// One ring slot: the activation rows of one group, then its weight columns
+// (column n of a 16-column load is at 64 n of its 1 KB piece in HBM).
 //   a: row r, 16-byte chunk c (K bytes 16c..16c+15 of the group) at r*128 + 16*(c ^ ((r >> 1) & 7))
 //   w: column n, chunk c (packed bytes 16c..16c+15) at W + n*64 + 16*(c ^ ((n >> 2) & 3)),
 //      W = 256 * 128 (square tile) or 128 * 128 (wide tile)
@@ -292,25 +294,21 @@ __global__ __launch_bounds__(kThreads, 1) void gg_tiled_kernel(const uint8_t* __
         const int c = (lane & 7) ^ ((r >> 1) & 7);
         aoff[q] = (uint32_t)(a_rows ? a_rows[p] : p) * (uint32_t)K + 16u * (uint32_t)c;
       }
-      // weights: columns kWCols wave + 16 q + lane / 4 of the tile, chunk position lane % 4.
-      // Columns n and n + 16 q have the same swizzle, so one lane offset serves
-      // every q.  N % 64 == 0, so a wave's columns are either all below N or all
-      // past it, where the lane offset itself is out of the buffer's range and
-      // the loads return zeros.
+      // weights: columns kWCols wave + 16 q + lane / 4 of the tile, chunk position lane % 4:
+      // load q reads the 1 KB piece of its 16 weight rows and the group (the piece's base
+      // goes into the scalar offset; fused form: rows gate_up_row(vb + 16 q) .. +15).
+      // Columns n and n + 16 q have the same swizzle, so one lane offset serves every q.
+      // N % 64 == 0, so a wave's columns are either all below N or all past it; a wave
+      // past N reads rows from 0, unused.
       const __amdgpu_buffer_rsrc_t rw =
           buffer_rsrc(reinterpret_cast<const uint8_t*>(w_packed) + (int64_t)e * N * row_bytes, (uint32_t)N * row_bytes);
-      // (fused form: the 16 columns of load q are weight rows gate_up_row(vb + 16 q) .. +15; their base
-      // goes into the scalar offset, and a wave past N reads rows from 0, unused)
-      // (MX: 16 columns x 128 K are one contiguous 1 KB piece, column n of it at 64 n)
       const int vb = n0 + kWCols * wave < N ? n0 + kWCols * wave : 0;
-      const uint32_t wsw = 16u * (uint32_t)((lane & 3) ^ ((lane >> 4) & 3));
-      const uint32_t woff = kMx ? (uint32_t)(lane >> 2) * 64u + wsw
-                                : (kSwiglu ? 0u : (uint32_t)vb * row_bytes) + (uint32_t)(lane >> 2) * row_bytes + wsw;
+      const uint32_t woff = (uint32_t)(lane >> 2) * 64u + 16u * (uint32_t)((lane & 3) ^ ((lane >> 4) & 3));
+      // group scales: the words of group g of all N columns are contiguous
       const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(w_scale + (int64_t)e * N * G, (uint32_t)(N * G * 4));
       const int scol = min(n0 + 64 * wave + lane, (int)N - 1);
-      // (MX: the scale words of group g of all columns are contiguous)
-      const uint32_t soff = (uint32_t)(kSwiglu ? gate_up_row(scol, half) : scol) * (kMx ? 4u : (uint32_t)G * 4u);
-      const uint32_t sstep = kMx ? (uint32_t)N * 4u : 4u;    // scale offset step per group
+      const uint32_t soff = (uint32_t)(kSwiglu ? gate_up_row(scol, half) : scol) * 4u;
+      const uint32_t sstep = (uint32_t)N * 4u;    // scale offset step per group
 
       // loads of group g into slot S: the group scales, the activation rows, the weight columns
       auto stage = [&](auto S_, int g) {
@@ -323,9 +321,8 @@ __global__ __launch_bounds__(kThreads, 1) void gg_tiled_kernel(const uint8_t* __
 #pragma unroll
         for (int q = 0; q < kWLoads; ++q) {
           const int v = kSwiglu ? gate_up_row(vb + 16 * q, half) : vb + 16 * q;   // first weight row of load q
-          const uint32_t so = kMx ? ((uint32_t)(v >> 4) * (uint32_t)G + (uint32_t)g) * 1024u
-                                  : (uint32_t)g * 64u + (uint32_t)(kSwiglu ? v : 16 * q) * row_bytes;
-          dma16(rw, woff, so, &sl.b[kWBase + (kWCols * wave + 16 * q) * 64]);
+          dma16(rw, woff, ((uint32_t)(v >> 4) * (uint32_t)G + (uint32_t)g) * 1024u,
+                &sl.b[kWBase + (kWCols * wave + 16 * q) * 64]);
         }
       };
       // wait until only the loads of the group issued last are in flight

@@ -7,9 +7,12 @@
 
 namespace w4a8 {
 
-// One grouped GEMM.  a_rowsum == nullptr: the group-128 FP8 form (w_scale
-// [E][N][K/128]), or with mx set the MXFP4 form; otherwise the per-channel
-// INT8 form (INT8 activations with their row code sums, w_scale [E][N]).
+// One grouped GEMM on weights in the GEMM storage (launch_prepack): 1 KB per 16
+// rows x 128 K ([E][N/16][K/128][16][64] bytes), per-group scales group-major
+// ([E][K/128][N] 4-byte words).  a_rowsum == nullptr: the group-128 FP8 form
+// (w_scale fp32 group scales), or with mx set the MXFP4 form; otherwise the
+// per-channel INT8 form (INT8 activations with their row code sums, w_scale
+// fp32 [E][N]).
 struct GemmArgs {
   const uint8_t* a;
   const float* a_scale;
@@ -28,10 +31,9 @@ struct GemmArgs {
   // pmax [M_total][N/128] gets row maxima of |act| (each entry over some of
   // the row's columns; their max is the row's)
   float* pmax = nullptr;
-  // MXFP4 weights in the GEMM layout (prepack_mxfp4): w_packed holds E2M1 codes,
-  // 1 KB per 16 rows x 128 K ([E][N/16][K/128][16][64] bytes, element k in the
-  // low nibble of byte k/2 when k is even), w_scale the E8M0 block scales as
-  // [E][K/128][N][4] bytes (one 4-byte word per row and 128-wide K group)
+  // MXFP4 weights: w_packed holds E2M1 codes (element k in the low nibble of
+  // byte k/2 when k is even), w_scale the E8M0 block scales (the 4-byte word of
+  // a row and group holds its four 32-element blocks)
   bool mx = false;
 };
 
@@ -55,8 +57,8 @@ hipError_t launch_wquant(const float* w, int64_t rows, int64_t K, int mse_clip, 
                          hipStream_t stream);
 hipError_t launch_wquant_mxfp4(const float* w, int64_t rows, int64_t K, uint8_t* packed, uint8_t* scales,
                                hipStream_t stream);
-hipError_t launch_prepack_mxfp4(const uint8_t* w, const uint8_t* s, int64_t E, int64_t N, int64_t K, uint8_t* wb,
-                                uint8_t* sb, hipStream_t stream);
+hipError_t launch_prepack(const void* w, const void* s, int64_t E, int64_t N, int64_t K, void* wb, void* sb,
+                          hipStream_t stream);
 hipError_t launch_requant(const float* act, const float* pmax, int64_t M, int64_t I, uint8_t* q, float* s,
                           hipStream_t stream);
 hipError_t launch_requant_i8(const float* act, const float* pmax, int64_t M, int64_t I, int8_t* q, float* s,

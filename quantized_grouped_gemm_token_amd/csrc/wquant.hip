@@ -166,18 +166,20 @@ hipError_t launch_wquant_mxfp4(const float* w, int64_t rows, int64_t K, uint8_t*
   return hipGetLastError();
 }
 
-// MXFP4 weights into the layout the grouped GEMMs read (a pure permutation of
-// bytes).  Per expert e (G = K/128 groups):
+// 4-bit weights into the layout the grouped GEMMs read (a pure permutation of
+// bytes; INT4 words and MXFP4 bytes alike hold 64 bytes per row and 128-wide
+// K group).  Per expert e (G = K/128 groups):
 //   w: the 64 packed bytes of K group g of rows 16b .. 16b+15 become one 1 KB
 //      piece at ((e (N/16) + b) G + g) 1024 + 64 (row % 16), so that one
 //      16-row x 128-K operand block is a single contiguous load;
-//   s: the 4 scale bytes of row n and group g move to ((e G + g) N + n) 4, so
-//      that the scales of one group of all rows are contiguous.
+//   s: the 4 scale bytes of row n and group g (one fp32 group scale, or four
+//      E8M0 block scales) move to ((e G + g) N + n) 4, so that the scales of
+//      one group of all rows are contiguous (skipped when s is null).
 // One thread per 16 weight bytes and one per 4 scale bytes.
-__global__ __launch_bounds__(256) void prepack_mxfp4_kernel(const u32x4* __restrict__ w, const uint32_t* __restrict__ s,
+__global__ __launch_bounds__(256) void prepack_kernel(const u32x4* __restrict__ w, const uint32_t* __restrict__ s,
                                                             int64_t E, int64_t N, int64_t G,
                                                             u32x4* __restrict__ wb, uint32_t* __restrict__ sb) {
-  const int64_t nw = E * N * G * 4, ns = E * N * G;     // 16-byte pieces, 4-byte scale words
+  const int64_t nw = E * N * G * 4, ns = s ? E * N * G : 0;   // 16-byte pieces, 4-byte scale words
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < nw + ns; t += stride) {
     if (t < nw) {
@@ -192,12 +194,12 @@ __global__ __launch_bounds__(256) void prepack_mxfp4_kernel(const u32x4* __restr
   }
 }
 
-hipError_t launch_prepack_mxfp4(const uint8_t* w, const uint8_t* s, int64_t E, int64_t N, int64_t K, uint8_t* wb,
-                                uint8_t* sb, hipStream_t stream) {
-  const int64_t G = K / 128, total = E * N * G * 5;
+hipError_t launch_prepack(const void* w, const void* s, int64_t E, int64_t N, int64_t K, void* wb, void* sb,
+                          hipStream_t stream) {
+  const int64_t G = K / 128, total = E * N * G * (s ? 5 : 4);
   if (total == 0) return hipSuccess;
   const int64_t blocks = std::min<int64_t>((total + 255) / 256, 16384);
-  hipLaunchKernelGGL(prepack_mxfp4_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
+  hipLaunchKernelGGL(prepack_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
                      reinterpret_cast<const u32x4*>(w), reinterpret_cast<const uint32_t*>(s), E, N, G,
                      reinterpret_cast<u32x4*>(wb), reinterpret_cast<uint32_t*>(sb));
   return hipGetLastError();

@@ -8,8 +8,10 @@ gate/up GEMM with SwiGLU in its epilogue, writing act = silu(gate) * up and
 partial row maxima of |act|) and requant (the codes of act): the same results with half
 the intermediate bytes.
 
-Expert weights stay resident on the GPU in the packed format (int32
-[E][N][K/8] words of uint4b8 nibbles and fp32 [E][N][K/128] group scales).
+Expert weights are given in the packed format (int32 [E][N][K/8] words of
+uint4b8 nibbles and fp32 [E][N][K/128] group scales) and stay resident on the
+GPU in the GEMM storage (prepack_int4, once at construction: 1 KB per 16 rows
+x 128 K, group-major scales).
 W4A8MoEChannel is the per-channel INT4 x per-token INT8 variant: fp32 [E][N]
 scales, INT8 activations.  W4A8MoEMxfp4 holds MXFP4 group-32 experts (E2M1
 codes uint8 [E][N][K/2], E8M0 scales uint8 [E][N][K/32]) and uses the same
@@ -36,7 +38,7 @@ class W4A8MoE:
         c = self.K_PER_ITEM
         if E2 != E or N13 % 2 or KW13 * c != H or KW2 * c * 2 != N13:
             raise ValueError(f"w13 must be [E, 2I, H/{c}] and w2 [E, H, I/{c}]")
-        self.w13, self.s13, self.w2, self.s2 = w13, s13, w2, s2
+        self.w13, self.s13, self.w2, self.s2 = self.prepack(w13, s13, w2, s2)
         self.E, self.H, self.I, self.k = E, H, N13 // 2, k
         self.renormalize = renormalize
         self.fused = fused
@@ -61,6 +63,13 @@ class W4A8MoE:
             else:
                 self._bufs[T].update(h=e((R, 2 * self.I), torch.float32))
         return self._bufs[T]
+
+    @staticmethod
+    def prepack(w13, s13, w2, s2):
+        """The experts in the GEMM storage."""
+        w13b, s13b = ops.w4a8_moe_prepack_int4(w13, s13)
+        w2b, s2b = ops.w4a8_moe_prepack_int4(w2, s2)
+        return w13b, s13b, w2b, s2b
 
     STEPS = ("quant_act", "route", "permute", "gemm_gate_up", "swiglu", "gemm_down", "unpermute")
 
@@ -106,6 +115,10 @@ class W4A8MoE:
 class W4A8MoEChannel(W4A8MoE):
     """The per-channel INT4 x per-token INT8 variant: s13 [E, 2I] and s2 [E, H]
     are per-channel scales; steps 1, 4, 5 and 6 use the INT8 calls."""
+
+    @staticmethod
+    def prepack(w13, s13, w2, s2):
+        return ops.w4a8_moe_prepack_int4(w13)[0], s13, ops.w4a8_moe_prepack_int4(w2)[0], s2
 
     def buffers(self, T: int) -> dict:
         if T not in self._bufs:
@@ -163,7 +176,8 @@ class W4A8MoEMxfp4(W4A8MoE):
     GEMM = staticmethod(ops.w4a8_moe_grouped_gemm_mxfp4)
     GEMM_SWIGLU = staticmethod(ops.w4a8_moe_grouped_gemm_swiglu_mxfp4)
 
-    def __init__(self, w13, s13, w2, s2, k: int, renormalize: bool = True, fused: bool = True):
-        super().__init__(w13, s13, w2, s2, k, renormalize, fused)
-        self.w13, self.s13 = ops.w4a8_moe_prepack_mxfp4(w13, s13)
-        self.w2, self.s2 = ops.w4a8_moe_prepack_mxfp4(w2, s2)
+    @staticmethod
+    def prepack(w13, s13, w2, s2):
+        w13b, s13b = ops.w4a8_moe_prepack_mxfp4(w13, s13)
+        w2b, s2b = ops.w4a8_moe_prepack_mxfp4(w2, s2)
+        return w13b, s13b, w2b, s2b

@@ -52,6 +52,7 @@ _SIGNATURES = {
     "w4a8_moe_requant": (ctypes.c_int, [_c_p, _c_p, _i64, _i64, _c_p, _c_p, _c_p]),
     "w4a8_moe_requant_i8": (ctypes.c_int, [_c_p, _c_p, _i64, _i64, _c_p, _c_p, _c_p, _c_p]),
     "w4a8_moe_quantize_weights_mxfp4": (ctypes.c_int, [_c_p, _i64, _i64, _c_p, _c_p, _c_p]),
+    "w4a8_moe_prepack_int4": (ctypes.c_int, [_c_p, _c_p, _i32, _i64, _i64, _c_p, _c_p, _c_p]),
     "w4a8_moe_prepack_mxfp4": (ctypes.c_int, [_c_p, _c_p, _i32, _i64, _i64, _c_p, _c_p, _c_p]),
     "w4a8_moe_grouped_gemm_mxfp4": (ctypes.c_int, [_c_p, _c_p, _c_p, _i64, _c_p, _i32, _c_p, _c_p, _i64, _i64,
                                                    _c_p, _i32, _c_p]),
@@ -128,6 +129,15 @@ def _need(t: torch.Tensor, name: str, dtype, ndim: int, dev: torch.device | None
         raise ValueError(f"{name} must be contiguous")
 
 
+def _int4_storage(w: torch.Tensor, name: str, dev) -> tuple[int, int, int]:
+    """(E, N, K) of INT4 weights in the GEMM storage, int32 [E, N/16, K/128, 16, 16]."""
+    _need(w, name, torch.int32, 5, dev)
+    E, NB, G, sixteen, words = w.shape
+    if (sixteen, words) != (16, 16):
+        raise ValueError(f"{name} must be the GEMM storage [E, N/16, K/128, 16, 16] (w4a8_moe_prepack_int4)")
+    return E, 16 * NB, 128 * G
+
+
 # ------------------------------------------------------------------ calls
 def w4a8_moe_quant_act(x: torch.Tensor, qx: torch.Tensor | None = None, sx: torch.Tensor | None = None):
     """bf16 [T, H] -> (E4M3 codes uint8 [T, H], per-token scales fp32 [T])."""
@@ -194,7 +204,9 @@ def w4a8_moe_permute(ids: torch.Tensor, E: int, offsets=None, row_token=None, in
 def w4a8_moe_grouped_gemm(a: torch.Tensor, a_scale: torch.Tensor, a_rows: torch.Tensor | None,
                           offsets: torch.Tensor, w_packed: torch.Tensor, w_scale: torch.Tensor, M_total: int,
                           out: torch.Tensor | None = None, algo: int = W4A8_GG_AUTO):
-    """Grouped W4A8 GEMM -> out fp32 [M_total, N] (rows of expert e: offsets[e]..offsets[e+1])."""
+    """Grouped W4A8 GEMM -> out fp32 [M_total, N] (rows of expert e: offsets[e]..offsets[e+1]).
+
+    w_packed / w_scale: the GEMM storage written by w4a8_moe_prepack_int4."""
     _need(a, "a", torch.uint8, 2)
     dev = a.device
     _need(a_scale, "a_scale", torch.float32, 1, dev)
@@ -203,12 +215,11 @@ def w4a8_moe_grouped_gemm(a: torch.Tensor, a_scale: torch.Tensor, a_rows: torch.
         if a_rows.numel() < M_total:
             raise ValueError("a_rows must hold M_total entries")
     _need(offsets, "offsets", torch.int32, 1, dev)
-    _need(w_packed, "w_packed", torch.int32, 3, dev)
+    E, N, KW = _int4_storage(w_packed, "w_packed", dev)
     _need(w_scale, "w_scale", torch.float32, 3, dev)
-    E, N, KW = w_packed.shape
     K = a.shape[1]
-    if KW * 8 != K or tuple(w_scale.shape) != (E, N, K // 128) or offsets.numel() != E + 1:
-        raise ValueError("w_packed [E,N,K/8], w_scale [E,N,K/128] and offsets [E+1] must match a [*,K]")
+    if KW != K or tuple(w_scale.shape) != (E, K // 128, N) or offsets.numel() != E + 1:
+        raise ValueError("w_packed [E,N/16,K/128,16,16], w_scale [E,K/128,N] and offsets [E+1] must match a [*,K]")
     if a_scale.numel() != a.shape[0]:
         raise ValueError("a_scale must have one entry per row of a")
     out = torch.empty((M_total, N), dtype=torch.float32, device=dev) if out is None else out
@@ -312,16 +323,15 @@ def w4a8_moe_grouped_gemm_i8(a: torch.Tensor, a_scale: torch.Tensor, a_rowsum: t
                              a_rows: torch.Tensor | None, offsets: torch.Tensor, w_packed: torch.Tensor,
                              w_scale: torch.Tensor, out: torch.Tensor | None = None, M_total: int | None = None,
                              algo: int = W4A8_GG_AUTO):
-    """int8 [*, K] activations x per-channel INT4 experts [E, N, K/8] (scales [E, N]) -> fp32 [M_total, N]."""
+    """int8 [*, K] activations x per-channel INT4 experts (GEMM storage [E, N/16, K/128, 16, 16],
+    scales [E, N]) -> fp32 [M_total, N]."""
     _need(a, "a", torch.int8, 2)
     dev = a.device
     _need(a_scale, "a_scale", torch.float32, 1, dev)
     _need(a_rowsum, "a_rowsum", torch.int32, 1, dev)
     _need(offsets, "offsets", torch.int32, 1, dev)
-    _need(w_packed, "w_packed", torch.int32, 3, dev)
+    E, N, K = _int4_storage(w_packed, "w_packed", dev)
     _need(w_scale, "w_scale", torch.float32, 2, dev)
-    E, N, K8 = w_packed.shape
-    K = K8 * 8
     if a.shape[1] != K or tuple(w_scale.shape) != (E, N) or offsets.numel() != E + 1:
         raise ValueError("a must be [*, K], w_scale [E, N], offsets [E+1]")
     if a_rows is not None:
@@ -405,12 +415,11 @@ def w4a8_moe_grouped_gemm_swiglu(a: torch.Tensor, a_scale: torch.Tensor, a_rows:
         if a_rows.numel() < M_total:
             raise ValueError("a_rows must hold M_total entries")
     _need(offsets, "offsets", torch.int32, 1, dev)
-    _need(w13, "w13", torch.int32, 3, dev)
+    E, N2, KW = _int4_storage(w13, "w13", dev)
     _need(s13, "s13", torch.float32, 3, dev)
-    E, N2, KW = w13.shape
     K = a.shape[1]
-    if N2 % 2 or KW * 8 != K or tuple(s13.shape) != (E, N2, K // 128) or offsets.numel() != E + 1:
-        raise ValueError("w13 [E,2I,K/8], s13 [E,2I,K/128] and offsets [E+1] must match a [*,K]")
+    if N2 % 2 or KW != K or tuple(s13.shape) != (E, K // 128, N2) or offsets.numel() != E + 1:
+        raise ValueError("w13 [E,2I/16,K/128,16,16], s13 [E,K/128,2I] and offsets [E+1] must match a [*,K]")
     if a_scale.numel() != a.shape[0]:
         raise ValueError("a_scale must have one entry per row of a")
     I = N2 // 2
@@ -435,12 +444,11 @@ def w4a8_moe_grouped_gemm_swiglu_i8(a: torch.Tensor, a_scale: torch.Tensor, a_ro
         if a_rows.numel() < M_total:
             raise ValueError("a_rows must hold M_total entries")
     _need(offsets, "offsets", torch.int32, 1, dev)
-    _need(w13, "w13", torch.int32, 3, dev)
+    E, N2, KW = _int4_storage(w13, "w13", dev)
     _need(s13, "s13", torch.float32, 2, dev)
-    E, N2, KW = w13.shape
     K = a.shape[1]
-    if N2 % 2 or KW * 8 != K or tuple(s13.shape) != (E, N2) or offsets.numel() != E + 1:
-        raise ValueError("w13 [E,2I,K/8], s13 [E,2I] and offsets [E+1] must match a [*,K]")
+    if N2 % 2 or KW != K or tuple(s13.shape) != (E, N2) or offsets.numel() != E + 1:
+        raise ValueError("w13 [E,2I/16,K/128,16,16], s13 [E,2I] and offsets [E+1] must match a [*,K]")
     I = N2 // 2
     act, act_pmax = _act_out(M_total, I, dev, act, act_pmax)
     _check("w4a8_moe_grouped_gemm_swiglu_i8",
@@ -515,6 +523,35 @@ def w4a8_moe_quantize_weights_mxfp4(w: torch.Tensor, w_packed=None, w_scale=None
     _check("w4a8_moe_quantize_weights_mxfp4",
            lib().w4a8_moe_quantize_weights_mxfp4(_p(w), rows, K, _p(w_packed), _p(w_scale), _stream(dev)))
     return w_packed, w_scale
+
+
+def w4a8_moe_prepack_int4(w_packed: torch.Tensor, w_scale: torch.Tensor | None = None, w_blk=None, s_blk=None):
+    """Row-major INT4 experts (int32 [E, N, K/8], group scales fp32 [E, N, K/128] or None for per-channel
+    scales) -> the GEMM storage (w_blk int32 [E, N/16, K/128, 16, 16], s_blk fp32 [E, K/128, N] or None)."""
+    _need(w_packed, "w_packed", torch.int32, 3)
+    dev = w_packed.device
+    E, N, KW = w_packed.shape
+    K = 8 * KW
+    if N % 16 or K % 128:
+        raise ValueError("w_packed must be [E, N, K/8] with N % 16 == 0 and K % 128 == 0")
+    G = K // 128
+    w_blk = torch.empty((E, N // 16, G, 16, 16), dtype=torch.int32, device=dev) if w_blk is None else w_blk
+    _need(w_blk, "w_blk", torch.int32, 5, dev)
+    if tuple(w_blk.shape) != (E, N // 16, G, 16, 16):
+        raise ValueError("w_blk must be [E, N/16, K/128, 16, 16]")
+    if w_scale is not None:
+        _need(w_scale, "w_scale", torch.float32, 3, dev)
+        if tuple(w_scale.shape) != (E, N, G):
+            raise ValueError("w_scale must be [E, N, K/128]")
+        s_blk = torch.empty((E, G, N), dtype=torch.float32, device=dev) if s_blk is None else s_blk
+        _need(s_blk, "s_blk", torch.float32, 3, dev)
+        if tuple(s_blk.shape) != (E, G, N):
+            raise ValueError("s_blk must be [E, K/128, N]")
+    else:
+        s_blk = None
+    _check("w4a8_moe_prepack_int4",
+           lib().w4a8_moe_prepack_int4(_p(w_packed), _p(w_scale), E, N, K, _p(w_blk), _p(s_blk), _stream(dev)))
+    return w_blk, s_blk
 
 
 def w4a8_moe_prepack_mxfp4(w_packed: torch.Tensor, w_scale: torch.Tensor, w_blk=None, s_blk=None):

@@ -45,6 +45,12 @@ def bf16_to_dev(bits: np.ndarray) -> torch.Tensor:
     return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(DEV).view(torch.bfloat16)
 
 
+def prepack_int4(w: np.ndarray, s: np.ndarray | None = None):
+    """Device copies of row-major INT4 experts (and group scales) in the GEMM storage, through the library."""
+    from quantized_grouped_gemm_token_amd import ops
+    return ops.w4a8_moe_prepack_int4(to_dev(w), None if s is None else to_dev(s))
+
+
 def host(t: torch.Tensor) -> np.ndarray:
     torch.cuda.synchronize()
     if t.dtype == torch.bfloat16:

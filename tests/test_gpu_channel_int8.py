@@ -11,7 +11,7 @@ import pytest
 import torch
 
 import oracle
-from gpu_util import assert_float_parity, bf16_to_dev, host, say, to_dev
+from gpu_util import assert_float_parity, bf16_to_dev, host, prepack_int4, say, to_dev
 from quantized_grouped_gemm_token_amd import ops, workloads
 from quantized_grouped_gemm_token_amd.layer import W4A8MoEChannel
 
@@ -69,7 +69,7 @@ def _gemm(codes, scale, rowsum, rows, offsets, words, ws, algo):
     R = int(offsets[-1])
     out = ops.w4a8_moe_grouped_gemm_i8(to_dev(codes), to_dev(scale), to_dev(rowsum),
                                        to_dev(rows) if rows is not None else None, to_dev(offsets),
-                                       to_dev(words), to_dev(ws), M_total=R, algo=algo)
+                                       prepack_int4(words)[0], to_dev(ws), M_total=R, algo=algo)
     return host(out)
 
 
@@ -106,7 +106,7 @@ def test_grouped_gemm_swiglu_i8(E, I, K, counts, gather, algo, rng):
     say(f"grouped_gemm_swiglu_i8 E={E} I={I} K={K} counts={counts} algo={algo}")
     act, pmax = ops.w4a8_moe_grouped_gemm_swiglu_i8(
         to_dev(codes), to_dev(scale), to_dev(rowsum), to_dev(rows) if rows is not None else None, to_dev(offsets),
-        to_dev(words), to_dev(ws), R, algo=algo)
+        prepack_int4(words)[0], to_dev(ws), R, algo=algo)
     act, pmax = host(act), host(pmax)
     # the GEMM values differ from the oracle's by the rounding of the scale product only
     assert_float_parity(act, want, "grouped_gemm_swiglu_i8", fro_tight=1e-5)

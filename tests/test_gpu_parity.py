@@ -13,7 +13,7 @@ import torch
 
 import oracle
 from gpu_util import (GEMM_FRO_TIGHT, assert_float_parity, bf16_to_dev, edge_shape_maxrel, host, near_midpoint,
-                      say, to_dev, valid_code_choice)
+                      prepack_int4, say, to_dev, valid_code_choice)
 from quantized_grouped_gemm_token_amd import ops, workloads
 from quantized_grouped_gemm_token_amd.layer import W4A8MoE
 
@@ -109,6 +109,22 @@ def test_permute_empty():
 
 
 # --------------------------------------------------------------- steps 4/6
+@pytest.mark.parametrize("E,N,K,scales", [(1, 16, 128, True), (3, 64, 384, True), (2, 48, 256, False),
+                                          (2, 4096, 6144, True)])
+def test_prepack_int4(E, N, K, scales, rng):
+    w = rng.integers(0, 2**32, size=(E, N, K // 8), dtype=np.uint32).view(np.int32)
+    s = rng.standard_normal((E, N, K // 128)).astype(np.float32) if scales else None
+    say(f"prepack_int4 E={E} N={N} K={K} scales={scales}")
+    wb, sb = prepack_int4(w, s)
+    G = K // 128
+    # GEMM storage: [E][N/16][G][16][16] words, [E][G][N] scales
+    assert np.array_equal(host(wb), w.reshape(E, N // 16, 16, G, 16).transpose(0, 1, 3, 2, 4))
+    if scales:
+        assert np.array_equal(host(sb).view(np.uint32), s.transpose(0, 2, 1).view(np.uint32))
+    else:
+        assert sb is None
+
+
 def _gemm_problem(rng, E, N, K, counts, src_rows=None):
     w = rng.integers(0, 2**32, size=(E, N, K // 8), dtype=np.uint32).view(np.int32)
     s = rng.lognormal(-4, 0.5, size=(E, N, K // 128)).astype(np.float32)
@@ -136,7 +152,7 @@ def test_grouped_gemm(E, N, K, counts, gather, algo, rng):
     M = int(offsets[-1])
     say(f"grouped_gemm E={E} N={N} K={K} counts={counts} gather={gather} algo={algo}")
     out = ops.w4a8_moe_grouped_gemm(to_dev(a), to_dev(sa), None if rows is None else to_dev(rows), to_dev(offsets),
-                                    to_dev(w), to_dev(s), M, algo=algo)
+                                    *prepack_int4(w, s), M, algo=algo)
     assert_float_parity(host(out), want, "grouped_gemm", fro_tight=GEMM_FRO_TIGHT)
 
 
@@ -152,8 +168,8 @@ def test_grouped_gemm_exact_integers(algo, rng):
     offsets = np.array([0, 10, M], np.int32)
     want = oracle.grouped_gemm(codes, np.ones(M, np.float32), None, offsets, w, s)
     say(f"grouped_gemm exact integers algo={algo}")
-    out = ops.w4a8_moe_grouped_gemm(to_dev(codes), to_dev(np.ones(M, np.float32)), None, to_dev(offsets), to_dev(w),
-                                    to_dev(s), M, algo=algo)
+    out = ops.w4a8_moe_grouped_gemm(to_dev(codes), to_dev(np.ones(M, np.float32)), None, to_dev(offsets),
+                                    *prepack_int4(w, s), M, algo=algo)
     assert np.array_equal(host(out), want)
 
 
@@ -185,14 +201,15 @@ def test_grouped_gemm_swiglu(E, I, K, counts, gather, algo, rng):
     want = oracle.swiglu_f32(h)
     M = int(offsets[-1])
     say(f"grouped_gemm_swiglu E={E} I={I} K={K} counts={counts} gather={gather} algo={algo}")
+    wb, sb = prepack_int4(w, s)
     act, pmax = ops.w4a8_moe_grouped_gemm_swiglu(to_dev(a), to_dev(sa), None if rows is None else to_dev(rows),
-                                                 to_dev(offsets), to_dev(w), to_dev(s), M, algo=algo)
+                                                 to_dev(offsets), wb, sb, M, algo=algo)
     act, pmax = host(act), host(pmax)
     assert_float_parity(act, want, "grouped_gemm_swiglu", fro_tight=GEMM_FRO_TIGHT)
     _check_pmax(pmax, act)
     # the codes of the fused path against the unfused one on the same inputs
     out = ops.w4a8_moe_grouped_gemm(to_dev(a), to_dev(sa), None if rows is None else to_dev(rows), to_dev(offsets),
-                                    to_dev(w), to_dev(s), M, algo=algo)
+                                    wb, sb, M, algo=algo)
     q_ref, s_ref = ops.w4a8_moe_swiglu(out)
     q, sq = ops.w4a8_moe_requant(to_dev(act), to_dev(pmax))
     q, sq, q_ref, s_ref = host(q), host(sq), host(q_ref), host(s_ref)
