@@ -12,6 +12,11 @@ headline metric is quoted on; --config 3 runs the 8K-token prefill.
 Prints ONE JSON line: layer tokens/s, the roofline of the dominant kernel
 (the gate/up grouped GEMM, timed with events on its own stream), and the CPU
 oracle timed on a bounded sample of the same workload.
+
+The step is timed twice over K steps: launched kernel by kernel with events
+around each kernel (the per-kernel times and the roofline's launch duration),
+and replayed from a HIP graph of the same step (one launch per step: the
+headline value; --no-graph reports the eager rate instead).
 """
 from __future__ import annotations
 
@@ -174,6 +179,8 @@ def main() -> int:
                          "token; mxfp4: MXFP4 group-32 x FP8 per token")
     ap.add_argument("--op", choices=("layer", "wquant"), default="layer",
                     help="layer: the MoE layer (default); wquant: the offline INT4 weight quantizer")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="report the eager (kernel-by-kernel) step rate as the value instead of the graph replay")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="instead of the layer, run a plain device copy of this many bytes (5 times): the "
                          "reference for scaling HBM byte counters")
@@ -245,10 +252,23 @@ def main() -> int:
         moe(x, logits, y, events=evs[i])
     stop.record(stream)
     torch.cuda.synchronize()
-    total_ms = start.elapsed_time(stop)
-    ms_step = total_ms / args.steps
+    eager_ms = start.elapsed_time(stop) / args.steps
     per_step = {s: float(np.mean([e[s][0].elapsed_time(e[s][1]) for e in evs])) for s in steps}
     log("per step ms: " + ", ".join(f"{k}={v:.4f}" for k, v in per_step.items()))
+
+    # the same step replayed from a HIP graph: W untimed replays, then exactly K timed ones
+    graph = moe.capture(x, logits, y)
+    for _ in range(args.warmup):
+        graph.replay()
+    torch.cuda.synchronize()
+    start.record(stream)
+    for _ in range(args.steps):
+        graph.replay()
+    stop.record(stream)
+    torch.cuda.synchronize()
+    graph_ms = start.elapsed_time(stop) / args.steps
+    log(f"step: eager {eager_ms:.4f} ms, graph replay {graph_ms:.4f} ms")
+    ms_step = eager_ms if args.no_graph else graph_ms
 
     # algorithmic work of the routed experts actually touched
     offsets = moe.buffers(sh.T)["offsets"].cpu().numpy()
@@ -313,6 +333,8 @@ def main() -> int:
                                              "mxfp4": "mxfp4 g32 x fp8", "g128": "int4 g128 x fp8"}[args.scheme]},
         "roofline": roof, "cpu_baseline": cpu, "gemms": gemms,
         "step_ms": {k: round(v, 5) for k, v in per_step.items()},
+        "launch": "eager" if args.no_graph else "hip graph replay",
+        "eager_ms_per_step": round(eager_ms, 5), "graph_ms_per_step": round(graph_ms, 5),
         "device": torch.cuda.get_device_name(0), "kernel_sources_hash": khash,
     }
     print(json.dumps(line), flush=True)

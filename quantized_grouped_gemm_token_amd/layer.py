@@ -18,6 +18,9 @@ codes uint8 [E][N][K/2], E8M0 scales uint8 [E][N][K/32]) and uses the same
 FP8 activations.
 Intermediate buffers are allocated once per token count and reused, so a
 forward pass enqueues kernels only: no allocation, no host synchronisation.
+That also makes a step capturable: capture() records one forward into a HIP
+graph, whose replay re-runs the whole step on the current contents of the
+same x, logits and y tensors with a single launch.
 """
 from __future__ import annotations
 
@@ -110,6 +113,22 @@ class W4A8MoE:
         return step("unpermute", ops.w4a8_moe_unpermute, b["o"], b["inv_pos"], b["w"], y, y_dtype)
 
     __call__ = forward
+
+    def capture(self, x: torch.Tensor, logits: torch.Tensor, y: torch.Tensor,
+                y_dtype: torch.dtype = torch.float32, algo: int = ops.W4A8_GG_AUTO) -> torch.cuda.CUDAGraph:
+        """Record one forward on these tensors into a HIP graph and return it.
+
+        One eager forward runs first (it allocates the per-T buffers, which the
+        captured kernels then use); g.replay() then runs the step again on the
+        tensors' current contents.  The step enqueues no memset and no copy,
+        so the graph holds kernel nodes only."""
+        self.forward(x, logits, y, y_dtype=y_dtype, algo=algo)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            self.forward(x, logits, y, y_dtype=y_dtype, algo=algo)
+        torch.cuda.synchronize()
+        return g
 
 
 class W4A8MoEChannel(W4A8MoE):
