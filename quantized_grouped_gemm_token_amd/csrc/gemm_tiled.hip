@@ -1,11 +1,15 @@
 // Grouped W4A8 GEMM, tiled form: for many rows per expert (prefill).
 //
 // A persistent kernel (one workgroup of 8 waves per CU) walks the ragged
-// list of tiles of all experts.  An expert's rows are cut into square tiles
-// of up to 256 rows x 256 output columns, except a remainder of at most 128
-// rows, which gets wide tiles of 128 rows x 512 columns instead: half as many
-// tiles for the same weight bytes, so a short remainder costs about half as
-// much as it would in square tiles.
+// list of tiles of all experts.  An expert with more than 128 rows is cut into
+// n = ceil(rows / 256) square tiles of equal height (rows / n, rounded) x 256
+// output columns; one with at most 128 rows gets wide tiles of 128 rows x 512
+// columns instead (half as many tiles for the same weight bytes).  Equal
+// heights matter: the tiles that read the same weight columns, or the same
+// activation rows, run at the same speed and stay in step through K, so the
+// XCD's L2 serves the shared bytes to all of them.  With a full tile and a
+// short remainder tile the remainder ran ahead, and its weight reads, then the
+// full tile's, missed the L2 (2.4 GB more L2 misses per prefill launch).
 //   square: wave w = 4 rg + cg owns the columns 64 cg .. +63 and the 16-row
 //           A blocks rg, rg + 2, .., rg + 14 (interleaved, so that a short
 //           tile still splits its rows over both row groups);
@@ -25,7 +29,7 @@
 // Within a group the products are software-pipelined over the A blocks:
 // the MFMAs of block i are issued between the group-scale FMAs of block i - 1
 // (acc += s * D, one FMA per output), and the LDS reads of block i + 1 are in
-// flight meanwhile.  The tile body is compiled for 0, 1, 2, 4 and 8 blocks per
+// flight meanwhile.  The tile body is compiled for 0, 1, 2 and 4 to 8 blocks per
 // wave, so that the hot loop has no per-block branches.
 //
 // The +8 offset of the uint4b8 nibbles is removed with the per-row sums of
@@ -133,11 +137,11 @@ __device__ __forceinline__ T lds_load(const void* p) {
   return *reinterpret_cast<const T*>(__builtin_assume_aligned(p, 16));
 }
 
-// tiles of an expert with `rows` rows: square tiles per 256-column block (the
-// full 256-row blocks, and a remainder above 128 rows), plus one wide tile per
-// 512 columns for a remainder of 1..128 rows
-__device__ __forceinline__ int square_mblocks(int rows) { return rows / kTM + (rows % kTM > kWideRows ? 1 : 0); }
-__device__ __forceinline__ int has_wide(int rows) { return (rows % kTM != 0 && rows % kTM <= kWideRows) ? 1 : 0; }
+// tiles of an expert with `rows` rows: more than 128 rows, ceil(rows / 256)
+// square tiles of equal height per 256-column block; 1..128 rows, one wide
+// tile per 512 columns
+__device__ __forceinline__ int square_mblocks(int rows) { return rows > kWideRows ? (rows + kTM - 1) / kTM : 0; }
+__device__ __forceinline__ int has_wide(int rows) { return (rows > 0 && rows <= kWideRows) ? 1 : 0; }
 __device__ __forceinline__ int tiles_of(int rows, int nb, int nw) {
   return square_mblocks(rows) * nb + has_wide(rows) * nw;
 }
@@ -250,21 +254,23 @@ __global__ __launch_bounds__(kThreads, 1) void gg_tiled_kernel(const uint8_t* __
     bool is_wide;
     int r0, mlen, n0;
     if (rp < msq || (2 * pair + 1 < NB && rp < 2 * msq)) {
+      // square tile mb of msq: rows_e / msq rows, the first rows_e % msq tiles one more
       const int nb = rp < msq ? 2 * pair : 2 * pair + 1;
       const int mb = rp < msq ? rp : rp - msq;
+      const int base = rows_e / msq, extra = rows_e - base * msq;
       is_wide = false;
-      r0 = r_e + mb * kTM;
-      mlen = min(kTM, rows_e - mb * kTM);
+      r0 = r_e + mb * base + min(mb, extra);
+      mlen = base + (mb < extra ? 1 : 0);
       n0 = nb * kTN;
     } else {
       is_wide = true;
-      r0 = r_e + (rows_e / kTM) * kTM;
-      mlen = rows_e % kTM;
+      r0 = r_e;
+      mlen = rows_e;
       n0 = pair * kWideCols;
     }
 
     // The rest of the tile (K loop and epilogue) is compiled per tile shape
-    // and per number kNB of A blocks of the wave (0, 1, 2, 4 or 8), without
+    // and per number kNB of A blocks of the wave (0, 1, 2, 4, 5, 6, 7 or 8), without
     // branches between the blocks; a wave with nact blocks holding rows runs
     // the smallest kNB >= nact (the blocks past nact multiply clamped rows,
     // which the epilogue drops).
@@ -564,8 +570,9 @@ __global__ __launch_bounds__(kThreads, 1) void gg_tiled_kernel(const uint8_t* __
     // A blocks of this wave holding rows: wide tiles ceil(mlen / 16) (every
     // wave), square tiles those of rg + 2 i < ceil(mlen / 16); none if the
     // wave's 64 columns are past N (N % 64 == 0: a column group is wholly in
-    // or out).  A square tile has more than 128 rows, so each of its waves
-    // with columns has 4 to 8 blocks.
+    // or out).  A square tile has at least 128 rows, so each of its waves
+    // with columns has 4 to 8 blocks (a variant for each count: two tiles of
+    // an expert with 257..384 rows then cost what a full and a remainder tile did).
     const int mb16 = (mlen + 15) >> 4;
     if (is_wide) {
       const int nact = __builtin_amdgcn_readfirstlane(n0 + 64 * wave < N ? min(kABlocks, mb16) : 0);
@@ -577,7 +584,10 @@ __global__ __launch_bounds__(kThreads, 1) void gg_tiled_kernel(const uint8_t* __
     } else {
       const int rg = wave >> 2, cg = wave & 3;
       const int nact = __builtin_amdgcn_readfirstlane(n0 + 64 * cg < N ? min(kABlocks, (mb16 - rg + 1) >> 1) : 0);
-      if (nact > 4) run_tile(std::false_type{}, std::integral_constant<int, 8>{});
+      if (nact > 7) run_tile(std::false_type{}, std::integral_constant<int, 8>{});
+      else if (nact == 7) run_tile(std::false_type{}, std::integral_constant<int, 7>{});
+      else if (nact == 6) run_tile(std::false_type{}, std::integral_constant<int, 6>{});
+      else if (nact == 5) run_tile(std::false_type{}, std::integral_constant<int, 5>{});
       else if (nact > 0) run_tile(std::false_type{}, std::integral_constant<int, 4>{});
       else run_tile(std::false_type{}, std::integral_constant<int, 0>{});
     }

@@ -99,13 +99,14 @@ def _gemm(w, s, offsets, a, sa, rows, algo):
     (8, 512, 640, [16, 16, 16, 16, 0, 15, 17, 1], False),
     (3, 320, 256, [200, 241, 0], True),            # partial tiles; N not a multiple of 256
     (1, 768, 6144, [130], False),                  # a wide tile half past N, long K
+    (4, 256, 256, [128, 129, 257, 513], False),    # square tiles of equal height: 1, 2 and 3 per expert
 ])
 def test_grouped_gemm_mxfp4(E, N, K, counts, gather, algo, rng):
     w, s, offsets, a, sa, rows = _problem(rng, E, N, K, counts, src_rows=40 if gather else None)
     want = mx.grouped_gemm_mxfp4(a, sa, rows, offsets, w, s)
     say(f"grouped_gemm_mxfp4 E={E} N={N} K={K} counts={counts} gather={gather} algo={algo}")
     got = _gemm(w, s, offsets, a, sa, rows, algo)
-    assert_float_parity(got, want, "grouped_gemm_mxfp4", fro_tight=GEMM_FRO_TIGHT)
+    assert_float_parity(got, want, "grouped_gemm_mxfp4", fro_tight=GEMM_FRO_TIGHT, maxrel=edge_shape_maxrel(N))
 
 
 @pytest.mark.parametrize("algo", ALGOS)
@@ -142,7 +143,7 @@ def test_grouped_gemm_swiglu_mxfp4(E, I, K, counts, gather, algo, rng):
     act, pmax = ops.w4a8_moe_grouped_gemm_swiglu_mxfp4(to_dev(a), to_dev(sa), None if rows is None else to_dev(rows),
                                                        to_dev(offsets), wb, sb, M, algo=algo)
     act, pmax = host(act), host(pmax)
-    assert_float_parity(act, want, "grouped_gemm_swiglu_mxfp4", fro_tight=GEMM_FRO_TIGHT)
+    assert_float_parity(act, want, "grouped_gemm_swiglu_mxfp4", fro_tight=GEMM_FRO_TIGHT, maxrel=edge_shape_maxrel(I))
     row = np.abs(act).max(axis=1)
     assert pmax.shape == (M, I // 64)
     assert np.array_equal(pmax.max(axis=1), row)

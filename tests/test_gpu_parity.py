@@ -145,6 +145,8 @@ def _gemm_problem(rng, E, N, K, counts, src_rows=None):
     (2, 64, 1024, [300, 33], True),
     (8, 512, 640, [16, 16, 16, 16, 0, 15, 17, 1], False),
     (3, 320, 256, [200, 241, 0], True),            # partial tiles of 7/8 row blocks; N not a multiple of 256
+    (4, 256, 256, [128, 129, 257, 513], False),    # square tiles of equal height: 1, 2 and 3 per expert
+    (2, 512, 384, [512, 769], True),
 ])
 def test_grouped_gemm(E, N, K, counts, gather, algo, rng):
     w, s, offsets, a, sa, rows = _gemm_problem(rng, E, N, K, counts, src_rows=40 if gather else None)
@@ -153,7 +155,7 @@ def test_grouped_gemm(E, N, K, counts, gather, algo, rng):
     say(f"grouped_gemm E={E} N={N} K={K} counts={counts} gather={gather} algo={algo}")
     out = ops.w4a8_moe_grouped_gemm(to_dev(a), to_dev(sa), None if rows is None else to_dev(rows), to_dev(offsets),
                                     *prepack_int4(w, s), M, algo=algo)
-    assert_float_parity(host(out), want, "grouped_gemm", fro_tight=GEMM_FRO_TIGHT)
+    assert_float_parity(host(out), want, "grouped_gemm", fro_tight=GEMM_FRO_TIGHT, maxrel=edge_shape_maxrel(N))
 
 
 @pytest.mark.parametrize("algo", ALGOS)
@@ -205,7 +207,7 @@ def test_grouped_gemm_swiglu(E, I, K, counts, gather, algo, rng):
     act, pmax = ops.w4a8_moe_grouped_gemm_swiglu(to_dev(a), to_dev(sa), None if rows is None else to_dev(rows),
                                                  to_dev(offsets), wb, sb, M, algo=algo)
     act, pmax = host(act), host(pmax)
-    assert_float_parity(act, want, "grouped_gemm_swiglu", fro_tight=GEMM_FRO_TIGHT)
+    assert_float_parity(act, want, "grouped_gemm_swiglu", fro_tight=GEMM_FRO_TIGHT, maxrel=edge_shape_maxrel(I))
     _check_pmax(pmax, act)
     # the codes of the fused path against the unfused one on the same inputs
     out = ops.w4a8_moe_grouped_gemm(to_dev(a), to_dev(sa), None if rows is None else to_dev(rows), to_dev(offsets),
