@@ -107,6 +107,63 @@ def cpu_baseline(wl, n_tokens: int, scheme: str = "g128") -> dict:
                       f"'{wl.shape.name}', touching {touched} experts; {dt:.1f} s wall"}
 
 
+def bench_wquant_mxfp4(args, log) -> int:
+    """The MXFP4 quantizer on the gate/up weights of 16 experts (fp32 [16, 4096, 6144]): HBM-bound."""
+    import torch
+
+    from quantized_grouped_gemm_token_amd import ops
+
+    E, N, K = 16, 4096, 6144
+    gen = torch.Generator(device="cuda:0").manual_seed(1234)
+    w = torch.randn((E, N, K), generator=gen, device="cuda:0", dtype=torch.float32) * 0.02
+    packed = torch.empty((E, N, K // 2), dtype=torch.uint8, device="cuda:0")
+    scales = torch.empty((E, N, K // 32), dtype=torch.uint8, device="cuda:0")
+    for _ in range(max(args.warmup, 1)):
+        ops.w4a8_moe_quantize_weights_mxfp4(w, packed, scales)
+    stream = torch.cuda.current_stream()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        ops.w4a8_moe_quantize_weights_mxfp4(w, packed, scales)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / args.steps
+    in_bytes = w.numel() * 4
+    moved = in_bytes + packed.numel() + scales.numel()          # 4 + 1/2 + 1/32 bytes per weight
+    log(f"quantize mxfp4 {E}x{N}x{K}: {ms:.3f} ms")
+    cpu = None
+    if args.cpu_tokens > 0:
+        from oracle import mxfp4_oracle
+        try:
+            from threadpoolctl import threadpool_limits
+            limit = threadpool_limits(limits=1)
+        except Exception:   # pragma: no cover
+            limit = None
+        n_rows = 1024
+        sample = w[0, :n_rows].cpu().numpy()
+        t0 = time.perf_counter()
+        mxfp4_oracle.quantize_mxfp4(sample)
+        dt = time.perf_counter() - t0
+        if limit is not None:
+            limit.restore_original_limits()
+        cpu = {"value": round(n_rows * K * 4 / dt / 1e9, 4), "unit": "GB/s of fp32 weights", "cores": 1,
+               "kind": "oracle", "sample": f"oracle MXFP4 quantizer on {n_rows} rows x {K} of the same weights; "
+                                           f"{dt:.1f} s wall"}
+    achieved = moved / ms / 1e6
+    line = {"metric": "MXFP4 g32 weight quantizer GB/s of fp32 weights", "value": round(in_bytes / ms / 1e6, 1),
+            "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+            "dtype": "f32 in, e2m1 + e8m0 out", "data": "synthetic (seeded N(0, 0.02))",
+            "config": {"workload": f"gate/up weights of {E} experts [{E}, {N}, {K}]"},
+            "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                         "note": "algorithmic bytes: 4 read + 0.5 + 1/32 written per weight"},
+            "cpu_baseline": cpu}
+    print(json.dumps(line), flush=True)
+    return 0
+
+
 def bench_wquant(args, log) -> int:
     """The weight quantizer on the gate/up weights of 16 experts (fp32 [16, 4096, 6144])."""
     import torch
@@ -178,7 +235,8 @@ def main() -> int:
                     help="g128: INT4 group-128 x FP8 per token (default); channel: per-channel INT4 x INT8 per "
                          "token; mxfp4: MXFP4 group-32 x FP8 per token")
     ap.add_argument("--op", choices=("layer", "wquant"), default="layer",
-                    help="layer: the MoE layer (default); wquant: the offline INT4 weight quantizer")
+                    help="layer: the MoE layer (default); wquant: the offline weight quantizer (INT4 group 128, "
+                         "or MXFP4 with --scheme mxfp4)")
     ap.add_argument("--no-graph", action="store_true",
                     help="report the eager (kernel-by-kernel) step rate as the value instead of the graph replay")
     ap.add_argument("--copy-bytes", type=int, default=0,
@@ -215,7 +273,7 @@ def main() -> int:
         print("bench.py: cuda:0 is not a gfx950: " + ops.last_error(), file=sys.stderr)
         return 1
     if args.op == "wquant":
-        return bench_wquant(args, log)
+        return bench_wquant_mxfp4(args, log) if args.scheme == "mxfp4" else bench_wquant(args, log)
     dev = "cuda:0"
     t0 = time.time()
     wl = workloads.make_config(args.config)
