@@ -286,8 +286,12 @@ __global__ __launch_bounds__(kThreads, 1) void gg_tiled_kernel(const uint8_t* __
       constexpr int kBlockStride = kWide ? 16 : 32;        // rows between a wave's A blocks
       const int rg = kWide ? 0 : wave >> 2;                // row group (its first A block)
       const int cg = kWide ? wave : wave & 3;              // column group (64 columns)
-      // this wave's group scales: columns 64 wave + lane (FP8 form; square tiles: waves 0..3)
-      const bool scale_loader = !kInt8 && (kWide || wave < 4);
+      // this wave's group scales: columns 64 sw + lane (the per-group forms).  Square
+      // tiles have 256 columns: waves 4..7 repeat the loads of waves 0..3 (the same
+      // bytes to the same LDS words), so that every wave issues the same loads per
+      // stage and the K loop waits with one constant count, without branches.
+      constexpr bool kScales = !kInt8;
+      const int sw = kWide ? wave : (wave & 3);
 
       // ---- direct-load roles of this lane
       // activations: rows kARows wave + 8 q + lane / 8, chunk position lane % 8
@@ -312,7 +316,7 @@ __global__ __launch_bounds__(kThreads, 1) void gg_tiled_kernel(const uint8_t* __
       const uint32_t woff = (uint32_t)(lane >> 2) * 64u + 16u * (uint32_t)((lane & 3) ^ ((lane >> 4) & 3));
       // group scales: the words of group g of all N columns are contiguous
       const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(w_scale + (int64_t)e * N * G, (uint32_t)(N * G * 4));
-      const int scol = min(n0 + 64 * wave + lane, (int)N - 1);
+      const int scol = min(n0 + 64 * sw + lane, (int)N - 1);
       const uint32_t soff = (uint32_t)(kSwiglu ? gate_up_row(scol, half) : scol) * 4u;
       const uint32_t sstep = (uint32_t)N * 4u;    // scale offset step per group
 
@@ -320,7 +324,7 @@ __global__ __launch_bounds__(kThreads, 1) void gg_tiled_kernel(const uint8_t* __
       auto stage = [&](auto S_, int g) {
         constexpr int S = decltype(S_)::value;
         RingSlot& sl = slot<S>(ring0, ring1, ring2);
-        if (scale_loader) dma4(rs, soff, (uint32_t)g * sstep, &slot<S>(sc0, sc1, sc2)[64 * wave]);
+        if constexpr (kScales) dma4(rs, soff, (uint32_t)g * sstep, &slot<S>(sc0, sc1, sc2)[64 * sw]);
 #pragma unroll
         for (int q = 0; q < kALoads; ++q)
           dma16(ra, aoff[q], (uint32_t)g * kGroup, &sl.b[(kARows * wave + 8 * q) * kGroup]);
@@ -333,10 +337,9 @@ __global__ __launch_bounds__(kThreads, 1) void gg_tiled_kernel(const uint8_t* __
       };
       // wait until only the loads of the group issued last are in flight
       auto wait_last_stage = [&]() {
-        constexpr int kBase = kALoads + kWLoads;
-        static_assert(kBase + 1 <= 15, "vmcnt field");
-        if (scale_loader) __builtin_amdgcn_s_waitcnt(0x0F70 | (kBase + 1));
-        else __builtin_amdgcn_s_waitcnt(0x0F70 | kBase);
+        constexpr int kStage = kALoads + kWLoads + (kScales ? 1 : 0);   // loads per stage
+        static_assert(kStage <= 15, "vmcnt field");
+        __builtin_amdgcn_s_waitcnt(0x0F70 | kStage);
       };
       // -2^-6 * (sum of the activation codes) of this wave's rows for the group in slot S
       auto row_sums = [&](auto S_, int g) {
@@ -364,11 +367,14 @@ __global__ __launch_bounds__(kThreads, 1) void gg_tiled_kernel(const uint8_t* __
 
       // One K group in slot S: prefetch group g+2; multiply group g; in the
       // middle, once this wave's loads of group g+1 have landed, publish that
-      // group's row sums; then one barrier.
-      auto step = [&](auto S_, int g) {
+      // group's row sums; then one barrier.  kMore: groups g+1 and g+2 exist (the
+      // main part of the K loop), so the step has no branches: with a branch around
+      // the middle wait, the compiler moved the first half's products below it.
+      auto step = [&](auto S_, auto M_, int g) {
         constexpr int S = decltype(S_)::value;
-        if (g >= G) return;
-        const bool more = g + 2 < G;
+        constexpr bool kMore = decltype(M_)::value;
+        if (!kMore && g >= G) return;
+        const bool more = kMore || g + 2 < G;
         // scales of group g (MX: the E8M0 byte of the lane's K quarter, in byte 0)
         float s[kBBlocks];
         int sb[kBBlocks];
@@ -387,7 +393,7 @@ __global__ __launch_bounds__(kThreads, 1) void gg_tiled_kernel(const uint8_t* __
         auto mid = [&]() {
           if (more) wait_last_stage();
           else __builtin_amdgcn_s_waitcnt(0x0F70);              // vmcnt(0)
-          if (!kInt8 && !kMx && g + 1 < G) row_sums(std::integral_constant<int, (S + 1) % 3>{}, g + 1);
+          if (!kInt8 && !kMx && (kMore || g + 1 < G)) row_sums(std::integral_constant<int, (S + 1) % 3>{}, g + 1);
         };
         // the products of this group: kNB A blocks x kBBlocks B blocks
         auto compute = [&]() {
@@ -496,10 +502,27 @@ __global__ __launch_bounds__(kThreads, 1) void gg_tiled_kernel(const uint8_t* __
         if constexpr (kInt8) dma4(buffer_rsrc(a_rowsum, 0xffffffffu), asrc, 0, &rowsum_sm[64 * wave]);
       }
 
-      for (int g = 0; g < G; g += 3) {
-        step(std::integral_constant<int, 0>{}, g);
-        step(std::integral_constant<int, 1>{}, g + 1);
-        step(std::integral_constant<int, 2>{}, g + 2);
+      // MX and INT8 forms: three steps at a time while every step has a next stage,
+      // then the last 2..4 groups (all of them when G < 5), whose slots start again
+      // at 0.  The group-128 form keeps checked steps throughout: with the products
+      // of the first half held before the middle wait it spills inside the K loop.
+      if constexpr (kInt8 || kMx) {
+        int g = 0;
+        for (; g + 5 <= G; g += 3) {
+          step(std::integral_constant<int, 0>{}, std::true_type{}, g);
+          step(std::integral_constant<int, 1>{}, std::true_type{}, g + 1);
+          step(std::integral_constant<int, 2>{}, std::true_type{}, g + 2);
+        }
+        step(std::integral_constant<int, 0>{}, std::false_type{}, g);
+        step(std::integral_constant<int, 1>{}, std::false_type{}, g + 1);
+        step(std::integral_constant<int, 2>{}, std::false_type{}, g + 2);
+        step(std::integral_constant<int, 0>{}, std::false_type{}, g + 3);
+      } else {
+        for (int g = 0; g < G; g += 3) {
+          step(std::integral_constant<int, 0>{}, std::false_type{}, g);
+          step(std::integral_constant<int, 1>{}, std::false_type{}, g + 1);
+          step(std::integral_constant<int, 2>{}, std::false_type{}, g + 2);
+        }
       }
 
       // ---- epilogue: D lane holds column lr of its B block, rows 4 lq .. +3 of its A block
