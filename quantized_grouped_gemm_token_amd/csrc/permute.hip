@@ -4,7 +4,9 @@
 // parallelism is required for W4A8: "GLM-5.3-W4A8" card, sections 性能 and
 // 部署); inside one GPU that dispatch is this permutation.
 //
-// Three launches, all deterministic (no order-dependent atomics):
+// Up to 1024 routed indices (decode batches) take one launch that does all
+// three steps in one block; more take three launches, all deterministic (no
+// order-dependent atomics):
 //   1. count   -- one block per 1024 routed indices: per-expert counts of the
 //                 block, written to counts[e][b];
 //   2. scan    -- one block: exclusive prefix sum over counts in (expert,
@@ -88,21 +90,16 @@ __global__ __launch_bounds__(1024) void permute_scan_kernel(int32_t* __restrict_
   if (tid == 0) offsets[E] = carry_s;
 }
 
-__global__ __launch_bounds__(kPermThreads) void permute_scatter_kernel(const int32_t* __restrict__ ids, int64_t R,
-                                                                        int k, int E, int nblk,
-                                                                        const int32_t* __restrict__ bases,
-                                                                        int32_t* __restrict__ row_token,
-                                                                        int32_t* __restrict__ inv_pos) {
-  __shared__ int run[kPermMaxE];                     // next free row of each expert for this block
-  __shared__ int wcnt[kPermWaves][kPermMaxE];        // per-wave counts of the current round
+// The stable scatter of the kPermBlock indices from `base`: run[e] holds the
+// next free row of expert e for them (advanced here), wcnt is zero.  Rounds of
+// 256 indices in index order; within a round the rank of an index among the
+// round's earlier indices with the same expert comes from ballot-based peer
+// matching inside a wave and per-wave counts across waves.
+__device__ __forceinline__ void permute_scatter_rounds(const int32_t* __restrict__ ids, int64_t R, int k, int E,
+                                                       int64_t base, int* run, int (*wcnt)[kPermMaxE],
+                                                       int32_t* __restrict__ row_token,
+                                                       int32_t* __restrict__ inv_pos) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  for (int e = tid; e < E; e += kPermThreads) {
-    run[e] = bases[(int64_t)e * nblk + blockIdx.x];
-#pragma unroll
-    for (int w = 0; w < kPermWaves; ++w) wcnt[w][e] = 0;
-  }
-  __syncthreads();
-  const int64_t base = (int64_t)blockIdx.x * kPermBlock;
   const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   for (int round = 0; round < kPermBlock / kPermThreads; ++round) {
     const int64_t f = base + (int64_t)round * kPermThreads + tid;   // rounds, then threads: index order
@@ -138,6 +135,70 @@ __global__ __launch_bounds__(kPermThreads) void permute_scatter_kernel(const int
   }
 }
 
+__global__ __launch_bounds__(kPermThreads) void permute_scatter_kernel(const int32_t* __restrict__ ids, int64_t R,
+                                                                        int k, int E, int nblk,
+                                                                        const int32_t* __restrict__ bases,
+                                                                        int32_t* __restrict__ row_token,
+                                                                        int32_t* __restrict__ inv_pos) {
+  __shared__ int run[kPermMaxE];                     // next free row of each expert for this block
+  __shared__ int wcnt[kPermWaves][kPermMaxE];        // per-wave counts of the current round
+  const int tid = threadIdx.x;
+  for (int e = tid; e < E; e += kPermThreads) {
+    run[e] = bases[(int64_t)e * nblk + blockIdx.x];
+#pragma unroll
+    for (int w = 0; w < kPermWaves; ++w) wcnt[w][e] = 0;
+  }
+  __syncthreads();
+  permute_scatter_rounds(ids, R, k, E, (int64_t)blockIdx.x * kPermBlock, run, wcnt, row_token, inv_pos);
+}
+
+// All three steps in one block when R <= kPermBlock (one block of indices):
+// counts in LDS, the exclusive scan over experts (4 consecutive experts per
+// thread, then a wavefront scan and the 4 wave totals), then the scatter.
+__global__ __launch_bounds__(kPermThreads) void permute_small_kernel(const int32_t* __restrict__ ids, int64_t R,
+                                                                      int k, int E,
+                                                                      int32_t* __restrict__ offsets,
+                                                                      int32_t* __restrict__ row_token,
+                                                                      int32_t* __restrict__ inv_pos) {
+  __shared__ int run[kPermMaxE];
+  __shared__ int wcnt[kPermWaves][kPermMaxE];
+  __shared__ int wave_tot[kPermWaves];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  for (int e = tid; e < kPermMaxE; e += kPermThreads) {
+    run[e] = 0;
+#pragma unroll
+    for (int w = 0; w < kPermWaves; ++w) wcnt[w][e] = 0;
+  }
+  __syncthreads();
+  for (int i = tid; i < R; i += kPermThreads) {
+    const int e = ids[i];
+    if ((unsigned)e < (unsigned)E) atomicAdd(&run[e], 1);   // integer counts: order does not matter
+  }
+  __syncthreads();
+  // thread t: experts 4t .. 4t + 3 (counts past E are 0)
+  int c[4], local = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    c[j] = run[4 * tid + j];
+    local += c[j];
+  }
+  const int incl = wave_inclusive_scan(local, lane);
+  if (lane == 63) wave_tot[wave] = incl;
+  __syncthreads();
+  int excl = incl - local;
+  for (int w = 0; w < wave; ++w) excl += wave_tot[w];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int e = 4 * tid + j;
+    if (e < E) offsets[e] = excl;
+    run[e] = excl;                                   // the first row of expert e
+    excl += c[j];
+  }
+  if (tid == kPermThreads - 1) offsets[E] = excl;    // E <= 4 * 256: the last thread ends the scan
+  __syncthreads();
+  permute_scatter_rounds(ids, R, k, E, 0, run, wcnt, row_token, inv_pos);
+}
+
 int64_t permute_workspace_bytes(int64_t R, int E) {
   const int64_t nblk = (R + kPermBlock - 1) / kPermBlock;
   return (nblk > 0 ? nblk : 1) * (int64_t)E * (int64_t)sizeof(int32_t);
@@ -145,6 +206,11 @@ int64_t permute_workspace_bytes(int64_t R, int E) {
 
 hipError_t launch_permute(const int32_t* ids, int64_t R, int k, int E, int32_t* offsets, int32_t* row_token,
                           int32_t* inv_pos, int32_t* counts, hipStream_t stream) {
+  if (R <= kPermBlock) {
+    hipLaunchKernelGGL(permute_small_kernel, dim3(1), dim3(kPermThreads), 0, stream, ids, R, k, E, offsets,
+                       row_token, inv_pos);
+    return hipGetLastError();
+  }
   const int64_t nblk64 = (R + kPermBlock - 1) / kPermBlock;
   const int nblk = (int)(nblk64 > 0 ? nblk64 : 1);
   if (R > 0)

@@ -33,7 +33,7 @@ def _bf16(x32):
 
 
 # ------------------------------------------------------------------ step 1
-@pytest.mark.parametrize("T,H", [(1, 128), (37, 512), (256, 6144)])
+@pytest.mark.parametrize("T,H", [(1, 128), (37, 512), (256, 6144), (3, 16384), (2, 17408)])
 def test_quant_act_i8(T, H, rng):
     x = rng.standard_normal((T, H)).astype(np.float32)
     x[:, rng.choice(H, max(1, H // 100), replace=False)] *= 20.0
@@ -115,7 +115,7 @@ def test_grouped_gemm_swiglu_i8(E, I, K, counts, gather, algo, rng):
     assert np.all(pmax <= np.abs(act).max(axis=1, keepdims=True))
 
 
-@pytest.mark.parametrize("M,I", [(1, 128), (300, 2048)])
+@pytest.mark.parametrize("M,I", [(1, 128), (300, 2048), (3, 8192), (2, 8320)])
 def test_requant_i8(M, I, rng):
     act = (rng.standard_normal((M, I)) * 3.0).astype(np.float32)
     if M > 2:

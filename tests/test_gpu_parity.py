@@ -59,7 +59,7 @@ def test_quant_act_special_values():
     assert np.array_equal(host(sx), want_s)
 
 
-@pytest.mark.parametrize("T,H", [(1, 128), (37, 384), (300, 6144)])
+@pytest.mark.parametrize("T,H", [(1, 128), (37, 384), (300, 6144), (5, 2176), (3, 16384), (2, 17408)])
 def test_quant_act_random(T, H, rng):
     mag = np.exp2(rng.integers(-12, 12, size=(T, 1))).astype(np.float32)
     x = (rng.standard_normal((T, H)).astype(np.float32) * mag)
@@ -75,10 +75,12 @@ def test_quant_act_random(T, H, rng):
 # ------------------------------------------------------------------ step 2
 @pytest.mark.parametrize("T,E,k,renorm", [(1, 8, 8, True), (50, 256, 8, True), (50, 256, 8, False),
                                           (33, 1024, 16, True), (20, 100, 100, True), (7, 65, 3, False),
-                                          (16, 4, 1, True)])
+                                          (16, 4, 1, True), (9, 500, 8, True), (9, 500, 8, False)])
 def test_route(T, E, k, renorm, rng):
     logits = rng.standard_normal((T, E)).astype(np.float32)
     logits[:, 5 % E] = logits[:, 2 % E]                        # forced ties
+    logits[:, 36 % E] = logits[:, 20 % E]                      # ... between lanes of different 16-lane rows
+    logits[:, 67 % E] = logits[:, 3 % E]                       # ... between slots of one lane
     logits[0, :] = np.round(logits[0, :])                     # many ties in one row
     want_ids, want_w = oracle.route(logits, k, renorm)
     say(f"route T={T} E={E} k={k} renorm={renorm}")
@@ -90,7 +92,7 @@ def test_route(T, E, k, renorm, rng):
 
 # ------------------------------------------------------------------ step 3
 @pytest.mark.parametrize("T,E,k", [(16, 8, 2), (128, 256, 8), (3000, 256, 8), (1500, 1024, 8), (700, 3, 2),
-                                   (2048, 256, 8)])
+                                   (2048, 256, 8), (127, 256, 8), (100, 1024, 8), (1, 1024, 1), (129, 256, 8)])
 def test_permute(T, E, k, rng):
     ids = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
     if T == 700:
@@ -220,7 +222,7 @@ def test_grouped_gemm_swiglu(E, I, K, counts, gather, algo, rng):
     assert np.all(near_midpoint(want, s_ref, rel=1e-4)[diff]), f"{int(diff.sum())} codes differ off a midpoint"
 
 
-@pytest.mark.parametrize("M,I", [(1, 128), (37, 256), (500, 2048)])
+@pytest.mark.parametrize("M,I", [(1, 128), (37, 256), (500, 2048), (7, 1152), (3, 8192), (2, 8320)])
 def test_requant(M, I, rng):
     act = (rng.standard_normal((M, I)) * np.exp2(rng.integers(-6, 6, size=(M, 1)))).astype(np.float32)
     if M > 2:
