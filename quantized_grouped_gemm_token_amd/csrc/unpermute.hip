@@ -19,15 +19,26 @@ __global__ __launch_bounds__(256) void unpermute_kernel(const float* __restrict_
   const int64_t col = ((int64_t)blockIdx.y * 256 + threadIdx.x) * 4;
   if (col >= H) return;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int j = 0; j < k; ++j) {
-    const int p = inv_pos[t * k + j];
-    if (p < 0) continue;
-    const float wj = w[t * k + j];
-    const f32x4 v = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(o + (int64_t)p * H + col));
-    acc.x = fmaf(wj, v[0], acc.x);
-    acc.y = fmaf(wj, v[1], acc.y);
-    acc.z = fmaf(wj, v[2], acc.z);
-    acc.w = fmaf(wj, v[3], acc.w);
+  // eight expert rows at a time: all their loads in flight (an unrouted or
+  // missing row loads row 0 and is skipped), then the sums in j order
+  constexpr int kU = 8;
+  for (int j0 = 0; j0 < k; j0 += kU) {
+    int p[kU];
+    f32x4 v[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) p[u] = j0 + u < k ? inv_pos[t * k + j0 + u] : -1;
+#pragma unroll
+    for (int u = 0; u < kU; ++u)
+      v[u] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(o + (int64_t)max(p[u], 0) * H + col));
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      if (p[u] < 0) continue;
+      const float wj = w[t * k + j0 + u];
+      acc.x = fmaf(wj, v[u][0], acc.x);
+      acc.y = fmaf(wj, v[u][1], acc.y);
+      acc.z = fmaf(wj, v[u][2], acc.z);
+      acc.w = fmaf(wj, v[u][3], acc.w);
+    }
   }
   if (BF16_OUT) {
     const uint32_t lo = f32_to_bf16(acc.x) | (f32_to_bf16(acc.y) << 16);
