@@ -125,7 +125,10 @@ int w4a8_moe_permute(const int32_t* ids, int64_t T, int32_t k, int32_t E,
  * words row by row, is the input of w4a8_moe_prepack_int4.)  G = K/128:
  *   weights : int32 [E][N/16][G][16][16] (INT4) or u8 [E][N/16][G][16][64]
  *             (MXFP4): row n, group g (row-major words 16g .. 16g+15, bytes
- *             64g .. 64g+63) at byte ((e (N/16) + n/16) G + g) 1024 + 64 (n % 16);
+ *             64g .. 64g+63) at byte ((e (N/16) + n/16) G + g) 1024 + 64 (n % 16).
+ *             An INT4 word keeps its eight K elements but holds their nibbles
+ *             in the order k0 k4 k1 k5 k2 k6 k3 k7 (bits 0..31), so that one
+ *             mask yields k0..k3 and one shift and mask k4..k7, a byte each;
  *   scales  : fp32 [E][G][N] (INT4 group 128) or u8 [E][G][N][4] (MXFP4):
  *             row n, group g at ((e G + g) N + n) 4.  Per-channel scales
  *             ([E][N]) need no change.
@@ -137,7 +140,8 @@ int w4a8_moe_permute(const int32_t* ids, int64_t T, int32_t k, int32_t E,
  * Offline layout step, INT4: row-major uint4b8 words w_packed int32 [E][N][K/8]
  * (and, for the group-128 form, w_scale fp32 [E][N][K/128]) -> GEMM storage
  * w_blk int32 [E][N/16][K/128][16][16] (and s_blk fp32 [E][K/128][N]).  A
- * permutation of bytes.  Pass w_scale = s_blk = NULL for per-channel scales,
+ * permutation of the words, and of the nibbles inside each word (see above).
+ * Pass w_scale = s_blk = NULL for per-channel scales,
  * which the GEMMs read as they are.
  *   Rules : 0 <= E <= 1024, N % 16 == 0, K % 128 == 0; weights 16-byte
  *   aligned, scales 4-byte aligned; no overlap of inputs and outputs.

@@ -404,7 +404,7 @@ int w4a8_moe_prepack_mxfp4(const uint8_t* w_packed, const uint8_t* w_scale, int3
     return fail(W4A8_ERR_ALIGN, "prepack_mxfp4: weights must be 16-byte aligned, scales 4-byte");
   if (int st = check_device()) return st;
   (void)hipGetLastError();
-  return launched(w4a8::launch_prepack(w_packed, w_scale, E, N, K, w_blk, s_blk, as_stream(stream)), "prepack_mxfp4");
+  return launched(w4a8::launch_prepack(w_packed, w_scale, E, N, K, 0, w_blk, s_blk, as_stream(stream)), "prepack_mxfp4");
 }
 
 int w4a8_moe_prepack_int4(const int32_t* w_packed, const float* w_scale, int32_t E, int64_t N, int64_t K,
@@ -422,7 +422,7 @@ int w4a8_moe_prepack_int4(const int32_t* w_packed, const float* w_scale, int32_t
     return fail(W4A8_ERR_ALIGN, "prepack_int4: weights must be 16-byte aligned, scales 4-byte");
   if (int st = check_device()) return st;
   (void)hipGetLastError();
-  return launched(w4a8::launch_prepack(w_packed, w_scale, E, N, K, w_blk, s_blk, as_stream(stream)), "prepack_int4");
+  return launched(w4a8::launch_prepack(w_packed, w_scale, E, N, K, 1, w_blk, s_blk, as_stream(stream)), "prepack_int4");
 }
 
 // the kernel for an MXFP4 GEMM (plain or fused), once every argument is checked

@@ -85,21 +85,18 @@ __device__ __forceinline__ v16f mfma32x32x64(v8i a, v8i b, v16f c) {
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
 }
 
-// 32 packed nibbles (K order: word c holds k = 8c .. 8c+7, nibble j at bits
-// 4j) -> 32 bytes u_k in K order, each read by the MFMA as u_k * 2^-9.
+// 32 nibbles of the GEMM storage (word c holds k = 8c .. 8c+7 in the nibble
+// order k0 k4 k1 k5 k2 k6 k3 k7) -> 32 bytes u_k in K order, each read by the
+// MFMA as u_k * 2^-9: one mask for k0..k3 and a shift and a mask for k4..k7.
 __device__ __forceinline__ v8i nibbles_to_fp8(i32x4 w) {
-  const uint32_t ws[4] = {(uint32_t)w[0], (uint32_t)w[1], (uint32_t)w[2], (uint32_t)w[3]};
   v8i r;
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
-    const uint32_t lo = ws[c] & 0x0f0f0f0fu;           // u0 u2 u4 u6
-    const uint32_t hi = (ws[c] >> 4) & 0x0f0f0f0fu;    // u1 u3 u5 u7
-    r[2 * c] = (int)__builtin_amdgcn_perm(hi, lo, 0x05010400u);       // u0 u1 u2 u3
-    r[2 * c + 1] = (int)__builtin_amdgcn_perm(hi, lo, 0x07030602u);   // u4 u5 u6 u7
+    r[2 * c] = (int)((uint32_t)w[c] & 0x0f0f0f0fu);             // u0 u1 u2 u3
+    r[2 * c + 1] = (int)(((uint32_t)w[c] >> 4) & 0x0f0f0f0fu);  // u4 u5 u6 u7
   }
   return r;
 }
-
 // Fused SwiGLU: the gate/up GEMM reads its weight rows interleaved by 16, so
 // that two neighbouring 16-column blocks of a tile hold the gate and the up
 // rows of the same 16 output columns.  Tile column v reads weight row

@@ -8,7 +8,8 @@
 namespace w4a8 {
 
 // One grouped GEMM on weights in the GEMM storage (launch_prepack): 1 KB per 16
-// rows x 128 K ([E][N/16][K/128][16][64] bytes), per-group scales group-major
+// rows x 128 K ([E][N/16][K/128][16][64] bytes; INT4 words with their nibbles
+// in the order k0 k4 k1 k5 k2 k6 k3 k7), per-group scales group-major
 // ([E][K/128][N] 4-byte words).  a_rowsum == nullptr: the group-128 FP8 form
 // (w_scale fp32 group scales), or with mx set the MXFP4 form; otherwise the
 // per-channel INT8 form (INT8 activations with their row code sums, w_scale
@@ -57,8 +58,8 @@ hipError_t launch_wquant(const float* w, int64_t rows, int64_t K, int mse_clip, 
                          hipStream_t stream);
 hipError_t launch_wquant_mxfp4(const float* w, int64_t rows, int64_t K, uint8_t* packed, uint8_t* scales,
                                hipStream_t stream);
-hipError_t launch_prepack(const void* w, const void* s, int64_t E, int64_t N, int64_t K, void* wb, void* sb,
-                          hipStream_t stream);
+hipError_t launch_prepack(const void* w, const void* s, int64_t E, int64_t N, int64_t K, int nibble_split,
+                          void* wb, void* sb, hipStream_t stream);
 hipError_t launch_requant(const float* act, const float* pmax, int64_t M, int64_t I, uint8_t* q, float* s,
                           hipStream_t stream);
 hipError_t launch_requant_i8(const float* act, const float* pmax, int64_t M, int64_t I, int8_t* q, float* s,

@@ -176,9 +176,21 @@ hipError_t launch_wquant_mxfp4(const float* w, int64_t rows, int64_t K, uint8_t*
 //      E8M0 block scales) move to ((e G + g) N + n) 4, so that the scales of
 //      one group of all rows are contiguous (skipped when s is null).
 // One thread per 16 weight bytes and one per 4 scale bytes.
+// INT4 words in the GEMM storage hold their eight nibbles k0..k7 in the order
+// k0 k4 k1 k5 k2 k6 k3 k7 (bits 0..31), so that w & 0x0f0f0f0f holds k0..k3
+// and (w >> 4) & 0x0f0f0f0f holds k4..k7, one per byte
+__device__ __forceinline__ uint32_t nibble_split(uint32_t w) {
+  auto spread = [](uint32_t x) {      // nibble i of a 16-bit value -> nibble 2i
+    x = (x | (x << 8)) & 0x00ff00ffu;
+    return (x | (x << 4)) & 0x0f0f0f0fu;
+  };
+  return spread(w & 0xffffu) | (spread(w >> 16) << 4);
+}
+
+template <bool kSplit>
 __global__ __launch_bounds__(256) void prepack_kernel(const u32x4* __restrict__ w, const uint32_t* __restrict__ s,
-                                                            int64_t E, int64_t N, int64_t G,
-                                                            u32x4* __restrict__ wb, uint32_t* __restrict__ sb) {
+                                                      int64_t E, int64_t N, int64_t G, u32x4* __restrict__ wb,
+                                                      uint32_t* __restrict__ sb) {
   const int64_t nw = E * N * G * 4, ns = s ? E * N * G : 0;   // 16-byte pieces, 4-byte scale words
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < nw + ns; t += stride) {
@@ -186,7 +198,12 @@ __global__ __launch_bounds__(256) void prepack_kernel(const u32x4* __restrict__ 
       // source piece t: row r = t / (4G) of all E N rows, group g, chunk c
       const int64_t r = t / (4 * G), rem = t - r * 4 * G, g = rem >> 2, c = rem & 3;
       const int64_t e = r / N, n = r - e * N;
-      wb[(((e * (N / 16) + n / 16) * G + g) * 16 + n % 16) * 4 + c] = __builtin_nontemporal_load(w + t);
+      u32x4 v = __builtin_nontemporal_load(w + t);
+      if constexpr (kSplit) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] = nibble_split(v[i]);
+      }
+      wb[(((e * (N / 16) + n / 16) * G + g) * 16 + n % 16) * 4 + c] = v;
     } else {
       const int64_t u = t - nw, r = u / G, g = u - r * G, e = r / N, n = r - e * N;
       sb[(e * G + g) * N + n] = s[u];
@@ -194,14 +211,15 @@ __global__ __launch_bounds__(256) void prepack_kernel(const u32x4* __restrict__ 
   }
 }
 
-hipError_t launch_prepack(const void* w, const void* s, int64_t E, int64_t N, int64_t K, void* wb, void* sb,
-                          hipStream_t stream) {
+hipError_t launch_prepack(const void* w, const void* s, int64_t E, int64_t N, int64_t K, int nibble_split,
+                          void* wb, void* sb, hipStream_t stream) {
   const int64_t G = K / 128, total = E * N * G * (s ? 5 : 4);
   if (total == 0) return hipSuccess;
   const int64_t blocks = std::min<int64_t>((total + 255) / 256, 16384);
-  hipLaunchKernelGGL(prepack_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
-                     reinterpret_cast<const u32x4*>(w), reinterpret_cast<const uint32_t*>(s), E, N, G,
-                     reinterpret_cast<u32x4*>(wb), reinterpret_cast<uint32_t*>(sb));
+  auto kernel = nibble_split ? prepack_kernel<true> : prepack_kernel<false>;
+  hipLaunchKernelGGL(kernel, dim3((unsigned)blocks), dim3(256), 0, stream, reinterpret_cast<const u32x4*>(w),
+                     reinterpret_cast<const uint32_t*>(s), E, N, G, reinterpret_cast<u32x4*>(wb),
+                     reinterpret_cast<uint32_t*>(sb));
   return hipGetLastError();
 }
 

@@ -119,8 +119,14 @@ def test_prepack_int4(E, N, K, scales, rng):
     say(f"prepack_int4 E={E} N={N} K={K} scales={scales}")
     wb, sb = prepack_int4(w, s)
     G = K // 128
-    # GEMM storage: [E][N/16][G][16][16] words, [E][G][N] scales
-    assert np.array_equal(host(wb), w.reshape(E, N // 16, 16, G, 16).transpose(0, 1, 3, 2, 4))
+    # GEMM storage: [E][N/16][G][16][16] words, [E][G][N] scales; inside a word the
+    # nibble of k = 8c + i (i < 4) moves to nibble 2i, that of k = 8c + 4 + i to 2i + 1
+    blk = w.reshape(E, N // 16, 16, G, 16).transpose(0, 1, 3, 2, 4).view(np.uint32)
+    want = np.zeros_like(blk)
+    for i in range(8):
+        pos = 2 * i if i < 4 else 2 * (i - 4) + 1
+        want |= ((blk >> np.uint32(4 * i)) & np.uint32(15)) << np.uint32(4 * pos)
+    assert np.array_equal(host(wb).view(np.uint32), want)
     if scales:
         assert np.array_equal(host(sb).view(np.uint32), s.transpose(0, 2, 1).view(np.uint32))
     else:
