@@ -244,7 +244,7 @@ def main() -> int:
                          "reference for scaling HBM byte counters")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
+        print(f"bench.py: this benchmark runs on one GPU; --gpus {args.gpus} is not supported "
               "(the layer holds all experts on one device and has no multi-GPU path)", file=sys.stderr)
         return 2
 

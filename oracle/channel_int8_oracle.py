@@ -13,7 +13,7 @@ What it computes, and where that is stated:
 * The rest of the layer (routing, permutation, SwiGLU, the routing-weighted
   combine) is the same as in the group-128 FP8 variant of w4a8_oracle.
 
-Readings where the page is silent (each is listed in the design doc):
+Readings where the page is silent:
   * a weight row n has one fp32 scale s[n] = fl32(amax_n / 7) (1/7 for an
     all-zero row); q = clamp(round-half-even(w / s), -8, 7) from the exact
     quotient; the codes are packed as uint4b8 (q + 8) in int32 words, the

@@ -18,7 +18,7 @@ What it computes, and where that is stated:
   b meaning 2^(b - 127)); elements are FP4 E2M1 (1 sign, 2 exponent bits with
   bias 1, 1 mantissa bit): magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6.
 
-Readings where the pages are silent (each is listed in the design doc):
+Readings where the pages are silent:
   * the block scale follows the MX rule: X = floor(log2(amax)) - 2 (2 is the
     largest E2M1 exponent), so amax / 2^X lies in [4, 8) and values above 6
     saturate; an all-zero block is treated as amax = 1.  This rule gives

@@ -23,7 +23,7 @@ What it computes, and where that is stated (page title, then section):
   projection, routing-weighted combine) and the FP8 format (E4M3, amax/448)
   are the problem statement's; the pages give no formula for them.
 
-Readings where the pages are silent (each is listed in the design doc):
+Readings where the pages are silent:
   * FP8 is OCP E4M3FN (bias 7, max 448, no infinities); conversion is round
     to nearest, ties to even, saturating at 448, sign kept on zero.
   * per-token scale = fl32(amax / 448) (1.0 for an all-zero row); the code of

@@ -53,7 +53,7 @@ class Shape:
         return self.T * self.k
 
 
-CONFIGS = (
+WORKLOADS = (
     Shape("tiny T=16 H=256 I=128 E=8 top-2", 16, 256, 128, 8, 2),
     Shape("decode T=128 H=6144 I=2048 E=256 top-8", 128, 6144, 2048, 256, 8, outlier_frac=0.01),
     Shape("decode T=256 H=6144 I=2048 E=256 top-8", 256, 6144, 2048, 256, 8, outlier_frac=0.01),
@@ -121,7 +121,7 @@ def make_workload(shape: Shape, seed: int, with_weights: bool = True) -> Workloa
 
 def make_config(index: int, with_weights: bool = True) -> Workload:
     """Workload index 0..4 (tiny, decode 128, decode 256, prefill 8K, skewed 16K)."""
-    return make_workload(CONFIGS[index], 1000 + index, with_weights)
+    return make_workload(WORKLOADS[index], 1000 + index, with_weights)
 
 
 def make_custom(T: int, H: int, I: int, E: int, k: int, seed: int, **kw) -> Workload:

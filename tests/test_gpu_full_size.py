@@ -58,10 +58,10 @@ def _sample_rows(offsets, rng, per_expert=3, n_random=4):
     return np.array(sorted(rows), dtype=np.int64)
 
 
-CONFIGS = [1, 2, 3, 4]
+WORKLOADS = [1, 2, 3, 4]
 
 
-@pytest.mark.parametrize("index", CONFIGS)
+@pytest.mark.parametrize("index", WORKLOADS)
 def test_routing_and_permutation(index):
     wl, _, got = _run(index)
     ids, w = oracle.route(wl.logits, wl.shape.k)
@@ -78,7 +78,7 @@ def test_routing_and_permutation(index):
         assert (counts == 0).sum() >= 1                    # skew leaves some experts empty
 
 
-@pytest.mark.parametrize("index", CONFIGS)
+@pytest.mark.parametrize("index", WORKLOADS)
 def test_sampled_tokens_end_to_end(index):
     wl, _, got = _run(index)
     T = wl.shape.T
@@ -108,7 +108,7 @@ def test_sampled_tokens_end_to_end(index):
     assert_float_parity(host(y), res["y"], "unpermute", fro_tight=1e-6)
 
 
-@pytest.mark.parametrize("index", CONFIGS)
+@pytest.mark.parametrize("index", WORKLOADS)
 def test_sampled_rows_per_call(index):
     wl, moe, got = _run(index)
     sh = wl.shape

@@ -50,10 +50,10 @@ def _sample_rows(offsets, rng, n_random=4):
     return np.array(sorted(rows), dtype=np.int64)
 
 
-CONFIGS = [1, 3]
+WORKLOADS = [1, 3]
 
 
-@pytest.mark.parametrize("index", CONFIGS)
+@pytest.mark.parametrize("index", WORKLOADS)
 def test_mxfp4_routing_and_tokens(index):
     wl, (w13, s13, w2, s2), _, got = _run(index)
     ids, _ = oracle.route(wl.logits, wl.shape.k)
@@ -81,7 +81,7 @@ def test_mxfp4_routing_and_tokens(index):
     say(f"config {index} MXFP4 output vs oracle: fro {fro_own:.2e}; {flips} midpoint code choices; {r}")
 
 
-@pytest.mark.parametrize("index", CONFIGS)
+@pytest.mark.parametrize("index", WORKLOADS)
 def test_mxfp4_sampled_rows_per_call(index):
     wl, (w13, s13, w2, s2), moe, got = _run(index)
     sh = wl.shape
