@@ -167,3 +167,117 @@ def test_binding_rejects_host_tensors():
         ops.w4a8_moe_quant_act(torch.zeros((4, 256), dtype=torch.float32))
     with pytest.raises(ValueError):
         ops.w4a8_moe_route(torch.zeros((4, 8), dtype=torch.float32), 2)
+
+
+def test_binding_declares_every_symbol():
+    # every entry point of the header has a ctypes signature in the binding, and no other
+    assert set(declared_symbols()) == set(ops._SIGNATURES)
+
+
+def test_int8_variant_checks(L):
+    q = L.w4a8_moe_quant_act_i8
+    assert q(P, 4, 100, 100, P, P, P, None) == ERR_SHAPE            # H % 128
+    assert q(P, 4, 256, 256, P, P, None, None) == ERR_NULL          # row sums are required
+    assert q(P + 8, 4, 256, 256, P, P, P, None) == ERR_ALIGN
+    assert q(None, 0, 256, 256, None, None, None, None) == OK
+    g = L.w4a8_moe_grouped_gemm_i8
+    good = dict(a=P, sa=P, rs=P, rows=None, M=64, off=P, E=8, w=P, ws=P, N=256, K=256, out=P, algo=0)
+
+    def call(**kw):
+        d = dict(good, **kw)
+        return g(d["a"], d["sa"], d["rs"], d["rows"], d["M"], d["off"], d["E"], d["w"], d["ws"], d["N"], d["K"],
+                 d["out"], d["algo"], None)
+    assert call(K=(1 << 20) + 128) == ERR_SHAPE                  # int32 sums could overflow
+    assert call(N=96) == ERR_SHAPE
+    assert call(algo=3) == ERR_SHAPE
+    assert call(rs=None) == ERR_NULL
+    assert call(rows=P + 2) == ERR_ALIGN
+    assert call(M=0, a=None, rs=None) == OK
+    s = L.w4a8_moe_swiglu_i8
+    assert s(P, 4, 100, P, P, P, None) == ERR_SHAPE
+    assert s(P, 4, 128, P, P, None, None) == ERR_NULL
+    assert s(P, 4, 128, P + 2, P, P, None) == ERR_ALIGN             # qa 4-byte
+    assert s(None, 0, 128, None, None, None, None) == OK
+    c = L.w4a8_moe_quantize_weights_channel
+    assert c(P, 4, 100, P, P, None) == ERR_SHAPE
+    assert c(P, 4, 128, None, P, None) == ERR_NULL
+    assert c(P + 4, 4, 128, P, P, None) == ERR_ALIGN
+    assert c(None, 0, 128, None, None, None) == OK
+
+
+def test_fused_epilogue_checks(L):
+    f = L.w4a8_moe_grouped_gemm_swiglu
+    good = dict(a=P, sa=P, rows=None, M=64, off=P, E=8, w=P, s=P, I=128, K=256, act=P, pm=P, algo=0)
+
+    def call(fn, **kw):
+        d = dict(good, **kw)
+        return fn(d["a"], d["sa"], d["rows"], d["M"], d["off"], d["E"], d["w"], d["s"], d["I"], d["K"], d["act"],
+                  d["pm"], d["algo"], None)
+    for fn in (f, L.w4a8_moe_grouped_gemm_swiglu_mxfp4):
+        assert call(fn, I=64) == ERR_SHAPE                       # I % 128
+        assert call(fn, K=100) == ERR_SHAPE
+        assert call(fn, E=0) == ERR_SHAPE
+        assert call(fn, algo=5) == ERR_SHAPE
+        assert call(fn, pm=None) == ERR_NULL
+        assert call(fn, act=P + 4) == ERR_ALIGN                  # act 16-byte
+        assert call(fn, pm=P + 2) == ERR_ALIGN
+        assert call(fn, M=0, a=None, w=None, act=None, pm=None) == OK
+    g = L.w4a8_moe_grouped_gemm_swiglu_i8
+    assert g(P, P, None, None, 64, P, 8, P, P, 128, 256, P, P, 0, None) == ERR_NULL      # row sums
+    assert g(P, P, P, None, 64, P, 8, P, P, 128, (1 << 20) + 128, P, P, 0, None) == ERR_SHAPE
+    r = L.w4a8_moe_requant
+    assert r(P, P, 4, 100, P, P, None) == ERR_SHAPE
+    assert r(P, None, 4, 128, P, P, None) == ERR_NULL
+    assert r(P + 4, P, 4, 128, P, P, None) == ERR_ALIGN
+    assert r(None, None, 0, 128, None, None, None) == OK
+    r8 = L.w4a8_moe_requant_i8
+    assert r8(P, P, 4, 128, P, P, None, None) == ERR_NULL
+    assert r8(P, P, 4, 128, P, P, P + 2, None) == ERR_ALIGN
+    assert r8(None, None, 0, 128, None, None, None, None) == OK
+
+
+def test_prepack_and_mxfp4_checks(L):
+    pi = L.w4a8_moe_prepack_int4
+    assert pi(P, P, 2, 24, 256, P, P, None) == ERR_SHAPE            # N % 16
+    assert pi(P, P, 2, 32, 200, P, P, None) == ERR_SHAPE            # K % 128
+    assert pi(P, P, -1, 32, 256, P, P, None) == ERR_SHAPE
+    assert pi(P, P, 2, 32, 256, P, None, None) == ERR_NULL          # scales: both or neither
+    assert pi(P, None, 2, 32, 256, P, P, None) == ERR_NULL
+    assert pi(P + 8, None, 2, 32, 256, P, None, None) == ERR_ALIGN
+    assert pi(None, None, 0, 32, 256, None, None, None) == OK
+    pm = L.w4a8_moe_prepack_mxfp4
+    assert pm(P, P, 2, 24, 256, P, P, None) == ERR_SHAPE
+    assert pm(P, None, 2, 32, 256, P, P, None) == ERR_NULL          # MXFP4 scales are required
+    assert pm(P, P, 2, 32, 256, P + 8, P, None) == ERR_ALIGN
+    assert pm(None, None, 0, 32, 256, None, None, None) == OK
+    qm = L.w4a8_moe_quantize_weights_mxfp4
+    assert qm(P, 4, 48, P, P, None) == ERR_SHAPE                    # K % 32
+    assert qm(P, 4, 64, P, None, None) == ERR_NULL
+    assert qm(P + 8, 4, 64, P, P, None) == ERR_ALIGN               # w 16-byte
+    assert qm(P, 4, 64, P + 1, P, None) == ERR_ALIGN               # codes 2-byte
+    assert qm(None, 0, 64, None, None, None) == OK
+    gm = L.w4a8_moe_grouped_gemm_mxfp4
+    assert gm(P, P, None, 64, P, 8, P, P, 96, 256, P, 0, None) == ERR_SHAPE      # N % 64
+    assert gm(P, P, None, 64, P, 8, P, P, 256, 192, P, 0, None) == ERR_SHAPE     # K % 128
+    assert gm(P, P, None, 64, P, 8, P, P, 256, 256, P, 9, None) == ERR_SHAPE     # algo
+    assert gm(P, P, None, 64, P, 8, P, None, 256, 256, P, 0, None) == ERR_NULL
+    assert gm(P, P, None, 64, P, 8, P + 8, P, 256, 256, P, 0, None) == ERR_ALIGN
+    assert gm(None, None, None, 0, None, 8, None, None, 256, 256, None, 0, None) == OK
+
+
+def test_later_calls_report_missing_device(L, no_device):
+    if not no_device:
+        pytest.skip("a supported GPU is present; these fake pointers must not reach it")
+    assert L.w4a8_moe_quant_act_i8(P, 4, 256, 256, P, P, P, None) == ERR_DEVICE
+    assert L.w4a8_moe_grouped_gemm_i8(P, P, P, None, 8, P, 8, P, P, 256, 256, P, 0, None) == ERR_DEVICE
+    assert L.w4a8_moe_swiglu_i8(P, 4, 128, P, P, P, None) == ERR_DEVICE
+    assert L.w4a8_moe_quantize_weights_channel(P, 4, 128, P, P, None) == ERR_DEVICE
+    assert L.w4a8_moe_grouped_gemm_swiglu(P, P, None, 8, P, 8, P, P, 128, 256, P, P, 0, None) == ERR_DEVICE
+    assert L.w4a8_moe_grouped_gemm_swiglu_i8(P, P, P, None, 8, P, 8, P, P, 128, 256, P, P, 0, None) == ERR_DEVICE
+    assert L.w4a8_moe_requant(P, P, 4, 128, P, P, None) == ERR_DEVICE
+    assert L.w4a8_moe_requant_i8(P, P, 4, 128, P, P, P, None) == ERR_DEVICE
+    assert L.w4a8_moe_quantize_weights_mxfp4(P, 4, 64, P, P, None) == ERR_DEVICE
+    assert L.w4a8_moe_prepack_int4(P, P, 2, 32, 256, P, P, None) == ERR_DEVICE
+    assert L.w4a8_moe_prepack_mxfp4(P, P, 2, 32, 256, P, P, None) == ERR_DEVICE
+    assert L.w4a8_moe_grouped_gemm_mxfp4(P, P, None, 8, P, 8, P, P, 256, 256, P, 0, None) == ERR_DEVICE
+    assert L.w4a8_moe_grouped_gemm_swiglu_mxfp4(P, P, None, 8, P, 8, P, P, 128, 256, P, P, 0, None) == ERR_DEVICE
