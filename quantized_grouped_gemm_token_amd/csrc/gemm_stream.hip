@@ -154,8 +154,11 @@ __device__ __forceinline__ void pair_compute_i8(const WPair<NS>& w, const uint8_
 // up rows of the same 16 output columns (gate_up_row), and the epilogue
 // writes act = silu(gate) * up [M][N/2] and the workgroup's max |act| of each
 // row (its 64 output columns) to pmax[p][blockIdx.x].
+// At least 3 waves per SIMD (3 workgroups per CU): the kernel is bound by the
+// weight loads it has in flight.  Without the bound the group-128 form put its
+// accumulators in AGPRs on top of 156 VGPRs and ran 2 waves per SIMD.
 template <int NS, int CH, int kForm, bool kSwiglu>
-__global__ __launch_bounds__(kStreamThreads) void gg_stream_kernel(const uint8_t* __restrict__ a,
+__global__ __launch_bounds__(kStreamThreads, 3) void gg_stream_kernel(const uint8_t* __restrict__ a,
                                                                    const float* __restrict__ a_scale,
                                                                    const int32_t* __restrict__ a_rowsum,
                                                                    const int32_t* __restrict__ a_rows,
