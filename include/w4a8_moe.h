@@ -106,6 +106,9 @@ int64_t w4a8_moe_permute_workspace_bytes(int64_t T, int32_t k, int32_t E);
  *   offsets = exclusive prefix sum of counts (E + 1 entries, offsets[E] = T*k);
  *   rows of expert e are offsets[e] .. offsets[e+1]-1, ordered by f;
  *   row_token[p] = token of routed row p;  inv_pos[f] = row of index f.
+ *   An id outside [0, E) is not routed: it is not counted (offsets[E] is then
+ *   the number of routed ids, and row_token past it is not written) and its
+ *   inv_pos is -1, which w4a8_moe_unpermute skips.
  *   ids : int32 [T*k].  offsets : int32 [E+1].  row_token, inv_pos : int32 [T*k].
  *   workspace : device memory of w4a8_moe_permute_workspace_bytes(T, k, E)
  *   bytes, 4-byte aligned (contents need no initialisation).

@@ -104,6 +104,23 @@ def test_permute(T, E, k, rng):
         assert np.array_equal(host(g), w_), name
 
 
+@pytest.mark.parametrize("T,E,k", [(100, 64, 4), (700, 256, 8)])     # the one-block and the three-launch paths
+def test_permute_skips_ids_out_of_range(T, E, k, rng):
+    ids = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+    bad = rng.random(ids.shape) < 0.05
+    ids[bad] = np.where(rng.random(int(bad.sum())) < 0.5, -1, E + 3).astype(np.int32)
+    # the oracle on the same ids with every out-of-range one sent to an extra expert E, which sorts last
+    want_off, want_rt, want_inv = oracle.permute(np.where(bad, E, ids), E + 1)
+    say(f"permute with {int(bad.sum())} ids out of range, T={T} E={E} k={k}")
+    offsets, row_token, inv_pos = (host(t) for t in ops.w4a8_moe_permute(to_dev(ids), E))
+    routed = int(want_off[E])
+    assert routed == T * k - int(bad.sum())
+    assert np.array_equal(offsets, want_off[:E + 1])
+    assert np.array_equal(row_token[:routed], want_rt[:routed])
+    assert np.array_equal(inv_pos[~bad.reshape(-1)], want_inv[~bad.reshape(-1)])
+    assert np.all(inv_pos[bad.reshape(-1)] == -1)
+
+
 def test_permute_empty():
     say("permute T=0")
     offsets, _, _ = ops.w4a8_moe_permute(torch.zeros((0, 4), dtype=torch.int32, device="cuda:0"), 16)
