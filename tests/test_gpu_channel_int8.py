@@ -33,7 +33,7 @@ def _bf16(x32):
 
 
 # ------------------------------------------------------------------ step 1
-@pytest.mark.parametrize("T,H", [(1, 128), (37, 512), (256, 6144), (3, 16384), (2, 17408)])
+@pytest.mark.parametrize("T,H", [(1, 128), (37, 512), (256, 6144), (3, 16384), (2, 17408), (1100, 6144), (1030, 2176)])
 def test_quant_act_i8(T, H, rng):
     x = rng.standard_normal((T, H)).astype(np.float32)
     x[:, rng.choice(H, max(1, H // 100), replace=False)] *= 20.0

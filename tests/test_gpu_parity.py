@@ -59,7 +59,8 @@ def test_quant_act_special_values():
     assert np.array_equal(host(sx), want_s)
 
 
-@pytest.mark.parametrize("T,H", [(1, 128), (37, 384), (300, 6144), (5, 2176), (3, 16384), (2, 17408)])
+@pytest.mark.parametrize("T,H", [(1, 128), (37, 384), (300, 6144), (5, 2176), (3, 16384), (2, 17408),
+                                 (1100, 6144), (1024, 2176), (1030, 1024), (1500, 8192), (1025, 9216)])
 def test_quant_act_random(T, H, rng):
     mag = np.exp2(rng.integers(-12, 12, size=(T, 1))).astype(np.float32)
     x = (rng.standard_normal((T, H)).astype(np.float32) * mag)
