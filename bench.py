@@ -300,7 +300,7 @@ def main() -> int:
     torch.cuda.synchronize()
     log(f"warmup {args.warmup} done")
 
-    steps = W4A8MoE.STEPS
+    steps = moe.steps
     evs = [{s: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for s in steps}
            for _ in range(args.steps)]
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)

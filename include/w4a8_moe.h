@@ -120,6 +120,28 @@ int w4a8_moe_permute(const int32_t* ids, int64_t T, int32_t k, int32_t E,
                      void* workspace, int64_t workspace_bytes, void* stream);
 
 /*
+ * Steps 1, 2 and 3 in one call: w4a8_moe_quant_act, w4a8_moe_route and
+ * w4a8_moe_permute on the same arguments, with the same results.  For decode
+ * batches (T*k <= 1024 and H <= 8192) they run as one kernel: the quantizer
+ * and the router side by side, and the router workgroup that finishes last
+ * sorts the routed rows; otherwise as the three kernels.
+ *   counter : one uint32 on the device, 4-byte aligned, zero before the
+ *             first call; every call leaves it zero.  Calls that share a
+ *             counter must not overlap (use one per stream).
+ *   Every other argument and rule: as in the three calls.
+ */
+int w4a8_moe_front(const uint16_t* x_bf16, int64_t T, int64_t H, int64_t ld_x, uint8_t* qx, float* sx,
+                   const float* logits, int32_t E, int32_t k, int32_t renormalize, int32_t* ids, float* w,
+                   int32_t* offsets, int32_t* row_token, int32_t* inv_pos, void* workspace, int64_t workspace_bytes,
+                   uint32_t* counter, void* stream);
+
+/* The same with the INT8 quantizer of w4a8_moe_quant_act_i8 (codes plus row sums). */
+int w4a8_moe_front_i8(const uint16_t* x_bf16, int64_t T, int64_t H, int64_t ld_x, int8_t* qx, float* sx,
+                      int32_t* rowsum, const float* logits, int32_t E, int32_t k, int32_t renormalize, int32_t* ids,
+                      float* w, int32_t* offsets, int32_t* row_token, int32_t* inv_pos, void* workspace,
+                      int64_t workspace_bytes, uint32_t* counter, void* stream);
+
+/*
  * ---- GEMM storage of the expert weights ------------------------------------
  * The grouped GEMMs read the 4-bit weights in a permuted order, written once
  * by a prepack call: the 64 packed bytes of one 128-wide K group of 16

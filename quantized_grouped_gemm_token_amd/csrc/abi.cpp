@@ -149,6 +149,67 @@ int w4a8_moe_permute(const int32_t* ids, int64_t T, int32_t k, int32_t E, int32_
                   "permute");
 }
 
+// steps 1-3: the rules of w4a8_moe_quant_act[_i8], w4a8_moe_route and w4a8_moe_permute together
+static int run_front(const char* name, const uint16_t* x, int64_t T, int64_t H, int64_t ld_x, void* qx, float* sx,
+                     int32_t* rowsum, bool int8, const float* logits, int32_t E, int32_t k, int32_t renormalize,
+                     int32_t* ids, float* w, int32_t* offsets, int32_t* row_token, int32_t* inv_pos,
+                     void* workspace, int64_t workspace_bytes, uint32_t* counter, void* stream) {
+  if (T < 0 || T >= kMaxRows) return fail(W4A8_ERR_SHAPE, "%s: T=%lld out of range", name, (long long)T);
+  if (H <= 0 || H % 128)
+    return fail(W4A8_ERR_SHAPE, "%s: H=%lld must be a positive multiple of 128", name, (long long)H);
+  if (ld_x < H || ld_x % 8)
+    return fail(W4A8_ERR_SHAPE, "%s: ld_x=%lld must be >= H and a multiple of 8", name, (long long)ld_x);
+  if (E < 1 || E > 1024 || k < 1 || k > E)
+    return fail(W4A8_ERR_SHAPE, "%s: need 1 <= k <= E <= 1024 (k=%d, E=%d)", name, k, E);
+  if (T * (int64_t)k >= kMaxRows) return fail(W4A8_ERR_SHAPE, "%s: T*k must be < 2^31", name);
+  if (!offsets || !workspace || !counter) return fail(W4A8_ERR_NULL, "%s: null offsets, workspace or counter", name);
+  if (T > 0 && (!x || !qx || !sx || !logits || !ids || !w || !row_token || !inv_pos || (int8 && !rowsum)))
+    return fail(W4A8_ERR_NULL, "%s: null pointer", name);
+  const int64_t need = w4a8::permute_workspace_bytes(T * (int64_t)k, E);
+  if (workspace_bytes < need)
+    return fail(W4A8_ERR_WORKSPACE, "%s: workspace of %lld bytes, need %lld", name, (long long)workspace_bytes,
+                (long long)need);
+  if (!aligned(x, 16) || !aligned(qx, 8) || !aligned(sx, 4) || !aligned(rowsum, 4) || !aligned(logits, 4) ||
+      !aligned(ids, 4) || !aligned(w, 4) || !aligned(offsets, 4) || !aligned(row_token, 4) ||
+      !aligned(inv_pos, 4) || !aligned(workspace, 4) || !aligned(counter, 4))
+    return fail(W4A8_ERR_ALIGN, "%s: x must be 16-byte, qx 8-byte, the other arrays 4-byte aligned", name);
+  if (int st = check_device()) return st;
+  (void)hipGetLastError();
+  hipStream_t st = as_stream(stream);
+  if (w4a8::front_fits(T, H, k)) {
+    const w4a8::FrontArgs f{x, T, H, ld_x, static_cast<uint8_t*>(qx), sx, rowsum, logits, E, k, renormalize ? 1 : 0,
+                            ids, w, offsets, row_token, inv_pos, counter};
+    return launched(w4a8::launch_front(f, int8, st), name);
+  }
+  // other shapes: the three kernels one after the other (the counter is not used)
+  if (T > 0) {
+    const hipError_t e = int8 ? w4a8::launch_quant_act_i8(x, T, H, ld_x, static_cast<int8_t*>(qx), sx, rowsum, st)
+                              : w4a8::launch_quant_act(x, T, H, ld_x, static_cast<uint8_t*>(qx), sx, st);
+    if (e != hipSuccess) return launched(e, name);
+    if (hipError_t e2 = w4a8::launch_route(logits, T, E, k, renormalize ? 1 : 0, ids, w, st); e2 != hipSuccess)
+      return launched(e2, name);
+  }
+  return launched(w4a8::launch_permute(ids, T * (int64_t)k, k, E, offsets, row_token, inv_pos,
+                                       static_cast<int32_t*>(workspace), st),
+                  name);
+}
+
+int w4a8_moe_front(const uint16_t* x_bf16, int64_t T, int64_t H, int64_t ld_x, uint8_t* qx, float* sx,
+                   const float* logits, int32_t E, int32_t k, int32_t renormalize, int32_t* ids, float* w,
+                   int32_t* offsets, int32_t* row_token, int32_t* inv_pos, void* workspace, int64_t workspace_bytes,
+                   uint32_t* counter, void* stream) {
+  return run_front("front", x_bf16, T, H, ld_x, qx, sx, nullptr, false, logits, E, k, renormalize, ids, w, offsets,
+                   row_token, inv_pos, workspace, workspace_bytes, counter, stream);
+}
+
+int w4a8_moe_front_i8(const uint16_t* x_bf16, int64_t T, int64_t H, int64_t ld_x, int8_t* qx, float* sx,
+                      int32_t* rowsum, const float* logits, int32_t E, int32_t k, int32_t renormalize, int32_t* ids,
+                      float* w, int32_t* offsets, int32_t* row_token, int32_t* inv_pos, void* workspace,
+                      int64_t workspace_bytes, uint32_t* counter, void* stream) {
+  return run_front("front_i8", x_bf16, T, H, ld_x, qx, sx, rowsum, true, logits, E, k, renormalize, ids, w,
+                   offsets, row_token, inv_pos, workspace, workspace_bytes, counter, stream);
+}
+
 int w4a8_moe_grouped_gemm_algo(const uint8_t* a, const float* a_scale, const int32_t* a_rows, int64_t M_total,
                                const int32_t* offsets, int32_t E, const int32_t* w_packed, const float* w_scale,
                                int64_t N, int64_t K, float* out, int32_t algo, void* stream) {

@@ -64,6 +64,25 @@ hipError_t launch_requant(const float* act, const float* pmax, int64_t M, int64_
                           hipStream_t stream);
 hipError_t launch_requant_i8(const float* act, const float* pmax, int64_t M, int64_t I, int8_t* q, float* s,
                              int32_t* rowsum, hipStream_t stream);
+// layer steps 1-3 in one launch (front.hip); front_fits tells whether a shape
+// qualifies (T k <= 1024 routed rows, H <= 8192)
+struct FrontArgs {
+  const uint16_t* x;
+  int64_t T, H, ld;
+  uint8_t* q;
+  float* s;
+  int32_t* rowsum;        // INT8 form only
+  const float* logits;
+  int E, k, renormalize;
+  int32_t* ids;
+  float* w;
+  int32_t* offsets;
+  int32_t* row_token;
+  int32_t* inv_pos;
+  uint32_t* counter;      // zero before the call; left zero
+};
+bool front_fits(int64_t T, int64_t H, int k);
+hipError_t launch_front(const FrontArgs& f, bool int8, hipStream_t stream);
 hipError_t launch_unpermute(const float* o, const int32_t* inv_pos, const float* w, int64_t T, int k, int64_t H,
                             void* y, int bf16_out, hipStream_t stream);
 

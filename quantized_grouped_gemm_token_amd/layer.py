@@ -35,7 +35,7 @@ class W4A8MoE:
     GEMM_SWIGLU = staticmethod(ops.w4a8_moe_grouped_gemm_swiglu)
 
     def __init__(self, w13: torch.Tensor, s13: torch.Tensor, w2: torch.Tensor, s2: torch.Tensor, k: int,
-                 renormalize: bool = True, fused: bool = True):
+                 renormalize: bool = True, fused: bool = True, front: bool = True):
         E, N13, KW13 = w13.shape
         E2, H, KW2 = w2.shape
         c = self.K_PER_ITEM
@@ -45,6 +45,8 @@ class W4A8MoE:
         self.E, self.H, self.I, self.k = E, H, N13 // 2, k
         self.renormalize = renormalize
         self.fused = fused
+        self.front = front                                # steps 1-3 as one call (w4a8_moe_front)
+        self.steps = (("front",) if front else ("quant_act", "route", "permute")) + self.STEPS[3:]
         self._bufs: dict[int, dict] = {}
 
     def buffers(self, T: int) -> dict:
@@ -59,6 +61,7 @@ class W4A8MoE:
                 ids=e((T, self.k), torch.int32), w=e((T, self.k), torch.float32),
                 offsets=e((self.E + 1,), torch.int32), row_token=e((R,), torch.int32),
                 inv_pos=e((R,), torch.int32), workspace=e((max(nbytes, 4),), torch.uint8),
+                counter=torch.zeros((1,), dtype=torch.int32, device=dev),   # the front call's counter
                 qa=e((R, self.I), torch.uint8), sa=e((R,), torch.float32), o=e((R, self.H), torch.float32),
             )
             if self.fused:
@@ -81,8 +84,8 @@ class W4A8MoE:
                 events: dict | None = None) -> torch.Tensor:
         """x bf16 [T, H], router logits fp32 [T, E] -> y [T, H].
 
-        events, if given, maps step names (STEPS) to (start, end) CUDA events
-        that are recorded on the current stream around each step.
+        events, if given, maps step names (self.steps) to (start, end) CUDA
+        events that are recorded on the current stream around each step.
         """
         T = x.shape[0]
         b = self.buffers(T)
@@ -97,10 +100,14 @@ class W4A8MoE:
                 ev[1].record()
             return r
 
-        step("quant_act", ops.w4a8_moe_quant_act, x, b["qx"], b["sx"])
-        step("route", ops.w4a8_moe_route, logits, self.k, self.renormalize, b["ids"], b["w"])
-        step("permute", ops.w4a8_moe_permute, b["ids"], self.E, b["offsets"], b["row_token"], b["inv_pos"],
-             b["workspace"])
+        if self.front:
+            step("front", ops.w4a8_moe_front, x, logits, self.k, b["counter"], self.renormalize, False, b["qx"],
+                 b["sx"], None, b["ids"], b["w"], b["offsets"], b["row_token"], b["inv_pos"], b["workspace"])
+        else:
+            step("quant_act", ops.w4a8_moe_quant_act, x, b["qx"], b["sx"])
+            step("route", ops.w4a8_moe_route, logits, self.k, self.renormalize, b["ids"], b["w"])
+            step("permute", ops.w4a8_moe_permute, b["ids"], self.E, b["offsets"], b["row_token"], b["inv_pos"],
+                 b["workspace"])
         if self.fused:
             step("gemm_gate_up", self.GEMM_SWIGLU, b["qx"], b["sx"], b["row_token"], b["offsets"],
                  self.w13, self.s13, R, b["act"], b["pmax"], algo)
@@ -167,10 +174,14 @@ class W4A8MoEChannel(W4A8MoE):
                 ev[1].record()
             return r
 
-        step("quant_act", ops.w4a8_moe_quant_act_i8, x, b["qx"], b["sx"], b["rx"])
-        step("route", ops.w4a8_moe_route, logits, self.k, self.renormalize, b["ids"], b["w"])
-        step("permute", ops.w4a8_moe_permute, b["ids"], self.E, b["offsets"], b["row_token"], b["inv_pos"],
-             b["workspace"])
+        if self.front:
+            step("front", ops.w4a8_moe_front, x, logits, self.k, b["counter"], self.renormalize, True, b["qx"],
+                 b["sx"], b["rx"], b["ids"], b["w"], b["offsets"], b["row_token"], b["inv_pos"], b["workspace"])
+        else:
+            step("quant_act", ops.w4a8_moe_quant_act_i8, x, b["qx"], b["sx"], b["rx"])
+            step("route", ops.w4a8_moe_route, logits, self.k, self.renormalize, b["ids"], b["w"])
+            step("permute", ops.w4a8_moe_permute, b["ids"], self.E, b["offsets"], b["row_token"], b["inv_pos"],
+                 b["workspace"])
         if self.fused:
             step("gemm_gate_up", ops.w4a8_moe_grouped_gemm_swiglu_i8, b["qx"], b["sx"], b["rx"], b["row_token"],
                  b["offsets"], self.w13, self.s13, R, b["act"], b["pmax"], algo)

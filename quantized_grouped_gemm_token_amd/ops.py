@@ -58,6 +58,10 @@ _SIGNATURES = {
                                                    _c_p, _i32, _c_p]),
     "w4a8_moe_grouped_gemm_swiglu_mxfp4": (ctypes.c_int, [_c_p, _c_p, _c_p, _i64, _c_p, _i32, _c_p, _c_p, _i64,
                                                           _i64, _c_p, _c_p, _i32, _c_p]),
+    "w4a8_moe_front": (ctypes.c_int, [_c_p, _i64, _i64, _i64, _c_p, _c_p, _c_p, _i32, _i32, _i32, _c_p, _c_p, _c_p,
+                                      _c_p, _c_p, _c_p, _i64, _c_p, _c_p]),
+    "w4a8_moe_front_i8": (ctypes.c_int, [_c_p, _i64, _i64, _i64, _c_p, _c_p, _c_p, _c_p, _i32, _i32, _i32, _c_p,
+                                         _c_p, _c_p, _c_p, _c_p, _c_p, _i64, _c_p, _c_p]),
     "w4a8_moe_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "w4a8_moe_last_error": (ctypes.c_char_p, []),
     "w4a8_moe_device_supported": (ctypes.c_int, []),
@@ -176,6 +180,58 @@ def w4a8_moe_permute_workspace_bytes(T: int, k: int, E: int) -> int:
     if n < 0:
         raise ValueError(f"bad sizes T={T} k={k} E={E}")
     return n
+
+
+def w4a8_moe_front(x: torch.Tensor, logits: torch.Tensor, k: int, counter: torch.Tensor, renormalize: bool = True,
+                   int8: bool = False, qx=None, sx=None, rowsum=None, ids=None, w=None, offsets=None, row_token=None,
+                   inv_pos=None, workspace=None):
+    """Steps 1-3 in one call (w4a8_moe_front, or w4a8_moe_front_i8 with int8): x bf16 [T, H], router
+    logits fp32 [T, E], counter int32 [1] on the device (zero before the first call; left zero)
+    -> (qx, sx, rowsum or None, ids, w, offsets, row_token, inv_pos)."""
+    _need(x, "x", torch.bfloat16, 2)
+    _need(logits, "logits", torch.float32, 2, x.device)
+    _need(counter, "counter", torch.int32, 1, x.device)
+    T, H = x.shape
+    E = logits.shape[1]
+    if logits.shape[0] != T or counter.numel() < 1:
+        raise ValueError("logits must be [T, E] for x [T, H]; counter must hold one int32")
+    dev = x.device
+    R = T * k
+    cdt = torch.int8 if int8 else torch.uint8
+    qx = torch.empty((T, H), dtype=cdt, device=dev) if qx is None else qx
+    sx = torch.empty((T,), dtype=torch.float32, device=dev) if sx is None else sx
+    if int8:
+        rowsum = torch.empty((T,), dtype=torch.int32, device=dev) if rowsum is None else rowsum
+        _need(rowsum, "rowsum", torch.int32, 1, dev)
+    ids = torch.empty((T, k), dtype=torch.int32, device=dev) if ids is None else ids
+    w = torch.empty((T, k), dtype=torch.float32, device=dev) if w is None else w
+    offsets = torch.empty((E + 1,), dtype=torch.int32, device=dev) if offsets is None else offsets
+    row_token = torch.empty((R,), dtype=torch.int32, device=dev) if row_token is None else row_token
+    inv_pos = torch.empty((R,), dtype=torch.int32, device=dev) if inv_pos is None else inv_pos
+    nbytes = w4a8_moe_permute_workspace_bytes(T, k, E)
+    if workspace is None:
+        workspace = torch.empty((max(nbytes, 4),), dtype=torch.uint8, device=dev)
+    _need(qx, "qx", cdt, 2, dev)
+    _need(sx, "sx", torch.float32, 1, dev)
+    _need(ids, "ids", torch.int32, 2, dev)
+    _need(w, "w", torch.float32, 2, dev)
+    _need(offsets, "offsets", torch.int32, 1, dev)
+    _need(row_token, "row_token", torch.int32, 1, dev)
+    _need(inv_pos, "inv_pos", torch.int32, 1, dev)
+    _need(workspace, "workspace", torch.uint8, 1, dev)
+    if (tuple(qx.shape) != (T, H) or sx.numel() != T or tuple(ids.shape) != (T, k) or tuple(w.shape) != (T, k)
+            or offsets.numel() != E + 1 or row_token.numel() != R or inv_pos.numel() != R):
+        raise ValueError("output shapes do not match x [T, H], logits [T, E] and k")
+    if int8:
+        _check("w4a8_moe_front_i8", lib().w4a8_moe_front_i8(
+            _p(x), T, H, H, _p(qx), _p(sx), _p(rowsum), _p(logits), E, k, int(bool(renormalize)), _p(ids),
+            _p(w), _p(offsets), _p(row_token), _p(inv_pos), _p(workspace), workspace.numel(), _p(counter),
+            _stream(dev)))
+    else:
+        _check("w4a8_moe_front", lib().w4a8_moe_front(
+            _p(x), T, H, H, _p(qx), _p(sx), _p(logits), E, k, int(bool(renormalize)), _p(ids), _p(w),
+            _p(offsets), _p(row_token), _p(inv_pos), _p(workspace), workspace.numel(), _p(counter), _stream(dev)))
+    return qx, sx, rowsum if int8 else None, ids, w, offsets, row_token, inv_pos
 
 
 def w4a8_moe_permute(ids: torch.Tensor, E: int, offsets=None, row_token=None, inv_pos=None, workspace=None):
@@ -314,7 +370,7 @@ def w4a8_moe_quant_act_i8(x: torch.Tensor, qx=None, sx=None, rowsum=None):
     _need(rowsum, "rowsum", torch.int32, 1, dev)
     if tuple(qx.shape) != (T, H) or tuple(sx.shape) != (T,) or tuple(rowsum.shape) != (T,):
         raise ValueError("qx must be [T, H], sx and rowsum [T]")
-    _check("w4a8_moe_quant_act_i8", lib().w4a8_moe_quant_act_i8(_p(x), T, H, x.stride(0), _p(qx), _p(sx),
+    _check("w4a8_moe_quant_act_i8", lib().w4a8_moe_quant_act_i8(_p(x), T, H, H, _p(qx), _p(sx),
                                                                 _p(rowsum), _stream(dev)))
     return qx, sx, rowsum
 

@@ -281,3 +281,30 @@ def test_later_calls_report_missing_device(L, no_device):
     assert L.w4a8_moe_prepack_mxfp4(P, P, 2, 32, 256, P, P, None) == ERR_DEVICE
     assert L.w4a8_moe_grouped_gemm_mxfp4(P, P, None, 8, P, 8, P, P, 256, 256, P, 0, None) == ERR_DEVICE
     assert L.w4a8_moe_grouped_gemm_swiglu_mxfp4(P, P, None, 8, P, 8, P, P, 128, 256, P, P, 0, None) == ERR_DEVICE
+
+
+def test_front_checks(L, no_device):
+    f = L.w4a8_moe_front
+    need = L.w4a8_moe_permute_workspace_bytes(128, 8, 256)
+
+    def call(fn=f, int8=False, **kw):
+        d = dict(x=P, T=128, H=6144, ld=6144, qx=P, sx=P, rs=P, lg=P, E=256, k=8, ren=1, ids=P, w=P, off=P, rt=P,
+                 inv=P, ws=P, nws=need, cnt=P)
+        d.update(kw)
+        if int8:
+            return fn(d["x"], d["T"], d["H"], d["ld"], d["qx"], d["sx"], d["rs"], d["lg"], d["E"], d["k"], d["ren"],
+                      d["ids"], d["w"], d["off"], d["rt"], d["inv"], d["ws"], d["nws"], d["cnt"], None)
+        return fn(d["x"], d["T"], d["H"], d["ld"], d["qx"], d["sx"], d["lg"], d["E"], d["k"], d["ren"], d["ids"],
+                  d["w"], d["off"], d["rt"], d["inv"], d["ws"], d["nws"], d["cnt"], None)
+    assert call(H=100, ld=100) == ERR_SHAPE
+    assert call(k=9, E=8) == ERR_SHAPE
+    assert call(cnt=None) == ERR_NULL                          # the counter is required
+    assert call(nws=need - 4) == ERR_WORKSPACE
+    assert call(cnt=P + 2) == ERR_ALIGN
+    assert call(qx=P + 4) == ERR_ALIGN                         # qx 8-byte
+    g = L.w4a8_moe_front_i8
+    assert call(g, True, rs=None) == ERR_NULL                  # row sums are required
+    assert call(g, True, H=200, ld=200) == ERR_SHAPE
+    if no_device:
+        assert call() == ERR_DEVICE
+        assert call(g, True) == ERR_DEVICE
