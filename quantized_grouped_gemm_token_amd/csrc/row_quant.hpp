@@ -1,5 +1,5 @@
 // Per-row activation quantizer of layer step 1, as device code shared by the
-// quantizer kernels and the fused front of the layer (row_quant.hpp).
+// quantizer kernels and the fused front of the layer (front.hip).
 #pragma once
 
 #include "common.hpp"
