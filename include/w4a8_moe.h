@@ -122,7 +122,7 @@ int w4a8_moe_permute(const int32_t* ids, int64_t T, int32_t k, int32_t E,
 /*
  * Steps 1, 2 and 3 in one call: w4a8_moe_quant_act, w4a8_moe_route and
  * w4a8_moe_permute on the same arguments, with the same results.  For decode
- * batches (T*k <= 1024 and H <= 8192) they run as one kernel: the quantizer
+ * batches (T*k <= 4096 and H <= 8192) they run as one kernel: the quantizer
  * and the router side by side, and the router workgroup that finishes last
  * sorts the routed rows; otherwise as the three kernels.
  *   counter : one uint32 on the device, 4-byte aligned, zero before the

@@ -1,4 +1,4 @@
-// Layer steps 1, 2 and 3 in one launch, for decode batches (T k <= 1024 routed
+// Layer steps 1, 2 and 3 in one launch, for decode batches (T k <= 4096 routed
 // rows, H <= 8192).
 //
 // Steps 1 and 2 share no data, so one grid holds both: workgroups 0 .. T-1
@@ -64,7 +64,7 @@ static void launch_front_slots(const FrontArgs& f, hipStream_t stream) {
 }
 
 bool front_fits(int64_t T, int64_t H, int k) {
-  return T >= 1 && T * k <= kPermBlock && ((H >> 3) + kRowThreads - 1) / kRowThreads <= 4;
+  return T >= 1 && T * k <= kPermSmallMax && ((H >> 3) + kRowThreads - 1) / kRowThreads <= 4;
 }
 
 hipError_t launch_front(const FrontArgs& f, bool int8, hipStream_t stream) {

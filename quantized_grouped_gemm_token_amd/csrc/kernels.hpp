@@ -65,7 +65,7 @@ hipError_t launch_requant(const float* act, const float* pmax, int64_t M, int64_
 hipError_t launch_requant_i8(const float* act, const float* pmax, int64_t M, int64_t I, int8_t* q, float* s,
                              int32_t* rowsum, hipStream_t stream);
 // layer steps 1-3 in one launch (front.hip); front_fits tells whether a shape
-// qualifies (T k <= 1024 routed rows, H <= 8192)
+// qualifies (T k <= 4096 routed rows, H <= 8192)
 struct FrontArgs {
   const uint16_t* x;
   int64_t T, H, ld;

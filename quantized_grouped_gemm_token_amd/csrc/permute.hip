@@ -4,7 +4,7 @@
 // parallelism is required for W4A8: "GLM-5.3-W4A8" card, sections 性能 and
 // 部署); inside one GPU that dispatch is this permutation.
 //
-// Up to 1024 routed indices (decode batches) take one launch that does all
+// Up to 4096 routed indices (decode batches) take one launch that does all
 // three steps in one block; more take three launches, all deterministic (no
 // order-dependent atomics):
 //   1. count   -- one block per 1024 routed indices: per-expert counts of the
@@ -93,7 +93,7 @@ __global__ __launch_bounds__(kPermThreads) void permute_scatter_kernel(const int
   permute_scatter_rounds(ids, R, k, E, (int64_t)blockIdx.x * kPermBlock, run, wcnt, row_token, inv_pos);
 }
 
-// all three steps in one block when R <= kPermBlock (permute_small.hpp)
+// all three steps in one block when R <= kPermSmallMax (permute_small.hpp)
 __global__ __launch_bounds__(kPermThreads) void permute_small_kernel(const int32_t* __restrict__ ids, int64_t R,
                                                                       int k, int E,
                                                                       int32_t* __restrict__ offsets,
@@ -109,7 +109,7 @@ int64_t permute_workspace_bytes(int64_t R, int E) {
 
 hipError_t launch_permute(const int32_t* ids, int64_t R, int k, int E, int32_t* offsets, int32_t* row_token,
                           int32_t* inv_pos, int32_t* counts, hipStream_t stream) {
-  if (R <= kPermBlock) {
+  if (R <= kPermSmallMax) {
     hipLaunchKernelGGL(permute_small_kernel, dim3(1), dim3(kPermThreads), 0, stream, ids, R, k, E, offsets,
                        row_token, inv_pos);
     return hipGetLastError();

@@ -66,9 +66,11 @@ __device__ __forceinline__ void permute_scatter_rounds(const int32_t* __restrict
   }
 }
 
-// All three steps in one block when R <= kPermBlock (one block of indices):
-// counts in LDS, the exclusive scan over experts (4 consecutive experts per
-// thread, then a wavefront scan and the 4 wave totals), then the scatter.
+// All three steps in one block when R <= kPermSmallMax: counts in LDS, the
+// exclusive scan over experts (4 consecutive experts per thread, then a
+// wavefront scan and the 4 wave totals), then the scatter of each block of
+// kPermBlock indices in order (run[] carries every expert's next row across them).
+constexpr int64_t kPermSmallMax = 4 * kPermBlock;
 __device__ __forceinline__ void permute_small(const int32_t* __restrict__ ids, int64_t R, int k, int E,
                                               int32_t* __restrict__ offsets, int32_t* __restrict__ row_token,
                                               int32_t* __restrict__ inv_pos) {
@@ -108,7 +110,8 @@ __device__ __forceinline__ void permute_small(const int32_t* __restrict__ ids, i
   }
   if (tid == kPermThreads - 1) offsets[E] = excl;    // E <= 4 * 256: the last thread ends the scan
   __syncthreads();
-  permute_scatter_rounds(ids, R, k, E, 0, run, wcnt, row_token, inv_pos);
+  for (int64_t base = 0; base < R; base += kPermBlock)
+    permute_scatter_rounds(ids, R, k, E, base, run, wcnt, row_token, inv_pos);
 }
 
 }  // namespace w4a8

@@ -1,6 +1,6 @@
 """Steps 1-3 in one call (w4a8_moe_front / w4a8_moe_front_i8) against the oracle.
 
-The decode shapes (T*k <= 1024, H <= 8192) run the fused kernel, whose last
+The decode shapes (T*k <= 4096, H <= 8192) run the fused kernel, whose last
 routing workgroup sorts the routed rows; the others run the three kernels.
 Three calls in a row on one counter, the last on new inputs, must each give
 the oracle's codes, routing and permutation, and leave the counter at zero.
@@ -24,7 +24,8 @@ def _bits(x):
     (128, 6144, 256, 8, False), (128, 6144, 256, 8, True),       # the decode workload, both quantizers
     (16, 256, 8, 2, False), (100, 1024, 100, 6, False), (64, 2048, 500, 8, True), (30, 512, 1024, 16, False),
     (1, 128, 4, 1, False), (127, 8192, 256, 8, True),             # one token; the largest fused row
-    (200, 1024, 256, 8, False), (64, 12288, 64, 4, True),         # three kernels: T*k > 1024; H > 8192
+    (200, 1024, 256, 8, False), (512, 1024, 64, 8, True),         # 1600 and 4096 routed rows: still one kernel
+    (600, 512, 256, 8, False), (64, 12288, 64, 4, True),          # three kernels: T*k > 4096; H > 8192
 ])
 def test_front_matches_oracle(T, H, E, k, int8, rng):
     counter = torch.zeros((1,), dtype=torch.int32, device="cuda:0")

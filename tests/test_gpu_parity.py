@@ -93,7 +93,8 @@ def test_route(T, E, k, renorm, rng):
 
 # ------------------------------------------------------------------ step 3
 @pytest.mark.parametrize("T,E,k", [(16, 8, 2), (128, 256, 8), (3000, 256, 8), (1500, 1024, 8), (700, 3, 2),
-                                   (2048, 256, 8), (127, 256, 8), (100, 1024, 8), (1, 1024, 1), (129, 256, 8)])
+                                   (2048, 256, 8), (127, 256, 8), (100, 1024, 8), (1, 1024, 1), (129, 256, 8),
+                                   (500, 256, 8), (512, 1024, 8), (513, 256, 8)])   # one block up to 4096 indices
 def test_permute(T, E, k, rng):
     ids = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
     if T == 700:
@@ -105,7 +106,7 @@ def test_permute(T, E, k, rng):
         assert np.array_equal(host(g), w_), name
 
 
-@pytest.mark.parametrize("T,E,k", [(100, 64, 4), (700, 256, 8)])     # the one-block and the three-launch paths
+@pytest.mark.parametrize("T,E,k", [(100, 64, 4), (700, 256, 8), (1000, 256, 8)])   # one block; three launches
 def test_permute_skips_ids_out_of_range(T, E, k, rng):
     ids = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
     bad = rng.random(ids.shape) < 0.05
