@@ -20,14 +20,15 @@ def _bits(x):
     return torch.from_numpy(x.astype(np.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
 
 
-@pytest.mark.parametrize("T,H,E,k,int8", [
+@pytest.mark.parametrize("T,H,E,k,int8,renorm", [(128, 6144, 256, 8, False, False), (100, 1024, 100, 6, True, False)] + [
+    c + (True,) for c in [
     (128, 6144, 256, 8, False), (128, 6144, 256, 8, True),       # the decode workload, both quantizers
     (16, 256, 8, 2, False), (100, 1024, 100, 6, False), (64, 2048, 500, 8, True), (30, 512, 1024, 16, False),
     (1, 128, 4, 1, False), (127, 8192, 256, 8, True),             # one token; the largest fused row
     (200, 1024, 256, 8, False), (512, 1024, 64, 8, True),         # 1600 and 4096 routed rows: still one kernel
     (600, 512, 256, 8, False), (64, 12288, 64, 4, True),          # three kernels: T*k > 4096; H > 8192
-])
-def test_front_matches_oracle(T, H, E, k, int8, rng):
+]])
+def test_front_matches_oracle(T, H, E, k, int8, renorm, rng):
     counter = torch.zeros((1,), dtype=torch.int32, device="cuda:0")
     for call in range(3):
         if call != 1:   # calls 0 and 1 on the same inputs, call 2 on new ones
@@ -35,9 +36,10 @@ def test_front_matches_oracle(T, H, E, k, int8, rng):
             logits = rng.standard_normal((T, E)).astype(np.float32)
             logits[:, 5 % E] = logits[:, 2 % E]                      # forced ties
             bits = _bits(x)
-        say(f"front T={T} H={H} E={E} k={k} int8={int8} call {call}")
+        say(f"front T={T} H={H} E={E} k={k} int8={int8} renorm={renorm} call {call}")
         qx, sx, rs, ids, w, offsets, row_token, inv_pos = ops.w4a8_moe_front(bf16_to_dev(bits), to_dev(logits), k,
-                                                                             counter, int8=int8)
+                                                                             counter, renormalize=renorm,
+                                                                             int8=int8)
         if int8:
             q_ref, s_ref, r_ref = oracle.quant_act_i8(bits)
             assert np.array_equal(host(rs), r_ref)
@@ -45,7 +47,7 @@ def test_front_matches_oracle(T, H, E, k, int8, rng):
             q_ref, s_ref = oracle.quant_act(bits)
         assert np.array_equal(host(qx), q_ref)
         assert np.array_equal(host(sx).view(np.uint32), s_ref.view(np.uint32))
-        ids_ref, w_ref = oracle.route(logits, k, True)
+        ids_ref, w_ref = oracle.route(logits, k, renorm)
         assert np.array_equal(host(ids), ids_ref)
         assert np.all(np.abs(host(w).astype(np.float64) - w_ref) <= 1e-6 * np.abs(w_ref))
         off_ref, rt_ref, inv_ref = oracle.permute(ids_ref, E)
