@@ -54,13 +54,18 @@ struct AChunk {
   i32x4 v[kPerThread];
 };
 
+// A thread whose row is past the expert's last one stages zeros instead: the
+// products of such a row are never stored, and each output row depends only
+// on its own activation row, so its bytes need not be read.
 template <int CH>
-__device__ __forceinline__ void a_chunk_load(AChunk<CH>& r, const uint8_t* arow_t, int g0, int ngroups) {
+__device__ __forceinline__ void a_chunk_load(AChunk<CH>& r, const uint8_t* arow_t, bool row_valid, int g0,
+                                             int ngroups) {
   const int c0 = threadIdx.x & 15;
 #pragma unroll
   for (int i = 0; i < AChunk<CH>::kPerThread; ++i) {
     const int c = c0 + 16 * i;               // 16-byte piece of the chunk's row bytes
-    if (c * 16 < ngroups * kGroup) r.v[i] = *reinterpret_cast<const i32x4*>(arow_t + g0 * kGroup + c * 16);
+    if (c * 16 < ngroups * kGroup)
+      r.v[i] = row_valid ? *reinterpret_cast<const i32x4*>(arow_t + g0 * kGroup + c * 16) : i32x4{0, 0, 0, 0};
   }
 }
 
@@ -194,8 +199,9 @@ __global__ __launch_bounds__(kStreamThreads, 3) void gg_stream_kernel(const uint
   }
 
   for (int m0 = r0; m0 < r1; m0 += 16) {
-    // activation row staged by this thread (rows past the end repeat the last one; never stored)
+    // activation row staged by this thread (rows past the end are zeros; never stored)
     const int p_t = min(m0 + (int)(threadIdx.x >> 4), r1 - 1);
+    const bool row_valid = m0 + (int)(threadIdx.x >> 4) < r1;
     const uint8_t* arow_t = a + (int64_t)(a_rows ? a_rows[p_t] : p_t) * K;
     using Acc = std::conditional_t<kInt8, i32x4, v4f>;
     Acc acc[NS];
@@ -205,7 +211,7 @@ __global__ __launch_bounds__(kStreamThreads, 3) void gg_stream_kernel(const uint
     const int nchunks = (G + 2 * CH - 1) / (2 * CH);
     {
       AChunk<CH> ar;
-      a_chunk_load(ar, arow_t, 0, min(G, 2 * CH));
+      a_chunk_load(ar, arow_t, row_valid, 0, min(G, 2 * CH));
       a_chunk_store<CH, kMx>(ar, sm, 0, min(G, 2 * CH));
     }
     __syncthreads();
@@ -216,7 +222,7 @@ __global__ __launch_bounds__(kStreamThreads, 3) void gg_stream_kernel(const uint
       AChunk<CH> next;
       const bool has_next = ci + 1 < nchunks;
       const int ng_next = has_next ? min(2 * CH, G - g0 - 2 * CH) : 0;
-      if (has_next) a_chunk_load(next, arow_t, g0 + 2 * CH, ng_next);
+      if (has_next) a_chunk_load(next, arow_t, row_valid, g0 + 2 * CH, ng_next);
       if (active) {
         // group scales of this chunk (bits: fp32, or MX words shifted so that byte 0 is the lane's quarter)
         uint32_t sc[NS][2 * CH];
