@@ -380,9 +380,9 @@ static void launch_variant(const GemmArgs& g, hipStream_t stream) {
 
 hipError_t launch_gg_stream(const GemmArgs& g, hipStream_t stream) {
   if (g.pmax) {
-    // the fused gate/up GEMM: chunks of 4 groups for the FP8 forms (128 VGPRs or
-    // fewer, so 4 waves per SIMD; 1.1% faster at decode), of 8 for the INT8 one
-    if (g.a_rowsum) launch_variant<2, 4, kFormChannel, true>(g, stream);
+    // the fused gate/up GEMM: chunks of 4 groups (128 VGPRs or fewer, so 4 waves
+    // per SIMD; 1.1% faster at decode for the FP8 forms, 0.4% for the INT8 one)
+    if (g.a_rowsum) launch_variant<2, 2, kFormChannel, true>(g, stream);
     else if (g.mx) launch_variant<2, 2, kFormMx, true>(g, stream);
     else launch_variant<2, 2, kFormG128, true>(g, stream);
   } else {
