@@ -10,7 +10,7 @@ from .w4a8_oracle import (E4M3_VALUES, FP8_MAX, GROUP, SHRINK_RATIOS,  # noqa: F
                           grouped_gemm_exact_groups, int4_pack, int4_unpack, moe_layer,
                           permute, quant_act, quant_rows, quantize_int4_g128, relative_l2,
                           route, swiglu, swiglu_f32, unpermute)
-from .channel_int8_oracle import (grouped_gemm_i8, moe_layer_i8, quant_act_i8,  # noqa: F401
-                                  quant_rows_i8, quantize_int4_channel, swiglu_i8)
+from .channel_int8_oracle import (code_row_sums, grouped_gemm_i8, moe_layer_i8,  # noqa: F401
+                                  quant_act_i8, quant_rows_i8, quantize_int4_channel, swiglu_i8)
 from .mxfp4_oracle import (dequant_mxfp4, e2m1_decode, e2m1_encode, fp4_pack, fp4_unpack,  # noqa: F401
                            grouped_gemm_mxfp4, moe_layer_mxfp4, quantize_mxfp4)

@@ -38,25 +38,29 @@ INT8_MAX = 127.0
 INT4_MAX = 7.0
 
 
-def quant_rows_i8(x) -> tuple[np.ndarray, np.ndarray, np.ndarray]:
-    """Per-row INT8 codes of an fp32 matrix [M, K].
-
-    Returns (codes int8 [M, K], scale fp32 [M], row sum of the codes int32 [M]).
-    The row sums are what the integer GEMM needs to undo the +8 offset of the
-    stored weight nibbles; they are part of the quantized activation.
-    """
+def quant_rows_i8(x) -> tuple[np.ndarray, np.ndarray]:
+    """Per-row INT8 codes of an fp32 matrix [M, K] -> (codes int8 [M, K], scale fp32 [M])."""
     x = np.asarray(x, dtype=np.float32)
     amax = np.abs(x).max(axis=1) if x.shape[1] else np.zeros(x.shape[0], np.float32)
     scale = np.where(amax > 0, (amax / np.float32(INT8_MAX)).astype(np.float32), np.float32(1.0))
     q = np.rint((x / scale[:, None]).astype(np.float32))
     codes = np.clip(q, -INT8_MAX, INT8_MAX).astype(np.int8)
-    rowsum = codes.astype(np.int64).sum(axis=1).astype(np.int32)
-    return codes, scale.astype(np.float32), rowsum
+    return codes, scale.astype(np.float32)
 
 
-def quant_act_i8(x_bf16_bits) -> tuple[np.ndarray, np.ndarray, np.ndarray]:
-    """Step 1 of the variant: bf16 activations [T, H] -> INT8 codes, scales, row sums."""
+def quant_act_i8(x_bf16_bits) -> tuple[np.ndarray, np.ndarray]:
+    """Step 1 of the variant: bf16 activations [T, H] -> INT8 codes and per-token scales."""
     return quant_rows_i8(bf16_bits_to_f32(x_bf16_bits))
+
+
+def code_row_sums(codes) -> np.ndarray:
+    """Sum of each row's INT8 codes (int32 [M]).
+
+    Not a step of the method: the library's INT8 calls return these sums next
+    to the codes (its GEMM subtracts 8 times them to undo the uint4b8 offset),
+    and the tests compare them with this plain sum.
+    """
+    return np.asarray(codes, dtype=np.int64).sum(axis=1).astype(np.int32)
 
 
 def quantize_int4_channel(W) -> tuple[np.ndarray, np.ndarray]:
@@ -97,7 +101,7 @@ def grouped_gemm_i8(a_codes, a_scale, a_rows, offsets, w_packed, w_scale) -> np.
     return out
 
 
-def swiglu_i8(h) -> tuple[np.ndarray, np.ndarray, np.ndarray]:
+def swiglu_i8(h) -> tuple[np.ndarray, np.ndarray]:
     """Step 5 of the variant: silu(gate) * up in fp64 -> fp32, then per-row INT8 codes."""
     return quant_rows_i8(swiglu_f32(h))
 
@@ -109,13 +113,13 @@ def moe_layer_i8(x_bf16_bits, logits, w13, s13, w2, s2, k: int, renormalize: boo
     s2 [E, H] are the per-channel scales.
     """
     E = w13.shape[0]
-    qx, sx, rx = quant_act_i8(x_bf16_bits)
+    qx, sx = quant_act_i8(x_bf16_bits)
     ids, w = route(logits, k, renormalize)
     offsets, row_token, inv_pos = permute(ids, E)
     h = grouped_gemm_i8(qx, sx, row_token, offsets, w13, s13)
     a_f32 = swiglu_f32(h)
-    qa, sa, ra = quant_rows_i8(a_f32)
+    qa, sa = quant_rows_i8(a_f32)
     o = grouped_gemm_i8(qa, sa, None, offsets, w2, s2)
     y = unpermute(o, inv_pos, w)
-    return dict(qx=qx, sx=sx, rx=rx, ids=ids, w=w, offsets=offsets, row_token=row_token, inv_pos=inv_pos,
-                h=h, a_f32=a_f32, qa=qa, sa=sa, ra=ra, o=o, y=y)
+    return dict(qx=qx, sx=sx, ids=ids, w=w, offsets=offsets, row_token=row_token, inv_pos=inv_pos,
+                h=h, a_f32=a_f32, qa=qa, sa=sa, o=o, y=y)

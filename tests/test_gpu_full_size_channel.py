@@ -61,7 +61,8 @@ def test_channel_routing_and_tokens(index):
     assert np.array_equal(got["ids"], ids)
     assert np.array_equal(got["offsets"], offsets)
     assert np.array_equal(got["row_token"], row_token) and np.array_equal(got["inv_pos"], inv_pos)
-    qx, sx, rx = oracle.quant_act_i8(wl.x_bf16)
+    qx, sx = oracle.quant_act_i8(wl.x_bf16)
+    rx = oracle.code_row_sums(qx)
     assert np.array_equal(got["qx"], qx) and np.array_equal(got["rx"], rx)
     assert np.array_equal(got["sx"].view(np.uint32), sx.view(np.uint32))
     T = wl.shape.T
@@ -84,12 +85,13 @@ def test_channel_sampled_rows_per_call(index):
     sub_off = np.zeros(sh.E + 1, np.int32)
     np.add.at(sub_off, experts + 1, 1)
     sub_off = np.cumsum(sub_off).astype(np.int32)
-    qx, sx, _ = oracle.quant_act_i8(wl.x_bf16[got["row_token"][P]])
+    qx, sx = oracle.quant_act_i8(wl.x_bf16[got["row_token"][P]])
     say(f"config {index}: per-channel oracle gate/up on {P.size} rows")
     a32 = oracle.swiglu_f32(oracle.grouped_gemm_i8(qx, sx, None, sub_off, wl.w13, s13))
     assert_float_parity(got["act"][P], a32, f"config {index} per-channel gate/up + SwiGLU", fro_tight=GEMM_FRO_TIGHT)
     assert np.array_equal(got["pmax"][P].max(axis=1), np.abs(got["act"][P]).max(axis=1))
-    qa, sa, ra = oracle.quant_rows_i8(a32)
+    qa, sa = oracle.quant_rows_i8(a32)
+    ra = oracle.code_row_sums(qa)
     pm = np.abs(a32).reshape(a32.shape[0], -1, 64).max(axis=2).astype(np.float32)
     rq, rs, rr = ops.w4a8_moe_requant_i8(to_dev(a32), to_dev(pm))
     assert np.array_equal(host(rq), qa) and np.array_equal(host(rr), ra)

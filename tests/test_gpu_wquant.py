@@ -105,3 +105,32 @@ def test_quantize_empty():
     w = torch.empty((0, 256), dtype=torch.float32, device="cuda:0")
     words, scales = ops.w4a8_moe_quantize_weights(w)
     assert words.shape == (0, 32) and scales.shape == (0, 2)
+
+
+def test_quantize_hand_computed_groups():
+    """The groups whose results are worked out by hand in test_oracle_wquant.py
+    (ties to even, the -8 clamp deciding the ratio, ties keeping the larger
+    ratio), checked on the GPU against the literal results."""
+    ints = np.tile(np.arange(-7, 8, dtype=np.float32), 8)
+    half = np.float32([0.5, 1.5, 2.5, 3.5, -0.5, -1.5, -2.5, -3.5])
+    mult = np.resize(np.arange(-7, 8, dtype=np.float32), 127)
+    W = np.zeros((2, 256), np.float32)
+    W[0, :128] = np.concatenate([ints, half])                           # ratio 1.00, half to even
+    W[0, 128:] = np.concatenate([np.float32([-8.0]), mult * np.float32(0.8)])   # ratio 0.70, -10 -> -8
+    W[1, 128:] = np.tile(np.arange(-7, 8, dtype=np.float32), 9)[:128]   # exact at ratio 1.00
+    # W[1, :128] stays zero: an 11-way tie, kept at ratio 1.00
+    say("quantize_weights hand-computed groups")
+    words, scales = ops.w4a8_moe_quantize_weights(to_dev(W), mse_clip=True)
+    words, scales = host(words), host(scales)
+    assert scales.tolist() == [[np.float32(1.0), np.float32(0.8)], [np.float32(1.0 / 7.0), np.float32(1.0)]]
+    q = oracle.int4_unpack(words)
+    assert np.array_equal(q[0, :120], ints.astype(np.int8))
+    assert q[0, 120:128].tolist() == [0, 2, 2, 4, 0, -2, -2, -4]
+    assert q[0, 128] == -8 and np.array_equal(q[0, 129:], mult.astype(np.int8))
+    assert not q[1, :128].any() and np.array_equal(q[1, 128:], W[1, 128:].astype(np.int8))
+    # round to nearest without the clip search: scale fl32(amax / 7)
+    Wr = np.zeros((1, 128), np.float32)
+    Wr[0, :15] = [7.0, 0.5, 1.5, 2.5, 3.5, 4.5, 5.5, 6.5, -0.5, -1.5, -2.5, -3.5, -4.5, -5.5, -6.5]
+    words, scales = ops.w4a8_moe_quantize_weights(to_dev(Wr), mse_clip=False)
+    assert host(scales)[0, 0] == np.float32(1.0)
+    assert oracle.int4_unpack(host(words))[0, :15].tolist() == [7, 0, 2, 2, 4, 4, 6, 6, 0, -2, -2, -4, -4, -6, -6]

@@ -20,7 +20,8 @@ def _act(rng, M, K):
 
 def test_quant_rows_i8_matches_torch_rounding(rng):
     x = _act(rng, 64, 512)
-    codes, scale, rowsum = oracle.quant_rows_i8(x)
+    codes, scale = oracle.quant_rows_i8(x)
+    rowsum = oracle.code_row_sums(codes)
     t = torch.from_numpy(x)
     s = (t.abs().amax(dim=1) / 127.0)                          # fp32, as torch computes it
     ref = torch.clamp(torch.round(t / s[:, None]), -127, 127).to(torch.int8).numpy()
@@ -31,18 +32,19 @@ def test_quant_rows_i8_matches_torch_rounding(rng):
 
 def test_quant_rows_i8_invariants(rng):
     x = _act(rng, 32, 256)
-    codes, scale, _ = oracle.quant_rows_i8(x)
+    codes, scale = oracle.quant_rows_i8(x)
     assert np.all(np.abs(codes).max(axis=1) == 127)           # the largest element lands on +-127
-    c_neg, s_neg, r_neg = oracle.quant_rows_i8(-x)
+    c_neg, s_neg = oracle.quant_rows_i8(-x)
     assert np.array_equal(c_neg, -codes) and np.array_equal(s_neg, scale)
-    c_2, s_2, _ = oracle.quant_rows_i8(x * np.float32(2.0 ** 5))
+    c_2, s_2 = oracle.quant_rows_i8(x * np.float32(2.0 ** 5))
     assert np.array_equal(c_2, codes) and np.array_equal(s_2, scale * np.float32(2.0 ** 5))
     err = np.abs(x.astype(np.float64) - codes * scale.astype(np.float64)[:, None])
     assert np.all(err <= 0.5 * scale.astype(np.float64)[:, None] * (1 + 1e-6))
 
 
 def test_quant_rows_i8_zero_row():
-    codes, scale, rowsum = oracle.quant_rows_i8(np.zeros((2, 128), np.float32))
+    codes, scale = oracle.quant_rows_i8(np.zeros((2, 128), np.float32))
+    rowsum = oracle.code_row_sums(codes)
     assert np.all(codes == 0) and np.all(scale == 1.0) and np.all(rowsum == 0)
 
 
@@ -70,7 +72,7 @@ def _problem(rng, E, N, K, counts, gather):
     R = int(np.sum(counts))
     offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
     x = _act(rng, T if gather else R, K)
-    codes, scale, _ = oracle.quant_rows_i8(x)
+    codes, scale = oracle.quant_rows_i8(x)
     rows = rng.integers(0, T, size=R).astype(np.int32) if gather else None
     q = rng.integers(-8, 8, size=(E, N, K)).astype(np.int8)
     words = np.stack([oracle.int4_pack(q[e]) for e in range(E)])
@@ -113,7 +115,7 @@ def test_moe_layer_i8_brute_force_tiny(rng):
     s13 = rng.lognormal(-4, 0.5, size=(E, 2 * I)).astype(np.float32)
     s2 = rng.lognormal(-4, 0.5, size=(E, H)).astype(np.float32)
     res = oracle.moe_layer_i8(xb, logits, w13, s13, w2, s2, k)
-    qx, sx, _ = oracle.quant_act_i8(xb)
+    qx, sx = oracle.quant_act_i8(xb)
     ids, w = oracle.route(logits, k)
     for t in range(T):
         y = np.zeros(H)
@@ -121,7 +123,7 @@ def test_moe_layer_i8_brute_force_tiny(rng):
             e = ids[t, j]
             h = (qx[t].astype(np.float64) * float(sx[t])) @ (q13[e].astype(np.float64) * s13[e][:, None]).T
             a = oracle.swiglu_f32(h.astype(np.float32)[None, :])
-            qa, sa, _ = oracle.quant_rows_i8(a)
+            qa, sa = oracle.quant_rows_i8(a)
             o = (qa[0].astype(np.float64) * float(sa[0])) @ (q2[e].astype(np.float64) * s2[e][:, None]).T
             y += float(w[t, j]) * o.astype(np.float32).astype(np.float64)
         assert np.allclose(res["y"][t], y, rtol=1e-5, atol=1e-6 * np.abs(y).max())
