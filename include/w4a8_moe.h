@@ -20,9 +20,20 @@
  *   - Array pointers are DEVICE pointers; arrays are row-major, contiguous
  *     unless a leading dimension is given.  "u8 E4M3" arrays hold OCP
  *     E4M3FN codes (bias 7, max 448, no infinities).
- *   - Packed weights: int32 [E][N][K/8]; the nibble for k sits at bits
- *     4*(k mod 8) of word k/8 and holds q + 8 (q in -8..7).
- *     Group scales: fp32 [E][N][K/128].
+ *   - Expert weights come in one of two formats, and each GEMM call names
+ *     the one it takes:
+ *       stored (the calls without "_prepacked"): the format the pages
+ *         store, INT4 int32 [E][N][K/8] words whose nibble for k sits at
+ *         bits 4*(k mod 8) of word k/8 and holds q + 8 (q in -8..7), with
+ *         group scales fp32 [E][N][K/128]; MXFP4 u8 [E][N][K/2] codes and
+ *         u8 [E][N][K/32] E8M0 scales;
+ *       GEMM storage (the "_prepacked" calls): the same bytes permuted once
+ *         by w4a8_moe_prepack_int4 / w4a8_moe_prepack_mxfp4, which the fast
+ *         kernels read (described before w4a8_moe_prepack_int4).
+ *     The two formats have the same size and the library cannot tell them
+ *     apart from a pointer: weights in the wrong format give wrong numbers
+ *     with status W4A8_OK.  The stored-format calls run the streaming kernel
+ *     only (correct at any size, slower for many rows per expert).
  *   - The caller owns every buffer, including workspaces.  The library does
  *     not allocate, free, or keep any pointer after a call returns.
  *   - `stream` is a hipStream_t (NULL = the default stream).  Every call
@@ -61,8 +72,8 @@ typedef enum w4a8_status {
 #define W4A8_Y_F32 0
 #define W4A8_Y_BF16 1
 
-/* algo values of w4a8_moe_grouped_gemm_algo */
-#define W4A8_GG_AUTO 0     /* choose from M_total / E                             */
+/* algo values of the _prepacked grouped GEMM calls */
+#define W4A8_GG_AUTO 0     /* choose from M_total / E (the _prepacked calls)     */
 #define W4A8_GG_STREAM 1   /* weight-streaming kernel for few rows per expert     */
 #define W4A8_GG_TILED 2    /* LDS-tiled persistent kernel for many rows per expert */
 
@@ -143,8 +154,8 @@ int w4a8_moe_front_i8(const uint16_t* x_bf16, int64_t T, int64_t H, int64_t ld_x
 
 /*
  * ---- GEMM storage of the expert weights ------------------------------------
- * The grouped GEMMs read the 4-bit weights in a permuted order, written once
- * by a prepack call: the 64 packed bytes of one 128-wide K group of 16
+ * The "_prepacked" grouped GEMMs read the 4-bit weights in a permuted order,
+ * written once by a prepack call: the 64 packed bytes of one 128-wide K group of 16
  * consecutive weight rows are one contiguous 1 KB piece, and the per-group
  * scales are group-major.  (The INT4 form the pages store, int32 uint4b8
  * words row by row, is the input of w4a8_moe_prepack_int4.)  G = K/128:
@@ -175,9 +186,11 @@ int w4a8_moe_prepack_int4(const int32_t* w_packed, const float* w_scale, int32_t
                           int32_t* w_blk, float* s_blk, void* stream);
 
 /*
- * Steps 4 and 6 -- grouped W4A8 GEMM over the experts' row ranges.
+ * Steps 4 and 6 -- grouped W4A8 GEMM over the experts' row ranges, on the
+ * weights as stored.
  * ("GLM-5.3-W4A8" card, section 量化方式: INT4 weights become FP8 inside
- * the kernel, FP8 matrix multiply, no BF16 dequantization.)
+ * the kernel, FP8 matrix multiply, no BF16 dequantization; the weights are
+ * compressed-tensors pack-quantized uint4b8 in int32 with group size 128.)
  *   For expert e and each row p in [offsets[e], offsets[e+1]), with
  *   r = a_rows ? a_rows[p] : p:
  *     out[p, n] = a_scale[r] * sum_g w_scale[e, n, g] *
@@ -186,28 +199,37 @@ int w4a8_moe_prepack_int4(const int32_t* w_packed, const float* w_scale, int32_t
  *              a_rows when it is not NULL).   a_scale : fp32 [*].
  *   a_rows   : int32 [M_total] or NULL.
  *   offsets  : int32 [E+1] on the device, offsets[E] == M_total.
- *   w_packed : GEMM storage int32 [E][N/16][K/128][16][16] of q + 8
- *              (w4a8_moe_prepack_int4), 16-byte aligned.
- *   w_scale  : GEMM storage fp32 [E][K/128][N].
+ *   w_packed : int32 [E][N][K/8]: nibble k of row n at bits 4 (k mod 8) of
+ *              word k/8, holding q + 8; 16-byte aligned.
+ *   w_scale  : fp32 [E][N][K/128].
  *   out      : fp32 [M_total][N], 16-byte aligned.
- *   Rules    : M_total >= 0, 1 <= E <= 1024, N > 0, N % 64 == 0, K > 0,
+ *   Rules    : M_total >= 0, 1 <= E <= 1024, N > 0, N % 16 == 0, K > 0,
  *              K % 128 == 0.  Unchecked: with a_rows, a_rows[p] * K < 2^32.
  *   Accumulation is fp32 per 128-wide group, then the group scale is
  *   applied in fp32.  The matrix cores' FP8 dot products round within about
  *   1e-5 of the group's sum of |products|, so results agree with the exact
  *   sum to about 1e-5 relative (Frobenius norm over a matrix).
+ *   Runs the weight-streaming kernel, which reads each expert's weights once
+ *   per 16 of its rows: right for decode; for many rows per expert, prepack
+ *   the weights and call w4a8_moe_grouped_gemm_prepacked.
  */
 int w4a8_moe_grouped_gemm(const uint8_t* a, const float* a_scale, const int32_t* a_rows,
                           int64_t M_total, const int32_t* offsets, int32_t E,
                           const int32_t* w_packed, const float* w_scale,
                           int64_t N, int64_t K, float* out, void* stream);
 
-/* As w4a8_moe_grouped_gemm, with the kernel chosen by `algo` (W4A8_GG_*).
- * Every algo computes the same result; the choice only affects speed. */
-int w4a8_moe_grouped_gemm_algo(const uint8_t* a, const float* a_scale, const int32_t* a_rows,
-                               int64_t M_total, const int32_t* offsets, int32_t E,
-                               const int32_t* w_packed, const float* w_scale,
-                               int64_t N, int64_t K, float* out, int32_t algo, void* stream);
+/*
+ * The same on weights in the GEMM storage (w4a8_moe_prepack_int4):
+ *   w_blk : int32 [E][N/16][K/128][16][16], 16-byte aligned.
+ *   s_blk : fp32 [E][K/128][N].
+ *   algo  : W4A8_GG_AUTO, W4A8_GG_STREAM or W4A8_GG_TILED; every algo
+ *           computes the same result, the choice only affects speed.
+ *   Rules : as w4a8_moe_grouped_gemm, with N % 64 == 0.
+ */
+int w4a8_moe_grouped_gemm_prepacked(const uint8_t* a, const float* a_scale, const int32_t* a_rows,
+                                    int64_t M_total, const int32_t* offsets, int32_t E,
+                                    const int32_t* w_blk, const float* s_blk,
+                                    int64_t N, int64_t K, float* out, int32_t algo, void* stream);
 
 /*
  * Step 5 -- SwiGLU of the gate/up output and per-row FP8 re-quantization.
@@ -274,7 +296,7 @@ int w4a8_moe_quant_act_i8(const uint16_t* x_bf16, int64_t T, int64_t H, int64_t 
                           int8_t* qx, float* sx, int32_t* rowsum, void* stream);
 
 /*
- * Steps 4 and 6, INT8 -- grouped GEMM with per-channel INT4 weights.
+ * Steps 4 and 6, INT8 -- grouped GEMM with per-channel INT4 weights, as stored.
  *   For expert e and each row p in [offsets[e], offsets[e+1]), with
  *   r = a_rows ? a_rows[p] : p:
  *     out[p, n] = a_scale[r] * w_scale[e, n] * sum_k a[r, k] * q[e, n, k]
@@ -282,15 +304,22 @@ int w4a8_moe_quant_act_i8(const uint16_t* x_bf16, int64_t T, int64_t H, int64_t 
  *   (K <= 2^20), then the two scales in fp32.
  *   a : int8 [*][K], 16-byte aligned.  a_scale : fp32 [*].  a_rowsum : int32 [*].
  *   a_rows, offsets : as in w4a8_moe_grouped_gemm.
- *   w_packed : GEMM storage int32 [E][N/16][K/128][16][16] uint4b8 (w4a8_moe_prepack_int4),
- *              16-byte aligned.  w_scale : fp32 [E][N].
- *   out : fp32 [M_total][N], 16-byte aligned.  algo : W4A8_GG_*.
+ *   w_packed : int32 [E][N][K/8] uint4b8 words as stored, 16-byte aligned.
+ *   w_scale : fp32 [E][N].  out : fp32 [M_total][N], 16-byte aligned.
  *   Rules : as in w4a8_moe_grouped_gemm, and K <= 2^20.
  */
 int w4a8_moe_grouped_gemm_i8(const int8_t* a, const float* a_scale, const int32_t* a_rowsum,
                              const int32_t* a_rows, int64_t M_total, const int32_t* offsets, int32_t E,
                              const int32_t* w_packed, const float* w_scale, int64_t N, int64_t K,
-                             float* out, int32_t algo, void* stream);
+                             float* out, void* stream);
+
+/* The same on weights in the GEMM storage (w_blk int32 [E][N/16][K/128][16][16],
+ * w4a8_moe_prepack_int4 with no scales); per-channel scales w_scale [E][N] as
+ * they are.  algo : W4A8_GG_*.  Rules : N % 64 == 0, otherwise as above. */
+int w4a8_moe_grouped_gemm_i8_prepacked(const int8_t* a, const float* a_scale, const int32_t* a_rowsum,
+                                       const int32_t* a_rows, int64_t M_total, const int32_t* offsets, int32_t E,
+                                       const int32_t* w_blk, const float* w_scale, int64_t N, int64_t K,
+                                       float* out, int32_t algo, void* stream);
 
 /*
  * Step 5, INT8 -- SwiGLU of the gate/up output, then the step-1 INT8 rule
@@ -324,33 +353,45 @@ int w4a8_moe_quantize_weights_channel(const float* w, int64_t rows, int64_t K, i
  */
 
 /*
- * Steps 4 + 5a, group-128 FP8 form.
+ * Steps 4 + 5a, group-128 FP8 form, weights as stored.
  *   For expert e and row p in [offsets[e], offsets[e+1]) (r = a_rows ? a_rows[p] : p):
  *     gate[n] = h[p, n], up[n] = h[p, I + n] of w4a8_moe_grouped_gemm with N = 2I;
  *     act[p, n] = silu(gate[n]) * up[n], silu(z) = z / (1 + e^-z), fp32 (hardware
  *     exponential and reciprocal: within a few ulp of the exact value);
  *     act_pmax[p, s], s < I/64: maxima of |act[p, :]| over parts of the row, whose
  *     maximum is max_n |act[p, n]| (every entry is written; no zeroing needed).
- *   a, a_scale, a_rows, offsets, algo : as in w4a8_moe_grouped_gemm.
- *   w13 : GEMM storage of the int32 uint4b8 rows [E][2I] (gate rows 0..I-1, up rows
- *         I..2I-1), 16-byte aligned.
- *   s13 : GEMM storage fp32 [E][K/128][2I].
+ *   a, a_scale, a_rows, offsets : as in w4a8_moe_grouped_gemm.
+ *   w13 : int32 [E][2I][K/8] as stored (gate rows 0..I-1, up rows I..2I-1),
+ *         16-byte aligned.   s13 : fp32 [E][2I][K/128].
  *   act : fp32 [M_total][I], 16-byte aligned.  act_pmax : fp32 [M_total][I/64], 4-byte aligned.
  *   Rules : I > 0, I % 128 == 0, K % 128 == 0, 1 <= E <= 1024; otherwise as in w4a8_moe_grouped_gemm.
  */
 int w4a8_moe_grouped_gemm_swiglu(const uint8_t* a, const float* a_scale, const int32_t* a_rows, int64_t M_total,
                                  const int32_t* offsets, int32_t E, const int32_t* w13, const float* s13, int64_t I,
-                                 int64_t K, float* act, float* act_pmax, int32_t algo, void* stream);
+                                 int64_t K, float* act, float* act_pmax, void* stream);
+
+/* The same on the GEMM storage of w13 (int32 [E][2I/16][K/128][16][16]) and
+ * s13 (fp32 [E][K/128][2I]); algo : W4A8_GG_*. */
+int w4a8_moe_grouped_gemm_swiglu_prepacked(const uint8_t* a, const float* a_scale, const int32_t* a_rows,
+                                           int64_t M_total, const int32_t* offsets, int32_t E, const int32_t* w13,
+                                           const float* s13, int64_t I, int64_t K, float* act, float* act_pmax,
+                                           int32_t algo, void* stream);
 
 /*
  * Steps 4 + 5a, per-channel INT8 form: as w4a8_moe_grouped_gemm_swiglu with
  * the products of w4a8_moe_grouped_gemm_i8 (a : int8 codes with row sums
- * a_rowsum; s13 : fp32 [E][2I]; K <= 2^20).
+ * a_rowsum; w13 : int32 [E][2I][K/8] as stored; s13 : fp32 [E][2I]; K <= 2^20).
  */
 int w4a8_moe_grouped_gemm_swiglu_i8(const int8_t* a, const float* a_scale, const int32_t* a_rowsum,
                                     const int32_t* a_rows, int64_t M_total, const int32_t* offsets, int32_t E,
                                     const int32_t* w13, const float* s13, int64_t I, int64_t K, float* act,
-                                    float* act_pmax, int32_t algo, void* stream);
+                                    float* act_pmax, void* stream);
+
+/* The same on the GEMM storage of w13; algo : W4A8_GG_*. */
+int w4a8_moe_grouped_gemm_swiglu_i8_prepacked(const int8_t* a, const float* a_scale, const int32_t* a_rowsum,
+                                              const int32_t* a_rows, int64_t M_total, const int32_t* offsets,
+                                              int32_t E, const int32_t* w13, const float* s13, int64_t I, int64_t K,
+                                              float* act, float* act_pmax, int32_t algo, void* stream);
 
 /*
  * Step 5b, FP8 -- the step-1 rule per row, from the row maxima of the fused GEMM:
@@ -415,28 +456,41 @@ int w4a8_moe_prepack_mxfp4(const uint8_t* w_packed, const uint8_t* w_scale, int3
                            uint8_t* w_blk, uint8_t* s_blk, void* stream);
 
 /*
- * Step 4, MXFP4 weights:
+ * Step 4, MXFP4 weights, as stored:
  *   out[p, n] = a_scale[r] * sum_k E4M3(a[r, k]) * E2M1(w[e, n, k]) * 2^(w_scale[e, n, k/32] - 127)
  *   (r = a_rows ? a_rows[p] : p; exact products, fp32 sums).
- *   a, a_scale, a_rows, offsets, out, algo : as in w4a8_moe_grouped_gemm_algo.
- *   w_packed : GEMM storage u8 [E][N/16][K/128][16][64], 16-byte aligned.
- *   w_scale : GEMM storage u8 [E][K/128][N][4], 4-byte aligned.
- *   Rules : N % 64 == 0, K % 128 == 0, 1 <= E <= 1024; errors as in w4a8_moe_grouped_gemm_algo.
+ *   a, a_scale, a_rows, offsets, out : as in w4a8_moe_grouped_gemm.
+ *   w_packed : u8 [E][N][K/2] (row-major storage above), 16-byte aligned.
+ *   w_scale : u8 [E][N][K/32], 4-byte aligned.
+ *   Rules : N % 16 == 0, K % 128 == 0, 1 <= E <= 1024; errors as in w4a8_moe_grouped_gemm.
  */
 int w4a8_moe_grouped_gemm_mxfp4(const uint8_t* a, const float* a_scale, const int32_t* a_rows, int64_t M_total,
                                 const int32_t* offsets, int32_t E, const uint8_t* w_packed, const uint8_t* w_scale,
-                                int64_t N, int64_t K, float* out, int32_t algo, void* stream);
+                                int64_t N, int64_t K, float* out, void* stream);
+
+/* The same on the GEMM storage (w_blk u8 [E][N/16][K/128][16][64], s_blk u8
+ * [E][K/128][N][4], from w4a8_moe_prepack_mxfp4); algo : W4A8_GG_*; N % 64 == 0. */
+int w4a8_moe_grouped_gemm_mxfp4_prepacked(const uint8_t* a, const float* a_scale, const int32_t* a_rows,
+                                          int64_t M_total, const int32_t* offsets, int32_t E, const uint8_t* w_blk,
+                                          const uint8_t* s_blk, int64_t N, int64_t K, float* out, int32_t algo,
+                                          void* stream);
 
 /*
  * Steps 4 + 5a, MXFP4 weights: as w4a8_moe_grouped_gemm_swiglu with the
- * products of w4a8_moe_grouped_gemm_mxfp4 (w13 : GEMM storage of the [E][2I]
- * rows, 16-byte aligned; s13 : GEMM storage of their scales, 4-byte aligned).
+ * products of w4a8_moe_grouped_gemm_mxfp4 (w13 : u8 [E][2I][K/2] as stored,
+ * 16-byte aligned; s13 : u8 [E][2I][K/32], 4-byte aligned).
  * Follow with w4a8_moe_requant.
  */
 int w4a8_moe_grouped_gemm_swiglu_mxfp4(const uint8_t* a, const float* a_scale, const int32_t* a_rows,
                                        int64_t M_total, const int32_t* offsets, int32_t E, const uint8_t* w13,
                                        const uint8_t* s13, int64_t I, int64_t K, float* act, float* act_pmax,
-                                       int32_t algo, void* stream);
+                                       void* stream);
+
+/* The same on the GEMM storage of w13 and s13; algo : W4A8_GG_*. */
+int w4a8_moe_grouped_gemm_swiglu_mxfp4_prepacked(const uint8_t* a, const float* a_scale, const int32_t* a_rows,
+                                                 int64_t M_total, const int32_t* offsets, int32_t E,
+                                                 const uint8_t* w13, const uint8_t* s13, int64_t I, int64_t K,
+                                                 float* act, float* act_pmax, int32_t algo, void* stream);
 
 /* Static name of a status code ("W4A8_OK", ...). */
 const char* w4a8_moe_status_string(int status);

@@ -210,37 +210,142 @@ int w4a8_moe_front_i8(const uint16_t* x_bf16, int64_t T, int64_t H, int64_t ld_x
                    offsets, row_token, inv_pos, workspace, workspace_bytes, counter, stream);
 }
 
-int w4a8_moe_grouped_gemm_algo(const uint8_t* a, const float* a_scale, const int32_t* a_rows, int64_t M_total,
-                               const int32_t* offsets, int32_t E, const int32_t* w_packed, const float* w_scale,
-                               int64_t N, int64_t K, float* out, int32_t algo, void* stream) {
+// ---- grouped GEMMs: three weight forms, plain or with the fused SwiGLU
+// epilogue, on the row-major stored weights or on the GEMM storage
+enum class Form { kG128, kChannel, kMx };
+
+// Checks every argument of one grouped GEMM, then launches it.  fused: N is
+// 2I (gate and up rows) and out is act [M_total][I] with pmax [M_total][I/64].
+// row_major: the weights as stored (N % 16), else the GEMM storage (N % 64).
+static int run_gemm(const char* name, Form form, bool fused, bool row_major, const void* a, const float* a_scale,
+                    const int32_t* a_rowsum, const int32_t* a_rows, int64_t M_total, const int32_t* offsets,
+                    int32_t E, const void* w, const void* s, int64_t N, int64_t K, float* out, float* pmax,
+                    int32_t algo, void* stream) {
   if (M_total < 0 || M_total >= kMaxRows)
-    return fail(W4A8_ERR_SHAPE, "grouped_gemm: M_total=%lld out of range", (long long)M_total);
-  if (E < 1 || E > 1024) return fail(W4A8_ERR_SHAPE, "grouped_gemm: E=%d must be in [1, 1024]", E);
-  if (N <= 0 || N % 64) return fail(W4A8_ERR_SHAPE, "grouped_gemm: N=%lld must be a positive multiple of 64",
-                                    (long long)N);
-  if (K <= 0 || K % 128) return fail(W4A8_ERR_SHAPE, "grouped_gemm: K=%lld must be a positive multiple of 128",
-                                     (long long)K);
-  if (algo < W4A8_GG_AUTO || algo > W4A8_GG_TILED)
-    return fail(W4A8_ERR_SHAPE, "grouped_gemm: unknown algo %d", algo);
+    return fail(W4A8_ERR_SHAPE, "%s: M_total=%lld out of range", name, (long long)M_total);
+  if (E < 1 || E > 1024) return fail(W4A8_ERR_SHAPE, "%s: E=%d must be in [1, 1024]", name, E);
+  if (fused) {
+    if (N <= 0 || (N / 2) % 128 || N >= kMaxRows)
+      return fail(W4A8_ERR_SHAPE, "%s: I=%lld must be a positive multiple of 128", name, (long long)(N / 2));
+  } else {
+    const int64_t mult = row_major ? 16 : 64;
+    if (N <= 0 || N % mult || N >= kMaxRows)
+      return fail(W4A8_ERR_SHAPE, "%s: N=%lld must be a positive multiple of %lld", name, (long long)N,
+                  (long long)mult);
+  }
+  if (K <= 0 || K % 128 || K >= kMaxRows)
+    return fail(W4A8_ERR_SHAPE, "%s: K=%lld must be a positive multiple of 128", name, (long long)K);
+  if (form == Form::kChannel && K > (int64_t)1 << 20)
+    return fail(W4A8_ERR_SHAPE, "%s: K=%lld would overflow the int32 sums", name, (long long)K);
+  if (algo < W4A8_GG_AUTO || algo > W4A8_GG_TILED) return fail(W4A8_ERR_SHAPE, "%s: unknown algo %d", name, algo);
   if (M_total == 0) return ok();
-  if (!a || !a_scale || !offsets || !w_packed || !w_scale || !out)
-    return fail(W4A8_ERR_NULL, "grouped_gemm: null pointer");
-  if (!aligned(a, 16) || !aligned(w_packed, 16) || !aligned(out, 16) || !aligned(a_scale, 4) ||
-      !aligned(w_scale, 4) || !aligned(offsets, 4) || !aligned(a_rows, 4))
-    return fail(W4A8_ERR_ALIGN, "grouped_gemm: a, w_packed and out must be 16-byte aligned, the rest 4-byte");
+  if (!a || !a_scale || !offsets || !w || !s || !out || (fused && !pmax) || (form == Form::kChannel && !a_rowsum))
+    return fail(W4A8_ERR_NULL, "%s: null pointer", name);
+  if (!aligned(a, 16) || !aligned(w, 16) || !aligned(out, 16) || !aligned(a_scale, 4) || !aligned(s, 4) ||
+      !aligned(offsets, 4) || !aligned(a_rows, 4) || !aligned(pmax, 4) || !aligned(a_rowsum, 4))
+    return fail(W4A8_ERR_ALIGN, "%s: a, the weights and the output must be 16-byte aligned, the rest 4-byte", name);
   if (int st = check_device()) return st;
-  const w4a8::GemmArgs g{a, a_scale, nullptr, a_rows, M_total, offsets, E, w_packed, w_scale, N, K, out};
+  w4a8::GemmArgs g{static_cast<const uint8_t*>(a), a_scale, form == Form::kChannel ? a_rowsum : nullptr, a_rows,
+                   M_total, offsets, E, static_cast<const int32_t*>(w), static_cast<const float*>(s), N, K, out};
+  g.pmax = fused ? pmax : nullptr;
+  g.mx = form == Form::kMx;
+  g.row_major = row_major;
+  if (row_major) algo = W4A8_GG_STREAM;   // the tiled kernel reads the GEMM storage only
   if (algo == W4A8_GG_AUTO) algo = (M_total <= 32 * (int64_t)E) ? W4A8_GG_STREAM : W4A8_GG_TILED;
   (void)hipGetLastError();
-  if (algo == W4A8_GG_STREAM) return launched(w4a8::launch_gg_stream(g, as_stream(stream)), "grouped_gemm");
-  return launched(w4a8::launch_gg_tiled(g, as_stream(stream)), "grouped_gemm");
+  if (algo == W4A8_GG_STREAM) return launched(w4a8::launch_gg_stream(g, as_stream(stream)), name);
+  return launched(w4a8::launch_gg_tiled(g, as_stream(stream)), name);
 }
 
 int w4a8_moe_grouped_gemm(const uint8_t* a, const float* a_scale, const int32_t* a_rows, int64_t M_total,
                           const int32_t* offsets, int32_t E, const int32_t* w_packed, const float* w_scale,
                           int64_t N, int64_t K, float* out, void* stream) {
-  return w4a8_moe_grouped_gemm_algo(a, a_scale, a_rows, M_total, offsets, E, w_packed, w_scale, N, K, out,
-                                    W4A8_GG_AUTO, stream);
+  return run_gemm("grouped_gemm", Form::kG128, false, true, a, a_scale, nullptr, a_rows, M_total, offsets, E,
+                  w_packed, w_scale, N, K, out, nullptr, W4A8_GG_AUTO, stream);
+}
+
+int w4a8_moe_grouped_gemm_prepacked(const uint8_t* a, const float* a_scale, const int32_t* a_rows, int64_t M_total,
+                                    const int32_t* offsets, int32_t E, const int32_t* w_blk, const float* s_blk,
+                                    int64_t N, int64_t K, float* out, int32_t algo, void* stream) {
+  return run_gemm("grouped_gemm_prepacked", Form::kG128, false, false, a, a_scale, nullptr, a_rows, M_total,
+                  offsets, E, w_blk, s_blk, N, K, out, nullptr, algo, stream);
+}
+
+int w4a8_moe_grouped_gemm_swiglu(const uint8_t* a, const float* a_scale, const int32_t* a_rows, int64_t M_total,
+                                 const int32_t* offsets, int32_t E, const int32_t* w13, const float* s13, int64_t I,
+                                 int64_t K, float* act, float* act_pmax, void* stream) {
+  return run_gemm("grouped_gemm_swiglu", Form::kG128, true, true, a, a_scale, nullptr, a_rows, M_total, offsets, E,
+                  w13, s13, 2 * I, K, act, act_pmax, W4A8_GG_AUTO, stream);
+}
+
+int w4a8_moe_grouped_gemm_swiglu_prepacked(const uint8_t* a, const float* a_scale, const int32_t* a_rows,
+                                           int64_t M_total, const int32_t* offsets, int32_t E, const int32_t* w13,
+                                           const float* s13, int64_t I, int64_t K, float* act, float* act_pmax,
+                                           int32_t algo, void* stream) {
+  return run_gemm("grouped_gemm_swiglu_prepacked", Form::kG128, true, false, a, a_scale, nullptr, a_rows, M_total,
+                  offsets, E, w13, s13, 2 * I, K, act, act_pmax, algo, stream);
+}
+
+int w4a8_moe_grouped_gemm_i8(const int8_t* a, const float* a_scale, const int32_t* a_rowsum, const int32_t* a_rows,
+                             int64_t M_total, const int32_t* offsets, int32_t E, const int32_t* w_packed,
+                             const float* w_scale, int64_t N, int64_t K, float* out, void* stream) {
+  return run_gemm("grouped_gemm_i8", Form::kChannel, false, true, a, a_scale, a_rowsum, a_rows, M_total, offsets, E,
+                  w_packed, w_scale, N, K, out, nullptr, W4A8_GG_AUTO, stream);
+}
+
+int w4a8_moe_grouped_gemm_i8_prepacked(const int8_t* a, const float* a_scale, const int32_t* a_rowsum,
+                                       const int32_t* a_rows, int64_t M_total, const int32_t* offsets, int32_t E,
+                                       const int32_t* w_blk, const float* w_scale, int64_t N, int64_t K, float* out,
+                                       int32_t algo, void* stream) {
+  return run_gemm("grouped_gemm_i8_prepacked", Form::kChannel, false, false, a, a_scale, a_rowsum, a_rows, M_total,
+                  offsets, E, w_blk, w_scale, N, K, out, nullptr, algo, stream);
+}
+
+int w4a8_moe_grouped_gemm_swiglu_i8(const int8_t* a, const float* a_scale, const int32_t* a_rowsum,
+                                    const int32_t* a_rows, int64_t M_total, const int32_t* offsets, int32_t E,
+                                    const int32_t* w13, const float* s13, int64_t I, int64_t K, float* act,
+                                    float* act_pmax, void* stream) {
+  return run_gemm("grouped_gemm_swiglu_i8", Form::kChannel, true, true, a, a_scale, a_rowsum, a_rows, M_total,
+                  offsets, E, w13, s13, 2 * I, K, act, act_pmax, W4A8_GG_AUTO, stream);
+}
+
+int w4a8_moe_grouped_gemm_swiglu_i8_prepacked(const int8_t* a, const float* a_scale, const int32_t* a_rowsum,
+                                              const int32_t* a_rows, int64_t M_total, const int32_t* offsets,
+                                              int32_t E, const int32_t* w13, const float* s13, int64_t I, int64_t K,
+                                              float* act, float* act_pmax, int32_t algo, void* stream) {
+  return run_gemm("grouped_gemm_swiglu_i8_prepacked", Form::kChannel, true, false, a, a_scale, a_rowsum, a_rows,
+                  M_total, offsets, E, w13, s13, 2 * I, K, act, act_pmax, algo, stream);
+}
+
+int w4a8_moe_grouped_gemm_mxfp4(const uint8_t* a, const float* a_scale, const int32_t* a_rows, int64_t M_total,
+                                const int32_t* offsets, int32_t E, const uint8_t* w_packed, const uint8_t* w_scale,
+                                int64_t N, int64_t K, float* out, void* stream) {
+  return run_gemm("grouped_gemm_mxfp4", Form::kMx, false, true, a, a_scale, nullptr, a_rows, M_total, offsets, E,
+                  w_packed, w_scale, N, K, out, nullptr, W4A8_GG_AUTO, stream);
+}
+
+int w4a8_moe_grouped_gemm_mxfp4_prepacked(const uint8_t* a, const float* a_scale, const int32_t* a_rows,
+                                          int64_t M_total, const int32_t* offsets, int32_t E, const uint8_t* w_blk,
+                                          const uint8_t* s_blk, int64_t N, int64_t K, float* out, int32_t algo,
+                                          void* stream) {
+  return run_gemm("grouped_gemm_mxfp4_prepacked", Form::kMx, false, false, a, a_scale, nullptr, a_rows, M_total,
+                  offsets, E, w_blk, s_blk, N, K, out, nullptr, algo, stream);
+}
+
+int w4a8_moe_grouped_gemm_swiglu_mxfp4(const uint8_t* a, const float* a_scale, const int32_t* a_rows,
+                                       int64_t M_total, const int32_t* offsets, int32_t E, const uint8_t* w13,
+                                       const uint8_t* s13, int64_t I, int64_t K, float* act, float* act_pmax,
+                                       void* stream) {
+  return run_gemm("grouped_gemm_swiglu_mxfp4", Form::kMx, true, true, a, a_scale, nullptr, a_rows, M_total, offsets,
+                  E, w13, s13, 2 * I, K, act, act_pmax, W4A8_GG_AUTO, stream);
+}
+
+int w4a8_moe_grouped_gemm_swiglu_mxfp4_prepacked(const uint8_t* a, const float* a_scale, const int32_t* a_rows,
+                                                 int64_t M_total, const int32_t* offsets, int32_t E,
+                                                 const uint8_t* w13, const uint8_t* s13, int64_t I, int64_t K,
+                                                 float* act, float* act_pmax, int32_t algo, void* stream) {
+  return run_gemm("grouped_gemm_swiglu_mxfp4_prepacked", Form::kMx, true, false, a, a_scale, nullptr, a_rows,
+                  M_total, offsets, E, w13, s13, 2 * I, K, act, act_pmax, algo, stream);
 }
 
 int w4a8_moe_swiglu(const float* h, int64_t M, int64_t I, uint8_t* qa, float* sa, void* stream) {
@@ -303,35 +408,6 @@ int w4a8_moe_swiglu_i8(const float* h, int64_t M, int64_t I, int8_t* qa, float* 
   return launched(w4a8::launch_swiglu_i8(h, M, I, qa, sa, rowsum, as_stream(stream)), "swiglu_i8");
 }
 
-int w4a8_moe_grouped_gemm_i8(const int8_t* a, const float* a_scale, const int32_t* a_rowsum, const int32_t* a_rows,
-                             int64_t M_total, const int32_t* offsets, int32_t E, const int32_t* w_packed,
-                             const float* w_scale, int64_t N, int64_t K, float* out, int32_t algo, void* stream) {
-  if (M_total < 0 || M_total >= kMaxRows)
-    return fail(W4A8_ERR_SHAPE, "grouped_gemm_i8: M_total=%lld out of range", (long long)M_total);
-  if (E < 1 || E > 1024) return fail(W4A8_ERR_SHAPE, "grouped_gemm_i8: E=%d must be in [1, 1024]", E);
-  if (N <= 0 || N % 64) return fail(W4A8_ERR_SHAPE, "grouped_gemm_i8: N=%lld must be a positive multiple of 64",
-                                    (long long)N);
-  if (K <= 0 || K % 128) return fail(W4A8_ERR_SHAPE, "grouped_gemm_i8: K=%lld must be a positive multiple of 128",
-                                     (long long)K);
-  if (K > (int64_t)1 << 20) return fail(W4A8_ERR_SHAPE, "grouped_gemm_i8: K=%lld would overflow the int32 sums",
-                                        (long long)K);
-  if (algo < W4A8_GG_AUTO || algo > W4A8_GG_TILED)
-    return fail(W4A8_ERR_SHAPE, "grouped_gemm_i8: unknown algo %d", algo);
-  if (M_total == 0) return ok();
-  if (!a || !a_scale || !a_rowsum || !offsets || !w_packed || !w_scale || !out)
-    return fail(W4A8_ERR_NULL, "grouped_gemm_i8: null pointer");
-  if (!aligned(a, 16) || !aligned(w_packed, 16) || !aligned(out, 16) || !aligned(a_scale, 4) ||
-      !aligned(a_rowsum, 4) || !aligned(w_scale, 4) || !aligned(offsets, 4) || !aligned(a_rows, 4))
-    return fail(W4A8_ERR_ALIGN, "grouped_gemm_i8: a, w_packed and out must be 16-byte aligned, the rest 4-byte");
-  if (int st = check_device()) return st;
-  const w4a8::GemmArgs g{reinterpret_cast<const uint8_t*>(a), a_scale, a_rowsum, a_rows, M_total, offsets, E,
-                         w_packed, w_scale, N, K, out};
-  if (algo == W4A8_GG_AUTO) algo = (M_total <= 32 * (int64_t)E) ? W4A8_GG_STREAM : W4A8_GG_TILED;
-  (void)hipGetLastError();
-  if (algo == W4A8_GG_STREAM) return launched(w4a8::launch_gg_stream(g, as_stream(stream)), "grouped_gemm_i8");
-  return launched(w4a8::launch_gg_tiled(g, as_stream(stream)), "grouped_gemm_i8");
-}
-
 int w4a8_moe_quantize_weights_channel(const float* w, int64_t rows, int64_t K, int32_t* w_packed, float* w_scale,
                                       void* stream) {
   if (rows < 0 || rows >= kMaxRows)
@@ -346,65 +422,6 @@ int w4a8_moe_quantize_weights_channel(const float* w, int64_t rows, int64_t K, i
   (void)hipGetLastError();
   return launched(w4a8::launch_wquant_channel(w, rows, K, w_packed, w_scale, as_stream(stream)),
                   "quantize_weights_channel");
-}
-
-// the shape, pointer and alignment rules shared by the two fused gate/up GEMMs
-static int check_gemm_swiglu(const char* name, const void* a, const float* a_scale, const int32_t* a_rows,
-                             int64_t M_total, const int32_t* offsets, int32_t E, const void* w13, const void* s13,
-                             int64_t I, int64_t K, const float* act, const float* act_pmax, int32_t algo) {
-  if (M_total < 0 || M_total >= kMaxRows)
-    return fail(W4A8_ERR_SHAPE, "%s: M_total=%lld out of range", name, (long long)M_total);
-  if (E < 1 || E > 1024) return fail(W4A8_ERR_SHAPE, "%s: E=%d must be in [1, 1024]", name, E);
-  if (I <= 0 || I % 128) return fail(W4A8_ERR_SHAPE, "%s: I=%lld must be a positive multiple of 128", name,
-                                     (long long)I);
-  if (K <= 0 || K % 128) return fail(W4A8_ERR_SHAPE, "%s: K=%lld must be a positive multiple of 128", name,
-                                     (long long)K);
-  if (algo < W4A8_GG_AUTO || algo > W4A8_GG_TILED) return fail(W4A8_ERR_SHAPE, "%s: unknown algo %d", name, algo);
-  if (M_total == 0) return W4A8_OK;
-  if (!a || !a_scale || !offsets || !w13 || !s13 || !act || !act_pmax) return fail(W4A8_ERR_NULL, "%s: null pointer", name);
-  if (!aligned(a, 16) || !aligned(w13, 16) || !aligned(act, 16) || !aligned(a_scale, 4) || !aligned(s13, 4) ||
-      !aligned(offsets, 4) || !aligned(a_rows, 4) || !aligned(act_pmax, 4))
-    return fail(W4A8_ERR_ALIGN, "%s: a, w13 and act must be 16-byte aligned, the rest 4-byte", name);
-  return W4A8_OK;
-}
-
-int w4a8_moe_grouped_gemm_swiglu(const uint8_t* a, const float* a_scale, const int32_t* a_rows, int64_t M_total,
-                                 const int32_t* offsets, int32_t E, const int32_t* w13, const float* s13, int64_t I,
-                                 int64_t K, float* act, float* act_pmax, int32_t algo, void* stream) {
-  if (int st = check_gemm_swiglu("grouped_gemm_swiglu", a, a_scale, a_rows, M_total, offsets, E, w13, s13, I, K, act,
-                                 act_pmax, algo))
-    return st;
-  if (M_total == 0) return ok();
-  if (int st = check_device()) return st;
-  w4a8::GemmArgs g{a, a_scale, nullptr, a_rows, M_total, offsets, E, w13, s13, 2 * I, K, act};
-  g.pmax = act_pmax;
-  if (algo == W4A8_GG_AUTO) algo = (M_total <= 32 * (int64_t)E) ? W4A8_GG_STREAM : W4A8_GG_TILED;
-  (void)hipGetLastError();
-  if (algo == W4A8_GG_STREAM) return launched(w4a8::launch_gg_stream(g, as_stream(stream)), "grouped_gemm_swiglu");
-  return launched(w4a8::launch_gg_tiled(g, as_stream(stream)), "grouped_gemm_swiglu");
-}
-
-int w4a8_moe_grouped_gemm_swiglu_i8(const int8_t* a, const float* a_scale, const int32_t* a_rowsum,
-                                    const int32_t* a_rows, int64_t M_total, const int32_t* offsets, int32_t E,
-                                    const int32_t* w13, const float* s13, int64_t I, int64_t K, float* act,
-                                    float* act_pmax, int32_t algo, void* stream) {
-  if (int st = check_gemm_swiglu("grouped_gemm_swiglu_i8", a, a_scale, a_rows, M_total, offsets, E, w13, s13, I, K,
-                                 act, act_pmax, algo))
-    return st;
-  if (K > (int64_t)1 << 20)
-    return fail(W4A8_ERR_SHAPE, "grouped_gemm_swiglu_i8: K=%lld would overflow the int32 sums", (long long)K);
-  if (M_total == 0) return ok();
-  if (!a_rowsum) return fail(W4A8_ERR_NULL, "grouped_gemm_swiglu_i8: null pointer");
-  if (!aligned(a_rowsum, 4)) return fail(W4A8_ERR_ALIGN, "grouped_gemm_swiglu_i8: a_rowsum must be 4-byte aligned");
-  if (int st = check_device()) return st;
-  w4a8::GemmArgs g{reinterpret_cast<const uint8_t*>(a), a_scale, a_rowsum, a_rows, M_total, offsets, E, w13, s13,
-                   2 * I, K, act};
-  g.pmax = act_pmax;
-  if (algo == W4A8_GG_AUTO) algo = (M_total <= 32 * (int64_t)E) ? W4A8_GG_STREAM : W4A8_GG_TILED;
-  (void)hipGetLastError();
-  if (algo == W4A8_GG_STREAM)
-    return launched(w4a8::launch_gg_stream(g, as_stream(stream)), "grouped_gemm_swiglu_i8");
-  return launched(w4a8::launch_gg_tiled(g, as_stream(stream)), "grouped_gemm_swiglu_i8");
 }
 
 int w4a8_moe_requant(const float* act, const float* act_pmax, int64_t M, int64_t I, uint8_t* qa, float* sa,
@@ -484,55 +501,6 @@ int w4a8_moe_prepack_int4(const int32_t* w_packed, const float* w_scale, int32_t
   if (int st = check_device()) return st;
   (void)hipGetLastError();
   return launched(w4a8::launch_prepack(w_packed, w_scale, E, N, K, 1, w_blk, s_blk, as_stream(stream)), "prepack_int4");
-}
-
-// the kernel for an MXFP4 GEMM (plain or fused), once every argument is checked
-static int run_gemm_mx(w4a8::GemmArgs g, int32_t algo, const char* name, void* stream) {
-  g.mx = true;
-  if (algo == W4A8_GG_AUTO) algo = (g.M_total <= 32 * (int64_t)g.E) ? W4A8_GG_STREAM : W4A8_GG_TILED;
-  (void)hipGetLastError();
-  if (algo == W4A8_GG_STREAM) return launched(w4a8::launch_gg_stream(g, as_stream(stream)), name);
-  return launched(w4a8::launch_gg_tiled(g, as_stream(stream)), name);
-}
-
-int w4a8_moe_grouped_gemm_mxfp4(const uint8_t* a, const float* a_scale, const int32_t* a_rows, int64_t M_total,
-                                const int32_t* offsets, int32_t E, const uint8_t* w_packed, const uint8_t* w_scale,
-                                int64_t N, int64_t K, float* out, int32_t algo, void* stream) {
-  if (M_total < 0 || M_total >= kMaxRows)
-    return fail(W4A8_ERR_SHAPE, "grouped_gemm_mxfp4: M_total=%lld out of range", (long long)M_total);
-  if (E < 1 || E > 1024) return fail(W4A8_ERR_SHAPE, "grouped_gemm_mxfp4: E=%d must be in [1, 1024]", E);
-  if (N <= 0 || N % 64)
-    return fail(W4A8_ERR_SHAPE, "grouped_gemm_mxfp4: N=%lld must be a positive multiple of 64", (long long)N);
-  if (K <= 0 || K % 128)
-    return fail(W4A8_ERR_SHAPE, "grouped_gemm_mxfp4: K=%lld must be a positive multiple of 128", (long long)K);
-  if (algo < W4A8_GG_AUTO || algo > W4A8_GG_TILED)
-    return fail(W4A8_ERR_SHAPE, "grouped_gemm_mxfp4: unknown algo %d", algo);
-  if (M_total == 0) return ok();
-  if (!a || !a_scale || !offsets || !w_packed || !w_scale || !out)
-    return fail(W4A8_ERR_NULL, "grouped_gemm_mxfp4: null pointer");
-  if (!aligned(a, 16) || !aligned(w_packed, 16) || !aligned(out, 16) || !aligned(a_scale, 4) ||
-      !aligned(w_scale, 4) || !aligned(offsets, 4) || !aligned(a_rows, 4))
-    return fail(W4A8_ERR_ALIGN, "grouped_gemm_mxfp4: a, w_packed and out must be 16-byte aligned, the rest 4-byte");
-  if (int st = check_device()) return st;
-  const w4a8::GemmArgs g{a, a_scale, nullptr, a_rows, M_total, offsets, E,
-                         reinterpret_cast<const int32_t*>(w_packed), reinterpret_cast<const float*>(w_scale), N, K,
-                         out};
-  return run_gemm_mx(g, algo, "grouped_gemm_mxfp4", stream);
-}
-
-int w4a8_moe_grouped_gemm_swiglu_mxfp4(const uint8_t* a, const float* a_scale, const int32_t* a_rows,
-                                       int64_t M_total, const int32_t* offsets, int32_t E, const uint8_t* w13,
-                                       const uint8_t* s13, int64_t I, int64_t K, float* act, float* act_pmax,
-                                       int32_t algo, void* stream) {
-  if (int st = check_gemm_swiglu("grouped_gemm_swiglu_mxfp4", a, a_scale, a_rows, M_total, offsets, E, w13, s13, I,
-                                 K, act, act_pmax, algo))
-    return st;
-  if (M_total == 0) return ok();
-  if (int st = check_device()) return st;
-  w4a8::GemmArgs g{a, a_scale, nullptr, a_rows, M_total, offsets, E, reinterpret_cast<const int32_t*>(w13),
-                   reinterpret_cast<const float*>(s13), 2 * I, K, act};
-  g.pmax = act_pmax;
-  return run_gemm_mx(g, algo, "grouped_gemm_swiglu_mxfp4", stream);
 }
 
 int w4a8_moe_unpermute(const float* o, const int32_t* inv_pos, const float* w, int64_t T, int32_t k, int64_t H,

@@ -25,7 +25,6 @@ namespace w4a8 {
 
 typedef int v8i __attribute__((ext_vector_type(8)));     // 32 E4M3 bytes
 typedef float v4f __attribute__((ext_vector_type(4)));   // 16x16 fp32 tile, 4 per lane
-typedef float v16f __attribute__((ext_vector_type(16))); // 32x32 fp32 tile, 16 per lane
 
 constexpr int kBiasWord = (int)0x88888888u;                // four E4M3 -2^-6
 constexpr float kUnitScale = 512.0f;                        // 2^9
@@ -64,25 +63,11 @@ enum WeightForm : int {
 // INT8 matrix-core products for the per-channel variant (int32 accumulation).
 // 16x16x64: lane l supplies A row (l % 16) and B column (l % 16), K elements
 // 16 * (l / 16) .. +16 of the 64; D as in the 16x16 FP8 form.
-// 32x32x32: lane l supplies A row (l % 32) and B column (l % 32), K elements
-// 16 * (l / 32) .. +16 of the 32; D as in the 32x32 FP8 form.
 // A 32-byte FP8 operand of a lane becomes two INT8 operands (its 16-byte
 // halves, with the same split on both sides), so the kernels keep their FP8
 // data layout: the two products cover the same K elements between them.
-typedef int v16i __attribute__((ext_vector_type(16)));
 __device__ __forceinline__ i32x4 mfma_i8_16x16x64(i32x4 a, i32x4 b, i32x4 c) {
   return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);
-}
-__device__ __forceinline__ v16i mfma_i8_32x32x32(i32x4 a, i32x4 b, v16i c) {
-  return __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, c, 0, 0, 0);
-}
-
-// v_mfma_f32_32x32x64_f8f6f4 with both operands E4M3 and no block scaling.
-// Lane l supplies A row (l % 32) and B column (l % 32), K elements
-// 32 * (l / 32) .. +32 of the 64; D element v of lane l is row
-// 8 * (v / 4) + 4 * (l / 32) + v % 4, column l % 32.
-__device__ __forceinline__ v16f mfma32x32x64(v8i a, v8i b, v16f c) {
-  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
 }
 
 // 32 nibbles of the GEMM storage (word c holds k = 8c .. 8c+7 in the nibble
@@ -94,6 +79,20 @@ __device__ __forceinline__ v8i nibbles_to_fp8(i32x4 w) {
   for (int c = 0; c < 4; ++c) {
     r[2 * c] = (int)((uint32_t)w[c] & 0x0f0f0f0fu);             // u0 u1 u2 u3
     r[2 * c + 1] = (int)(((uint32_t)w[c] >> 4) & 0x0f0f0f0fu);  // u4 u5 u6 u7
+  }
+  return r;
+}
+// The same from the row-major stored words (the nibble of k at bits 4 (k mod 8)):
+// a mask and a shift give the even elements k0 k2 k4 k6 and the odd ones
+// k1 k3 k5 k7, and two byte permutes interleave them into K order.
+__device__ __forceinline__ v8i nibbles_rowmajor_to_fp8(i32x4 w) {
+  v8i r;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const uint32_t ev = (uint32_t)w[c] & 0x0f0f0f0fu;           // u0 u2 u4 u6
+    const uint32_t od = ((uint32_t)w[c] >> 4) & 0x0f0f0f0fu;    // u1 u3 u5 u7
+    r[2 * c] = (int)__builtin_amdgcn_perm(od, ev, 0x05010400u);      // u0 u1 u2 u3
+    r[2 * c + 1] = (int)__builtin_amdgcn_perm(od, ev, 0x07030602u);  // u4 u5 u6 u7
   }
   return r;
 }

@@ -90,18 +90,27 @@ struct WPair {
   i32x4 wa[NS], wb[NS];
 };
 
-template <int NS>
+// kGStride: bytes between a lane's weights of two consecutive groups (1024 in
+// the GEMM storage, 64 in the row-major stored format)
+template <int NS, int kGStride>
 __device__ __forceinline__ void w_pair_load(WPair<NS>& w, const uint8_t* const (&pw)[NS], int g) {
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
-    w.wa[s] = __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(pw[s] + g * 1024));
-    w.wb[s] = __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(pw[s] + (g + 1) * 1024));
+    w.wa[s] = __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(pw[s] + g * kGStride));
+    w.wb[s] = __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(pw[s] + (g + 1) * kGStride));
   }
+}
+
+// the lane's 32 weight bytes u_k in K order, from the GEMM storage or (kRM) the row-major words
+template <bool kRM>
+__device__ __forceinline__ v8i split_nibbles(i32x4 w) {
+  if constexpr (kRM) return nibbles_rowmajor_to_fp8(w);
+  else return nibbles_to_fp8(w);
 }
 
 // group-128 INT4 form of one group pair: A operands from LDS, the +8 offset
 // removed by the bias MFMAs (accumulator input), then acc += s * D per group
-template <int NS>
+template <int NS, bool kRM>
 __device__ __forceinline__ void pair_compute(const WPair<NS>& w, const float (&s0)[NS], const float (&s1)[NS],
                                              const uint8_t* a0, const uint8_t* a1, v4f (&acc)[NS]) {
   const v8i av0 = *reinterpret_cast<const v8i*>(a0);
@@ -112,8 +121,8 @@ __device__ __forceinline__ void pair_compute(const WPair<NS>& w, const float (&s
   const v4f c1 = mfma16x16x128(av1, kb, zero);
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
-    const v4f d0 = mfma16x16x128(av0, nibbles_to_fp8(w.wa[s]), c0);
-    const v4f d1 = mfma16x16x128(av1, nibbles_to_fp8(w.wb[s]), c1);
+    const v4f d0 = mfma16x16x128(av0, split_nibbles<kRM>(w.wa[s]), c0);
+    const v4f d1 = mfma16x16x128(av1, split_nibbles<kRM>(w.wb[s]), c1);
 #pragma unroll
     for (int r = 0; r < 4; ++r) acc[s][r] = fmaf(s1[s], d1[r], fmaf(s0[s], d0[r], acc[s][r]));
   }
@@ -136,14 +145,14 @@ __device__ __forceinline__ void pair_compute_mx(const WPair<NS>& w, const int (&
 // the per-channel INT8 form of one group pair: int32 products, no scales
 // (the nibbles u = q + 8 are the INT8 B operand; the offset is removed with
 // the activation row sums in the epilogue)
-template <int NS>
+template <int NS, bool kRM>
 __device__ __forceinline__ void pair_compute_i8(const WPair<NS>& w, const uint8_t* a0, const uint8_t* a1,
                                                 i32x4 (&acc)[NS]) {
   const v8i av0 = *reinterpret_cast<const v8i*>(a0);
   const v8i av1 = *reinterpret_cast<const v8i*>(a1);
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
-    const v8i b0 = nibbles_to_fp8(w.wa[s]), b1 = nibbles_to_fp8(w.wb[s]);
+    const v8i b0 = split_nibbles<kRM>(w.wa[s]), b1 = split_nibbles<kRM>(w.wb[s]);
     acc[s] = mfma_i8_16x16x64(av0.lo, b0.lo, acc[s]);
     acc[s] = mfma_i8_16x16x64(av0.hi, b0.hi, acc[s]);
     acc[s] = mfma_i8_16x16x64(av1.lo, b1.lo, acc[s]);
@@ -159,10 +168,17 @@ __device__ __forceinline__ void pair_compute_i8(const WPair<NS>& w, const uint8_
 // up rows of the same 16 output columns (gate_up_row), and the epilogue
 // writes act = silu(gate) * up [M][N/2] and the workgroup's max |act| of each
 // row (its 64 output columns) to pmax[p][blockIdx.x].
+// kRM: the weights come in the row-major stored format instead of the GEMM
+// storage (int32 [E][N][K/8] uint4b8 words or u8 [E][N][K/2] E2M1 codes, scales
+// [E][N][K/128] fp32 or [E][N][K/32] E8M0 bytes): each lane still loads its own
+// 16-byte operand per group (row col, bytes 16 kq .. +15 of the row's group),
+// a wave's load then reading 64 bytes of each of 16 rows instead of one 1 KB
+// piece, and the INT4 nibbles need two byte permutes more to reach K order.
+// N % 16 == 0 is enough there: a subtile past N loads row 0 and stores nothing.
 // At least 3 waves per SIMD (3 workgroups per CU): the kernel is bound by the
 // weight loads it has in flight.  Without the bound the group-128 form put its
 // accumulators in AGPRs on top of 156 VGPRs and ran 2 waves per SIMD.
-template <int NS, int CH, int kForm, bool kSwiglu>
+template <int NS, int CH, int kForm, bool kSwiglu, bool kRM>
 __global__ __launch_bounds__(kStreamThreads, 3) void gg_stream_kernel(const uint8_t* __restrict__ a,
                                                                    const float* __restrict__ a_scale,
                                                                    const int32_t* __restrict__ a_rowsum,
@@ -189,13 +205,23 @@ __global__ __launch_bounds__(kStreamThreads, 3) void gg_stream_kernel(const uint
 
   // subtile s: weight rows nb .. nb+15 are the G pieces of 1 KB from their block's base;
   // the lane reads row col, bytes 16 kq .. +15 of each.  Group scales: word (g, nb + col).
+  // Row-major (kRM): row nb + col, bytes 64 g + 16 kq .. +15; scales word (nb + col, g).
+  constexpr int kGStride = kRM ? 64 : 1024;
+  const int64_t sstride = kRM ? 1 : N;         // scale words between two groups of a column
   const uint8_t* pw[NS];
   const uint32_t* srow[NS];
+  bool sub_ok[NS];                             // subtile s holds columns below N
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
-    const int64_t nb = active ? (kSwiglu ? (int64_t)gate_up_row((int)(n0 + 16 * s), (int)(N / 2)) : n0 + 16 * s) : 0;
-    pw[s] = reinterpret_cast<const uint8_t*>(w_packed) + ((int64_t)e * N + nb) * row_bytes + col * 64 + kq * 16;
-    srow[s] = reinterpret_cast<const uint32_t*>(w_scale) + (int64_t)e * N * G + nb + col;
+    sub_ok[s] = n0 + 16 * s < N;
+    const int64_t nb = sub_ok[s] ? (kSwiglu ? (int64_t)gate_up_row((int)(n0 + 16 * s), (int)(N / 2)) : n0 + 16 * s) : 0;
+    if constexpr (kRM) {
+      pw[s] = reinterpret_cast<const uint8_t*>(w_packed) + ((int64_t)e * N + nb + col) * row_bytes + kq * 16;
+      srow[s] = reinterpret_cast<const uint32_t*>(w_scale) + ((int64_t)e * N + nb + col) * G;
+    } else {
+      pw[s] = reinterpret_cast<const uint8_t*>(w_packed) + ((int64_t)e * N + nb) * row_bytes + col * 64 + kq * 16;
+      srow[s] = reinterpret_cast<const uint32_t*>(w_scale) + (int64_t)e * N * G + nb + col;
+    }
   }
 
   for (int m0 = r0; m0 < r1; m0 += 16) {
@@ -231,7 +257,7 @@ __global__ __launch_bounds__(kStreamThreads, 3) void gg_stream_kernel(const uint
           for (int s = 0; s < NS; ++s) {
 #pragma unroll
             for (int h = 0; h < 2 * CH; ++h) {
-              sc[s][h] = h < ng ? srow[s][(int64_t)(g0 + h) * N] : 0u;
+              sc[s][h] = h < ng ? srow[s][(int64_t)(g0 + h) * sstride] : 0u;
               if constexpr (kMx) sc[s][h] >>= 8 * kq;
             }
           }
@@ -242,15 +268,15 @@ __global__ __launch_bounds__(kStreamThreads, 3) void gg_stream_kernel(const uint
           if (u < npairs) {
             WPair<NS> w0, w1;
             const bool two = u + 1 < npairs;
-            w_pair_load(w0, pw, g0 + 2 * u);
-            if (two) w_pair_load(w1, pw, g0 + 2 * u + 2);
+            w_pair_load<NS, kGStride>(w0, pw, g0 + 2 * u);
+            if (two) w_pair_load<NS, kGStride>(w1, pw, g0 + 2 * u + 2);
             const uint8_t* a00 = &sm.a[buf][2 * u][lane][0];
             const uint8_t* a01 = &sm.a[buf][2 * u + 1][lane][0];
             const uint8_t* a10 = &sm.a[buf][2 * u + 2][lane][0];
             const uint8_t* a11 = &sm.a[buf][2 * u + 3][lane][0];
             if constexpr (kInt8) {
-              pair_compute_i8(w0, a00, a01, acc);
-              if (two) pair_compute_i8(w1, a10, a11, acc);
+              pair_compute_i8<NS, kRM>(w0, a00, a01, acc);
+              if (two) pair_compute_i8<NS, kRM>(w1, a10, a11, acc);
             } else if constexpr (kMx) {
               int s0[NS], s1[NS];
 #pragma unroll
@@ -268,14 +294,14 @@ __global__ __launch_bounds__(kStreamThreads, 3) void gg_stream_kernel(const uint
                 s0[s] = __uint_as_float(sc[s][2 * u]);
                 s1[s] = __uint_as_float(sc[s][2 * u + 1]);
               }
-              pair_compute(w0, s0, s1, a00, a01, acc);
+              pair_compute<NS, kRM>(w0, s0, s1, a00, a01, acc);
               if (two) {
 #pragma unroll
                 for (int s = 0; s < NS; ++s) {
                   s0[s] = __uint_as_float(sc[s][2 * u + 2]);
                   s1[s] = __uint_as_float(sc[s][2 * u + 3]);
                 }
-                pair_compute(w1, s0, s1, a10, a11, acc);
+                pair_compute<NS, kRM>(w1, s0, s1, a10, a11, acc);
               }
             }
           }
@@ -287,15 +313,15 @@ __global__ __launch_bounds__(kStreamThreads, 3) void gg_stream_kernel(const uint
                                        : mfma16x16x128(av, bias_operand(), v4f{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
           for (int s = 0; s < NS; ++s) {
-            const i32x4 wq = __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(pw[s] + (g0 + h) * 1024));
+            const i32x4 wq = __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(pw[s] + (g0 + h) * kGStride));
             if constexpr (kInt8) {
-              const v8i b = nibbles_to_fp8(wq);
+              const v8i b = split_nibbles<kRM>(wq);
               acc[s] = mfma_i8_16x16x64(av.lo, b.lo, acc[s]);
               acc[s] = mfma_i8_16x16x64(av.hi, b.hi, acc[s]);
             } else if constexpr (kMx) {
               acc[s] = mfma_mx(av, wq, acc[s], (int)sc[s][h]);
             } else {
-              const v4f d = mfma16x16x128(av, nibbles_to_fp8(wq), c);
+              const v4f d = mfma16x16x128(av, split_nibbles<kRM>(wq), c);
 #pragma unroll
               for (int r = 0; r < 4; ++r) acc[s][r] = fmaf(__uint_as_float(sc[s][h]), d[r], acc[s][r]);
             }
@@ -312,7 +338,7 @@ __global__ __launch_bounds__(kStreamThreads, 3) void gg_stream_kernel(const uint
         float ws[NS];
 #pragma unroll
         for (int s = 0; s < NS; ++s) {
-          const int v = (int)(n0 + 16 * s) + col;
+          const int v = sub_ok[s] ? (int)(n0 + 16 * s) + col : 0;
           ws[s] = w_scale[(int64_t)e * N + (kSwiglu ? gate_up_row(v, (int)(N / 2)) : v)];
         }
 #pragma unroll
@@ -334,7 +360,7 @@ __global__ __launch_bounds__(kStreamThreads, 3) void gg_stream_kernel(const uint
             const float as = a_scale[src];
 #pragma unroll
             for (int s = 0; s < NS; ++s)
-              out[(int64_t)p * N + n0 + 16 * s + col] = (float)(acc[s][r] - off) * as * ws[s];
+              if (sub_ok[s]) out[(int64_t)p * N + n0 + 16 * s + col] = (float)(acc[s][r] - off) * as * ws[s];
           }
         }
       } else {
@@ -353,7 +379,8 @@ __global__ __launch_bounds__(kStreamThreads, 3) void gg_stream_kernel(const uint
             const int64_t src = a_rows ? a_rows[p] : p;
             const float rs = a_scale[src] * (kMx ? 1.0f : kUnitScale);
 #pragma unroll
-            for (int s = 0; s < NS; ++s) out[(int64_t)p * N + n0 + 16 * s + col] = acc[s][r] * rs;
+            for (int s = 0; s < NS; ++s)
+              if (sub_ok[s]) out[(int64_t)p * N + n0 + 16 * s + col] = acc[s][r] * rs;
           }
         }
       }
@@ -374,7 +401,8 @@ __global__ __launch_bounds__(kStreamThreads, 3) void gg_stream_kernel(const uint
 template <int NS, int CH, int kForm, bool kSwiglu>
 static void launch_variant(const GemmArgs& g, hipStream_t stream) {
   const dim3 grid((unsigned)((g.N + 64 * NS - 1) / (64 * NS)), (unsigned)g.E);
-  hipLaunchKernelGGL((gg_stream_kernel<NS, CH, kForm, kSwiglu>), grid, dim3(kStreamThreads), 0, stream, g.a,
+  auto kernel = g.row_major ? gg_stream_kernel<NS, CH, kForm, kSwiglu, true> : gg_stream_kernel<NS, CH, kForm, kSwiglu, false>;
+  hipLaunchKernelGGL(kernel, grid, dim3(kStreamThreads), 0, stream, g.a,
                      g.a_scale, g.a_rowsum, g.a_rows, g.offsets, g.w_packed, g.w_scale, g.N, g.K, g.out, g.pmax);
 }
 

@@ -36,6 +36,10 @@ struct GemmArgs {
   // byte k/2 when k is even), w_scale the E8M0 block scales (the 4-byte word of
   // a row and group holds its four 32-element blocks)
   bool mx = false;
+  // the weights in the row-major stored format (INT4 int32 [E][N][K/8] words,
+  // nibble k at bits 4 (k mod 8); MXFP4 u8 [E][N][K/2]) with scales [E][N][K/128]
+  // (fp32) or [E][N][K/32] (E8M0): the stream kernel only
+  bool row_major = false;
 };
 
 hipError_t launch_quant_act(const uint16_t* x, int64_t T, int64_t H, int64_t ld, uint8_t* q, float* s,

@@ -11,7 +11,7 @@ the intermediate bytes.
 Expert weights are given in the packed format (int32 [E][N][K/8] words of
 uint4b8 nibbles and fp32 [E][N][K/128] group scales) and stay resident on the
 GPU in the GEMM storage (prepack_int4, once at construction: 1 KB per 16 rows
-x 128 K, group-major scales).
+x 128 K, group-major scales), which the _prepacked GEMM calls read.
 W4A8MoEChannel is the per-channel INT4 x per-token INT8 variant: fp32 [E][N]
 scales, INT8 activations.  W4A8MoEMxfp4 holds MXFP4 group-32 experts (E2M1
 codes uint8 [E][N][K/2], E8M0 scales uint8 [E][N][K/32]) and uses the same
@@ -31,8 +31,8 @@ from . import ops
 
 class W4A8MoE:
     K_PER_ITEM = 8                                        # K elements per item of a weight row (int32 words)
-    GEMM = staticmethod(ops.w4a8_moe_grouped_gemm)
-    GEMM_SWIGLU = staticmethod(ops.w4a8_moe_grouped_gemm_swiglu)
+    GEMM = staticmethod(ops.w4a8_moe_grouped_gemm_prepacked)
+    GEMM_SWIGLU = staticmethod(ops.w4a8_moe_grouped_gemm_swiglu_prepacked)
 
     def __init__(self, w13: torch.Tensor, s13: torch.Tensor, w2: torch.Tensor, s2: torch.Tensor, k: int,
                  renormalize: bool = True, fused: bool = True, front: bool = True):
@@ -183,15 +183,15 @@ class W4A8MoEChannel(W4A8MoE):
             step("permute", ops.w4a8_moe_permute, b["ids"], self.E, b["offsets"], b["row_token"], b["inv_pos"],
                  b["workspace"])
         if self.fused:
-            step("gemm_gate_up", ops.w4a8_moe_grouped_gemm_swiglu_i8, b["qx"], b["sx"], b["rx"], b["row_token"],
-                 b["offsets"], self.w13, self.s13, R, b["act"], b["pmax"], algo)
+            step("gemm_gate_up", ops.w4a8_moe_grouped_gemm_swiglu_i8_prepacked, b["qx"], b["sx"], b["rx"],
+                 b["row_token"], b["offsets"], self.w13, self.s13, R, b["act"], b["pmax"], algo)
             step("swiglu", ops.w4a8_moe_requant_i8, b["act"], b["pmax"], b["qa"], b["sa"], b["ra"])
         else:
-            step("gemm_gate_up", ops.w4a8_moe_grouped_gemm_i8, b["qx"], b["sx"], b["rx"], b["row_token"],
-                 b["offsets"], self.w13, self.s13, b["h"], R, algo)
+            step("gemm_gate_up", ops.w4a8_moe_grouped_gemm_i8_prepacked, b["qx"], b["sx"], b["rx"],
+                 b["row_token"], b["offsets"], self.w13, self.s13, b["h"], R, algo)
             step("swiglu", ops.w4a8_moe_swiglu_i8, b["h"], b["qa"], b["sa"], b["ra"])
-        step("gemm_down", ops.w4a8_moe_grouped_gemm_i8, b["qa"], b["sa"], b["ra"], None, b["offsets"], self.w2,
-             self.s2, b["o"], R, algo)
+        step("gemm_down", ops.w4a8_moe_grouped_gemm_i8_prepacked, b["qa"], b["sa"], b["ra"], None, b["offsets"],
+             self.w2, self.s2, b["o"], R, algo)
         return step("unpermute", ops.w4a8_moe_unpermute, b["o"], b["inv_pos"], b["w"], y, y_dtype)
 
     __call__ = forward
@@ -203,8 +203,8 @@ class W4A8MoEMxfp4(W4A8MoE):
     GEMM storage (prepack_mxfp4, once at construction), with the FP8
     activations of the group-128 form: only the two GEMMs differ."""
     K_PER_ITEM = 2                                        # two E2M1 codes per byte
-    GEMM = staticmethod(ops.w4a8_moe_grouped_gemm_mxfp4)
-    GEMM_SWIGLU = staticmethod(ops.w4a8_moe_grouped_gemm_swiglu_mxfp4)
+    GEMM = staticmethod(ops.w4a8_moe_grouped_gemm_mxfp4_prepacked)
+    GEMM_SWIGLU = staticmethod(ops.w4a8_moe_grouped_gemm_swiglu_mxfp4_prepacked)
 
     @staticmethod
     def prepack(w13, s13, w2, s2):

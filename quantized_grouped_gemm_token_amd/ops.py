@@ -33,35 +33,44 @@ _SIGNATURES = {
     "w4a8_moe_route": (ctypes.c_int, [_c_p, _i64, _i32, _i32, _i32, _c_p, _c_p, _c_p]),
     "w4a8_moe_permute_workspace_bytes": (ctypes.c_int64, [_i64, _i32, _i32]),
     "w4a8_moe_permute": (ctypes.c_int, [_c_p, _i64, _i32, _i32, _c_p, _c_p, _c_p, _c_p, _i64, _c_p]),
-    "w4a8_moe_grouped_gemm": (ctypes.c_int, [_c_p, _c_p, _c_p, _i64, _c_p, _i32, _c_p, _c_p, _i64, _i64, _c_p,
-                                             _c_p]),
-    "w4a8_moe_grouped_gemm_algo": (ctypes.c_int, [_c_p, _c_p, _c_p, _i64, _c_p, _i32, _c_p, _c_p, _i64, _i64,
-                                                  _c_p, _i32, _c_p]),
     "w4a8_moe_swiglu": (ctypes.c_int, [_c_p, _i64, _i64, _c_p, _c_p, _c_p]),
     "w4a8_moe_unpermute": (ctypes.c_int, [_c_p, _c_p, _c_p, _i64, _i32, _i64, _c_p, _i32, _c_p]),
     "w4a8_moe_quantize_weights": (ctypes.c_int, [_c_p, _i64, _i64, _i32, _c_p, _c_p, _c_p]),
     "w4a8_moe_quant_act_i8": (ctypes.c_int, [_c_p, _i64, _i64, _i64, _c_p, _c_p, _c_p, _c_p]),
-    "w4a8_moe_grouped_gemm_i8": (ctypes.c_int, [_c_p, _c_p, _c_p, _c_p, _i64, _c_p, _i32, _c_p, _c_p, _i64, _i64,
-                                                _c_p, _i32, _c_p]),
     "w4a8_moe_swiglu_i8": (ctypes.c_int, [_c_p, _i64, _i64, _c_p, _c_p, _c_p, _c_p]),
     "w4a8_moe_quantize_weights_channel": (ctypes.c_int, [_c_p, _i64, _i64, _c_p, _c_p, _c_p]),
-    "w4a8_moe_grouped_gemm_swiglu": (ctypes.c_int, [_c_p, _c_p, _c_p, _i64, _c_p, _i32, _c_p, _c_p, _i64, _i64,
-                                                    _c_p, _c_p, _i32, _c_p]),
-    "w4a8_moe_grouped_gemm_swiglu_i8": (ctypes.c_int, [_c_p, _c_p, _c_p, _c_p, _i64, _c_p, _i32, _c_p, _c_p, _i64,
-                                                       _i64, _c_p, _c_p, _i32, _c_p]),
     "w4a8_moe_requant": (ctypes.c_int, [_c_p, _c_p, _i64, _i64, _c_p, _c_p, _c_p]),
     "w4a8_moe_requant_i8": (ctypes.c_int, [_c_p, _c_p, _i64, _i64, _c_p, _c_p, _c_p, _c_p]),
     "w4a8_moe_quantize_weights_mxfp4": (ctypes.c_int, [_c_p, _i64, _i64, _c_p, _c_p, _c_p]),
     "w4a8_moe_prepack_int4": (ctypes.c_int, [_c_p, _c_p, _i32, _i64, _i64, _c_p, _c_p, _c_p]),
     "w4a8_moe_prepack_mxfp4": (ctypes.c_int, [_c_p, _c_p, _i32, _i64, _i64, _c_p, _c_p, _c_p]),
-    "w4a8_moe_grouped_gemm_mxfp4": (ctypes.c_int, [_c_p, _c_p, _c_p, _i64, _c_p, _i32, _c_p, _c_p, _i64, _i64,
-                                                   _c_p, _i32, _c_p]),
-    "w4a8_moe_grouped_gemm_swiglu_mxfp4": (ctypes.c_int, [_c_p, _c_p, _c_p, _i64, _c_p, _i32, _c_p, _c_p, _i64,
-                                                          _i64, _c_p, _c_p, _i32, _c_p]),
     "w4a8_moe_front": (ctypes.c_int, [_c_p, _i64, _i64, _i64, _c_p, _c_p, _c_p, _i32, _i32, _i32, _c_p, _c_p, _c_p,
                                       _c_p, _c_p, _c_p, _i64, _c_p, _c_p]),
     "w4a8_moe_front_i8": (ctypes.c_int, [_c_p, _i64, _i64, _i64, _c_p, _c_p, _c_p, _c_p, _i32, _i32, _i32, _c_p,
                                          _c_p, _c_p, _c_p, _c_p, _c_p, _i64, _c_p, _c_p]),
+    "w4a8_moe_grouped_gemm": (ctypes.c_int, [_c_p, _c_p, _c_p, _i64, _c_p, _i32, _c_p, _c_p, _i64, _i64, _c_p, _c_p]),
+    "w4a8_moe_grouped_gemm_prepacked": (ctypes.c_int,
+        [_c_p, _c_p, _c_p, _i64, _c_p, _i32, _c_p, _c_p, _i64, _i64, _c_p, _i32, _c_p]),
+    "w4a8_moe_grouped_gemm_swiglu": (ctypes.c_int,
+        [_c_p, _c_p, _c_p, _i64, _c_p, _i32, _c_p, _c_p, _i64, _i64, _c_p, _c_p, _c_p]),
+    "w4a8_moe_grouped_gemm_swiglu_prepacked": (ctypes.c_int,
+        [_c_p, _c_p, _c_p, _i64, _c_p, _i32, _c_p, _c_p, _i64, _i64, _c_p, _c_p, _i32, _c_p]),
+    "w4a8_moe_grouped_gemm_i8": (ctypes.c_int,
+        [_c_p, _c_p, _c_p, _c_p, _i64, _c_p, _i32, _c_p, _c_p, _i64, _i64, _c_p, _c_p]),
+    "w4a8_moe_grouped_gemm_i8_prepacked": (ctypes.c_int,
+        [_c_p, _c_p, _c_p, _c_p, _i64, _c_p, _i32, _c_p, _c_p, _i64, _i64, _c_p, _i32, _c_p]),
+    "w4a8_moe_grouped_gemm_swiglu_i8": (ctypes.c_int,
+        [_c_p, _c_p, _c_p, _c_p, _i64, _c_p, _i32, _c_p, _c_p, _i64, _i64, _c_p, _c_p, _c_p]),
+    "w4a8_moe_grouped_gemm_swiglu_i8_prepacked": (ctypes.c_int,
+        [_c_p, _c_p, _c_p, _c_p, _i64, _c_p, _i32, _c_p, _c_p, _i64, _i64, _c_p, _c_p, _i32, _c_p]),
+    "w4a8_moe_grouped_gemm_mxfp4": (ctypes.c_int,
+        [_c_p, _c_p, _c_p, _i64, _c_p, _i32, _c_p, _c_p, _i64, _i64, _c_p, _c_p]),
+    "w4a8_moe_grouped_gemm_mxfp4_prepacked": (ctypes.c_int,
+        [_c_p, _c_p, _c_p, _i64, _c_p, _i32, _c_p, _c_p, _i64, _i64, _c_p, _i32, _c_p]),
+    "w4a8_moe_grouped_gemm_swiglu_mxfp4": (ctypes.c_int,
+        [_c_p, _c_p, _c_p, _i64, _c_p, _i32, _c_p, _c_p, _i64, _i64, _c_p, _c_p, _c_p]),
+    "w4a8_moe_grouped_gemm_swiglu_mxfp4_prepacked": (ctypes.c_int,
+        [_c_p, _c_p, _c_p, _i64, _c_p, _i32, _c_p, _c_p, _i64, _i64, _c_p, _c_p, _i32, _c_p]),
     "w4a8_moe_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "w4a8_moe_last_error": (ctypes.c_char_p, []),
     "w4a8_moe_device_supported": (ctypes.c_int, []),
@@ -257,37 +266,6 @@ def w4a8_moe_permute(ids: torch.Tensor, E: int, offsets=None, row_token=None, in
     return offsets, row_token, inv_pos
 
 
-def w4a8_moe_grouped_gemm(a: torch.Tensor, a_scale: torch.Tensor, a_rows: torch.Tensor | None,
-                          offsets: torch.Tensor, w_packed: torch.Tensor, w_scale: torch.Tensor, M_total: int,
-                          out: torch.Tensor | None = None, algo: int = W4A8_GG_AUTO):
-    """Grouped W4A8 GEMM -> out fp32 [M_total, N] (rows of expert e: offsets[e]..offsets[e+1]).
-
-    w_packed / w_scale: the GEMM storage written by w4a8_moe_prepack_int4."""
-    _need(a, "a", torch.uint8, 2)
-    dev = a.device
-    _need(a_scale, "a_scale", torch.float32, 1, dev)
-    if a_rows is not None:
-        _need(a_rows, "a_rows", torch.int32, 1, dev)
-        if a_rows.numel() < M_total:
-            raise ValueError("a_rows must hold M_total entries")
-    _need(offsets, "offsets", torch.int32, 1, dev)
-    E, N, KW = _int4_storage(w_packed, "w_packed", dev)
-    _need(w_scale, "w_scale", torch.float32, 3, dev)
-    K = a.shape[1]
-    if KW != K or tuple(w_scale.shape) != (E, K // 128, N) or offsets.numel() != E + 1:
-        raise ValueError("w_packed [E,N/16,K/128,16,16], w_scale [E,K/128,N] and offsets [E+1] must match a [*,K]")
-    if a_scale.numel() != a.shape[0]:
-        raise ValueError("a_scale must have one entry per row of a")
-    out = torch.empty((M_total, N), dtype=torch.float32, device=dev) if out is None else out
-    _need(out, "out", torch.float32, 2, dev)
-    if tuple(out.shape) != (M_total, N):
-        raise ValueError("out must be [M_total, N]")
-    _check("w4a8_moe_grouped_gemm",
-           lib().w4a8_moe_grouped_gemm_algo(_p(a), _p(a_scale), _p(a_rows), M_total, _p(offsets), E,
-                                            _p(w_packed), _p(w_scale), N, K, _p(out), algo, _stream(dev)))
-    return out
-
-
 def w4a8_moe_swiglu(h: torch.Tensor, qa: torch.Tensor | None = None, sa: torch.Tensor | None = None):
     """fp32 [M, 2I] -> (E4M3 codes uint8 [M, I], per-row scales fp32 [M])."""
     _need(h, "h", torch.float32, 2)
@@ -375,36 +353,6 @@ def w4a8_moe_quant_act_i8(x: torch.Tensor, qx=None, sx=None, rowsum=None):
     return qx, sx, rowsum
 
 
-def w4a8_moe_grouped_gemm_i8(a: torch.Tensor, a_scale: torch.Tensor, a_rowsum: torch.Tensor,
-                             a_rows: torch.Tensor | None, offsets: torch.Tensor, w_packed: torch.Tensor,
-                             w_scale: torch.Tensor, out: torch.Tensor | None = None, M_total: int | None = None,
-                             algo: int = W4A8_GG_AUTO):
-    """int8 [*, K] activations x per-channel INT4 experts (GEMM storage [E, N/16, K/128, 16, 16],
-    scales [E, N]) -> fp32 [M_total, N]."""
-    _need(a, "a", torch.int8, 2)
-    dev = a.device
-    _need(a_scale, "a_scale", torch.float32, 1, dev)
-    _need(a_rowsum, "a_rowsum", torch.int32, 1, dev)
-    _need(offsets, "offsets", torch.int32, 1, dev)
-    E, N, K = _int4_storage(w_packed, "w_packed", dev)
-    _need(w_scale, "w_scale", torch.float32, 2, dev)
-    if a.shape[1] != K or tuple(w_scale.shape) != (E, N) or offsets.numel() != E + 1:
-        raise ValueError("a must be [*, K], w_scale [E, N], offsets [E+1]")
-    if a_rows is not None:
-        _need(a_rows, "a_rows", torch.int32, 1, dev)
-        M = a_rows.numel() if M_total is None else M_total
-    else:
-        M = a.shape[0] if M_total is None else M_total
-    out = torch.empty((M, N), dtype=torch.float32, device=dev) if out is None else out
-    _need(out, "out", torch.float32, 2, dev)
-    if out.shape[0] < M or out.shape[1] != N:
-        raise ValueError("out must be at least [M_total, N]")
-    _check("w4a8_moe_grouped_gemm_i8",
-           lib().w4a8_moe_grouped_gemm_i8(_p(a), _p(a_scale), _p(a_rowsum), _p(a_rows), M, _p(offsets), E,
-                                          _p(w_packed), _p(w_scale), N, K, _p(out), algo, _stream(dev)))
-    return out
-
-
 def w4a8_moe_swiglu_i8(h: torch.Tensor, qa=None, sa=None, rowsum=None):
     """fp32 [M, 2I] -> (int8 codes [M, I], scales fp32 [M], code row sums int32 [M])."""
     _need(h, "h", torch.float32, 2)
@@ -455,62 +403,6 @@ def _act_out(M: int, I: int, dev, act, act_pmax):
     _need(act_pmax, "act_pmax", torch.float32, 2, dev)
     if act.shape[0] < M or act.shape[1] != I or act_pmax.shape[0] < M or act_pmax.shape[1] != I // 64:
         raise ValueError("act must be at least [M_total, I] and act_pmax [M_total, I/64]")
-    return act, act_pmax
-
-
-def w4a8_moe_grouped_gemm_swiglu(a: torch.Tensor, a_scale: torch.Tensor, a_rows: torch.Tensor | None,
-                                 offsets: torch.Tensor, w13: torch.Tensor, s13: torch.Tensor, M_total: int,
-                                 act: torch.Tensor | None = None, act_pmax: torch.Tensor | None = None,
-                                 algo: int = W4A8_GG_AUTO):
-    """Gate/up GEMM with SwiGLU in its epilogue -> (act fp32 [M_total, I], partial row maxima of |act| [M_total, I/64])."""
-    _need(a, "a", torch.uint8, 2)
-    dev = a.device
-    _need(a_scale, "a_scale", torch.float32, 1, dev)
-    if a_rows is not None:
-        _need(a_rows, "a_rows", torch.int32, 1, dev)
-        if a_rows.numel() < M_total:
-            raise ValueError("a_rows must hold M_total entries")
-    _need(offsets, "offsets", torch.int32, 1, dev)
-    E, N2, KW = _int4_storage(w13, "w13", dev)
-    _need(s13, "s13", torch.float32, 3, dev)
-    K = a.shape[1]
-    if N2 % 2 or KW != K or tuple(s13.shape) != (E, K // 128, N2) or offsets.numel() != E + 1:
-        raise ValueError("w13 [E,2I/16,K/128,16,16], s13 [E,K/128,2I] and offsets [E+1] must match a [*,K]")
-    if a_scale.numel() != a.shape[0]:
-        raise ValueError("a_scale must have one entry per row of a")
-    I = N2 // 2
-    act, act_pmax = _act_out(M_total, I, dev, act, act_pmax)
-    _check("w4a8_moe_grouped_gemm_swiglu",
-           lib().w4a8_moe_grouped_gemm_swiglu(_p(a), _p(a_scale), _p(a_rows), M_total, _p(offsets), E, _p(w13),
-                                              _p(s13), I, K, _p(act), _p(act_pmax), algo, _stream(dev)))
-    return act, act_pmax
-
-
-def w4a8_moe_grouped_gemm_swiglu_i8(a: torch.Tensor, a_scale: torch.Tensor, a_rowsum: torch.Tensor,
-                                    a_rows: torch.Tensor | None, offsets: torch.Tensor, w13: torch.Tensor,
-                                    s13: torch.Tensor, M_total: int, act: torch.Tensor | None = None,
-                                    act_pmax: torch.Tensor | None = None, algo: int = W4A8_GG_AUTO):
-    """INT8 form of w4a8_moe_grouped_gemm_swiglu (per-channel scales s13 [E, 2I])."""
-    _need(a, "a", torch.int8, 2)
-    dev = a.device
-    _need(a_scale, "a_scale", torch.float32, 1, dev)
-    _need(a_rowsum, "a_rowsum", torch.int32, 1, dev)
-    if a_rows is not None:
-        _need(a_rows, "a_rows", torch.int32, 1, dev)
-        if a_rows.numel() < M_total:
-            raise ValueError("a_rows must hold M_total entries")
-    _need(offsets, "offsets", torch.int32, 1, dev)
-    E, N2, KW = _int4_storage(w13, "w13", dev)
-    _need(s13, "s13", torch.float32, 2, dev)
-    K = a.shape[1]
-    if N2 % 2 or KW != K or tuple(s13.shape) != (E, N2) or offsets.numel() != E + 1:
-        raise ValueError("w13 [E,2I/16,K/128,16,16], s13 [E,2I] and offsets [E+1] must match a [*,K]")
-    I = N2 // 2
-    act, act_pmax = _act_out(M_total, I, dev, act, act_pmax)
-    _check("w4a8_moe_grouped_gemm_swiglu_i8",
-           lib().w4a8_moe_grouped_gemm_swiglu_i8(_p(a), _p(a_scale), _p(a_rowsum), _p(a_rows), M_total,
-                                                 _p(offsets), E, _p(w13), _p(s13), I, K, _p(act), _p(act_pmax),
-                                                 algo, _stream(dev)))
     return act, act_pmax
 
 
@@ -632,58 +524,253 @@ def w4a8_moe_prepack_mxfp4(w_packed: torch.Tensor, w_scale: torch.Tensor, w_blk=
     return w_blk, s_blk
 
 
-def _check_mx_weights(a, a_scale, a_rows, offsets, w, s, M_total, names):
-    """Checks of a GEMM on MXFP4 weights in the GEMM storage: w [E, N/16, K/128, 16, 64], s [E, K/128, N, 4]."""
-    _need(a, "a", torch.uint8, 2)
+
+
+# ------------------------------------------------------------ grouped GEMMs
+# Each GEMM exists twice: on the weights as stored (row-major: INT4 int32
+# [E, N, K/8] uint4b8 words, MXFP4 uint8 [E, N, K/2] codes) and, with the
+# suffix _prepacked, on the GEMM storage written by w4a8_moe_prepack_int4 /
+# w4a8_moe_prepack_mxfp4 (INT4 int32 [E, N/16, K/128, 16, 16], MXFP4 uint8
+# [E, N/16, K/128, 16, 64]), which the layer classes use.
+def _int4_weights(w: torch.Tensor, name: str, dev, prepacked: bool) -> tuple[int, int, int]:
+    """(E, N, K) of INT4 weights in either format."""
+    if prepacked:
+        return _int4_storage(w, name, dev)
+    _need(w, name, torch.int32, 3, dev)
+    E, N, KW = w.shape
+    return E, N, 8 * KW
+
+
+def _g128_scales(s: torch.Tensor, name: str, dev, E: int, N: int, K: int, prepacked: bool) -> None:
+    _need(s, name, torch.float32, 3, dev)
+    want = (E, K // 128, N) if prepacked else (E, N, K // 128)
+    if tuple(s.shape) != want:
+        raise ValueError(f"{name} must be {list(want)} ({'[E, K/128, N]' if prepacked else '[E, N, K/128]'})")
+
+
+def _mx_weights(w: torch.Tensor, s: torch.Tensor, names, dev, prepacked: bool) -> tuple[int, int, int]:
+    """(E, N, K) of MXFP4 weights: stored w [E, N, K/2] with s [E, N, K/32], or the GEMM
+    storage w [E, N/16, K/128, 16, 64] with s [E, K/128, N, 4]."""
+    if prepacked:
+        _need(w, names[0], torch.uint8, 5, dev)
+        _need(s, names[1], torch.uint8, 4, dev)
+        E, NB, G, sixteen, sixtyfour = w.shape
+        N, K = 16 * NB, 128 * G
+        if (sixteen, sixtyfour) != (16, 64) or tuple(s.shape) != (E, G, N, 4):
+            raise ValueError(f"{names[0]} [E,N/16,K/128,16,64] and {names[1]} [E,K/128,N,4] must match "
+                             "(prepack_mxfp4 writes this storage)")
+        return E, N, K
+    _need(w, names[0], torch.uint8, 3, dev)
+    _need(s, names[1], torch.uint8, 3, dev)
+    E, N, KB = w.shape
+    K = 2 * KB
+    if tuple(s.shape) != (E, N, K // 32):
+        raise ValueError(f"{names[0]} [E,N,K/2] and {names[1]} [E,N,K/32] must match")
+    return E, N, K
+
+
+def _gemm_inputs(a, a_scale, a_rows, offsets, M_total, a_dtype):
+    _need(a, "a", a_dtype, 2)
     dev = a.device
     _need(a_scale, "a_scale", torch.float32, 1, dev)
     if a_rows is not None:
         _need(a_rows, "a_rows", torch.int32, 1, dev)
         if a_rows.numel() < M_total:
             raise ValueError("a_rows must hold M_total entries")
+    elif a.shape[0] < M_total:
+        raise ValueError("a must hold M_total rows when a_rows is None")
     _need(offsets, "offsets", torch.int32, 1, dev)
-    _need(w, names[0], torch.uint8, 5, dev)
-    _need(s, names[1], torch.uint8, 4, dev)
-    E, NB, G, sixteen, sixtyfour = w.shape
-    N = 16 * NB
-    K = a.shape[1]
-    if (sixteen, sixtyfour) != (16, 64) or G * 128 != K or tuple(s.shape) != (E, G, N, 4) or \
-            offsets.numel() != E + 1:
-        raise ValueError(f"{names[0]} [E,N/16,K/128,16,64], {names[1]} [E,K/128,N,4] and offsets [E+1] must match "
-                         "a [*,K] (prepack_mxfp4 writes this storage)")
     if a_scale.numel() != a.shape[0]:
         raise ValueError("a_scale must have one entry per row of a")
-    return dev, E, N, K
+    return dev
+
+
+def _plain_out(out, M_total: int, N: int, dev):
+    out = torch.empty((M_total, N), dtype=torch.float32, device=dev) if out is None else out
+    _need(out, "out", torch.float32, 2, dev)
+    if out.shape[0] < M_total or out.shape[1] != N:
+        raise ValueError("out must be at least [M_total, N]")
+    return out
+
+
+def _gemm_g128(prepacked, a, a_scale, a_rows, offsets, w_packed, w_scale, M_total, out, algo):
+    dev = _gemm_inputs(a, a_scale, a_rows, offsets, M_total, torch.uint8)
+    E, N, K = _int4_weights(w_packed, "w_packed", dev, prepacked)
+    _g128_scales(w_scale, "w_scale", dev, E, N, K, prepacked)
+    if a.shape[1] != K or offsets.numel() != E + 1:
+        raise ValueError("w_packed, w_scale and offsets [E+1] must match a [*, K]")
+    out = _plain_out(out, M_total, N, dev)
+    args = (_p(a), _p(a_scale), _p(a_rows), M_total, _p(offsets), E, _p(w_packed), _p(w_scale), N, K, _p(out))
+    if prepacked:
+        _check("w4a8_moe_grouped_gemm_prepacked", lib().w4a8_moe_grouped_gemm_prepacked(*args, algo, _stream(dev)))
+    else:
+        _check("w4a8_moe_grouped_gemm", lib().w4a8_moe_grouped_gemm(*args, _stream(dev)))
+    return out
+
+
+def w4a8_moe_grouped_gemm(a: torch.Tensor, a_scale: torch.Tensor, a_rows: torch.Tensor | None,
+                          offsets: torch.Tensor, w_packed: torch.Tensor, w_scale: torch.Tensor, M_total: int,
+                          out: torch.Tensor | None = None):
+    """Grouped W4A8 GEMM on stored weights (int32 [E, N, K/8], fp32 [E, N, K/128]) -> fp32 [M_total, N]
+    (rows of expert e: offsets[e]..offsets[e+1])."""
+    return _gemm_g128(False, a, a_scale, a_rows, offsets, w_packed, w_scale, M_total, out, W4A8_GG_AUTO)
+
+
+def w4a8_moe_grouped_gemm_prepacked(a: torch.Tensor, a_scale: torch.Tensor, a_rows: torch.Tensor | None,
+                                    offsets: torch.Tensor, w_packed: torch.Tensor, w_scale: torch.Tensor,
+                                    M_total: int, out: torch.Tensor | None = None, algo: int = W4A8_GG_AUTO):
+    """The same on the GEMM storage (w4a8_moe_prepack_int4: int32 [E, N/16, K/128, 16, 16], fp32 [E, K/128, N])."""
+    return _gemm_g128(True, a, a_scale, a_rows, offsets, w_packed, w_scale, M_total, out, algo)
+
+
+def _gemm_i8(prepacked, a, a_scale, a_rowsum, a_rows, offsets, w_packed, w_scale, out, M_total, algo):
+    if M_total is None:
+        M_total = a_rows.numel() if a_rows is not None else a.shape[0]
+    dev = _gemm_inputs(a, a_scale, a_rows, offsets, M_total, torch.int8)
+    _need(a_rowsum, "a_rowsum", torch.int32, 1, dev)
+    E, N, K = _int4_weights(w_packed, "w_packed", dev, prepacked)
+    _need(w_scale, "w_scale", torch.float32, 2, dev)
+    if a.shape[1] != K or tuple(w_scale.shape) != (E, N) or offsets.numel() != E + 1:
+        raise ValueError("a must be [*, K], w_scale [E, N], offsets [E+1]")
+    out = _plain_out(out, M_total, N, dev)
+    args = (_p(a), _p(a_scale), _p(a_rowsum), _p(a_rows), M_total, _p(offsets), E, _p(w_packed), _p(w_scale), N,
+            K, _p(out))
+    if prepacked:
+        _check("w4a8_moe_grouped_gemm_i8_prepacked",
+               lib().w4a8_moe_grouped_gemm_i8_prepacked(*args, algo, _stream(dev)))
+    else:
+        _check("w4a8_moe_grouped_gemm_i8", lib().w4a8_moe_grouped_gemm_i8(*args, _stream(dev)))
+    return out
+
+
+def w4a8_moe_grouped_gemm_i8(a: torch.Tensor, a_scale: torch.Tensor, a_rowsum: torch.Tensor,
+                             a_rows: torch.Tensor | None, offsets: torch.Tensor, w_packed: torch.Tensor,
+                             w_scale: torch.Tensor, out: torch.Tensor | None = None, M_total: int | None = None):
+    """int8 [*, K] activations x per-channel INT4 experts as stored (int32 [E, N, K/8], scales [E, N])
+    -> fp32 [M_total, N]."""
+    return _gemm_i8(False, a, a_scale, a_rowsum, a_rows, offsets, w_packed, w_scale, out, M_total, W4A8_GG_AUTO)
+
+
+def w4a8_moe_grouped_gemm_i8_prepacked(a: torch.Tensor, a_scale: torch.Tensor, a_rowsum: torch.Tensor,
+                                       a_rows: torch.Tensor | None, offsets: torch.Tensor, w_packed: torch.Tensor,
+                                       w_scale: torch.Tensor, out: torch.Tensor | None = None,
+                                       M_total: int | None = None, algo: int = W4A8_GG_AUTO):
+    """The same on the GEMM storage of the weights (int32 [E, N/16, K/128, 16, 16])."""
+    return _gemm_i8(True, a, a_scale, a_rowsum, a_rows, offsets, w_packed, w_scale, out, M_total, algo)
+
+
+def _act_out(M: int, I: int, dev, act, act_pmax):
+    act = torch.empty((M, I), dtype=torch.float32, device=dev) if act is None else act
+    act_pmax = torch.empty((M, I // 64), dtype=torch.float32, device=dev) if act_pmax is None else act_pmax
+    _need(act, "act", torch.float32, 2, dev)
+    _need(act_pmax, "act_pmax", torch.float32, 2, dev)
+    if act.shape[0] < M or act.shape[1] != I or act_pmax.shape[0] < M or act_pmax.shape[1] != I // 64:
+        raise ValueError("act must be at least [M_total, I] and act_pmax [M_total, I/64]")
+    return act, act_pmax
+
+
+def _gemm_swiglu(form, prepacked, a, a_scale, a_rowsum, a_rows, offsets, w13, s13, M_total, act, act_pmax, algo):
+    dev = _gemm_inputs(a, a_scale, a_rows, offsets, M_total, torch.int8 if form == "i8" else torch.uint8)
+    if form == "mxfp4":
+        E, N2, K = _mx_weights(w13, s13, ("w13", "s13"), dev, prepacked)
+    else:
+        E, N2, K = _int4_weights(w13, "w13", dev, prepacked)
+        if form == "i8":
+            _need(a_rowsum, "a_rowsum", torch.int32, 1, dev)
+            _need(s13, "s13", torch.float32, 2, dev)
+            if tuple(s13.shape) != (E, N2):
+                raise ValueError("s13 must be [E, 2I]")
+        else:
+            _g128_scales(s13, "s13", dev, E, N2, K, prepacked)
+    if N2 % 2 or a.shape[1] != K or offsets.numel() != E + 1:
+        raise ValueError("w13 must hold 2I rows of K, offsets [E+1], and a [*, K]")
+    I = N2 // 2
+    act, act_pmax = _act_out(M_total, I, dev, act, act_pmax)
+    head = (_p(a), _p(a_scale)) + ((_p(a_rowsum),) if form == "i8" else ())
+    args = head + (_p(a_rows), M_total, _p(offsets), E, _p(w13), _p(s13), I, K, _p(act), _p(act_pmax))
+    name = "w4a8_moe_grouped_gemm_swiglu" + ("" if form == "g128" else "_" + form) + ("_prepacked" if prepacked else "")
+    fn = getattr(lib(), name)
+    _check(name, fn(*args, algo, _stream(dev)) if prepacked else fn(*args, _stream(dev)))
+    return act, act_pmax
+
+
+def w4a8_moe_grouped_gemm_swiglu(a: torch.Tensor, a_scale: torch.Tensor, a_rows: torch.Tensor | None,
+                                 offsets: torch.Tensor, w13: torch.Tensor, s13: torch.Tensor, M_total: int,
+                                 act: torch.Tensor | None = None, act_pmax: torch.Tensor | None = None):
+    """Gate/up GEMM with SwiGLU in its epilogue on stored weights (int32 [E, 2I, K/8], fp32 [E, 2I, K/128])
+    -> (act fp32 [M_total, I], partial row maxima of |act| [M_total, I/64])."""
+    return _gemm_swiglu("g128", False, a, a_scale, None, a_rows, offsets, w13, s13, M_total, act, act_pmax,
+                        W4A8_GG_AUTO)
+
+
+def w4a8_moe_grouped_gemm_swiglu_prepacked(a: torch.Tensor, a_scale: torch.Tensor, a_rows: torch.Tensor | None,
+                                           offsets: torch.Tensor, w13: torch.Tensor, s13: torch.Tensor,
+                                           M_total: int, act: torch.Tensor | None = None,
+                                           act_pmax: torch.Tensor | None = None, algo: int = W4A8_GG_AUTO):
+    """The same on the GEMM storage (int32 [E, 2I/16, K/128, 16, 16], fp32 [E, K/128, 2I])."""
+    return _gemm_swiglu("g128", True, a, a_scale, None, a_rows, offsets, w13, s13, M_total, act, act_pmax, algo)
+
+
+def w4a8_moe_grouped_gemm_swiglu_i8(a: torch.Tensor, a_scale: torch.Tensor, a_rowsum: torch.Tensor,
+                                    a_rows: torch.Tensor | None, offsets: torch.Tensor, w13: torch.Tensor,
+                                    s13: torch.Tensor, M_total: int, act: torch.Tensor | None = None,
+                                    act_pmax: torch.Tensor | None = None):
+    """INT8 form of w4a8_moe_grouped_gemm_swiglu (stored w13 int32 [E, 2I, K/8], per-channel s13 [E, 2I])."""
+    return _gemm_swiglu("i8", False, a, a_scale, a_rowsum, a_rows, offsets, w13, s13, M_total, act, act_pmax,
+                        W4A8_GG_AUTO)
+
+
+def w4a8_moe_grouped_gemm_swiglu_i8_prepacked(a: torch.Tensor, a_scale: torch.Tensor, a_rowsum: torch.Tensor,
+                                              a_rows: torch.Tensor | None, offsets: torch.Tensor, w13: torch.Tensor,
+                                              s13: torch.Tensor, M_total: int, act: torch.Tensor | None = None,
+                                              act_pmax: torch.Tensor | None = None, algo: int = W4A8_GG_AUTO):
+    """The same on the GEMM storage of w13."""
+    return _gemm_swiglu("i8", True, a, a_scale, a_rowsum, a_rows, offsets, w13, s13, M_total, act, act_pmax, algo)
+
+
+def _gemm_mx(prepacked, a, a_scale, a_rows, offsets, w_packed, w_scale, M_total, out, algo):
+    dev = _gemm_inputs(a, a_scale, a_rows, offsets, M_total, torch.uint8)
+    E, N, K = _mx_weights(w_packed, w_scale, ("w_packed", "w_scale"), dev, prepacked)
+    if a.shape[1] != K or offsets.numel() != E + 1:
+        raise ValueError("w_packed, w_scale and offsets [E+1] must match a [*, K]")
+    out = _plain_out(out, M_total, N, dev)
+    args = (_p(a), _p(a_scale), _p(a_rows), M_total, _p(offsets), E, _p(w_packed), _p(w_scale), N, K, _p(out))
+    if prepacked:
+        _check("w4a8_moe_grouped_gemm_mxfp4_prepacked",
+               lib().w4a8_moe_grouped_gemm_mxfp4_prepacked(*args, algo, _stream(dev)))
+    else:
+        _check("w4a8_moe_grouped_gemm_mxfp4", lib().w4a8_moe_grouped_gemm_mxfp4(*args, _stream(dev)))
+    return out
 
 
 def w4a8_moe_grouped_gemm_mxfp4(a: torch.Tensor, a_scale: torch.Tensor, a_rows: torch.Tensor | None,
                                 offsets: torch.Tensor, w_packed: torch.Tensor, w_scale: torch.Tensor, M_total: int,
-                                out: torch.Tensor | None = None, algo: int = W4A8_GG_AUTO):
-    """Grouped FP8 x MXFP4 GEMM -> out fp32 [M_total, N] (rows of expert e: offsets[e]..offsets[e+1])."""
-    dev, E, N, K = _check_mx_weights(a, a_scale, a_rows, offsets, w_packed, w_scale, M_total,
-                                     ("w_packed", "w_scale"))
-    out = torch.empty((M_total, N), dtype=torch.float32, device=dev) if out is None else out
-    _need(out, "out", torch.float32, 2, dev)
-    if tuple(out.shape) != (M_total, N):
-        raise ValueError("out must be [M_total, N]")
-    _check("w4a8_moe_grouped_gemm_mxfp4",
-           lib().w4a8_moe_grouped_gemm_mxfp4(_p(a), _p(a_scale), _p(a_rows), M_total, _p(offsets), E,
-                                             _p(w_packed), _p(w_scale), N, K, _p(out), algo, _stream(dev)))
-    return out
+                                out: torch.Tensor | None = None):
+    """Grouped FP8 x MXFP4 GEMM on stored weights (uint8 [E, N, K/2] codes, [E, N, K/32] E8M0 scales)
+    -> out fp32 [M_total, N]."""
+    return _gemm_mx(False, a, a_scale, a_rows, offsets, w_packed, w_scale, M_total, out, W4A8_GG_AUTO)
+
+
+def w4a8_moe_grouped_gemm_mxfp4_prepacked(a: torch.Tensor, a_scale: torch.Tensor, a_rows: torch.Tensor | None,
+                                          offsets: torch.Tensor, w_packed: torch.Tensor, w_scale: torch.Tensor,
+                                          M_total: int, out: torch.Tensor | None = None,
+                                          algo: int = W4A8_GG_AUTO):
+    """The same on the GEMM storage (w4a8_moe_prepack_mxfp4)."""
+    return _gemm_mx(True, a, a_scale, a_rows, offsets, w_packed, w_scale, M_total, out, algo)
 
 
 def w4a8_moe_grouped_gemm_swiglu_mxfp4(a: torch.Tensor, a_scale: torch.Tensor, a_rows: torch.Tensor | None,
                                        offsets: torch.Tensor, w13: torch.Tensor, s13: torch.Tensor, M_total: int,
-                                       act: torch.Tensor | None = None, act_pmax: torch.Tensor | None = None,
-                                       algo: int = W4A8_GG_AUTO):
-    """MXFP4 gate/up GEMM with SwiGLU in its epilogue -> (act fp32 [M_total, I], partial row maxima [M_total, I/64])."""
-    dev, E, N2, K = _check_mx_weights(a, a_scale, a_rows, offsets, w13, s13, M_total, ("w13", "s13"))
-    if N2 % 2:
-        raise ValueError("w13 must have 2I rows")
-    I = N2 // 2
-    act, act_pmax = _act_out(M_total, I, dev, act, act_pmax)
-    _check("w4a8_moe_grouped_gemm_swiglu_mxfp4",
-           lib().w4a8_moe_grouped_gemm_swiglu_mxfp4(_p(a), _p(a_scale), _p(a_rows), M_total, _p(offsets), E,
-                                                    _p(w13), _p(s13), I, K, _p(act), _p(act_pmax), algo,
-                                                    _stream(dev)))
-    return act, act_pmax
+                                       act: torch.Tensor | None = None, act_pmax: torch.Tensor | None = None):
+    """MXFP4 gate/up GEMM with SwiGLU in its epilogue on stored weights -> (act [M_total, I], row maxima)."""
+    return _gemm_swiglu("mxfp4", False, a, a_scale, None, a_rows, offsets, w13, s13, M_total, act, act_pmax,
+                        W4A8_GG_AUTO)
+
+
+def w4a8_moe_grouped_gemm_swiglu_mxfp4_prepacked(a: torch.Tensor, a_scale: torch.Tensor,
+                                                 a_rows: torch.Tensor | None, offsets: torch.Tensor,
+                                                 w13: torch.Tensor, s13: torch.Tensor, M_total: int,
+                                                 act: torch.Tensor | None = None,
+                                                 act_pmax: torch.Tensor | None = None, algo: int = W4A8_GG_AUTO):
+    """The same on the GEMM storage of w13 and s13."""
+    return _gemm_swiglu("mxfp4", True, a, a_scale, None, a_rows, offsets, w13, s13, M_total, act, act_pmax, algo)

@@ -92,26 +92,30 @@ def test_permute_checks(L):
 
 
 def test_grouped_gemm_checks(L):
-    f = L.w4a8_moe_grouped_gemm
+    f = L.w4a8_moe_grouped_gemm                    # weights as stored: N % 16
+    fp = L.w4a8_moe_grouped_gemm_prepacked         # GEMM storage: N % 64, and an algo
     good = dict(a=P, sa=P, rows=None, M=64, off=P, E=8, w=P, ws=P, N=256, K=256, out=P)
 
-    def call(**kw):
+    def call(fn=f, algo=None, **kw):
         d = dict(good, **kw)
-        return f(d["a"], d["sa"], d["rows"], d["M"], d["off"], d["E"], d["w"], d["ws"], d["N"], d["K"], d["out"],
-                 None)
-    assert call(N=96) == ERR_SHAPE                # N % 64
-    assert call(K=192) == ERR_SHAPE               # K % 128
-    assert call(E=0) == ERR_SHAPE
-    assert call(E=2000) == ERR_SHAPE
-    assert call(M=-1) == ERR_SHAPE
-    assert call(w=None) == ERR_NULL
-    assert call(off=None) == ERR_NULL
-    assert call(a=P + 8) == ERR_ALIGN
-    assert call(w=P + 4) == ERR_ALIGN
-    assert call(out=P + 4) == ERR_ALIGN
-    assert call(M=0, a=None, w=None) == OK        # no rows: no-op
-    g = L.w4a8_moe_grouped_gemm_algo
-    assert g(P, P, None, 64, P, 8, P, P, 256, 256, P, 7, None) == ERR_SHAPE   # unknown algo
+        args = (d["a"], d["sa"], d["rows"], d["M"], d["off"], d["E"], d["w"], d["ws"], d["N"], d["K"], d["out"])
+        return fn(*args, None) if algo is None else fn(*args, algo, None)
+    for fn, algo in ((f, None), (fp, 0)):
+        assert call(fn, algo, N=24) == ERR_SHAPE          # N % 16
+        assert call(fn, algo, N=0) == ERR_SHAPE
+        assert call(fn, algo, K=192) == ERR_SHAPE         # K % 128
+        assert call(fn, algo, E=0) == ERR_SHAPE
+        assert call(fn, algo, E=2000) == ERR_SHAPE
+        assert call(fn, algo, M=-1) == ERR_SHAPE
+        assert call(fn, algo, w=None) == ERR_NULL
+        assert call(fn, algo, off=None) == ERR_NULL
+        assert call(fn, algo, a=P + 8) == ERR_ALIGN
+        assert call(fn, algo, w=P + 4) == ERR_ALIGN
+        assert call(fn, algo, out=P + 4) == ERR_ALIGN
+        assert call(fn, algo, M=0, a=None, w=None) == OK  # no rows: no-op
+    assert call(fp, 0, N=96) == ERR_SHAPE                 # the GEMM storage needs N % 64
+    assert call(fp, 7) == ERR_SHAPE                       # unknown algo
+    assert call(f, None, N=48, M=0, a=None, w=None) == OK  # stored weights: N % 16 is enough
 
 
 def test_swiglu_unpermute_checks(L):
@@ -180,19 +184,21 @@ def test_int8_variant_checks(L):
     assert q(P, 4, 256, 256, P, P, None, None) == ERR_NULL          # row sums are required
     assert q(P + 8, 4, 256, 256, P, P, P, None) == ERR_ALIGN
     assert q(None, 0, 256, 256, None, None, None, None) == OK
-    g = L.w4a8_moe_grouped_gemm_i8
-    good = dict(a=P, sa=P, rs=P, rows=None, M=64, off=P, E=8, w=P, ws=P, N=256, K=256, out=P, algo=0)
+    good = dict(a=P, sa=P, rs=P, rows=None, M=64, off=P, E=8, w=P, ws=P, N=256, K=256, out=P)
 
-    def call(**kw):
+    def call(fn, algo=None, **kw):
         d = dict(good, **kw)
-        return g(d["a"], d["sa"], d["rs"], d["rows"], d["M"], d["off"], d["E"], d["w"], d["ws"], d["N"], d["K"],
-                 d["out"], d["algo"], None)
-    assert call(K=(1 << 20) + 128) == ERR_SHAPE                  # int32 sums could overflow
-    assert call(N=96) == ERR_SHAPE
-    assert call(algo=3) == ERR_SHAPE
-    assert call(rs=None) == ERR_NULL
-    assert call(rows=P + 2) == ERR_ALIGN
-    assert call(M=0, a=None, rs=None) == OK
+        args = (d["a"], d["sa"], d["rs"], d["rows"], d["M"], d["off"], d["E"], d["w"], d["ws"], d["N"], d["K"],
+                d["out"])
+        return fn(*args, None) if algo is None else fn(*args, algo, None)
+    for fn, algo in ((L.w4a8_moe_grouped_gemm_i8, None), (L.w4a8_moe_grouped_gemm_i8_prepacked, 0)):
+        assert call(fn, algo, K=(1 << 20) + 128) == ERR_SHAPE    # int32 sums could overflow
+        assert call(fn, algo, N=24) == ERR_SHAPE
+        assert call(fn, algo, rs=None) == ERR_NULL
+        assert call(fn, algo, rows=P + 2) == ERR_ALIGN
+        assert call(fn, algo, M=0, a=None, rs=None) == OK
+    assert call(L.w4a8_moe_grouped_gemm_i8_prepacked, 0, N=96) == ERR_SHAPE
+    assert call(L.w4a8_moe_grouped_gemm_i8_prepacked, 3) == ERR_SHAPE
     s = L.w4a8_moe_swiglu_i8
     assert s(P, 4, 100, P, P, P, None) == ERR_SHAPE
     assert s(P, 4, 128, P, P, None, None) == ERR_NULL
@@ -206,25 +212,31 @@ def test_int8_variant_checks(L):
 
 
 def test_fused_epilogue_checks(L):
-    f = L.w4a8_moe_grouped_gemm_swiglu
-    good = dict(a=P, sa=P, rows=None, M=64, off=P, E=8, w=P, s=P, I=128, K=256, act=P, pm=P, algo=0)
+    good = dict(a=P, sa=P, rows=None, M=64, off=P, E=8, w=P, s=P, I=128, K=256, act=P, pm=P)
 
-    def call(fn, **kw):
+    def call(fn, algo=None, **kw):
         d = dict(good, **kw)
-        return fn(d["a"], d["sa"], d["rows"], d["M"], d["off"], d["E"], d["w"], d["s"], d["I"], d["K"], d["act"],
-                  d["pm"], d["algo"], None)
-    for fn in (f, L.w4a8_moe_grouped_gemm_swiglu_mxfp4):
-        assert call(fn, I=64) == ERR_SHAPE                       # I % 128
-        assert call(fn, K=100) == ERR_SHAPE
-        assert call(fn, E=0) == ERR_SHAPE
-        assert call(fn, algo=5) == ERR_SHAPE
-        assert call(fn, pm=None) == ERR_NULL
-        assert call(fn, act=P + 4) == ERR_ALIGN                  # act 16-byte
-        assert call(fn, pm=P + 2) == ERR_ALIGN
-        assert call(fn, M=0, a=None, w=None, act=None, pm=None) == OK
+        args = (d["a"], d["sa"], d["rows"], d["M"], d["off"], d["E"], d["w"], d["s"], d["I"], d["K"], d["act"],
+                d["pm"])
+        return fn(*args, None) if algo is None else fn(*args, algo, None)
+    for fn, algo in ((L.w4a8_moe_grouped_gemm_swiglu, None), (L.w4a8_moe_grouped_gemm_swiglu_mxfp4, None),
+                     (L.w4a8_moe_grouped_gemm_swiglu_prepacked, 0),
+                     (L.w4a8_moe_grouped_gemm_swiglu_mxfp4_prepacked, 0)):
+        assert call(fn, algo, I=64) == ERR_SHAPE                       # I % 128
+        assert call(fn, algo, K=100) == ERR_SHAPE
+        assert call(fn, algo, E=0) == ERR_SHAPE
+        assert call(fn, algo, pm=None) == ERR_NULL
+        assert call(fn, algo, act=P + 4) == ERR_ALIGN                  # act 16-byte
+        assert call(fn, algo, pm=P + 2) == ERR_ALIGN
+        assert call(fn, algo, M=0, a=None, w=None, act=None, pm=None) == OK
+        if algo is not None:
+            assert call(fn, 5) == ERR_SHAPE
     g = L.w4a8_moe_grouped_gemm_swiglu_i8
-    assert g(P, P, None, None, 64, P, 8, P, P, 128, 256, P, P, 0, None) == ERR_NULL      # row sums
-    assert g(P, P, P, None, 64, P, 8, P, P, 128, (1 << 20) + 128, P, P, 0, None) == ERR_SHAPE
+    assert g(P, P, None, None, 64, P, 8, P, P, 128, 256, P, P, None) == ERR_NULL      # row sums
+    assert g(P, P, P, None, 64, P, 8, P, P, 128, (1 << 20) + 128, P, P, None) == ERR_SHAPE
+    gp = L.w4a8_moe_grouped_gemm_swiglu_i8_prepacked
+    assert gp(P, P, None, None, 64, P, 8, P, P, 128, 256, P, P, 0, None) == ERR_NULL
+    assert gp(P, P, P, None, 64, P, 8, P, P, 128, 256, P, P, 4, None) == ERR_SHAPE
     r = L.w4a8_moe_requant
     assert r(P, P, 4, 100, P, P, None) == ERR_SHAPE
     assert r(P, None, 4, 128, P, P, None) == ERR_NULL
@@ -257,30 +269,43 @@ def test_prepack_and_mxfp4_checks(L):
     assert qm(P, 4, 64, P + 1, P, None) == ERR_ALIGN               # codes 2-byte
     assert qm(None, 0, 64, None, None, None) == OK
     gm = L.w4a8_moe_grouped_gemm_mxfp4
-    assert gm(P, P, None, 64, P, 8, P, P, 96, 256, P, 0, None) == ERR_SHAPE      # N % 64
-    assert gm(P, P, None, 64, P, 8, P, P, 256, 192, P, 0, None) == ERR_SHAPE     # K % 128
-    assert gm(P, P, None, 64, P, 8, P, P, 256, 256, P, 9, None) == ERR_SHAPE     # algo
-    assert gm(P, P, None, 64, P, 8, P, None, 256, 256, P, 0, None) == ERR_NULL
-    assert gm(P, P, None, 64, P, 8, P + 8, P, 256, 256, P, 0, None) == ERR_ALIGN
-    assert gm(None, None, None, 0, None, 8, None, None, 256, 256, None, 0, None) == OK
+    assert gm(P, P, None, 64, P, 8, P, P, 24, 256, P, None) == ERR_SHAPE         # N % 16
+    assert gm(P, P, None, 64, P, 8, P, P, 256, 192, P, None) == ERR_SHAPE        # K % 128
+    assert gm(P, P, None, 64, P, 8, P, None, 256, 256, P, None) == ERR_NULL
+    assert gm(P, P, None, 64, P, 8, P + 8, P, 256, 256, P, None) == ERR_ALIGN
+    assert gm(None, None, None, 0, None, 8, None, None, 256, 256, None, None) == OK
+    gmp = L.w4a8_moe_grouped_gemm_mxfp4_prepacked
+    assert gmp(P, P, None, 64, P, 8, P, P, 96, 256, P, 0, None) == ERR_SHAPE     # N % 64
+    assert gmp(P, P, None, 64, P, 8, P, P, 256, 256, P, 9, None) == ERR_SHAPE    # algo
+    assert gmp(P, P, None, 64, P, 8, P, None, 256, 256, P, 0, None) == ERR_NULL
+    assert gmp(None, None, None, 0, None, 8, None, None, 256, 256, None, 0, None) == OK
 
 
 def test_later_calls_report_missing_device(L, no_device):
     if not no_device:
         pytest.skip("a supported GPU is present; these fake pointers must not reach it")
     assert L.w4a8_moe_quant_act_i8(P, 4, 256, 256, P, P, P, None) == ERR_DEVICE
-    assert L.w4a8_moe_grouped_gemm_i8(P, P, P, None, 8, P, 8, P, P, 256, 256, P, 0, None) == ERR_DEVICE
+    assert L.w4a8_moe_grouped_gemm_i8(P, P, P, None, 8, P, 8, P, P, 256, 256, P, None) == ERR_DEVICE
+    assert L.w4a8_moe_grouped_gemm_i8_prepacked(P, P, P, None, 8, P, 8, P, P, 256, 256, P, 0, None) == ERR_DEVICE
+    assert L.w4a8_moe_grouped_gemm_prepacked(P, P, None, 8, P, 8, P, P, 256, 256, P, 0, None) == ERR_DEVICE
+    assert L.w4a8_moe_grouped_gemm(P, P, None, 8, P, 8, P, P, 48, 256, P, None) == ERR_DEVICE
     assert L.w4a8_moe_swiglu_i8(P, 4, 128, P, P, P, None) == ERR_DEVICE
     assert L.w4a8_moe_quantize_weights_channel(P, 4, 128, P, P, None) == ERR_DEVICE
-    assert L.w4a8_moe_grouped_gemm_swiglu(P, P, None, 8, P, 8, P, P, 128, 256, P, P, 0, None) == ERR_DEVICE
-    assert L.w4a8_moe_grouped_gemm_swiglu_i8(P, P, P, None, 8, P, 8, P, P, 128, 256, P, P, 0, None) == ERR_DEVICE
+    assert L.w4a8_moe_grouped_gemm_swiglu(P, P, None, 8, P, 8, P, P, 128, 256, P, P, None) == ERR_DEVICE
+    assert L.w4a8_moe_grouped_gemm_swiglu_prepacked(P, P, None, 8, P, 8, P, P, 128, 256, P, P, 0, None) == ERR_DEVICE
+    assert L.w4a8_moe_grouped_gemm_swiglu_i8(P, P, P, None, 8, P, 8, P, P, 128, 256, P, P, None) == ERR_DEVICE
+    assert L.w4a8_moe_grouped_gemm_swiglu_i8_prepacked(P, P, P, None, 8, P, 8, P, P, 128, 256, P, P, 0,
+                                                       None) == ERR_DEVICE
     assert L.w4a8_moe_requant(P, P, 4, 128, P, P, None) == ERR_DEVICE
     assert L.w4a8_moe_requant_i8(P, P, 4, 128, P, P, P, None) == ERR_DEVICE
     assert L.w4a8_moe_quantize_weights_mxfp4(P, 4, 64, P, P, None) == ERR_DEVICE
     assert L.w4a8_moe_prepack_int4(P, P, 2, 32, 256, P, P, None) == ERR_DEVICE
     assert L.w4a8_moe_prepack_mxfp4(P, P, 2, 32, 256, P, P, None) == ERR_DEVICE
-    assert L.w4a8_moe_grouped_gemm_mxfp4(P, P, None, 8, P, 8, P, P, 256, 256, P, 0, None) == ERR_DEVICE
-    assert L.w4a8_moe_grouped_gemm_swiglu_mxfp4(P, P, None, 8, P, 8, P, P, 128, 256, P, P, 0, None) == ERR_DEVICE
+    assert L.w4a8_moe_grouped_gemm_mxfp4(P, P, None, 8, P, 8, P, P, 256, 256, P, None) == ERR_DEVICE
+    assert L.w4a8_moe_grouped_gemm_mxfp4_prepacked(P, P, None, 8, P, 8, P, P, 256, 256, P, 0, None) == ERR_DEVICE
+    assert L.w4a8_moe_grouped_gemm_swiglu_mxfp4(P, P, None, 8, P, 8, P, P, 128, 256, P, P, None) == ERR_DEVICE
+    assert L.w4a8_moe_grouped_gemm_swiglu_mxfp4_prepacked(P, P, None, 8, P, 8, P, P, 128, 256, P, P, 0,
+                                                          None) == ERR_DEVICE
 
 
 def test_front_checks(L, no_device):

@@ -69,7 +69,7 @@ def _problem(rng, E, N, K, counts, gather):
 
 def _gemm(codes, scale, rowsum, rows, offsets, words, ws, algo):
     R = int(offsets[-1])
-    out = ops.w4a8_moe_grouped_gemm_i8(to_dev(codes), to_dev(scale), to_dev(rowsum),
+    out = ops.w4a8_moe_grouped_gemm_i8_prepacked(to_dev(codes), to_dev(scale), to_dev(rowsum),
                                        to_dev(rows) if rows is not None else None, to_dev(offsets),
                                        prepack_int4(words)[0], to_dev(ws), M_total=R, algo=algo)
     return host(out)
@@ -106,7 +106,7 @@ def test_grouped_gemm_swiglu_i8(E, I, K, counts, gather, algo, rng):
     R = int(offsets[-1])
     want = oracle.swiglu_f32(oracle.grouped_gemm_i8(codes, scale, rows, offsets, words, ws))
     say(f"grouped_gemm_swiglu_i8 E={E} I={I} K={K} counts={counts} algo={algo}")
-    act, pmax = ops.w4a8_moe_grouped_gemm_swiglu_i8(
+    act, pmax = ops.w4a8_moe_grouped_gemm_swiglu_i8_prepacked(
         to_dev(codes), to_dev(scale), to_dev(rowsum), to_dev(rows) if rows is not None else None, to_dev(offsets),
         prepack_int4(words)[0], to_dev(ws), R, algo=algo)
     act, pmax = host(act), host(pmax)

@@ -135,7 +135,7 @@ def test_sampled_rows_per_call(index):
     # the unfused gate/up GEMM on the sampled rows, both kernels
     for algo in (ops.W4A8_GG_STREAM, ops.W4A8_GG_TILED):
         say(f"config {index}: gate/up GEMM on {P.size} rows algo={algo}")
-        gh = ops.w4a8_moe_grouped_gemm(to_dev(qx), to_dev(sx), None, to_dev(sub_off), moe.w13, moe.s13, P.size,
+        gh = ops.w4a8_moe_grouped_gemm_prepacked(to_dev(qx), to_dev(sx), None, to_dev(sub_off), moe.w13, moe.s13, P.size,
                                        algo=algo)
         assert_float_parity(host(gh), h, f"config {index} gate/up algo={algo}", fro_tight=GEMM_FRO_TIGHT)
     # SwiGLU on the oracle's h
@@ -149,6 +149,6 @@ def test_sampled_rows_per_call(index):
     o = oracle.grouped_gemm(qa, sa, None, sub_off, wl.w2, wl.s2)
     for algo in (ops.W4A8_GG_STREAM, ops.W4A8_GG_TILED):
         say(f"config {index}: down GEMM on {P.size} oracle rows algo={algo}")
-        go = ops.w4a8_moe_grouped_gemm(to_dev(qa), to_dev(sa), None, to_dev(sub_off), moe.w2, moe.s2, P.size,
+        go = ops.w4a8_moe_grouped_gemm_prepacked(to_dev(qa), to_dev(sa), None, to_dev(sub_off), moe.w2, moe.s2, P.size,
                                        algo=algo)
         assert_float_parity(host(go), o, f"config {index} down algo={algo}", fro_tight=GEMM_FRO_TIGHT)

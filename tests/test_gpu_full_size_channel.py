@@ -99,6 +99,6 @@ def test_channel_sampled_rows_per_call(index):
     o = oracle.grouped_gemm_i8(qa, sa, None, sub_off, wl.w2, s2)
     for algo in (ops.W4A8_GG_STREAM, ops.W4A8_GG_TILED):
         say(f"config {index}: per-channel down GEMM on {P.size} oracle rows algo={algo}")
-        go = ops.w4a8_moe_grouped_gemm_i8(to_dev(qa), to_dev(sa), to_dev(ra), None, to_dev(sub_off), moe.w2, moe.s2,
+        go = ops.w4a8_moe_grouped_gemm_i8_prepacked(to_dev(qa), to_dev(sa), to_dev(ra), None, to_dev(sub_off), moe.w2, moe.s2,
                                           M_total=P.size, algo=algo)
         assert_float_parity(host(go), o, f"config {index} per-channel down algo={algo}", fro_tight=GEMM_FRO_TIGHT)

@@ -104,6 +104,6 @@ def test_mxfp4_sampled_rows_per_call(index):
     o = mx.grouped_gemm_mxfp4(qa, sa, None, sub_off, w2, s2)
     for algo in (ops.W4A8_GG_STREAM, ops.W4A8_GG_TILED):
         say(f"config {index}: MXFP4 down GEMM on {P.size} oracle rows algo={algo}")
-        go = ops.w4a8_moe_grouped_gemm_mxfp4(to_dev(qa), to_dev(sa), None, to_dev(sub_off), moe.w2, moe.s2, P.size,
+        go = ops.w4a8_moe_grouped_gemm_mxfp4_prepacked(to_dev(qa), to_dev(sa), None, to_dev(sub_off), moe.w2, moe.s2, P.size,
                                               algo=algo)
         assert_float_parity(host(go), o, f"config {index} MXFP4 down algo={algo}", fro_tight=GEMM_FRO_TIGHT)

@@ -85,7 +85,7 @@ def _problem(rng, E, N, K, counts, src_rows=None, scale_lo=118, scale_hi=136):
 def _gemm(w, s, offsets, a, sa, rows, algo):
     M = int(offsets[-1])
     wb, sb = _prepacked(w, s)
-    out = ops.w4a8_moe_grouped_gemm_mxfp4(to_dev(a), to_dev(sa), None if rows is None else to_dev(rows),
+    out = ops.w4a8_moe_grouped_gemm_mxfp4_prepacked(to_dev(a), to_dev(sa), None if rows is None else to_dev(rows),
                                           to_dev(offsets), wb, sb, M, algo=algo)
     return host(out)
 
@@ -140,7 +140,7 @@ def test_grouped_gemm_swiglu_mxfp4(E, I, K, counts, gather, algo, rng):
     want = oracle.swiglu_f32(mx.grouped_gemm_mxfp4(a, sa, rows, offsets, w, s))
     say(f"grouped_gemm_swiglu_mxfp4 E={E} I={I} K={K} counts={counts} algo={algo}")
     wb, sb = _prepacked(w, s)
-    act, pmax = ops.w4a8_moe_grouped_gemm_swiglu_mxfp4(to_dev(a), to_dev(sa), None if rows is None else to_dev(rows),
+    act, pmax = ops.w4a8_moe_grouped_gemm_swiglu_mxfp4_prepacked(to_dev(a), to_dev(sa), None if rows is None else to_dev(rows),
                                                        to_dev(offsets), wb, sb, M, algo=algo)
     act, pmax = host(act), host(pmax)
     assert_float_parity(act, want, "grouped_gemm_swiglu_mxfp4", fro_tight=GEMM_FRO_TIGHT, maxrel=edge_shape_maxrel(I))
@@ -149,7 +149,7 @@ def test_grouped_gemm_swiglu_mxfp4(E, I, K, counts, gather, algo, rng):
     assert np.array_equal(pmax.max(axis=1), row)
     assert np.all(pmax <= row[:, None])
     # the fused path's codes against the unfused one's on the same inputs
-    out = ops.w4a8_moe_grouped_gemm_mxfp4(to_dev(a), to_dev(sa), None if rows is None else to_dev(rows),
+    out = ops.w4a8_moe_grouped_gemm_mxfp4_prepacked(to_dev(a), to_dev(sa), None if rows is None else to_dev(rows),
                                           to_dev(offsets), wb, sb, M, algo=algo)
     q_ref, s_ref = ops.w4a8_moe_swiglu(out)
     q, sq = ops.w4a8_moe_requant(to_dev(act), to_dev(pmax))

@@ -180,7 +180,7 @@ def test_grouped_gemm(E, N, K, counts, gather, algo, rng):
     want = oracle.grouped_gemm(a, sa, rows, offsets, w, s)
     M = int(offsets[-1])
     say(f"grouped_gemm E={E} N={N} K={K} counts={counts} gather={gather} algo={algo}")
-    out = ops.w4a8_moe_grouped_gemm(to_dev(a), to_dev(sa), None if rows is None else to_dev(rows), to_dev(offsets),
+    out = ops.w4a8_moe_grouped_gemm_prepacked(to_dev(a), to_dev(sa), None if rows is None else to_dev(rows), to_dev(offsets),
                                     *prepack_int4(w, s), M, algo=algo)
     assert_float_parity(host(out), want, "grouped_gemm", fro_tight=GEMM_FRO_TIGHT, maxrel=edge_shape_maxrel(N))
 
@@ -197,7 +197,7 @@ def test_grouped_gemm_exact_integers(algo, rng):
     offsets = np.array([0, 10, M], np.int32)
     want = oracle.grouped_gemm(codes, np.ones(M, np.float32), None, offsets, w, s)
     say(f"grouped_gemm exact integers algo={algo}")
-    out = ops.w4a8_moe_grouped_gemm(to_dev(codes), to_dev(np.ones(M, np.float32)), None, to_dev(offsets),
+    out = ops.w4a8_moe_grouped_gemm_prepacked(to_dev(codes), to_dev(np.ones(M, np.float32)), None, to_dev(offsets),
                                     *prepack_int4(w, s), M, algo=algo)
     assert np.array_equal(host(out), want)
 
@@ -231,13 +231,13 @@ def test_grouped_gemm_swiglu(E, I, K, counts, gather, algo, rng):
     M = int(offsets[-1])
     say(f"grouped_gemm_swiglu E={E} I={I} K={K} counts={counts} gather={gather} algo={algo}")
     wb, sb = prepack_int4(w, s)
-    act, pmax = ops.w4a8_moe_grouped_gemm_swiglu(to_dev(a), to_dev(sa), None if rows is None else to_dev(rows),
+    act, pmax = ops.w4a8_moe_grouped_gemm_swiglu_prepacked(to_dev(a), to_dev(sa), None if rows is None else to_dev(rows),
                                                  to_dev(offsets), wb, sb, M, algo=algo)
     act, pmax = host(act), host(pmax)
     assert_float_parity(act, want, "grouped_gemm_swiglu", fro_tight=GEMM_FRO_TIGHT, maxrel=edge_shape_maxrel(I))
     _check_pmax(pmax, act)
     # the codes of the fused path against the unfused one on the same inputs
-    out = ops.w4a8_moe_grouped_gemm(to_dev(a), to_dev(sa), None if rows is None else to_dev(rows), to_dev(offsets),
+    out = ops.w4a8_moe_grouped_gemm_prepacked(to_dev(a), to_dev(sa), None if rows is None else to_dev(rows), to_dev(offsets),
                                     wb, sb, M, algo=algo)
     q_ref, s_ref = ops.w4a8_moe_swiglu(out)
     q, sq = ops.w4a8_moe_requant(to_dev(act), to_dev(pmax))
