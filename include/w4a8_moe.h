@@ -131,6 +131,22 @@ int w4a8_moe_permute(const int32_t* ids, int64_t T, int32_t k, int32_t E,
                      void* workspace, int64_t workspace_bytes, void* stream);
 
 /*
+ * w4a8_moe_permute without a workspace, for callers that cannot allocate
+ * device memory (code under HIP graph capture, serving loops that forbid
+ * hipMalloc): the sort's per-(expert, block) counts go to a buffer of 1 MiB
+ * that the library holds on each GPU until the process ends, and nothing is
+ * allocated.  Same arguments (minus the workspace), results and rules as
+ * w4a8_moe_permute, and:
+ *   - sizes that need more than 1 MiB (w4a8_moe_permute_workspace_bytes(T, k,
+ *     E) > 1048576, e.g. T*k above 1,048,576 routed rows at E = 256) return
+ *     W4A8_ERR_WORKSPACE and launch nothing;
+ *   - every call on one GPU shares that GPU's buffer: calls that overlap on
+ *     one GPU (several streams or host threads) race and must not be made.
+ */
+int w4a8_moe_permute_noalloc(const int32_t* ids, int64_t T, int32_t k, int32_t E,
+                             int32_t* offsets, int32_t* row_token, int32_t* inv_pos, void* stream);
+
+/*
  * Steps 1, 2 and 3 in one call: w4a8_moe_quant_act, w4a8_moe_route and
  * w4a8_moe_permute on the same arguments, with the same results.  For decode
  * batches (T*k <= 4096 and H <= 8192) they run as one kernel: the quantizer

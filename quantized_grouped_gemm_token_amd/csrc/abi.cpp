@@ -149,6 +149,32 @@ int w4a8_moe_permute(const int32_t* ids, int64_t T, int32_t k, int32_t E, int32_
                   "permute");
 }
 
+int w4a8_moe_permute_noalloc(const int32_t* ids, int64_t T, int32_t k, int32_t E, int32_t* offsets,
+                             int32_t* row_token, int32_t* inv_pos, void* stream) {
+  if (T < 0) return fail(W4A8_ERR_SHAPE, "permute_noalloc: T=%lld < 0", (long long)T);
+  if (E < 1 || E > 1024 || k < 1 || k > E)
+    return fail(W4A8_ERR_SHAPE, "permute_noalloc: need 1 <= k <= E <= 1024 (k=%d, E=%d)", k, E);
+  if (T * (int64_t)k >= kMaxRows) return fail(W4A8_ERR_SHAPE, "permute_noalloc: T*k must be < 2^31");
+  const int64_t need = w4a8::permute_workspace_bytes(T * (int64_t)k, E);
+  if (need > w4a8::kPermScratchBytes)
+    return fail(W4A8_ERR_WORKSPACE, "permute_noalloc: T=%lld, k=%d, E=%d need %lld bytes of scratch; the library "
+                "holds %lld (use w4a8_moe_permute with a workspace)", (long long)T, k, E, (long long)need,
+                (long long)w4a8::kPermScratchBytes);
+  if (!offsets) return fail(W4A8_ERR_NULL, "permute_noalloc: null offsets");
+  if (T > 0 && (!ids || !row_token || !inv_pos)) return fail(W4A8_ERR_NULL, "permute_noalloc: null pointer");
+  if (!aligned(ids, 4) || !aligned(offsets, 4) || !aligned(row_token, 4) || !aligned(inv_pos, 4))
+    return fail(W4A8_ERR_ALIGN, "permute_noalloc: arrays must be 4-byte aligned");
+  if (int st = check_device()) return st;
+  int32_t* scratch = nullptr;
+  if (hipError_t e = w4a8::permute_scratch(&scratch); e != hipSuccess)
+    return fail(W4A8_ERR_HIP, "permute_noalloc: no address for the library's scratch buffer (%s)",
+                hipGetErrorString(e));
+  (void)hipGetLastError();
+  return launched(w4a8::launch_permute(ids, T * (int64_t)k, k, E, offsets, row_token, inv_pos, scratch,
+                                       as_stream(stream)),
+                  "permute_noalloc");
+}
+
 // steps 1-3: the rules of w4a8_moe_quant_act[_i8], w4a8_moe_route and w4a8_moe_permute together
 static int run_front(const char* name, const uint16_t* x, int64_t T, int64_t H, int64_t ld_x, void* qx, float* sx,
                      int32_t* rowsum, bool int8, const float* logits, int32_t E, int32_t k, int32_t renormalize,

@@ -47,6 +47,10 @@ hipError_t launch_quant_act(const uint16_t* x, int64_t T, int64_t H, int64_t ld,
 hipError_t launch_route(const float* logits, int64_t T, int E, int k, int renormalize, int32_t* ids, float* w,
                         hipStream_t stream);
 int64_t permute_workspace_bytes(int64_t R, int E);
+// bytes of the buffer w4a8_moe_permute_noalloc uses in place of the workspace
+constexpr int64_t kPermScratchBytes = (int64_t)1 << 20;
+// the device address of that buffer on the current device (looked up once per device)
+hipError_t permute_scratch(int32_t** ptr);
 hipError_t launch_permute(const int32_t* ids, int64_t R, int k, int E, int32_t* offsets, int32_t* row_token,
                           int32_t* inv_pos, int32_t* counts, hipStream_t stream);
 hipError_t launch_gg_stream(const GemmArgs& g, hipStream_t stream);

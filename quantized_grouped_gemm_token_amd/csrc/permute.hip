@@ -21,6 +21,8 @@
 #include "kernels.hpp"
 #include "permute_small.hpp"
 
+#include <atomic>
+
 namespace w4a8 {
 
 __global__ __launch_bounds__(kPermThreads) void permute_count_kernel(const int32_t* __restrict__ ids, int64_t R,
@@ -105,6 +107,33 @@ __global__ __launch_bounds__(kPermThreads) void permute_small_kernel(const int32
 int64_t permute_workspace_bytes(int64_t R, int E) {
   const int64_t nblk = (R + kPermBlock - 1) / kPermBlock;
   return (nblk > 0 ? nblk : 1) * (int64_t)E * (int64_t)sizeof(int32_t);
+}
+
+// ---- the workspace of w4a8_moe_permute_noalloc, for callers that cannot
+// allocate device memory: a buffer the library holds on each GPU until the
+// process ends.  In host code `scratch` names a host-side stand-in, not the
+// device buffer: kernels and copies get its device address from
+// permute_scratch(), taken once per device with hipGetSymbolAddress.
+static __device__ __align__(256) int32_t scratch[kPermScratchBytes / sizeof(int32_t)];
+
+namespace {
+constexpr int kScratchDevices = 64;
+std::atomic<int32_t*> g_scratch_ptr[kScratchDevices];
+}  // namespace
+
+hipError_t permute_scratch(int32_t** ptr) {
+  int dev = -1;
+  if (hipError_t e = hipGetDevice(&dev); e != hipSuccess) return e;
+  if (dev < 0 || dev >= kScratchDevices) return hipErrorInvalidDevice;
+  int32_t* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    void* addr = nullptr;
+    if (hipError_t e = hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch)); e != hipSuccess) return e;
+    p = static_cast<int32_t*>(addr);
+    g_scratch_ptr[dev].store(p, std::memory_order_release);
+  }
+  *ptr = p;
+  return hipSuccess;
 }
 
 hipError_t launch_permute(const int32_t* ids, int64_t R, int k, int E, int32_t* offsets, int32_t* row_token,

@@ -44,6 +44,7 @@ _SIGNATURES = {
     "w4a8_moe_quantize_weights_mxfp4": (ctypes.c_int, [_c_p, _i64, _i64, _c_p, _c_p, _c_p]),
     "w4a8_moe_prepack_int4": (ctypes.c_int, [_c_p, _c_p, _i32, _i64, _i64, _c_p, _c_p, _c_p]),
     "w4a8_moe_prepack_mxfp4": (ctypes.c_int, [_c_p, _c_p, _i32, _i64, _i64, _c_p, _c_p, _c_p]),
+    "w4a8_moe_permute_noalloc": (ctypes.c_int, [_c_p, _i64, _i32, _i32, _c_p, _c_p, _c_p, _c_p]),
     "w4a8_moe_front": (ctypes.c_int, [_c_p, _i64, _i64, _i64, _c_p, _c_p, _c_p, _i32, _i32, _i32, _c_p, _c_p, _c_p,
                                       _c_p, _c_p, _c_p, _i64, _c_p, _c_p]),
     "w4a8_moe_front_i8": (ctypes.c_int, [_c_p, _i64, _i64, _i64, _c_p, _c_p, _c_p, _c_p, _i32, _i32, _i32, _c_p,
@@ -263,6 +264,25 @@ def w4a8_moe_permute(ids: torch.Tensor, E: int, offsets=None, row_token=None, in
         raise ValueError("offsets must be [E+1], row_token / inv_pos [T*k]")
     _check("w4a8_moe_permute", lib().w4a8_moe_permute(_p(ids), T, k, E, _p(offsets), _p(row_token), _p(inv_pos),
                                                       _p(workspace), workspace.numel(), _stream(dev)))
+    return offsets, row_token, inv_pos
+
+
+def w4a8_moe_permute_noalloc(ids: torch.Tensor, E: int, offsets=None, row_token=None, inv_pos=None):
+    """w4a8_moe_permute with its workspace in the library's own device buffer (no allocation by the
+    library; pass every output to allocate nothing here either) -> (offsets, row_token, inv_pos)."""
+    _need(ids, "ids", torch.int32, 2)
+    T, k = ids.shape
+    dev = ids.device
+    R = T * k
+    offsets = torch.empty((E + 1,), dtype=torch.int32, device=dev) if offsets is None else offsets
+    row_token = torch.empty((R,), dtype=torch.int32, device=dev) if row_token is None else row_token
+    inv_pos = torch.empty((R,), dtype=torch.int32, device=dev) if inv_pos is None else inv_pos
+    for t, n, size in ((offsets, "offsets", E + 1), (row_token, "row_token", R), (inv_pos, "inv_pos", R)):
+        _need(t, n, torch.int32, 1, dev)
+        if t.numel() != size:
+            raise ValueError(f"{n} must have {size} entries")
+    _check("w4a8_moe_permute_noalloc",
+           lib().w4a8_moe_permute_noalloc(_p(ids), T, k, E, _p(offsets), _p(row_token), _p(inv_pos), _stream(dev)))
     return offsets, row_token, inv_pos
 
 

@@ -91,6 +91,21 @@ def test_permute_checks(L):
     assert f(P, 128, 8, 256, P + 1, P, P, P, need, None) == ERR_ALIGN
 
 
+def test_permute_noalloc_checks(L, no_device):
+    f = L.w4a8_moe_permute_noalloc
+    assert f(P, 128, 9, 8, P, P, P, None) == ERR_SHAPE               # k > E
+    assert f(P, -1, 8, 256, P, P, P, None) == ERR_SHAPE
+    assert f(P, 128, 8, 256, None, P, P, None) == ERR_NULL
+    assert f(P, 128, 8, 256, P, None, P, None) == ERR_NULL
+    assert f(P, 128, 8, 256, P + 2, P, P, None) == ERR_ALIGN
+    # more than the library's 1 MiB of scratch: refused, whatever the pointers
+    assert L.w4a8_moe_permute_workspace_bytes(1 << 18, 8, 256) > (1 << 20)
+    assert f(P, 1 << 18, 8, 256, P, P, P, None) == ERR_WORKSPACE
+    assert "1048576" in ops.last_error()
+    if no_device:
+        assert f(P, 1 << 17, 8, 256, P, P, P, None) == ERR_DEVICE    # the largest size that fits
+
+
 def test_grouped_gemm_checks(L):
     f = L.w4a8_moe_grouped_gemm                    # weights as stored: N % 16
     fp = L.w4a8_moe_grouped_gemm_prepacked         # GEMM storage: N % 64, and an algo
