@@ -16,7 +16,7 @@
 //     group), and the 2^9 goes into the epilogue with the token scale.
 //
 // The only work per weight is splitting the nibbles of a word into bytes
-// (two ANDs, a shift and two byte permutes per 8 weights).
+// (in the GEMM storage's nibble order: two ANDs and a shift per 8 weights).
 #pragma once
 
 #include "common.hpp"

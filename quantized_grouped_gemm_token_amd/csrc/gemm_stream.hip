@@ -27,6 +27,10 @@
 // expert with no rows returns at once; one with more than 16 rows loops over
 // M blocks, re-streaming its weights (the tiled kernel is the one for many
 // rows per expert).
+//
+// The same kernel reads the weights in the row-major stored format too (the
+// grouped GEMM calls without "_prepacked"): the lane's operand of a group is
+// then 16 bytes of its own row, so a wave's load covers 64 bytes of 16 rows.
 #include "gemm_common.hpp"
 #include "kernels.hpp"
 
