@@ -24,8 +24,8 @@ Readings where the page is silent:
   * the product sums the integer codes exactly and applies the two scales
     once: out = a_scale[row] * w_scale[n] * sum_k a[k] q[n, k].
 
-Every integer sum here is exact (int64); scales are applied in fp64 and the
-result rounded once to fp32.
+Every integer sum here is exact (integers below 2^30, held exactly by fp64);
+scales are applied in fp64 and the result rounded once to fp32.
 """
 from __future__ import annotations
 
@@ -79,7 +79,8 @@ def grouped_gemm_i8(a_codes, a_scale, a_rows, offsets, w_packed, w_scale) -> np.
     r = a_rows[p] when a gather list is given, else p; e is the expert whose
     row range holds p.  a_codes [*, K] int8, a_scale [*] fp32, offsets [E+1],
     w_packed [E, N, K/8] int32 (uint4b8), w_scale [E, N] fp32.  The integer
-    sums are exact (int64); the scales are applied in fp64.
+    sums are exact (each partial sum an integer below 2^30); the scales are
+    applied in fp64.
     """
     offsets = np.asarray(offsets, dtype=np.int64)
     E = offsets.size - 1
@@ -93,10 +94,14 @@ def grouped_gemm_i8(a_codes, a_scale, a_rows, offsets, w_packed, w_scale) -> np.
         if r1 == r0:
             continue
         rows = np.asarray(a_rows[r0:r1]) if a_rows is not None else np.arange(r0, r1)
-        A = np.asarray(a_codes[rows], dtype=np.int64)
-        Q = int4_unpack(w_packed[e]).astype(np.int64)
+        # the integer sums, formed exactly: |a q| <= 127 * 8, so with K <= 2^20 every
+        # partial sum is an integer below 2^30, which fp64 holds exactly in any order
+        A = np.asarray(a_codes[rows], dtype=np.int8).astype(np.float64)
+        Q = int4_unpack(w_packed[e]).astype(np.float64)
+        if A.shape[1] > 1 << 20:
+            raise ValueError("K above 2^20: the integer sums would not be exact in fp64")
         acc = A @ Q.T
-        out[r0:r1] = (acc.astype(np.float64) * a_scale[rows].astype(np.float64)[:, None]
+        out[r0:r1] = (acc * a_scale[rows].astype(np.float64)[:, None]
                       * w_scale[e].astype(np.float64)[None, :]).astype(np.float32)
     return out
 

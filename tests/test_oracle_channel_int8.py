@@ -93,6 +93,25 @@ def test_grouped_gemm_i8_matches_dequantized_blas(rng):
         assert np.allclose(got[r0:r1], want, rtol=2 ** -23, atol=0)
 
 
+def test_grouped_gemm_i8_integer_sums_are_exact(rng):
+    # extreme codes (127 against -8 everywhere) at a long K: each sum is checked
+    # against Python integers, so no rounding anywhere can hide
+    K = 8192
+    codes = np.full((3, K), 127, np.int8)
+    codes[1] = -127
+    codes[2] = rng.integers(-127, 128, size=K).astype(np.int8)
+    q = np.full((1, 2, K), -8, np.int8)
+    q[0, 1] = rng.integers(-8, 8, size=K)
+    words = np.stack([oracle.int4_pack(q[0])])
+    got = oracle.grouped_gemm_i8(codes, np.ones(3, np.float32), None, np.array([0, 3]), words,
+                                 np.ones((1, 2), np.float32))
+    for r in range(3):
+        for n in range(2):
+            exact = sum(int(a) * int(b) for a, b in zip(codes[r].tolist(), q[0, n].tolist()))
+            assert got[r, n] == np.float32(exact)
+    assert got[0, 0] == np.float32(-127 * 8 * K)
+
+
 def test_grouped_gemm_i8_linear_in_scales_and_dense_case(rng):
     codes, scale, rows, offsets, q, words, ws = _problem(rng, 1, 32, 128, [7], gather=False)
     a = oracle.grouped_gemm_i8(codes, scale, None, offsets, words, ws)
