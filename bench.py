@@ -7,11 +7,14 @@ A step is one pass of the whole layer (quant_act, route, permute, gate/up
 grouped GEMM, SwiGLU, down grouped GEMM, combine) over one batch of
 synthetic tokens, inputs already resident in HBM.  The default workload is
 decode at 128 tokens (H=6144, I=2048, 256 experts, top-8), the shape the
-headline metric is quoted on; --config 3 runs the 8K-token prefill.
+headline value is quoted on; the same run then times the 8K-token prefill
+(the metric's other half) into a "prefill" block of the line (--no-prefill
+skips it; --config 3 makes the prefill the headline workload).
 
 Prints ONE JSON line: layer tokens/s, the roofline of the dominant kernel
-(the gate/up grouped GEMM, timed with events on its own stream), and the CPU
-oracle timed on a bounded sample of the same workload.
+(the gate/up grouped GEMM, timed with events on its own stream: HBM bytes at
+decode, FP8 MFMA FLOPs at prefill), and the CPU oracle timed on a bounded
+sample of the decode workload on every host core and on one.
 
 The step is timed twice over K steps: launched kernel by kernel with events
 around each kernel (the per-kernel times and the roofline's launch duration),
@@ -78,33 +81,39 @@ def workload_tag(shape) -> str:
     return shape.name.split()[0] + f"_T{shape.T}"
 
 
-def cpu_baseline(wl, n_tokens: int, scheme: str = "g128") -> dict:
-    """The oracle layer on the first n_tokens tokens (single thread)."""
+def _oracle_layer(wl, sel, scheme: str) -> dict:
+    """The oracle's whole layer on the tokens sel of the workload (the plain oracle, as it stands)."""
     import oracle
-    try:
-        from threadpoolctl import threadpool_limits
-        limit = threadpool_limits(limits=1)
-    except Exception:   # pragma: no cover - threadpoolctl is installed in this image
-        limit = None
-    sel = np.arange(n_tokens)
-    t0 = time.perf_counter()
+    from quantized_grouped_gemm_token_amd import workloads
     if scheme == "channel":
-        from quantized_grouped_gemm_token_amd import workloads
         s13c, s2c = workloads.channel_scales(wl)
-        res = oracle.moe_layer_i8(wl.x_bf16[sel], wl.logits[sel], wl.w13, s13c, wl.w2, s2c, k=wl.shape.k)
-    elif scheme == "mxfp4":
-        from quantized_grouped_gemm_token_amd import workloads
+        return oracle.moe_layer_i8(wl.x_bf16[sel], wl.logits[sel], wl.w13, s13c, wl.w2, s2c, k=wl.shape.k)
+    if scheme == "mxfp4":
         w13m, s13m, w2m, s2m = workloads.mxfp4_weights(wl)
-        res = oracle.moe_layer_mxfp4(wl.x_bf16[sel], wl.logits[sel], w13m, s13m, w2m, s2m, k=wl.shape.k)
-    else:
-        res = oracle.moe_layer(wl.x_bf16[sel], wl.logits[sel], wl.w13, wl.s13, wl.w2, wl.s2, k=wl.shape.k)
-    dt = time.perf_counter() - t0
-    if limit is not None:
-        limit.restore_original_limits()
+        return oracle.moe_layer_mxfp4(wl.x_bf16[sel], wl.logits[sel], w13m, s13m, w2m, s2m, k=wl.shape.k)
+    return oracle.moe_layer(wl.x_bf16[sel], wl.logits[sel], wl.w13, wl.s13, wl.w2, wl.s2, k=wl.shape.k)
+
+
+def cpu_baseline(wl, n_tokens: int, scheme: str = "g128") -> dict:
+    """The oracle layer on the first n_tokens tokens of the workload, timed on this host: with every
+    core for BLAS (the value), then with one thread."""
+    from threadpoolctl import threadpool_limits
+    sel = np.arange(n_tokens)
+    cores = os.cpu_count() or 1
+    runs = {}
+    for threads in (cores, 1):
+        with threadpool_limits(limits=threads):
+            t0 = time.perf_counter()
+            res = _oracle_layer(wl, sel, scheme)
+            runs[threads] = time.perf_counter() - t0
     touched = int((np.diff(res["offsets"]) > 0).sum())
-    return {"value": n_tokens / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"oracle layer (numpy, fp64 sums, 1 thread) on {n_tokens} of the {wl.shape.T} tokens of "
-                      f"'{wl.shape.name}', touching {touched} experts; {dt:.1f} s wall"}
+    sample = (f"the oracle's whole layer (numpy, fp64 sums; BLAS on {cores} threads, its per-expert "
+              f"dequantization single-threaded numpy) on {n_tokens} of the {wl.shape.T} tokens of "
+              f"'{wl.shape.name}', touching {touched} experts; {runs[cores]:.1f} s wall")
+    return {"value": round(n_tokens / runs[cores], 4), "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": sample,
+            "single_thread": {"value": round(n_tokens / runs[1], 4), "unit": "tokens/s", "cores": 1,
+                              "sample": f"the same {n_tokens} tokens with BLAS on 1 thread; {runs[1]:.1f} s wall"}}
 
 
 def bench_wquant_mxfp4(args, log) -> int:
@@ -229,7 +238,9 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=1, help="workload index: 1 decode T=128 (default), "
                                                           "2 decode T=256, 3 prefill T=8192, 4 skewed T=16384")
-    ap.add_argument("--cpu-tokens", type=int, default=16, help="tokens in the CPU oracle sample (0: skip)")
+    ap.add_argument("--cpu-tokens", type=int, default=32, help="tokens in the CPU oracle sample (0: skip)")
+    ap.add_argument("--no-prefill", action="store_true",
+                    help="with the default decode workload, skip the prefill T=8192 block of the line")
     ap.add_argument("--quiet", action="store_true")
     ap.add_argument("--scheme", choices=("g128", "channel", "mxfp4"), default="g128",
                     help="g128: INT4 group-128 x FP8 per token (default); channel: per-channel INT4 x INT8 per "
@@ -250,8 +261,7 @@ def main() -> int:
 
     import torch
 
-    from quantized_grouped_gemm_token_amd import ops, workloads
-    from quantized_grouped_gemm_token_amd.layer import W4A8MoE, W4A8MoEChannel, W4A8MoEMxfp4
+    from quantized_grouped_gemm_token_amd import ops
 
     log = (lambda *a: None) if args.quiet else (lambda *a: print("[bench]", *a, file=sys.stderr, flush=True))
     if args.copy_bytes:
@@ -274,9 +284,49 @@ def main() -> int:
         return 1
     if args.op == "wquant":
         return bench_wquant_mxfp4(args, log) if args.scheme == "mxfp4" else bench_wquant(args, log)
+    m = measure_layer(args.config, args, log)
+    line = {
+        "metric": METRIC, "value": round(m["shape"].T / (m["ms_step"] * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(m["ms_step"], 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None,
+        "dtype": {"channel": "int8 x int4 (int32 accumulate)", "mxfp4": "fp8e4m3 x mxfp4 e2m1 (fp32 accumulate)",
+                  "g128": "fp8e4m3 x int4 (fp32 accumulate)"}[args.scheme],
+        "data": "synthetic (seeded; uniform 4-bit codes, lognormal scales, N(0,1) bf16 activations)",
+        "config": m["config"], "roofline": m["roofline"], "cpu_baseline": None, "gemms": m["gemms"],
+        "step_ms": m["step_ms"], "launch": "eager" if args.no_graph else "hip graph replay",
+        "eager_ms_per_step": m["eager_ms"], "graph_ms_per_step": m["graph_ms"],
+        "device": m["device"], "kernel_sources_hash": m["roofline"]["kernel_sources_hash"],
+    }
+    wl = m.pop("wl")
+    del m
+    if args.config == 1 and not args.no_prefill:
+        # the prefill half of the metric: the 8K-token prompt, in the same run
+        p = measure_layer(3, args, log)
+        line["prefill"] = {
+            "workload": p["shape"].name, "tokens_per_s": round(p["shape"].T / (p["ms_step"] * 1e-3), 1),
+            "ms_per_step": round(p["ms_step"], 5), "launch": line["launch"], "roofline": p["roofline"],
+            "gemms": p["gemms"], "step_ms": p["step_ms"], "eager_ms_per_step": p["eager_ms"],
+            "graph_ms_per_step": p["graph_ms"]}
+        del p
+    if args.cpu_tokens > 0:
+        n = min(args.cpu_tokens, wl.shape.T)
+        log(f"CPU oracle on {n} tokens ({os.cpu_count()} BLAS threads, then 1) ...")
+        line["cpu_baseline"] = cpu_baseline(wl, n, args.scheme)
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+def measure_layer(index: int, args, log) -> dict:
+    """Time the layer on workload `index` (per-step kernel events, then graph replay) and price its
+    gate/up GEMM against its roofline."""
+    import torch
+
+    from quantized_grouped_gemm_token_amd import workloads
+    from quantized_grouped_gemm_token_amd.layer import W4A8MoE, W4A8MoEChannel, W4A8MoEMxfp4
+
     dev = "cuda:0"
     t0 = time.time()
-    wl = workloads.make_config(args.config)
+    wl = workloads.make_config(index)
     sh = wl.shape
     log(f"generated {sh.name} in {time.time() - t0:.1f} s")
     to = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)  # noqa: E731
@@ -298,7 +348,7 @@ def main() -> int:
     for _ in range(args.warmup):
         moe(x, logits, y)
     torch.cuda.synchronize()
-    log(f"warmup {args.warmup} done")
+    log(f"{sh.name}: warmup {args.warmup} done")
 
     steps = moe.steps
     evs = [{s: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for s in steps}
@@ -312,7 +362,7 @@ def main() -> int:
     torch.cuda.synchronize()
     eager_ms = start.elapsed_time(stop) / args.steps
     per_step = {s: float(np.mean([e[s][0].elapsed_time(e[s][1]) for e in evs])) for s in steps}
-    log("per step ms: " + ", ".join(f"{k}={v:.4f}" for k, v in per_step.items()))
+    log(f"{sh.name}: per step ms: " + ", ".join(f"{k}={v:.4f}" for k, v in per_step.items()))
 
     # the same step replayed from a HIP graph: W untimed replays, then exactly K timed ones
     graph = moe.capture(x, logits, y)
@@ -325,7 +375,7 @@ def main() -> int:
     stop.record(stream)
     torch.cuda.synchronize()
     graph_ms = start.elapsed_time(stop) / args.steps
-    log(f"step: eager {eager_ms:.4f} ms, graph replay {graph_ms:.4f} ms")
+    log(f"{sh.name}: step: eager {eager_ms:.4f} ms, graph replay {graph_ms:.4f} ms")
     ms_step = eager_ms if args.no_graph else graph_ms
 
     # algorithmic work of the routed experts actually touched
@@ -333,6 +383,7 @@ def main() -> int:
     counts = np.diff(offsets)
     touched = int((counts > 0).sum())
     R = sh.T * sh.k
+
     # packed 4-bit weights plus scales: fp32 per row (channel), fp32 per 128 (g128), one E8M0 byte per 32 (mxfp4)
     def scale_bytes(n_rows, k):
         return n_rows * (4 if channel else (k // 32 if mxfp4 else k // 128 * 4))
@@ -347,7 +398,7 @@ def main() -> int:
     down_flops = 2.0 * R * sh.H * sh.I
     t_gu = per_step["gemm_gate_up"] * 1e-3
     t_dn = per_step["gemm_down"] * 1e-3
-    decode = args.config in (0, 1, 2)
+    decode = index in (0, 1, 2)
     kernel = "gg_stream" if decode else "gg_tiled"
     khash = kernel_sources_hash(kernel)
     tag = workload_tag(sh) + ("" if args.scheme == "g128" else "_" + args.scheme)
@@ -365,38 +416,27 @@ def main() -> int:
     roof["algorithmic_bytes"] = int(gate_up_bytes)
     roof["algorithmic_flops"] = gate_up_flops
     roof["avg_launch_ms"] = round(per_step["gemm_gate_up"], 5)
+    roof["kernel_sources_hash"] = khash
 
     both_weight_bytes = touched * (w13_bytes + w2_bytes)
     gemms = {"weight_GBps": round(both_weight_bytes / (t_gu + t_dn) / 1e9, 1),
              "tflops": round((gate_up_flops + down_flops) / (t_gu + t_dn) / 1e12, 2),
              "hbm_frac_weights": round(both_weight_bytes / (t_gu + t_dn) / 1e9 / HBM_PEAK_GBS, 4),
              "mfma_frac": round((gate_up_flops + down_flops) / (t_gu + t_dn) / 1e12 / FP8_PEAK_TFLOPS, 4),
+             "down_mfma_frac": round(down_flops / t_dn / 1e12 / FP8_PEAK_TFLOPS, 4),
+             "down_weight_GBps": round(touched * w2_bytes / t_dn / 1e9, 1),
              "touched_experts": touched, "max_rows_per_expert": int(counts.max()),
              "empty_experts": int((counts == 0).sum())}
-
-    cpu = None
-    if args.cpu_tokens > 0:
-        log(f"CPU oracle on {args.cpu_tokens} tokens ...")
-        cpu = cpu_baseline(wl, min(args.cpu_tokens, sh.T), args.scheme)
-
-    line = {
-        "metric": METRIC, "value": round(sh.T / (ms_step * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 5), "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None,
-        "dtype": {"channel": "int8 x int4 (int32 accumulate)", "mxfp4": "fp8e4m3 x mxfp4 e2m1 (fp32 accumulate)",
-                  "g128": "fp8e4m3 x int4 (fp32 accumulate)"}[args.scheme],
-        "data": "synthetic (seeded; uniform 4-bit codes, lognormal scales, N(0,1) bf16 activations)",
-        "config": {"workload": sh.name, "tokens": sh.T, "hidden": sh.H, "intermediate": sh.I, "experts": sh.E,
-                   "top_k": sh.k, "scheme": {"channel": "per-channel int4 x per-token int8",
-                                             "mxfp4": "mxfp4 g32 x fp8", "g128": "int4 g128 x fp8"}[args.scheme]},
-        "roofline": roof, "cpu_baseline": cpu, "gemms": gemms,
-        "step_ms": {k: round(v, 5) for k, v in per_step.items()},
-        "launch": "eager" if args.no_graph else "hip graph replay",
-        "eager_ms_per_step": round(eager_ms, 5), "graph_ms_per_step": round(graph_ms, 5),
-        "device": torch.cuda.get_device_name(0), "kernel_sources_hash": khash,
-    }
-    print(json.dumps(line), flush=True)
-    return 0
+    config = {"workload": sh.name, "tokens": sh.T, "hidden": sh.H, "intermediate": sh.I, "experts": sh.E,
+              "top_k": sh.k, "scheme": {"channel": "per-channel int4 x per-token int8",
+                                        "mxfp4": "mxfp4 g32 x fp8", "g128": "int4 g128 x fp8"}[args.scheme]}
+    device = torch.cuda.get_device_name(0)
+    del graph, moe, x, logits, y
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return dict(wl=wl, shape=sh, ms_step=ms_step, eager_ms=round(eager_ms, 5), graph_ms=round(graph_ms, 5),
+                step_ms={k: round(v, 5) for k, v in per_step.items()}, roofline=roof, gemms=gemms, config=config,
+                device=device)
 
 
 if __name__ == "__main__":

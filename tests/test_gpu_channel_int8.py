@@ -11,7 +11,8 @@ import pytest
 import torch
 
 import oracle
-from gpu_util import assert_float_parity, bf16_to_dev, host, prepack_int4, say, to_dev
+from gpu_util import (assert_float_parity, bf16_to_dev, check_layer_output, check_requant, host, prepack_int4, say,
+                      to_dev)
 from quantized_grouped_gemm_token_amd import ops, workloads
 from quantized_grouped_gemm_token_amd.layer import W4A8MoEChannel
 
@@ -177,4 +178,13 @@ def test_layer_channel_int8(cfg, algo, fused):
     moe = W4A8MoEChannel(to_dev(wl.w13), to_dev(s13), to_dev(wl.w2), to_dev(s2), k=sh.k, fused=fused)
     y = host(moe(bf16_to_dev(wl.x_bf16), to_dev(wl.logits), algo=algo))
     ref = oracle.moe_layer_i8(wl.x_bf16, wl.logits, wl.w13, s13, wl.w2, s2, k=sh.k)
-    assert_float_parity(y, ref["y"], f"layer_i8 {sh.name}")
+    b = moe.buffers(sh.T)
+    act_gpu = host(b["act"]) if fused else oracle.swiglu_f32(host(b["h"]))
+    qa_gpu, sa_gpu = host(b["qa"]), host(b["sa"])
+    flipped = check_requant(act_gpu, qa_gpu, sa_gpu, ref["qa"], int8=True, act_exact=fused)
+    assert np.array_equal(host(b["ra"]), oracle.code_row_sums(qa_gpu))
+    token_flipped = flipped.any(axis=1)[ref["inv_pos"]].reshape(sh.T, sh.k).any(axis=1)
+    o_same = oracle.grouped_gemm_i8(qa_gpu, sa_gpu, None, ref["offsets"], wl.w2, s2)
+    y_same = oracle.unpermute(o_same, ref["inv_pos"], ref["w"])
+    r = check_layer_output(y, ref["y"], y_same, token_flipped, f"layer_i8 {sh.name}")
+    say(f"layer_i8 output vs oracle: {r}; {int(flipped.sum())} codes differ from the independent run")

@@ -12,8 +12,8 @@ import pytest
 import torch
 
 import oracle
-from gpu_util import (GEMM_FRO_TIGHT, assert_float_parity, bf16_to_dev, edge_shape_maxrel, host, near_midpoint,
-                      prepack_int4, say, to_dev, valid_code_choice)
+from gpu_util import (GEMM_FRO_TIGHT, assert_float_parity, bf16_to_dev, check_layer_output, check_requant,
+                      edge_shape_maxrel, host, near_midpoint, prepack_int4, say, to_dev)
 from quantized_grouped_gemm_token_amd import ops, workloads
 from quantized_grouped_gemm_token_amd.layer import W4A8MoE
 
@@ -320,17 +320,22 @@ def _layer_vs_oracle(wl, algo=ops.W4A8_GG_AUTO, y_dtype=torch.float32, fused=Tru
     yy = host(y)
     if y_dtype == torch.bfloat16:
         yy = oracle.bf16_bits_to_f32(yy)
-    # SwiGLU re-quantization: the GPU may round an activation lying at a
-    # midpoint the other way; check each such code is a valid rounding and
-    # compare the output with the oracle's result for that choice of codes
-    codes, flips = valid_code_choice(res["a_f32"], res["sa"], res["qa"], host(b["qa"]))
-    assert flips <= max(2, 1e-2 * codes.size), flips
-    o_ref = oracle.grouped_gemm(codes, res["sa"], None, res["offsets"], wl.w2, wl.s2)
-    y_ref = oracle.unpermute(o_ref, res["inv_pos"], res["w"])
-    fro_own = np.linalg.norm(yy - res["y"]) / np.linalg.norm(res["y"])
-    assert fro_own <= 2e-3, fro_own
-    r = assert_float_parity(yy, y_ref, "layer output", maxrel=maxrel_bar)
-    say(f"layer output vs oracle: fro {fro_own:.2e}; {flips} midpoint code choices; vs matching reference {r}")
+    # the re-quantized codes: exact on the GPU's own act (recomputed from its h on the unfused
+    # path), and where they differ from the independent run, explained by the act difference
+    act_gpu = host(b["act"]) if fused else oracle.swiglu_f32(host(b["h"]))
+    qa_gpu, sa_gpu = host(b["qa"]), host(b["sa"])
+    flipped = check_requant(act_gpu, qa_gpu, sa_gpu, res["qa"], act_exact=fused)
+    token_flipped = flipped.any(axis=1)[res["inv_pos"]].reshape(sh.T, sh.k).any(axis=1)
+    o_same = oracle.grouped_gemm(qa_gpu, sa_gpu, None, res["offsets"], wl.w2, wl.s2)
+    y_same = oracle.unpermute(o_same, res["inv_pos"], res["w"])
+    if y_dtype == torch.bfloat16:
+        # the bf16 output carries its own rounding (2^-9 relative): the per-element bars are its own
+        fro = np.linalg.norm(yy - res["y"]) / np.linalg.norm(res["y"])
+        assert fro <= 2e-3, fro
+        r = assert_float_parity(yy, y_same, "layer output (bf16)", maxrel=maxrel_bar)
+    else:
+        r = check_layer_output(yy, res["y"], y_same, token_flipped, "layer output", maxrel=maxrel_bar)
+    say(f"layer output vs oracle: {r}; {int(flipped.sum())} codes differ from the independent run")
     return moe, y, r
 
 
