@@ -14,7 +14,9 @@ import os
 
 import torch
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libw4a8moe.so")
+# the in-tree build; W4A8_MOE_LIB names another build of the same library (the tests load a host
+# sanitizer build of the C ABI this way)
+LIB_PATH = os.environ.get("W4A8_MOE_LIB") or os.path.join(os.path.dirname(os.path.abspath(__file__)), "libw4a8moe.so")
 
 W4A8_Y_F32 = 0
 W4A8_Y_BF16 = 1

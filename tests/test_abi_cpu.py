@@ -348,3 +348,23 @@ def test_front_checks(L, no_device):
     if no_device:
         assert call() == ERR_DEVICE
         assert call(g, True) == ERR_DEVICE
+
+
+def test_last_error_per_thread(L):
+    # each thread sees the detail of its own last call, whatever the others do meanwhile
+    import threading
+    errors = []
+
+    def worker(i):
+        for r in range(200):
+            bad_h = 128 * (i + 1) + 1
+            if L.w4a8_moe_swiglu(P, 4, bad_h, P, P, None) != ERR_SHAPE or f"I={bad_h}" not in ops.last_error():
+                errors.append((i, r))
+            if L.w4a8_moe_swiglu(None, 0, 128, None, None, None) != OK or ops.last_error() != "":
+                errors.append((i, r, "ok"))
+    threads = [threading.Thread(target=worker, args=(i,)) for i in range(8)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    assert not errors, errors[:5]
