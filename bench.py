@@ -241,6 +241,10 @@ def main() -> int:
     ap.add_argument("--cpu-tokens", type=int, default=32, help="tokens in the CPU oracle sample (0: skip)")
     ap.add_argument("--no-prefill", action="store_true",
                     help="with the default decode workload, skip the prefill T=8192 block of the line")
+    ap.add_argument("--tokens", type=int, default=0, help="run the config's shape with this many tokens")
+    ap.add_argument("--zipf", action="store_true", help="skew the routing of the config's shape by Zipf(1.1)")
+    ap.add_argument("--algo", choices=("auto", "stream", "tiled"), default="auto",
+                    help="grouped-GEMM kernel of both GEMMs (default: the library's automatic choice)")
     ap.add_argument("--quiet", action="store_true")
     ap.add_argument("--scheme", choices=("g128", "channel", "mxfp4"), default="g128",
                     help="g128: INT4 group-128 x FP8 per token (default); channel: per-channel INT4 x INT8 per "
@@ -321,12 +325,22 @@ def measure_layer(index: int, args, log) -> dict:
     gate/up GEMM against its roofline."""
     import torch
 
-    from quantized_grouped_gemm_token_amd import workloads
+    from quantized_grouped_gemm_token_amd import ops, workloads
     from quantized_grouped_gemm_token_amd.layer import W4A8MoE, W4A8MoEChannel, W4A8MoEMxfp4
 
     dev = "cuda:0"
     t0 = time.time()
-    wl = workloads.make_config(index)
+    if args.tokens or args.zipf:
+        # the config's shape with another token count and / or Zipf(1.1)-skewed routing
+        import dataclasses
+        base = workloads.WORKLOADS[index]
+        T = args.tokens or base.T
+        shape = dataclasses.replace(base, T=T, zipf_s=1.1 if args.zipf else base.zipf_s,
+                                    name=base.name.split(" T=")[0] + f" T={T}" + base.name[base.name.index(" H="):]
+                                    + (" zipf1.1" if args.zipf and base.zipf_s is None else ""))
+        wl = workloads.make_workload(shape, 1000 + index)
+    else:
+        wl = workloads.make_config(index)
     sh = wl.shape
     log(f"generated {sh.name} in {time.time() - t0:.1f} s")
     to = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)  # noqa: E731
@@ -342,11 +356,12 @@ def measure_layer(index: int, args, log) -> dict:
         moe = W4A8MoE(to(wl.w13), to(wl.s13), to(wl.w2), to(wl.s2), k=sh.k)
     x = torch.from_numpy(wl.x_bf16.view(np.int16)).to(dev).view(torch.bfloat16)
     logits = to(wl.logits)
+    algo = {"auto": ops.W4A8_GG_AUTO, "stream": ops.W4A8_GG_STREAM, "tiled": ops.W4A8_GG_TILED}[args.algo]
     y = torch.empty((sh.T, sh.H), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream()
 
     for _ in range(args.warmup):
-        moe(x, logits, y)
+        moe(x, logits, y, algo=algo)
     torch.cuda.synchronize()
     log(f"{sh.name}: warmup {args.warmup} done")
 
@@ -357,7 +372,7 @@ def measure_layer(index: int, args, log) -> dict:
     torch.cuda.synchronize()
     start.record(stream)
     for i in range(args.steps):
-        moe(x, logits, y, events=evs[i])
+        moe(x, logits, y, events=evs[i], algo=algo)
     stop.record(stream)
     torch.cuda.synchronize()
     eager_ms = start.elapsed_time(stop) / args.steps
@@ -365,7 +380,7 @@ def measure_layer(index: int, args, log) -> dict:
     log(f"{sh.name}: per step ms: " + ", ".join(f"{k}={v:.4f}" for k, v in per_step.items()))
 
     # the same step replayed from a HIP graph: W untimed replays, then exactly K timed ones
-    graph = moe.capture(x, logits, y)
+    graph = moe.capture(x, logits, y, algo=algo)
     for _ in range(args.warmup):
         graph.replay()
     torch.cuda.synchronize()
@@ -398,7 +413,9 @@ def measure_layer(index: int, args, log) -> dict:
     down_flops = 2.0 * R * sh.H * sh.I
     t_gu = per_step["gemm_gate_up"] * 1e-3
     t_dn = per_step["gemm_down"] * 1e-3
-    decode = index in (0, 1, 2)
+    # the kernel that ran: the library's automatic choice takes the streaming one while no expert has more
+    # than 32 rows and the average at most 12, else the tiled one
+    decode = args.algo == "stream" or (args.algo == "auto" and R <= 12 * sh.E and int(counts.max()) <= 32)
     kernel = "gg_stream" if decode else "gg_tiled"
     khash = kernel_sources_hash(kernel)
     tag = workload_tag(sh) + ("" if args.scheme == "g128" else "_" + args.scheme)

@@ -72,8 +72,13 @@ typedef enum w4a8_status {
 #define W4A8_Y_F32 0
 #define W4A8_Y_BF16 1
 
-/* algo values of the _prepacked grouped GEMM calls */
-#define W4A8_GG_AUTO 0     /* choose from M_total / E (the _prepacked calls)     */
+/* algo values of the _prepacked grouped GEMM calls.  W4A8_GG_AUTO takes the
+ * streaming kernel while no expert has more than 32 rows and the average expert
+ * at most 12 (M_total <= 12 E), else the tiled one.  Where M_total does not
+ * settle it, both kernels are enqueued and the one the largest expert (known on
+ * the device only) does not call for returns at once.  The calls without
+ * _prepacked always take the streaming kernel. */
+#define W4A8_GG_AUTO 0     /* choose from the rows per expert                     */
 #define W4A8_GG_STREAM 1   /* weight-streaming kernel for few rows per expert     */
 #define W4A8_GG_TILED 2    /* LDS-tiled persistent kernel for many rows per expert */
 
@@ -239,7 +244,7 @@ int w4a8_moe_grouped_gemm(const uint8_t* a, const float* a_scale, const int32_t*
  *   w_blk : int32 [E][N/16][K/128][16][16], 16-byte aligned.
  *   s_blk : fp32 [E][K/128][N].
  *   algo  : W4A8_GG_AUTO, W4A8_GG_STREAM or W4A8_GG_TILED; every algo
- *           computes the same result, the choice only affects speed.
+ *           computes the same bits, the choice only affects speed.
  *   Rules : as w4a8_moe_grouped_gemm, with N % 64 == 0.
  */
 int w4a8_moe_grouped_gemm_prepacked(const uint8_t* a, const float* a_scale, const int32_t* a_rows,

@@ -165,7 +165,7 @@ __global__ __launch_bounds__(kThreads, 1) void gg_tiled_kernel(const uint8_t* __
                                                                const int32_t* __restrict__ w_packed,
                                                                const float* __restrict__ w_scale, int64_t N,
                                                                int64_t K, float* __restrict__ out,
-                                                               float* __restrict__ pmax) {
+                                                               float* __restrict__ pmax, int sel_rows) {
   constexpr bool kInt8 = kForm == kFormChannel;
   constexpr bool kMx = kForm == kFormMx;
   __shared__ RingSlot ring0, ring1, ring2;
@@ -173,7 +173,7 @@ __global__ __launch_bounds__(kThreads, 1) void gg_tiled_kernel(const uint8_t* __
   __shared__ __attribute__((aligned(16))) float bias_sm[2][kTM];   // -2^-6 * group code sums: [group parity][row]
   __shared__ __attribute__((aligned(16))) float ascale_sm[kTM];    // token scales of the tile's rows
   __shared__ int tile_start[kMaxExperts + 1];                      // first tile index of each expert
-  __shared__ int wsum[kWaves];
+  __shared__ int wsum[kWaves], wmax[kWaves];
   __shared__ unsigned int rmax_sm[2][kTM];                         // fused form: row max |act| of the tile, by tile parity
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -190,21 +190,32 @@ __global__ __launch_bounds__(kThreads, 1) void gg_tiled_kernel(const uint8_t* __
   {
     constexpr int kPer = kMaxExperts / kThreads;   // experts per thread
     int cnt[kPer];
-    int local = 0;
+    int local = 0, most = 0;
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
       const int ex = tid * kPer + i;
-      cnt[i] = ex < E ? tiles_of(offsets[ex + 1] - offsets[ex], NB, NW) : 0;
+      const int rows = ex < E ? offsets[ex + 1] - offsets[ex] : 0;
+      cnt[i] = tiles_of(rows, NB, NW);
       local += cnt[i];
+      most = max(most, rows);
     }
     int incl = local;
 #pragma unroll
     for (int off = 1; off < kWave; off <<= 1) {
       const int o = __shfl_up(incl, off, kWave);
       if (lane >= off) incl += o;
+      most = max(most, __shfl_xor(most, off, kWave));
     }
     if (lane == kWave - 1) wsum[wave] = incl;
+    if (lane == 0) wmax[wave] = most;
     __syncthreads();
+    // the choice on the device: nothing to do when the stream kernel takes the batch
+    if (sel_rows >= 0) {
+      int top = 0;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) top = max(top, wmax[w]);
+      if (top <= sel_rows) return;
+    }
     int run = 0;
     for (int w = 0; w < wave; ++w) run += wsum[w];
     run += incl - local;
@@ -630,14 +641,21 @@ static int cu_count() {
   return cus;
 }
 
-hipError_t launch_gg_tiled(const GemmArgs& g, hipStream_t stream) {
+bool tiled_fits(const GemmArgs& g) {
   // the tiled kernel addresses its operands with 32-bit byte offsets
   constexpr int64_t k4G = (int64_t)1 << 32;
-  if (g.M_total * g.K >= k4G || g.M_total * 4 >= k4G || g.N * (g.K / 2) >= k4G || g.N * (g.K / 128) * 4 >= k4G)
-    return launch_gg_stream(g, stream);
+  return g.M_total * g.K < k4G && g.M_total * 4 < k4G && g.N * (g.K / 2) < k4G && g.N * (g.K / 128) * 4 < k4G;
+}
+
+hipError_t launch_gg_tiled(const GemmArgs& g, hipStream_t stream) {
+  if (!tiled_fits(g)) {
+    GemmArgs all = g;
+    all.sel_rows = -1;
+    return launch_gg_stream(all, stream);
+  }
   auto go = [&](auto kernel) {
     hipLaunchKernelGGL(kernel, dim3(cu_count()), dim3(kThreads), 0, stream, g.a, g.a_scale, g.a_rowsum, g.a_rows,
-                       g.offsets, g.E, g.w_packed, g.w_scale, g.N, g.K, g.out, g.pmax);
+                       g.offsets, g.E, g.w_packed, g.w_scale, g.N, g.K, g.out, g.pmax, (int)g.sel_rows);
   };
   if (g.pmax) {
     if (g.a_rowsum) go(gg_tiled_kernel<kFormChannel, true>);

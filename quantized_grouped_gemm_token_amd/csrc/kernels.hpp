@@ -40,6 +40,10 @@ struct GemmArgs {
   // nibble k at bits 4 (k mod 8); MXFP4 u8 [E][N][K/2]) with scales [E][N][K/128]
   // (fp32) or [E][N][K/32] (E8M0): the stream kernel only
   bool row_major = false;
+  // the kernel choice taken on the device from the batch's largest expert: when
+  // >= 0, both kernels are launched, the stream kernel returning at once if some
+  // expert has more than sel_rows rows and the tiled kernel if none has
+  int32_t sel_rows = -1;
 };
 
 hipError_t launch_quant_act(const uint16_t* x, int64_t T, int64_t H, int64_t ld, uint8_t* q, float* s,
@@ -55,6 +59,9 @@ hipError_t launch_permute(const int32_t* ids, int64_t R, int k, int E, int32_t* 
                           int32_t* inv_pos, int32_t* counts, hipStream_t stream);
 hipError_t launch_gg_stream(const GemmArgs& g, hipStream_t stream);
 hipError_t launch_gg_tiled(const GemmArgs& g, hipStream_t stream);
+// whether the tiled kernel's 32-bit byte offsets reach every operand (else
+// launch_gg_tiled runs the stream kernel)
+bool tiled_fits(const GemmArgs& g);
 hipError_t launch_swiglu(const float* h, int64_t M, int64_t I, uint8_t* q, float* s, hipStream_t stream);
 hipError_t launch_quant_act_i8(const uint16_t* x, int64_t T, int64_t H, int64_t ld, int8_t* q, float* s,
                                int32_t* rowsum, hipStream_t stream);

@@ -16,7 +16,9 @@ intermediate size 2048 implied by the card's section 局限性 (TP8 slices of
 * activations are N(0, 1) fp32 rounded to bf16; the decode shapes scale 1% of
   the hidden channels (a seeded choice shared by all tokens) by 20 first;
 * router logits are N(0, 1) fp32; the skewed prefill adds log p(rank) of a
-  Zipf(1.1) law over a seeded ranking of the experts.
+  Zipf(1.1) law over a seeded ranking of the experts (and so does a sixth
+  shape, skewed decode at 256 tokens, seed 1005, which is no benchmark
+  config).
 
 Streams: numpy PCG64 seeded by SeedSequence(1000 + index), spawned in the
 fixed order W13, S13, W2, S2, x, outlier channels, logits, expert ranking;
@@ -61,6 +63,13 @@ WORKLOADS = (
     Shape("skewed prefill T=16384 H=6144 I=2048 E=256 top-8 zipf1.1", 16384, 6144, 2048, 256, 8,
           zipf_s=1.1),
 )
+
+
+# decode at 256 tokens with the routing of the skewed prefill (Zipf(1.1) over a
+# seeded ranking): a test case and a benchmark option, not one of the five above
+SKEWED_DECODE = Shape("skewed decode T=256 H=6144 I=2048 E=256 top-8 zipf1.1", 256, 6144, 2048, 256, 8,
+                      outlier_frac=0.01, zipf_s=1.1)
+SKEWED_DECODE_SEED = 1005
 
 
 @dataclass
@@ -122,6 +131,11 @@ def make_workload(shape: Shape, seed: int, with_weights: bool = True) -> Workloa
 def make_config(index: int, with_weights: bool = True) -> Workload:
     """Workload index 0..4 (tiny, decode 128, decode 256, prefill 8K, skewed 16K)."""
     return make_workload(WORKLOADS[index], 1000 + index, with_weights)
+
+
+def make_skewed_decode(with_weights: bool = True) -> Workload:
+    """The skewed decode workload (SKEWED_DECODE)."""
+    return make_workload(SKEWED_DECODE, SKEWED_DECODE_SEED, with_weights)
 
 
 def make_custom(T: int, H: int, I: int, E: int, k: int, seed: int, **kw) -> Workload:

@@ -1,7 +1,8 @@
 """GPU parity at the full workload sizes, for the three weight forms.
 
-decode T=128 and T=256, prefill T=8192 and skewed prefill T=16384 (H=6144,
-I=2048, E=256, top-8), each with the group-128 INT4 x FP8 experts, the
+decode T=128 and T=256, prefill T=8192, skewed prefill T=16384 and skewed
+decode T=256 (H=6144, I=2048, E=256, top-8; the skewed routings Zipf(1.1),
+where the hottest expert gets most of the tokens), each with the group-128 INT4 x FP8 experts, the
 per-channel INT4 x INT8 ones and the MXFP4 ones.  The layer runs on the GPU
 as the benchmark runs it (prepacked experts, automatic kernel choice, fused
 SwiGLU, the one-launch front at decode), once per workload and form, and
@@ -44,7 +45,7 @@ from quantized_grouped_gemm_token_amd.layer import W4A8MoE, W4A8MoEChannel, W4A8
 
 pytestmark = pytest.mark.gpu
 
-CONFIGS = [1, 2, 3, 4]
+CONFIGS = [1, 2, 3, 4, "skewed-decode"]
 FORMS = ["g128", "channel", "mxfp4"]
 LAYERS = {"g128": W4A8MoE, "channel": W4A8MoEChannel, "mxfp4": W4A8MoEMxfp4}
 
@@ -57,12 +58,12 @@ def _workload_of(index):
     if index not in _workload:
         _workload.clear()
         say(f"generate config {index}")
-        _workload[index] = workloads.make_config(index)
+        _workload[index] = workloads.make_skewed_decode() if index == "skewed-decode" else workloads.make_config(index)
     return _workload[index]
 
 
 # workload-major order: each workload's 5 GB of experts is drawn once for its three forms
-@pytest.fixture(scope="module", params=[(c, f) for c in CONFIGS for f in FORMS], ids=lambda p: f"config{p[0]}-{p[1]}")
+@pytest.fixture(scope="module", params=[(c, f) for c in CONFIGS for f in FORMS], ids=lambda p: f"{p[0] if isinstance(p[0], str) else f'config{p[0]}'}-{p[1]}")
 def run(request):
     index, form = request.param
     wl = _workload_of(index)

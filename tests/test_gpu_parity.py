@@ -19,7 +19,7 @@ from quantized_grouped_gemm_token_amd.layer import W4A8MoE
 
 pytestmark = pytest.mark.gpu
 
-ALGOS = (ops.W4A8_GG_STREAM, ops.W4A8_GG_TILED)
+ALGOS = (ops.W4A8_GG_STREAM, ops.W4A8_GG_TILED, ops.W4A8_GG_AUTO)
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -174,6 +174,9 @@ def _gemm_problem(rng, E, N, K, counts, src_rows=None):
     (3, 320, 256, [200, 241, 0], True),            # partial tiles of 7/8 row blocks; N not a multiple of 256
     (4, 256, 256, [128, 129, 257, 513], False),    # square tiles of equal height: 1, 2 and 3 per expert
     (2, 512, 384, [512, 769], True),
+    (6, 128, 256, [17, 3, 0, 1, 2, 0], True),       # M_total <= 4 E: the one-block stream kernel, 2 row passes
+    (8, 256, 384, [9, 40, 0, 3, 1, 0, 2, 5], False),  # AUTO: both kernels launched, the tiled one runs
+    (8, 256, 384, [9, 30, 0, 3, 1, 0, 2, 5], True),   # AUTO: both kernels launched, the stream one runs
 ])
 def test_grouped_gemm(E, N, K, counts, gather, algo, rng):
     w, s, offsets, a, sa, rows = _gemm_problem(rng, E, N, K, counts, src_rows=40 if gather else None)
@@ -200,6 +203,35 @@ def test_grouped_gemm_exact_integers(algo, rng):
     out = ops.w4a8_moe_grouped_gemm_prepacked(to_dev(codes), to_dev(np.ones(M, np.float32)), None, to_dev(offsets),
                                     *prepack_int4(w, s), M, algo=algo)
     assert np.array_equal(host(out), want)
+
+
+@pytest.mark.parametrize("fused", [False, True])
+@pytest.mark.parametrize("counts", [
+    [17, 3, 0, 1, 2, 0],             # one-block stream kernel
+    [9, 40, 0, 3, 1, 0],             # a 40-row expert: the tiled kernel under AUTO
+    [30, 31, 32, 0, 5, 1],           # the most rows AUTO gives the stream kernel
+    [64, 65, 33, 16, 0, 2],          # the multi-block stream kernel: 4, 2 and 1 blocks per load
+])
+def test_algos_agree_bitwise(counts, fused, rng):
+    """The kernel choice is a matter of speed only: the three algos give the same bits (same
+    products, same group order, same fp32 operations), whichever kernel runs each expert."""
+    E, K = len(counts), 384
+    N = 256
+    w, s, offsets, a, sa, rows = _gemm_problem(rng, E, N, K, counts, src_rows=50)
+    M = int(offsets[-1])
+    wb, sb = prepack_int4(w, s)
+    say(f"algos agree counts={counts} fused={fused}")
+    outs = []
+    for algo in ALGOS:
+        if fused:
+            act, pmax = ops.w4a8_moe_grouped_gemm_swiglu_prepacked(to_dev(a), to_dev(sa), to_dev(rows),
+                                                                   to_dev(offsets), wb, sb, M, algo=algo)
+            outs.append(np.concatenate([host(act).ravel(), host(pmax).max(axis=1)]))
+        else:
+            outs.append(host(ops.w4a8_moe_grouped_gemm_prepacked(to_dev(a), to_dev(sa), to_dev(rows),
+                                                                 to_dev(offsets), wb, sb, M, algo=algo)).ravel())
+    for o in outs[1:]:
+        assert np.array_equal(o.view(np.uint32), outs[0].view(np.uint32))
 
 
 # ------------------------------------------------------- steps 4 + 5, fused
