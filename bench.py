@@ -9,12 +9,15 @@ synthetic tokens, inputs already resident in HBM.  The default workload is
 decode at 128 tokens (H=6144, I=2048, 256 experts, top-8), the shape the
 headline value is quoted on; the same run then times the 8K-token prefill
 (the metric's other half) into a "prefill" block of the line (--no-prefill
-skips it; --config 3 makes the prefill the headline workload).
+skips it; --config 3 makes the prefill the headline workload), and decode at
+256 tokens with Zipf(1.1)-skewed routing into a "skewed_decode" block
+(--no-skewed skips it; --config 5 makes it the headline workload).
 
 Prints ONE JSON line: layer tokens/s, the roofline of the dominant kernel
-(the gate/up grouped GEMM, timed with events on its own stream: HBM bytes at
-decode, FP8 MFMA FLOPs at prefill), and the CPU oracle timed on a bounded
-sample of the decode workload on every host core and on one.
+(the gate/up grouped GEMM, timed with events on its own stream: HBM bytes
+where its FLOPs per algorithmic byte are below the chip's ridge point, as at
+decode, FP8 MFMA FLOPs above it, as at prefill), and the CPU oracle timed on
+a bounded sample of the decode workload on every host core and on one.
 
 The step is timed twice over K steps: launched kernel by kernel with events
 around each kernel (the per-kernel times and the roofline's launch duration),
@@ -237,10 +240,13 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=1, help="workload index: 1 decode T=128 (default), "
-                                                          "2 decode T=256, 3 prefill T=8192, 4 skewed T=16384")
+                                                          "2 decode T=256, 3 prefill T=8192, 4 skewed T=16384, "
+                                                          "5 skewed decode T=256")
     ap.add_argument("--cpu-tokens", type=int, default=32, help="tokens in the CPU oracle sample (0: skip)")
     ap.add_argument("--no-prefill", action="store_true",
                     help="with the default decode workload, skip the prefill T=8192 block of the line")
+    ap.add_argument("--no-skewed", action="store_true",
+                    help="with the default decode workload, skip the skewed decode T=256 block of the line")
     ap.add_argument("--tokens", type=int, default=0, help="run the config's shape with this many tokens")
     ap.add_argument("--zipf", action="store_true", help="skew the routing of the config's shape by Zipf(1.1)")
     ap.add_argument("--algo", choices=("auto", "stream", "tiled"), default="auto",
@@ -312,6 +318,15 @@ def main() -> int:
             "gemms": p["gemms"], "step_ms": p["step_ms"], "eager_ms_per_step": p["eager_ms"],
             "graph_ms_per_step": p["graph_ms"]}
         del p
+    if args.config == 1 and not args.no_skewed:
+        # decode with skewed routing: the hottest expert holds most of the batch's tokens
+        q = measure_layer(5, args, log)
+        line["skewed_decode"] = {
+            "workload": q["shape"].name, "tokens_per_s": round(q["shape"].T / (q["ms_step"] * 1e-3), 1),
+            "ms_per_step": round(q["ms_step"], 5), "launch": line["launch"], "roofline": q["roofline"],
+            "gemms": q["gemms"], "step_ms": q["step_ms"], "eager_ms_per_step": q["eager_ms"],
+            "graph_ms_per_step": q["graph_ms"]}
+        del q
     if args.cpu_tokens > 0:
         n = min(args.cpu_tokens, wl.shape.T)
         log(f"CPU oracle on {n} tokens ({os.cpu_count()} BLAS threads, then 1) ...")
@@ -333,14 +348,14 @@ def measure_layer(index: int, args, log) -> dict:
     if args.tokens or args.zipf:
         # the config's shape with another token count and / or Zipf(1.1)-skewed routing
         import dataclasses
-        base = workloads.WORKLOADS[index]
+        base = workloads.SKEWED_DECODE if index == 5 else workloads.WORKLOADS[index]
         T = args.tokens or base.T
         shape = dataclasses.replace(base, T=T, zipf_s=1.1 if args.zipf else base.zipf_s,
                                     name=base.name.split(" T=")[0] + f" T={T}" + base.name[base.name.index(" H="):]
                                     + (" zipf1.1" if args.zipf and base.zipf_s is None else ""))
         wl = workloads.make_workload(shape, 1000 + index)
     else:
-        wl = workloads.make_config(index)
+        wl = workloads.make_skewed_decode() if index == 5 else workloads.make_config(index)
     sh = wl.shape
     log(f"generated {sh.name} in {time.time() - t0:.1f} s")
     to = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)  # noqa: E731
@@ -420,7 +435,8 @@ def measure_layer(index: int, args, log) -> dict:
     khash = kernel_sources_hash(kernel)
     tag = workload_tag(sh) + ("" if args.scheme == "g128" else "_" + args.scheme)
     traffic = load_traffic(os.path.join(ROOT, "profiles", f"{kernel}_{tag}_pmc.txt"), khash)
-    if decode:
+    # the roofline that bounds the GEMM: HBM below the ridge point (FLOPs per byte of the peaks), else MFMA
+    if gate_up_flops / gate_up_bytes < FP8_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9):
         achieved = gate_up_bytes / t_gu / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic}

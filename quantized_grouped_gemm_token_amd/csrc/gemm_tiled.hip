@@ -35,10 +35,14 @@
 // The +8 offset of the uint4b8 nibbles is removed with the per-row sums of
 // the activation codes of each group (see gemm_common.hpp): each wave loads
 // exactly the activation rows whose sums it computes, with 16x16x128 MFMAs
-// against the constant -2^-6, so the sums of group g + 1 are computed in the
-// middle of group g's products, as soon as the wave's own loads of g + 1 have
-// landed, and are published by the one barrier per group.  They enter each
-// product as its accumulator input.
+// against the constant -2^-6, so the sums of group g + 1 are computed after
+// the last A block of group g's products, once the wave's own loads of g + 1
+// have landed, and are published by the one barrier per group.  They enter
+// each product as its accumulator input.  Waiting there rather than halfway
+// through the group leaves the loads nearly two groups of time to land: the
+// kernel is bound by their latency (with the in-loop loads taken out, as a
+// timing experiment, the gate/up GEMM ran 21% faster; without the scale FMAs
+// and nibble splits, 5%).
 //
 // The weights come in the GEMM storage (16 columns x 128 K contiguous, scales
 // group-major), so each weight load reads one contiguous 1 KB piece and each
@@ -365,6 +369,10 @@ __global__ __launch_bounds__(kThreads, 1) void gg_tiled_kernel(const uint8_t* __
         }
       };
 
+      // where the wait for group g+1 goes: the group-128 form after the last A block
+      // (7% faster gate/up at prefill than halfway); the MX and INT8 forms halfway,
+      // where they were 2-5% faster (the later wait made the MX form spill)
+      constexpr int kWaitRegion = (kInt8 || kMx) ? (kNB - 1) / 2 : kNB - 1;
       using Acc = std::conditional_t<kInt8, i32x4, v4f>;
       Acc acc[kNB > 0 ? kNB : 1][kBBlocks];
 #pragma unroll
@@ -376,11 +384,12 @@ __global__ __launch_bounds__(kThreads, 1) void gg_tiled_kernel(const uint8_t* __
       const uint32_t a_blk0 = (uint32_t)(16 * rg) * kGroup;             // first A block of the wave
       const uint32_t w_rd = kWBase + (uint32_t)(64 * cg) * 64u + w_rd_lane;
 
-      // One K group in slot S: prefetch group g+2; multiply group g; in the
-      // middle, once this wave's loads of group g+1 have landed, publish that
-      // group's row sums; then one barrier.  kMore: groups g+1 and g+2 exist (the
-      // main part of the K loop), so the step has no branches: with a branch around
-      // the middle wait, the compiler moved the first half's products below it.
+      // One K group in slot S: prefetch group g+2; multiply group g; after the
+      // last A block's products (MX and INT8 forms: halfway through them), once
+      // this wave's loads of group g+1 have landed, publish that group's row sums;
+      // then one barrier.  kMore: groups g+1 and g+2
+      // exist (the main part of the K loop), so the step has no branches: with a
+      // branch around the wait, the compiler moved earlier products below it.
       auto step = [&](auto S_, auto M_, int g) {
         constexpr int S = decltype(S_)::value;
         constexpr bool kMore = decltype(M_)::value;
@@ -465,7 +474,7 @@ __global__ __launch_bounds__(kThreads, 1) void gg_tiled_kernel(const uint8_t* __
               for (int j = 0; j < kBBlocks; ++j) scale_into(std::integral_constant<int, i - 1>{}, j);
             }
             __builtin_amdgcn_sched_barrier(0);   // regions stay in order: no hoisting of later reads
-            if constexpr (i == (kNB - 1) / 2) mid();   // the middle of the group's products
+            if constexpr (i == kWaitRegion) mid();
           };
           region(std::integral_constant<int, 0>{});
           region(std::integral_constant<int, 1>{});
@@ -515,8 +524,8 @@ __global__ __launch_bounds__(kThreads, 1) void gg_tiled_kernel(const uint8_t* __
 
       // MX and INT8 forms: three steps at a time while every step has a next stage,
       // then the last 2..4 groups (all of them when G < 5), whose slots start again
-      // at 0.  The group-128 form keeps checked steps throughout: with the products
-      // of the first half held before the middle wait it spills inside the K loop.
+      // at 0.  The group-128 form keeps checked steps throughout: with its products
+      // held before the wait it spills inside the K loop.
       if constexpr (kInt8 || kMx) {
         int g = 0;
         for (; g + 5 <= G; g += 3) {
