@@ -501,9 +501,10 @@ __global__ __launch_bounds__(kStreamThreads, kMaxMB == 1 ? 4 : 3) void gg_stream
 // The multi-block kernel when the average expert has more than 8 rows.  The
 // one-block kernel runs at 4 waves per SIMD, the multi-block one at 3: measured
 // on the decode shape (H 6144, I 2048, 256 experts, top-8), uniform routing, the
-// layer took 1.6% less time with the one-block kernel at 128 tokens and 1.3% less
-// at 256; at 384 tokens the multi-block one was 0.5% faster, at 512 22% and at
-// 1024 36%, and on Zipf-skewed routing 25-42%.
+// layer took 1.5% less time with the one-block kernel at 128 tokens and 0.8% less
+// at 256; with one block per weight load the layer took 7% more time than the
+// multi-block kernel at 384 tokens, 24% at 512, 56% at 1024, and 33-72% on
+// Zipf-skewed routing.
 template <int NS, int CH, int kForm, bool kSwiglu>
 static void launch_variant(const GemmArgs& g, hipStream_t stream) {
   const dim3 grid((unsigned)((g.N + 64 * NS - 1) / (64 * NS)), (unsigned)g.E);
