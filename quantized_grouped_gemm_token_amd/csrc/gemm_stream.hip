@@ -24,13 +24,19 @@
 // for lane group q).
 //
 // Grid: (ceil(N / (64 NS)), E); 256 threads = 4 waves side by side in N.  An
-// expert with no rows returns at once.  Each weight load feeds up to MB = 4
-// M blocks of 16 rows: the workgroup picks MB from its expert's row count (1
-// for up to 16 rows, 2 for up to 32, else 4), so an expert's weights are
-// streamed once for every 64 of its rows.  A skewed batch, whose hot experts
-// get many of its rows, then reads little more than the weights it touches.
-// LDS holds 2 buffers of 8 (group, M block) activation tiles of 2 KB: 4-group
-// chunks for MB = 1 and 2, group-pair chunks for MB = 4.
+// expert with no rows returns at once.  In the multi-block form each weight
+// load feeds up to MB = 4 M blocks of 16 rows: the workgroup picks MB from its
+// expert's row count (1 for up to 16 rows, 2 for up to 32, else 4), so an
+// expert's weights are streamed once for every 64 of its rows, and a skewed
+// batch, whose hot experts get many of its rows, reads little more than the
+// weights it touches.  Its LDS holds 2 buffers of 8 (group, M block)
+// activation tiles of 2 KB: 4-group chunks for MB = 1 and 2, group-pair chunks
+// for MB = 4.  The one-block form (MB = 1 only; batches of at most 8 rows per
+// expert on average) keeps 2 buffers of one chunk's tiles and fewer registers,
+// for 4 waves per SIMD.
+// With the kernel choice taken on the device (sel_rows >= 0), every wave first
+// reads the E + 1 expert offsets and the workgroup returns at once if an
+// expert has more rows than the streaming kernel takes.
 //
 // The same kernel reads the weights in the row-major stored format too (the
 // grouped GEMM calls without "_prepacked"): the lane's operand of a group is
