@@ -40,9 +40,16 @@
  *     only enqueues work on it and never synchronizes; ragged sizes (expert
  *     row offsets) stay on the device, so a chained layer is capturable.
  *   - Return value: W4A8_OK (0) or a w4a8_status code.  All argument checks
- *     run on the host before anything is launched: an error means nothing
- *     was enqueued.  w4a8_moe_last_error() gives the calling thread's last
- *     error detail.  Sizes of zero tokens/rows are valid no-ops.
+ *     run on the host before anything is launched: an argument error means
+ *     nothing was enqueued.  W4A8_ERR_HIP reports a failed launch; where a
+ *     call makes several launches (the layer's steps, or both GEMM kernels
+ *     under W4A8_GG_AUTO), the ones before it may already be enqueued, and
+ *     the outputs are then undefined.  w4a8_moe_last_error() gives the
+ *     calling thread's last error detail.  Sizes of zero tokens/rows are
+ *     valid no-ops.
+ *   - The "not allocate" rule has one exception, for callers that cannot
+ *     allocate: w4a8_moe_permute_noalloc uses a 1 MiB device array that the
+ *     library holds per GPU.
  *   - Data preconditions that are NOT checked (undefined if violated):
  *     expert ids in [0, E); offsets monotone with offsets[E] == M_total;
  *     gather rows in range; no NaN/Inf in activations, logits or scales.

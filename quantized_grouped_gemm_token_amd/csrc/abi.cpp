@@ -1,6 +1,7 @@
 // C ABI of the W4A8 MoE layer: host-side argument checks, then kernel
 // launches on the caller's stream.  Every check runs before anything is
-// enqueued, so an error status means no work was launched.
+// enqueued, so an argument error means no work was launched (a failed launch,
+// W4A8_ERR_HIP, may follow launches of the same call that were enqueued).
 #include "w4a8_moe.h"
 
 #include <atomic>
