@@ -8,10 +8,12 @@ grouped GEMM, SwiGLU, down grouped GEMM, combine) over one batch of
 synthetic tokens, inputs already resident in HBM.  The default workload is
 decode at 128 tokens (H=6144, I=2048, 256 experts, top-8), the shape the
 headline value is quoted on; the same run then times the 8K-token prefill
-(the metric's other half) into a "prefill" block of the line (--no-prefill
-skips it; --config 3 makes the prefill the headline workload), and decode at
-256 tokens with Zipf(1.1)-skewed routing into a "skewed_decode" block
-(--no-skewed skips it; --config 5 makes it the headline workload).
+(the metric's other half) into a "prefill" block of the line and the skewed
+16K-token prefill into a "skewed_prefill" block (--no-prefill skips both;
+--config 3 or 4 makes either the headline workload), and decode at 256 tokens
+with Zipf(1.1)-skewed routing into a "skewed_decode" block (--no-skewed skips
+it; --config 5 makes it the headline workload).  Each workload also reports
+the median, p10 and p90 of single graph replays, timed after its timed region.
 
 Prints ONE JSON line: layer tokens/s, the roofline of the dominant kernel
 (the gate/up grouped GEMM, timed with events on its own stream: HBM bytes
@@ -244,7 +246,8 @@ def main() -> int:
                                                           "5 skewed decode T=256")
     ap.add_argument("--cpu-tokens", type=int, default=32, help="tokens in the CPU oracle sample (0: skip)")
     ap.add_argument("--no-prefill", action="store_true",
-                    help="with the default decode workload, skip the prefill T=8192 block of the line")
+                    help="with the default decode workload, skip the prefill T=8192 and skewed prefill "
+                         "T=16384 blocks of the line")
     ap.add_argument("--no-skewed", action="store_true",
                     help="with the default decode workload, skip the skewed decode T=256 block of the line")
     ap.add_argument("--tokens", type=int, default=0, help="run the config's shape with this many tokens")
@@ -305,27 +308,24 @@ def main() -> int:
         "config": m["config"], "roofline": m["roofline"], "cpu_baseline": None, "gemms": m["gemms"],
         "step_ms": m["step_ms"], "launch": "eager" if args.no_graph else "hip graph replay",
         "eager_ms_per_step": m["eager_ms"], "graph_ms_per_step": m["graph_ms"],
-        "device": m["device"], "kernel_sources_hash": m["roofline"]["kernel_sources_hash"],
+        "replay_ms_single_steps": m["replay_stats"], "device": m["device"], "kernel_sources_hash": m["roofline"]["kernel_sources_hash"],
     }
     wl = m.pop("wl")
     del m
+    # the other workloads of the metric, in the same run: the prefill half (the 8K-token prompt), the
+    # skewed prefill (reported against the same bar) and decode with skewed routing
+    blocks = []
     if args.config == 1 and not args.no_prefill:
-        # the prefill half of the metric: the 8K-token prompt, in the same run
-        p = measure_layer(3, args, log)
-        line["prefill"] = {
-            "workload": p["shape"].name, "tokens_per_s": round(p["shape"].T / (p["ms_step"] * 1e-3), 1),
-            "ms_per_step": round(p["ms_step"], 5), "launch": line["launch"], "roofline": p["roofline"],
-            "gemms": p["gemms"], "step_ms": p["step_ms"], "eager_ms_per_step": p["eager_ms"],
-            "graph_ms_per_step": p["graph_ms"]}
-        del p
+        blocks += [("prefill", 3), ("skewed_prefill", 4)]
     if args.config == 1 and not args.no_skewed:
-        # decode with skewed routing: the hottest expert holds most of the batch's tokens
-        q = measure_layer(5, args, log)
-        line["skewed_decode"] = {
+        blocks += [("skewed_decode", 5)]
+    for key, index in blocks:
+        q = measure_layer(index, args, log)
+        line[key] = {
             "workload": q["shape"].name, "tokens_per_s": round(q["shape"].T / (q["ms_step"] * 1e-3), 1),
             "ms_per_step": round(q["ms_step"], 5), "launch": line["launch"], "roofline": q["roofline"],
             "gemms": q["gemms"], "step_ms": q["step_ms"], "eager_ms_per_step": q["eager_ms"],
-            "graph_ms_per_step": q["graph_ms"]}
+            "graph_ms_per_step": q["graph_ms"], "replay_ms_single_steps": q["replay_stats"]}
         del q
     if args.cpu_tokens > 0:
         n = min(args.cpu_tokens, wl.shape.T)
@@ -407,6 +407,18 @@ def measure_layer(index: int, args, log) -> dict:
     graph_ms = start.elapsed_time(stop) / args.steps
     log(f"{sh.name}: step: eager {eager_ms:.4f} ms, graph replay {graph_ms:.4f} ms")
     ms_step = eager_ms if args.no_graph else graph_ms
+    # the spread of single steps: K more replays, each between its own pair of events (after the timed
+    # region, so that its events add nothing to it)
+    rev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for a, b in rev:
+        a.record(stream)
+        graph.replay()
+        b.record(stream)
+    torch.cuda.synchronize()
+    one = np.array([a.elapsed_time(b) for a, b in rev])
+    replay_stats = {"median": round(float(np.median(one)), 5), "p10": round(float(np.percentile(one, 10)), 5),
+                    "p90": round(float(np.percentile(one, 90)), 5), "steps": int(one.size)}
 
     # algorithmic work of the routed experts actually touched
     offsets = moe.buffers(sh.T)["offsets"].cpu().numpy()
@@ -469,7 +481,7 @@ def measure_layer(index: int, args, log) -> dict:
     torch.cuda.empty_cache()
     return dict(wl=wl, shape=sh, ms_step=ms_step, eager_ms=round(eager_ms, 5), graph_ms=round(graph_ms, 5),
                 step_ms={k: round(v, 5) for k, v in per_step.items()}, roofline=roof, gemms=gemms, config=config,
-                device=device)
+                device=device, replay_stats=replay_stats)
 
 
 if __name__ == "__main__":
