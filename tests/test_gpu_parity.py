@@ -175,6 +175,7 @@ def _gemm_problem(rng, E, N, K, counts, src_rows=None):
     (4, 256, 256, [128, 129, 257, 513], False),    # square tiles of equal height: 1, 2 and 3 per expert
     (2, 512, 384, [512, 769], True),
     (6, 128, 256, [17, 3, 0, 1, 2, 0], True),       # M_total <= 4 E: the one-block stream kernel, 2 row passes
+    (3, 768, 256, [1400, 5, 300], True),            # 6 M blocks: a group of 4 and a partial group of 2 (tiled order)
     (8, 256, 384, [9, 40, 0, 3, 1, 0, 2, 5], False),  # AUTO: both kernels launched, the tiled one runs
     (8, 256, 384, [9, 30, 0, 3, 1, 0, 2, 5], True),   # AUTO: both kernels launched, the stream one runs
 ])
@@ -211,6 +212,7 @@ def test_grouped_gemm_exact_integers(algo, rng):
     [9, 40, 0, 3, 1, 0],             # a 40-row expert: the tiled kernel under AUTO
     [30, 31, 32, 0, 5, 1],           # the most rows AUTO gives the stream kernel
     [64, 65, 33, 16, 0, 2],          # the multi-block stream kernel: 4, 2 and 1 blocks per load
+    [1400, 3, 0, 1, 2, 0],           # 6 M blocks of equal height in the tiled kernel, 22 row passes in the other
 ])
 def test_algos_agree_bitwise(counts, fused, rng):
     """The kernel choice is a matter of speed only: the three algos give the same bits (same
@@ -255,6 +257,7 @@ def _check_pmax(pmax, act):
     (3, 256, 384, [70, 1, 129], False),
     (2, 384, 1024, [300, 33], True),                  # N = 768: a wide tile half past N
     (3, 128, 640, [200, 241, 0], True),
+    (2, 256, 256, [1300, 9], False),                  # 6 M blocks in the tiled order's groups
 ])
 def test_grouped_gemm_swiglu(E, I, K, counts, gather, algo, rng):
     w, s, offsets, a, sa, rows = _gemm_problem(rng, E, 2 * I, K, counts, src_rows=40 if gather else None)
