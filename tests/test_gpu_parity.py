@@ -236,6 +236,28 @@ def test_algos_agree_bitwise(counts, fused, rng):
         assert np.array_equal(o.view(np.uint32), outs[0].view(np.uint32))
 
 
+@pytest.mark.parametrize("hot", [None, 517])
+def test_auto_choice_many_experts(hot, rng):
+    """The device-side kernel choice with more experts than one pass of its offsets scan covers (256):
+    with every expert at 3 rows or fewer the streaming kernel runs, with a 100-row expert at index 517 the
+    tiled one; either way the result holds the GEMM bar and equals both forced choices bit for bit."""
+    E, N, K = 600, 128, 256
+    counts = rng.integers(0, 4, size=E)
+    if hot is not None:
+        counts[hot] = 100
+    w, s, offsets, a, sa, rows = _gemm_problem(rng, E, N, K, list(counts), src_rows=64)
+    M = int(offsets[-1])
+    assert 32 < M <= 12 * E                       # the band where both kernels are launched
+    want = oracle.grouped_gemm(a, sa, rows, offsets, w, s)
+    wb, sb = prepack_int4(w, s)
+    say(f"auto choice E={E} hot={hot} M={M}")
+    outs = [host(ops.w4a8_moe_grouped_gemm_prepacked(to_dev(a), to_dev(sa), to_dev(rows), to_dev(offsets), wb, sb, M,
+                                                     algo=algo)) for algo in ALGOS]
+    assert_float_parity(outs[-1], want, "grouped_gemm auto", fro_tight=GEMM_FRO_TIGHT, maxrel=edge_shape_maxrel(N))
+    for o in outs[:-1]:
+        assert np.array_equal(o.view(np.uint32), outs[-1].view(np.uint32))
+
+
 # ------------------------------------------------------- steps 4 + 5, fused
 def _pmax_of(act):
     """Partial row maxima of |act|, one per 64 columns (what the fused GEMM may write)."""
