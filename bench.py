@@ -81,6 +81,12 @@ def load_traffic(path: str, kernel_hash: str):
         return None
 
 
+def roofline_bound(flops: float, algorithmic_bytes: float) -> str:
+    """The roofline that bounds a kernel: "hbm" while its FLOPs per algorithmic byte are below the
+    ridge point of the two published peaks (625 FLOP/B), else "mfma"."""
+    return "hbm" if flops / algorithmic_bytes < FP8_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9) else "mfma"
+
+
 def workload_tag(shape) -> str:
     """File-name tag of a workload, e.g. decode_T128."""
     return shape.name.split()[0] + f"_T{shape.T}"
@@ -447,8 +453,7 @@ def measure_layer(index: int, args, log) -> dict:
     khash = kernel_sources_hash(kernel)
     tag = workload_tag(sh) + ("" if args.scheme == "g128" else "_" + args.scheme)
     traffic = load_traffic(os.path.join(ROOT, "profiles", f"{kernel}_{tag}_pmc.txt"), khash)
-    # the roofline that bounds the GEMM: HBM below the ridge point (FLOPs per byte of the peaks), else MFMA
-    if gate_up_flops / gate_up_bytes < FP8_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9):
+    if roofline_bound(gate_up_flops, gate_up_bytes) == "hbm":
         achieved = gate_up_bytes / t_gu / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic}
