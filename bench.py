@@ -260,6 +260,9 @@ def main() -> int:
     ap.add_argument("--zipf", action="store_true", help="skew the routing of the config's shape by Zipf(1.1)")
     ap.add_argument("--algo", choices=("auto", "stream", "tiled"), default="auto",
                     help="grouped-GEMM kernel of both GEMMs (default: the library's automatic choice)")
+    ap.add_argument("--scatter", choices=("auto", "on", "off"), default="auto",
+                    help="step 7: on = routing weights applied in the down GEMM's epilogue, token-major rows, "
+                         "then a contiguous combine; off = the gather combine; auto = the layer's choice")
     ap.add_argument("--quiet", action="store_true")
     ap.add_argument("--scheme", choices=("g128", "channel", "mxfp4"), default="g128",
                     help="g128: INT4 group-128 x FP8 per token (default); channel: per-channel INT4 x INT8 per "
@@ -367,14 +370,15 @@ def measure_layer(index: int, args, log) -> dict:
     to = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)  # noqa: E731
     channel = args.scheme == "channel"
     mxfp4 = args.scheme == "mxfp4"
+    scatter = {"auto": None, "on": True, "off": False}[args.scatter]
     if channel:
         s13c, s2c = workloads.channel_scales(wl)
-        moe = W4A8MoEChannel(to(wl.w13), to(s13c), to(wl.w2), to(s2c), k=sh.k)
+        moe = W4A8MoEChannel(to(wl.w13), to(s13c), to(wl.w2), to(s2c), k=sh.k, scatter=scatter)
     elif mxfp4:
         w13m, s13m, w2m, s2m = workloads.mxfp4_weights(wl)
-        moe = W4A8MoEMxfp4(to(w13m), to(s13m), to(w2m), to(s2m), k=sh.k)
+        moe = W4A8MoEMxfp4(to(w13m), to(s13m), to(w2m), to(s2m), k=sh.k, scatter=scatter)
     else:
-        moe = W4A8MoE(to(wl.w13), to(wl.s13), to(wl.w2), to(wl.s2), k=sh.k)
+        moe = W4A8MoE(to(wl.w13), to(wl.s13), to(wl.w2), to(wl.s2), k=sh.k, scatter=scatter)
     x = torch.from_numpy(wl.x_bf16.view(np.int16)).to(dev).view(torch.bfloat16)
     logits = to(wl.logits)
     algo = {"auto": ops.W4A8_GG_AUTO, "stream": ops.W4A8_GG_STREAM, "tiled": ops.W4A8_GG_TILED}[args.algo]
@@ -479,7 +483,8 @@ def measure_layer(index: int, args, log) -> dict:
              "empty_experts": int((counts == 0).sum())}
     config = {"workload": sh.name, "tokens": sh.T, "hidden": sh.H, "intermediate": sh.I, "experts": sh.E,
               "top_k": sh.k, "scheme": {"channel": "per-channel int4 x per-token int8",
-                                        "mxfp4": "mxfp4 g32 x fp8", "g128": "int4 g128 x fp8"}[args.scheme]}
+                                        "mxfp4": "mxfp4 g32 x fp8", "g128": "int4 g128 x fp8"}[args.scheme],
+              "combine": "scatter in the down GEMM + contiguous sum" if moe.uses_scatter(sh.T) else "gather"}
     device = torch.cuda.get_device_name(0)
     del graph, moe, x, logits, y
     torch.cuda.synchronize()

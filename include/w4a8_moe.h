@@ -283,6 +283,60 @@ int w4a8_moe_unpermute(const float* o, const int32_t* inv_pos, const float* w,
                        int64_t T, int32_t k, int64_t H, void* y, int32_t y_dtype, void* stream);
 
 /*
+ * Step 7 with the routing-weighted scatter done in the down GEMM's epilogue:
+ * each expert output row is weighted and written to its token's slot, and the
+ * combine sums each token's k slots.  (Each token's output is the sum of its
+ * top-k experts' outputs weighted by the router's weights: "从 755GB 到
+ * 395GB", section 我们量化了什么, 256 routed experts per layer, and the
+ * "GLM-5.3-W4A8" card, section 量化方式.)  Three calls:
+ *
+ * w4a8_moe_row_sources -- for every routed index f = t*k + j (inv_pos[f] = p,
+ *   0 <= p < M_total): row_src[p] = f and row_scale[p] = fl32(a_scale[p] * w[f]).
+ *   inv_pos : int32 [T*k].  w : fp32 [T][k].  a_scale : fp32 [M_total] (the down
+ *   GEMM's activation scales, sa of step 5).  row_src : int32 [M_total],
+ *   row_scale : fp32 [M_total].  All 4-byte aligned.
+ *   Rules : T >= 0, k >= 1, T * k < 2^31, 0 <= M_total <= T * k.  M_total = 0 is
+ *   a no-op (pointers may then be null).  inv_pos must map the routed indices
+ *   one to one onto [0, M_total), as w4a8_moe_permute writes it; values outside
+ *   that range are skipped.
+ *
+ * w4a8_moe_grouped_gemm_scatter_prepacked (and _i8_, _mxfp4_) -- the grouped
+ *   GEMM of the matching _prepacked call, with row p of the result stored as
+ *   row row_dst[p] of out.  Called with a_scale = row_scale and row_dst = row_src
+ *   it writes o_tok[f, :] = w[f] * o[p, :] (the weight enters through the row's
+ *   scale).  row_dst : int32 [M_total], 4-byte aligned, each value a distinct
+ *   row of out (not checked).  out : fp32 [rows][N], 16-byte aligned; rows of
+ *   out that no row_dst names are left as they were.  Other arguments and rules
+ *   as in the _prepacked call.
+ *
+ * w4a8_moe_combine -- y[t, :] = sum over j = 0..k-1 with inv_pos[t*k + j] >= 0,
+ *   j ascending, of o_tok[t*k + j, :] (fp32 adds).  o_tok : fp32 [T*k][H],
+ *   16-byte aligned.  y and y_dtype as in w4a8_moe_unpermute.
+ *   Rules : as w4a8_moe_unpermute.
+ *
+ * The chain gives step 7's y up to the rounding of w * o before the sum (one
+ * fp32 rounding more per term); its reads of the expert outputs are contiguous
+ * k-row blocks instead of gathered rows.
+ */
+int w4a8_moe_row_sources(const int32_t* inv_pos, const float* w, const float* a_scale, int64_t T, int32_t k,
+                         int64_t M_total, int32_t* row_src, float* row_scale, void* stream);
+int w4a8_moe_grouped_gemm_scatter_prepacked(const uint8_t* a, const float* a_scale, const int32_t* a_rows,
+                                            int64_t M_total, const int32_t* offsets, int32_t E,
+                                            const int32_t* w_blk, const float* s_blk, int64_t N, int64_t K,
+                                            const int32_t* row_dst, float* out, int32_t algo, void* stream);
+int w4a8_moe_grouped_gemm_scatter_i8_prepacked(const int8_t* a, const float* a_scale, const int32_t* a_rowsum,
+                                               const int32_t* a_rows, int64_t M_total, const int32_t* offsets,
+                                               int32_t E, const int32_t* w_blk, const float* w_scale, int64_t N,
+                                               int64_t K, const int32_t* row_dst, float* out, int32_t algo,
+                                               void* stream);
+int w4a8_moe_grouped_gemm_scatter_mxfp4_prepacked(const uint8_t* a, const float* a_scale, const int32_t* a_rows,
+                                                  int64_t M_total, const int32_t* offsets, int32_t E,
+                                                  const uint8_t* w_blk, const uint8_t* s_blk, int64_t N, int64_t K,
+                                                  const int32_t* row_dst, float* out, int32_t algo, void* stream);
+int w4a8_moe_combine(const float* o_tok, const int32_t* inv_pos, int64_t T, int32_t k, int64_t H, void* y,
+                     int32_t y_dtype, void* stream);
+
+/*
  * Offline step before the layer -- quantize expert weights to the layer's
  * INT4 format.  ("GLM-5.3-W4A8" card, section 量化方式: float32 weights,
  * symmetric INT4 with group size 128 along K, each group's scale chosen by the

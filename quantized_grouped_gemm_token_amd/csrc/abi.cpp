@@ -256,7 +256,7 @@ constexpr int32_t kAutoStreamAvg = 12;
 static int run_gemm(const char* name, Form form, bool fused, bool row_major, const void* a, const float* a_scale,
                     const int32_t* a_rowsum, const int32_t* a_rows, int64_t M_total, const int32_t* offsets,
                     int32_t E, const void* w, const void* s, int64_t N, int64_t K, float* out, float* pmax,
-                    int32_t algo, void* stream) {
+                    int32_t algo, void* stream, const int32_t* out_rows = nullptr) {
   if (M_total < 0 || M_total >= kMaxRows)
     return fail(W4A8_ERR_SHAPE, "%s: M_total=%lld out of range", name, (long long)M_total);
   if (E < 1 || E > 1024) return fail(W4A8_ERR_SHAPE, "%s: E=%d must be in [1, 1024]", name, E);
@@ -278,7 +278,8 @@ static int run_gemm(const char* name, Form form, bool fused, bool row_major, con
   if (!a || !a_scale || !offsets || !w || !s || !out || (fused && !pmax) || (form == Form::kChannel && !a_rowsum))
     return fail(W4A8_ERR_NULL, "%s: null pointer", name);
   if (!aligned(a, 16) || !aligned(w, 16) || !aligned(out, 16) || !aligned(a_scale, 4) || !aligned(s, 4) ||
-      !aligned(offsets, 4) || !aligned(a_rows, 4) || !aligned(pmax, 4) || !aligned(a_rowsum, 4))
+      !aligned(offsets, 4) || !aligned(a_rows, 4) || !aligned(pmax, 4) || !aligned(a_rowsum, 4) ||
+      !aligned(out_rows, 4))
     return fail(W4A8_ERR_ALIGN, "%s: a, the weights and the output must be 16-byte aligned, the rest 4-byte", name);
   if (int st = check_device()) return st;
   w4a8::GemmArgs g{static_cast<const uint8_t*>(a), a_scale, form == Form::kChannel ? a_rowsum : nullptr, a_rows,
@@ -286,6 +287,7 @@ static int run_gemm(const char* name, Form form, bool fused, bool row_major, con
   g.pmax = fused ? pmax : nullptr;
   g.mx = form == Form::kMx;
   g.row_major = row_major;
+  g.out_rows = out_rows;
   if (row_major) algo = W4A8_GG_STREAM;   // the tiled kernel reads the GEMM storage only
   (void)hipGetLastError();
   if (algo == W4A8_GG_AUTO) {
@@ -378,6 +380,35 @@ int w4a8_moe_grouped_gemm_mxfp4_prepacked(const uint8_t* a, const float* a_scale
                                           void* stream) {
   return run_gemm("grouped_gemm_mxfp4_prepacked", Form::kMx, false, false, a, a_scale, nullptr, a_rows, M_total,
                   offsets, E, w_blk, s_blk, N, K, out, nullptr, algo, stream);
+}
+
+// the scatter forms: GEMM row p stored as row row_dst[p] of out
+int w4a8_moe_grouped_gemm_scatter_prepacked(const uint8_t* a, const float* a_scale, const int32_t* a_rows,
+                                            int64_t M_total, const int32_t* offsets, int32_t E, const int32_t* w_blk,
+                                            const float* s_blk, int64_t N, int64_t K, const int32_t* row_dst,
+                                            float* out, int32_t algo, void* stream) {
+  if (M_total > 0 && !row_dst) return fail(W4A8_ERR_NULL, "grouped_gemm_scatter_prepacked: null row_dst");
+  return run_gemm("grouped_gemm_scatter_prepacked", Form::kG128, false, false, a, a_scale, nullptr, a_rows,
+                  M_total, offsets, E, w_blk, s_blk, N, K, out, nullptr, algo, stream, row_dst);
+}
+
+int w4a8_moe_grouped_gemm_scatter_i8_prepacked(const int8_t* a, const float* a_scale, const int32_t* a_rowsum,
+                                               const int32_t* a_rows, int64_t M_total, const int32_t* offsets,
+                                               int32_t E, const int32_t* w_blk, const float* w_scale, int64_t N,
+                                               int64_t K, const int32_t* row_dst, float* out, int32_t algo,
+                                               void* stream) {
+  if (M_total > 0 && !row_dst) return fail(W4A8_ERR_NULL, "grouped_gemm_scatter_i8_prepacked: null row_dst");
+  return run_gemm("grouped_gemm_scatter_i8_prepacked", Form::kChannel, false, false, a, a_scale, a_rowsum, a_rows,
+                  M_total, offsets, E, w_blk, w_scale, N, K, out, nullptr, algo, stream, row_dst);
+}
+
+int w4a8_moe_grouped_gemm_scatter_mxfp4_prepacked(const uint8_t* a, const float* a_scale, const int32_t* a_rows,
+                                                  int64_t M_total, const int32_t* offsets, int32_t E,
+                                                  const uint8_t* w_blk, const uint8_t* s_blk, int64_t N, int64_t K,
+                                                  const int32_t* row_dst, float* out, int32_t algo, void* stream) {
+  if (M_total > 0 && !row_dst) return fail(W4A8_ERR_NULL, "grouped_gemm_scatter_mxfp4_prepacked: null row_dst");
+  return run_gemm("grouped_gemm_scatter_mxfp4_prepacked", Form::kMx, false, false, a, a_scale, nullptr, a_rows,
+                  M_total, offsets, E, w_blk, s_blk, N, K, out, nullptr, algo, stream, row_dst);
 }
 
 int w4a8_moe_grouped_gemm_swiglu_mxfp4(const uint8_t* a, const float* a_scale, const int32_t* a_rows,
@@ -567,6 +598,41 @@ int w4a8_moe_unpermute(const float* o, const int32_t* inv_pos, const float* w, i
   (void)hipGetLastError();
   return launched(w4a8::launch_unpermute(o, inv_pos, w, T, k, H, y, y_dtype == W4A8_Y_BF16, as_stream(stream)),
                   "unpermute");
+}
+
+int w4a8_moe_row_sources(const int32_t* inv_pos, const float* w, const float* a_scale, int64_t T, int32_t k,
+                         int64_t M_total, int32_t* row_src, float* row_scale, void* stream) {
+  if (T < 0 || T >= kMaxRows) return fail(W4A8_ERR_SHAPE, "row_sources: T=%lld out of range", (long long)T);
+  if (k < 1 || T * (int64_t)k >= kMaxRows) return fail(W4A8_ERR_SHAPE, "row_sources: bad k=%d", k);
+  if (M_total < 0 || M_total > T * (int64_t)k)
+    return fail(W4A8_ERR_SHAPE, "row_sources: M_total=%lld must be in [0, T k]", (long long)M_total);
+  if (M_total == 0) return ok();                  // nothing routed: no row to name
+  if (!inv_pos || !w || !a_scale || !row_src || !row_scale) return fail(W4A8_ERR_NULL, "row_sources: null pointer");
+  if (!aligned(inv_pos, 4) || !aligned(w, 4) || !aligned(a_scale, 4) || !aligned(row_src, 4) ||
+      !aligned(row_scale, 4))
+    return fail(W4A8_ERR_ALIGN, "row_sources: every array must be 4-byte aligned");
+  if (int st = check_device()) return st;
+  (void)hipGetLastError();
+  return launched(w4a8::launch_row_sources(inv_pos, w, a_scale, T * (int64_t)k, M_total, row_src, row_scale,
+                                           as_stream(stream)), "row_sources");
+}
+
+int w4a8_moe_combine(const float* o_tok, const int32_t* inv_pos, int64_t T, int32_t k, int64_t H, void* y,
+                     int32_t y_dtype, void* stream) {
+  if (T < 0 || T >= kMaxRows) return fail(W4A8_ERR_SHAPE, "combine: T=%lld out of range", (long long)T);
+  if (k < 1 || T * (int64_t)k >= kMaxRows) return fail(W4A8_ERR_SHAPE, "combine: bad k=%d", k);
+  if (H <= 0 || H % 128) return fail(W4A8_ERR_SHAPE, "combine: H=%lld must be a positive multiple of 128",
+                                     (long long)H);
+  if (y_dtype != W4A8_Y_F32 && y_dtype != W4A8_Y_BF16)
+    return fail(W4A8_ERR_SHAPE, "combine: y_dtype=%d must be W4A8_Y_F32 or W4A8_Y_BF16", y_dtype);
+  if (T == 0) return ok();
+  if (!o_tok || !inv_pos || !y) return fail(W4A8_ERR_NULL, "combine: null pointer");
+  if (!aligned(o_tok, 16) || !aligned(inv_pos, 4) || !aligned(y, y_dtype == W4A8_Y_F32 ? 16 : 8))
+    return fail(W4A8_ERR_ALIGN, "combine: o_tok and f32 y must be 16-byte, bf16 y 8-byte aligned");
+  if (int st = check_device()) return st;
+  (void)hipGetLastError();
+  return launched(w4a8::launch_combine(o_tok, inv_pos, T, k, H, y, y_dtype == W4A8_Y_BF16 ? 1 : 0,
+                                       as_stream(stream)), "combine");
 }
 
 }  // extern "C"

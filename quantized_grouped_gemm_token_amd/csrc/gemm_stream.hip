@@ -253,7 +253,8 @@ __global__ __launch_bounds__(kStreamThreads, kMaxMB == 1 ? 4 : 3) void gg_stream
                                                                    const int32_t* __restrict__ w_packed,
                                                                    const float* __restrict__ w_scale, int64_t N,
                                                                    int64_t K, float* __restrict__ out,
-                                                                   float* __restrict__ pmax, int E, int sel_rows) {
+                                                                   float* __restrict__ pmax, int E, int sel_rows,
+                                                                   const int32_t* __restrict__ out_rows) {
   static_assert(!kSwiglu || NS == 2, "fused SwiGLU pairs the two subtiles of a wave");
   static_assert(2 * CH <= kStreamTiles, "the chunk's tiles must fit the LDS buffer");
   constexpr bool kInt8 = kForm == kFormChannel;
@@ -461,17 +462,18 @@ __global__ __launch_bounds__(kStreamThreads, kMaxMB == 1 ? 4 : 3) void gg_stream
               if (col == 0) sm.rmax[wave][rb] = m;
             } else if (p < r1) {
               const int64_t src = a_rows ? a_rows[p] : p;
+              const int64_t dp = out_rows ? out_rows[p] : p;   // the row of out (the scatter form: a token-major slot)
               if constexpr (kInt8) {
                 const int off = 8 * a_rowsum[src];
                 const float as = a_scale[src];
 #pragma unroll
                 for (int s = 0; s < NS; ++s)
-                  if (sub_ok[s]) out[(int64_t)p * N + n0 + 16 * s + col] = (float)(acc[b][s][r] - off) * as * ws[s];
+                  if (sub_ok[s]) out[dp * N + n0 + 16 * s + col] = (float)(acc[b][s][r] - off) * as * ws[s];
               } else {
                 const float rs = a_scale[src] * (kMx ? 1.0f : kUnitScale);
 #pragma unroll
                 for (int s = 0; s < NS; ++s)
-                  if (sub_ok[s]) out[(int64_t)p * N + n0 + 16 * s + col] = acc[b][s][r] * rs;
+                  if (sub_ok[s]) out[dp * N + n0 + 16 * s + col] = acc[b][s][r] * rs;
               }
             }
           }
@@ -521,7 +523,7 @@ static void launch_variant(const GemmArgs& g, hipStream_t stream) {
                                      : gg_stream_kernel<NS, CH, kForm, kSwiglu, false, 1>);
   hipLaunchKernelGGL(kernel, grid, dim3(kStreamThreads), 0, stream, g.a,
                      g.a_scale, g.a_rowsum, g.a_rows, g.offsets, g.w_packed, g.w_scale, g.N, g.K, g.out, g.pmax,
-                     g.E, (int)g.sel_rows);
+                     g.E, (int)g.sel_rows, g.out_rows);
 }
 
 hipError_t launch_gg_stream(const GemmArgs& g, hipStream_t stream) {

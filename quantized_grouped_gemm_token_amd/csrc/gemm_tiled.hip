@@ -166,7 +166,9 @@ __device__ __forceinline__ int tiles_of(int rows, int nb, int nw) {
 // up rows of the same 16 output columns; the epilogue writes
 // act = silu(gate) * up [M][N/2] and the tile's max |act| of each row to
 // pmax[p][s] for the slots s of 64 output columns the tile covers.
-template <int kForm, bool kSwiglu>
+// kScatter (plain form only): row p of the result is stored as row
+// out_rows[p] of out (the down GEMM writing token-major rows).
+template <int kForm, bool kSwiglu, bool kScatter = false>
 __global__ __launch_bounds__(kThreads, 1) void gg_tiled_kernel(const uint8_t* __restrict__ a,
                                                                const float* __restrict__ a_scale,
                                                                const int32_t* __restrict__ a_rowsum,
@@ -175,7 +177,8 @@ __global__ __launch_bounds__(kThreads, 1) void gg_tiled_kernel(const uint8_t* __
                                                                const int32_t* __restrict__ w_packed,
                                                                const float* __restrict__ w_scale, int64_t N,
                                                                int64_t K, float* __restrict__ out,
-                                                               float* __restrict__ pmax, int sel_rows) {
+                                                               float* __restrict__ pmax, int sel_rows,
+                                                               const int32_t* __restrict__ out_rows) {
   constexpr bool kInt8 = kForm == kFormChannel;
   constexpr bool kMx = kForm == kFormMx;
   __shared__ RingSlot ring0, ring1, ring2;
@@ -185,6 +188,7 @@ __global__ __launch_bounds__(kThreads, 1) void gg_tiled_kernel(const uint8_t* __
   __shared__ int tile_start[kMaxExperts + 1];                      // first tile index of each expert
   __shared__ int wsum[kWaves], wmax[kWaves];
   __shared__ unsigned int rmax_sm[2][kTM];                         // fused form: row max |act| of the tile, by tile parity
+  __shared__ __attribute__((aligned(16))) int dst_sm[kScatter ? kTM : 4];   // scatter form: the rows of out
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: keeps wave-indexed values scalar
@@ -544,6 +548,9 @@ __global__ __launch_bounds__(kThreads, 1) void gg_tiled_kernel(const uint8_t* __
       if (wave < kRows / 64) {
         dma4(buffer_rsrc(a_scale, 0xffffffffu), asrc, 0, &ascale_sm[64 * wave]);
         if constexpr (kInt8) dma4(buffer_rsrc(a_rowsum, 0xffffffffu), asrc, 0, &rowsum_sm[64 * wave]);
+        if constexpr (kScatter)   // the rows of out: p itself indexes out_rows (no load to wait for)
+          dma4(buffer_rsrc(out_rows, 0xffffffffu), (uint32_t)(r0 + min(64 * wave + lane, mlen - 1)) * 4u, 0,
+               &dst_sm[64 * wave]);
       }
 
       // MX and INT8 forms: three steps at a time while every step has a next stage,
@@ -590,6 +597,8 @@ __global__ __launch_bounds__(kThreads, 1) void gg_tiled_kernel(const uint8_t* __
             const v4f sc4 = lds_load<v4f>(&ascale_sm[rt]);
             i32x4 rs4 = {0, 0, 0, 0};
             if constexpr (kInt8) rs4 = lds_load<i32x4>(&rowsum_sm[rt]);
+            i32x4 dst4 = {0, 0, 0, 0};
+            if constexpr (kScatter) dst4 = lds_load<i32x4>(&dst_sm[rt]);
             // the GEMM output of B block j and row v (the value the unfused form stores)
             auto h = [&](int j, int v) {
               if constexpr (kInt8) return (float)(acc[i][j][v] - 8 * rs4[v]) * sc4[v] * ws[j];
@@ -611,7 +620,8 @@ __global__ __launch_bounds__(kThreads, 1) void gg_tiled_kernel(const uint8_t* __
                 m = max16(ok ? m : 0.0f);
                 if (ok && lr == 0) atomicMax(&rmax_sm[tpar][rt + v], __float_as_uint(m));
               } else if (rt + v < mlen) {
-                float* orow = out + (int64_t)(r0 + rt + v) * N + n0 + 64 * cg + lr;
+                const int64_t dp = kScatter ? dst4[v] : r0 + rt + v;   // the row of out
+                float* orow = out + dp * N + n0 + 64 * cg + lr;
 #pragma unroll
                 for (int j = 0; j < kBBlocks; ++j) __builtin_nontemporal_store(h(j, v), orow + 16 * j);
               }
@@ -688,12 +698,17 @@ hipError_t launch_gg_tiled(const GemmArgs& g, hipStream_t stream) {
   }
   auto go = [&](auto kernel) {
     hipLaunchKernelGGL(kernel, dim3(cu_count()), dim3(kThreads), 0, stream, g.a, g.a_scale, g.a_rowsum, g.a_rows,
-                       g.offsets, g.E, g.w_packed, g.w_scale, g.N, g.K, g.out, g.pmax, (int)g.sel_rows);
+                       g.offsets, g.E, g.w_packed, g.w_scale, g.N, g.K, g.out, g.pmax, (int)g.sel_rows,
+                       g.out_rows);
   };
   if (g.pmax) {
     if (g.a_rowsum) go(gg_tiled_kernel<kFormChannel, true>);
     else if (g.mx) go(gg_tiled_kernel<kFormMx, true>);
     else go(gg_tiled_kernel<kFormG128, true>);
+  } else if (g.out_rows) {
+    if (g.a_rowsum) go(gg_tiled_kernel<kFormChannel, false, true>);
+    else if (g.mx) go(gg_tiled_kernel<kFormMx, false, true>);
+    else go(gg_tiled_kernel<kFormG128, false, true>);
   } else {
     if (g.a_rowsum) go(gg_tiled_kernel<kFormChannel, false>);
     else if (g.mx) go(gg_tiled_kernel<kFormMx, false>);

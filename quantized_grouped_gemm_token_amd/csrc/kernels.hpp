@@ -44,6 +44,10 @@ struct GemmArgs {
   // >= 0, both kernels are launched, the stream kernel returning at once if some
   // expert has more than sel_rows rows and the tiled kernel if none has
   int32_t sel_rows = -1;
+  // plain form only: when set, GEMM row p is stored as row out_rows[p] of out
+  // (the routing-weighted scatter: with a_scale holding sa[p] w[f], row p lands
+  // weighted in its token-major slot f = t k + j)
+  const int32_t* out_rows = nullptr;
 };
 
 hipError_t launch_quant_act(const uint16_t* x, int64_t T, int64_t H, int64_t ld, uint8_t* q, float* s,
@@ -100,5 +104,11 @@ bool front_fits(int64_t T, int64_t H, int k);
 hipError_t launch_front(const FrontArgs& f, bool int8, hipStream_t stream);
 hipError_t launch_unpermute(const float* o, const int32_t* inv_pos, const float* w, int64_t T, int k, int64_t H,
                             void* y, int bf16_out, hipStream_t stream);
+// row_src[p] = f and row_scale[p] = a_scale[p] * w[f] for every routed index f (inv_pos[f] = p >= 0)
+hipError_t launch_row_sources(const int32_t* inv_pos, const float* w, const float* a_scale, int64_t R,
+                              int64_t M_total, int32_t* row_src, float* row_scale, hipStream_t stream);
+// y[t] = sum over j of o_tok[t k + j] for the routed j, j ascending
+hipError_t launch_combine(const float* o_tok, const int32_t* inv_pos, int64_t T, int k, int64_t H, void* y,
+                          int bf16_out, hipStream_t stream);
 
 }  // namespace w4a8

@@ -8,6 +8,12 @@ gate/up GEMM with SwiGLU in its epilogue, writing act = silu(gate) * up and
 partial row maxima of |act|) and requant (the codes of act): the same results with half
 the intermediate bytes.
 
+With scatter=True step 7 moves into the down GEMM's epilogue: row_sources
+gives each GEMM row p its routed index f = t k + j and the scale
+a_scale[p] w[t, j], the GEMM stores row p as row f (token-major, the routing
+weight applied), and combine sums each token's k contiguous rows in j order.
+scatter=None takes that path from SCATTER_MIN_ROWS routed rows on.
+
 Expert weights are given in the packed format (int32 [E][N][K/8] words of
 uint4b8 nibbles and fp32 [E][N][K/128] group scales) and stay resident on the
 GPU in the GEMM storage (prepack_int4, once at construction: 1 KB per 16 rows
@@ -33,9 +39,11 @@ class W4A8MoE:
     K_PER_ITEM = 8                                        # K elements per item of a weight row (int32 words)
     GEMM = staticmethod(ops.w4a8_moe_grouped_gemm_prepacked)
     GEMM_SWIGLU = staticmethod(ops.w4a8_moe_grouped_gemm_swiglu_prepacked)
+    GEMM_SCATTER = staticmethod(ops.w4a8_moe_grouped_gemm_scatter_prepacked)
+    SCATTER_MIN_ROWS = 1 << 62                            # scatter=None: the gather combine at every size
 
     def __init__(self, w13: torch.Tensor, s13: torch.Tensor, w2: torch.Tensor, s2: torch.Tensor, k: int,
-                 renormalize: bool = True, fused: bool = True, front: bool = True):
+                 renormalize: bool = True, fused: bool = True, front: bool = True, scatter: bool | None = None):
         E, N13, KW13 = w13.shape
         E2, H, KW2 = w2.shape
         c = self.K_PER_ITEM
@@ -45,6 +53,7 @@ class W4A8MoE:
         self.E, self.H, self.I, self.k = E, H, N13 // 2, k
         self.renormalize = renormalize
         self.fused = fused
+        self.scatter = scatter
         self.front = front                                # steps 1-3 as one call (w4a8_moe_front)
         self.steps = (("front",) if front else ("quant_act", "route", "permute")) + self.STEPS[3:]
         self._bufs: dict[int, dict] = {}
@@ -63,6 +72,7 @@ class W4A8MoE:
                 inv_pos=e((R,), torch.int32), workspace=e((max(nbytes, 4),), torch.uint8),
                 counter=torch.zeros((1,), dtype=torch.int32, device=dev),   # the front call's counter
                 qa=e((R, self.I), torch.uint8), sa=e((R,), torch.float32), o=e((R, self.H), torch.float32),
+                row_src=e((R,), torch.int32), row_scale=e((R,), torch.float32),
             )
             if self.fused:
                 self._bufs[T].update(act=e((R, self.I), torch.float32), pmax=e((R, self.I // 64), torch.float32))
@@ -78,6 +88,10 @@ class W4A8MoE:
         return w13b, s13b, w2b, s2b
 
     STEPS = ("quant_act", "route", "permute", "gemm_gate_up", "swiglu", "gemm_down", "unpermute")
+
+    def uses_scatter(self, T: int) -> bool:
+        """Whether a forward over T tokens folds the routing weights into the down GEMM."""
+        return self.scatter if self.scatter is not None else T * self.k >= self.SCATTER_MIN_ROWS
 
     def forward(self, x: torch.Tensor, logits: torch.Tensor, y: torch.Tensor | None = None,
                 y_dtype: torch.dtype = torch.float32, algo: int = ops.W4A8_GG_AUTO,
@@ -116,6 +130,13 @@ class W4A8MoE:
             step("gemm_gate_up", self.GEMM, b["qx"], b["sx"], b["row_token"], b["offsets"],
                  self.w13, self.s13, R, b["h"], algo)
             step("swiglu", ops.w4a8_moe_swiglu, b["h"], b["qa"], b["sa"])
+        if self.uses_scatter(T):
+            def down():
+                ops.w4a8_moe_row_sources(b["inv_pos"], b["w"], b["sa"], R, b["row_src"], b["row_scale"])
+                self.GEMM_SCATTER(b["qa"], b["row_scale"], None, b["offsets"], self.w2, self.s2, R, b["row_src"],
+                                  b["o"], algo)
+            step("gemm_down", down)
+            return step("unpermute", ops.w4a8_moe_combine, b["o"], b["inv_pos"], T, self.k, y, y_dtype)
         step("gemm_down", self.GEMM, b["qa"], b["sa"], None, b["offsets"], self.w2, self.s2, R, b["o"], algo)
         return step("unpermute", ops.w4a8_moe_unpermute, b["o"], b["inv_pos"], b["w"], y, y_dtype)
 
@@ -190,6 +211,13 @@ class W4A8MoEChannel(W4A8MoE):
             step("gemm_gate_up", ops.w4a8_moe_grouped_gemm_i8_prepacked, b["qx"], b["sx"], b["rx"],
                  b["row_token"], b["offsets"], self.w13, self.s13, b["h"], R, algo)
             step("swiglu", ops.w4a8_moe_swiglu_i8, b["h"], b["qa"], b["sa"], b["ra"])
+        if self.uses_scatter(T):
+            def down():
+                ops.w4a8_moe_row_sources(b["inv_pos"], b["w"], b["sa"], R, b["row_src"], b["row_scale"])
+                ops.w4a8_moe_grouped_gemm_scatter_i8_prepacked(b["qa"], b["row_scale"], b["ra"], None, b["offsets"],
+                                                              self.w2, self.s2, R, b["row_src"], b["o"], algo)
+            step("gemm_down", down)
+            return step("unpermute", ops.w4a8_moe_combine, b["o"], b["inv_pos"], T, self.k, y, y_dtype)
         step("gemm_down", ops.w4a8_moe_grouped_gemm_i8_prepacked, b["qa"], b["sa"], b["ra"], None, b["offsets"],
              self.w2, self.s2, b["o"], R, algo)
         return step("unpermute", ops.w4a8_moe_unpermute, b["o"], b["inv_pos"], b["w"], y, y_dtype)
@@ -205,6 +233,7 @@ class W4A8MoEMxfp4(W4A8MoE):
     K_PER_ITEM = 2                                        # two E2M1 codes per byte
     GEMM = staticmethod(ops.w4a8_moe_grouped_gemm_mxfp4_prepacked)
     GEMM_SWIGLU = staticmethod(ops.w4a8_moe_grouped_gemm_swiglu_mxfp4_prepacked)
+    GEMM_SCATTER = staticmethod(ops.w4a8_moe_grouped_gemm_scatter_mxfp4_prepacked)
 
     @staticmethod
     def prepack(w13, s13, w2, s2):

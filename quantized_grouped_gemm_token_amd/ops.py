@@ -74,6 +74,14 @@ _SIGNATURES = {
         [_c_p, _c_p, _c_p, _i64, _c_p, _i32, _c_p, _c_p, _i64, _i64, _c_p, _c_p, _c_p]),
     "w4a8_moe_grouped_gemm_swiglu_mxfp4_prepacked": (ctypes.c_int,
         [_c_p, _c_p, _c_p, _i64, _c_p, _i32, _c_p, _c_p, _i64, _i64, _c_p, _c_p, _i32, _c_p]),
+    "w4a8_moe_row_sources": (ctypes.c_int, [_c_p, _c_p, _c_p, _i64, _i32, _i64, _c_p, _c_p, _c_p]),
+    "w4a8_moe_grouped_gemm_scatter_prepacked": (ctypes.c_int,
+        [_c_p, _c_p, _c_p, _i64, _c_p, _i32, _c_p, _c_p, _i64, _i64, _c_p, _c_p, _i32, _c_p]),
+    "w4a8_moe_grouped_gemm_scatter_i8_prepacked": (ctypes.c_int,
+        [_c_p, _c_p, _c_p, _c_p, _i64, _c_p, _i32, _c_p, _c_p, _i64, _i64, _c_p, _c_p, _i32, _c_p]),
+    "w4a8_moe_grouped_gemm_scatter_mxfp4_prepacked": (ctypes.c_int,
+        [_c_p, _c_p, _c_p, _i64, _c_p, _i32, _c_p, _c_p, _i64, _i64, _c_p, _c_p, _i32, _c_p]),
+    "w4a8_moe_combine": (ctypes.c_int, [_c_p, _c_p, _i64, _i32, _i64, _c_p, _i32, _c_p]),
     "w4a8_moe_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "w4a8_moe_last_error": (ctypes.c_char_p, []),
     "w4a8_moe_device_supported": (ctypes.c_int, []),
@@ -615,13 +623,29 @@ def _plain_out(out, M_total: int, N: int, dev):
     return out
 
 
-def _gemm_g128(prepacked, a, a_scale, a_rows, offsets, w_packed, w_scale, M_total, out, algo):
+def _row_dst(row_dst, M_total: int, out, dev):
+    """The scatter forms: row_dst int32 [>= M_total], and an explicit out."""
+    _need(row_dst, "row_dst", torch.int32, 1, dev)
+    if row_dst.numel() < M_total:
+        raise ValueError("row_dst must hold M_total entries")
+    if out is None:
+        raise ValueError("the scatter forms write into a given out (its rows are row_dst's targets)")
+
+
+def _gemm_g128(prepacked, a, a_scale, a_rows, offsets, w_packed, w_scale, M_total, out, algo, row_dst=None):
     dev = _gemm_inputs(a, a_scale, a_rows, offsets, M_total, torch.uint8)
     E, N, K = _int4_weights(w_packed, "w_packed", dev, prepacked)
     _g128_scales(w_scale, "w_scale", dev, E, N, K, prepacked)
     if a.shape[1] != K or offsets.numel() != E + 1:
         raise ValueError("w_packed, w_scale and offsets [E+1] must match a [*, K]")
+    if row_dst is not None:
+        _row_dst(row_dst, M_total, out, dev)
     out = _plain_out(out, M_total, N, dev)
+    if row_dst is not None:
+        _check("w4a8_moe_grouped_gemm_scatter_prepacked", lib().w4a8_moe_grouped_gemm_scatter_prepacked(
+            _p(a), _p(a_scale), _p(a_rows), M_total, _p(offsets), E, _p(w_packed), _p(w_scale), N, K, _p(row_dst),
+            _p(out), algo, _stream(dev)))
+        return out
     args = (_p(a), _p(a_scale), _p(a_rows), M_total, _p(offsets), E, _p(w_packed), _p(w_scale), N, K, _p(out))
     if prepacked:
         _check("w4a8_moe_grouped_gemm_prepacked", lib().w4a8_moe_grouped_gemm_prepacked(*args, algo, _stream(dev)))
@@ -645,7 +669,7 @@ def w4a8_moe_grouped_gemm_prepacked(a: torch.Tensor, a_scale: torch.Tensor, a_ro
     return _gemm_g128(True, a, a_scale, a_rows, offsets, w_packed, w_scale, M_total, out, algo)
 
 
-def _gemm_i8(prepacked, a, a_scale, a_rowsum, a_rows, offsets, w_packed, w_scale, out, M_total, algo):
+def _gemm_i8(prepacked, a, a_scale, a_rowsum, a_rows, offsets, w_packed, w_scale, out, M_total, algo, row_dst=None):
     if M_total is None:
         M_total = a_rows.numel() if a_rows is not None else a.shape[0]
     dev = _gemm_inputs(a, a_scale, a_rows, offsets, M_total, torch.int8)
@@ -654,7 +678,14 @@ def _gemm_i8(prepacked, a, a_scale, a_rowsum, a_rows, offsets, w_packed, w_scale
     _need(w_scale, "w_scale", torch.float32, 2, dev)
     if a.shape[1] != K or tuple(w_scale.shape) != (E, N) or offsets.numel() != E + 1:
         raise ValueError("a must be [*, K], w_scale [E, N], offsets [E+1]")
+    if row_dst is not None:
+        _row_dst(row_dst, M_total, out, dev)
     out = _plain_out(out, M_total, N, dev)
+    if row_dst is not None:
+        _check("w4a8_moe_grouped_gemm_scatter_i8_prepacked", lib().w4a8_moe_grouped_gemm_scatter_i8_prepacked(
+            _p(a), _p(a_scale), _p(a_rowsum), _p(a_rows), M_total, _p(offsets), E, _p(w_packed), _p(w_scale), N, K,
+            _p(row_dst), _p(out), algo, _stream(dev)))
+        return out
     args = (_p(a), _p(a_scale), _p(a_rowsum), _p(a_rows), M_total, _p(offsets), E, _p(w_packed), _p(w_scale), N,
             K, _p(out))
     if prepacked:
@@ -750,12 +781,19 @@ def w4a8_moe_grouped_gemm_swiglu_i8_prepacked(a: torch.Tensor, a_scale: torch.Te
     return _gemm_swiglu("i8", True, a, a_scale, a_rowsum, a_rows, offsets, w13, s13, M_total, act, act_pmax, algo)
 
 
-def _gemm_mx(prepacked, a, a_scale, a_rows, offsets, w_packed, w_scale, M_total, out, algo):
+def _gemm_mx(prepacked, a, a_scale, a_rows, offsets, w_packed, w_scale, M_total, out, algo, row_dst=None):
     dev = _gemm_inputs(a, a_scale, a_rows, offsets, M_total, torch.uint8)
     E, N, K = _mx_weights(w_packed, w_scale, ("w_packed", "w_scale"), dev, prepacked)
     if a.shape[1] != K or offsets.numel() != E + 1:
         raise ValueError("w_packed, w_scale and offsets [E+1] must match a [*, K]")
+    if row_dst is not None:
+        _row_dst(row_dst, M_total, out, dev)
     out = _plain_out(out, M_total, N, dev)
+    if row_dst is not None:
+        _check("w4a8_moe_grouped_gemm_scatter_mxfp4_prepacked", lib().w4a8_moe_grouped_gemm_scatter_mxfp4_prepacked(
+            _p(a), _p(a_scale), _p(a_rows), M_total, _p(offsets), E, _p(w_packed), _p(w_scale), N, K, _p(row_dst),
+            _p(out), algo, _stream(dev)))
+        return out
     args = (_p(a), _p(a_scale), _p(a_rows), M_total, _p(offsets), E, _p(w_packed), _p(w_scale), N, K, _p(out))
     if prepacked:
         _check("w4a8_moe_grouped_gemm_mxfp4_prepacked",
@@ -779,6 +817,75 @@ def w4a8_moe_grouped_gemm_mxfp4_prepacked(a: torch.Tensor, a_scale: torch.Tensor
                                           algo: int = W4A8_GG_AUTO):
     """The same on the GEMM storage (w4a8_moe_prepack_mxfp4)."""
     return _gemm_mx(True, a, a_scale, a_rows, offsets, w_packed, w_scale, M_total, out, algo)
+
+
+# -------------------------------------------------- step 7 with the scatter in the down GEMM
+def w4a8_moe_row_sources(inv_pos: torch.Tensor, w: torch.Tensor, a_scale: torch.Tensor, M_total: int,
+                         row_src: torch.Tensor | None = None, row_scale: torch.Tensor | None = None):
+    """inv_pos int32 [T*k], w fp32 [T, k], a_scale fp32 [>= M_total] -> (row_src int32 [M_total]: the routed
+    index f of each row p, row_scale fp32 [M_total]: a_scale[p] * w[f])."""
+    _need(inv_pos, "inv_pos", torch.int32, 1)
+    dev = inv_pos.device
+    _need(w, "w", torch.float32, 2, dev)
+    _need(a_scale, "a_scale", torch.float32, 1, dev)
+    T, k = w.shape
+    if inv_pos.numel() != T * k or a_scale.numel() < M_total:
+        raise ValueError("inv_pos must be [T*k] and a_scale hold M_total entries")
+    row_src = torch.empty((M_total,), dtype=torch.int32, device=dev) if row_src is None else row_src
+    row_scale = torch.empty((M_total,), dtype=torch.float32, device=dev) if row_scale is None else row_scale
+    _need(row_src, "row_src", torch.int32, 1, dev)
+    _need(row_scale, "row_scale", torch.float32, 1, dev)
+    if row_src.numel() < M_total or row_scale.numel() < M_total:
+        raise ValueError("row_src and row_scale must hold M_total entries")
+    _check("w4a8_moe_row_sources", lib().w4a8_moe_row_sources(_p(inv_pos), _p(w), _p(a_scale), T, k, M_total,
+                                                              _p(row_src), _p(row_scale), _stream(dev)))
+    return row_src, row_scale
+
+
+def w4a8_moe_grouped_gemm_scatter_prepacked(a: torch.Tensor, a_scale: torch.Tensor, a_rows: torch.Tensor | None,
+                                            offsets: torch.Tensor, w_packed: torch.Tensor, w_scale: torch.Tensor,
+                                            M_total: int, row_dst: torch.Tensor, out: torch.Tensor,
+                                            algo: int = W4A8_GG_AUTO):
+    """w4a8_moe_grouped_gemm_prepacked with row p of the result stored as row row_dst[p] of out."""
+    return _gemm_g128(True, a, a_scale, a_rows, offsets, w_packed, w_scale, M_total, out, algo, row_dst)
+
+
+def w4a8_moe_grouped_gemm_scatter_i8_prepacked(a: torch.Tensor, a_scale: torch.Tensor, a_rowsum: torch.Tensor,
+                                               a_rows: torch.Tensor | None, offsets: torch.Tensor,
+                                               w_packed: torch.Tensor, w_scale: torch.Tensor, M_total: int,
+                                               row_dst: torch.Tensor, out: torch.Tensor, algo: int = W4A8_GG_AUTO):
+    """w4a8_moe_grouped_gemm_i8_prepacked with row p of the result stored as row row_dst[p] of out."""
+    return _gemm_i8(True, a, a_scale, a_rowsum, a_rows, offsets, w_packed, w_scale, out, M_total, algo, row_dst)
+
+
+def w4a8_moe_grouped_gemm_scatter_mxfp4_prepacked(a: torch.Tensor, a_scale: torch.Tensor,
+                                                  a_rows: torch.Tensor | None, offsets: torch.Tensor,
+                                                  w_packed: torch.Tensor, w_scale: torch.Tensor, M_total: int,
+                                                  row_dst: torch.Tensor, out: torch.Tensor,
+                                                  algo: int = W4A8_GG_AUTO):
+    """w4a8_moe_grouped_gemm_mxfp4_prepacked with row p of the result stored as row row_dst[p] of out."""
+    return _gemm_mx(True, a, a_scale, a_rows, offsets, w_packed, w_scale, M_total, out, algo, row_dst)
+
+
+def w4a8_moe_combine(o_tok: torch.Tensor, inv_pos: torch.Tensor, T: int, k: int, y: torch.Tensor | None = None,
+                     y_dtype: torch.dtype = torch.float32):
+    """o_tok fp32 [T*k, H] (token-major), inv_pos int32 [T*k] -> y [T, H]: each token's routed rows summed."""
+    _need(o_tok, "o_tok", torch.float32, 2)
+    dev = o_tok.device
+    _need(inv_pos, "inv_pos", torch.int32, 1, dev)
+    H = o_tok.shape[1]
+    if inv_pos.numel() != T * k or o_tok.shape[0] < T * k:
+        raise ValueError("inv_pos must be [T*k] and o_tok at least [T*k, H]")
+    if y is None:
+        y = torch.empty((T, H), dtype=y_dtype, device=dev)
+    if y.dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("y must be float32 or bfloat16")
+    _need(y, "y", y.dtype, 2, dev)
+    if tuple(y.shape) != (T, H):
+        raise ValueError("y must be [T, H]")
+    code = W4A8_Y_F32 if y.dtype == torch.float32 else W4A8_Y_BF16
+    _check("w4a8_moe_combine", lib().w4a8_moe_combine(_p(o_tok), _p(inv_pos), T, k, H, _p(y), code, _stream(dev)))
+    return y
 
 
 def w4a8_moe_grouped_gemm_swiglu_mxfp4(a: torch.Tensor, a_scale: torch.Tensor, a_rows: torch.Tensor | None,

@@ -32,6 +32,13 @@ hipError_t launch_permute(const int32_t*, int64_t, int, int, int32_t*, int32_t*,
 hipError_t launch_gg_stream(const GemmArgs&, hipStream_t) { return absent(); }
 hipError_t launch_gg_tiled(const GemmArgs&, hipStream_t) { return absent(); }
 bool tiled_fits(const GemmArgs&) { return true; }
+hipError_t launch_row_sources(const int32_t*, const float*, const float*, int64_t, int64_t, int32_t*, float*,
+                              hipStream_t) {
+  return absent();
+}
+hipError_t launch_combine(const float*, const int32_t*, int64_t, int, int64_t, void*, int, hipStream_t) {
+  return absent();
+}
 hipError_t launch_swiglu(const float*, int64_t, int64_t, uint8_t*, float*, hipStream_t) { return absent(); }
 hipError_t launch_quant_act_i8(const uint16_t*, int64_t, int64_t, int64_t, int8_t*, float*, int32_t*, hipStream_t) {
   return absent();

@@ -368,3 +368,44 @@ def test_last_error_per_thread(L):
     for t in threads:
         t.join()
     assert not errors, errors[:5]
+
+
+def test_scatter_combine_checks(L, no_device):
+    """Step 7 with the routing weights applied in the down GEMM's epilogue: the
+    scatter GEMMs take the prepacked forms' checks plus a row_dst, and the row
+    sources and combine calls check their own shapes."""
+    g = L.w4a8_moe_grouped_gemm_scatter_prepacked
+    mx = L.w4a8_moe_grouped_gemm_scatter_mxfp4_prepacked
+    i8 = L.w4a8_moe_grouped_gemm_scatter_i8_prepacked
+    for fn in (g, mx):
+        assert fn(P, P, None, 64, P, 8, P, P, 256, 256, None, P, 0, None) == ERR_NULL     # row_dst
+        assert fn(P, P, None, 64, P, 8, P, P, 256, 256, P + 2, P, 0, None) == ERR_ALIGN  # row_dst
+        assert fn(P, P, None, 64, P, 8, P, P, 96, 256, P, P, 0, None) == ERR_SHAPE       # N % 64
+        assert fn(P, P, None, 64, P, 8, P, P, 256, 256, P, P, 7, None) == ERR_SHAPE      # algo
+        assert fn(None, None, None, 0, None, 8, None, None, 256, 256, None, None, 0, None) == OK
+    assert i8(P, P, P, None, 64, P, 8, P, P, 256, 256, None, P, 0, None) == ERR_NULL
+    assert i8(P, P, P, None, 64, P, 8, P, P, 256, 256, P + 2, P, 0, None) == ERR_ALIGN
+    assert i8(None, None, None, None, 0, None, 8, None, None, 256, 256, None, None, 0, None) == OK
+
+    rs = L.w4a8_moe_row_sources
+    assert rs(P, P, P, 4, 0, 4, P, P, None) == ERR_SHAPE            # k >= 1
+    assert rs(P, P, P, 4, 2, 9, P, P, None) == ERR_SHAPE            # M_total <= T k
+    assert rs(P, P, P, -1, 2, 0, P, P, None) == ERR_SHAPE
+    assert rs(P, None, P, 4, 2, 8, P, P, None) == ERR_NULL
+    assert rs(P, P, P, 4, 2, 8, P, P + 2, None) == ERR_ALIGN
+    assert rs(None, None, None, 0, 2, 0, None, None, None) == OK
+
+    c = L.w4a8_moe_combine
+    assert c(P, P, 4, 2, 100, P, 0, None) == ERR_SHAPE               # H % 128
+    assert c(P, P, 4, 2, 256, P, 5, None) == ERR_SHAPE               # y dtype
+    assert c(P, P, 4, 0, 256, P, 0, None) == ERR_SHAPE
+    assert c(P + 4, P, 4, 2, 256, P, 0, None) == ERR_ALIGN           # o_tok 16 bytes
+    assert c(P, P, 4, 2, 256, P + 8, 0, None) == ERR_ALIGN           # f32 y 16 bytes
+    assert c(P, None, 4, 2, 256, P, 0, None) == ERR_NULL
+    assert c(None, None, 0, 2, 256, None, 0, None) == OK
+    if no_device:
+        assert g(P, P, None, 64, P, 8, P, P, 256, 256, P, P, 0, None) == ERR_DEVICE
+        assert i8(P, P, P, None, 64, P, 8, P, P, 256, 256, P, P, 0, None) == ERR_DEVICE
+        assert mx(P, P, None, 64, P, 8, P, P, 256, 256, P, P, 0, None) == ERR_DEVICE
+        assert rs(P, P, P, 4, 2, 8, P, P, None) == ERR_DEVICE
+        assert c(P, P, 4, 2, 256, P + 8, 1, None) == ERR_DEVICE      # bf16 y: 8 bytes suffice
