@@ -323,3 +323,37 @@ def test_unfused_calls_sampled_rows(run):
             go = ops.w4a8_moe_grouped_gemm_mxfp4_prepacked(to_dev(qa), to_dev(sa), None, to_dev(sub), moe.w2,
                                                            moe.s2, P.size, algo=algo)
         assert_float_parity(host(go), o, f"{sh.name} ({form}) down algo={algo}", fro_tight=fro)
+
+
+def test_scatter_chain(run):
+    """Step 7 as a scatter from the down GEMM, at full size on the layer's own buffers: the row sources
+    invert the permutation exactly, the scatter GEMM's rows are bit for bit the plain GEMM's (same codes,
+    same scales row_scale = sa w, the same automatic kernel choice), and the contiguous combine gives the
+    layer's gather output (checked against the oracle above) up to one more fp32 rounding per term."""
+    wl, got, form, moe = run["wl"], run["got"], run["form"], run["moe"]
+    sh = wl.shape
+    b = moe.buffers(sh.T)
+    R = sh.T * sh.k
+    say(f"{sh.name} ({form}): scatter chain")
+    row_src, row_scale = ops.w4a8_moe_row_sources(b["inv_pos"], b["w"], b["sa"], R)
+    inv = got["inv_pos"]
+    want_src = np.empty(R, np.int32)
+    want_src[inv] = np.arange(R, dtype=np.int32)
+    assert np.array_equal(host(row_src), want_src)
+    o_tok = torch.empty((R, sh.H), dtype=torch.float32, device="cuda:0")
+    if form == "channel":
+        plain = ops.w4a8_moe_grouped_gemm_i8_prepacked(b["qa"], row_scale, b["ra"], None, b["offsets"], moe.w2,
+                                                       moe.s2, M_total=R)
+        ops.w4a8_moe_grouped_gemm_scatter_i8_prepacked(b["qa"], row_scale, b["ra"], None, b["offsets"], moe.w2,
+                                                       moe.s2, R, row_src, o_tok)
+    else:
+        plain = moe.GEMM(b["qa"], row_scale, None, b["offsets"], moe.w2, moe.s2, R)
+        moe.GEMM_SCATTER(b["qa"], row_scale, None, b["offsets"], moe.w2, moe.s2, R, row_src, o_tok)
+    # every row of the scatter output against the plain GEMM's row, compared on the device
+    same = torch.equal(o_tok.index_select(0, row_src.long()).view(torch.int32), plain.view(torch.int32))
+    del plain
+    assert same, "scatter rows differ from the plain GEMM's"
+    y = host(ops.w4a8_moe_combine(o_tok, b["inv_pos"], sh.T, sh.k))
+    del o_tok
+    r = assert_float_parity(y, got["y"], f"{sh.name} ({form}) scatter vs gather output", fro_tight=1e-6)
+    say(f"{sh.name} ({form}) scatter chain output vs the gather output: {r}")
