@@ -57,3 +57,35 @@ def test_graph_replay_matches_eager(scheme, shape):
     g.replay()
     torch.cuda.synchronize()
     assert torch.equal(y, y2_eager)
+
+
+@pytest.mark.parametrize("scheme", ["g128", "channel", "mxfp4"])
+def test_graph_follows_the_routing(scheme):
+    """The automatic kernel choice is taken on the device, so one captured graph serves batches that
+    call for either kernel: captured on uniform routing (a few rows per expert: the streaming kernel
+    runs), replayed on routing that sends 100 tokens to one expert (the tiled kernel runs), and back.
+    Before each replay an eager step on the other batch leaves its values in every shared buffer, so a
+    replay in which neither kernel ran would not give the expected output."""
+    wl = workloads.make_custom(128, 512, 256, 64, 2, seed=61)
+    say(f"graph follows the routing {scheme}")
+    moe = _layer(wl, scheme)
+    x, logits = bf16_to_dev(wl.x_bf16), to_dev(wl.logits)
+    skew = logits.clone()
+    skew[:100, 5] += 100.0                      # expert 5: 100 rows, past the streaming kernel's 32
+    uniform = logits.clone()
+    y_uni = moe(x, uniform).clone()
+    y_skew = moe(x, skew).clone()
+    torch.cuda.synchronize()
+    assert not torch.equal(y_uni, y_skew)
+    counts = torch.diff(moe.buffers(128)["offsets"]).cpu()
+    assert int(counts.max()) >= 100
+    y = torch.empty_like(y_uni)
+    g = moe.capture(x, logits, y)                # captured on the uniform batch
+    for i, (src, other, want) in enumerate([(skew, uniform, y_skew), (uniform, skew, y_uni), (skew, uniform, y_skew)]):
+        moe(x, other)                            # the other batch's values in every buffer
+        torch.cuda.synchronize()
+        logits.copy_(src)
+        y.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y, want), f"replay {i} differs from the eager step on the same routing"
