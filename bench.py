@@ -127,6 +127,35 @@ def cpu_baseline(wl, n_tokens: int, scheme: str = "g128") -> dict:
                               "sample": f"the same {n_tokens} tokens with BLAS on 1 thread; {runs[1]:.1f} s wall"}}
 
 
+def oracle_configs(indices, log) -> int:
+    """The oracle's whole layer on every token of each listed workload, timed on this host's cores (BLAS
+    on all of them; for the decode-sized workloads also on one thread): one JSON line per workload."""
+    from threadpoolctl import threadpool_limits
+
+    from quantized_grouped_gemm_token_amd import workloads
+    cores = os.cpu_count() or 1
+    for index in indices:
+        t0 = time.perf_counter()
+        wl = workloads.make_skewed_decode() if index == 5 else workloads.make_config(index)
+        gen_s = time.perf_counter() - t0
+        sh = wl.shape
+        sel = np.arange(sh.T)
+        log(f"oracle on {sh.name} (generated in {gen_s:.1f} s)")
+        line = {"oracle_workload": sh.name, "tokens": sh.T, "cores": cores}
+        for threads in ((cores, 1) if sh.T <= 256 and index != 5 else (cores,)):
+            with threadpool_limits(limits=threads):
+                t0 = time.perf_counter()
+                res = _oracle_layer(wl, sel, "g128")
+                sec = time.perf_counter() - t0
+            key = "all_cores" if threads == cores else "one_thread"
+            line[key] = {"seconds": round(sec, 2), "tokens_per_s": round(sh.T / sec, 3)}
+            log(f"  {key}: {sec:.1f} s")
+        line["touched_experts"] = int((np.diff(res["offsets"]) > 0).sum())
+        print(json.dumps(line), flush=True)
+        del wl, res
+    return 0
+
+
 def bench_wquant_mxfp4(args, log) -> int:
     """The MXFP4 quantizer on the gate/up weights of 16 experts (fp32 [16, 4096, 6144]): HBM-bound."""
     import torch
@@ -263,6 +292,9 @@ def main() -> int:
     ap.add_argument("--scatter", choices=("auto", "on", "off"), default="auto",
                     help="step 7: on = routing weights applied in the down GEMM's epilogue, token-major rows, "
                          "then a contiguous combine; off = the gather combine; auto = the layer's choice")
+    ap.add_argument("--oracle-configs", default="",
+                    help="instead of the GPU benchmark, time the CPU oracle's whole layer on every token of "
+                         "these workloads (comma-separated indices, e.g. 0,1,2,3,4,5): one JSON line each")
     ap.add_argument("--quiet", action="store_true")
     ap.add_argument("--scheme", choices=("g128", "channel", "mxfp4"), default="g128",
                     help="g128: INT4 group-128 x FP8 per token (default); channel: per-channel INT4 x INT8 per "
@@ -280,6 +312,10 @@ def main() -> int:
         print(f"bench.py: this benchmark runs on one GPU; --gpus {args.gpus} is not supported "
               "(the layer holds all experts on one device and has no multi-GPU path)", file=sys.stderr)
         return 2
+
+    log = (lambda *a: None) if args.quiet else (lambda *a: print("[bench]", *a, file=sys.stderr, flush=True))
+    if args.oracle_configs:
+        return oracle_configs([int(c) for c in args.oracle_configs.split(",")], log)
 
     import torch
 
