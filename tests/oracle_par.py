@@ -29,7 +29,7 @@ FORMS = {
 
 
 def workers() -> int:
-    """Threads to use: the host's cores, at most 16 (a GPU machine's CPU share)."""
+    """Threads to use: the host's cores, at most 16 (the CPU share of a one-GPU host)."""
     return max(1, min(16, os.cpu_count() or 1))
 
 
