@@ -27,6 +27,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libw4a8moe.so")
 ARCH = "gfx950"
+C_CALLER_SRC = os.path.join(ROOT, "tests", "c_caller", "moe_layer.cpp")
+C_CALLER = os.path.join(ROOT, "tests", "c_caller", "moe_layer")
 
 
 def hipcc() -> str:
@@ -68,7 +70,23 @@ def build(verbose: bool = True) -> str:
     os.replace(tmp, LIB)
     if verbose:
         print(f"built {LIB} from {len(srcs)} sources", file=sys.stderr)
+    if os.path.exists(C_CALLER_SRC):
+        build_c_caller(verbose)
     return LIB
+
+
+def build_c_caller(verbose: bool = True) -> str:
+    """The native test caller (host code only, linked against the library with a relative rpath)."""
+    tmp = C_CALLER + ".tmp"
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-O2", "-std=c++17", "-Wall", f"-I{INCLUDE}", C_CALLER_SRC,
+           "-o", tmp, f"-L{PKG}", "-lw4a8moe", "-Wl,-rpath,$ORIGIN/../../quantized_grouped_gemm_token_amd"]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"build of the native caller failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, C_CALLER)
+    if verbose:
+        print(f"built {C_CALLER}", file=sys.stderr)
+    return C_CALLER
 
 
 if __name__ == "__main__":

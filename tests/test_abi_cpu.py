@@ -409,3 +409,19 @@ def test_scatter_combine_checks(L, no_device):
         assert mx(P, P, None, 64, P, 8, P, P, 256, 256, P, P, 0, None) == ERR_DEVICE
         assert rs(P, P, P, 4, 2, 8, P, P, None) == ERR_DEVICE
         assert c(P, P, 4, 2, 256, P + 8, 1, None) == ERR_DEVICE      # bf16 y: 8 bytes suffice
+
+
+def test_native_caller_without_device(no_device, tmp_path):
+    """The native C++ caller (built with the library) links against it through a relative path and,
+    on a host without a gfx950, exits with status 2 and the library's message before any allocation."""
+    from quantized_grouped_gemm_token_amd import build as B
+    assert os.path.exists(B.C_CALLER), "build the library first (it builds the native caller too)"
+    if not no_device:
+        pytest.skip("a supported GPU is present; the GPU tests run the caller")
+    r = subprocess.run([B.C_CALLER, str(tmp_path), "4", "256", "128", "8", "2"], capture_output=True, text=True,
+                       timeout=60)
+    assert r.returncode == 2, (r.returncode, r.stderr)
+    assert "no gfx950 device" in r.stderr
+    r = subprocess.run([B.C_CALLER, str(tmp_path), "4", "200", "128", "8", "2"], capture_output=True, text=True,
+                       timeout=60)
+    assert r.returncode == 1 and "bad sizes" in r.stderr
