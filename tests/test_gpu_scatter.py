@@ -262,3 +262,55 @@ def test_layer_scatter_graph_replay(scheme):
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(y, y_eager), f"replay {i} differs from the eager step"
+
+
+@pytest.mark.parametrize("form", ["g128", "channel", "mxfp4"])
+@pytest.mark.parametrize("algo", ALGOS)
+@pytest.mark.parametrize("E,N,K,counts,src_rows", [
+    (4, 256, 256, [3, 0, 17, 1], 9),                # gathered rows (a_rows), one-block stream kernel
+    (3, 320, 384, [70, 1, 129], 40),                # gathered rows, ragged tiles
+    (1, 64, 128, [1], 1),                           # one row
+    (1024, 128, 128, [1 if e % 97 == 0 else 0 for e in range(1023)] + [40], 30),   # 1024 experts, 11 used
+])
+def test_grouped_gemm_scatter_gather_and_edges(form, E, N, K, counts, src_rows, algo, rng):
+    """The scatter forms with gathered activation rows (row p of A is a[a_rows[p]]), a single row and the
+    most experts: rows bit-identical to the plain GEMM's at their destinations."""
+    M = int(np.sum(counts))
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    x = rng.standard_normal((src_rows, K)).astype(np.float32)
+    a, sa = oracle.quant_rows_i8(x) if form == "channel" else oracle.quant_rows(x)
+    rows = rng.integers(0, src_rows, size=M).astype(np.int32)
+    R = M + 5
+    dst = rng.permutation(R)[:M].astype(np.int32)
+    out = torch.full((R, N), float(SENTINEL), dtype=torch.float32, device="cuda:0")
+    say(f"scatter gather/edges {form} E={E} N={N} K={K} M={M} algo={algo}")
+    if form == "g128":
+        w = rng.integers(0, 2**32, size=(E, N, K // 8), dtype=np.uint32).view(np.int32)
+        s = rng.lognormal(-4, 0.5, size=(E, N, K // 128)).astype(np.float32)
+        wb, sb = prepack_int4(w, s)
+        plain = ops.w4a8_moe_grouped_gemm_prepacked(to_dev(a), to_dev(sa), to_dev(rows), to_dev(offsets), wb, sb, M,
+                                                    algo=algo)
+        ops.w4a8_moe_grouped_gemm_scatter_prepacked(to_dev(a), to_dev(sa), to_dev(rows), to_dev(offsets), wb, sb, M,
+                                                    to_dev(dst), out, algo=algo)
+    elif form == "channel":
+        w = rng.integers(0, 2**32, size=(E, N, K // 8), dtype=np.uint32).view(np.int32)
+        ws = rng.lognormal(-4, 0.5, size=(E, N)).astype(np.float32)
+        rowsum = oracle.code_row_sums(a)
+        wb = prepack_int4(w)[0]
+        plain = ops.w4a8_moe_grouped_gemm_i8_prepacked(to_dev(a), to_dev(sa), to_dev(rowsum), to_dev(rows),
+                                                       to_dev(offsets), wb, to_dev(ws), M_total=M, algo=algo)
+        ops.w4a8_moe_grouped_gemm_scatter_i8_prepacked(to_dev(a), to_dev(sa), to_dev(rowsum), to_dev(rows),
+                                                       to_dev(offsets), wb, to_dev(ws), M, to_dev(dst), out,
+                                                       algo=algo)
+    else:
+        w = rng.integers(0, 256, size=(E, N, K // 2), dtype=np.uint8)
+        s = rng.integers(118, 136, size=(E, N, K // 32)).astype(np.uint8)
+        wb, sb = ops.w4a8_moe_prepack_mxfp4(to_dev(w), to_dev(s))
+        plain = ops.w4a8_moe_grouped_gemm_mxfp4_prepacked(to_dev(a), to_dev(sa), to_dev(rows), to_dev(offsets), wb,
+                                                          sb, M, algo=algo)
+        ops.w4a8_moe_grouped_gemm_scatter_mxfp4_prepacked(to_dev(a), to_dev(sa), to_dev(rows), to_dev(offsets), wb,
+                                                          sb, M, to_dev(dst), out, algo=algo)
+    got = host(out)
+    assert np.array_equal(got[dst].view(np.uint32), host(plain).view(np.uint32))
+    untouched = np.setdiff1d(np.arange(R), dst)
+    assert np.all(got[untouched].view(np.uint32) == SENTINEL.view(np.uint32))
