@@ -353,6 +353,24 @@ def test_unpermute(T, k, H, dt, rng):
         assert_float_parity(oracle.bf16_bits_to_f32(host(yb)), want, "unpermute bf16")
 
 
+@pytest.mark.parametrize("T,k,H", [(37, 3, 384), (200, 8, 1024)])
+def test_unpermute_skips_unrouted(T, k, H, rng):
+    """Routed indices the permutation left out (inv_pos = -1: ids out of range) contribute nothing: the
+    oracle's step 7 with those weights set to zero (and any row index in their place)."""
+    R = T * k
+    unrouted = rng.random(R) < 0.1
+    M = int((~unrouted).sum())
+    inv = np.full(R, -1, np.int32)
+    inv[~unrouted] = rng.permutation(M).astype(np.int32)
+    o = rng.standard_normal((R, H)).astype(np.float32)      # rows M.. are never named
+    w = rng.random((T, k)).astype(np.float32)
+    w_zeroed = np.where(unrouted.reshape(T, k), np.float32(0), w)
+    want = oracle.unpermute(o, np.maximum(inv, 0), w_zeroed)
+    say(f"unpermute with {int(unrouted.sum())} unrouted indices T={T} k={k} H={H}")
+    y = host(ops.w4a8_moe_unpermute(to_dev(o), to_dev(inv), to_dev(w)))
+    assert_float_parity(y, want, "unpermute with unrouted indices", fro_tight=1e-6)
+
+
 # -------------------------------------------------------------- whole layer
 def _layer_vs_oracle(wl, algo=ops.W4A8_GG_AUTO, y_dtype=torch.float32, fused=True):
     sh = wl.shape
