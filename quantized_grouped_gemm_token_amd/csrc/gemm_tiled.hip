@@ -91,8 +91,8 @@ static_assert(kSlotBytes == kWideRows * kGroup + kWideCols * kGroup / 2, "slot s
 
 // One ring slot: the activation rows of one group, then its weight columns
 // (column n of a 16-column load is at 64 n of its 1 KB piece in HBM).
-//   a: row r, 16-byte chunk c (K bytes 16c..16c+15 of the group) at r*128 + 16*(c ^ ((r >> 1) & 7))
-//   w: column n, chunk c (packed bytes 16c..16c+15) at W + n*64 + 16*(c ^ ((n >> 2) & 3)),
+//   a: row r, 16-byte chunk c (K bytes 16c..16c+15 of the group) at r*128 + 16*(c ^ swz_a(r))
+//   w: column n, chunk c (packed bytes 16c..16c+15) at W + n*64 + 16*(c ^ swz_w(n)),
 //      W = 256 * 128 (square tile) or 128 * 128 (wide tile)
 // The three slots are separate LDS variables addressed with compile-time
 // slot numbers, so that the compiler can tell the slot being read from the
@@ -100,6 +100,20 @@ static_assert(kSlotBytes == kWideRows * kGroup + kWideCols * kGroup / 2, "slot s
 struct __attribute__((aligned(16))) RingSlot {
   uint8_t b[kSlotBytes];
 };
+
+// The swizzles.  A 16-byte LDS read of a wave is served a few lanes at a time:
+// 8 lanes per cycle over 32 four-byte banks, or 16 lanes over 64 banks.  The
+// operand reads have lane l read row (or column) l % 16 of a block at one chunk
+// position, so the chunk slots of those rows must spread over the banks in
+// either case:
+//   rows (128 bytes apart): the slots of rows 0..7 and of rows 8..15 are all
+//     different (8 lanes, 32 banks), and so are those of the even rows and of
+//     the odd rows (16 lanes, 64 banks: rows 2i and 2i + 1 sit 32 banks apart);
+//   columns (64 bytes apart, 4 slots): (n mod 2, slot) differs among columns
+//     0..7 and among 8..15, and (n mod 4, slot) among 0..15.
+// Both depend on the row or column modulo 16 only.
+__device__ __forceinline__ int swz_a(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+__device__ __forceinline__ int swz_w(int n) { return ((n >> 2) ^ (n >> 1)) & 3; }
 
 template <int S, typename T>
 __device__ __forceinline__ T& slot(T& r0, T& r1, T& r2) {
@@ -248,11 +262,11 @@ __global__ __launch_bounds__(kThreads, 1) void gg_tiled_kernel(const uint8_t* __
   // bases of the blocks are multiples of 16, so the swizzle depends on lr only);
   // the A operand's two 16-byte chunks: 2 lq and 2 lq + 1 (K bytes 32 lq .. +31),
   // in the MX form lq and lq + 4
-  const int fa = (lr >> 1) & 7;                   // activation swizzle of row 16 b + lr
+  const int fa = swz_a(lr);                       // activation swizzle of row 16 b + lr
   const int ca0 = kMx ? lq : 2 * lq, ca1 = kMx ? lq + 4 : 2 * lq + 1;
   const uint32_t a_rd0 = (uint32_t)lr * kGroup + 16u * (uint32_t)(ca0 ^ fa);
   const uint32_t a_rd1 = (uint32_t)lr * kGroup + 16u * (uint32_t)(ca1 ^ fa);
-  const uint32_t w_rd_lane = (uint32_t)lr * 64u + 16u * (uint32_t)(lq ^ ((lr >> 2) & 3));
+  const uint32_t w_rd_lane = (uint32_t)lr * 64u + 16u * (uint32_t)(lq ^ swz_w(lr));
 
   // Tile t runs on the XCD and in the round that keep data sharing local:
   // workgroups are dispatched round-robin over the XCDs, so workgroup w sits
@@ -328,7 +342,7 @@ __global__ __launch_bounds__(kThreads, 1) void gg_tiled_kernel(const uint8_t* __
       for (int q = 0; q < kALoads; ++q) {
         const int r = kARows * wave + 8 * q + (lane >> 3);
         const int p = r0 + min(r, mlen - 1);
-        const int c = (lane & 7) ^ ((r >> 1) & 7);
+        const int c = (lane & 7) ^ swz_a(r);
         aoff[q] = (uint32_t)(a_rows ? a_rows[p] : p) * (uint32_t)K + 16u * (uint32_t)c;
       }
       // weights: columns kWCols wave + 16 q + lane / 4 of the tile, chunk position lane % 4:
@@ -340,7 +354,7 @@ __global__ __launch_bounds__(kThreads, 1) void gg_tiled_kernel(const uint8_t* __
       const __amdgpu_buffer_rsrc_t rw =
           buffer_rsrc(reinterpret_cast<const uint8_t*>(w_packed) + (int64_t)e * N * row_bytes, (uint32_t)N * row_bytes);
       const int vb = n0 + kWCols * wave < N ? n0 + kWCols * wave : 0;
-      const uint32_t woff = (uint32_t)(lane >> 2) * 64u + 16u * (uint32_t)((lane & 3) ^ ((lane >> 4) & 3));
+      const uint32_t woff = (uint32_t)(lane >> 2) * 64u + 16u * (uint32_t)((lane & 3) ^ swz_w(lane >> 2));
       // group scales: the words of group g of all N columns are contiguous
       const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(w_scale + (int64_t)e * N * G, (uint32_t)(N * G * 4));
       const int scol = min(n0 + 64 * sw + lane, (int)N - 1);
