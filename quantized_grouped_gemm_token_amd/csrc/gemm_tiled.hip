@@ -1,10 +1,11 @@
 // Grouped W4A8 GEMM, tiled form: for many rows per expert (prefill).
 //
 // A persistent kernel (one workgroup of 8 waves per CU) walks the ragged
-// list of tiles of all experts.  An expert with more than 128 rows is cut into
-// n = ceil(rows / 256) square tiles of equal height (rows / n, rounded) x 256
-// output columns; one with at most 128 rows gets wide tiles of 128 rows x 512
-// columns instead (half as many tiles for the same weight bytes).  Equal
+// list of tiles of all experts.  An expert's rows are cut into M blocks of
+// equal height (rows / n, rounded): n = ceil(rows / 256) square ones, tiled by
+// 256 output columns, or n = ceil(rows / 128) wide ones, tiled by 512 columns
+// (at most 128 rows: half as many tiles per M block for the same weight bytes),
+// whichever shape fills its tiles better (see square_mblocks).  Equal
 // heights matter: the tiles that read the same weight columns, or the same
 // activation rows, run at the same speed and stay in step through K, so the
 // XCD's L2 serves the shared bytes to all of them.  With a full tile and a
@@ -161,13 +162,23 @@ __device__ __forceinline__ T lds_load(const void* p) {
   return *reinterpret_cast<const T*>(__builtin_assume_aligned(p, 16));
 }
 
-// tiles of an expert with `rows` rows: more than 128 rows, ceil(rows / 256)
-// square tiles of equal height per 256-column block; 1..128 rows, one wide
-// tile per 512 columns
-__device__ __forceinline__ int square_mblocks(int rows) { return rows > kWideRows ? (rows + kTM - 1) / kTM : 0; }
-__device__ __forceinline__ int has_wide(int rows) { return (rows > 0 && rows <= kWideRows) ? 1 : 0; }
+// tiles of an expert with `rows` rows: M blocks of equal height, either
+// ceil(rows / 256) square ones (per 256-column block) or ceil(rows / 128) wide
+// ones (per 512 columns), whichever fills its tiles better.  Wide when
+// rows mod 256 is 1..128 (and for 1..128 rows): 280 rows make three wide M
+// blocks of 93-94 rows (24 tiles of 6 A blocks per wave at N = 4096) where two
+// square ones of 140 rows ran 32 tiles of 5 blocks and loaded 256 activation
+// rows per tile for 140.
+__device__ __forceinline__ int square_mblocks(int rows) {
+  if (rows <= kWideRows) return 0;
+  const int nsq = (rows + kTM - 1) / kTM, nwide = (rows + kWideRows - 1) / kWideRows;
+  return nwide < 2 * nsq ? 0 : nsq;
+}
+__device__ __forceinline__ int wide_mblocks(int rows) {
+  return rows > 0 && square_mblocks(rows) == 0 ? (rows + kWideRows - 1) / kWideRows : 0;
+}
 __device__ __forceinline__ int tiles_of(int rows, int nb, int nw) {
-  return square_mblocks(rows) * nb + has_wide(rows) * nw;
+  return square_mblocks(rows) * nb + wide_mblocks(rows) * nw;
 }
 
 // kForm: kFormG128, the group-128 FP8 form; kFormChannel, the per-channel
@@ -288,27 +299,21 @@ __global__ __launch_bounds__(kThreads, 1) void gg_tiled_kernel(const uint8_t* __
     const int r_e = offsets[e], rows_e = offsets[e + 1] - r_e;
     const int msq = square_mblocks(rows_e);    // 0: the expert has wide tiles only
     const int local = t - tile_start[e];
-    bool is_wide;
-    int r0, mlen, n0;
-    if (msq > 0) {
-      // square tile (mb, nb): the expert's M blocks in groups of kGroupM, each group
-      // walking the column blocks with its M blocks adjacent
-      const int mg = local / (kGroupM * NB);
-      const int gm0 = mg * kGroupM, gsz = min(kGroupM, msq - gm0);
-      const int r = local - mg * kGroupM * NB;
-      const int nb = r / gsz, mb = gm0 + (r - nb * gsz);
-      // M block mb of msq: rows_e / msq rows, the first rows_e % msq blocks one more
-      const int base = rows_e / msq, extra = rows_e - base * msq;
-      is_wide = false;
-      r0 = r_e + mb * base + min(mb, extra);
-      mlen = base + (mb < extra ? 1 : 0);
-      n0 = nb * kTN;
-    } else {
-      is_wide = true;
-      r0 = r_e;
-      mlen = rows_e;
-      n0 = local * kWideCols;
-    }
+    // tile (mb, nb) of the expert's M blocks and column blocks (square: 256 columns,
+    // wide: 512): the M blocks in groups of kGroupM, each group walking the column
+    // blocks with its M blocks adjacent
+    const bool is_wide = msq == 0;
+    const int nm = is_wide ? wide_mblocks(rows_e) : msq;
+    const int ncb = is_wide ? NW : NB;
+    const int mg = local / (kGroupM * ncb);
+    const int gm0 = mg * kGroupM, gsz = min(kGroupM, nm - gm0);
+    const int rr = local - mg * kGroupM * ncb;
+    const int nb = rr / gsz, mb = gm0 + (rr - nb * gsz);
+    // M block mb of nm: rows_e / nm rows, the first rows_e % nm blocks one more
+    const int base = rows_e / nm, extra = rows_e - base * nm;
+    const int r0 = r_e + mb * base + min(mb, extra);
+    const int mlen = base + (mb < extra ? 1 : 0);
+    const int n0 = nb * (is_wide ? kWideCols : kTN);
 
     // The rest of the tile (K loop and epilogue) is compiled per tile shape
     // and per number kNB of A blocks of the wave (0, 1, 2, 4, 5, 6, 7 or 8), without
@@ -662,12 +667,15 @@ __global__ __launch_bounds__(kThreads, 1) void gg_tiled_kernel(const uint8_t* __
     // wave), square tiles those of rg + 2 i < ceil(mlen / 16); none if the
     // wave's 64 columns are past N (N % 64 == 0: a column group is wholly in
     // or out).  A square tile has at least 128 rows, so each of its waves
-    // with columns has 4 to 8 blocks (a variant for each count: two tiles of
-    // an expert with 257..384 rows then cost what a full and a remainder tile did).
+    // with columns has 4 to 8 blocks; a wide tile of an expert with more than
+    // 128 rows has at least 65, so 5 to 8 (a variant for each count).
     const int mb16 = (mlen + 15) >> 4;
     if (is_wide) {
       const int nact = __builtin_amdgcn_readfirstlane(n0 + 64 * wave < N ? min(kABlocks, mb16) : 0);
-      if (nact > 4) run_tile(std::true_type{}, std::integral_constant<int, 8>{});
+      if (nact > 7) run_tile(std::true_type{}, std::integral_constant<int, 8>{});
+      else if (nact == 7) run_tile(std::true_type{}, std::integral_constant<int, 7>{});
+      else if (nact == 6) run_tile(std::true_type{}, std::integral_constant<int, 6>{});
+      else if (nact == 5) run_tile(std::true_type{}, std::integral_constant<int, 5>{});
       else if (nact > 2) run_tile(std::true_type{}, std::integral_constant<int, 4>{});
       else if (nact == 2) run_tile(std::true_type{}, std::integral_constant<int, 2>{});
       else if (nact == 1) run_tile(std::true_type{}, std::integral_constant<int, 1>{});
