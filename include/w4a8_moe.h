@@ -80,8 +80,8 @@ typedef enum w4a8_status {
 #define W4A8_Y_BF16 1
 
 /* algo values of the _prepacked grouped GEMM calls.  W4A8_GG_AUTO takes the
- * streaming kernel while no expert has more than 32 rows and the average expert
- * at most 12 (M_total <= 12 E), else the tiled one.  Where M_total does not
+ * streaming kernel while no expert has more than 20 rows and the average expert
+ * at most 10 (M_total <= 10 E), else the tiled one.  Where M_total does not
  * settle it, both kernels are enqueued and the one the largest expert (known on
  * the device only) does not call for returns at once.  The calls without
  * _prepacked always take the streaming kernel. */

@@ -242,13 +242,14 @@ int w4a8_moe_front_i8(const uint16_t* x_bf16, int64_t T, int64_t H, int64_t ld_x
 enum class Form { kG128, kChannel, kMx };
 
 // W4A8_GG_AUTO: the stream kernel while no expert has more than kAutoStreamRows
-// rows and the average expert at most kAutoStreamAvg.  Measured layer times on the
-// decode shape (H 6144, I 2048, 256 experts, top-8): uniform routing at 384 tokens
-// (12 rows on average, 24 at most) ties, at 512 (16, 33) and 768 (24, 41) the tiled
-// kernel is 3-13% faster; Zipf(1.1)-skewed routing at 128-384 tokens (126-376 rows
-// in the hottest expert) favours it by 22-36%.
-constexpr int32_t kAutoStreamRows = 32;
-constexpr int32_t kAutoStreamAvg = 12;
+// rows and the average expert at most kAutoStreamAvg.  Measured gate/up GEMM times
+// on the decode shape (H 6144, I 2048, 256 experts, top-8, uniform routing; stream
+// against tiled): 256 tokens (8 rows on average, 18 at most) 0.544 against 0.561
+// ms; 384 tokens (12, 24) 0.581 against 0.569; 512 (16, 33) 0.635 against 0.578;
+// 1024 (32, 51) 0.854 against 0.625.  Zipf(1.1)-skewed routing at 128-384 tokens
+// (126-376 rows in the hottest expert) favours the tiled kernel by 22-36%.
+constexpr int32_t kAutoStreamRows = 20;
+constexpr int32_t kAutoStreamAvg = 10;
 
 // Checks every argument of one grouped GEMM, then launches it.  fused: N is
 // 2I (gate and up rows) and out is act [M_total][I] with pmax [M_total][I/64].

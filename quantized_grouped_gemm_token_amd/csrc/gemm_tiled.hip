@@ -425,6 +425,27 @@ __global__ __launch_bounds__(kThreads, 1) void gg_tiled_kernel(const uint8_t* __
         for (int j = 0; j < kBBlocks; ++j)
 #pragma unroll
           for (int v = 0; v < 4; ++v) acc[i][j][v] = 0;
+      // group-128 form: the last A block's products of a group and their group scales, scaled
+      // into acc at the start of the next group (after its barrier, while its first LDS reads are
+      // in flight) rather than before the barrier; zero before the first group
+      v4f c_pend[kBBlocks];
+      float s_pend[kBBlocks];
+#pragma unroll
+      for (int j = 0; j < kBBlocks; ++j) {
+        s_pend[j] = 0.0f;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) c_pend[j][v] = 0.0f;
+      }
+      auto apply_pending = [&]() {
+        if constexpr (!kInt8 && !kMx && kNB > 0) {
+#pragma unroll
+          for (int j = 0; j < kBBlocks; ++j) {
+#pragma unroll
+            for (int v = 0; v < 4; ++v) acc[kNB - 1][j][v] = fmaf(s_pend[j], c_pend[j][v], acc[kNB - 1][j][v]);
+            asm volatile("" : "+v"(acc[kNB - 1][j]));
+          }
+        }
+      };
       const uint32_t a_blk0 = (uint32_t)(16 * rg) * kGroup;             // first A block of the wave
       const uint32_t w_rd = kWBase + (uint32_t)(64 * cg) * 64u + w_rd_lane;
 
@@ -464,9 +485,15 @@ __global__ __launch_bounds__(kThreads, 1) void gg_tiled_kernel(const uint8_t* __
           v8i b[kBBlocks];
           i32x4 bx[kBBlocks];   // MX: the packed bytes are the operand
 #pragma unroll
-          for (int j = 0; j < kBBlocks; ++j) {
-            if constexpr (kMx) bx[j] = lds_load<i32x4>(&sl.b[w_rd + j * 16 * 64]);
-            else b[j] = nibbles_to_fp8(lds_load<i32x4>(&sl.b[w_rd + j * 16 * 64]));
+          for (int j = 0; j < kBBlocks; ++j) bx[j] = lds_load<i32x4>(&sl.b[w_rd + j * 16 * 64]);
+          if constexpr (!kInt8 && !kMx) {
+            __builtin_amdgcn_sched_barrier(0);
+            apply_pending();
+            __builtin_amdgcn_sched_barrier(0);
+          }
+          if constexpr (!kMx) {
+#pragma unroll
+            for (int j = 0; j < kBBlocks; ++j) b[j] = nibbles_to_fp8(bx[j]);
           }
           const float* bsum = &bias_sm[g & 1][16 * rg + 4 * lq];
           // operands of A block i: two 16-byte halves of the lane's 32 K bytes
@@ -515,7 +542,10 @@ __global__ __launch_bounds__(kThreads, 1) void gg_tiled_kernel(const uint8_t* __
               }
             } else if constexpr (!kInt8 && !kMx && i == kNB && i >= 1) {
 #pragma unroll
-              for (int j = 0; j < kBBlocks; ++j) scale_into(std::integral_constant<int, i - 1>{}, j);
+              for (int j = 0; j < kBBlocks; ++j) {
+                c_pend[j] = c[j];
+                s_pend[j] = s[j];
+              }
             }
             __builtin_amdgcn_sched_barrier(0);   // regions stay in order: no hoisting of later reads
             if constexpr (i == ((kNB >= 2 && kWaitRegion >= 1) ? 1 : 0)) {   // before the wait, which counts them
@@ -595,6 +625,7 @@ __global__ __launch_bounds__(kThreads, 1) void gg_tiled_kernel(const uint8_t* __
         }
       }
 
+      apply_pending();   // the last group's last A block
       // ---- epilogue: D lane holds column lr of its B block, rows 4 lq .. +3 of its A block
       if constexpr (kNB > 0) {
         // lane roles taken afresh: addresses built from them are not hoisted out of the tile
