@@ -487,8 +487,8 @@ def measure_layer(index: int, args, log) -> dict:
     t_gu = per_step["gemm_gate_up"] * 1e-3
     t_dn = per_step["gemm_down"] * 1e-3
     # the kernel that ran: the library's automatic choice takes the streaming one while no expert has more
-    # than 32 rows and the average at most 12, else the tiled one
-    decode = args.algo == "stream" or (args.algo == "auto" and R <= 12 * sh.E and int(counts.max()) <= 32)
+    # than 20 rows and the average at most 10, else the tiled one
+    decode = args.algo == "stream" or (args.algo == "auto" and R <= 10 * sh.E and int(counts.max()) <= 20)
     kernel = "gg_stream" if decode else "gg_tiled"
     khash = kernel_sources_hash(kernel)
     tag = workload_tag(sh) + ("" if args.scheme == "g128" else "_" + args.scheme)
