@@ -172,10 +172,12 @@ def _gemm_problem(rng, E, N, K, counts, src_rows=None):
     (2, 64, 1024, [300, 33], True),
     (8, 512, 640, [16, 16, 16, 16, 0, 15, 17, 1], False),
     (3, 320, 256, [200, 241, 0], True),            # partial tiles of 7/8 row blocks; N not a multiple of 256
-    (4, 256, 256, [128, 129, 257, 513], False),    # square tiles of equal height: 1, 2 and 3 per expert
+    (4, 256, 256, [128, 129, 257, 513], False),    # one wide M block, one square, 3 and 5 wide of equal height
+    (3, 512, 256, [70, 280, 525], True),           # wide bodies of 5, 6 and 7 A blocks; 1, 3 and 5 wide M blocks
     (2, 512, 384, [512, 769], True),
     (6, 128, 256, [17, 3, 0, 1, 2, 0], True),       # M_total <= 4 E: the one-block stream kernel, 2 row passes
-    (3, 768, 256, [1400, 5, 300], True),            # 6 M blocks: a group of 4 and a partial group of 2 (tiled order)
+    (3, 768, 256, [1500, 5, 300], True),            # 6 square M blocks: a group of 4 and a partial group of 2 (tiled order)
+    (3, 768, 256, [1400, 5, 300], True),            # 11 wide M blocks: groups of 4, 4 and 3
     (8, 256, 384, [9, 40, 0, 3, 1, 0, 2, 5], False),  # AUTO: both kernels launched, the tiled one runs
     (8, 256, 384, [9, 20, 0, 3, 1, 0, 2, 5], True),   # AUTO: both kernels launched, the stream one runs
 ])
@@ -212,7 +214,8 @@ def test_grouped_gemm_exact_integers(algo, rng):
     [9, 40, 0, 3, 1, 0],             # a 40-row expert: the tiled kernel under AUTO
     [18, 19, 20, 0, 2, 1],           # the most rows AUTO gives the stream kernel
     [64, 65, 33, 16, 0, 2],          # the multi-block stream kernel: 4, 2 and 1 blocks per load
-    [1400, 3, 0, 1, 2, 0],           # 6 M blocks of equal height in the tiled kernel, 22 row passes in the other
+    [1500, 3, 0, 1, 2, 0],           # 6 square M blocks of equal height in the tiled kernel, 24 row passes in the other
+    [70, 280, 525, 0, 3, 1],         # wide M blocks: 1, 3 and 5 per expert, bodies of 5, 6 and 7 A blocks
 ])
 def test_algos_agree_bitwise(counts, fused, rng):
     """The kernel choice is a matter of speed only: the three algos give the same bits (same

@@ -100,7 +100,8 @@ def _scatter_case(rng, counts, K, i8):
     (3, 320, 384, [70, 1, 129]),                    # ragged tiles, N not a multiple of 256
     (8, 256, 384, [9, 40, 0, 3, 1, 0, 2, 5]),       # AUTO: the tiled kernel runs
     (6, 256, 256, [64, 65, 33, 16, 0, 2]),          # multi-block stream kernel
-    (3, 768, 256, [1400, 5, 300]),                  # several M blocks per expert
+    (3, 768, 256, [1400, 5, 300]),                  # several M blocks per expert (11 wide)
+    (3, 768, 256, [1500, 5, 300]),                  # 6 square M blocks
 ])
 def test_grouped_gemm_scatter(form, E, N, K, counts, algo, rng):
     a, sa, offsets, dst, R = _scatter_case(rng, counts, K, form == "channel")
