@@ -483,7 +483,7 @@ __global__ __launch_bounds__(kThreads, 1) void gg_tiled_kernel(const uint8_t* __
         // the products of this group: kNB A blocks x kBBlocks B blocks
         auto compute = [&]() {
           v8i b[kBBlocks];
-          i32x4 bx[kBBlocks];   // MX: the packed bytes are the operand
+          i32x4 bx[kBBlocks];   // the packed bytes (MX: the operand as it is)
 #pragma unroll
           for (int j = 0; j < kBBlocks; ++j) bx[j] = lds_load<i32x4>(&sl.b[w_rd + j * 16 * 64]);
           if constexpr (!kInt8 && !kMx) {
@@ -699,7 +699,7 @@ __global__ __launch_bounds__(kThreads, 1) void gg_tiled_kernel(const uint8_t* __
     // wave's 64 columns are past N (N % 64 == 0: a column group is wholly in
     // or out).  A square tile has at least 128 rows, so each of its waves
     // with columns has 4 to 8 blocks; a wide tile of an expert with more than
-    // 128 rows has at least 65, so 5 to 8 (a variant for each count).
+    // 128 rows has at least 85, so 6 to 8 (a variant for each count).
     const int mb16 = (mlen + 15) >> 4;
     if (is_wide) {
       const int nact = __builtin_amdgcn_readfirstlane(n0 + 64 * wave < N ? min(kABlocks, mb16) : 0);
