@@ -180,6 +180,23 @@ __device__ __forceinline__ int wide_mblocks(int rows) {
 __device__ __forceinline__ int tiles_of(int rows, int nb, int nw) {
   return square_mblocks(rows) * nb + wide_mblocks(rows) * nw;
 }
+// Relative cost of one tile of an expert with `rows` rows: the A blocks per wave of
+// the body its tallest M block runs, plus 2 for the work of each K group that does not
+// grow with them (barrier, row sums, load issue).  3..10 for an expert with rows.
+constexpr int kMaxTileCost = 10;
+__device__ __forceinline__ int tile_cost(int rows) {
+  const int msq = square_mblocks(rows);
+  const int nm = msq > 0 ? msq : wide_mblocks(rows);
+  if (nm == 0) return 0;
+  const int mb16 = ((rows + nm - 1) / nm + 15) >> 4;
+  const int nact = min(kABlocks, msq > 0 ? (mb16 + 1) >> 1 : mb16);
+  const int body = nact > 4 ? nact : (msq > 0 || nact > 2) ? 4 : nact;
+  return body + 2;
+}
+// an entry of the tile list: the first tile of an expert above the expert's index
+constexpr int kExpertBits = 10;                      // kMaxExperts = 1024
+constexpr int kExpertMask = (1 << kExpertBits) - 1;
+constexpr int kMaxTiles = 1 << (31 - kExpertBits);  // tile numbers that fit an entry
 
 // kForm: kFormG128, the group-128 FP8 form; kFormChannel, the per-channel
 // variant (INT8 activations with row code sums a_rowsum, one scale per weight
@@ -210,8 +227,8 @@ __global__ __launch_bounds__(kThreads, 1) void gg_tiled_kernel(const uint8_t* __
   __shared__ __attribute__((aligned(16))) float sc0[kWideCols], sc1[kWideCols], sc2[kWideCols];   // group scales (MX: E8M0 words)
   __shared__ __attribute__((aligned(16))) float bias_sm[2][kTM];   // -2^-6 * group code sums: [group parity][row]
   __shared__ __attribute__((aligned(16))) float ascale_sm[kTM];    // token scales of the tile's rows
-  __shared__ int tile_start[kMaxExperts + 1];                      // first tile index of each expert
-  __shared__ int wsum[kWaves], wmax[kWaves];
+  __shared__ int tile_start[kMaxExperts + 1];                      // the tile list: (first tile << 10) | expert
+  __shared__ int wscan[2][2][kWaves], wmax[kWaves];
   __shared__ unsigned int rmax_sm[2][kTM];                         // fused form: row max |act| of the tile, by tile parity
   __shared__ __attribute__((aligned(16))) int dst_sm[kScatter ? kTM : 4];   // scatter form: the rows of out
 
@@ -225,27 +242,30 @@ __global__ __launch_bounds__(kThreads, 1) void gg_tiled_kernel(const uint8_t* __
   const int half = (int)(N >> 1);                              // output columns of the fused form
   int* rowsum_sm = reinterpret_cast<int*>(&bias_sm[0][0]);   // the INT8 form has no group sums: row code sums
 
-  // ---- tile numbering: exclusive prefix of per-expert tile counts (wave-level scans)
+  // ---- tile numbering.  In the fused gate/up form the experts with rows go in
+  // order of their tile cost, dearest first (ties by index), so that the last,
+  // partial round of tiles holds the cheapest ones: with 20.1 rounds of 256
+  // tiles at prefill T=8192, the workgroups that run one tile more end that
+  // much later than the rest (measured 2.5-4% off that GEMM at prefill).  The
+  // other forms keep the experts in index order: the same ordering made the
+  // down GEMM 2-9% slower.  Entry i of tile_start is the i-th expert's first
+  // tile number above its index; one block-wide scan per cost class numbers
+  // the class's tiles and entries (a single class in index order).
+  int n_list = 0;                                   // experts with rows (entries of the list)
   {
     constexpr int kPer = kMaxExperts / kThreads;   // experts per thread
-    int cnt[kPer];
-    int local = 0, most = 0;
+    int cnt[kPer], cst[kPer];
+    int most = 0;
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
       const int ex = tid * kPer + i;
       const int rows = ex < E ? offsets[ex + 1] - offsets[ex] : 0;
       cnt[i] = tiles_of(rows, NB, NW);
-      local += cnt[i];
+      cst[i] = tile_cost(rows);
       most = max(most, rows);
     }
-    int incl = local;
 #pragma unroll
-    for (int off = 1; off < kWave; off <<= 1) {
-      const int o = __shfl_up(incl, off, kWave);
-      if (lane >= off) incl += o;
-      most = max(most, __shfl_xor(most, off, kWave));
-    }
-    if (lane == kWave - 1) wsum[wave] = incl;
+    for (int off = 1; off < kWave; off <<= 1) most = max(most, __shfl_xor(most, off, kWave));
     if (lane == 0) wmax[wave] = most;
     __syncthreads();
     // the choice on the device: nothing to do when the stream kernel takes the batch
@@ -255,19 +275,60 @@ __global__ __launch_bounds__(kThreads, 1) void gg_tiled_kernel(const uint8_t* __
       for (int w = 0; w < kWaves; ++w) top = max(top, wmax[w]);
       if (top <= sel_rows) return;
     }
-    int run = 0;
-    for (int w = 0; w < wave; ++w) run += wsum[w];
-    run += incl - local;
+    int tile_base = 0;                              // tiles and entries of the dearer classes
+    if constexpr (!kSwiglu) {
 #pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-      const int ex = tid * kPer + i;
-      if (ex < E) tile_start[ex] = run;
-      run += cnt[i];
+      for (int i = 0; i < kPer; ++i) cst[i] = 1;
     }
-    if (tid == kThreads - 1) tile_start[E] = run;   // the grand total
+    for (int c = kSwiglu ? kMaxTileCost : 1; c >= 1; --c) {
+      int lt = 0, ln = 0;                           // this thread's tiles and experts of class c
+#pragma unroll
+      for (int i = 0; i < kPer; ++i)
+        if (cnt[i] > 0 && cst[i] == c) {
+          lt += cnt[i];
+          ++ln;
+        }
+      int it = lt, in = ln;
+#pragma unroll
+      for (int off = 1; off < kWave; off <<= 1) {
+        const int ot = __shfl_up(it, off, kWave), on = __shfl_up(in, off, kWave);
+        if (lane >= off) {
+          it += ot;
+          in += on;
+        }
+      }
+      // two buffers by class parity: a wave writing one has passed the barrier
+      // after which every wave read it last
+      int (&buf)[2][kWaves] = wscan[c & 1];
+      if (lane == kWave - 1) {
+        buf[0][wave] = it;
+        buf[1][wave] = in;
+      }
+      __syncthreads();
+      int bt = 0, bn = 0, tt = 0, tn = 0;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        if (w < wave) {
+          bt += buf[0][w];
+          bn += buf[1][w];
+        }
+        tt += buf[0][w];
+        tn += buf[1][w];
+      }
+      int t0 = tile_base + bt + it - lt, s0 = n_list + bn + in - ln;
+#pragma unroll
+      for (int i = 0; i < kPer; ++i)
+        if (cnt[i] > 0 && cst[i] == c) {
+          tile_start[s0++] = (t0 << kExpertBits) | (tid * kPer + i);
+          t0 += cnt[i];
+        }
+      tile_base += tt;
+      n_list += tn;
+    }
+    if (tid == 0) tile_start[n_list] = tile_base << kExpertBits;   // the grand total
     __syncthreads();
   }
-  const int total = tile_start[E];
+  const int total = tile_start[n_list] >> kExpertBits;
 
   // lane-constant parts of the swizzled LDS addresses (the row or column
   // bases of the blocks are multiples of 16, so the swizzle depends on lr only);
@@ -290,15 +351,16 @@ __global__ __launch_bounds__(kThreads, 1) void gg_tiled_kernel(const uint8_t* __
   int tpar = 0;                                                    // parity of this workgroup's tile count
   for (int t = my_slot; t < total; t += grid, tpar ^= 1) {
     // ---- which expert, and which tile of it
-    int lo_e = 0, hi_e = E;                    // tile_start[lo_e] <= t < tile_start[hi_e]
+    int lo_e = 0, hi_e = n_list;               // entry lo_e: first tile <= t < the next entry's
     while (hi_e - lo_e > 1) {
       const int mid = (lo_e + hi_e) >> 1;
-      if (tile_start[mid] <= t) lo_e = mid; else hi_e = mid;
+      if ((tile_start[mid] >> kExpertBits) <= t) lo_e = mid; else hi_e = mid;
     }
-    const int e = __builtin_amdgcn_readfirstlane(lo_e);
+    const int entry = __builtin_amdgcn_readfirstlane(tile_start[lo_e]);
+    const int e = entry & kExpertMask;
     const int r_e = offsets[e], rows_e = offsets[e + 1] - r_e;
     const int msq = square_mblocks(rows_e);    // 0: the expert has wide tiles only
-    const int local = t - tile_start[e];
+    const int local = t - (entry >> kExpertBits);
     // tile (mb, nb) of the expert's M blocks and column blocks (square: 256 columns,
     // wide: 512): the M blocks in groups of kGroupM, each group walking the column
     // blocks with its M blocks adjacent
@@ -740,7 +802,10 @@ static int cu_count() {
 bool tiled_fits(const GemmArgs& g) {
   // the tiled kernel addresses its operands with 32-bit byte offsets
   constexpr int64_t k4G = (int64_t)1 << 32;
-  return g.M_total * g.K < k4G && g.M_total * 4 < k4G && g.N * (g.K / 2) < k4G && g.N * (g.K / 128) * 4 < k4G;
+  // and the tile numbers fit an entry of the tile list: at most M_total / 128 + E M blocks
+  const int64_t tiles = (g.M_total / kWideRows + g.E + 1) * ((g.N + kTN - 1) / kTN);
+  return g.M_total * g.K < k4G && g.M_total * 4 < k4G && g.N * (g.K / 2) < k4G && g.N * (g.K / 128) * 4 < k4G &&
+         tiles < kMaxTiles;
 }
 
 hipError_t launch_gg_tiled(const GemmArgs& g, hipStream_t stream) {
