@@ -238,8 +238,9 @@ int w4a8_moe_prepack_int4(const int32_t* w_packed, const float* w_scale, int32_t
  *   1e-5 of the group's sum of |products|, so results agree with the exact
  *   sum to about 1e-5 relative (Frobenius norm over a matrix).
  *   Runs the weight-streaming kernel, which reads each expert's weights once
- *   per 16 of its rows: right for decode; for many rows per expert, prepack
- *   the weights and call w4a8_moe_grouped_gemm_prepacked.
+ *   per 16 of its rows (once per 64 when M_total > 8 E): right for decode;
+ *   for many rows per expert, prepack the weights and call
+ *   w4a8_moe_grouped_gemm_prepacked.
  */
 int w4a8_moe_grouped_gemm(const uint8_t* a, const float* a_scale, const int32_t* a_rows,
                           int64_t M_total, const int32_t* offsets, int32_t E,
