@@ -32,10 +32,18 @@ __device__ __forceinline__ void permute_scatter_rounds(const int32_t* __restrict
                                                        int32_t* __restrict__ inv_pos) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  for (int round = 0; round < kPermBlock / kPermThreads; ++round) {
+  constexpr int kRounds = kPermBlock / kPermThreads;
+  int keys[kRounds];                                // every round's id loaded at once: one wait, not one per round
+#pragma unroll
+  for (int round = 0; round < kRounds; ++round) {
+    const int64_t f = base + (int64_t)round * kPermThreads + tid;
+    keys[round] = f < R ? ids[f] : kPermMaxE;       // sentinel key for the tail
+  }
+#pragma unroll
+  for (int round = 0; round < kRounds; ++round) {
     const int64_t f = base + (int64_t)round * kPermThreads + tid;   // rounds, then threads: index order
     const bool valid = f < R;
-    int key = valid ? ids[f] : kPermMaxE;           // sentinel key for the tail
+    int key = keys[round];
     if ((unsigned)key >= (unsigned)E) key = kPermMaxE;
     if (valid && key == kPermMaxE) inv_pos[f] = -1;   // an id outside [0, E) is not routed
     const bool routed = key != kPermMaxE;
@@ -84,10 +92,17 @@ __device__ __forceinline__ void permute_small(const int32_t* __restrict__ ids, i
     for (int w = 0; w < kPermWaves; ++w) wcnt[w][e] = 0;
   }
   __syncthreads();
-  for (int i = tid; i < R; i += kPermThreads) {
-    const int e = ids[i];
-    if ((unsigned)e < (unsigned)E) atomicAdd(&run[e], 1);   // integer counts: order does not matter
+  // every id of this thread loaded at once (R <= kPermSmallMax: at most 16 each), then counted
+  constexpr int kMaxPer = (int)(kPermSmallMax / kPermThreads);
+  int mine[kMaxPer];
+#pragma unroll
+  for (int j = 0; j < kMaxPer; ++j) {
+    const int64_t i = tid + (int64_t)j * kPermThreads;
+    mine[j] = i < R ? ids[i] : -1;
   }
+#pragma unroll
+  for (int j = 0; j < kMaxPer; ++j)
+    if ((unsigned)mine[j] < (unsigned)E) atomicAdd(&run[mine[j]], 1);   // integer counts: order does not matter
   __syncthreads();
   // thread t: experts 4t .. 4t + 3 (counts past E are 0)
   int c[4], local = 0;
